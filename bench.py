@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA gather-decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config ds32_slice] [--fused]
+
+Prints ONE JSON line.  A "step" is one full pass of the path (index build,
+front-fold, cache-row write, absorption, gather-attention core, output
+absorption, o-projection) over one batch of synthetic, seeded inputs that are
+resident in HBM before timing starts.
+
+Timing: W untimed warm-up steps, then K timed steps.  Before each timed step a
+1 GiB buffer is read and written so that neither the L2s nor the 256 MB
+Infinity Cache hold the weights or the pool (cold-cache steps); HIP events on
+the step's stream bracket the step itself (the flush is outside them) and each
+of its kernels.  ``value`` is the mean step latency in microseconds.  Warm
+(back-to-back, no flush) and HIP-graph numbers are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA gather-decode step µs + achieved HBM GB/s (% of peak), n_prior=2048"
+HBM_PEAK_GBPS = 8000.0
+
+
+def alg_bytes(sh, inp) -> dict:
+    """Algorithmic HBM bytes of one step, per kernel of the separately launched
+    variant: every weight once, the gammas, activations in and out, the index
+    tensors, the RoPE tables, each distinct valid gathered row once, and the
+    written rows.  Split-K partials and query-tile round trips are overheads."""
+    import numpy as np
+
+    T, H, Q, r, dn, dr, dv, nh = (sh.n_tokens, sh.hidden, sh.q_lora_rank, sh.kv_lora_rank,
+                                  sh.qk_nope_head_dim, sh.qk_rope_head_dim, sh.v_head_dim, sh.n_heads)
+    kvr = r + dr
+    P, MB = sh.n_prior, sh.max_blocks_per_seq
+    gi = inp["gather_indices"].numpy()
+    pos = inp["positions"].numpy()
+    uniq = sum(len(np.unique(gi[t][(gi[t] >= 0) & (gi[t] <= pos[t])])) for t in range(T))
+    b = {
+        "k_down": 2 * H * (Q + kvr) + 2 * T * H + 4 * H + 4 * T * P + 4 * T + 4 * T * MB,
+        "k_qup": 2 * Q * nh * (dn + dr) + 4 * Q + 4 * r + 4 * T * dr + 4 * T + 2 * T * kvr,
+        "k_absorb": 2 * nh * dn * r,
+        "k_core": 2 * kvr * uniq,
+        "k_oabsorb": 2 * nh * dv * r,
+        "k_oproj": 2 * nh * dv * H + 2 * T * H,
+    }
+    b["step"] = sum(b.values())
+    return b
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_gather_mla_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp_cpu, budget_s: float) -> dict:
+    """The fp64 oracle, as it is, on the host cores: whole steps of this
+    workload repeated for about `budget_s` seconds (at least one)."""
+    import numpy as np
+
+    import oracle
+    from tests.harness import token_slice
+
+    sh = wl.shape
+    T = sh.n_tokens
+    o = oracle.to_f64_inputs(token_slice(inp_cpu, range(T)), block_size=sh.block_size)
+    pool = inp_cpu["kv_cache"].view(-1, sh.kv_row_dim).double().numpy()  # widened once, outside timing
+    reader = oracle.dense_row_reader(pool)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.mla_gather_decode_step(o, reader)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    return {"value": el / reps * 1e6, "unit": "us", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full {wl.name} steps (all {T} tokens, n_prior={sh.n_prior}), fp64 numpy, "
+                      f"weights and pool pre-widened to fp64 outside the timed region"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="ds32_slice")
+    ap.add_argument("--fused", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the step is single-GPU; the multi-GPU design is documented, not built)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sparse_gather_mla_amd import Dims, MlaGatherDecode
+    from tests.harness import gpu_inputs
+    from workload import config_by_name, make_inputs
+
+    wl = config_by_name(args.config)
+    sh = wl.shape
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    small_pool = sh.n_blocks * sh.block_size * sh.kv_row_dim * 2 <= (256 << 20)
+    inp = make_inputs(wl, with_pool=small_pool)  # host copy of the pool only when small (CPU baseline)
+    g = gpu_inputs(wl, inp, device=dev)
+    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens, device=0, fused=args.fused)
+    names = mod.kernel_names()
+    nk = len(names)
+    out = torch.empty((sh.n_tokens, sh.hidden), dtype=torch.bfloat16, device=dev)
+    flush = torch.empty((1 << 30) // 4, dtype=torch.float32, device=dev)
+    flush.zero_()
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        mod(g, out=out)
+    torch.cuda.synchronize()
+
+    # --- timed cold steps -------------------------------------------------
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(K):
+        flush.add_(1.0)  # read + write 1 GiB: evicts L2 and the Infinity Cache
+        mod(g, out=out, events=evs[k], stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [evs[k][0].elapsed_time(evs[k][nk]) for k in range(K)]
+    stage_ms = {names[i]: [evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)] for i in range(nk)}
+
+    # --- warm steps (no flush, back to back) ------------------------------
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        mod(g, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) / K * 1e3
+
+    # --- HIP graph of the step, cold ----------------------------------------
+    graph_us = None
+    try:
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            mod(g, out=out)  # warm the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gr, stream=side):
+                mod(g, out=out)
+        torch.cuda.synchronize()
+        gts = []
+        for _ in range(K):
+            flush.add_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            gr.replay()
+            b.record(stream)
+            gts.append((a, b))
+        torch.cuda.synchronize()
+        graph_us = statistics.mean(a.elapsed_time(b) for a, b in gts) * 1e3
+    except Exception as exc:  # pragma: no cover - reported, not fatal
+        print(f"graph capture failed: {exc}", file=sys.stderr)
+
+    ab = alg_bytes(sh, inp)
+    mean_ms = statistics.mean(step_ms)
+    stage_us = {n: statistics.mean(v) * 1e3 for n, v in stage_ms.items()}
+    dom = max(stage_us, key=stage_us.get)
+    dom_bytes = ab[dom]
+    dom_gbps = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
+    q = np.percentile(step_ms, [10, 50, 90])
+    step_gbps = ab["step"] / (mean_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(mean_ms * 1e3, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_ms, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.description}", "n_tokens": sh.n_tokens, "n_heads": sh.n_heads,
+                   "hidden": sh.hidden, "kv_lora_rank": sh.kv_lora_rank, "n_prior": sh.n_prior,
+                   "variant": "fused" if args.fused else "separate", "cache_state": "cold (1 GiB flush per step)"},
+        "achieved_GBps": round(step_gbps, 1),
+        "pct_of_hbm_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2),
+        "alg_bytes_per_step": ab["step"],
+        "step_us_p10_p50_p90": [round(x * 1e3, 3) for x in q],
+        "warm_us": round(warm_us, 3),
+        "graph_cold_us": None if graph_us is None else round(graph_us, 3),
+        "wall_ms_per_step_incl_flush": round(wall / K * 1e3, 4),
+        "stages": {n: {"us": round(stage_us[n], 3), "alg_bytes": ab[n],
+                       "GBps": round(ab[n] / (stage_us[n] * 1e-6) / 1e9, 1)} for n in names},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(dom, wl.name), "alg_bytes_per_launch": dom_bytes},
+        "accumulate": "fp32",
+    }
+    if not args.no_cpu_baseline and small_pool:
+        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

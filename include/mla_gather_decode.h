@@ -1,0 +1,188 @@
+/*
+ * mla_gather_decode.h -- C ABI of one MLA gather-decode step on an MI355X (gfx950).
+ *
+ * The step is the operation of the "MLA Attention Block Gather Decode Kernel
+ * API Reference" page (awsdocs-neuron, nkilib experimental deepseek_v32): one
+ * DeepSeek-V3.2 MLA decode step from the residual stream to this rank's
+ * attention-block output, attending only over the prior positions a lightning
+ * indexer selected.  Tensor names, shapes and meanings are the page's
+ * ("API Reference" parameter list; "Notes"; "Dimensions").
+ *
+ * Conventions for every call:
+ *   - Every tensor pointer is a DEVICE pointer on the handle's device, in
+ *     row-major layout with the shape given below.  bf16 tensors are raw
+ *     16-bit bfloat16 words.  The caller owns every buffer; the library never
+ *     allocates, frees or keeps a pointer after a call returns.
+ *   - bf16 tensor pointers and the workspace must be 16-byte aligned (the
+ *     kernels use 16-byte vector loads); fp32 and int32 pointers 4-byte.
+ *   - Calls return 0 (MLA_GD_OK) or a positive error code; nothing is thrown
+ *     across the ABI.  mla_gather_decode_strerror() names a code.
+ *   - mla_gather_decode_step() only enqueues work on the given HIP stream and
+ *     never synchronises the host; errors inside kernels are not reported
+ *     (device data validity -- slot and block ids in range, distinct slots --
+ *     is the caller's contract, as on the page).
+ *   - A handle may be used from one thread at a time.  Two steps that overlap
+ *     in time must use different workspaces.
+ */
+#ifndef MLA_GATHER_DECODE_H
+#define MLA_GATHER_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_GD_ABI_VERSION 1
+
+/* error codes */
+#define MLA_GD_OK 0
+#define MLA_GD_E_INVAL 1        /* null pointer, non-positive or inconsistent dimension, bad flag */
+#define MLA_GD_E_ALIGN 2        /* a pointer is not aligned as required above */
+#define MLA_GD_E_WORKSPACE 3    /* workspace smaller than mla_gather_decode_workspace_size() */
+#define MLA_GD_E_UNSUPPORTED 4  /* dimensions outside what the kernels handle (see create) */
+#define MLA_GD_E_HIP 5          /* a HIP runtime call or kernel launch failed */
+
+/* flags (mla_gd_dims.flags) */
+#define MLA_GD_FLAG_FUSED 1u    /* run the step as one persistent launch (ablation variant) */
+
+/*
+ * Dimensions of the step, fixed when the handle is created.  The page passes
+ * n_heads, qk_nope_head_dim, qk_rope_head_dim, kv_lora_rank, softmax_scale
+ * and norm_eps as arguments and reads every other size off tensor shapes; a C
+ * ABI has no shapes, so they are all explicit here.
+ *   hidden              width of the residual stream (hidden_states [T, hidden])
+ *   q_lora_rank         query latent width (wq_a [hidden, q_lora_rank])
+ *   kv_lora_rank        latent width of a cache row
+ *   qk_nope_head_dim    per-head query/key width RoPE does not rotate
+ *   qk_rope_head_dim    per-head query/key width RoPE rotates (even)
+ *   v_head_dim          per-head value width (out_absorb_w [n_heads, v_head_dim, kv_lora_rank])
+ *   n_heads             attention heads on this rank
+ *   block_size          rows per cache block
+ *   max_blocks_per_seq  columns of block_table
+ *   n_blocks            blocks in the cache pool
+ *   n_prior             selected prior positions per token (width of gather_indices)
+ *   max_tokens          largest n_tokens a step may be called with
+ *   softmax_scale       score scale (conventionally 1/sqrt(qk_nope_head_dim + qk_rope_head_dim))
+ *   norm_eps            epsilon of every RMSNorm (the page's default is 1e-6)
+ * A cache row is kv_lora_rank + qk_rope_head_dim wide: [normalised latent | rotated key].
+ */
+typedef struct mla_gd_dims {
+  int32_t hidden;
+  int32_t q_lora_rank;
+  int32_t kv_lora_rank;
+  int32_t qk_nope_head_dim;
+  int32_t qk_rope_head_dim;
+  int32_t v_head_dim;
+  int32_t n_heads;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t n_blocks;
+  int32_t n_prior;
+  int32_t max_tokens;
+  float softmax_scale;
+  float norm_eps;
+  uint32_t flags;
+} mla_gd_dims;
+
+/*
+ * The tensors of one step (T = n_tokens; nh, dn, dr, dv, r as in mla_gd_dims;
+ * kv_row = r + dr).  Shapes and meanings are the page's parameter list.
+ */
+typedef struct mla_gd_tensors {
+  const void* hidden_states;   /* [T, hidden] bf16: this step's residual-stream hidden states */
+  const float* input_norm_w;   /* [hidden] fp32: RMSNorm gamma of the layer input */
+  const void* wq_a;            /* [hidden, q_lora_rank] bf16: query down-projection */
+  const float* q_norm_w;       /* [q_lora_rank] fp32: RMSNorm gamma of the query latent */
+  const void* wq_b;            /* [q_lora_rank, nh*(dn+dr)] bf16: query up-projection, per head [q_nope | q_pe] */
+  const void* wkv_a;           /* [hidden, kv_row] bf16: KV down-projection, one cache row per token */
+  const float* kv_norm_w;      /* [r] fp32: RMSNorm gamma of the KV latent */
+  const void* q_absorb_w;      /* [nh, dn, r] bf16: nope half of wkv_b (nope query -> latent) */
+  const void* out_absorb_w;    /* [nh, dv, r] bf16: value half of wkv_b (latent output -> value width) */
+  const void* o_proj_w;        /* [nh*dv, hidden] bf16: this rank's shard of the o-projection */
+  const float* cos_table;      /* [T, dr/2] fp32: cosine table of interleaved RoPE */
+  const float* sin_table;      /* [T, dr/2] fp32: sine table of interleaved RoPE */
+  void* kv_cache;              /* [n_blocks, 1, block_size, kv_row] bf16, MUTATED IN PLACE:
+                                  row slot_mapping[t] is overwritten with token t's row */
+  const int32_t* slot_mapping; /* [T] int32: flat cache row each token's own key is written to */
+  const int32_t* block_table;  /* [T, max_blocks_per_seq] int32: logical-to-physical block map */
+  const int32_t* positions;    /* [T] int32: this step's absolute position per token */
+  const int32_t* gather_indices; /* [T, n_prior] int32: selected absolute prior positions, unsorted */
+  void* out;                   /* [T, hidden] bf16, written: this rank's attention-block output
+                                  (partial o-projection; no residual add, no cross-rank reduction) */
+  int32_t* gather_rows_out;    /* optional (may be NULL) [T, n_prior] int32, written: the flat cache
+                                  row each selected position resolved to, or -1 where the causal
+                                  mask removed it */
+} mla_gd_tensors;
+
+typedef struct mla_gd_handle mla_gd_handle;
+
+/*
+ * Validate dims and create a handle for HIP device `device`.  The handle holds
+ * host-side configuration only.  Returns MLA_GD_E_INVAL for inconsistent dims
+ * and MLA_GD_E_UNSUPPORTED for shapes the kernels do not handle: every
+ * projection width (hidden, q_lora_rank, kv_lora_rank + qk_rope_head_dim,
+ * n_heads*(dn+dr), kv_lora_rank) must be a multiple of 8, kv_lora_rank a
+ * multiple of 16 and at most 512, qk_rope_head_dim even and at most 128,
+ * max_tokens at most 4096.
+ */
+int mla_gather_decode_create(const mla_gd_dims* dims, int device, mla_gd_handle** out_handle);
+
+/* Release a handle (NULL is accepted). */
+void mla_gather_decode_destroy(mla_gd_handle* handle);
+
+/*
+ * Bytes of device workspace that serves every step of up to n_tokens tokens
+ * (0 if the handle is NULL or n_tokens is out of range).  The workspace holds split-K
+ * partial sums, the query tiles, attention partials and arrival counters.
+ */
+size_t mla_gather_decode_workspace_size(const mla_gd_handle* handle, int32_t n_tokens);
+
+/*
+ * Zero a workspace of `bytes` bytes on `stream` (hipStream_t; NULL = default
+ * stream).  A workspace must be zeroed once before its first step; every step
+ * leaves it ready for the next one.
+ */
+int mla_gather_decode_workspace_init(const mla_gd_handle* handle, void* workspace, size_t bytes,
+                                     void* stream);
+
+/*
+ * Enqueue one decode step for n_tokens tokens (1 <= n_tokens <= max_tokens) on
+ * `stream` (hipStream_t; NULL = default stream).  Reads every input tensor,
+ * writes `out`, row slot_mapping[t] of kv_cache for every token, the optional
+ * gather_rows_out, and the workspace.  The row a token writes is visible to
+ * the gather of every token in the same step (a token that selects its own
+ * position reads this step's row).
+ */
+int mla_gather_decode_step(mla_gd_handle* handle, const mla_gd_tensors* tensors, int32_t n_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-kernel timing.  The step runs as mla_gather_decode_kernel_count() kernel
+ * launches; mla_gather_decode_step_profiled() is mla_gather_decode_step() plus
+ * hipEventRecord(events[i], stream) before kernel i and events[count] after
+ * the last one.  `events` holds n_events >= count + 1 created hipEvent_t
+ * handles (owned by the caller).  Kernel names are static strings ("" for an
+ * index out of range).
+ */
+int mla_gather_decode_kernel_count(const mla_gd_handle* handle);
+const char* mla_gather_decode_kernel_name(const mla_gd_handle* handle, int index);
+int mla_gather_decode_step_profiled(mla_gd_handle* handle, const mla_gd_tensors* tensors, int32_t n_tokens,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* const* events, int n_events);
+
+/* Human-readable name of an error code (never NULL). */
+const char* mla_gather_decode_strerror(int code);
+
+/* hipError_t of the last failed HIP call made through this handle (0 if none). */
+int mla_gather_decode_last_hip_error(const mla_gd_handle* handle);
+
+/* MLA_GD_ABI_VERSION of the built library. */
+int mla_gather_decode_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_GATHER_DECODE_H */

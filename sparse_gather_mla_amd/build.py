@@ -1,0 +1,50 @@
+"""Offline build of the HIP library for gfx950 (hipcc cross-compiles without a GPU)."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB_NAME = "libmla_gather_decode.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+SOURCES = [os.path.join(CSRC, "mla_gather_decode.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("device_util.h", "phases.h", "step_params.h")] + [
+    os.path.join(ROOT, "include", "mla_gather_decode.h")]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build_command(out: str) -> list:
+    return [
+        hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # packed fp32 VALU forms stay off (plain scalar/float2 code only)
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"),
+        *SOURCES, "-o", out,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library in-tree and return its path.  Always recompiles."""
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = build_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

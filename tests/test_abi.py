@@ -1,0 +1,135 @@
+"""The C-ABI library: it loads, exports every function the header declares, and
+rejects bad arguments with the documented codes before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_gather_mla_amd as sgm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_gather_decode.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_gather_decode_\w+)\s*\(", src)))
+
+
+def _codes():
+    src = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(MLA_GD_\w+)\s+(\d+)", src)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sgm.LIB_PATH):
+        pytest.fail("library not built (run sparse_gather_mla_amd/build.py)")
+    return sgm.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_strerror(lib):
+    c = _codes()
+    assert lib.mla_gather_decode_abi_version() == c["MLA_GD_ABI_VERSION"]
+    seen = set()
+    for name in ("MLA_GD_OK", "MLA_GD_E_INVAL", "MLA_GD_E_ALIGN", "MLA_GD_E_WORKSPACE", "MLA_GD_E_UNSUPPORTED",
+                 "MLA_GD_E_HIP"):
+        s = lib.mla_gather_decode_strerror(c[name]).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.mla_gather_decode_strerror(12345).decode() == "unknown error"
+
+
+def _dims(**kw):
+    base = dict(hidden=256, q_lora_rank=64, kv_lora_rank=64, qk_nope_head_dim=32, qk_rope_head_dim=16,
+                v_head_dim=32, n_heads=4, block_size=16, max_blocks_per_seq=8, n_blocks=16, n_prior=32,
+                max_tokens=2, softmax_scale=0.144, norm_eps=1e-6, flags=0)
+    base.update(kw)
+    return sgm._Dims(**base)
+
+
+def _create(lib, d):
+    h = ctypes.c_void_p()
+    rc = lib.mla_gather_decode_create(ctypes.byref(d), 0, ctypes.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, "MLA_GD_OK"),
+    ({"hidden": 0}, "MLA_GD_E_INVAL"),
+    ({"n_prior": -1}, "MLA_GD_E_INVAL"),
+    ({"qk_rope_head_dim": 15}, "MLA_GD_E_INVAL"),
+    ({"flags": 8}, "MLA_GD_E_INVAL"),
+    ({"norm_eps": -1.0}, "MLA_GD_E_INVAL"),
+    ({"softmax_scale": float("nan")}, "MLA_GD_E_INVAL"),
+    ({"hidden": 260}, "MLA_GD_E_UNSUPPORTED"),
+    ({"kv_lora_rank": 1024}, "MLA_GD_E_UNSUPPORTED"),
+    ({"kv_lora_rank": 72}, "MLA_GD_E_UNSUPPORTED"),
+    ({"qk_rope_head_dim": 256}, "MLA_GD_E_UNSUPPORTED"),
+])
+def test_create_validates_dims(lib, kw, code):
+    rc, h = _create(lib, _dims(**kw))
+    assert rc == _codes()[code]
+    if rc == 0:
+        assert h.value
+        lib.mla_gather_decode_destroy(h)
+    else:
+        assert not h.value
+
+
+def test_workspace_size_and_step_argument_checks(lib):
+    c = _codes()
+    rc, h = _create(lib, _dims(max_tokens=4))
+    assert rc == 0
+    try:
+        assert lib.mla_gather_decode_workspace_size(h, 0) == 0
+        assert lib.mla_gather_decode_workspace_size(h, 5) == 0
+        sizes = [lib.mla_gather_decode_workspace_size(h, t) for t in (1, 2, 3, 4)]
+        assert all(s > 0 and s % 256 == 0 for s in sizes)
+        assert lib.mla_gather_decode_workspace_size(None, 1) == 0
+        tn = sgm._Tensors()
+        # missing tensors / workspace / handle: rejected before any device work
+        assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 1, ctypes.c_void_p(256), 1 << 20, None) == c["MLA_GD_E_INVAL"]
+        assert lib.mla_gather_decode_step(None, ctypes.byref(tn), 1, ctypes.c_void_p(256), 1 << 20, None) == c["MLA_GD_E_INVAL"]
+        for f in sgm.TENSOR_FIELDS:
+            if f != "gather_rows_out":
+                setattr(tn, f, 4096)
+        ws = ctypes.c_void_p(1 << 20)
+        assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 0, ws, sizes[0], None) == c["MLA_GD_E_INVAL"]
+        assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 5, ws, sizes[0], None) == c["MLA_GD_E_INVAL"]
+        assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 1, ws, sizes[0] - 1, None) == c["MLA_GD_E_WORKSPACE"]
+        tn.wq_b = 4096 + 8  # bf16 pointers need 16-byte alignment
+        assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 1, ws, sizes[0], None) == c["MLA_GD_E_ALIGN"]
+        tn.wq_b = 4096
+        tn.positions = 4096 + 2
+        assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 1, ws, sizes[0], None) == c["MLA_GD_E_ALIGN"]
+        tn.positions = 4096
+        assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 1, ctypes.c_void_p((1 << 20) + 16), sizes[0],
+                                          None) == c["MLA_GD_E_ALIGN"]
+        assert lib.mla_gather_decode_workspace_init(h, None, 1024, None) == c["MLA_GD_E_INVAL"]
+        assert lib.mla_gather_decode_kernel_count(h) >= 1
+        names = [lib.mla_gather_decode_kernel_name(h, i).decode() for i in range(lib.mla_gather_decode_kernel_count(h))]
+        assert all(names) and len(set(names)) == len(names)
+        assert lib.mla_gather_decode_kernel_name(h, 99) == b""
+        # profiled step: a missing or short event list is rejected
+        assert lib.mla_gather_decode_step_profiled(h, ctypes.byref(tn), 1, ws, sizes[0], None, None, 0) == c["MLA_GD_E_INVAL"]
+        ev = (ctypes.c_void_p * 2)(1, 1)
+        assert lib.mla_gather_decode_step_profiled(h, ctypes.byref(tn), 1, ws, sizes[0], None, ev, 2) == c["MLA_GD_E_INVAL"]
+    finally:
+        lib.mla_gather_decode_destroy(h)
+    lib.mla_gather_decode_destroy(None)  # NULL-safe
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(sgm, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        sgm.load_library(str(tmp_path / "missing.so"))
