@@ -52,7 +52,8 @@ def alg_bytes(sh, inp) -> dict:
         "k_absorb": 2 * nh * dn * r,
         "k_core": 2 * kvr * uniq,
         "k_oabsorb": 2 * nh * dv * r,
-        "k_oproj": 2 * nh * dv * H + 2 * T * H,
+        "k_oproj": 2 * nh * dv * H,
+        "k_out": 2 * T * H,
     }
     b["step"] = sum(b.values())
     return b
@@ -206,7 +207,7 @@ def main() -> int:
     mean_ms = statistics.mean(step_ms)
     stage_us = {n: statistics.mean(v) * 1e3 for n, v in stage_ms.items()}
     dom = max(stage_us, key=stage_us.get)
-    dom_bytes = ab[dom]
+    dom_bytes = ab.get(dom, 0)
     dom_gbps = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
     q = np.percentile(step_ms, [10, 50, 90])
     step_gbps = ab["step"] / (mean_ms * 1e-3) / 1e9
@@ -234,8 +235,8 @@ def main() -> int:
         "warm_us": round(warm_us, 3),
         "graph_cold_us": None if graph_us is None else round(graph_us, 3),
         "wall_ms_per_step_incl_flush": round(wall / K * 1e3, 4),
-        "stages": {n: {"us": round(stage_us[n], 3), "alg_bytes": ab[n],
-                       "GBps": round(ab[n] / (stage_us[n] * 1e-6) / 1e9, 1)} for n in names},
+        "stages": {n: {"us": round(stage_us[n], 3), "alg_bytes": ab.get(n, 0),
+                       "GBps": round(ab.get(n, 0) / (stage_us[n] * 1e-6) / 1e9, 1)} for n in names},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(dom, wl.name), "alg_bytes_per_launch": dom_bytes},

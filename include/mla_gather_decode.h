@@ -121,10 +121,10 @@ typedef struct mla_gd_handle mla_gd_handle;
 /*
  * Validate dims and create a handle for HIP device `device`.  The handle holds
  * host-side configuration only.  Returns MLA_GD_E_INVAL for inconsistent dims
- * and MLA_GD_E_UNSUPPORTED for shapes the kernels do not handle: every
- * projection width (hidden, q_lora_rank, kv_lora_rank + qk_rope_head_dim,
- * n_heads*(dn+dr), kv_lora_rank) must be a multiple of 8, kv_lora_rank a
- * multiple of 16 and at most 512, qk_rope_head_dim even and at most 128,
+ * and MLA_GD_E_UNSUPPORTED for shapes the kernels do not handle: hidden,
+ * q_lora_rank, qk_nope_head_dim, kv_lora_rank + qk_rope_head_dim and
+ * n_heads*(dn+dr) must be multiples of 8; kv_lora_rank one of 64, 128, 256,
+ * 512; qk_rope_head_dim even and at most 64; qk_nope_head_dim at most 512;
  * max_tokens at most 4096.
  */
 int mla_gather_decode_create(const mla_gd_dims* dims, int device, mla_gd_handle** out_handle);

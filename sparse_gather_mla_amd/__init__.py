@@ -250,6 +250,9 @@ class MlaGatherDecode:
         if events is None:
             rc = self.lib.mla_gather_decode_step(self.handle, ctypes.byref(tn), T, ws_ptr, ws_bytes, st)
         else:
+            for ev in events:
+                if not ev.cuda_event:  # torch creates the HIP event on first record
+                    ev.record(stream)
             arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
             rc = self.lib.mla_gather_decode_step_profiled(self.handle, ctypes.byref(tn), T, ws_ptr, ws_bytes, st,
                                                           arr, len(events))

@@ -16,38 +16,43 @@
 using namespace mla;
 
 // ---------------------------------------------------------------------------
-// kernels: one phase each (separately launched variant)
+// kernels: one phase each, launched in order on the caller's stream
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kBlock) void k_down(StepParams p) {
-  __shared__ float lds[4 * kGemvTT * kTile];
-  __shared__ int flag;
-  phase_down(p, blockIdx.x, lds, &flag);
+  extern __shared__ float lds[];
+  phase_down(p, blockIdx.x, lds);
 }
 
 __global__ __launch_bounds__(kBlock) void k_qup(StepParams p) {
-  __shared__ float lds[4 * kGemvTT * kTile];
-  __shared__ int flag;
-  phase_qup(p, blockIdx.x, lds, &flag);
+  extern __shared__ float lds[];
+  phase_qup(p, blockIdx.x, lds);
 }
 
 __global__ __launch_bounds__(kBlock) void k_absorb(StepParams p) {
-  __shared__ float lds[4 * kGemvTT * kTile];
+  extern __shared__ float lds[];
   phase_absorb(p, blockIdx.x, lds);
 }
 
-__global__ __launch_bounds__(kBlock) void k_core(StepParams p) {
-  __shared__ float lds[kCoreLds];
-  __shared__ int flag;
-  phase_core(p, blockIdx.x, lds, &flag);
+template <int NT, int HG, int NW>
+__global__ __launch_bounds__(NW * 64) void k_core(StepParams p) {
+  extern __shared__ float lds[];
+  core_phase<NT, HG, NW>(p, blockIdx.x, reinterpret_cast<char*>(lds));
 }
 
-__global__ __launch_bounds__(kBlock) void k_oabsorb(StepParams p) { phase_oabsorb(p, blockIdx.x); }
+__global__ __launch_bounds__(kBlock) void k_oabsorb(StepParams p) {
+  extern __shared__ float lds[];
+  phase_oabsorb(p, blockIdx.x, lds);
+}
 
 __global__ __launch_bounds__(kBlock) void k_oproj(StepParams p) {
-  __shared__ float lds[4 * kGemvTT * kTile];
-  __shared__ int flag;
-  phase_oproj(p, blockIdx.x, lds, &flag);
+  extern __shared__ float lds[];
+  phase_oproj(p, blockIdx.x, lds);
+}
+
+__global__ __launch_bounds__(kBlock) void k_out(StepParams p) {
+  extern __shared__ float lds[];
+  phase_out(p, blockIdx.x, lds);
 }
 
 __global__ __launch_bounds__(kBlock) void k_zero_u32(uint32_t* p, size_t n) {
@@ -62,25 +67,43 @@ struct mla_gd_handle {
   mla_gd_dims d;
   int device;
   int last_hip_error;
+  bool lds_ready;  // dynamic-LDS limits of the kernels raised on this device
 };
 
 namespace {
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// split-K factor: about `target` workgroups in total, at least `min_rows` rows
-// per slab, and partial sums no larger than a quarter of the weight bytes.
-void choose_split(int K, int ntiles, int T, int min_rows, int* s_out, int* ks_out) {
-  const int target = 512;
-  int s = std::max(1, cdiv(target, ntiles));
-  s = std::min(s, std::max(1, K / min_rows));
-  s = std::min(s, std::max(1, K / (4 * T)));
+constexpr int kTargetWG = 384;  // workgroups per GEMV phase (1.5 per CU)
+
+// split-K: about kTargetWG workgroups over `ntiles` column tiles, slabs of at
+// most 512 rows (the LDS activation slab) and at least 16.
+void choose_split(int K, int ntiles, int* s_out, int* ks_out) {
+  int s = cdiv(kTargetWG, ntiles);
+  s = clampi(s, cdiv(K, kTile), std::max(1, K / 16));
   int ks = cdiv(K, s);
-  ks = (ks + 3) / 4 * 4;
-  s = cdiv(K, ks);
-  *s_out = s;
+  ks = std::min(kTile, (ks + 3) / 4 * 4);
   *ks_out = ks;
+  *s_out = cdiv(K, ks);
+}
+
+struct CoreShape {
+  int hg, nw;
+};
+
+CoreShape core_shape(int n_heads) { return n_heads <= 16 ? CoreShape{1, 4} : CoreShape{8, 8}; }
+
+int core_row_pitch(int kvr) { return cdiv(kvr, 32) * 32 + 8; }
+
+size_t core_lds(const mla_gd_dims& d) {
+  const CoreShape cs = core_shape(d.n_heads);
+  const int rs = cs.nw / cs.hg;
+  const int rp = core_row_pitch(d.kv_lora_rank + d.qk_rope_head_dim);
+  size_t bytes = core_lds_bytes(rp, rs);
+  if (rs > 1) bytes = std::max(bytes, (size_t)(2 * rs * 16 + 16 * d.kv_lora_rank) * sizeof(float));
+  return bytes;
 }
 
 Plan make_plan(const mla_gd_dims& d, int T) {
@@ -88,26 +111,33 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   memset(&pl, 0, sizeof(pl));
   const int H = d.hidden, Q = d.q_lora_rank, R = d.kv_lora_rank, DR = d.qk_rope_head_dim;
   const int KVR = R + DR, QKH = d.qk_nope_head_dim + DR, N2 = d.n_heads * QKH, NH = d.n_heads;
-  const int P = d.n_prior;
+  const int P = d.n_prior, DV = d.v_head_dim;
   pl.T = T;
   pl.nt_q = cdiv(Q, kTile);
   pl.nt_kv = cdiv(KVR, kTile);
   pl.nt1 = pl.nt_q + pl.nt_kv;
-  choose_split(H, pl.nt1, T, 16, &pl.s1, &pl.ks1);
+  choose_split(H, pl.nt1, &pl.s1, &pl.ks1);
   pl.n_idx_wg = cdiv(T * P, kBlock);
   pl.nt2 = cdiv(N2, kTile);
-  choose_split(Q, pl.nt2, T, 16, &pl.s2, &pl.ks2);
-  pl.nt_r = cdiv(R, kTile);
-  pl.nhg = cdiv(NH, kHeadGroup);
+  choose_split(Q, pl.nt2, &pl.s2, &pl.ks2);
+  pl.ncc3 = R / 64;
+  const CoreShape cs = core_shape(NH);
+  pl.core_hg = cs.hg;
+  pl.core_nw = cs.nw;
+  pl.core_nhb = cdiv(NH, 16 * cs.hg);
   {
-    int ns = std::max(1, cdiv(512, T * pl.nhg));
-    ns = std::min(ns, cdiv(P, kChunk));
-    pl.ps = cdiv(cdiv(P, ns), kChunk) * kChunk;
+    const int rows_per_iter = 16 * (cs.nw / cs.hg);
+    int ns = clampi(cdiv(256, T * pl.core_nhb), 1, std::min(256, cdiv(P, rows_per_iter)));
+    pl.ps = cdiv(cdiv(P, ns), rows_per_iter) * rows_per_iter;
     pl.nsplit = cdiv(P, pl.ps);
   }
-  pl.n_oabs_wg = cdiv(NH * d.v_head_dim, 4);
-  pl.nt5 = cdiv(H, kTile);
-  choose_split(NH * d.v_head_dim, pl.nt5, T, 16, &pl.s5, &pl.ks5);
+  pl.dc5 = 16;
+  pl.nd5 = cdiv(DV, pl.dc5);
+  pl.tc5 = std::min(T, kTT);
+  pl.nt5c = cdiv(T, pl.tc5);
+  pl.nt6 = cdiv(H, kTile);
+  choose_split(NH * DV, pl.nt6, &pl.s6, &pl.ks6);
+  pl.n7 = T * cdiv(H, 64);
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -115,32 +145,18 @@ Plan make_plan(const mla_gd_dims& d, int T) {
     off = align_up(off + bytes, 256);
     return o;
   };
-  // Arrival counters first, at a fixed offset and sized for max_tokens, so a
-  // step with fewer tokens finds them where the previous step left them (zero).
-  pl.cnt1 = 0;
-  pl.cnt2 = pl.cnt1 + pl.nt1;
-  pl.cnt3 = pl.cnt2 + pl.nt2;
-  pl.cnt5 = pl.cnt3 + T * pl.nhg;
-  pl.n_cnt = (size_t)pl.cnt5 + pl.nt5;
-  const size_t max_cnt = (size_t)pl.nt1 + pl.nt2 + (size_t)d.max_tokens * pl.nhg + pl.nt5;
-  pl.off_cnt = take(max_cnt * sizeof(unsigned));
   const size_t f = sizeof(float);
   pl.off_rows = take((size_t)T * P * sizeof(int32_t));
   pl.off_part1 = take((size_t)pl.s1 * T * (Q + KVR) * f);
-  pl.off_ss1 = take((size_t)pl.nt1 * pl.s1 * T * f);
-  pl.off_qa = take((size_t)T * Q * f);
-  pl.off_kv = take((size_t)T * KVR * f);
+  pl.off_ssx = take((size_t)pl.s1 * T * f);
   pl.off_part2 = take((size_t)pl.s2 * T * N2 * f);
-  pl.off_ss2 = take((size_t)pl.nt2 * pl.s2 * T * f);
-  pl.off_q = take((size_t)T * N2 * f);
-  pl.off_qlat = take((size_t)T * NH * R * f);
-  pl.off_qpe = take((size_t)T * NH * DR * f);
-  pl.off_cm = take((size_t)T * pl.nsplit * NH * f);
-  pl.off_cl = take((size_t)T * pl.nsplit * NH * f);
-  pl.off_co = take((size_t)T * pl.nsplit * NH * R * f);
-  pl.off_olat = take((size_t)T * NH * R * f);
-  pl.off_ov = take((size_t)T * NH * d.v_head_dim * f);
-  pl.off_part5 = take((size_t)pl.s5 * T * H * f);
+  pl.off_ssq = take((size_t)pl.s2 * T * f);
+  pl.off_qcat = take((size_t)T * NH * KVR * sizeof(uint16_t));
+  pl.off_pm = take((size_t)T * pl.nsplit * NH * f);
+  pl.off_pl = take((size_t)T * pl.nsplit * NH * f);
+  pl.off_po = take((size_t)T * pl.nsplit * NH * R * f);
+  pl.off_ov = take((size_t)T * NH * DV * f);
+  pl.off_part6 = take((size_t)pl.s6 * T * H * f);
   pl.total = off;
   return pl;
 }
@@ -157,13 +173,48 @@ int validate_dims(const mla_gd_dims& d) {
   if (!isfinite(d.softmax_scale) || !isfinite(d.norm_eps) || d.norm_eps < 0.f) return MLA_GD_E_INVAL;
   const long long KVR = (long long)d.kv_lora_rank + d.qk_rope_head_dim;
   const long long N2 = (long long)d.n_heads * (d.qk_nope_head_dim + d.qk_rope_head_dim);
-  if (d.hidden % 8 || d.q_lora_rank % 8 || KVR % 8 || N2 % 8 || d.kv_lora_rank % 16) return MLA_GD_E_UNSUPPORTED;
-  if (d.kv_lora_rank > 512 || d.qk_rope_head_dim > 128) return MLA_GD_E_UNSUPPORTED;
+  if (d.hidden % 8 || d.q_lora_rank % 8 || KVR % 8 || N2 % 8 || d.qk_nope_head_dim % 8) return MLA_GD_E_UNSUPPORTED;
+  const int r = d.kv_lora_rank;
+  if (r != 64 && r != 128 && r != 256 && r != 512) return MLA_GD_E_UNSUPPORTED;
+  if (d.qk_rope_head_dim > 64 || d.qk_nope_head_dim > 512 || d.v_head_dim > 4096) return MLA_GD_E_UNSUPPORTED;
   if (d.max_tokens > 4096) return MLA_GD_E_UNSUPPORTED;
   // flat cache rows and element offsets must fit the kernels' index arithmetic
   if ((long long)d.n_blocks * d.block_size > (1LL << 31) - 1) return MLA_GD_E_UNSUPPORTED;
   if ((long long)d.max_tokens * d.n_prior > (1LL << 31) - 1) return MLA_GD_E_UNSUPPORTED;
   return MLA_GD_OK;
+}
+
+typedef void (*core_kernel_t)(StepParams);
+
+template <int HG, int NW>
+core_kernel_t pick_core_nt(int nt) {
+  switch (nt) {
+    case 4: return k_core<4, HG, NW>;
+    case 8: return k_core<8, HG, NW>;
+    case 16: return k_core<16, HG, NW>;
+    default: return k_core<32, HG, NW>;
+  }
+}
+
+core_kernel_t pick_core(const Plan& pl, int R) {
+  return pl.core_hg == 1 ? pick_core_nt<1, 4>(R / 16) : pick_core_nt<8, 8>(R / 16);
+}
+
+const char* const kKernelNames[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"};
+constexpr int kNumKernels = 7;
+constexpr size_t kGemvLdsBytes = kGemvLdsFloats * sizeof(float);
+
+hipError_t set_lds_limits(const mla_gd_dims& d) {
+  hipError_t e = hipSuccess;
+  const void* gemv[] = {(const void*)k_down, (const void*)k_qup, (const void*)k_absorb, (const void*)k_oabsorb,
+                        (const void*)k_oproj, (const void*)k_out};
+  for (const void* k : gemv)
+    if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
+  Plan pl = make_plan(d, 1);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)pick_core(pl, d.kv_lora_rank), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)core_lds(d));
+  return e;
 }
 
 }  // namespace
@@ -195,6 +246,7 @@ int mla_gather_decode_create(const mla_gd_dims* dims, int device, mla_gd_handle*
   h->d = *dims;
   h->device = device;
   h->last_hip_error = 0;
+  h->lds_ready = false;
   *out_handle = h;
   return MLA_GD_OK;
 }
@@ -229,9 +281,6 @@ int mla_gather_decode_workspace_init(const mla_gd_handle* handle, void* workspac
 
 namespace {
 
-const char* const kKernelNames[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj"};
-constexpr int kNumKernels = 6;
-
 int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void* workspace,
              size_t workspace_bytes, void* stream, void* const* events, int n_events) {
   if (!h || !tn || !workspace) return MLA_GD_E_INVAL;
@@ -260,8 +309,8 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   p.H = d.hidden; p.Q = d.q_lora_rank; p.R = d.kv_lora_rank; p.DN = d.qk_nope_head_dim;
   p.DR = d.qk_rope_head_dim; p.DV = d.v_head_dim; p.NH = d.n_heads; p.BS = d.block_size;
   p.MB = d.max_blocks_per_seq; p.P = d.n_prior; p.KVR = p.R + p.DR; p.QKH = p.DN + p.DR;
-  p.N2 = p.NH * p.QKH; p.NBLK = d.n_blocks;
-  p.scale_log2 = d.softmax_scale * kLog2e;
+  p.N2 = p.NH * p.QKH;
+  p.scale_log2 = d.softmax_scale * 1.4426950408889634f;
   p.eps = d.norm_eps;
   p.x = (const uint16_t*)tn->hidden_states; p.g_in = tn->input_norm_w; p.wq_a = (const uint16_t*)tn->wq_a;
   p.g_q = tn->q_norm_w; p.wq_b = (const uint16_t*)tn->wq_b; p.wkv_a = (const uint16_t*)tn->wkv_a;
@@ -271,34 +320,41 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   p.gidx = tn->gather_indices; p.out = (uint16_t*)tn->out; p.rows_out = tn->gather_rows_out;
   char* ws = (char*)workspace;
   p.rows = (int32_t*)(ws + pl.off_rows);
-  p.part1 = (float*)(ws + pl.off_part1); p.ss1 = (float*)(ws + pl.off_ss1); p.qa = (float*)(ws + pl.off_qa);
-  p.kvb = (float*)(ws + pl.off_kv); p.part2 = (float*)(ws + pl.off_part2); p.ss2 = (float*)(ws + pl.off_ss2);
-  p.q = (float*)(ws + pl.off_q); p.qlat = (float*)(ws + pl.off_qlat); p.qpe = (float*)(ws + pl.off_qpe);
-  p.cm = (float*)(ws + pl.off_cm); p.cl = (float*)(ws + pl.off_cl); p.co = (float*)(ws + pl.off_co);
-  p.olat = (float*)(ws + pl.off_olat); p.ov = (float*)(ws + pl.off_ov); p.part5 = (float*)(ws + pl.off_part5);
-  p.cnt = (unsigned*)(ws + pl.off_cnt);
+  p.part1 = (float*)(ws + pl.off_part1); p.ssx = (float*)(ws + pl.off_ssx);
+  p.part2 = (float*)(ws + pl.off_part2); p.ssq = (float*)(ws + pl.off_ssq);
+  p.qcat = (uint16_t*)(ws + pl.off_qcat);
+  p.pm = (float*)(ws + pl.off_pm); p.pden = (float*)(ws + pl.off_pl); p.po = (float*)(ws + pl.off_po);
+  p.ov = (float*)(ws + pl.off_ov); p.part6 = (float*)(ws + pl.off_part6);
   p.pl = pl;
 
   hipError_t e = hipSetDevice(h->device);
+  if (e == hipSuccess && !h->lds_ready) {
+    e = set_lds_limits(d);
+    h->lds_ready = (e == hipSuccess);
+  }
   if (e != hipSuccess) { h->last_hip_error = (int)e; return MLA_GD_E_HIP; }
   hipStream_t s = (hipStream_t)stream;
   const int T = n_tokens;
   auto mark = [&](int i) {
     if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], s);
   };
+  const size_t gl = kGemvLdsBytes;
   mark(0);
-  hipLaunchKernelGGL(k_down, dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL(k_down, dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), dim3(kBlock), gl, s, p);
   mark(1);
-  hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T), dim3(kBlock), gl, s, p);
   mark(2);
-  hipLaunchKernelGGL(k_absorb, dim3(p.NH * pl.nt_r), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL(k_absorb, dim3(p.NH * pl.ncc3), dim3(kBlock), gl, s, p);
   mark(3);
-  hipLaunchKernelGGL(k_core, dim3(T * pl.nhg * pl.nsplit), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL(pick_core(pl, p.R), dim3(T * pl.nsplit * pl.core_nhb), dim3(64 * pl.core_nw), core_lds(d), s,
+                     p);
   mark(4);
-  hipLaunchKernelGGL(k_oabsorb, dim3(pl.n_oabs_wg), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), dim3(kBlock), gl, s, p);
   mark(5);
-  hipLaunchKernelGGL(k_oproj, dim3(pl.nt5 * pl.s5), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL(k_oproj, dim3(pl.nt6 * pl.s6), dim3(kBlock), gl, s, p);
   mark(6);
+  hipLaunchKernelGGL(k_out, dim3(pl.n7), dim3(kBlock), gl, s, p);
+  mark(7);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) { h->last_hip_error = (int)e; return MLA_GD_E_HIP; }
   return MLA_GD_OK;

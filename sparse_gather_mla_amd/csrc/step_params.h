@@ -9,30 +9,30 @@ namespace mla {
 // Work decomposition of one step.  Computed on the host from the dimensions
 // and n_tokens; every kernel reads the same copy.
 struct Plan {
-  int T;             // tokens in this step
-  // down-projection [wq_a | wkv_a]: 512-column tiles x K-slabs over hidden
+  int T;  // tokens in this step
+  // k_down: index build + [wq_a | wkv_a] split-K GEMV (512-column tiles x slabs of hidden)
   int nt_q, nt_kv, nt1, s1, ks1, n_idx_wg;
-  // up-projection wq_b: tiles x slabs over q_lora_rank
+  // k_qup: wq_b split-K GEMV (tiles x slabs of q_lora_rank) + one kv-branch workgroup per token
   int nt2, s2, ks2;
-  // q absorption: heads x 512-column tiles over kv_lora_rank
-  int nt_r;
-  // attention core: head groups of 16 x splits of n_prior
-  int nhg, nsplit, ps;
-  // output absorption: rows (h, d) of out_absorb_w, 4 per workgroup
-  int n_oabs_wg;
-  // o-projection: tiles over hidden x slabs over n_heads*v_head_dim
-  int nt5, s5, ks5;
+  // k_absorb: heads x 64-column chunks of kv_lora_rank
+  int ncc3;
+  // k_core: (token, split, head block); hg head groups of 16 per workgroup, nw waves
+  int core_hg, core_nw, core_nhb, nsplit, ps;
+  // k_oabsorb: heads x chunks of dc5 rows of v_head_dim x token chunks of tc5
+  int dc5, nd5, tc5, nt5c;
+  // k_oproj: 512-column tiles over hidden x slabs of n_heads*v_head_dim
+  int nt6, s6, ks6;
+  // k_out: 64-column groups x token chunks
+  int n7;
   // workspace layout (byte offsets)
-  size_t off_rows, off_part1, off_ss1, off_qa, off_kv, off_part2, off_ss2, off_q;
-  size_t off_qlat, off_qpe, off_cm, off_cl, off_co, off_olat, off_ov, off_part5, off_cnt;
-  size_t n_cnt, total;
-  // counter bases (in counters)
-  int cnt1, cnt2, cnt3, cnt5;
+  size_t off_rows, off_part1, off_ssx, off_part2, off_ssq, off_qcat;
+  size_t off_pm, off_pl, off_po, off_ov, off_part6;
+  size_t total;
 };
 
 struct StepParams {
   // dimensions
-  int H, Q, R, DN, DR, DV, NH, BS, MB, P, KVR, QKH, N2, NBLK;
+  int H, Q, R, DN, DR, DV, NH, BS, MB, P, KVR, QKH, N2;
   float scale_log2;  // softmax_scale * log2(e): scores live in the log2 domain
   float eps;
   // inputs (device pointers)
@@ -56,9 +56,17 @@ struct StepParams {
   uint16_t* out;
   int32_t* rows_out;  // optional
   // workspace views
-  int32_t* rows;
-  float *part1, *ss1, *qa, *kvb, *part2, *ss2, *q, *qlat, *qpe, *cm, *cl, *co, *olat, *ov, *part5;
-  unsigned* cnt;
+  int32_t* rows;    // [T][P] flat cache row or -1
+  float* part1;     // [s1][T][Q+KVR] split-K partials of (x*gamma) @ [wq_a | wkv_a]
+  float* ssx;       // [s1][T] partial sums of x^2
+  float* part2;     // [s2][T][N2] split-K partials of (acc_q*gamma_q) @ wq_b
+  float* ssq;       // [s2][T] partial sums of acc_q^2
+  uint16_t* qcat;   // [T][NH][KVR] bf16: per head [q_lat | roped q_pe]
+  float* pm;        // [T][nsplit][NH] running max (log2 domain) per split
+  float* pden;      // [T][nsplit][NH] softmax denominators per split
+  float* po;        // [T][nsplit][NH][R] unnormalised latent outputs per split
+  float* ov;        // [T][NH*DV] output-absorbed values
+  float* part6;     // [s6][T][H] split-K partials of the o-projection
   Plan pl;
 };
 

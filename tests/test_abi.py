@@ -75,6 +75,9 @@ def _create(lib, d):
     ({"kv_lora_rank": 1024}, "MLA_GD_E_UNSUPPORTED"),
     ({"kv_lora_rank": 72}, "MLA_GD_E_UNSUPPORTED"),
     ({"qk_rope_head_dim": 256}, "MLA_GD_E_UNSUPPORTED"),
+    ({"qk_rope_head_dim": 72, "kv_lora_rank": 64}, "MLA_GD_E_UNSUPPORTED"),
+    ({"kv_lora_rank": 96}, "MLA_GD_E_UNSUPPORTED"),
+    ({"max_tokens": 5000}, "MLA_GD_E_UNSUPPORTED"),
 ])
 def test_create_validates_dims(lib, kw, code):
     rc, h = _create(lib, _dims(**kw))
@@ -95,6 +98,7 @@ def test_workspace_size_and_step_argument_checks(lib):
         assert lib.mla_gather_decode_workspace_size(h, 5) == 0
         sizes = [lib.mla_gather_decode_workspace_size(h, t) for t in (1, 2, 3, 4)]
         assert all(s > 0 and s % 256 == 0 for s in sizes)
+        assert sizes == sorted(sizes)  # a workspace for n tokens serves every smaller step
         assert lib.mla_gather_decode_workspace_size(None, 1) == 0
         tn = sgm._Tensors()
         # missing tensors / workspace / handle: rejected before any device work
