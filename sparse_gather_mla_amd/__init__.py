@@ -17,7 +17,8 @@ from dataclasses import dataclass
 from typing import Dict, Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmla_gather_decode.so")
+# MLA_GD_LIBRARY selects another build of the same library (same ABI).
+LIB_PATH = os.environ.get("MLA_GD_LIBRARY") or os.path.join(_PKG, "libmla_gather_decode.so")
 
 MLA_GD_FLAG_FUSED = 1
 

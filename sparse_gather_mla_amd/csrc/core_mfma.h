@@ -1,16 +1,24 @@
 // Gather-attention core on the matrix cores (gfx950, wave64).
 //
-// For one token, every head attends over the rows its selected positions
-// resolve to.  Scores and the latent output are two dense contractions over
-// the gathered rows, shared by all heads (MLA keeps one latent KV head):
-//   S^T[row, head] = sum_k K[row, k] * Qcat[head, k]        (k over kv_row = latent | rope)
-//   O[head, c]    += sum_row P[head, row] * K[row, c]         (c over the latent width)
-// Both run as 16x16 MFMA tiles: a wave owns 16 heads ("head group") and takes
-// 16 gathered rows per step.  The score tile's output layout (lane l holds rows
-// 4*(l/16)+i of head l%16) is exactly the A-operand layout of the 16x16x16
-// product, so the probabilities never leave registers; the value operand is
-// read from the LDS copy of the rows with the transposing LDS read, which hands
-// lane l four consecutive rows of column l%16.
+// For one token, every head attends over the cache rows its selected
+// positions resolve to.  Scores and the latent output are two dense
+// contractions over the gathered rows, shared by all heads (MLA keeps one
+// latent KV head):
+//   S^T[row, head] = sum_k K[row, k] * Qcat[head, k]    (k over kv_row = latent | rope)
+//   O[head, c]    += sum_row P[head, row] * K[row, c]     (c over the latent width)
+// A wave owns 16 heads ("head group") and a slice of the latent columns.  Each
+// step takes a chunk of 32 gathered rows: two 16x16x32 bf16 score tiles (rows
+// 0-15 and 16-31), an online-softmax update, and one 16x16x32 bf16 PV product
+// per 16 output columns.  The score tiles' output layout (lane l holds rows
+// 4*(l/16)+i and 16+4*(l/16)+i of head l%16) is used directly as the PV
+// A operand; the value operand takes the same rows with two transposing LDS
+// reads (each hands lane l four consecutive rows of one column), so the
+// contraction index matches on both sides.
+//
+// Rows reach LDS through a ring of three 32-row buffers filled by direct
+// global-to-LDS loads two chunks ahead (no staging registers); the chunk's
+// flat row ids are read from LDS, staged once per workgroup.  Inside a buffer, row r keeps its 16-byte
+// pieces XOR-swizzled by (r mod sw) to spread LDS banks.
 #pragma once
 
 #include "device_util.h"
@@ -20,221 +28,277 @@ namespace mla {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
-__device__ __forceinline__ i16x4_t pack4_bf16(float a, float b, float c, float d) {
-  i16x4_t r;
-  r[0] = (short)f32_to_bf16(a);
-  r[1] = (short)f32_to_bf16(b);
-  r[2] = (short)f32_to_bf16(c);
-  r[3] = (short)f32_to_bf16(d);
-  return r;
+constexpr int kCoreChunk = 32;  // gathered rows per step
+constexpr int kCoreRing = 3;    // chunk buffers in flight
+
+// s_waitcnt (gfx9 encoding) until at most N vector-memory operations of this
+// wave are outstanding; the other counters are left unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-// LDS bytes of the core for a given row pitch (bf16 elements) and row streams.
-__host__ __device__ constexpr int core_lds_bytes(int rp, int rs) { return rs * 16 * rp * 2 + rs * 16 * 4; }
+constexpr int kMaxSplitRows = 4096;  // row ids staged in LDS per core workgroup
 
-// NT: latent width / 16.  HG: head groups (of 16) per workgroup.  NW: waves.
-// Row streams RS = NW / HG; stream s walks 16-row chunks s, s+RS, ... of the
-// split, and each stream writes its own partial result (m, l, o).
-template <int NT, int HG, int NW>
-__device__ void core_phase(const StepParams& p, int b, char* lds_raw) {
-  constexpr int RS = NW / HG;
+// Direct global->LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16*l (lds_base is wave-uniform).  Issued from asm so that the
+// compiler does not tie later LDS reads of other ring buffers to it; the ring
+// waits on vmcnt explicitly instead.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+}
+
+// Bytes of one ring buffer for a latent width of 16*NT (kv_row <= 16*NT + 64).
+__host__ __device__ constexpr int core_buf_bytes(int nt) { return kCoreChunk * (2 * nt + 8) * 16; }
+
+__device__ __forceinline__ short bf16s(float f) { return (short)f32_to_bf16(f); }
+
+// NT: latent width / 16.  HG: head groups of 16 per workgroup.  CS: column
+// splits.  The CS waves of a head group each own NT/CS output tiles; they
+// split the score's k-steps between them and add their partial score tiles
+// through LDS (`sx`), so every wave of the group holds the same scores and
+// the same softmax state.  The workgroup has HG*CS waves.
+template <int NT, int HG, int CS>
+__device__ __attribute__((always_inline)) void core_phase(const StepParams& p, int b, char* ring, int* ids,
+                                                          char* sink, f32x4_t* sx) {
+  constexpr int NW = HG * CS;
+  constexpr int NTW = NT / CS;       // output tiles (16 columns) per wave
   constexpr int KSMAX = NT / 2 + 2;  // 32-wide k-steps over kv_row = 16*NT + DR, DR <= 64
-  constexpr int LS = 64 * HG;        // lanes loading one stream's chunk
-  constexpr int PSTRIDE = LS / 16;   // 16-byte pieces of a row taken per lane step
-  constexpr int PFMAX = (2 * NT + 8 + PSTRIDE - 1) / PSTRIDE;  // pieces per lane (kv_row/8 <= 2*NT+8)
+  constexpr int KSW = (KSMAX + CS - 1) / CS;  // score k-steps per wave
+  constexpr int NPMAX = 2 * NT + 8;  // 16-byte pieces per row, upper bound (a multiple of 4)
+  constexpr int NI = (kCoreChunk * NPMAX + 64 * NW - 1) / (64 * NW);  // loads per wave per chunk
   const Plan& pl = p.pl;
   const int KVR = p.KVR;
-  const int ks = (KVR + 31) >> 5;
-  const int RP = ks * 32 + 8;  // padded LDS row pitch in bf16
-  const int npieces = KVR >> 3;
+  const int ks = (KVR + 31) >> 5;          // score k-steps (32 columns = 4 pieces each)
+  const int npieces = KVR >> 3;            // 16-byte pieces of a cache row
+  const int npad = ks * 4;                 // 16-byte slots per row in LDS (<= NPMAX)
+  const int sw = (npad % 8 == 0) ? 8 : 4;  // swizzle period (npad is a multiple of 4)
+  const int slots = kCoreChunk * npad;     // 16-byte slots per chunk
 
-  const int per_t = pl.nsplit * pl.core_nhb;
-  const int t = b / per_t;
-  const int rem = b % per_t;
-  const int hb = rem / pl.nsplit, split = rem % pl.nsplit;
+  // Workgroups of the same (token, split) but different head blocks sit 8
+  // block indices apart, so they land on the same XCD and share the gathered
+  // rows through its L2.
+  const int nhb = pl.core_nhb;
+  const int pair = (b / (8 * nhb)) * 8 + (b % 8);
+  const int hb = (b / 8) % nhb;
+  if (pair >= pl.T * pl.nsplit) return;  // padding workgroup (whole group exits before any barrier)
+  const int t = pair / pl.nsplit, split = pair % pl.nsplit;
   const int j0 = split * pl.ps, j1 = min(p.P, j0 + pl.ps);
-  const int nchunks = (j1 - j0 + 15) >> 4;
-  const int iters = (nchunks + RS - 1) / RS;
+  const int nrows = j1 - j0;
+  const int nchunks = (nrows + kCoreChunk - 1) / kCoreChunk;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hg = wave % HG, rs = wave / HG;
+  const int hg = wave / CS, cs = wave % CS;
   const int g = lane >> 4, l16 = lane & 15;
-  const int head = (hb * HG + hg) * 16 + l16;  // this lane's head for Q / softmax state
+  const int hbase = (hb * HG + hg) * 16;
+  const int head = hbase + l16;  // this lane's head for Q fragments and softmax state
 
-  bf16_t* buf = reinterpret_cast<bf16_t*>(lds_raw) + rs * 16 * RP;
-  int* valid = reinterpret_cast<int*>(lds_raw + RS * 16 * RP * 2) + rs * 16;
+  // this split's flat row ids (-1: causally masked, or past the split)
+  for (int i = tid; i < nchunks * kCoreChunk; i += NW * 64)
+    ids[i] = (i < nrows) ? p.rows[(size_t)t * p.P + j0 + i] : -1;
 
-  // zero the padded columns once (never overwritten by row data)
-  for (int i = tid; i < RS * 16 * (RP - KVR); i += NW * 64) {
-    const int row = i / (RP - KVR), c = KVR + i % (RP - KVR);
-    reinterpret_cast<bf16_t*>(lds_raw)[row * RP + c] = 0;
-  }
-
-  // Q fragments (B operand of the score product): lane l holds Qcat[head][32*kk + 8*g .. +8]
-  bf16x8_t qf[KSMAX];
+  // this wave's k-steps: kk = kb + j, j < KSW; steps at or past ks carry zero
+  // Q fragments and read a valid slot (step ks-1), so they add exactly zero
+  const int kb = cs * KSW;
+  // Q fragments: lane l holds Qcat[head][32*kk + 8*g .. +8] (B operand of the score product)
+  bf16x8_t qf[KSW];
 #pragma unroll
-  for (int kk = 0; kk < KSMAX; ++kk) {
-    const int k = 32 * kk + 8 * g;
+  for (int j = 0; j < KSW; ++j) {
+    const int k = 32 * (kb + j) + 8 * g;
     u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (kk < ks && head < p.NH && k < KVR)
+    if (kb + j < ks && head < p.NH && k < KVR)
       v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * p.NH + head) * KVR + k);
-    qf[kk] = __builtin_bit_cast(bf16x8_t, v);
+    qf[j] = __builtin_bit_cast(bf16x8_t, v);
   }
+  __syncthreads();  // row ids visible
 
-  f32x4_t o[NT];
+  // direct global->LDS load of chunk c into ring buffer c % kCoreRing.  Every
+  // wave issues exactly NI loads per chunk (those past the chunk read the zero
+  // row into the sink) so that the vmcnt arithmetic below is static.
+  // Per-lane geometry of those loads, the same for every chunk: the row inside
+  // the chunk (-1: nothing to load) and the byte offset of the piece in a row.
+  int lrow[NI], lofs[NI];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // chunk loader: this lane's stream-local index, row within the chunk and first piece
-  const int sl = hg * 64 + lane;  // 0 .. LS-1
-  const int lrow = sl & 15, lp0 = sl >> 4;
-  u32x4_t pf[PFMAX];
-  int prow = -1;
-  auto prefetch = [&](int it) {
-    const int chunk = it * RS + rs;
-    const int j = j0 + 16 * chunk + lrow;
-    prow = (chunk < nchunks && j < j1) ? p.rows[(size_t)t * p.P + j] : -1;
+  for (int i = 0; i < NI; ++i) {
+    const int s = (i * NW + wave) * 64 + lane;
+    lrow[i] = -1;
+    lofs[i] = 0;
+    if (s < slots) {
+      const int r = s / npad, pc = (s % npad) ^ (r % sw);
+      if (pc < npieces) {
+        lrow[i] = r;
+        lofs[i] = pc * 16;
+      }
+    }
+  }
+  const size_t row_bytes = (size_t)KVR * 2;
+  auto issue_chunk = [&](int c) {
+    char* buf = ring + (c % kCoreRing) * core_buf_bytes(NT);
+    const int* cid = ids + min(c, nchunks - 1) * kCoreChunk;
 #pragma unroll
-    for (int u = 0; u < PFMAX; ++u) {
-      const int pc = lp0 + u * PSTRIDE;
-      pf[u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (prow >= 0 && pc < npieces)
-        pf[u] = *reinterpret_cast<const u32x4_t*>(p.cache + (size_t)prow * KVR + 8 * pc);
+    for (int i = 0; i < NI; ++i) {
+      const int s0 = (i * NW + wave) * 64;  // first slot of this load
+      const char* src = reinterpret_cast<const char*>(p.zero16);
+      if (c < nchunks && lrow[i] >= 0) {
+        const int rid = cid[lrow[i]];
+        if (rid >= 0) src = reinterpret_cast<const char*>(p.cache) + (size_t)(unsigned)rid * row_bytes + lofs[i];
+      }
+      dma16(src, (s0 < slots) ? buf + s0 * 16 : sink);
     }
   };
 
-  if (iters > 0) prefetch(0);
-  for (int it = 0; it < iters; ++it) {
-    const int chunk = it * RS + rs;
-    __syncthreads();  // the previous chunk is fully consumed
+  f32x4_t o[NTW];
 #pragma unroll
-    for (int u = 0; u < PFMAX; ++u) {
-      const int pc = lp0 + u * PSTRIDE;
-      if (pc < npieces) *reinterpret_cast<u32x4_t*>(buf + lrow * RP + 8 * pc) = pf[u];
-    }
-    if (lp0 == 0) valid[lrow] = prow >= 0;
-    __syncthreads();
-    if (it + 1 < iters) prefetch(it + 1);
-    if (chunk >= nchunks) continue;  // wave-uniform: this stream has no chunk this round
+  for (int n = 0; n < NTW; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
 
-    // scores S^T[row 4g+i][head l16]
-    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  wait_vmcnt<0>();  // Q fragments and row ids are in registers / LDS; only ring loads follow
 #pragma unroll
-    for (int kk = 0; kk < KSMAX; ++kk) {
-      if (kk < ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(buf + l16 * RP + 32 * kk + 8 * g);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc, 0, 0, 0);
+  for (int c = 0; c < kCoreRing - 1; ++c) issue_chunk(c);
+
+  for (int c = 0; c < nchunks; ++c) {
+    // chunk c's loads are this wave's oldest; the younger chunk may stay in flight
+    wait_vmcnt<NI * (kCoreRing - 2)>();
+    __syncthreads();  // chunk c visible to every wave; buffer (c-1) % ring consumed
+    issue_chunk(c + kCoreRing - 1);
+    const char* buf = ring + (c % kCoreRing) * core_buf_bytes(NT);
+    const int* cid = ids + c * kCoreChunk;
+    // scores: tile A rows 0-15, tile B rows 16-31; lane l reads row l16 (+16), piece 4*kk + g
+    f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      // this wave's k-steps, fragments loaded two steps ahead of the MFMAs
+      const int ra = l16, rb = 16 + l16;
+      const int xa = ra % sw, xb = rb % sw;
+      const char* rowa = buf + ra * npad * 16;
+      const char* rowb = buf + rb * npad * 16;
+      auto frag = [&](const char* row, int x, int j) {
+        const int pc = 4 * min(kb + j, ks - 1) + g;
+        return *reinterpret_cast<const bf16x8_t*>(row + (pc ^ x) * 16);
+      };
+      bf16x8_t fa0 = frag(rowa, xa, 0), fb0 = frag(rowb, xb, 0);
+      bf16x8_t fa1 = fa0, fb1 = fb0;
+      if (KSW > 1) {
+        fa1 = frag(rowa, xa, 1);
+        fb1 = frag(rowb, xb, 1);
+      }
+#pragma unroll
+      for (int j = 0; j < KSW; ++j) {
+        bf16x8_t fa2 = fa1, fb2 = fb1;
+        if (j + 2 < KSW) {
+          fa2 = frag(rowa, xa, j + 2);
+          fb2 = frag(rowb, xb, j + 2);
+        }
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, qf[j], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb0, qf[j], sb, 0, 0, 0);
+        fa0 = fa1; fb0 = fb1;
+        fa1 = fa2; fb1 = fb2;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    float s[4];
-    float mx = -INFINITY;
+    if constexpr (CS > 1) {
+      // add the group's partial score tiles, in wave order (identical in every wave)
+      f32x4_t* mine = sx + ((hg * CS + cs) * 2) * 64;
+      mine[lane] = sa;
+      mine[64 + lane] = sb;
+      __syncthreads();
+      const f32x4_t* grp = sx + (hg * CS * 2) * 64;
+      sa = grp[lane];
+      sb = grp[64 + lane];
+#pragma unroll
+      for (int w = 1; w < CS; ++w) {
+        sa += grp[w * 128 + lane];
+        sb += grp[w * 128 + 64 + lane];
+      }
+    }
+    float s[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s[i] = valid[4 * g + i] ? sacc[i] * p.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[i]);
+      s[i] = (cid[4 * g + i] >= 0) ? sa[i] * p.scale_log2 : -INFINITY;
+      s[4 + i] = (cid[16 + 4 * g + i] >= 0) ? sb[i] * p.scale_log2 : -INFINITY;
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, s[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    float alpha = 1.f, pr[4] = {0.f, 0.f, 0.f, 0.f};
-    if (m_new != -INFINITY) {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = exp2f(s[i] - m_new);  // -inf -> 0
+    // Lazy rescaling: the reference maximum m_run (log2 domain) moves only when
+    // a chunk's maximum exceeds it by more than 8, so probabilities stay below
+    // 2^8 and most chunks leave the accumulators alone.  The result is exact:
+    // (m, l, o) are kept consistent with whatever reference is in use.
+    float alpha = 1.f;
+    if (mx > m_run + 8.f) {  // also the first valid chunk (m_run = -inf)
+      alpha = exp2f(m_run - mx);  // m_run = -inf gives 0
+      m_run = mx;
     }
-    float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    float pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = (m_run == -INFINITY) ? 0.f : exp2f(s[i] - m_run);  // masked: 0
+    float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
     ps += __shfl_xor(ps, 16, kWave);
     ps += __shfl_xor(ps, 32, kWave);
     l_run = l_run * alpha + ps;
-    m_run = m_new;
-    // rescale the accumulators: lane l holds heads 4g+i of each output tile
-    float ai[4];
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // wave-uniform
+      // rescale: lane l holds heads 4g+i of each output tile
+      float ai[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i, kWave);
+      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i, kWave);
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+      for (int n = 0; n < NTW; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[n][i] *= ai[i];
-    // O[head][c] += P[head][rows] * V[rows][c]
-    const i16x4_t pa = pack4_bf16(pr[0], pr[1], pr[2], pr[3]);
-    const bf16_t* vbase = buf + (4 * g + (l16 >> 2)) * RP + 4 * (l16 & 3);
+        for (int i = 0; i < 4; ++i) o[n][i] *= ai[i];
+    }
+    // PV: A slots 0-3 = rows 4g+i, slots 4-7 = rows 16+4g+i; B takes the same rows
+    bf16x8_t pab;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vbase + 16 * n));
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[n], 0, 0, 0);
+    for (int i = 0; i < 8; ++i) pab[i] = (__bf16)pr[i];
+    const int r1 = 4 * g + (l16 >> 2), r2 = 16 + r1;
+    const int x1 = r1 % sw, x2 = r2 % sw;
+    const char* row1 = buf + r1 * npad * 16;
+    const char* row2 = buf + r2 * npad * 16;
+    const int cofs = 4 * (l16 & 3);  // column offset inside the 16-column tile
+    auto vfrag = [&](int n) {
+      const int col = 16 * (cs * NTW + n) + cofs;
+      const int pc = col >> 3, within = (col & 7) * 2;
+      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(row1 + (pc ^ x1) * 16 + within));
+      const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(row2 + (pc ^ x2) * 16 + within));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t vf = vfrag(0);
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) {
+      bf16x8_t vn = vf;
+      if (n + 1 < NTW) vn = vfrag(n + 1);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pab, vf, o[n], 0, 0, 0);
+      vf = vn;
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  wait_vmcnt<0>();  // the trailing loads (zero rows into unused buffers or the sink)
 
+  // this split's partial result; waves of one head group hold identical (m, l)
   const size_t pb = ((size_t)t * pl.nsplit + split) * p.NH;
-  const int hbase = (hb * HG + hg) * 16;
-  if constexpr (RS == 1) {
-    // one stream: its (m, l, o) is this split's partial result
-    if (g == 0 && head < p.NH) {
-      p.pm[pb + head] = m_run;
-      p.pden[pb + head] = l_run;
-    }
+  if (cs == 0 && g == 0 && head < p.NH) {
+    p.pm[pb + head] = m_run;
+    p.pden[pb + head] = l_run;
+  }
+  constexpr int R = 16 * NT;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = hbase + 4 * g + i;
-        if (h < p.NH) p.po[(pb + h) * (16 * NT) + 16 * n + l16] = o[n][i];
-      }
-  } else {
-    // HG == 1: merge the RS streams (same 16 heads) in LDS, in stream order
-    float* ml = reinterpret_cast<float*>(lds_raw);      // [RS][16] m, then [RS][16] l
-    float* acc = ml + 2 * RS * 16;                      // [16][16*NT]
-    __syncthreads();                                    // row buffers are free now
-    if (g == 0) {
-      ml[rs * 16 + l16] = m_run;
-      ml[RS * 16 + rs * 16 + l16] = l_run;
-    }
-    __syncthreads();
-    // this lane's heads 4g+i: merged max and the stream's weight
-    float wi[4];
+  for (int n = 0; n < NTW; ++n)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hh = 4 * g + i;
-      float M = -INFINITY;
-#pragma unroll
-      for (int s2 = 0; s2 < RS; ++s2) M = fmaxf(M, ml[s2 * 16 + hh]);
-      wi[i] = (M == -INFINITY) ? 0.f : exp2f(ml[rs * 16 + hh] - M);
+      const int h = hbase + 4 * g + i;
+      if (h < p.NH) p.po[(pb + h) * R + 16 * (cs * NTW + n) + l16] = o[n][i];
     }
-    for (int s2 = 0; s2 < RS; ++s2) {
-      if (rs == s2) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float* a = acc + (4 * g + i) * (16 * NT) + 16 * n + l16;
-            const float v = o[n][i] * wi[i];
-            *a = (s2 == 0) ? v : *a + v;
-          }
-      }
-      __syncthreads();
-    }
-    if (rs == 0) {
-      if (g == 0 && head < p.NH) {
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < RS; ++s2) M = fmaxf(M, ml[s2 * 16 + l16]);
-        float L = 0.f;
-        if (M != -INFINITY)
-          for (int s2 = 0; s2 < RS; ++s2) L += ml[RS * 16 + s2 * 16 + l16] * exp2f(ml[s2 * 16 + l16] - M);
-        p.pm[pb + head] = M;
-        p.pden[pb + head] = L;
-      }
-      for (int idx = lane; idx < 16 * 16 * NT; idx += 64) {
-        const int h = hbase + idx / (16 * NT);
-        if (h < p.NH) p.po[(pb + h) * (16 * NT) + idx % (16 * NT)] = acc[idx];
-      }
-    }
-  }
 }
 
 }  // namespace mla

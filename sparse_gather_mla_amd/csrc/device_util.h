@@ -16,14 +16,8 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// Round to nearest even; NaN stays a quiet NaN.  Adding 0x7fff plus the kept
-// part's lowest bit to the fp32 bits and truncating rounds half to even.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// Round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ void unpack8(const uint4 v, float* w) {
   w[0] = bf16lo(v.x); w[1] = bf16hi(v.x);

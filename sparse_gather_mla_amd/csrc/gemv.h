@@ -11,7 +11,7 @@ constexpr int kUnroll = 8;  // 16-byte weight loads in flight per lane
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Streaming 16-byte weight load that does not allocate in the caches on the way.
+// Streaming 16-byte weight load (non-temporal: the weight is read once).
 __device__ __forceinline__ u32x4 ld_stream(const bf16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -23,10 +23,10 @@ __device__ __forceinline__ void unpack8v(const u32x4 v, float* w) {
   w[6] = bf16lo(v[3]); w[7] = bf16hi(v[3]);
 }
 
-// dst[i] = sum_{s < S} src[s*sstride + (i / w)*tstride + (i % w)] for i < n.
-// Deterministic: part sp of nsp sums s = sp, sp+nsp, ... in order, then the parts
-// are added in order.  dst and scratch are LDS; scratch holds 256 floats.
-// Every thread of the workgroup must call it.
+// dst[i] = sum_{s < S} src[s*sstride + (i / w)*tstride + (i % w)] for i < n (floats).
+// Deterministic: part sp of nsp sums s = sp, sp+nsp, ... in order, then the
+// parts are added in order.  dst and scratch (256 floats) are LDS.  Every
+// thread of the workgroup must call it.
 __device__ __forceinline__ void reduce_parts(const float* __restrict__ src, size_t sstride, int S, int n, int w,
                                              size_t tstride, float* dst, float* scratch) {
   const int tid = threadIdx.x;
@@ -36,63 +36,136 @@ __device__ __forceinline__ void reduce_parts(const float* __restrict__ src, size
   for (int idx = tid; idx < n * nsp; idx += kBlock) {
     const int i = idx % n, sp = idx / n;
     const float* s0 = src + (size_t)(i / w) * tstride + (i % w);
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    float a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = 0.f;
     int s = sp;
-    for (; s + 3 * nsp < S; s += 4 * nsp) {
-      a0 += s0[(size_t)s * sstride];
-      a1 += s0[(size_t)(s + nsp) * sstride];
-      a2 += s0[(size_t)(s + 2 * nsp) * sstride];
-      a3 += s0[(size_t)(s + 3 * nsp) * sstride];
-    }
-    for (; s < S; s += nsp) a0 += s0[(size_t)s * sstride];
-    out[sp * n + i] = (a0 + a1) + (a2 + a3);
+    for (; s + 7 * nsp < S; s += 8 * nsp)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] += s0[(size_t)(s + u * nsp) * sstride];
+    for (; s < S; s += nsp) a[0] += s0[(size_t)s * sstride];
+    out[sp * n + i] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   }
   __syncthreads();
   if (nsp > 1) {
     for (int i = tid; i < n; i += kBlock) {
-      float a = 0.f;
-      for (int sp = 0; sp < nsp; ++sp) a += scratch[sp * n + i];
-      dst[i] = a;
+      float acc = 0.f;
+      for (int sp = 0; sp < nsp; ++sp) acc += scratch[sp * n + i];
+      dst[i] = acc;
     }
     __syncthreads();
   }
 }
 
-// One GEMV tile for up to kTT tokens:
-//   out[tt*ldo + c0 + c] = sum_{r < ks} xs[tt*xstride + r] * W[(k0 + r)*N + c0 + c],  c < nc <= 512.
-// W is [K, N] row-major bf16 (N and nc multiples of 8), xs is LDS.  Lanes of a
-// wave cover one row with lpr lanes (8 columns each) and 64/lpr rows at once;
-// the four waves take interleaved rows; kUnroll loads per lane are in flight.
-// Partial sums are combined across lanes by shuffles and across waves in LDS
-// (`red`: 3*kTT*512 floats).
-__device__ __forceinline__ void gemv_tile(const bf16_t* __restrict__ W, int N, int k0, int ks, int c0, int nc,
-                                          const float* xs, int xstride, int nt, float* __restrict__ out,
-                                          size_t ldo, float* red) {
+// As reduce_parts for groups of 4 floats: items are float4 at element offset
+// (i / w4)*tstride + 4*(i % w4); tstride and the source must be 16-byte
+// aligned.  scratch holds 256 float4.
+__device__ __forceinline__ void reduce_parts4(const float* __restrict__ src, size_t sstride, int S, int n4, int w4,
+                                              size_t tstride, float* dst, float* scratch) {
+  const int tid = threadIdx.x;
+  int nsp = (n4 > 0) ? kBlock / n4 : 1;
+  nsp = max(1, min(nsp, 16));
+  float4* out = reinterpret_cast<float4*>((nsp == 1) ? dst : scratch);
+  for (int idx = tid; idx < n4 * nsp; idx += kBlock) {
+    const int i = idx % n4, sp = idx / n4;
+    const float* s0 = src + (size_t)(i / w4) * tstride + 4 * (i % w4);
+    float4 a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = sp;
+    for (; s + 3 * nsp < S; s += 4 * nsp) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 v = *reinterpret_cast<const float4*>(s0 + (size_t)(s + u * nsp) * sstride);
+        a[u].x += v.x; a[u].y += v.y; a[u].z += v.z; a[u].w += v.w;
+      }
+    }
+    for (; s < S; s += nsp) {
+      const float4 v = *reinterpret_cast<const float4*>(s0 + (size_t)s * sstride);
+      a[0].x += v.x; a[0].y += v.y; a[0].z += v.z; a[0].w += v.w;
+    }
+    out[sp * n4 + i] = make_float4((a[0].x + a[1].x) + (a[2].x + a[3].x), (a[0].y + a[1].y) + (a[2].y + a[3].y),
+                                   (a[0].z + a[1].z) + (a[2].z + a[3].z), (a[0].w + a[1].w) + (a[2].w + a[3].w));
+  }
+  __syncthreads();
+  if (nsp > 1) {
+    const float4* sc = reinterpret_cast<const float4*>(scratch);
+    float4* d = reinterpret_cast<float4*>(dst);
+    for (int i = tid; i < n4; i += kBlock) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int sp = 0; sp < nsp; ++sp) {
+        const float4 v = sc[sp * n4 + i];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      d[i] = acc;
+    }
+    __syncthreads();
+  }
+}
+
+// Lane geometry of one GEMV tile: a row of nc columns is covered by lpr lanes
+// (8 columns each), a wave covers 64/lpr rows at once, the four waves take
+// interleaved rows.
+struct GemvGeom {
+  int lpr, rpi, cg, rsub, rstep, r0;
+  bool active;
+};
+__device__ __forceinline__ GemvGeom gemv_geom(int nc) {
+  GemvGeom g;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ngroups = nc >> 3;
-  int lpr = 64;
-  while (lpr > 8 && (lpr >> 1) >= ngroups) lpr >>= 1;
-  const int rpi = 64 / lpr;
-  const int cg = lane % lpr, rsub = lane / lpr;
-  const bool active = cg < ngroups;
-  const int rstep = 4 * rpi;
+  g.lpr = 64;
+  while (g.lpr > 8 && (g.lpr >> 1) >= ngroups) g.lpr >>= 1;
+  g.rpi = 64 / g.lpr;
+  g.cg = lane % g.lpr;
+  g.rsub = lane / g.lpr;
+  g.active = g.cg < ngroups;
+  g.rstep = 4 * g.rpi;
+  g.r0 = wv * g.rpi + g.rsub;
+  return g;
+}
+
+// The first kUnroll weight loads of a tile, issued before the activations are ready.
+__device__ __forceinline__ void gemv_first(const bf16_t* __restrict__ W, int N, int k0, int ks, int c0, int nc,
+                                           u32x4* v) {
+  const GemvGeom g = gemv_geom(nc);
+  const bf16_t* wp = W + (size_t)k0 * N + c0 + 8 * g.cg;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int r = g.r0 + u * g.rstep;
+    if (g.active && r < ks) v[u] = ld_stream(wp + (size_t)r * N);
+    else v[u] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// One GEMV tile for up to kTT tokens:
+//   out[tt*ldo + c0 + c] = sum_{r < ks} xs[tt*xstride + r] * W[(k0 + r)*N + c0 + c],  c < nc <= 512.
+// W is [K, N] row-major bf16 (N and nc multiples of 8), xs is LDS.  `v` holds
+// the loads of gemv_first.  Lanes of equal column combine by shuffles, waves
+// through LDS (`red`: 3*kTT*512 floats).
+__device__ __forceinline__ void gemv_tile(const bf16_t* __restrict__ W, int N, int k0, int ks, int c0, int nc,
+                                          const float* xs, int xstride, int nt, float* __restrict__ out,
+                                          size_t ldo, float* red, u32x4* v) {
+  const GemvGeom g = gemv_geom(nc);
+  const int wv = threadIdx.x >> 6;
   float acc[kTT][8];
 #pragma unroll
   for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[tt][i] = 0.f;
-  const bf16_t* wp = W + (size_t)k0 * N + c0 + 8 * cg;
-  for (int r0 = wv * rpi + rsub; r0 < ks; r0 += rstep * kUnroll) {
-    u32x4 v[kUnroll];
+  const bf16_t* wp = W + (size_t)k0 * N + c0 + 8 * g.cg;
+  for (int r0 = g.r0; r0 < ks; r0 += g.rstep * kUnroll) {
+    if (r0 != g.r0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int r = r0 + u * rstep;
-      if (active && r < ks) v[u] = ld_stream(wp + (size_t)r * N);
-      else v[u] = u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < kUnroll; ++u) {
+        const int r = r0 + u * g.rstep;
+        if (g.active && r < ks) v[u] = ld_stream(wp + (size_t)r * N);
+        else v[u] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int r = min(r0 + u * rstep, ks - 1);  // out-of-range rows carry zero weights
+      const int r = min(r0 + u * g.rstep, ks - 1);  // rows past the slab carry zero weights
       float w[8];
       unpack8v(v[u], w);
 #pragma unroll
@@ -105,30 +178,30 @@ __device__ __forceinline__ void gemv_tile(const bf16_t* __restrict__ W, int N, i
       }
     }
   }
-  for (int off = lpr; off < 64; off <<= 1)
+  for (int off = g.lpr; off < 64; off <<= 1)
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt)
       if (tt < nt)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[tt][i] += __shfl_xor(acc[tt][i], off, kWave);
-  if (wv > 0 && rsub == 0 && active) {
+  if (wv > 0 && g.rsub == 0 && g.active) {
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt)
       if (tt < nt)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) red[((wv - 1) * kTT + tt) * kTile + 8 * cg + i] = acc[tt][i];
+        for (int i = 0; i < 8; ++i) red[((wv - 1) * kTT + tt) * kTile + 8 * g.cg + i] = acc[tt][i];
   }
   __syncthreads();
-  if (wv == 0 && rsub == 0 && active) {
+  if (wv == 0 && g.rsub == 0 && g.active) {
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
       if (tt < nt) {
         float o[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          o[i] = acc[tt][i] + red[(0 * kTT + tt) * kTile + 8 * cg + i] + red[(1 * kTT + tt) * kTile + 8 * cg + i] +
-                 red[(2 * kTT + tt) * kTile + 8 * cg + i];
-        float4* dst = reinterpret_cast<float4*>(out + (size_t)tt * ldo + c0 + 8 * cg);
+          o[i] = acc[tt][i] + red[(0 * kTT + tt) * kTile + 8 * g.cg + i] + red[(1 * kTT + tt) * kTile + 8 * g.cg + i] +
+                 red[(2 * kTT + tt) * kTile + 8 * g.cg + i];
+        float4* dst = reinterpret_cast<float4*>(out + (size_t)tt * ldo + c0 + 8 * g.cg);
         dst[0] = make_float4(o[0], o[1], o[2], o[3]);
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);
       }

@@ -34,10 +34,13 @@ __global__ __launch_bounds__(kBlock) void k_absorb(StepParams p) {
   phase_absorb(p, blockIdx.x, lds);
 }
 
-template <int NT, int HG, int NW>
-__global__ __launch_bounds__(NW * 64) void k_core(StepParams p) {
-  extern __shared__ float lds[];
-  core_phase<NT, HG, NW>(p, blockIdx.x, reinterpret_cast<char*>(lds));
+template <int NT, int HG, int CS>
+__global__ __launch_bounds__(HG * CS * 64) void k_core(StepParams p) {
+  __shared__ __attribute__((aligned(16))) char ring[kCoreRing * core_buf_bytes(NT)];
+  __shared__ int ids[kMaxSplitRows];
+  __shared__ __attribute__((aligned(16))) char sink[1024];
+  __shared__ f32x4_t sx[HG * CS * 2 * 64];  // partial score tiles exchanged within a head group
+  core_phase<NT, HG, CS>(p, blockIdx.x, ring, ids, sink, sx);
 }
 
 __global__ __launch_bounds__(kBlock) void k_oabsorb(StepParams p) {
@@ -90,21 +93,15 @@ void choose_split(int K, int ntiles, int* s_out, int* ks_out) {
 }
 
 struct CoreShape {
-  int hg, nw;
+  int hg, cs;
 };
 
-CoreShape core_shape(int n_heads) { return n_heads <= 16 ? CoreShape{1, 4} : CoreShape{8, 8}; }
+// <= 16 heads: one head group, four waves splitting the latent columns;
+// otherwise four head groups (64 heads) per workgroup, two waves per group
+// splitting the latent columns.
+CoreShape core_shape(int n_heads) { return n_heads <= 16 ? CoreShape{1, 4} : CoreShape{4, 2}; }
 
-int core_row_pitch(int kvr) { return cdiv(kvr, 32) * 32 + 8; }
-
-size_t core_lds(const mla_gd_dims& d) {
-  const CoreShape cs = core_shape(d.n_heads);
-  const int rs = cs.nw / cs.hg;
-  const int rp = core_row_pitch(d.kv_lora_rank + d.qk_rope_head_dim);
-  size_t bytes = core_lds_bytes(rp, rs);
-  if (rs > 1) bytes = std::max(bytes, (size_t)(2 * rs * 16 + 16 * d.kv_lora_rank) * sizeof(float));
-  return bytes;
-}
+int core_grid(const Plan& pl) { return cdiv(pl.T * pl.nsplit, 8) * 8 * pl.core_nhb; }
 
 Plan make_plan(const mla_gd_dims& d, int T) {
   Plan pl;
@@ -120,15 +117,18 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.n_idx_wg = cdiv(T * P, kBlock);
   pl.nt2 = cdiv(N2, kTile);
   choose_split(Q, pl.nt2, &pl.s2, &pl.ks2);
+  pl.nkv = cdiv(KVR, 64);
   pl.ncc3 = R / 64;
   const CoreShape cs = core_shape(NH);
   pl.core_hg = cs.hg;
-  pl.core_nw = cs.nw;
+  pl.core_cs = cs.cs;
   pl.core_nhb = cdiv(NH, 16 * cs.hg);
   {
-    const int rows_per_iter = 16 * (cs.nw / cs.hg);
-    int ns = clampi(cdiv(256, T * pl.core_nhb), 1, std::min(256, cdiv(P, rows_per_iter)));
-    pl.ps = cdiv(cdiv(P, ns), rows_per_iter) * rows_per_iter;
+    // about one workgroup per CU, at most 16 splits (the combine reads every split)
+    int ns = cdiv(256, T * pl.core_nhb);
+    ns = std::min(ns, 16);
+    ns = clampi(ns, cdiv(P, kMaxSplitRows), cdiv(P, kCoreChunk));
+    pl.ps = cdiv(cdiv(P, ns), kCoreChunk) * kCoreChunk;
     pl.nsplit = cdiv(P, pl.ps);
   }
   pl.dc5 = 16;
@@ -146,11 +146,14 @@ Plan make_plan(const mla_gd_dims& d, int T) {
     return o;
   };
   const size_t f = sizeof(float);
+  pl.off_zero = take(256);
   pl.off_rows = take((size_t)T * P * sizeof(int32_t));
   pl.off_part1 = take((size_t)pl.s1 * T * (Q + KVR) * f);
   pl.off_ssx = take((size_t)pl.s1 * T * f);
   pl.off_part2 = take((size_t)pl.s2 * T * N2 * f);
   pl.off_ssq = take((size_t)pl.s2 * T * f);
+  pl.off_kvr = take((size_t)T * KVR * f);
+  pl.off_kvss = take((size_t)T * pl.nkv * f);
   pl.off_qcat = take((size_t)T * NH * KVR * sizeof(uint16_t));
   pl.off_pm = take((size_t)T * pl.nsplit * NH * f);
   pl.off_pl = take((size_t)T * pl.nsplit * NH * f);
@@ -174,6 +177,7 @@ int validate_dims(const mla_gd_dims& d) {
   const long long KVR = (long long)d.kv_lora_rank + d.qk_rope_head_dim;
   const long long N2 = (long long)d.n_heads * (d.qk_nope_head_dim + d.qk_rope_head_dim);
   if (d.hidden % 8 || d.q_lora_rank % 8 || KVR % 8 || N2 % 8 || d.qk_nope_head_dim % 8) return MLA_GD_E_UNSUPPORTED;
+  if ((d.qk_nope_head_dim + d.qk_rope_head_dim) % 4) return MLA_GD_E_UNSUPPORTED;
   const int r = d.kv_lora_rank;
   if (r != 64 && r != 128 && r != 256 && r != 512) return MLA_GD_E_UNSUPPORTED;
   if (d.qk_rope_head_dim > 64 || d.qk_nope_head_dim > 512 || d.v_head_dim > 4096) return MLA_GD_E_UNSUPPORTED;
@@ -186,18 +190,18 @@ int validate_dims(const mla_gd_dims& d) {
 
 typedef void (*core_kernel_t)(StepParams);
 
-template <int HG, int NW>
+template <int HG, int CS>
 core_kernel_t pick_core_nt(int nt) {
   switch (nt) {
-    case 4: return k_core<4, HG, NW>;
-    case 8: return k_core<8, HG, NW>;
-    case 16: return k_core<16, HG, NW>;
-    default: return k_core<32, HG, NW>;
+    case 4: return k_core<4, HG, CS>;
+    case 8: return k_core<8, HG, CS>;
+    case 16: return k_core<16, HG, CS>;
+    default: return k_core<32, HG, CS>;
   }
 }
 
 core_kernel_t pick_core(const Plan& pl, int R) {
-  return pl.core_hg == 1 ? pick_core_nt<1, 4>(R / 16) : pick_core_nt<8, 8>(R / 16);
+  return pl.core_hg == 1 ? pick_core_nt<1, 4>(R / 16) : pick_core_nt<4, 2>(R / 16);
 }
 
 const char* const kKernelNames[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"};
@@ -210,10 +214,6 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
                         (const void*)k_oproj, (const void*)k_out};
   for (const void* k : gemv)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
-  Plan pl = make_plan(d, 1);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void*)pick_core(pl, d.kv_lora_rank), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)core_lds(d));
   return e;
 }
 
@@ -319,9 +319,11 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   p.cache = (uint16_t*)tn->kv_cache; p.slot = tn->slot_mapping; p.btab = tn->block_table; p.pos = tn->positions;
   p.gidx = tn->gather_indices; p.out = (uint16_t*)tn->out; p.rows_out = tn->gather_rows_out;
   char* ws = (char*)workspace;
+  p.zero16 = (const uint16_t*)(ws + pl.off_zero);
   p.rows = (int32_t*)(ws + pl.off_rows);
   p.part1 = (float*)(ws + pl.off_part1); p.ssx = (float*)(ws + pl.off_ssx);
   p.part2 = (float*)(ws + pl.off_part2); p.ssq = (float*)(ws + pl.off_ssq);
+  p.kvr = (float*)(ws + pl.off_kvr); p.kvss = (float*)(ws + pl.off_kvss);
   p.qcat = (uint16_t*)(ws + pl.off_qcat);
   p.pm = (float*)(ws + pl.off_pm); p.pden = (float*)(ws + pl.off_pl); p.po = (float*)(ws + pl.off_po);
   p.ov = (float*)(ws + pl.off_ov); p.part6 = (float*)(ws + pl.off_part6);
@@ -342,12 +344,12 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   mark(0);
   hipLaunchKernelGGL(k_down, dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), dim3(kBlock), gl, s, p);
   mark(1);
-  hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T), dim3(kBlock), gl, s, p);
+  hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T * pl.nkv), dim3(kBlock), gl, s, p);
   mark(2);
-  hipLaunchKernelGGL(k_absorb, dim3(p.NH * pl.ncc3), dim3(kBlock), gl, s, p);
+  hipLaunchKernelGGL(k_absorb, dim3(p.NH * pl.ncc3 + T), dim3(kBlock), gl, s, p);
   mark(3);
-  hipLaunchKernelGGL(pick_core(pl, p.R), dim3(T * pl.nsplit * pl.core_nhb), dim3(64 * pl.core_nw), core_lds(d), s,
-                     p);
+  hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), dim3(64 * pl.core_hg * pl.core_cs),
+                     0, s, p);
   mark(4);
   hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), dim3(kBlock), gl, s, p);
   mark(5);

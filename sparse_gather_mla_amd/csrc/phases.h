@@ -8,7 +8,8 @@
 //
 // Split-K partial sums are plain stores; the consuming phase reduces them in
 // a fixed order (no atomics, no arrival counters), so a step is bitwise
-// reproducible for a given n_tokens.
+// reproducible for a given n_tokens.  Each GEMV workgroup issues its first
+// weight loads before it reduces its activations, so the two latencies overlap.
 //
 // Every RMSNorm's 1/rms is a per-token scalar, so it is factored out of the
 // GEMV that follows the norm and applied where the reduced sums are consumed:
@@ -24,12 +25,13 @@
 
 namespace mla {
 
-// LDS of the GEMV phases (floats): xs [kTT][512], red [3][kTT][512], scratch [256], aux [1024]
+// LDS of the GEMV phases (floats): xs [kTT][512], red [3][kTT][512], scratch [1024], aux [1024]
 constexpr int kLdsXs = 0;
 constexpr int kLdsRed = kTT * kTile;
 constexpr int kLdsScratch = kLdsRed + 3 * kTT * kTile;
-constexpr int kLdsAux = kLdsScratch + 256;
+constexpr int kLdsAux = kLdsScratch + 1024;
 constexpr int kGemvLdsFloats = kLdsAux + 1024;
+constexpr int kKvSlice = 64;  // kv-row columns reduced per kv-branch workgroup
 
 __device__ __forceinline__ float inv_rms(float sumsq, int n, float eps) {
   return 1.f / sqrtf(sumsq / (float)n + eps);
@@ -69,6 +71,8 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
   float* red = lds + kLdsRed;
   for (int t0 = 0; t0 < T; t0 += kTT) {
     const int nt = min(kTT, T - t0);
+    u32x4 v[kUnroll];
+    gemv_first(W, N, k0, ks, c0, nc, v);
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) {
       const int tt = idx / ks, r = idx % ks;
       xs[tt * kTile + r] = bf16_to_f32(p.x[(size_t)(t0 + tt) * p.H + k0 + r]) * p.g_in[k0 + r];
@@ -79,8 +83,8 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
       float s = 0.f;
       if (tt < nt)
         for (int r = rp; r < ks; r += 32) {
-          const float v = bf16_to_f32(p.x[(size_t)(t0 + tt) * p.H + k0 + r]);
-          s = fmaf(v, v, s);
+          const float xv = bf16_to_f32(p.x[(size_t)(t0 + tt) * p.H + k0 + r]);
+          s = fmaf(xv, xv, s);
         }
 #pragma unroll
       for (int off = 16; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
@@ -88,14 +92,14 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
     }
     __syncthreads();
     float* part = p.part1 + ((size_t)slab * T + t0) * N1 + (is_q ? 0 : p.Q);
-    gemv_tile(W, N, k0, ks, c0, nc, xs, kTile, nt, part, N1, red);
+    gemv_tile(W, N, k0, ks, c0, nc, xs, kTile, nt, part, N1, red, v);
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_qup: (acc_a * g_q) @ wq_b split-K partials and sums of acc_a^2; one extra
-// workgroup per token runs the kv branch (kv-latent RMSNorm, RoPE of the
-// rotary part, bf16 cache-row write at slot_mapping[t]).
+// k_qup: (acc_a * g_q) @ wq_b split-K partials and sums of acc_a^2.  Extra
+// workgroups (token t, 64-column slice) reduce the kv row: kvr = alpha * acc_kv
+// and partial sums of squares of its latent columns.
 // ---------------------------------------------------------------------------
 __device__ void phase_qup(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
@@ -106,28 +110,21 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
   float* red = lds + kLdsRed;
   float* scratch = lds + kLdsScratch;
   if (b >= n_gemv) {
-    const int t = b - n_gemv;
-    float* kv = xs;  // [KVR]
-    float* sc = kv + p.KVR;
-    reduce_parts(p.part1 + (size_t)t * N1 + p.Q, (size_t)T * N1, pl.s1, p.KVR, p.KVR, 0, kv, scratch);
-    reduce_parts(p.ssx + t, T, pl.s1, 1, 1, 0, sc, scratch);
-    const float alpha = inv_rms(sc[0], p.H, p.eps);
+    const int t = (b - n_gemv) / pl.nkv, sl = (b - n_gemv) % pl.nkv;
+    const int c0 = sl * kKvSlice, nc = min(kKvSlice, p.KVR - c0);
+    float* kv = xs;  // [64]
+    float* sx = xs + kKvSlice;
+    reduce_parts4(p.part1 + (size_t)t * N1 + p.Q + c0, (size_t)T * N1, pl.s1, nc / 4, nc / 4, 0, kv, scratch);
+    reduce_parts(p.ssx + t, T, pl.s1, 1, 1, 0, sx, scratch);
+    const float alpha = inv_rms(sx[0], p.H, p.eps);
     float ss = 0.f;
-    for (int c = threadIdx.x; c < p.R; c += kBlock) {
-      const float v = alpha * kv[c];
-      ss = fmaf(v, v, ss);
+    for (int c = threadIdx.x; c < nc; c += kBlock) {
+      const float y = alpha * kv[c];
+      p.kvr[(size_t)t * p.KVR + c0 + c] = y;
+      if (c0 + c < p.R) ss = fmaf(y, y, ss);
     }
     ss = block_sum(ss, scratch);
-    const float inv = inv_rms(ss, p.R, p.eps);
-    bf16_t* row = p.cache + (size_t)p.slot[t] * p.KVR;
-    for (int c = threadIdx.x; c < p.R; c += kBlock) row[c] = f32_to_bf16(alpha * kv[c] * inv * p.g_kv[c]);
-    const int half = p.DR / 2;
-    for (int i = threadIdx.x; i < half; i += kBlock) {
-      const float x0 = alpha * kv[p.R + 2 * i], x1 = alpha * kv[p.R + 2 * i + 1];
-      const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
-      row[p.R + 2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
-      row[p.R + 2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
-    }
+    if (threadIdx.x == 0) p.kvss[(size_t)t * pl.nkv + sl] = ss;
     return;
   }
   const int slab = b / pl.nt2, tile = b % pl.nt2;
@@ -135,8 +132,10 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
   const int k0 = slab * pl.ks2, ks = min(pl.ks2, p.Q - k0);
   for (int t0 = 0; t0 < T; t0 += kTT) {
     const int nt = min(kTT, T - t0);
+    u32x4 v[kUnroll];
+    gemv_first(p.wq_b, p.N2, k0, ks, c0, nc, v);
     // acc_a[t][k0 .. k0+ks) reduced over the down-projection's slabs
-    reduce_parts(p.part1 + (size_t)t0 * N1 + k0, (size_t)T * N1, pl.s1, nt * ks, ks, N1, xs, scratch);
+    reduce_parts4(p.part1 + (size_t)t0 * N1 + k0, (size_t)T * N1, pl.s1, nt * ks / 4, ks / 4, N1, xs, scratch);
     if (tile == 0) {
       const int tt = threadIdx.x >> 5, rp = threadIdx.x & 31;
       float s = 0.f;
@@ -149,50 +148,72 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) xs[idx] *= p.g_q[k0 + idx % ks];
     __syncthreads();
-    gemv_tile(p.wq_b, p.N2, k0, ks, c0, nc, xs, ks, nt, p.part2 + ((size_t)slab * T + t0) * p.N2, p.N2, red);
+    gemv_tile(p.wq_b, p.N2, k0, ks, c0, nc, xs, ks, nt, p.part2 + ((size_t)slab * T + t0) * p.N2, p.N2, red, v);
   }
 }
 
-// per-token scalars: alpha = 1/rms(x), beta = alpha * inv_q (scale of the wq_b output)
-__device__ __forceinline__ void token_scales(const StepParams& p, int t0, int nt, float* alpha, float* beta,
-                                             float* tmp, float* scratch) {
+// per-token scalars: beta = alpha * inv_q (the scale of the wq_b output)
+__device__ __forceinline__ void token_betas(const StepParams& p, int t0, int nt, float* beta, float* tmp,
+                                            float* scratch) {
   const Plan& pl = p.pl;
   reduce_parts(p.ssx + t0, pl.T, pl.s1, nt, nt, 0, tmp, scratch);
-  reduce_parts(p.ssq + t0, pl.T, pl.s2, nt, nt, 0, tmp + nt, scratch);
+  reduce_parts(p.ssq + t0, pl.T, pl.s2, nt, nt, 0, tmp + kTT, scratch);
   for (int tt = threadIdx.x; tt < nt; tt += kBlock) {
     const float a = inv_rms(tmp[tt], p.H, p.eps);
-    const float iq = 1.f / sqrtf(a * a * tmp[nt + tt] / (float)p.Q + p.eps);
-    alpha[tt] = a;
+    const float iq = 1.f / sqrtf(a * a * tmp[kTT + tt] / (float)p.Q + p.eps);
     beta[tt] = a * iq;
   }
   __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// k_absorb: q = beta * sum of wq_b partials; q_lat[t,h,:] = q_nope[t,h,:] @ q_absorb_w[h]
-// for a 64-column chunk; the chunk-0 workgroup also ropes q_pe.  Output: bf16
-// Qcat[t][h] = [q_lat | q_pe], laid out like a cache row.
+// k_absorb: q = beta * (sum of wq_b partials); q_lat[t,h,:] = q_nope[t,h,:] @
+// q_absorb_w[h] for a 64-column chunk; the chunk-0 workgroup also ropes q_pe.
+// Output: bf16 Qcat[t][h] = [q_lat | q_pe], laid out like a cache row.  Extra
+// workgroups (one per token) finish the kv branch: kv-latent RMSNorm,
+// interleaved RoPE of the rotary part, bf16 write of the row at slot_mapping[t].
 // ---------------------------------------------------------------------------
 __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
   const int T = pl.T;
-  const int h = b / pl.ncc3, cc = b % pl.ncc3;
-  const int c0 = cc * 64;
-  float* xs = lds + kLdsXs;  // [kTT][DN], later [kTT][DR]
+  float* xs = lds + kLdsXs;
   float* red = lds + kLdsRed;
   float* scratch = lds + kLdsScratch;
-  float* alpha = lds + kLdsAux;
-  float* beta = alpha + kTT;
-  float* tmp = beta + kTT;         // [2*kTT]
+  const int n_abs = p.NH * pl.ncc3;
+  if (b >= n_abs) {
+    const int t = b - n_abs;
+    const float* kv = p.kvr + (size_t)t * p.KVR;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < pl.nkv; i += kBlock) ss += p.kvss[(size_t)t * pl.nkv + i];
+    ss = block_sum(ss, scratch);
+    const float inv = inv_rms(ss, p.R, p.eps);
+    bf16_t* row = p.cache + (size_t)p.slot[t] * p.KVR;
+    for (int c = threadIdx.x; c < p.R; c += kBlock) row[c] = f32_to_bf16(kv[c] * inv * p.g_kv[c]);
+    const int half = p.DR / 2;
+    for (int i = threadIdx.x; i < half; i += kBlock) {
+      const float x0 = kv[p.R + 2 * i], x1 = kv[p.R + 2 * i + 1];
+      const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
+      row[p.R + 2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
+      row[p.R + 2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
+    }
+    return;
+  }
+  const int h = b / pl.ncc3, cc = b % pl.ncc3;
+  const int c0 = cc * 64;
+  float* beta = lds + kLdsAux;
+  float* tmp = beta + kTT;          // [2*kTT]
   float* qo = lds + kLdsAux + 512;  // [kTT][64]
+  const bf16_t* W = p.w_qabs + (size_t)h * p.DN * p.R;
   for (int t0 = 0; t0 < T; t0 += kTT) {
     const int nt = min(kTT, T - t0);
-    token_scales(p, t0, nt, alpha, beta, tmp, scratch);
-    reduce_parts(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH, (size_t)T * p.N2, pl.s2, nt * p.DN, p.DN,
-                 p.N2, xs, scratch);
+    u32x4 v[kUnroll];
+    gemv_first(W, p.R, 0, p.DN, c0, 64, v);
+    token_betas(p, t0, nt, beta, tmp, scratch);
+    reduce_parts4(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH, (size_t)T * p.N2, pl.s2, nt * p.DN / 4,
+                  p.DN / 4, p.N2, xs, scratch);
     for (int idx = threadIdx.x; idx < nt * p.DN; idx += kBlock) xs[idx] *= beta[idx / p.DN];
     __syncthreads();
-    gemv_tile(p.w_qabs + (size_t)h * p.DN * p.R, p.R, 0, p.DN, c0, 64, xs, p.DN, nt, qo - c0, 64, red);
+    gemv_tile(W, p.R, 0, p.DN, c0, 64, xs, p.DN, nt, qo - c0, 64, red, v);
     for (int idx = threadIdx.x; idx < nt * 64; idx += kBlock) {
       const int tt = idx / 64, c = idx % 64;
       p.qcat[((size_t)(t0 + tt) * p.NH + h) * p.KVR + c0 + c] = f32_to_bf16(qo[tt * 64 + c]);
@@ -218,6 +239,7 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
 // k_oabsorb: combine the core's split partials of head h into o_lat (softmax
 // normalisation; a token with no valid entry gets zeros), then
 // o_v[t, h*DV + d] = out_absorb_w[h, d, :] . o_lat[t, h, :] for dc5 rows d.
+// The weight rows are loaded first; the combine runs in parallel over splits.
 // ---------------------------------------------------------------------------
 __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
@@ -227,61 +249,91 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
   const int dch = rem / pl.nt5c, tch = rem % pl.nt5c;
   const int t0 = tch * pl.tc5, nt = min(pl.tc5, T - t0);
   const int d0 = dch * pl.dc5, nd = min(pl.dc5, p.DV - d0);
-  float* wsp = lds;                // [tc5][NSP] weights exp2(m_s - M)
-  float* linv = wsp + pl.tc5 * NSP;  // [tc5] 1/L (0 when nothing valid)
-  float* ol = linv + pl.tc5;       // [tc5][R]
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // weight rows d0 + wv + 4j, 8 columns per lane (R <= 512)
+  constexpr int kRowsPerWave = 4;  // dc5 = 16 rows over 4 waves
+  u32x4 wr[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int dd = wv + 4 * j, c = 8 * lane;
+    wr[j] = u32x4{0u, 0u, 0u, 0u};
+    if (dd < nd && c < R) wr[j] = ld_stream(p.w_oabs + ((size_t)h * p.DV + d0 + dd) * R + c);
+  }
+  float* pmL = lds;                  // [tc5][NSP]: maxima, then split weights
+  float* plL = pmL + pl.tc5 * NSP;   // [tc5][NSP]
+  float* linv = plL + pl.tc5 * NSP;  // [tc5]
+  float* ol = lds + kLdsRed;         // [tc5][R] (<= 4096 floats)
+  float* scratch = lds + kLdsRed + 4096;  // 256 float4
+  for (int idx = tid; idx < nt * NSP; idx += kBlock) {
+    const int tt = idx / NSP, s = idx % NSP;
+    const size_t q = ((size_t)(t0 + tt) * NSP + s) * p.NH + h;
+    pmL[idx] = p.pm[q];
+    plL[idx] = p.pden[q];
+  }
+  __syncthreads();
   if (tid < nt) {
-    const int t = t0 + tid;
     float M = -INFINITY;
-    for (int s = 0; s < NSP; ++s) M = fmaxf(M, p.pm[((size_t)t * NSP + s) * p.NH + h]);
+    for (int s = 0; s < NSP; ++s) M = fmaxf(M, pmL[tid * NSP + s]);
     float L = 0.f;
     for (int s = 0; s < NSP; ++s) {
-      const size_t q = ((size_t)t * NSP + s) * p.NH + h;
-      const float w = (M == -INFINITY) ? 0.f : exp2f(p.pm[q] - M);
-      wsp[tid * NSP + s] = w;
-      L = fmaf(p.pden[q], w, L);
+      const float w = (M == -INFINITY) ? 0.f : exp2f(pmL[tid * NSP + s] - M);
+      pmL[tid * NSP + s] = w;
+      L = fmaf(plL[tid * NSP + s], w, L);
     }
     linv[tid] = (L > 0.f) ? 1.f / L : 0.f;
   }
   __syncthreads();
-  for (int idx = tid; idx < nt * (R / 4); idx += kBlock) {
-    const int tt = idx / (R / 4), c4 = idx % (R / 4);
-    const int t = t0 + tt;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < NSP; ++s) {
-      const float w = wsp[tt * NSP + s];
-      const float4 v = *reinterpret_cast<const float4*>(p.po + (((size_t)t * NSP + s) * p.NH + h) * R + 4 * c4);
-      a.x = fmaf(w, v.x, a.x);
-      a.y = fmaf(w, v.y, a.y);
-      a.z = fmaf(w, v.z, a.z);
-      a.w = fmaf(w, v.w, a.w);
-    }
-    const float li = linv[tt];
-    float* d = ol + tt * R + 4 * c4;
-    d[0] = a.x * li; d[1] = a.y * li; d[2] = a.z * li; d[3] = a.w * li;
-  }
-  __syncthreads();
-  const int lane = tid & 63, wv = tid >> 6;
-  for (int dd = wv; dd < nd; dd += 4) {
-    const int d = d0 + dd;
-    const bf16_t* wrow = p.w_oabs + ((size_t)h * p.DV + d) * R;
-    float w[8];
-    for (int cbase = 0; cbase < R; cbase += 512) {
-      const int c = cbase + 8 * lane;
-      if (c < R) unpack8v(*reinterpret_cast<const u32x4*>(wrow + c), w);
-      for (int tt = 0; tt < nt; ++tt) {
-        float a = 0.f;
-        if (c < R) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) a = fmaf(w[i], ol[tt * R + c + i], a);
-        }
-        a = wave_sum(a);
-        if (lane == 0) {
-          float* dst = p.ov + (size_t)(t0 + tt) * p.NH * p.DV + (size_t)h * p.DV + d;
-          *dst = (cbase == 0) ? a : *dst + a;
-        }
+  // o_lat[tt][c] = linv * sum_s w_s * po[t][s][h][c]; float4 items, splits in parallel parts
+  {
+    const int n4 = nt * (R / 4);
+    const int nsp = max(1, min(16, kBlock / n4));
+    float4* out = reinterpret_cast<float4*>(nsp == 1 ? ol : scratch);
+    for (int idx = tid; idx < n4 * nsp; idx += kBlock) {
+      const int i = idx % n4, sp = idx / n4;
+      const int tt = i / (R / 4), c4 = i % (R / 4);
+      const float* src = p.po + ((size_t)(t0 + tt) * NSP * p.NH + h) * R + 4 * c4;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = sp; s < NSP; s += nsp) {
+        const float w = pmL[tt * NSP + s];
+        const float4 x = *reinterpret_cast<const float4*>(src + (size_t)s * p.NH * R);
+        a.x = fmaf(w, x.x, a.x);
+        a.y = fmaf(w, x.y, a.y);
+        a.z = fmaf(w, x.z, a.z);
+        a.w = fmaf(w, x.w, a.w);
       }
+      out[sp * n4 + i] = a;
+    }
+    __syncthreads();
+    if (nsp > 1) {
+      const float4* sc = reinterpret_cast<const float4*>(scratch);
+      for (int i = tid; i < n4; i += kBlock) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp = 0; sp < nsp; ++sp) {
+          const float4 x = sc[sp * n4 + i];
+          a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+        }
+        reinterpret_cast<float4*>(ol)[i] = a;
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < nt * R; i += kBlock) ol[i] *= linv[i / R];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int dd = wv + 4 * j;
+    if (dd >= nd) continue;  // wave-uniform
+    const int c = 8 * lane;
+    float w[8];
+    unpack8v(wr[j], w);
+    for (int tt = 0; tt < nt; ++tt) {
+      float a = 0.f;
+      if (c < R) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaf(w[i], ol[tt * R + c + i], a);
+      }
+      a = wave_sum(a);
+      if (lane == 0) p.ov[(size_t)(t0 + tt) * p.NH * p.DV + (size_t)h * p.DV + d0 + dd] = a;
     }
   }
 }
@@ -300,12 +352,14 @@ __device__ void phase_oproj(const StepParams& p, int b, float* lds) {
   float* red = lds + kLdsRed;
   for (int t0 = 0; t0 < T; t0 += kTT) {
     const int nt = min(kTT, T - t0);
+    u32x4 v[kUnroll];
+    gemv_first(p.w_o, p.H, k0, ks, c0, nc, v);
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) {
       const int tt = idx / ks, r = idx % ks;
       xs[tt * kTile + r] = p.ov[(size_t)(t0 + tt) * K + k0 + r];
     }
     __syncthreads();
-    gemv_tile(p.w_o, p.H, k0, ks, c0, nc, xs, kTile, nt, p.part6 + ((size_t)slab * T + t0) * p.H, p.H, red);
+    gemv_tile(p.w_o, p.H, k0, ks, c0, nc, xs, kTile, nt, p.part6 + ((size_t)slab * T + t0) * p.H, p.H, red, v);
   }
 }
 
@@ -319,7 +373,7 @@ __device__ void phase_out(const StepParams& p, int b, float* lds) {
   const int nc = min(64, p.H - c0);
   float* sum = lds;
   float* scratch = lds + 64;
-  reduce_parts(p.part6 + (size_t)t * p.H + c0, (size_t)pl.T * p.H, pl.s6, nc, nc, 0, sum, scratch);
+  reduce_parts4(p.part6 + (size_t)t * p.H + c0, (size_t)pl.T * p.H, pl.s6, nc / 4, nc / 4, 0, sum, scratch);
   for (int c = threadIdx.x; c < nc; c += kBlock) p.out[(size_t)t * p.H + c0 + c] = f32_to_bf16(sum[c]);
 }
 

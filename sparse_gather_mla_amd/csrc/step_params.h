@@ -12,12 +12,12 @@ struct Plan {
   int T;  // tokens in this step
   // k_down: index build + [wq_a | wkv_a] split-K GEMV (512-column tiles x slabs of hidden)
   int nt_q, nt_kv, nt1, s1, ks1, n_idx_wg;
-  // k_qup: wq_b split-K GEMV (tiles x slabs of q_lora_rank) + one kv-branch workgroup per token
-  int nt2, s2, ks2;
-  // k_absorb: heads x 64-column chunks of kv_lora_rank
+  // k_qup: wq_b split-K GEMV (tiles x slabs of q_lora_rank) + kv-row reduction (token x 64-column slice)
+  int nt2, s2, ks2, nkv;
+  // k_absorb: heads x 64-column chunks of kv_lora_rank, + one kv-finalise workgroup per token
   int ncc3;
-  // k_core: (token, split, head block); hg head groups of 16 per workgroup, nw waves
-  int core_hg, core_nw, core_nhb, nsplit, ps;
+  // k_core: (token, split, head block); hg head groups of 16 x cs column splits per workgroup
+  int core_hg, core_cs, core_nhb, nsplit, ps;
   // k_oabsorb: heads x chunks of dc5 rows of v_head_dim x token chunks of tc5
   int dc5, nd5, tc5, nt5c;
   // k_oproj: 512-column tiles over hidden x slabs of n_heads*v_head_dim
@@ -25,7 +25,7 @@ struct Plan {
   // k_out: 64-column groups x token chunks
   int n7;
   // workspace layout (byte offsets)
-  size_t off_rows, off_part1, off_ssx, off_part2, off_ssq, off_qcat;
+  size_t off_zero, off_rows, off_part1, off_ssx, off_part2, off_ssq, off_kvr, off_kvss, off_qcat;
   size_t off_pm, off_pl, off_po, off_ov, off_part6;
   size_t total;
 };
@@ -56,11 +56,14 @@ struct StepParams {
   uint16_t* out;
   int32_t* rows_out;  // optional
   // workspace views
+  const uint16_t* zero16;  // 256 zero bytes (source of padding loads)
   int32_t* rows;    // [T][P] flat cache row or -1
   float* part1;     // [s1][T][Q+KVR] split-K partials of (x*gamma) @ [wq_a | wkv_a]
   float* ssx;       // [s1][T] partial sums of x^2
   float* part2;     // [s2][T][N2] split-K partials of (acc_q*gamma_q) @ wq_b
   float* ssq;       // [s2][T] partial sums of acc_q^2
+  float* kvr;       // [T][KVR] alpha * (x * g_in) @ wkv_a: the kv row before its own norm
+  float* kvss;      // [T][nkv] partial sums of squares of the kv row's latent part
   uint16_t* qcat;   // [T][NH][KVR] bf16: per head [q_lat | roped q_pe]
   float* pm;        // [T][nsplit][NH] running max (log2 domain) per split
   float* pden;      // [T][nsplit][NH] softmax denominators per split
