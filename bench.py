@@ -145,7 +145,7 @@ def main() -> int:
     inp = make_inputs(wl, with_pool=small_pool)  # host copy of the pool only when small (CPU baseline)
     g = gpu_inputs(wl, inp, device=dev)
     mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens, device=0, fused=args.fused)
-    names = mod.kernel_names()
+    names = mod.kernel_names(sh.n_tokens)
     nk = len(names)
     out = torch.empty((sh.n_tokens, sh.hidden), dtype=torch.bfloat16, device=dev)
     flush = torch.empty((1 << 30) // 4, dtype=torch.float32, device=dev)

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MLA_GD_ABI_VERSION 1
+#define MLA_GD_ABI_VERSION 2
 
 /* error codes */
 #define MLA_GD_OK 0
@@ -125,6 +125,8 @@ typedef struct mla_gd_handle mla_gd_handle;
  * q_lora_rank, qk_nope_head_dim, kv_lora_rank + qk_rope_head_dim and
  * n_heads*(dn+dr) must be multiples of 8; kv_lora_rank one of 64, 128, 256,
  * 512; qk_rope_head_dim even and at most 64; qk_nope_head_dim at most 512;
+ * qk_nope_head_dim + qk_rope_head_dim a multiple of 4; q_lora_rank +
+ * kv_lora_rank + qk_rope_head_dim at most 16384; n_prior at most 262144;
  * max_tokens at most 4096.
  */
 int mla_gather_decode_create(const mla_gd_dims* dims, int device, mla_gd_handle** out_handle);
@@ -159,15 +161,18 @@ int mla_gather_decode_step(mla_gd_handle* handle, const mla_gd_tensors* tensors,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Per-kernel timing.  The step runs as mla_gather_decode_kernel_count() kernel
- * launches; mla_gather_decode_step_profiled() is mla_gather_decode_step() plus
+ * Per-kernel timing.  A step of n_tokens tokens runs as
+ * mla_gather_decode_kernel_count(handle, n_tokens) kernel launches (steps of
+ * more than 8 tokens run the projections on the matrix cores, with two more
+ * kernels; 0 for an invalid handle or n_tokens).
+ * mla_gather_decode_step_profiled() is mla_gather_decode_step() plus
  * hipEventRecord(events[i], stream) before kernel i and events[count] after
  * the last one.  `events` holds n_events >= count + 1 created hipEvent_t
  * handles (owned by the caller).  Kernel names are static strings ("" for an
  * index out of range).
  */
-int mla_gather_decode_kernel_count(const mla_gd_handle* handle);
-const char* mla_gather_decode_kernel_name(const mla_gd_handle* handle, int index);
+int mla_gather_decode_kernel_count(const mla_gd_handle* handle, int32_t n_tokens);
+const char* mla_gather_decode_kernel_name(const mla_gd_handle* handle, int32_t n_tokens, int index);
 int mla_gather_decode_step_profiled(mla_gd_handle* handle, const mla_gd_tensors* tensors, int32_t n_tokens,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     void* const* events, int n_events);

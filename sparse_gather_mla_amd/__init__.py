@@ -76,9 +76,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                                     ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.mla_gather_decode_step_profiled.restype = ctypes.c_int
-    lib.mla_gather_decode_kernel_count.argtypes = [ctypes.c_void_p]
+    lib.mla_gather_decode_kernel_count.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     lib.mla_gather_decode_kernel_count.restype = ctypes.c_int
-    lib.mla_gather_decode_kernel_name.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.mla_gather_decode_kernel_name.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int]
     lib.mla_gather_decode_kernel_name.restype = ctypes.c_char_p
     lib.mla_gather_decode_abi_version.argtypes = []
     lib.mla_gather_decode_abi_version.restype = ctypes.c_int
@@ -188,15 +188,16 @@ class MlaGatherDecode:
     def __call__(self, inp: Dict[str, object], **kw):
         return self.step(inp, **kw)
 
-    def kernel_names(self):
-        n = self.lib.mla_gather_decode_kernel_count(self.handle)
-        return [self.lib.mla_gather_decode_kernel_name(self.handle, i).decode() for i in range(n)]
+    def kernel_names(self, n_tokens: int):
+        """Names of the kernels a step of ``n_tokens`` tokens launches, in order."""
+        n = self.lib.mla_gather_decode_kernel_count(self.handle, n_tokens)
+        return [self.lib.mla_gather_decode_kernel_name(self.handle, n_tokens, i).decode() for i in range(n)]
 
     def step(self, inp: Dict[str, object], out=None, gather_rows_out=None, workspace=None, stream=None,
              events=None):
         """Enqueue one step on ``stream`` (default: torch's current stream); returns ``out``.
 
-        ``events``: optional list of kernel_count()+1 torch.cuda.Event(enable_timing=True)
+        ``events``: optional list of len(kernel_names(T))+1 torch.cuda.Event(enable_timing=True)
         recorded around each kernel of the step on that stream."""
         import torch
 

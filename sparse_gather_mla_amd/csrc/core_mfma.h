@@ -22,46 +22,18 @@
 #pragma once
 
 #include "device_util.h"
+#include "mfma_util.h"
 #include "step_params.h"
 
 namespace mla {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void global_cvoid_t;
-
 constexpr int kCoreChunk = 32;  // gathered rows per step
 constexpr int kCoreRing = 3;    // chunk buffers in flight
 
-// s_waitcnt (gfx9 encoding) until at most N vector-memory operations of this
-// wave are outstanding; the other counters are left unconstrained.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
-}
-
 constexpr int kMaxSplitRows = 4096;  // row ids staged in LDS per core workgroup
-
-// Direct global->LDS load of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16*l (lds_base is wave-uniform).  Issued from asm so that the
-// compiler does not tie later LDS reads of other ring buffers to it; the ring
-// waits on vmcnt explicitly instead.
-__device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
-}
 
 // Bytes of one ring buffer for a latent width of 16*NT (kv_row <= 16*NT + 64).
 __host__ __device__ constexpr int core_buf_bytes(int nt) { return kCoreChunk * (2 * nt + 8) * 16; }
-
-__device__ __forceinline__ short bf16s(float f) { return (short)f32_to_bf16(f); }
 
 // NT: latent width / 16.  HG: head groups of 16 per workgroup.  CS: column
 // splits.  The CS waves of a head group each own NT/CS output tiles; they

@@ -12,6 +12,7 @@
 
 #include "../../include/mla_gather_decode.h"
 #include "phases.h"
+#include "phases_mfma.h"
 
 using namespace mla;
 
@@ -56,6 +57,51 @@ __global__ __launch_bounds__(kBlock) void k_oproj(StepParams p) {
 __global__ __launch_bounds__(kBlock) void k_out(StepParams p) {
   extern __shared__ float lds[];
   phase_out(p, blockIdx.x, lds);
+}
+
+// matrix-core path (phases_mfma.h)
+
+__global__ __launch_bounds__(kBlock) void k_prep(StepParams p) {
+  extern __shared__ float lds[];
+  phase_prep(p, blockIdx.x, lds);
+}
+
+template <int MTB>
+__global__ __launch_bounds__(kBlock) void k_down_m(StepParams p) {
+  __shared__ __attribute__((aligned(16))) char ring[Mg<MTB>::kRing];
+  __shared__ __attribute__((aligned(16))) char sink[1024];
+  phase_down_m<MTB>(p, blockIdx.x, ring, sink);
+}
+
+__global__ __launch_bounds__(kBlock) void k_qa(StepParams p) {
+  extern __shared__ float lds[];
+  phase_qa(p, blockIdx.x, lds);
+}
+
+template <int MTB>
+__global__ __launch_bounds__(kBlock) void k_qup_m(StepParams p) {
+  __shared__ __attribute__((aligned(16))) char ring[Mg<MTB>::kRing];
+  __shared__ __attribute__((aligned(16))) char sink[1024];
+  phase_qup_m<MTB>(p, blockIdx.x, ring, sink);
+}
+
+template <int MTB>
+__global__ __launch_bounds__(kBlock) void k_absorb_m(StepParams p) {
+  extern __shared__ float lds[];
+  phase_absorb_m<MTB>(p, blockIdx.x, reinterpret_cast<char*>(lds));
+}
+
+template <int MTB>
+__global__ __launch_bounds__(kBlock) void k_oabsorb_m(StepParams p) {
+  extern __shared__ float lds[];
+  phase_oabsorb_m<MTB>(p, blockIdx.x, reinterpret_cast<char*>(lds));
+}
+
+template <int MTB>
+__global__ __launch_bounds__(kBlock) void k_oproj_m(StepParams p) {
+  __shared__ __attribute__((aligned(16))) char ring[Mg<MTB>::kRing];
+  __shared__ __attribute__((aligned(16))) char sink[1024];
+  phase_oproj_m<MTB>(p, blockIdx.x, ring, sink);
 }
 
 __global__ __launch_bounds__(kBlock) void k_zero_u32(uint32_t* p, size_t n) {
@@ -103,6 +149,85 @@ CoreShape core_shape(int n_heads) { return n_heads <= 16 ? CoreShape{1, 4} : Cor
 
 int core_grid(const Plan& pl) { return cdiv(pl.T * pl.nsplit, 8) * 8 * pl.core_nhb; }
 
+constexpr int kGemvMaxTokens = kTT;  // more tokens: projections on the matrix cores
+
+// Matrix-core split-K: about `target` workgroups over `units` (tile, token
+// block) pairs, slabs of at least 8 k-steps.
+void split_m(int kt, int units, int target, int* s_out, int* ks_out) {
+  int s = cdiv(target, units);
+  s = clampi(s, 1, std::max(1, kt / 8));
+  const int ks = cdiv(kt, s);
+  *ks_out = ks;
+  *s_out = cdiv(kt, ks);
+}
+
+int mg_grid(int nunits, int ntb) { return cdiv(nunits, 8) * 8 * ntb; }
+
+size_t absorb_lds_bytes(const Plan& pl, int DN) {
+  return (size_t)kMgDepth * Mg<1>::kBBytes + 1024 + (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2 * kAFragElems * 2;
+}
+
+size_t oabsorb_lds_bytes(const Plan& pl, int R) {
+  const size_t head = align_up((size_t)(2 * pl.mtb5 * 16 * pl.nsplit + pl.mtb5 * 16) * 4, 256);
+  return head + (size_t)(R / kMgK) * pl.mtb5 * 2 * kAFragElems * 2;
+}
+
+// Plan of the matrix-core path; `pl` already holds T, the index build and the core's split.
+Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
+  const int H = d.hidden, Q = d.q_lora_rank, R = d.kv_lora_rank, DR = d.qk_rope_head_dim;
+  const int KVR = R + DR, QKH = d.qk_nope_head_dim + DR, N2 = d.n_heads * QKH, NH = d.n_heads;
+  const int P = d.n_prior, DV = d.v_head_dim, DN = d.qk_nope_head_dim;
+  const int T = pl.T;
+  pl.mfma = 1;
+  pl.mtb = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
+  pl.ntb = cdiv(T, 16 * pl.mtb);
+  pl.mt_pad = pl.ntb * pl.mtb;
+  // about one workgroup per CU with the 96 KB ring of 4 m-tiles, two otherwise
+  const int target = pl.mtb == 4 ? 256 : 512;
+  pl.kt1 = cdiv(H, kMgK);
+  pl.ntq1m = cdiv(Q, kMgCols);
+  pl.nt1m = pl.ntq1m + cdiv(KVR, kMgCols);
+  split_m(pl.kt1, pl.nt1m * pl.ntb, target, &pl.s1, &pl.ks1m);
+  pl.kt2 = cdiv(Q, kMgK);
+  pl.nt2m = cdiv(N2, kMgCols);
+  split_m(pl.kt2, pl.nt2m * pl.ntb, target, &pl.s2, &pl.ks2m);
+  pl.nct3 = R / kMgCols;
+  pl.mtb3 = pl.mtb;
+  while (pl.mtb3 > 1 && (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2048 > 96 * 1024) pl.mtb3 /= 2;
+  pl.ntb3 = cdiv(T, 16 * pl.mtb3);
+  pl.mtb5 = std::min(pl.mtb, 2);
+  pl.ntb5 = cdiv(T, 16 * pl.mtb5);
+  pl.kt6 = cdiv(NH * DV, kMgK);
+  pl.nt6m = cdiv(H, kMgCols);
+  split_m(pl.kt6, pl.nt6m * pl.ntb, target, &pl.s6, &pl.ks6m);
+  pl.n7 = T * cdiv(H, 64);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t f = sizeof(float);
+  const size_t frag = 2 * kAFragElems * sizeof(uint16_t);  // one (k-step, m-tile): both halves
+  pl.off_zero = take(256);
+  pl.off_rows = take((size_t)T * P * sizeof(int32_t));
+  pl.off_a1 = take((size_t)pl.kt1 * pl.mt_pad * frag);
+  pl.off_ssx = take((size_t)T * f);
+  pl.off_part1 = take((size_t)pl.s1 * T * (Q + KVR) * f);
+  pl.off_beta = take((size_t)T * f);
+  pl.off_a2 = take((size_t)pl.kt2 * pl.mt_pad * frag);
+  pl.off_part2 = take((size_t)pl.s2 * T * N2 * f);
+  pl.off_qcat = take((size_t)T * NH * KVR * sizeof(uint16_t));
+  pl.off_pm = take((size_t)T * pl.nsplit * NH * f);
+  pl.off_pl = take((size_t)T * pl.nsplit * NH * f);
+  pl.off_po = take((size_t)T * pl.nsplit * NH * R * f);
+  pl.off_a5 = take((size_t)pl.kt6 * pl.mt_pad * frag);
+  pl.off_part6 = take((size_t)pl.s6 * T * H * f);
+  pl.total = off;
+  return pl;
+}
+
 Plan make_plan(const mla_gd_dims& d, int T) {
   Plan pl;
   memset(&pl, 0, sizeof(pl));
@@ -131,6 +256,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
     pl.ps = cdiv(cdiv(P, ns), kCoreChunk) * kCoreChunk;
     pl.nsplit = cdiv(P, pl.ps);
   }
+  if (T > kGemvMaxTokens) return make_plan_mfma(d, pl);
   pl.dc5 = 16;
   pl.nd5 = cdiv(DV, pl.dc5);
   pl.tc5 = std::min(T, kTT);
@@ -182,6 +308,9 @@ int validate_dims(const mla_gd_dims& d) {
   if (r != 64 && r != 128 && r != 256 && r != 512) return MLA_GD_E_UNSUPPORTED;
   if (d.qk_rope_head_dim > 64 || d.qk_nope_head_dim > 512 || d.v_head_dim > 4096) return MLA_GD_E_UNSUPPORTED;
   if (d.max_tokens > 4096) return MLA_GD_E_UNSUPPORTED;
+  // one token's down-projection row is reduced in LDS; the core's split partials fit its combine
+  if ((long long)d.q_lora_rank + KVR > 16384) return MLA_GD_E_UNSUPPORTED;
+  if (d.n_prior > 64 * kMaxSplitRows) return MLA_GD_E_UNSUPPORTED;
   // flat cache rows and element offsets must fit the kernels' index arithmetic
   if ((long long)d.n_blocks * d.block_size > (1LL << 31) - 1) return MLA_GD_E_UNSUPPORTED;
   if ((long long)d.max_tokens * d.n_prior > (1LL << 31) - 1) return MLA_GD_E_UNSUPPORTED;
@@ -204,18 +333,37 @@ core_kernel_t pick_core(const Plan& pl, int R) {
   return pl.core_hg == 1 ? pick_core_nt<1, 4>(R / 16) : pick_core_nt<4, 2>(R / 16);
 }
 
-const char* const kKernelNames[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"};
-constexpr int kNumKernels = 7;
+// Kernels of a step, in launch order: the GEMV path (few tokens) and the matrix-core path.
+const char* const kKernelNamesGemv[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"};
+const char* const kKernelNamesMfma[] = {"k_prep", "k_down", "k_qa", "k_qup", "k_absorb",
+                                        "k_core", "k_oabsorb", "k_oproj", "k_out"};
+constexpr int kNumKernelsGemv = 7;
+constexpr int kNumKernelsMfma = 9;
 constexpr size_t kGemvLdsBytes = kGemvLdsFloats * sizeof(float);
+constexpr int kMaxLdsBytes = 160 * 1024;
+
+int num_kernels(int n_tokens) { return n_tokens > kGemvMaxTokens ? kNumKernelsMfma : kNumKernelsGemv; }
 
 hipError_t set_lds_limits(const mla_gd_dims& d) {
   hipError_t e = hipSuccess;
   const void* gemv[] = {(const void*)k_down, (const void*)k_qup, (const void*)k_absorb, (const void*)k_oabsorb,
-                        (const void*)k_oproj, (const void*)k_out};
+                        (const void*)k_oproj, (const void*)k_out, (const void*)k_prep, (const void*)k_qa};
   for (const void* k : gemv)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
+  const void* big[] = {(const void*)k_absorb_m<1>, (const void*)k_absorb_m<2>, (const void*)k_absorb_m<4>,
+                       (const void*)k_oabsorb_m<1>, (const void*)k_oabsorb_m<2>};
+  for (const void* k : big)
+    if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   return e;
 }
+
+typedef void (*step_kernel_t)(StepParams);
+
+step_kernel_t pick_down_m(int mtb) { return mtb == 1 ? k_down_m<1> : (mtb == 2 ? k_down_m<2> : k_down_m<4>); }
+step_kernel_t pick_qup_m(int mtb) { return mtb == 1 ? k_qup_m<1> : (mtb == 2 ? k_qup_m<2> : k_qup_m<4>); }
+step_kernel_t pick_oproj_m(int mtb) { return mtb == 1 ? k_oproj_m<1> : (mtb == 2 ? k_oproj_m<2> : k_oproj_m<4>); }
+step_kernel_t pick_absorb_m(int mtb) { return mtb == 1 ? k_absorb_m<1> : (mtb == 2 ? k_absorb_m<2> : k_absorb_m<4>); }
+step_kernel_t pick_oabsorb_m(int mtb) { return mtb == 1 ? k_oabsorb_m<1> : k_oabsorb_m<2>; }
 
 }  // namespace
 
@@ -284,12 +432,13 @@ namespace {
 int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void* workspace,
              size_t workspace_bytes, void* stream, void* const* events, int n_events) {
   if (!h || !tn || !workspace) return MLA_GD_E_INVAL;
-  if (events && n_events < kNumKernels + 1) return MLA_GD_E_INVAL;
-  if (events)
-    for (int i = 0; i <= kNumKernels; ++i)
-      if (!events[i]) return MLA_GD_E_INVAL;
   const mla_gd_dims& d = h->d;
   if (n_tokens < 1 || n_tokens > d.max_tokens) return MLA_GD_E_INVAL;
+  const int nk = num_kernels(n_tokens);
+  if (events && n_events < nk + 1) return MLA_GD_E_INVAL;
+  if (events)
+    for (int i = 0; i <= nk; ++i)
+      if (!events[i]) return MLA_GD_E_INVAL;
   const void* bf[] = {tn->hidden_states, tn->wq_a, tn->wq_b, tn->wkv_a, tn->q_absorb_w, tn->out_absorb_w,
                       tn->o_proj_w, tn->kv_cache, tn->out};
   const void* w4[] = {tn->input_norm_w, tn->q_norm_w, tn->kv_norm_w, tn->cos_table, tn->sin_table,
@@ -327,6 +476,11 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   p.qcat = (uint16_t*)(ws + pl.off_qcat);
   p.pm = (float*)(ws + pl.off_pm); p.pden = (float*)(ws + pl.off_pl); p.po = (float*)(ws + pl.off_po);
   p.ov = (float*)(ws + pl.off_ov); p.part6 = (float*)(ws + pl.off_part6);
+  if (pl.mfma) {
+    p.kvr = nullptr; p.kvss = nullptr; p.ov = nullptr; p.ssq = nullptr;
+    p.a1 = (uint16_t*)(ws + pl.off_a1); p.a2 = (uint16_t*)(ws + pl.off_a2); p.a5 = (uint16_t*)(ws + pl.off_a5);
+    p.beta = (float*)(ws + pl.off_beta);
+  }
   p.pl = pl;
 
   hipError_t e = hipSetDevice(h->device);
@@ -341,22 +495,46 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
     if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], s);
   };
   const size_t gl = kGemvLdsBytes;
+  const dim3 blk(kBlock);
+  const dim3 core_blk(64 * pl.core_hg * pl.core_cs);
   mark(0);
-  hipLaunchKernelGGL(k_down, dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), dim3(kBlock), gl, s, p);
-  mark(1);
-  hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T * pl.nkv), dim3(kBlock), gl, s, p);
-  mark(2);
-  hipLaunchKernelGGL(k_absorb, dim3(p.NH * pl.ncc3 + T), dim3(kBlock), gl, s, p);
-  mark(3);
-  hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), dim3(64 * pl.core_hg * pl.core_cs),
-                     0, s, p);
-  mark(4);
-  hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), dim3(kBlock), gl, s, p);
-  mark(5);
-  hipLaunchKernelGGL(k_oproj, dim3(pl.nt6 * pl.s6), dim3(kBlock), gl, s, p);
-  mark(6);
-  hipLaunchKernelGGL(k_out, dim3(pl.n7), dim3(kBlock), gl, s, p);
-  mark(7);
+  if (!pl.mfma) {
+    hipLaunchKernelGGL(k_down, dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gl, s, p);
+    mark(1);
+    hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gl, s, p);
+    mark(2);
+    hipLaunchKernelGGL(k_absorb, dim3(p.NH * pl.ncc3 + T), blk, gl, s, p);
+    mark(3);
+    hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
+    mark(4);
+    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), blk, gl, s, p);
+    mark(5);
+    hipLaunchKernelGGL(k_oproj, dim3(pl.nt6 * pl.s6), blk, gl, s, p);
+    mark(6);
+    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
+    mark(7);
+  } else {
+    hipLaunchKernelGGL(k_prep, dim3(pl.n_idx_wg + T), blk, 1024, s, p);
+    mark(1);
+    hipLaunchKernelGGL(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), blk, 0, s, p);
+    mark(2);
+    hipLaunchKernelGGL(k_qa, dim3(T), blk, gl, s, p);
+    mark(3);
+    hipLaunchKernelGGL(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0, s, p);
+    mark(4);
+    hipLaunchKernelGGL(pick_absorb_m(pl.mtb3), dim3(mg_grid(p.NH * pl.nct3, pl.ntb3)), blk,
+                       absorb_lds_bytes(pl, p.DN), s, p);
+    mark(5);
+    hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
+    mark(6);
+    hipLaunchKernelGGL(pick_oabsorb_m(pl.mtb5), dim3(mg_grid(p.NH, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R), s,
+                       p);
+    mark(7);
+    hipLaunchKernelGGL(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), blk, 0, s, p);
+    mark(8);
+    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
+    mark(9);
+  }
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) { h->last_hip_error = (int)e; return MLA_GD_E_HIP; }
   return MLA_GD_OK;
@@ -378,11 +556,15 @@ int mla_gather_decode_step_profiled(mla_gd_handle* h, const mla_gd_tensors* tn, 
   return run_step(h, tn, n_tokens, workspace, workspace_bytes, stream, events, n_events);
 }
 
-int mla_gather_decode_kernel_count(const mla_gd_handle* h) { return h ? kNumKernels : 0; }
+int mla_gather_decode_kernel_count(const mla_gd_handle* h, int32_t n_tokens) {
+  if (!h || n_tokens < 1 || n_tokens > h->d.max_tokens) return 0;
+  return num_kernels(n_tokens);
+}
 
-const char* mla_gather_decode_kernel_name(const mla_gd_handle* h, int i) {
-  if (!h || i < 0 || i >= kNumKernels) return "";
-  return kKernelNames[i];
+const char* mla_gather_decode_kernel_name(const mla_gd_handle* h, int32_t n_tokens, int i) {
+  const int n = mla_gather_decode_kernel_count(h, n_tokens);
+  if (i < 0 || i >= n) return "";
+  return n == kNumKernelsMfma ? kKernelNamesMfma[i] : kKernelNamesGemv[i];
 }
 
 }  // extern "C"

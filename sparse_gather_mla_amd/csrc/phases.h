@@ -37,6 +37,20 @@ __device__ __forceinline__ float inv_rms(float sumsq, int n, float eps) {
   return 1.f / sqrtf(sumsq / (float)n + eps);
 }
 
+// Index build for entry idx = t*P + j: selected position -> flat cache row,
+// -1 where causally masked.  Masked entries touch neither the block table nor
+// the cache.
+__device__ __forceinline__ void index_build(const StepParams& p, int idx) {
+  if (idx >= p.pl.T * p.P) return;
+  const int t = idx / p.P;
+  const int g = p.gidx[idx];
+  const int ps = p.pos[t];
+  int row = -1;
+  if (g >= 0 && g <= ps) row = p.btab[(size_t)t * p.MB + g / p.BS] * p.BS + g % p.BS;
+  p.rows[idx] = row;
+  if (p.rows_out) p.rows_out[idx] = row;
+}
+
 // ---------------------------------------------------------------------------
 // k_down: index build; (x * g_in) @ [wq_a | wkv_a] split-K partials; sums of x^2
 // ---------------------------------------------------------------------------
@@ -45,18 +59,7 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
   const int T = pl.T;
   const int n_gemv = pl.nt1 * pl.s1;
   if (b >= n_gemv) {
-    // index build: selected position -> flat cache row, -1 where causally masked;
-    // masked entries touch neither the block table nor the cache
-    const int idx = (b - n_gemv) * kBlock + threadIdx.x;
-    if (idx < T * p.P) {
-      const int t = idx / p.P;
-      const int g = p.gidx[idx];
-      const int ps = p.pos[t];
-      int row = -1;
-      if (g >= 0 && g <= ps) row = p.btab[(size_t)t * p.MB + g / p.BS] * p.BS + g % p.BS;
-      p.rows[idx] = row;
-      if (p.rows_out) p.rows_out[idx] = row;
-    }
+    index_build(p, (b - n_gemv) * kBlock + threadIdx.x);
     return;
   }
   const int slab = b / pl.nt1, tile = b % pl.nt1;

@@ -24,9 +24,20 @@ struct Plan {
   int nt6, s6, ks6;
   // k_out: 64-column groups x token chunks
   int n7;
+  // Matrix-core path (more than a few tokens).  Token blocks of mtb m-tiles
+  // (16 tokens each), ntb blocks, m-tiles padded to mt_pad = ntb*mtb.  For each
+  // projection: kt* k-steps of 32 in all, ks* per slab, 64-column tiles.
+  int mfma;
+  int mtb, ntb, mt_pad;
+  int kt1, ks1m, nt1m, ntq1m;  // [wq_a | wkv_a]: slabs in s1
+  int kt2, ks2m, nt2m;         // wq_b: slabs in s2
+  int mtb3, ntb3, nct3;        // absorption: token blocks, 64-column tiles of kv_lora_rank
+  int mtb5, ntb5;              // output absorption: token blocks
+  int kt6, ks6m, nt6m;         // o_proj: slabs in s6
   // workspace layout (byte offsets)
   size_t off_zero, off_rows, off_part1, off_ssx, off_part2, off_ssq, off_kvr, off_kvss, off_qcat;
   size_t off_pm, off_pl, off_po, off_ov, off_part6;
+  size_t off_a1, off_a2, off_a5, off_beta;
   size_t total;
 };
 
@@ -59,7 +70,7 @@ struct StepParams {
   const uint16_t* zero16;  // 256 zero bytes (source of padding loads)
   int32_t* rows;    // [T][P] flat cache row or -1
   float* part1;     // [s1][T][Q+KVR] split-K partials of (x*gamma) @ [wq_a | wkv_a]
-  float* ssx;       // [s1][T] partial sums of x^2
+  float* ssx;       // [s1][T] partial sums of x^2 (matrix-core path: [T], whole sums)
   float* part2;     // [s2][T][N2] split-K partials of (acc_q*gamma_q) @ wq_b
   float* ssq;       // [s2][T] partial sums of acc_q^2
   float* kvr;       // [T][KVR] alpha * (x * g_in) @ wkv_a: the kv row before its own norm
@@ -70,6 +81,11 @@ struct StepParams {
   float* po;        // [T][nsplit][NH][R] unnormalised latent outputs per split
   float* ov;        // [T][NH*DV] output-absorbed values
   float* part6;     // [s6][T][H] split-K partials of the o-projection
+  // matrix-core path: activations in fragment order (hi/lo bf16), per-token scales
+  uint16_t* a1;     // x * g_in               [kt1][mt_pad][2][512]
+  uint16_t* a2;     // acc_q * g_q            [kt2][mt_pad][2][512]
+  uint16_t* a5;     // o_v                    [kt6][mt_pad][2][512]
+  float* beta;      // [T] alpha * inv_q, the scale of the wq_b output
   Plan pl;
 };
 

@@ -78,6 +78,8 @@ def _create(lib, d):
     ({"qk_rope_head_dim": 72, "kv_lora_rank": 64}, "MLA_GD_E_UNSUPPORTED"),
     ({"kv_lora_rank": 96}, "MLA_GD_E_UNSUPPORTED"),
     ({"max_tokens": 5000}, "MLA_GD_E_UNSUPPORTED"),
+    ({"q_lora_rank": 16384}, "MLA_GD_E_UNSUPPORTED"),
+    ({"n_prior": 262144 + 1}, "MLA_GD_E_UNSUPPORTED"),
 ])
 def test_create_validates_dims(lib, kw, code):
     rc, h = _create(lib, _dims(**kw))
@@ -120,10 +122,16 @@ def test_workspace_size_and_step_argument_checks(lib):
         assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 1, ctypes.c_void_p((1 << 20) + 16), sizes[0],
                                           None) == c["MLA_GD_E_ALIGN"]
         assert lib.mla_gather_decode_workspace_init(h, None, 1024, None) == c["MLA_GD_E_INVAL"]
-        assert lib.mla_gather_decode_kernel_count(h) >= 1
-        names = [lib.mla_gather_decode_kernel_name(h, i).decode() for i in range(lib.mla_gather_decode_kernel_count(h))]
-        assert all(names) and len(set(names)) == len(names)
-        assert lib.mla_gather_decode_kernel_name(h, 99) == b""
+        for T in (1, 4):
+            n = lib.mla_gather_decode_kernel_count(h, T)
+            assert n >= 1
+            names = [lib.mla_gather_decode_kernel_name(h, T, i).decode() for i in range(n)]
+            assert all(names) and len(set(names)) == len(names)
+            assert "k_core" in names and names[-1] == "k_out"
+            assert lib.mla_gather_decode_kernel_name(h, T, n) == b""
+        assert lib.mla_gather_decode_kernel_count(h, 0) == 0
+        assert lib.mla_gather_decode_kernel_count(h, 5) == 0
+        assert lib.mla_gather_decode_kernel_name(h, 0, 0) == b""
         # profiled step: a missing or short event list is rejected
         assert lib.mla_gather_decode_step_profiled(h, ctypes.byref(tn), 1, ws, sizes[0], None, None, 0) == c["MLA_GD_E_INVAL"]
         ev = (ctypes.c_void_p * 2)(1, 1)
@@ -137,3 +145,23 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(sgm, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         sgm.load_library(str(tmp_path / "missing.so"))
+
+
+def test_kernel_lists_of_both_paths(lib):
+    """Steps of up to 8 tokens run the GEMV path; larger ones the matrix-core
+    path with its two extra kernels.  The workspace covers both."""
+    rc, h = _create(lib, _dims(max_tokens=40))
+    assert rc == 0
+    try:
+        def names(T):
+            n = lib.mla_gather_decode_kernel_count(h, T)
+            return [lib.mla_gather_decode_kernel_name(h, T, i).decode() for i in range(n)]
+        gemv = names(8)
+        mfma = names(9)
+        assert gemv == ["k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"]
+        assert mfma == ["k_prep", "k_down", "k_qa", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"]
+        assert names(40) == mfma
+        sizes = [lib.mla_gather_decode_workspace_size(h, t) for t in range(1, 41)]
+        assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+    finally:
+        lib.mla_gather_decode_destroy(h)

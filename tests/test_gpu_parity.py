@@ -5,6 +5,7 @@ bit-exact; the bf16 output and the bf16 written cache-row values within
 max |err| <= 2e-2 * RMS(reference) (fp32 accumulation on the GPU).
 """
 import sys
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -97,6 +98,23 @@ RAGGED = Workload(
 
 def test_parity_ragged_shape():
     _run_and_check(RAGGED)
+
+
+# Steps of more than 8 tokens run the projections on the matrix cores.  Token
+# counts that give one m-tile (9), a ragged block of two (21), a ragged block
+# of four (37) and two blocks of four (70); the ragged shape also gives K not
+# a multiple of the 32-wide k-step and column tiles with tails in every GEMM.
+@pytest.mark.parametrize("T", [9, 21, 37, 70])
+def test_parity_ragged_shape_matrix_core_path(T):
+    wl = replace(RAGGED, name=f"ragged_T{T}", shape=replace(RAGGED.shape, n_tokens=T), seed=77 + T)
+    _run_and_check(wl)
+
+
+def test_parity_tiny_shape_matrix_core_path():
+    """Smallest dims (hidden 256, kv_lora_rank 64, 4 heads) with 24 tokens and the tiny recipe."""
+    wl = replace(CONFIGS[0], name="tiny_T24", shape=replace(CONFIGS[0].shape, n_tokens=24),
+                 contexts=None, context_range=(40, 120), seed=1024)
+    _run_and_check(wl)
 
 
 # ---------------------------------------------------------------------------
