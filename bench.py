@@ -1,19 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of one MLA gather-decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config ds32_slice] [--fused]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config ds32_slice] [--fused] [--extras]
+    python bench.py --traffic FETCH.csv WRITE.csv [--config NAME]   (offline, no GPU)
 
 Prints ONE JSON line.  A "step" is one full pass of the path (index build,
 front-fold, cache-row write, absorption, gather-attention core, output
 absorption, o-projection) over one batch of synthetic, seeded inputs that are
 resident in HBM before timing starts.
 
-Timing: W untimed warm-up steps, then K timed steps.  Before each timed step a
-1 GiB buffer is read and written so that neither the L2s nor the 256 MB
-Infinity Cache hold the weights or the pool (cold-cache steps); HIP events on
-the step's stream bracket the step itself (the flush is outside them) and each
-of its kernels.  ``value`` is the mean step latency in microseconds.  Warm
-(back-to-back, no flush) and HIP-graph numbers are reported beside it.
+Timing: W warm-up steps, then K timed steps, every one of them preceded by a
+read and write of a 1 GiB buffer so that neither the L2s nor the 256 MB
+Infinity Cache hold the weights or the pool (cold-cache steps).  HIP events on
+the step's stream bracket the step (the flush is outside them) and each of its
+kernels; ``value`` is the mean step latency in microseconds.  Since every
+dispatch of the run is a cold one, a rocprofv3 kernel trace of the same
+command averages the same launches.  ``--extras`` adds warm (back-to-back) and
+HIP-graph timings.
+
+``roofline`` is for the kernel with the largest mean duration: algorithmic
+bytes per launch over its event-timed mean duration, against 8 TB/s.
+``traffic`` is that kernel's HBM bytes per launch from two rocprofv3 counter
+runs (FETCH_SIZE, WRITE_SIZE), scaled by what the same counters read for a
+plain 512 MiB device copy, recorded by ``--traffic`` in profiles/traffic.json
+with a digest of the kernel sources; it is null once the sources change.
 """
 from __future__ import annotations
 
@@ -32,11 +42,11 @@ METRIC = "MLA gather-decode step µs + achieved HBM GB/s (% of peak), n_prior=20
 HBM_PEAK_GBPS = 8000.0
 
 
-def alg_bytes(sh, inp) -> dict:
-    """Algorithmic HBM bytes of one step, per kernel of the separately launched
-    variant: every weight once, the gammas, activations in and out, the index
-    tensors, the RoPE tables, each distinct valid gathered row once, and the
-    written rows.  Split-K partials and query-tile round trips are overheads."""
+def alg_bytes(sh, inp, names) -> dict:
+    """Algorithmic HBM bytes of one step, per kernel: every weight once, the
+    gammas, activations in and out, the index tensors, the RoPE tables, each
+    distinct valid gathered row once, and the written rows.  Split-K partials,
+    query tiles and split-combine traffic are overheads and count nothing."""
     import numpy as np
 
     T, H, Q, r, dn, dr, dv, nh = (sh.n_tokens, sh.hidden, sh.q_lora_rank, sh.kv_lora_rank,
@@ -46,15 +56,16 @@ def alg_bytes(sh, inp) -> dict:
     gi = inp["gather_indices"].numpy()
     pos = inp["positions"].numpy()
     uniq = sum(len(np.unique(gi[t][(gi[t] >= 0) & (gi[t] <= pos[t])])) for t in range(T))
-    b = {
-        "k_down": 2 * H * (Q + kvr) + 2 * T * H + 4 * H + 4 * T * P + 4 * T + 4 * T * MB,
-        "k_qup": 2 * Q * nh * (dn + dr) + 4 * Q + 4 * r + 4 * T * dr + 4 * T + 2 * T * kvr,
-        "k_absorb": 2 * nh * dn * r,
-        "k_core": 2 * kvr * uniq,
-        "k_oabsorb": 2 * nh * dv * r,
-        "k_oproj": 2 * nh * dv * H,
-        "k_out": 2 * T * H,
-    }
+    inputs = 2 * T * H + 4 * H + 4 * T * P + 4 * T + 4 * T * MB  # x, g_in, gather_indices, positions, table
+    kv_branch = 4 * Q + 4 * r + 4 * T * dr + 4 * T + 2 * T * kvr  # g_q, g_kv, cos+sin, slots, written rows
+    w_down, w_qb = 2 * H * (Q + kvr), 2 * Q * nh * (dn + dr)
+    if "k_prep" in names:  # matrix-core path
+        b = {"k_prep": inputs, "k_down": w_down, "k_qa": kv_branch, "k_qup": w_qb}
+    else:
+        b = {"k_down": w_down + inputs, "k_qup": w_qb + kv_branch}
+    b.update({"k_absorb": 2 * nh * dn * r, "k_core": 2 * kvr * uniq, "k_oabsorb": 2 * nh * dv * r,
+              "k_oproj": 2 * nh * dv * H, "k_out": 2 * T * H})
+    b = {n: b.get(n, 0) for n in names}
     b["step"] = sum(b.values())
     return b
 
@@ -114,6 +125,59 @@ def cpu_baseline(wl, inp_cpu, budget_s: float) -> dict:
                       f"weights and pool pre-widened to fp64 outside the timed region"}
 
 
+COPY_CAL_BYTES = 512 << 20  # the calibration copy: reads and writes this many bytes
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str, workload: str) -> int:
+    """Offline: per-kernel HBM bytes per launch from two rocprofv3 counter CSVs
+    (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) of a run with --calibrate-copy.
+    Each counter is scaled so that the 512 MiB calibration copies read (write)
+    exactly 512 MiB.  Writes profiles/traffic.json and prints a summary."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals, copies = {}, []
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                v = float(row["Counter_Value"])
+                vals.setdefault(row["Kernel_Name"], []).append(v)
+                if "copyBuffer" in row["Kernel_Name"]:
+                    copies.append((int(row["Dispatch_Id"]), v))
+        # the calibration copies are the run's last four copy-kernel dispatches
+        cal = [v for _, v in sorted(copies)[-4:]]
+        if len(cal) < 4 or min(cal) * 1024 < 0.2 * COPY_CAL_BYTES:
+            raise SystemExit(f"{path}: no calibration copies at the end of the run")
+        # the counter may read a fixed fraction of the bytes; that fraction is what the scale removes
+        return vals, COPY_CAL_BYTES / (statistics.mean(cal) * 1024)
+
+    fetch, sf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, sw = per_kernel(write_csv, "WRITE_SIZE")
+    nf = nw = 4
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            rec = json.load(f)
+    ent = {}
+    for k, v in fetch.items():
+        short = k.split("(")[0].replace("void ", "").split("<")[0].strip()
+        if not short.startswith("k_") or k not in write:
+            continue
+        f_kib, w_kib = statistics.mean(v), statistics.mean(write[k])
+        ent[short] = {"bytes_per_launch": round(f_kib * 1024 * sf + w_kib * 1024 * sw),
+                      "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1),
+                      "dispatches": len(v), "source_digest": source_digest()}
+    ent["_calibration"] = {"copy_bytes": COPY_CAL_BYTES, "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
+                           "copies": [nf, nw]}
+    rec[workload] = ent
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps({workload: ent}, indent=1))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,10 +185,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="ds32_slice")
     ap.add_argument("--fused", action="store_true")
+    ap.add_argument("--extras", action="store_true", help="also time warm steps and a HIP graph of the step")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with four plain 512 MiB device copies (for counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
 
+    if args.traffic:
+        return traffic_from_counters(args.traffic[0], args.traffic[1], args.config)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the step is single-GPU; the multi-GPU design is documented, not built)", file=sys.stderr)
@@ -152,58 +222,68 @@ def main() -> int:
     flush.zero_()
     stream = torch.cuda.current_stream(dev)
 
-    for _ in range(args.warmup):
-        mod(g, out=out)
-    torch.cuda.synchronize()
-
-    # --- timed cold steps -------------------------------------------------
-    K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
+    # --- warm-up and timed steps, all cold ----------------------------------
+    W, K = args.warmup, args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(W + K)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for k in range(K):
-        flush.add_(1.0)  # read + write 1 GiB: evicts L2 and the Infinity Cache
+    for k in range(W + K):
+        if k == W:
+            torch.cuda.synchronize()
+            wall0 = time.perf_counter()
+        flush.add_(1.0)  # read + write 1 GiB: evicts the L2s and the Infinity Cache
         mod(g, out=out, events=evs[k], stream=stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    evs = evs[W:]
     step_ms = [evs[k][0].elapsed_time(evs[k][nk]) for k in range(K)]
     stage_ms = {names[i]: [evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)] for i in range(nk)}
 
-    # --- warm steps (no flush, back to back) ------------------------------
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(K):
-        mod(g, out=out, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    warm_us = e0.elapsed_time(e1) / K * 1e3
-
-    # --- HIP graph of the step, cold ----------------------------------------
-    graph_us = None
-    try:
-        gr = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            mod(g, out=out)  # warm the capture stream
-            torch.cuda.synchronize()
-            with torch.cuda.graph(gr, stream=side):
-                mod(g, out=out)
-        torch.cuda.synchronize()
-        gts = []
+    warm_us = graph_us = None
+    if args.extras:
+        # warm steps (no flush, back to back)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         for _ in range(K):
-            flush.add_(1.0)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            gr.replay()
-            b.record(stream)
-            gts.append((a, b))
+            mod(g, out=out, stream=stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        graph_us = statistics.mean(a.elapsed_time(b) for a, b in gts) * 1e3
-    except Exception as exc:  # pragma: no cover - reported, not fatal
-        print(f"graph capture failed: {exc}", file=sys.stderr)
+        warm_us = e0.elapsed_time(e1) / K * 1e3
+        # HIP graph of the step, cold
+        try:
+            gr = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                mod(g, out=out)  # warm the capture stream
+                torch.cuda.synchronize()
+                with torch.cuda.graph(gr, stream=side):
+                    mod(g, out=out)
+            torch.cuda.synchronize()
+            gts = []
+            for _ in range(K):
+                flush.add_(1.0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                gr.replay()
+                b.record(stream)
+                gts.append((a, b))
+            torch.cuda.synchronize()
+            graph_us = statistics.mean(a.elapsed_time(b) for a, b in gts) * 1e3
+        except Exception as exc:  # pragma: no cover - reported, not fatal
+            print(f"graph capture failed: {exc}", file=sys.stderr)
 
-    ab = alg_bytes(sh, inp)
+    if args.calibrate_copy:
+        src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            flush.add_(1.0)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ab = alg_bytes(sh, inp, names)
     mean_ms = statistics.mean(step_ms)
     stage_us = {n: statistics.mean(v) * 1e3 for n, v in stage_ms.items()}
     dom = max(stage_us, key=stage_us.get)
@@ -218,7 +298,7 @@ def main() -> int:
         "unit": "us",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": W,
         "ms_per_step": round(mean_ms, 6),
         "higher_is_better": False,
         "scaling": "weak",
@@ -232,8 +312,6 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2),
         "alg_bytes_per_step": ab["step"],
         "step_us_p10_p50_p90": [round(x * 1e3, 3) for x in q],
-        "warm_us": round(warm_us, 3),
-        "graph_cold_us": None if graph_us is None else round(graph_us, 3),
         "wall_ms_per_step_incl_flush": round(wall / K * 1e3, 4),
         "stages": {n: {"us": round(stage_us[n], 3), "alg_bytes": ab.get(n, 0),
                        "GBps": round(ab.get(n, 0) / (stage_us[n] * 1e-6) / 1e9, 1)} for n in names},
@@ -242,6 +320,9 @@ def main() -> int:
                      "traffic": measured_traffic(dom, wl.name), "alg_bytes_per_launch": dom_bytes},
         "accumulate": "fp32",
     }
+    if args.extras:
+        res["warm_us"] = None if warm_us is None else round(warm_us, 3)
+        res["graph_cold_us"] = None if graph_us is None else round(graph_us, 3)
     if not args.no_cpu_baseline and small_pool:
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -182,10 +182,16 @@ __device__ __forceinline__ void mg_step(const char* bufA, const char* bufB,
 // direct loads per lane for step st (loads of zeros once st >= nsteps);
 // step(st, buf) consumes a landed step.  Returns with every load landed and
 // the ring free.
-template <int NDMA, class Issue, class Step>
-__device__ __forceinline__ void mg_ring(int nsteps, char* ring, int step_bytes, Issue&& issue, Step&& step) {
+// The ring's first kMgDepth-1 steps; issue them as early as possible (before
+// work the loop does not depend on), then run mg_ring_loop.
+template <class Issue>
+__device__ __forceinline__ void mg_ring_prologue(char* ring, int step_bytes, Issue&& issue) {
 #pragma unroll
   for (int s = 0; s < kMgDepth - 1; ++s) issue(s, ring + s * step_bytes);
+}
+
+template <int NDMA, class Issue, class Step>
+__device__ __forceinline__ void mg_ring_loop(int nsteps, char* ring, int step_bytes, Issue&& issue, Step&& step) {
   for (int s = 0; s < nsteps; ++s) {
     wait_vmcnt<NDMA * (kMgDepth - 2)>();  // step s landed (this wave's oldest loads)
     __syncthreads();                      // ... for every wave; buffer of step s-1 consumed
@@ -195,6 +201,12 @@ __device__ __forceinline__ void mg_ring(int nsteps, char* ring, int step_bytes, 
   }
   wait_vmcnt<0>();
   __syncthreads();
+}
+
+template <int NDMA, class Issue, class Step>
+__device__ __forceinline__ void mg_ring(int nsteps, char* ring, int step_bytes, Issue&& issue, Step&& step) {
+  mg_ring_prologue(ring, step_bytes, issue);
+  mg_ring_loop<NDMA>(nsteps, ring, step_bytes, issue, step);
 }
 
 // acc = A[token block] @ W[k0 : k0 + 32*nks, c0 : c0 + 64] with A from a

@@ -91,6 +91,8 @@ __global__ __launch_bounds__(kBlock) void k_absorb_m(StepParams p) {
   phase_absorb_m<MTB>(p, blockIdx.x, reinterpret_cast<char*>(lds));
 }
 
+__global__ __launch_bounds__(kBlock) void k_combine(StepParams p) { phase_combine(p, blockIdx.x); }
+
 template <int MTB>
 __global__ __launch_bounds__(kBlock) void k_oabsorb_m(StepParams p) {
   extern __shared__ float lds[];
@@ -164,13 +166,10 @@ void split_m(int kt, int units, int target, int* s_out, int* ks_out) {
 int mg_grid(int nunits, int ntb) { return cdiv(nunits, 8) * 8 * ntb; }
 
 size_t absorb_lds_bytes(const Plan& pl, int DN) {
-  return (size_t)kMgDepth * Mg<1>::kBBytes + 1024 + (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2 * kAFragElems * 2;
+  return (size_t)kMgDepth * Mg<1>::kBBytes + 1024 + 256 + (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2 * kAFragElems * 2;
 }
 
-size_t oabsorb_lds_bytes(const Plan& pl, int R) {
-  const size_t head = align_up((size_t)(2 * pl.mtb5 * 16 * pl.nsplit + pl.mtb5 * 16) * 4, 256);
-  return head + (size_t)(R / kMgK) * pl.mtb5 * 2 * kAFragElems * 2;
-}
+size_t oabsorb_lds_bytes(const Plan& pl, int R) { return 256 + (size_t)(R / kMgK) * pl.mtb5 * 2 * kAFragElems * 2; }
 
 // Plan of the matrix-core path; `pl` already holds T, the index build and the core's split.
 Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
@@ -195,8 +194,10 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   pl.mtb3 = pl.mtb;
   while (pl.mtb3 > 1 && (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2048 > 96 * 1024) pl.mtb3 /= 2;
   pl.ntb3 = cdiv(T, 16 * pl.mtb3);
-  pl.mtb5 = std::min(pl.mtb, 2);
+  pl.mtb5 = 1;
   pl.ntb5 = cdiv(T, 16 * pl.mtb5);
+  pl.nxc = cdiv(pl.kt1 * kMgK, kPrepChunk);
+  pl.nqc = cdiv(Q, kQaChunk);
   pl.kt6 = cdiv(NH * DV, kMgK);
   pl.nt6m = cdiv(H, kMgCols);
   split_m(pl.kt6, pl.nt6m * pl.ntb, target, &pl.s6, &pl.ks6m);
@@ -213,15 +214,16 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   pl.off_zero = take(256);
   pl.off_rows = take((size_t)T * P * sizeof(int32_t));
   pl.off_a1 = take((size_t)pl.kt1 * pl.mt_pad * frag);
-  pl.off_ssx = take((size_t)T * f);
+  pl.off_ssx = take((size_t)pl.nxc * T * f);
   pl.off_part1 = take((size_t)pl.s1 * T * (Q + KVR) * f);
-  pl.off_beta = take((size_t)T * f);
+  pl.off_ssq = take((size_t)pl.nqc * T * f);
   pl.off_a2 = take((size_t)pl.kt2 * pl.mt_pad * frag);
   pl.off_part2 = take((size_t)pl.s2 * T * N2 * f);
   pl.off_qcat = take((size_t)T * NH * KVR * sizeof(uint16_t));
   pl.off_pm = take((size_t)T * pl.nsplit * NH * f);
   pl.off_pl = take((size_t)T * pl.nsplit * NH * f);
   pl.off_po = take((size_t)T * pl.nsplit * NH * R * f);
+  pl.off_olat = take(pl.nsplit > 1 ? (size_t)T * NH * R * f : 0);
   pl.off_a5 = take((size_t)pl.kt6 * pl.mt_pad * frag);
   pl.off_part6 = take((size_t)pl.s6 * T * H * f);
   pl.total = off;
@@ -335,14 +337,25 @@ core_kernel_t pick_core(const Plan& pl, int R) {
 
 // Kernels of a step, in launch order: the GEMV path (few tokens) and the matrix-core path.
 const char* const kKernelNamesGemv[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"};
-const char* const kKernelNamesMfma[] = {"k_prep", "k_down", "k_qa", "k_qup", "k_absorb",
-                                        "k_core", "k_oabsorb", "k_oproj", "k_out"};
+const char* const kKernelNamesMfma[] = {"k_prep", "k_down", "k_qa",      "k_qup",   "k_absorb",
+                                        "k_core", "k_combine", "k_oabsorb", "k_oproj", "k_out"};
+const char* const kKernelNamesMfma1[] = {"k_prep", "k_down",    "k_qa",    "k_qup", "k_absorb",
+                                         "k_core", "k_oabsorb", "k_oproj", "k_out"};
 constexpr int kNumKernelsGemv = 7;
-constexpr int kNumKernelsMfma = 9;
+constexpr int kNumKernelsMfma = 10;  // with the split combine
+constexpr int kNumKernelsMfma1 = 9;  // the core runs one split per token
 constexpr size_t kGemvLdsBytes = kGemvLdsFloats * sizeof(float);
 constexpr int kMaxLdsBytes = 160 * 1024;
 
-int num_kernels(int n_tokens) { return n_tokens > kGemvMaxTokens ? kNumKernelsMfma : kNumKernelsGemv; }
+int num_kernels(const Plan& pl) {
+  if (!pl.mfma) return kNumKernelsGemv;
+  return pl.nsplit > 1 ? kNumKernelsMfma : kNumKernelsMfma1;
+}
+
+const char* kernel_name(const Plan& pl, int i) {
+  if (!pl.mfma) return kKernelNamesGemv[i];
+  return pl.nsplit > 1 ? kKernelNamesMfma[i] : kKernelNamesMfma1[i];
+}
 
 hipError_t set_lds_limits(const mla_gd_dims& d) {
   hipError_t e = hipSuccess;
@@ -351,7 +364,7 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
   for (const void* k : gemv)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
   const void* big[] = {(const void*)k_absorb_m<1>, (const void*)k_absorb_m<2>, (const void*)k_absorb_m<4>,
-                       (const void*)k_oabsorb_m<1>, (const void*)k_oabsorb_m<2>};
+                       (const void*)k_oabsorb_m<1>};
   for (const void* k : big)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   return e;
@@ -363,7 +376,7 @@ step_kernel_t pick_down_m(int mtb) { return mtb == 1 ? k_down_m<1> : (mtb == 2 ?
 step_kernel_t pick_qup_m(int mtb) { return mtb == 1 ? k_qup_m<1> : (mtb == 2 ? k_qup_m<2> : k_qup_m<4>); }
 step_kernel_t pick_oproj_m(int mtb) { return mtb == 1 ? k_oproj_m<1> : (mtb == 2 ? k_oproj_m<2> : k_oproj_m<4>); }
 step_kernel_t pick_absorb_m(int mtb) { return mtb == 1 ? k_absorb_m<1> : (mtb == 2 ? k_absorb_m<2> : k_absorb_m<4>); }
-step_kernel_t pick_oabsorb_m(int mtb) { return mtb == 1 ? k_oabsorb_m<1> : k_oabsorb_m<2>; }
+step_kernel_t pick_oabsorb_m(int) { return k_oabsorb_m<1>; }
 
 }  // namespace
 
@@ -434,7 +447,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   if (!h || !tn || !workspace) return MLA_GD_E_INVAL;
   const mla_gd_dims& d = h->d;
   if (n_tokens < 1 || n_tokens > d.max_tokens) return MLA_GD_E_INVAL;
-  const int nk = num_kernels(n_tokens);
+  const int nk = num_kernels(make_plan(d, n_tokens));
   if (events && n_events < nk + 1) return MLA_GD_E_INVAL;
   if (events)
     for (int i = 0; i <= nk; ++i)
@@ -477,9 +490,10 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   p.pm = (float*)(ws + pl.off_pm); p.pden = (float*)(ws + pl.off_pl); p.po = (float*)(ws + pl.off_po);
   p.ov = (float*)(ws + pl.off_ov); p.part6 = (float*)(ws + pl.off_part6);
   if (pl.mfma) {
-    p.kvr = nullptr; p.kvss = nullptr; p.ov = nullptr; p.ssq = nullptr;
+    p.kvr = nullptr; p.kvss = nullptr; p.ov = nullptr;
     p.a1 = (uint16_t*)(ws + pl.off_a1); p.a2 = (uint16_t*)(ws + pl.off_a2); p.a5 = (uint16_t*)(ws + pl.off_a5);
-    p.beta = (float*)(ws + pl.off_beta);
+    p.ssq = (float*)(ws + pl.off_ssq);
+    p.olat = pl.nsplit > 1 ? (float*)(ws + pl.off_olat) : nullptr;
   }
   p.pl = pl;
 
@@ -514,26 +528,31 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
     hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
     mark(7);
   } else {
-    hipLaunchKernelGGL(k_prep, dim3(pl.n_idx_wg + T), blk, 1024, s, p);
-    mark(1);
+    int ev = 1;
+    hipLaunchKernelGGL(k_prep, dim3(pl.n_idx_wg + T * pl.nxc), blk, 1024, s, p);
+    mark(ev++);
     hipLaunchKernelGGL(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), blk, 0, s, p);
-    mark(2);
-    hipLaunchKernelGGL(k_qa, dim3(T), blk, gl, s, p);
-    mark(3);
+    mark(ev++);
+    hipLaunchKernelGGL(k_qa, dim3(T * (pl.nqc + 1)), blk, gl, s, p);
+    mark(ev++);
     hipLaunchKernelGGL(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0, s, p);
-    mark(4);
+    mark(ev++);
     hipLaunchKernelGGL(pick_absorb_m(pl.mtb3), dim3(mg_grid(p.NH * pl.nct3, pl.ntb3)), blk,
                        absorb_lds_bytes(pl, p.DN), s, p);
-    mark(5);
+    mark(ev++);
     hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
-    mark(6);
+    mark(ev++);
+    if (pl.nsplit > 1) {
+      hipLaunchKernelGGL(k_combine, dim3(cdiv(T * p.NH * (p.R / 4), kBlock)), blk, 0, s, p);
+      mark(ev++);
+    }
     hipLaunchKernelGGL(pick_oabsorb_m(pl.mtb5), dim3(mg_grid(p.NH, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R), s,
                        p);
-    mark(7);
+    mark(ev++);
     hipLaunchKernelGGL(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), blk, 0, s, p);
-    mark(8);
+    mark(ev++);
     hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
-    mark(9);
+    mark(ev++);
   }
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) { h->last_hip_error = (int)e; return MLA_GD_E_HIP; }
@@ -558,13 +577,13 @@ int mla_gather_decode_step_profiled(mla_gd_handle* h, const mla_gd_tensors* tn, 
 
 int mla_gather_decode_kernel_count(const mla_gd_handle* h, int32_t n_tokens) {
   if (!h || n_tokens < 1 || n_tokens > h->d.max_tokens) return 0;
-  return num_kernels(n_tokens);
+  return num_kernels(make_plan(h->d, n_tokens));
 }
 
 const char* mla_gather_decode_kernel_name(const mla_gd_handle* h, int32_t n_tokens, int i) {
   const int n = mla_gather_decode_kernel_count(h, n_tokens);
   if (i < 0 || i >= n) return "";
-  return n == kNumKernelsMfma ? kKernelNamesMfma[i] : kKernelNamesGemv[i];
+  return kernel_name(make_plan(h->d, n_tokens), i);
 }
 
 }  // extern "C"

@@ -4,14 +4,16 @@
 // (gemm_mfma.h).  Each producer writes the next GEMM's activation already in
 // fragment order, so the GEMM kernels stream both operands with direct
 // global->LDS loads:
-//   k_prep    index build; A1 = x * g_in; sums of x^2
+//   k_prep    index build; A1 = x * g_in; partial sums of x^2
 //   k_down    split-K partials of A1 @ [wq_a | wkv_a]
-//   k_qa      per token: reduce them; A2 = acc_q * g_q; beta = alpha * inv_q;
-//             kv-latent RMSNorm, RoPE and the cache-row write
+//   k_qa      reduce them: A2 = acc_q * g_q and partial sums of acc_q^2 per
+//             column chunk; per token, kv-latent RMSNorm, RoPE, cache-row write
 //   k_qup     split-K partials of A2 @ wq_b
-//   k_absorb  q_lat = (beta * q_nope) @ q_absorb_w[h]; RoPE of q_pe -> Qcat
+//   k_absorb  q_lat = (beta * q_nope) @ q_absorb_w[h], beta = alpha * inv_q;
+//             RoPE of q_pe -> Qcat
 //   k_core    (shared with the GEMV path)
-//   k_oabsorb split combine; o_v = out_absorb_w[h] . o_lat -> A5
+//   k_combine the core's split partials -> normalised o_lat (only with splits)
+//   k_oabsorb o_v = out_absorb_w[h] . o_lat -> A5
 //   k_oproj   split-K partials of A5 @ o_proj_w
 //   k_out     (shared) reduction to the bf16 output
 // Rows of a token block past the last token carry unspecified values; they
@@ -25,9 +27,13 @@
 
 namespace mla {
 
+constexpr int kPrepChunk = 4 * kBlock * 2;  // hidden columns per k_prep workgroup
+constexpr int kQaChunk = 4 * kBlock;        // q_lora_rank columns per k_qa workgroup
+
 // ---------------------------------------------------------------------------
-// k_prep: index build (first n_idx_wg workgroups); then one workgroup per
-// token: A1 = x * g_in in fragment order (K padded with zeros) and sum of x^2.
+// k_prep: index build (first n_idx_wg workgroups); then workgroup (token t,
+// chunk of kPrepChunk hidden columns): A1 = x * g_in in fragment order (K
+// padded with zeros) and the chunk's sum of x^2.
 // ---------------------------------------------------------------------------
 __device__ void phase_prep(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
@@ -35,11 +41,14 @@ __device__ void phase_prep(const StepParams& p, int b, float* lds) {
     index_build(p, b * kBlock + threadIdx.x);
     return;
   }
-  const int t = b - pl.n_idx_wg;
+  const int t = (b - pl.n_idx_wg) / pl.nxc, ch = (b - pl.n_idx_wg) % pl.nxc;
   const int KP = pl.kt1 * kMgK;
   const bf16_t* xr = p.x + (size_t)t * p.H;
   float ss = 0.f;
-  for (int k = 4 * threadIdx.x; k < KP; k += 4 * kBlock) {
+#pragma unroll
+  for (int u = 0; u < kPrepChunk / (4 * kBlock); ++u) {
+    const int k = ch * kPrepChunk + u * 4 * kBlock + 4 * threadIdx.x;
+    if (k >= KP) break;
     float a[4] = {0.f, 0.f, 0.f, 0.f};
     if (k < p.H) {  // H % 8 == 0: a group of four is wholly inside or outside
       const uint2 v = *reinterpret_cast<const uint2*>(xr + k);
@@ -53,7 +62,22 @@ __device__ void phase_prep(const StepParams& p, int b, float* lds) {
     put_a4(p.a1, pl.mt_pad, t, k, a);
   }
   ss = block_sum(ss, lds);
-  if (threadIdx.x == 0) p.ssx[t] = ss;
+  if (threadIdx.x == 0) p.ssx[(size_t)ch * pl.T + t] = ss;
+}
+
+// alpha = 1/rms(x) of token t from the chunk sums (fixed order)
+__device__ __forceinline__ float mfma_alpha(const StepParams& p, int t) {
+  float s = 0.f;
+  for (int c = 0; c < p.pl.nxc; ++c) s += p.ssx[(size_t)c * p.pl.T + t];
+  return inv_rms(s, p.H, p.eps);
+}
+
+// beta = alpha / rms(alpha * acc_q) of token t: the scale of the wq_b output
+__device__ __forceinline__ float mfma_beta(const StepParams& p, int t) {
+  const float a = mfma_alpha(p, t);
+  float s = 0.f;
+  for (int c = 0; c < p.pl.nqc; ++c) s += p.ssq[(size_t)c * p.pl.T + t];
+  return a / sqrtf(a * a * s / (float)p.Q + p.eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -81,58 +105,80 @@ __device__ void phase_down_m(const StepParams& p, int b, char* ring, char* sink)
 }
 
 // ---------------------------------------------------------------------------
-// k_qa: one workgroup per token.  Reduces the down-projection over its slabs
-// (fixed order); alpha = 1/rms(x); A2 = acc_q * g_q in fragment order;
-// beta = alpha / rms(alpha * acc_q); and the kv branch: y = alpha * acc_kv,
-// RMSNorm of its latent part, RoPE of its rotary part, bf16 row at slot_mapping[t].
+// k_qa: workgroup (token t, w).  w < nqc: columns [w*kQaChunk, ...) of the
+// query latent, reduced over the down-projection's slabs (fixed order):
+// A2 = acc_q * g_q in fragment order (the chunks cover the K padding, which
+// gets zeros) and the chunk's sum of acc_q^2.  w == nqc: the kv row,
+// y = alpha * acc_kv, RMSNorm of its latent part, RoPE of its rotary part,
+// bf16 row at slot_mapping[t].
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float4 sum_slabs4(const float* src, size_t stride, int S) {
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = 0;
+  for (; s + 4 <= S; s += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)(s + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
+    }
+  }
+  for (; s < S; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)s * stride);
+    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  }
+  return a;
+}
+
 __device__ void phase_qa(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
-  const int T = pl.T, t = b, tid = threadIdx.x;
+  const int T = pl.T, tid = threadIdx.x;
+  const int t = b / (pl.nqc + 1), w = b % (pl.nqc + 1);
   const int N1 = p.Q + p.KVR;
-  float* row = lds;                           // [N1]
-  float* scratch = lds + ((N1 + 63) & ~63);   // block_sum scratch
-  for (int c4 = tid; c4 < N1 / 4; c4 += kBlock) {
-    const float* src = p.part1 + (size_t)t * N1 + 4 * c4;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < pl.s1; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(src + (size_t)s * T * N1);
-      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  const size_t sstride = (size_t)T * N1;
+  const float* src = p.part1 + (size_t)t * N1;
+  if (w < pl.nqc) {
+    const int k = w * kQaChunk + 4 * tid;
+    const int KP = pl.kt2 * kMgK;
+    float ss = 0.f;
+    if (k < KP) {
+      float a[4] = {0.f, 0.f, 0.f, 0.f};
+      if (k < p.Q) {  // Q % 8 == 0
+        const float4 v = sum_slabs4(src + k, sstride, pl.s1);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ss = fmaf(vv[i], vv[i], ss);
+          a[i] = vv[i] * p.g_q[k + i];
+        }
+      }
+      put_a4(p.a2, pl.mt_pad, t, k, a);
     }
-    *reinterpret_cast<float4*>(row + 4 * c4) = a;
+    ss = block_sum(ss, lds);
+    if (tid == 0) p.ssq[(size_t)w * T + t] = ss;
+    return;
+  }
+  float* y = lds;                            // [KVR]
+  float* scratch = lds + ((p.KVR + 63) & ~63);
+  const float alpha = mfma_alpha(p, t);
+  for (int c4 = tid; c4 < p.KVR / 4; c4 += kBlock) {
+    const float4 v = sum_slabs4(src + p.Q + 4 * c4, sstride, pl.s1);
+    y[4 * c4 + 0] = alpha * v.x;
+    y[4 * c4 + 1] = alpha * v.y;
+    y[4 * c4 + 2] = alpha * v.z;
+    y[4 * c4 + 3] = alpha * v.w;
   }
   __syncthreads();
-  const float alpha = inv_rms(p.ssx[t], p.H, p.eps);
-  const int KP = pl.kt2 * kMgK;
-  float ss = 0.f;
-  for (int k = 4 * tid; k < KP; k += 4 * kBlock) {
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    if (k < p.Q) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = row[k + i];
-        ss = fmaf(v, v, ss);
-        a[i] = v * p.g_q[k + i];
-      }
-    }
-    put_a4(p.a2, pl.mt_pad, t, k, a);
-  }
-  ss = block_sum(ss, scratch);
-  const float iq = 1.f / sqrtf(alpha * alpha * ss / (float)p.Q + p.eps);
-  if (tid == 0) p.beta[t] = alpha * iq;
-  const float* kv = row + p.Q;
   float sk = 0.f;
-  for (int c = tid; c < p.R; c += kBlock) {
-    const float y = alpha * kv[c];
-    sk = fmaf(y, y, sk);
-  }
+  for (int c = tid; c < p.R; c += kBlock) sk = fmaf(y[c], y[c], sk);
   sk = block_sum(sk, scratch);
   const float inv = inv_rms(sk, p.R, p.eps);
   bf16_t* crow = p.cache + (size_t)p.slot[t] * p.KVR;
-  for (int c = tid; c < p.R; c += kBlock) crow[c] = f32_to_bf16(alpha * kv[c] * inv * p.g_kv[c]);
+  for (int c = tid; c < p.R; c += kBlock) crow[c] = f32_to_bf16(y[c] * inv * p.g_kv[c]);
   const int half = p.DR / 2;
   for (int i = tid; i < half; i += kBlock) {
-    const float x0 = alpha * kv[p.R + 2 * i], x1 = alpha * kv[p.R + 2 * i + 1];
+    const float x0 = y[p.R + 2 * i], x1 = y[p.R + 2 * i + 1];
     const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
     crow[p.R + 2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
     crow[p.R + 2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
@@ -162,10 +208,10 @@ __device__ void phase_qup_m(const StepParams& p, int b, char* ring, char* sink) 
 
 // ---------------------------------------------------------------------------
 // k_absorb: workgroup (head h, 64-column tile of kv_lora_rank, token block).
-// A3 = beta * q_nope (wq_b slabs summed in order) goes to LDS in fragment
-// order; the weight tile streams through the ring; q_lat lands in Qcat as
-// bf16.  The tile-0 workgroups also rope q_pe into Qcat.
-// LDS: ring (kMgDepth x 4 KB) | sink (1 KB) | A3 (ceil(DN/32) x MTB x 2 KB).
+// The weight tile's loads are issued first; meanwhile A3 = beta * q_nope (wq_b
+// slabs summed in order) goes to LDS in fragment order.  q_lat lands in Qcat
+// as bf16.  The tile-0 workgroups also rope q_pe into Qcat.
+// LDS: ring (kMgDepth x 4 KB) | sink (1 KB) | beta (256 B) | A3 (ceil(DN/32) x MTB x 2 KB).
 // ---------------------------------------------------------------------------
 template <int MTB>
 __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
@@ -178,21 +224,22 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   const int t0 = tb * MTB * 16;
   const int KS = (p.DN + kMgK - 1) / kMgK;
   char* ring = lds;
-  char* sink = lds + kMgDepth * S::kBBytes;
-  char* ares = sink + 1024;
+  float* beta = reinterpret_cast<float*>(lds + kMgDepth * S::kBBytes + 1024);
+  char* ares = lds + kMgDepth * S::kBBytes + 1024 + 256;
+  const int c0 = j * kMgCols;
+  const BTileSrc bs = btile_src(p.w_qabs + (size_t)h * p.DN * p.R, p.DN, p.R, 0, c0);
+  auto issue = [&](int st, char* buf) { issue_btile(bs, st, st < KS, buf, p.zero16); };
+  mg_ring_prologue(ring, S::kBBytes, issue);
+  if (tid < MTB * 16) beta[tid] = (t0 + tid < T) ? mfma_beta(p, t0 + tid) : 0.f;
+  __syncthreads();
   for (int idx = tid; idx < MTB * 16 * KS * 8; idx += kBlock) {
     const int tt = idx / (KS * 8), k = 4 * (idx % (KS * 8));
     const int t = t0 + tt;
     float a[4] = {0.f, 0.f, 0.f, 0.f};
     if (t < T && k < p.DN) {  // DN % 8 == 0
-      const float* src = p.part2 + (size_t)t * p.N2 + (size_t)h * p.QKH + k;
-      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = 0; s < pl.s2; ++s) {
-        const float4 v = *reinterpret_cast<const float4*>(src + (size_t)s * T * p.N2);
-        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-      }
-      const float bt = p.beta[t];
-      a[0] = bt * sum.x; a[1] = bt * sum.y; a[2] = bt * sum.z; a[3] = bt * sum.w;
+      const float4 v = sum_slabs4(p.part2 + (size_t)t * p.N2 + (size_t)h * p.QKH + k, (size_t)T * p.N2, pl.s2);
+      const float bt = beta[tt];
+      a[0] = bt * v.x; a[1] = bt * v.y; a[2] = bt * v.z; a[3] = bt * v.w;
     }
     put_a4_lds<true>(ares, MTB, tt, k, a);
   }
@@ -202,29 +249,24 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   for (int mt = 0; mt < S::MTW; ++mt)
 #pragma unroll
     for (int nt = 0; nt < S::NTW; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int c0 = j * kMgCols;
-  const BTileSrc bs = btile_src(p.w_qabs + (size_t)h * p.DN * p.R, p.DN, p.R, 0, c0);
-  mg_ring<1>(
-      KS, ring, S::kBBytes,
-      [&](int st, char* buf) { issue_btile(bs, st, st < KS, buf, p.zero16); },
-      [&](int st, const char* buf) { mg_step<MTB>(ares + st * S::kABytes, buf, acc); });
+  mg_ring_loop<1>(KS, ring, S::kBBytes, issue,
+                  [&](int st, const char* buf) { mg_step<MTB>(ares + st * S::kABytes, buf, acc); });
   mg_for_outputs<MTB>(acc, t0, c0, [&](int t, int c, float v) {
     if (t < T) p.qcat[((size_t)t * p.NH + h) * p.KVR + c] = f32_to_bf16(v);
   });
   if (j == 0) {
     const int half = p.DR / 2;
     for (int idx = tid; idx < MTB * 16 * half; idx += kBlock) {
-      const int t = t0 + idx / half, i = idx % half;
+      const int tt = idx / half, i = idx % half, t = t0 + tt;
       if (t >= T) continue;
       const float* src = p.part2 + (size_t)t * p.N2 + (size_t)h * p.QKH + p.DN + 2 * i;
       float x0 = 0.f, x1 = 0.f;
-      for (int s = 0; s < pl.s2; ++s) {
-        x0 += src[(size_t)s * T * p.N2];
-        x1 += src[(size_t)s * T * p.N2 + 1];
+      for (int s2 = 0; s2 < pl.s2; ++s2) {
+        x0 += src[(size_t)s2 * T * p.N2];
+        x1 += src[(size_t)s2 * T * p.N2 + 1];
       }
-      const float bt = p.beta[t];
-      x0 *= bt;
-      x1 *= bt;
+      x0 *= beta[tt];
+      x1 *= beta[tt];
       const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
       bf16_t* q = p.qcat + ((size_t)t * p.NH + h) * p.KVR + p.R;
       q[2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
@@ -234,13 +276,43 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// k_oabsorb: workgroup (head h, token block).  Combines the core's split
-// partials into o_lat (softmax normalisation; no valid entry gives zeros),
-// stores it in LDS as hi/lo fragments in the plain order, and multiplies by
-// out_absorb_w[h] ([DV, R], k-contiguous: B fragments load straight from
-// memory).  o_v goes to A5 in fragment order; the last head's workgroups
-// write A5's K padding.
-// LDS: split weights [16*MTB][nsplit] | 1/L [16*MTB] | A4 (R/32 x MTB x 2 KB).
+// k_combine (when the core splits the selected rows): one thread per
+// (token, head, 4 latent columns).  Weights w_s = 2^(m_s - M) over the splits,
+// L = sum_s w_s * l_s, o_lat = sum_s w_s * o_s / L in split order; a token
+// with no valid entry (L = 0) gets zeros.
+// ---------------------------------------------------------------------------
+__device__ void phase_combine(const StepParams& p, int b) {
+  const Plan& pl = p.pl;
+  const int R4 = p.R / 4, NSP = pl.nsplit;
+  const int i = b * kBlock + threadIdx.x;
+  if (i >= pl.T * p.NH * R4) return;
+  const int c4 = i % R4, th = i / R4, h = th % p.NH, t = th / p.NH;
+  const float* pm = p.pm + (size_t)t * NSP * p.NH + h;
+  const float* pd = p.pden + (size_t)t * NSP * p.NH + h;
+  float M = -INFINITY;
+  for (int s = 0; s < NSP; ++s) M = fmaxf(M, pm[(size_t)s * p.NH]);
+  float L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+    const float* po = p.po + ((size_t)t * NSP * p.NH + h) * p.R + 4 * c4;
+    for (int s = 0; s < NSP; ++s) {
+      const float w = exp2f(pm[(size_t)s * p.NH] - M);
+      L = fmaf(pd[(size_t)s * p.NH], w, L);
+      const float4 v = *reinterpret_cast<const float4*>(po + (size_t)s * p.NH * p.R);
+      o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y); o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
+    }
+  }
+  const float li = (L > 0.f) ? 1.f / L : 0.f;
+  *reinterpret_cast<float4*>(p.olat + (size_t)th * p.R + 4 * c4) = make_float4(o.x * li, o.y * li, o.z * li, o.w * li);
+}
+
+// ---------------------------------------------------------------------------
+// k_oabsorb: workgroup (head h, token block).  o_lat (from k_combine, or the
+// core's single split divided by its denominator) goes to LDS as hi/lo
+// fragments in the plain order and meets out_absorb_w[h] ([DV, R],
+// k-contiguous: B fragments load straight from memory).  o_v goes to A5 in
+// fragment order; the last head's workgroups write A5's K padding.
+// LDS: 1/L [16*MTB] (256 B) | A4 (R/32 x MTB x 2 KB).
 // ---------------------------------------------------------------------------
 template <int MTB>
 __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
@@ -248,45 +320,29 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
   int u, tb;
   if (!mg_unit(b, p.NH, pl.ntb5, u, tb)) return;
   const int h = u;
-  const int T = pl.T, NSP = pl.nsplit, R = p.R, tid = threadIdx.x;
+  const int T = pl.T, R = p.R, tid = threadIdx.x;
   const int t0 = tb * MTB * 16;
   const int nt = min(MTB * 16, T - t0);
-  float* wsp = reinterpret_cast<float*>(lds);  // [16*MTB][NSP]
-  float* plv = wsp + MTB * 16 * NSP;           // [16*MTB][NSP] denominators
-  float* linv = plv + MTB * 16 * NSP;          // [16*MTB]
-  char* ares = lds + ((size_t)(2 * MTB * 16 * NSP + MTB * 16) * 4 + 255) / 256 * 256;
-  for (int idx = tid; idx < nt * NSP; idx += kBlock) {
-    const int tt = idx / NSP, s = idx % NSP;
-    const size_t q = ((size_t)(t0 + tt) * NSP + s) * p.NH + h;
-    wsp[idx] = p.pm[q];
-    plv[idx] = p.pden[q];
-  }
-  __syncthreads();
+  const bool split = pl.nsplit > 1;
+  float* linv = reinterpret_cast<float*>(lds);  // [16*MTB]
+  char* ares = lds + 256;
   if (tid < nt) {
-    float M = -INFINITY;
-    for (int s = 0; s < NSP; ++s) M = fmaxf(M, wsp[tid * NSP + s]);
-    float L = 0.f;
-    for (int s = 0; s < NSP; ++s) {
-      const float w = (M == -INFINITY) ? 0.f : exp2f(wsp[tid * NSP + s] - M);
-      wsp[tid * NSP + s] = w;
-      L = fmaf(plv[tid * NSP + s], w, L);
+    float li = 1.f;
+    if (!split) {
+      const float L = p.pden[(size_t)(t0 + tid) * p.NH + h];
+      li = (L > 0.f) ? 1.f / L : 0.f;
     }
-    linv[tid] = (L > 0.f) ? 1.f / L : 0.f;
+    linv[tid] = li;
   }
   __syncthreads();
+  const float* src = split ? p.olat : p.po;  // both [T][NH][R] here
   for (int idx = tid; idx < MTB * 16 * (R / 4); idx += kBlock) {
     const int tt = idx / (R / 4), c = 4 * (idx % (R / 4));
     float a[4] = {0.f, 0.f, 0.f, 0.f};
     if (tt < nt) {
-      const float* src = p.po + ((size_t)(t0 + tt) * NSP * p.NH + h) * R + c;
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = 0; s < NSP; ++s) {
-        const float w = wsp[tt * NSP + s];
-        const float4 v = *reinterpret_cast<const float4*>(src + (size_t)s * p.NH * R);
-        o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y); o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
-      }
+      const float4 v = *reinterpret_cast<const float4*>(src + ((size_t)(t0 + tt) * p.NH + h) * R + c);
       const float li = linv[tt];
-      a[0] = o.x * li; a[1] = o.y * li; a[2] = o.z * li; a[3] = o.w * li;
+      a[0] = v.x * li; a[1] = v.y * li; a[2] = v.z * li; a[3] = v.w * li;
     }
     put_a4_lds<false>(ares, MTB, tt, c, a);
   }

@@ -33,11 +33,12 @@ struct Plan {
   int kt2, ks2m, nt2m;         // wq_b: slabs in s2
   int mtb3, ntb3, nct3;        // absorption: token blocks, 64-column tiles of kv_lora_rank
   int mtb5, ntb5;              // output absorption: token blocks
+  int nxc, nqc;                // k_prep chunks of hidden; k_qa chunks of q_lora_rank (per token)
   int kt6, ks6m, nt6m;         // o_proj: slabs in s6
   // workspace layout (byte offsets)
   size_t off_zero, off_rows, off_part1, off_ssx, off_part2, off_ssq, off_kvr, off_kvss, off_qcat;
   size_t off_pm, off_pl, off_po, off_ov, off_part6;
-  size_t off_a1, off_a2, off_a5, off_beta;
+  size_t off_a1, off_a2, off_a5, off_olat;
   size_t total;
 };
 
@@ -70,9 +71,9 @@ struct StepParams {
   const uint16_t* zero16;  // 256 zero bytes (source of padding loads)
   int32_t* rows;    // [T][P] flat cache row or -1
   float* part1;     // [s1][T][Q+KVR] split-K partials of (x*gamma) @ [wq_a | wkv_a]
-  float* ssx;       // [s1][T] partial sums of x^2 (matrix-core path: [T], whole sums)
+  float* ssx;       // [s1][T] partial sums of x^2 (matrix-core path: [nxc][T])
   float* part2;     // [s2][T][N2] split-K partials of (acc_q*gamma_q) @ wq_b
-  float* ssq;       // [s2][T] partial sums of acc_q^2
+  float* ssq;       // [s2][T] partial sums of acc_q^2 (matrix-core path: [nqc][T])
   float* kvr;       // [T][KVR] alpha * (x * g_in) @ wkv_a: the kv row before its own norm
   float* kvss;      // [T][nkv] partial sums of squares of the kv row's latent part
   uint16_t* qcat;   // [T][NH][KVR] bf16: per head [q_lat | roped q_pe]
@@ -85,7 +86,7 @@ struct StepParams {
   uint16_t* a1;     // x * g_in               [kt1][mt_pad][2][512]
   uint16_t* a2;     // acc_q * g_q            [kt2][mt_pad][2][512]
   uint16_t* a5;     // o_v                    [kt6][mt_pad][2][512]
-  float* beta;      // [T] alpha * inv_q, the scale of the wq_b output
+  float* olat;      // [T][NH][R] combined, normalised latent outputs (when nsplit > 1)
   Plan pl;
 };
 
