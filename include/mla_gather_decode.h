@@ -45,7 +45,11 @@ extern "C" {
 #define MLA_GD_E_HIP 5          /* a HIP runtime call or kernel launch failed */
 
 /* flags (mla_gd_dims.flags) */
-#define MLA_GD_FLAG_FUSED 1u    /* run the step as one persistent launch (ablation variant) */
+/* Fused variant (ablation): the kv-row write, the absorption and the gather
+ * core run as one launch whose core workgroups wait on device-scope counters
+ * in the workspace instead of a kernel boundary.  Applies to steps of at most
+ * 8 tokens with at most 16 heads; other steps run the separate kernels. */
+#define MLA_GD_FLAG_FUSED 1u
 
 /*
  * Dimensions of the step, fixed when the handle is created.  The page passes

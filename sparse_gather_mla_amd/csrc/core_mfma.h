@@ -40,9 +40,18 @@ __host__ __device__ constexpr int core_buf_bytes(int nt) { return kCoreChunk * (
 // split the score's k-steps between them and add their partial score tiles
 // through LDS (`sx`), so every wave of the group holds the same scores and
 // the same softmax state.  The workgroup has HG*CS waves.
-template <int NT, int HG, int CS>
+// Hooks of the separately launched core: every input is complete at kernel start.
+struct CoreNoWait {
+  __device__ void before_rows(int) const {}
+  __device__ void before_q(int) const {}
+};
+
+// Hooks: before_rows(token) runs before the first read of the row ids or the
+// cache; before_q(first head) after the first row loads are issued and before
+// the query tiles are read.  Every thread of the workgroup calls both.
+template <int NT, int HG, int CS, class Hooks = CoreNoWait>
 __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, int b, char* ring, int* ids,
-                                                          char* sink, f32x4_t* sx) {
+                                                          char* sink, f32x4_t* sx, const Hooks& hooks = Hooks()) {
   constexpr int NW = HG * CS;
   constexpr int NTW = NT / CS;       // output tiles (16 columns) per wave
   constexpr int KSMAX = NT / 2 + 2;  // 32-wide k-steps over kv_row = 16*NT + DR, DR <= 64
@@ -75,24 +84,15 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   const int hbase = (hb * HG + hg) * 16;
   const int head = hbase + l16;  // this lane's head for Q fragments and softmax state
 
+  hooks.before_rows(t);
   // this split's flat row ids (-1: causally masked, or past the split)
   for (int i = tid; i < nchunks * kCoreChunk; i += NW * 64)
     ids[i] = (i < nrows) ? p.rows[(size_t)t * p.P + j0 + i] : -1;
+  __syncthreads();  // row ids visible
 
   // this wave's k-steps: kk = kb + j, j < KSW; steps at or past ks carry zero
   // Q fragments and read a valid slot (step ks-1), so they add exactly zero
   const int kb = cs * KSW;
-  // Q fragments: lane l holds Qcat[head][32*kk + 8*g .. +8] (B operand of the score product)
-  bf16x8_t qf[KSW];
-#pragma unroll
-  for (int j = 0; j < KSW; ++j) {
-    const int k = 32 * (kb + j) + 8 * g;
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (kb + j < ks && head < p.NH && k < KVR)
-      v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * p.NH + head) * KVR + k);
-    qf[j] = __builtin_bit_cast(bf16x8_t, v);
-  }
-  __syncthreads();  // row ids visible
 
   // direct global->LDS load of chunk c into ring buffer c % kCoreRing.  Every
   // wave issues exactly NI loads per chunk (those past the chunk read the zero
@@ -134,9 +134,23 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   for (int n = 0; n < NTW; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  wait_vmcnt<0>();  // Q fragments and row ids are in registers / LDS; only ring loads follow
 #pragma unroll
   for (int c = 0; c < kCoreRing - 1; ++c) issue_chunk(c);
+
+  hooks.before_q(hb * HG * 16);
+  // Q fragments: lane l holds Qcat[head][32*kk + 8*g .. +8] (B operand of the score product)
+  bf16x8_t qf[KSW];
+#pragma unroll
+  for (int j = 0; j < KSW; ++j) {
+    const int k = 32 * (kb + j) + 8 * g;
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (kb + j < ks && head < p.NH && k < KVR)
+      v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * p.NH + head) * KVR + k);
+    qf[j] = __builtin_bit_cast(bf16x8_t, v);
+  }
+  // loads return in order: the Q fragments land after the first ring chunks,
+  // so nothing but ring loads is outstanding below
+  wait_vmcnt<0>();
 
   for (int c = 0; c < nchunks; ++c) {
     // chunk c's loads are this wave's oldest; the younger chunk may stay in flight

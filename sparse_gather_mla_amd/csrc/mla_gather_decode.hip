@@ -44,6 +44,19 @@ __global__ __launch_bounds__(HG * CS * 64) void k_core(StepParams p) {
   core_phase<NT, HG, CS>(p, blockIdx.x, ring, ids, sink, sx);
 }
 
+// fused variant: kv rows, absorption and core in one launch (phase_absorb_core)
+template <int NT>
+__global__ __launch_bounds__(kBlock) void k_absorb_core(StepParams p) {
+  __shared__ __attribute__((aligned(16))) char ring[kCoreRing * core_buf_bytes(NT)];
+  __shared__ int ids[kMaxSplitRows];
+  __shared__ __attribute__((aligned(16))) char sink[1024];
+  __shared__ f32x4_t sx[1 * 4 * 2 * 64];
+  extern __shared__ float lds[];
+  constexpr bool kRingHolds = kCoreRing * core_buf_bytes(NT) >= kGemvLdsFloats * (int)sizeof(float);
+  float* plds = kRingHolds ? reinterpret_cast<float*>(ring) : lds;
+  phase_absorb_core<NT, 1, 4>(p, blockIdx.x, ring, ids, sink, sx, plds);
+}
+
 __global__ __launch_bounds__(kBlock) void k_oabsorb(StepParams p) {
   extern __shared__ float lds[];
   phase_oabsorb(p, blockIdx.x, lds);
@@ -212,6 +225,7 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   const size_t f = sizeof(float);
   const size_t frag = 2 * kAFragElems * sizeof(uint16_t);  // one (k-step, m-tile): both halves
   pl.off_zero = take(256);
+  pl.off_sync = take((size_t)(NH + 2) * 64);
   pl.off_rows = take((size_t)T * P * sizeof(int32_t));
   pl.off_a1 = take((size_t)pl.kt1 * pl.mt_pad * frag);
   pl.off_ssx = take((size_t)pl.nxc * T * f);
@@ -242,6 +256,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.nt1 = pl.nt_q + pl.nt_kv;
   choose_split(H, pl.nt1, &pl.s1, &pl.ks1);
   pl.n_idx_wg = cdiv(T * P, kBlock);
+
   pl.nt2 = cdiv(N2, kTile);
   choose_split(Q, pl.nt2, &pl.s2, &pl.ks2);
   pl.nkv = cdiv(KVR, 64);
@@ -259,6 +274,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
     pl.nsplit = cdiv(P, pl.ps);
   }
   if (T > kGemvMaxTokens) return make_plan_mfma(d, pl);
+  pl.fused = (d.flags & MLA_GD_FLAG_FUSED) && pl.core_hg == 1 && pl.core_cs == 4;
   pl.dc5 = 16;
   pl.nd5 = cdiv(DV, pl.dc5);
   pl.tc5 = std::min(T, kTT);
@@ -275,6 +291,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   };
   const size_t f = sizeof(float);
   pl.off_zero = take(256);
+  pl.off_sync = take((size_t)(NH + 2) * 64);
   pl.off_rows = take((size_t)T * P * sizeof(int32_t));
   pl.off_part1 = take((size_t)pl.s1 * T * (Q + KVR) * f);
   pl.off_ssx = take((size_t)pl.s1 * T * f);
@@ -331,12 +348,26 @@ core_kernel_t pick_core_nt(int nt) {
   }
 }
 
+core_kernel_t pick_fused(int R) {
+  switch (R / 16) {
+    case 4: return k_absorb_core<4>;
+    case 8: return k_absorb_core<8>;
+    case 16: return k_absorb_core<16>;
+    default: return k_absorb_core<32>;
+  }
+}
+
+size_t fused_dyn_lds(int R) {
+  return (size_t)kCoreRing * core_buf_bytes(R / 16) >= kGemvLdsFloats * sizeof(float) ? 0 : kGemvLdsFloats * sizeof(float);
+}
+
 core_kernel_t pick_core(const Plan& pl, int R) {
   return pl.core_hg == 1 ? pick_core_nt<1, 4>(R / 16) : pick_core_nt<4, 2>(R / 16);
 }
 
 // Kernels of a step, in launch order: the GEMV path (few tokens) and the matrix-core path.
 const char* const kKernelNamesGemv[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"};
+const char* const kKernelNamesFused[] = {"k_down", "k_qup", "k_absorb_core", "k_oabsorb", "k_oproj", "k_out"};
 const char* const kKernelNamesMfma[] = {"k_prep", "k_down", "k_qa",      "k_qup",   "k_absorb",
                                         "k_core", "k_combine", "k_oabsorb", "k_oproj", "k_out"};
 const char* const kKernelNamesMfma1[] = {"k_prep", "k_down",    "k_qa",    "k_qup", "k_absorb",
@@ -348,11 +379,13 @@ constexpr size_t kGemvLdsBytes = kGemvLdsFloats * sizeof(float);
 constexpr int kMaxLdsBytes = 160 * 1024;
 
 int num_kernels(const Plan& pl) {
+  if (pl.fused) return kNumKernelsGemv - 1;
   if (!pl.mfma) return kNumKernelsGemv;
   return pl.nsplit > 1 ? kNumKernelsMfma : kNumKernelsMfma1;
 }
 
 const char* kernel_name(const Plan& pl, int i) {
+  if (pl.fused) return kKernelNamesFused[i];
   if (!pl.mfma) return kKernelNamesGemv[i];
   return pl.nsplit > 1 ? kKernelNamesMfma[i] : kKernelNamesMfma1[i];
 }
@@ -362,6 +395,10 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
   const void* gemv[] = {(const void*)k_down, (const void*)k_qup, (const void*)k_absorb, (const void*)k_oabsorb,
                         (const void*)k_oproj, (const void*)k_out, (const void*)k_prep, (const void*)k_qa};
   for (const void* k : gemv)
+    if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
+  // fused kernels whose ring is smaller than the producers' LDS take it as dynamic LDS
+  const void* fused[] = {(const void*)k_absorb_core<4>, (const void*)k_absorb_core<8>, (const void*)k_absorb_core<16>};
+  for (const void* k : fused)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
   const void* big[] = {(const void*)k_absorb_m<1>, (const void*)k_absorb_m<2>, (const void*)k_absorb_m<4>,
                        (const void*)k_oabsorb_m<1>};
@@ -495,6 +532,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
     p.ssq = (float*)(ws + pl.off_ssq);
     p.olat = pl.nsplit > 1 ? (float*)(ws + pl.off_olat) : nullptr;
   }
+  p.sync = (unsigned*)(ws + pl.off_sync);
   p.pl = pl;
 
   hipError_t e = hipSetDevice(h->device);
@@ -512,7 +550,20 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   const dim3 blk(kBlock);
   const dim3 core_blk(64 * pl.core_hg * pl.core_cs);
   mark(0);
-  if (!pl.mfma) {
+  if (pl.fused) {
+    hipLaunchKernelGGL(k_down, dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gl, s, p);
+    mark(1);
+    hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gl, s, p);
+    mark(2);
+    hipLaunchKernelGGL(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, fused_dyn_lds(p.R), s, p);
+    mark(3);
+    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), blk, gl, s, p);
+    mark(4);
+    hipLaunchKernelGGL(k_oproj, dim3(pl.nt6 * pl.s6), blk, gl, s, p);
+    mark(5);
+    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
+    mark(6);
+  } else if (!pl.mfma) {
     hipLaunchKernelGGL(k_down, dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gl, s, p);
     mark(1);
     hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gl, s, p);

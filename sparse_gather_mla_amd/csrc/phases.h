@@ -19,6 +19,7 @@
 #pragma once
 
 #include "core_mfma.h"
+#include "mfma_util.h"
 #include "device_util.h"
 #include "gemv.h"
 #include "step_params.h"
@@ -52,12 +53,48 @@ __device__ __forceinline__ void index_build(const StepParams& p, int idx) {
 }
 
 // ---------------------------------------------------------------------------
+// Counters of the fused variant.  A producer workgroup publishes its stores
+// with a device-scope release and one atomic increment; a consumer polls with
+// relaxed device-scope loads (bounded: after kSpinLimit polls it raises the
+// error flag and goes on, so no wait can hang) and then fences before reading.
+// Producers always have lower workgroup indices than their consumers and never
+// wait themselves, so in-order dispatch guarantees progress.
+// ---------------------------------------------------------------------------
+constexpr int kSyncStride = 16;  // counters 64 bytes apart
+constexpr int kSpinLimit = 1 << 20;
+
+// The barrier completes every wave's stores; one device-scope fence then
+// writes the XCD's L2 back (it is shared by the workgroup's waves).
+__device__ __forceinline__ void count_done(unsigned* c) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Polls with relaxed device-scope loads (an acquire load would invalidate the
+// caches on every poll); the caller fences once after the wait.
+__device__ __forceinline__ void wait_count(const unsigned* c, unsigned target, unsigned* err) {
+  for (int it = 0; __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++it) {
+    if (it >= kSpinLimit) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_down: index build; (x * g_in) @ [wq_a | wkv_a] split-K partials; sums of x^2
 // ---------------------------------------------------------------------------
 __device__ void phase_down(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
   const int T = pl.T;
   const int n_gemv = pl.nt1 * pl.s1;
+  // the fused variant's counters start each step at zero (this step's later
+  // kernels run after this one; the previous step's have finished)
+  if (pl.fused && b == 0 && (int)threadIdx.x < p.NH + 2) p.sync[threadIdx.x * kSyncStride] = 0u;
   if (b >= n_gemv) {
     index_build(p, (b - n_gemv) * kBlock + threadIdx.x);
     return;
@@ -236,6 +273,55 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
     }
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// k_absorb_core (fused variant, <= 16 heads): workgroups [0, T) finish the kv
+// rows, [T, T + NH*ncc3) run the absorption tiles, the rest run the core.  A
+// core workgroup waits for every kv row before it reads the cache (a token may
+// select its own position), issues its first row loads, then waits for its
+// heads' query tiles.  The producers work in `plds` (the core's ring when it
+// is large enough).
+// ---------------------------------------------------------------------------
+template <int NT, int HG, int CS>
+struct CoreWaitFused {
+  const StepParams& p;
+  // one wave polls, fences (invalidating the CU's L1 and stale L2 lines for
+  // every wave of the workgroup), then releases the others at the barrier
+  __device__ void before_rows(int) const {
+    if (threadIdx.x == 0) {
+      wait_count(p.sync, (unsigned)p.pl.T, p.sync + kSyncStride);
+      __threadfence();
+    }
+    __syncthreads();
+  }
+  __device__ void before_q(int h0) const {
+    const int i = threadIdx.x;
+    if (i < 64) {
+      if (i < 16 * HG && h0 + i < p.NH)
+        wait_count(p.sync + (2 + h0 + i) * kSyncStride, (unsigned)p.pl.ncc3, p.sync + kSyncStride);
+      __threadfence();  // after every polling lane of the wave is done
+    }
+    __syncthreads();
+  }
+};
+
+template <int NT, int HG, int CS>
+__device__ void phase_absorb_core(const StepParams& p, int b, char* ring, int* ids, char* sink, f32x4_t* sx,
+                                  float* plds) {
+  const Plan& pl = p.pl;
+  const int T = pl.T, n_abs = p.NH * pl.ncc3;
+  if (b < T) {  // kv row of token b
+    phase_absorb(p, n_abs + b, plds);
+    count_done(p.sync);
+    return;
+  }
+  if (b < T + n_abs) {
+    phase_absorb(p, b - T, plds);
+    count_done(p.sync + (2 + (b - T) / pl.ncc3) * kSyncStride);
+    return;
+  }
+  core_phase<NT, HG, CS>(p, b - T - n_abs, ring, ids, sink, sx, CoreWaitFused<NT, HG, CS>{p});
 }
 
 // ---------------------------------------------------------------------------

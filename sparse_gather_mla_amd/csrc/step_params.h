@@ -24,6 +24,8 @@ struct Plan {
   int nt6, s6, ks6;
   // k_out: 64-column groups x token chunks
   int n7;
+  // fused variant: one launch for the kv-row write, the absorption and the core
+  int fused;
   // Matrix-core path (more than a few tokens).  Token blocks of mtb m-tiles
   // (16 tokens each), ntb blocks, m-tiles padded to mt_pad = ntb*mtb.  For each
   // projection: kt* k-steps of 32 in all, ks* per slab, 64-column tiles.
@@ -39,6 +41,7 @@ struct Plan {
   size_t off_zero, off_rows, off_part1, off_ssx, off_part2, off_ssq, off_kvr, off_kvss, off_qcat;
   size_t off_pm, off_pl, off_po, off_ov, off_part6;
   size_t off_a1, off_a2, off_a5, off_olat;
+  size_t off_sync;  // fused variant's counters (same offset for every n_tokens)
   size_t total;
 };
 
@@ -87,6 +90,9 @@ struct StepParams {
   uint16_t* a2;     // acc_q * g_q            [kt2][mt_pad][2][512]
   uint16_t* a5;     // o_v                    [kt6][mt_pad][2][512]
   float* olat;      // [T][NH][R] combined, normalised latent outputs (when nsplit > 1)
+  // fused variant: counters kSyncStride words apart -- [0] kv rows written,
+  // [1] error flag (a wait timed out), [2 + h] absorption tiles of head h done
+  unsigned* sync;
   Plan pl;
 };
 

@@ -168,3 +168,37 @@ def test_kernel_lists_of_both_paths(lib):
         assert all(b >= a for a, b in zip(sizes, sizes[1:]))
     finally:
         lib.mla_gather_decode_destroy(h)
+
+
+
+def test_fused_flag_kernel_list(lib):
+    """The fused variant replaces k_absorb + k_core by one launch on the GEMV
+    path (up to 16 heads); more heads, or steps on the matrix-core path, keep
+    the separate kernels."""
+    c = _codes()
+
+    def names(h, T):
+        n = lib.mla_gather_decode_kernel_count(h, T)
+        return [lib.mla_gather_decode_kernel_name(h, T, i).decode() for i in range(n)]
+
+    rc, h = _create(lib, _dims(max_tokens=12, flags=c["MLA_GD_FLAG_FUSED"]))
+    assert rc == 0
+    try:
+        assert names(h, 1) == ["k_down", "k_qup", "k_absorb_core", "k_oabsorb", "k_oproj", "k_out"]
+        assert names(h, 8) == names(h, 1)
+        assert "k_absorb_core" not in names(h, 9) and "k_core" in names(h, 9)
+        # the counters live in the workspace, so fused and separate sizes agree
+        rc2, h2 = _create(lib, _dims(max_tokens=12))
+        assert rc2 == 0
+        try:
+            assert lib.mla_gather_decode_workspace_size(h, 12) == lib.mla_gather_decode_workspace_size(h2, 12)
+        finally:
+            lib.mla_gather_decode_destroy(h2)
+    finally:
+        lib.mla_gather_decode_destroy(h)
+    rc, h = _create(lib, _dims(n_heads=20, flags=c["MLA_GD_FLAG_FUSED"]))
+    assert rc == 0
+    try:
+        assert "k_core" in names(h, 1) and "k_absorb_core" not in names(h, 1)
+    finally:
+        lib.mla_gather_decode_destroy(h)

@@ -110,6 +110,48 @@ def test_parity_ragged_shape_matrix_core_path(T):
     _run_and_check(wl)
 
 
+# ---------------------------------------------------------------------------
+# the fused variant: kv rows, absorption and core in one launch (<= 16 heads, <= 8 tokens)
+# ---------------------------------------------------------------------------
+def _fused_error_word(mod):
+    # the fused counters sit right after the workspace's first 256 bytes, 64 bytes apart;
+    # the second one is the error flag a timed-out wait raises
+    return int(mod.workspace.view(torch.int32)[(256 + 64) // 4].item())
+
+
+@pytest.mark.parametrize("name", ["tiny", "ds32_slice"])
+def test_parity_fused_variant(name):
+    wl = next(w for w in CONFIGS if w.name == name)
+    sh = wl.shape
+    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens, fused=True)
+    assert "k_absorb_core" in mod.kernel_names(sh.n_tokens)
+    _run_and_check(wl, fused=True)
+
+
+def test_fused_variant_self_row_and_all_masked():
+    """A token that selects its own position must see this step's row: the
+    fused core waits for the kv-row counter before it reads the cache."""
+    out, ref, inp, g = _run_and_check(TINY, fused=True, mutate=_self_row_and_all_masked)
+    assert torch.count_nonzero(out[1]).item() == 0
+
+
+def test_fused_variant_counters_and_repeat():
+    """Repeated fused steps give the same bits and never raise the wait-timeout flag."""
+    wl = TINY
+    sh = wl.shape
+    inp = make_inputs(wl, with_pool=False)
+    g = gpu_inputs(wl, inp)
+    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens, fused=True)
+    sep = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens)
+    outs = [mod(g).clone() for _ in range(3)]
+    ref = sep(g).clone()
+    torch.cuda.synchronize()
+    assert _fused_error_word(mod) == 0
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    ok, err, bound = within_tol(bf16_to_f64(outs[0]), bf16_to_f64(ref))
+    assert ok, (err, bound)
+
+
 def test_parity_tiny_shape_matrix_core_path():
     """Smallest dims (hidden 256, kv_lora_rank 64, 4 heads) with 24 tokens and the tiny recipe."""
     wl = replace(CONFIGS[0], name="tiny_T24", shape=replace(CONFIGS[0].shape, n_tokens=24),
