@@ -17,8 +17,13 @@
 //
 // Rows reach LDS through a ring of three 32-row buffers filled by direct
 // global-to-LDS loads two chunks ahead (no staging registers); the chunk's
-// flat row ids are read from LDS, staged once per workgroup.  Inside a buffer, row r keeps its 16-byte
-// pieces XOR-swizzled by (r mod sw) to spread LDS banks.
+// flat row ids are read from LDS, staged once per workgroup.  A buffer row
+// spans an odd number of 16-byte pieces (whole k-steps, zero past kv_row, then
+// one pad piece), so 16 rows read at one column fall on distinct LDS banks and
+// every fragment address is a per-lane base plus a compile-time offset.
+// Masked rows load zeros and get a -inf score bias, written once per chunk.
+// Query tiles arrive pre-scaled by softmax_scale * log2(e), so scores are in
+// the log2 domain as they leave the matrix cores.
 #pragma once
 
 #include "device_util.h"
@@ -32,14 +37,28 @@ constexpr int kCoreRing = 3;    // chunk buffers in flight
 
 constexpr int kMaxSplitRows = 4096;  // row ids staged in LDS per core workgroup
 
-// Bytes of one ring buffer for a latent width of 16*NT (kv_row <= 16*NT + 64).
-__host__ __device__ constexpr int core_buf_bytes(int nt) { return kCoreChunk * (2 * nt + 8) * 16; }
+// 16-byte pieces per LDS row for a latent width of 16*nt: whole 32-wide
+// k-steps over kv_row <= 16*nt + 64, made odd.  A buffer is rounded up to
+// whole 1 KB (64 slots), so the last wave load of a chunk, which may run past
+// the chunk's slots, stays inside its buffer.
+__host__ __device__ constexpr int core_row_pieces(int nt) { return (2 * nt + 8) | 1; }
+__host__ __device__ constexpr int core_buf_bytes(int nt) { return (kCoreChunk * core_row_pieces(nt) * 16 + 1023) / 1024 * 1024; }
 
-// NT: latent width / 16.  HG: head groups of 16 per workgroup.  CS: column
-// splits.  The CS waves of a head group each own NT/CS output tiles; they
-// split the score's k-steps between them and add their partial score tiles
-// through LDS (`sx`), so every wave of the group holds the same scores and
-// the same softmax state.  The workgroup has HG*CS waves.
+// LDS of a core workgroup, carved from one array: ring | row ids | sink |
+// partial score tiles (HG*CS*128 x 16 B) | score bias (kCoreRing x 32 floats).
+__host__ __device__ constexpr int core_ofs_ids(int nt) { return kCoreRing * core_buf_bytes(nt); }
+__host__ __device__ constexpr int core_ofs_sink(int nt) { return core_ofs_ids(nt) + kMaxSplitRows * 4; }
+__host__ __device__ constexpr int core_ofs_sx(int nt) { return core_ofs_sink(nt) + 1024; }
+__host__ __device__ constexpr int core_ofs_bias(int nt, int hg, int cs) { return core_ofs_sx(nt) + hg * cs * 128 * 16; }
+__host__ __device__ constexpr int core_lds_bytes(int nt, int hg, int cs) {
+  return core_ofs_bias(nt, hg, cs) + kCoreRing * kCoreChunk * 4;
+}
+
+// Lane permutes with precomputed byte addresses (ds_bpermute).
+__device__ __forceinline__ float bperm(int addr, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, v)));
+}
+
 // Hooks of the separately launched core: every input is complete at kernel start.
 struct CoreNoWait {
   __device__ void before_rows(int) const {}
@@ -49,22 +68,34 @@ struct CoreNoWait {
 // Hooks: before_rows(token) runs before the first read of the row ids or the
 // cache; before_q(first head) after the first row loads are issued and before
 // the query tiles are read.  Every thread of the workgroup calls both.
+// NT: latent width / 16.  HG: head groups of 16 per workgroup.  CS: column
+// splits.  The CS waves of a head group each own NT/CS output tiles; they
+// split the score's k-steps between them and add their partial score tiles
+// through LDS (`sx`), so every wave of the group holds the same scores and
+// the same softmax state.  The workgroup has HG*CS waves.  `lds` holds
+// core_lds_bytes(NT, HG, CS) bytes, 16-byte aligned.
 template <int NT, int HG, int CS, class Hooks = CoreNoWait>
-__device__ __attribute__((always_inline)) void core_phase(const StepParams& p, int b, char* ring, int* ids,
-                                                          char* sink, f32x4_t* sx, const Hooks& hooks = Hooks()) {
+__device__ __attribute__((always_inline)) void core_phase(const StepParams& p, int b, char* lds,
+                                                          const Hooks& hooks = Hooks()) {
+  char* ring = lds;
+  int* ids = reinterpret_cast<int*>(lds + core_ofs_ids(NT));
+  char* sink = lds + core_ofs_sink(NT);
+  f32x4_t* sx = reinterpret_cast<f32x4_t*>(lds + core_ofs_sx(NT));
+  float* bias = reinterpret_cast<float*>(lds + core_ofs_bias(NT, HG, CS));
   constexpr int NW = HG * CS;
   constexpr int NTW = NT / CS;       // output tiles (16 columns) per wave
   constexpr int KSMAX = NT / 2 + 2;  // 32-wide k-steps over kv_row = 16*NT + DR, DR <= 64
   constexpr int KSW = (KSMAX + CS - 1) / CS;  // score k-steps per wave
-  constexpr int NPMAX = 2 * NT + 8;  // 16-byte pieces per row, upper bound (a multiple of 4)
+  constexpr int NPMAX = core_row_pieces(NT);
   constexpr int NI = (kCoreChunk * NPMAX + 64 * NW - 1) / (64 * NW);  // loads per wave per chunk
+  constexpr int BUF = core_buf_bytes(NT);
   const Plan& pl = p.pl;
   const int KVR = p.KVR;
-  const int ks = (KVR + 31) >> 5;          // score k-steps (32 columns = 4 pieces each)
-  const int npieces = KVR >> 3;            // 16-byte pieces of a cache row
-  const int npad = ks * 4;                 // 16-byte slots per row in LDS (<= NPMAX)
-  const int sw = (npad % 8 == 0) ? 8 : 4;  // swizzle period (npad is a multiple of 4)
-  const int slots = kCoreChunk * npad;     // 16-byte slots per chunk
+  const int ks = (KVR + 31) >> 5;    // score k-steps
+  const int npieces = KVR >> 3;      // 16-byte pieces of a cache row
+  const int npad = (4 * ks) | 1;     // LDS row stride in pieces (odd, <= NPMAX)
+  const int rstride = npad * 16;
+  const int slots = kCoreChunk * npad;
 
   // Workgroups of the same (token, split) but different head blocks sit 8
   // block indices apart, so they land on the same XCD and share the gathered
@@ -90,15 +121,15 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
     ids[i] = (i < nrows) ? p.rows[(size_t)t * p.P + j0 + i] : -1;
   __syncthreads();  // row ids visible
 
-  // this wave's k-steps: kk = kb + j, j < KSW; steps at or past ks carry zero
-  // Q fragments and read a valid slot (step ks-1), so they add exactly zero
+  // this wave's k-steps: kk = kb + j for j < nj (nj may be smaller than KSW)
   const int kb = cs * KSW;
+  const int nj = min(KSW, ks - kb);
 
-  // direct global->LDS load of chunk c into ring buffer c % kCoreRing.  Every
-  // wave issues exactly NI loads per chunk (those past the chunk read the zero
-  // row into the sink) so that the vmcnt arithmetic below is static.
-  // Per-lane geometry of those loads, the same for every chunk: the row inside
-  // the chunk (-1: nothing to load) and the byte offset of the piece in a row.
+  // Direct global->LDS loads of chunk c into ring buffer c % kCoreRing.  Every
+  // wave issues exactly NI loads per chunk (slots past the buffer go to the
+  // sink) so that the vmcnt arithmetic below is static.  Per-lane geometry,
+  // the same for every chunk: the row inside the chunk of the piece this lane
+  // loads (-1: zeros) and its byte offset in the cache row.
   int lrow[NI], lofs[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -106,26 +137,30 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
     lrow[i] = -1;
     lofs[i] = 0;
     if (s < slots) {
-      const int r = s / npad, pc = (s % npad) ^ (r % sw);
+      const int r = s / npad, pc = s % npad;
       if (pc < npieces) {
         lrow[i] = r;
         lofs[i] = pc * 16;
       }
     }
   }
-  const size_t row_bytes = (size_t)KVR * 2;
+  const unsigned row_bytes = (unsigned)KVR * 2u;
   auto issue_chunk = [&](int c) {
-    char* buf = ring + (c % kCoreRing) * core_buf_bytes(NT);
+    const int bsel = c % kCoreRing;
+    char* buf = ring + bsel * BUF;
+    const bool live = c < nchunks;
     const int* cid = ids + min(c, nchunks - 1) * kCoreChunk;
+    if (wave == 0 && lane < kCoreChunk) bias[bsel * kCoreChunk + lane] = (live && cid[lane] >= 0) ? 0.f : -INFINITY;
+    int rid[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) rid[i] = cid[max(lrow[i], 0)];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int s0 = (i * NW + wave) * 64;  // first slot of this load
+      const int s0 = (i * NW + wave) * 64;  // first slot of this load (wave-uniform)
       const char* src = reinterpret_cast<const char*>(p.zero16);
-      if (c < nchunks && lrow[i] >= 0) {
-        const int rid = cid[lrow[i]];
-        if (rid >= 0) src = reinterpret_cast<const char*>(p.cache) + (size_t)(unsigned)rid * row_bytes + lofs[i];
-      }
-      dma16(src, (s0 < slots) ? buf + s0 * 16 : sink);
+      if (live && lrow[i] >= 0 && rid[i] >= 0)
+        src = reinterpret_cast<const char*>(p.cache) + (size_t)(unsigned)rid[i] * row_bytes + lofs[i];
+      dma16(src, (s0 < slots) ? buf + s0 * 16 : sink);  // lanes past `slots` stay inside the 1 KB-rounded buffer
     }
   };
 
@@ -144,7 +179,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   for (int j = 0; j < KSW; ++j) {
     const int k = 32 * (kb + j) + 8 * g;
     u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (kb + j < ks && head < p.NH && k < KVR)
+    if (j < nj && head < p.NH && k < KVR)
       v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * p.NH + head) * KVR + k);
     qf[j] = __builtin_bit_cast(bf16x8_t, v);
   }
@@ -152,43 +187,57 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   // so nothing but ring loads is outstanding below
   wait_vmcnt<0>();
 
+  // LDS-space views (addresses fold into the instructions' offset fields)
+  const lds_char_t* lring = (const lds_char_t*)ring;
+  const lds_char_t* lbias = (const lds_char_t*)bias;
+  // per-lane LDS offsets: score fragments (rows l16 and 16+l16, pieces 4*kk+g)
+  // and value fragments (rows r1 and r1+16, this wave's output columns)
+  const int sofs = l16 * rstride + 16 * g + 64 * kb;
+  const int r1 = 4 * g + (l16 >> 2);
+  const int vofs = r1 * rstride + 8 * (l16 & 3) + 32 * (cs * NTW);
+  const int rs16 = 16 * rstride;
+  const int px16 = (lane ^ 16) << 2, px32 = (lane ^ 32) << 2;
+
   for (int c = 0; c < nchunks; ++c) {
     // chunk c's loads are this wave's oldest; the younger chunk may stay in flight
     wait_vmcnt<NI * (kCoreRing - 2)>();
     __syncthreads();  // chunk c visible to every wave; buffer (c-1) % ring consumed
     issue_chunk(c + kCoreRing - 1);
-    const char* buf = ring + (c % kCoreRing) * core_buf_bytes(NT);
-    const int* cid = ids + c * kCoreChunk;
-    // scores: tile A rows 0-15, tile B rows 16-31; lane l reads row l16 (+16), piece 4*kk + g
+    const int bsel = c % kCoreRing;
+    const lds_char_t* buf = lring + bsel * BUF;
+    // scores: tile A rows 0-15, tile B rows 16-31, fragments loaded two steps ahead
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
-      // this wave's k-steps, fragments loaded two steps ahead of the MFMAs
-      const int ra = l16, rb = 16 + l16;
-      const int xa = ra % sw, xb = rb % sw;
-      const char* rowa = buf + ra * npad * 16;
-      const char* rowb = buf + rb * npad * 16;
-      auto frag = [&](const char* row, int x, int j) {
-        const int pc = 4 * min(kb + j, ks - 1) + g;
-        return *reinterpret_cast<const bf16x8_t*>(row + (pc ^ x) * 16);
-      };
-      bf16x8_t fa0 = frag(rowa, xa, 0), fb0 = frag(rowb, xb, 0);
-      bf16x8_t fa1 = fa0, fb1 = fb0;
-      if (KSW > 1) {
-        fa1 = frag(rowa, xa, 1);
-        fb1 = frag(rowb, xb, 1);
-      }
-#pragma unroll
-      for (int j = 0; j < KSW; ++j) {
-        bf16x8_t fa2 = fa1, fb2 = fb1;
-        if (j + 2 < KSW) {
-          fa2 = frag(rowa, xa, j + 2);
-          fb2 = frag(rowb, xb, j + 2);
+      const lds_char_t* pa = buf + sofs;
+      const lds_char_t* pb = pa + rs16;
+      auto ld = [&](const lds_char_t* q, int j) { return *(const lds_bf16x8_t*)(q + 64 * j); };
+      if (nj == KSW) {  // every k-step of this wave is live (uniform branch)
+        bf16x8_t fa0 = ld(pa, 0), fb0 = ld(pb, 0), fa1 = fa0, fb1 = fb0;
+        if (KSW > 1) {
+          fa1 = ld(pa, 1);
+          fb1 = ld(pb, 1);
         }
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, qf[j], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb0, qf[j], sb, 0, 0, 0);
-        fa0 = fa1; fb0 = fb1;
-        fa1 = fa2; fb1 = fb2;
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < KSW; ++j) {
+          bf16x8_t fa2 = fa1, fb2 = fb1;
+          if (j + 2 < KSW) {
+            fa2 = ld(pa, j + 2);
+            fb2 = ld(pb, j + 2);
+          }
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, qf[j], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb0, qf[j], sb, 0, 0, 0);
+          fa0 = fa1; fb0 = fb1;
+          fa1 = fa2; fb1 = fb2;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {  // the last column split of a short row: fewer live k-steps
+#pragma unroll
+        for (int j = 0; j < KSW; ++j) {
+          if (j < nj) {
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld(pa, j), qf[j], sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld(pb, j), qf[j], sb, 0, 0, 0);
+          }
+        }
       }
     }
     if constexpr (CS > 1) {
@@ -206,32 +255,38 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
         sb += grp[w * 128 + 64 + lane];
       }
     }
+    // rows 4g+i (tile A) and 16+4g+i (tile B): masked rows carry -inf
+    const f32x4_t ba = *(const lds_f32x4_t*)(lbias + 4 * (bsel * kCoreChunk + 4 * g));
+    const f32x4_t bb = *(const lds_f32x4_t*)(lbias + 4 * (bsel * kCoreChunk + 16 + 4 * g));
     float s[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s[i] = (cid[4 * g + i] >= 0) ? sa[i] * p.scale_log2 : -INFINITY;
-      s[4 + i] = (cid[16 + 4 * g + i] >= 0) ? sb[i] * p.scale_log2 : -INFINITY;
+      s[i] = sa[i] + ba[i];
+      s[4 + i] = sb[i] + bb[i];
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    mx = fmaxf(mx, bperm(px16, mx));
+    mx = fmaxf(mx, bperm(px32, mx));
     // Lazy rescaling: the reference maximum m_run (log2 domain) moves only when
     // a chunk's maximum exceeds it by more than 8, so probabilities stay below
     // 2^8 and most chunks leave the accumulators alone.  The result is exact:
     // (m, l, o) are kept consistent with whatever reference is in use.
     float alpha = 1.f;
     if (mx > m_run + 8.f) {  // also the first valid chunk (m_run = -inf)
-      alpha = exp2f(m_run - mx);  // m_run = -inf gives 0
+      alpha = __builtin_amdgcn_exp2f(m_run - mx);  // m_run = -inf gives 0
       m_run = mx;
     }
     float pr[8];
+    if (m_run != -INFINITY) {  // the same in every lane: all heads see the same valid rows
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pr[i] = (m_run == -INFINITY) ? 0.f : exp2f(s[i] - m_run);  // masked: 0
+      for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(s[i] - m_run);  // masked: exp2(-inf) = 0
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pr[i] = 0.f;
+    }
     float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-    ps += __shfl_xor(ps, 16, kWave);
-    ps += __shfl_xor(ps, 32, kWave);
+    ps += bperm(px16, ps);
+    ps += bperm(px32, ps);
     l_run = l_run * alpha + ps;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // wave-uniform
       // rescale: lane l holds heads 4g+i of each output tile
@@ -247,16 +302,11 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
     bf16x8_t pab;
 #pragma unroll
     for (int i = 0; i < 8; ++i) pab[i] = (__bf16)pr[i];
-    const int r1 = 4 * g + (l16 >> 2), r2 = 16 + r1;
-    const int x1 = r1 % sw, x2 = r2 % sw;
-    const char* row1 = buf + r1 * npad * 16;
-    const char* row2 = buf + r2 * npad * 16;
-    const int cofs = 4 * (l16 & 3);  // column offset inside the 16-column tile
+    // 32-bit LDS addresses of this lane's value fragments (tile n adds 32*n bytes)
+    const unsigned av = (unsigned)(uintptr_t)(buf + vofs), av2 = av + (unsigned)rs16;
     auto vfrag = [&](int n) {
-      const int col = 16 * (cs * NTW + n) + cofs;
-      const int pc = col >> 3, within = (col & 7) * 2;
-      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(row1 + (pc ^ x1) * 16 + within));
-      const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(row2 + (pc ^ x2) * 16 + within));
+      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(av + 32u * n));
+      const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(av2 + 32u * n));
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     bf16x8_t vf = vfrag(0);

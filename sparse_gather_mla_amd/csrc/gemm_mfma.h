@@ -8,17 +8,17 @@
 // meet the weight (two MFMAs per fragment): about 16 significant bits.  The
 // projections stay bound by the weight stream even with the matrix work doubled.
 //
-// Tiles: 16 tokens (an m-tile) x 64 columns x 32 k (a k-step).  A workgroup
-// of four waves owns one 64-column tile, one K slab and a block of MTB
-// m-tiles; the waves split the block 2 x 2 (1 x 4 for a single m-tile).
+// Tiles: 16 tokens (an m-tile) x NC columns (64 or 128) x 32 k (a k-step).  A
+// workgroup of four waves owns one NC-column tile, one K slab and a block of
+// MTB m-tiles; the waves split the block 2 x 2 (1 x 4 for a single m-tile).
 //
 // Both operands reach LDS through direct global->LDS loads into a ring of
 // kMgDepth k-steps, so the main loop holds no compiler-visible global load and
 // its only waits are the ring's explicit vmcnt waits.
 //   A comes from the previous kernel already in fragment order: for every
 //     (k-step, m-tile, half) a 1 KB block with lane l's eight bf16 at 16*l.
-//   B is the 32 x 64 weight tile; row r keeps its 16-byte pieces XOR-swizzled
-//     by r mod 8.  Transposing LDS reads (ds_read_b64_tr_b16) hand each lane
+//   B is the 32 x NC weight tile; row r keeps its 16-byte pieces XOR-swizzled
+//     (low three bits) by r mod 8.  Transposing LDS reads (ds_read_b64_tr_b16) hand each lane
 //     four consecutive k of one column, twice per fragment.
 // Contraction order inside a k-step: lane group g (= lane / 16) carries
 // k = 4g..4g+3 and 16+4g..16+4g+3, the order the transposing read delivers;
@@ -83,16 +83,21 @@ __device__ __forceinline__ void put_a4_lds(char* ares, int mtb, int tt, int k, c
   *reinterpret_cast<uint2*>(blk + kAFragElems * 2 + e * 2) = lo;
 }
 
-template <int MTB>
+// Columns per GEMM tile: 64 for one m-tile, 128 for larger token blocks (the
+// wider tile halves the activation bytes streamed per weight byte).
+__host__ __device__ constexpr int mg_cols(int mtb) { return mtb >= 2 ? 128 : 64; }
+
+template <int MTB, int NC = mg_cols(MTB)>
 struct Mg {
   static constexpr int WM = MTB >= 2 ? 2 : 1;  // waves along tokens
   static constexpr int WN = 4 / WM;            // waves along columns
   static constexpr int MTW = MTB / WM;         // m-tiles per wave
-  static constexpr int NTW = 4 / WN;           // 16-column n-tiles per wave
+  static constexpr int NTW = NC / 16 / WN;     // 16-column n-tiles per wave
   static constexpr int kABytes = MTB * 2 * kAFragElems * 2;
-  static constexpr int kBBytes = kMgK * kMgCols * 2;
+  static constexpr int kBBytes = kMgK * NC * 2;
   static constexpr int kStep = kABytes + kBBytes;
   static constexpr int kADma = (MTB * 128 + 255) / 256;  // A pieces per lane per step
+  static constexpr int kBDma = NC / 64;                  // B pieces per lane per step
   static constexpr int kRing = kMgDepth * kStep;
 };
 
@@ -106,29 +111,45 @@ __device__ __forceinline__ bool mg_unit(int b, int nunits, int ntb, int& u, int&
   return u < nunits;
 }
 
-// Source of this lane's piece of a 32 x 64 weight tile at k-step 0.
+// Swizzled 16-byte slot of piece pc in row r of a weight tile: the low three
+// bits are XORed with r mod 8 (transposing reads of four rows hit distinct banks).
+__device__ __forceinline__ int bswz(int pc, int r) { return (pc & ~7) | ((pc & 7) ^ (r & 7)); }
+
+// Sources of this lane's pieces of a 32 x NC weight tile at k-step 0.
+template <int NC>
 struct BTileSrc {
-  const bf16_t* p;  // nullptr: the piece's columns lie past N
-  size_t step;      // elements per k-step
-  int row, K;       // the piece's row at k-step 0; rows >= K read zeros
+  const bf16_t* p[NC / 64];  // nullptr: the piece's columns lie past N
+  int row[NC / 64];          // the piece's row at k-step 0; rows >= K read zeros
+  size_t step;               // elements per k-step
+  int K;
 };
 
-__device__ __forceinline__ BTileSrc btile_src(const bf16_t* W, int K, int N, int k0, int c0) {
-  const int L = threadIdx.x, r = L >> 3, pc = (L & 7) ^ (r & 7);
-  const int col = c0 + 8 * pc;
-  BTileSrc s;
-  s.p = (col < N) ? W + (size_t)(k0 + r) * N + col : nullptr;
+template <int NC>
+__device__ __forceinline__ BTileSrc<NC> btile_src(const bf16_t* W, int K, int N, int k0, int c0) {
+  BTileSrc<NC> s;
+#pragma unroll
+  for (int i = 0; i < NC / 64; ++i) {
+    const int q = i * 256 + threadIdx.x;  // LDS slot of this piece
+    const int r = q / (NC / 8), pc = bswz(q % (NC / 8), r);
+    const int col = c0 + 8 * pc;
+    s.p[i] = (col < N) ? W + (size_t)(k0 + r) * N + col : nullptr;
+    s.row[i] = k0 + r;
+  }
   s.step = (size_t)kMgK * N;
-  s.row = k0 + r;
   s.K = K;
   return s;
 }
 
-// One direct load per lane: k-step st of the weight tile into bufB (4 KB).
-__device__ __forceinline__ void issue_btile(const BTileSrc& s, int st, bool live, char* bufB, const void* zero16) {
-  const void* src = zero16;
-  if (live && s.p && s.row + kMgK * st < s.K) src = s.p + s.step * st;
-  dma16(src, bufB + (threadIdx.x >> 6) * 1024);
+// NC/64 direct loads per lane: k-step st of the weight tile into bufB.
+template <int NC>
+__device__ __forceinline__ void issue_btile(const BTileSrc<NC>& s, int st, bool live, char* bufB,
+                                            const void* zero16) {
+#pragma unroll
+  for (int i = 0; i < NC / 64; ++i) {
+    const void* src = zero16;
+    if (live && s.p[i] && s.row[i] + kMgK * st < s.K) src = s.p[i] + s.step * st;
+    dma16(src, bufB + (i * 256 + (threadIdx.x & ~63)) * 16);
+  }
 }
 
 // kADma direct loads per lane: the MTB m-tiles of k-step ks (both halves, contiguous) into bufA.
@@ -147,22 +168,22 @@ __device__ __forceinline__ void issue_atile(const bf16_t* A, int mt_pad, int mt0
 }
 
 // One k-step: B fragments by transposing reads, A fragments (hi, lo), MFMAs.
-template <int MTB>
+template <int MTB, int NC>
 __device__ __forceinline__ void mg_step(const char* bufA, const char* bufB,
-                                        f32x4_t (&acc)[Mg<MTB>::MTW][Mg<MTB>::NTW]) {
-  using S = Mg<MTB>;
+                                        f32x4_t (&acc)[Mg<MTB, NC>::MTW][Mg<MTB, NC>::NTW]) {
+  using S = Mg<MTB, NC>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::WN, wn = wave % S::WN;
   const int g = lane >> 4, l16 = lane & 15;
-  const int r1 = 4 * g + (l16 >> 2), x = r1 & 7;
+  const int r1 = 4 * g + (l16 >> 2);
   const int within = 8 * (l16 & 1);
   bf16x8_t bfr[S::NTW];
 #pragma unroll
   for (int nt = 0; nt < S::NTW; ++nt) {
     const int pc = 2 * (wn * S::NTW + nt) + ((l16 & 3) >> 1);
-    const char* a1 = bufB + r1 * 128 + ((pc ^ x) << 4) + within;
+    const char* a1 = bufB + r1 * (2 * NC) + (bswz(pc, r1) << 4) + within;  // rows r1 and r1+16 share r mod 8
     const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
-    const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 16 * 128));
+    const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 16 * (2 * NC)));
     bfr[nt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 #pragma unroll
@@ -182,62 +203,63 @@ __device__ __forceinline__ void mg_step(const char* bufA, const char* bufB,
 // direct loads per lane for step st (loads of zeros once st >= nsteps);
 // step(st, buf) consumes a landed step.  Returns with every load landed and
 // the ring free.
-// The ring's first kMgDepth-1 steps; issue them as early as possible (before
+// The ring's first DEPTH-1 steps; issue them as early as possible (before
 // work the loop does not depend on), then run mg_ring_loop.
-template <class Issue>
+template <int DEPTH = kMgDepth, class Issue>
 __device__ __forceinline__ void mg_ring_prologue(char* ring, int step_bytes, Issue&& issue) {
 #pragma unroll
-  for (int s = 0; s < kMgDepth - 1; ++s) issue(s, ring + s * step_bytes);
+  for (int s = 0; s < DEPTH - 1; ++s) issue(s, ring + s * step_bytes);
 }
 
-template <int NDMA, class Issue, class Step>
+template <int NDMA, int DEPTH = kMgDepth, class Issue, class Step>
 __device__ __forceinline__ void mg_ring_loop(int nsteps, char* ring, int step_bytes, Issue&& issue, Step&& step) {
+  static_assert(NDMA * (DEPTH - 2) < 64, "vmcnt range");
   for (int s = 0; s < nsteps; ++s) {
-    wait_vmcnt<NDMA * (kMgDepth - 2)>();  // step s landed (this wave's oldest loads)
-    __syncthreads();                      // ... for every wave; buffer of step s-1 consumed
-    const int sn = s + kMgDepth - 1;
-    issue(sn, ring + (sn % kMgDepth) * step_bytes);
-    step(s, ring + (s % kMgDepth) * step_bytes);
+    wait_vmcnt<NDMA * (DEPTH - 2)>();  // step s landed (this wave's oldest loads)
+    __syncthreads();                   // ... for every wave; buffer of step s-1 consumed
+    const int sn = s + DEPTH - 1;
+    issue(sn, ring + (sn % DEPTH) * step_bytes);
+    step(s, ring + (s % DEPTH) * step_bytes);
   }
   wait_vmcnt<0>();
   __syncthreads();
 }
 
-template <int NDMA, class Issue, class Step>
+template <int NDMA, int DEPTH = kMgDepth, class Issue, class Step>
 __device__ __forceinline__ void mg_ring(int nsteps, char* ring, int step_bytes, Issue&& issue, Step&& step) {
-  mg_ring_prologue(ring, step_bytes, issue);
-  mg_ring_loop<NDMA>(nsteps, ring, step_bytes, issue, step);
+  mg_ring_prologue<DEPTH>(ring, step_bytes, issue);
+  mg_ring_loop<NDMA, DEPTH>(nsteps, ring, step_bytes, issue, step);
 }
 
-// acc = A[token block] @ W[k0 : k0 + 32*nks, c0 : c0 + 64] with A from a
+// acc = A[token block] @ W[k0 : k0 + 32*nks, c0 : c0 + NC] with A from a
 // global fragment-order buffer (its m-tiles mt0 .. mt0+MTB-1).
-template <int MTB>
+template <int MTB, int NC = mg_cols(MTB)>
 __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, const bf16_t* W, int K, int N, int k0,
                                       int nks, int c0, const void* zero16, char* ring, char* sink,
-                                      f32x4_t (&acc)[Mg<MTB>::MTW][Mg<MTB>::NTW]) {
-  using S = Mg<MTB>;
+                                      f32x4_t (&acc)[Mg<MTB, NC>::MTW][Mg<MTB, NC>::NTW]) {
+  using S = Mg<MTB, NC>;
 #pragma unroll
   for (int mt = 0; mt < S::MTW; ++mt)
 #pragma unroll
     for (int nt = 0; nt < S::NTW; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const BTileSrc bs = btile_src(W, K, N, k0, c0);
+  const BTileSrc<NC> bs = btile_src<NC>(W, K, N, k0, c0);
   const int ks0 = k0 / kMgK;
-  mg_ring<S::kADma + 1>(
+  mg_ring<S::kADma + S::kBDma>(
       nks, ring, S::kStep,
       [&](int st, char* buf) {
         const bool live = st < nks;
         issue_atile<MTB>(A, mt_pad, mt0, ks0 + st, live, buf, sink, zero16);
-        issue_btile(bs, st, live, buf + S::kABytes, zero16);
+        issue_btile<NC>(bs, st, live, buf + S::kABytes, zero16);
       },
-      [&](int, const char* buf) { mg_step<MTB>(buf, buf + S::kABytes, acc); });
+      [&](int, const char* buf) { mg_step<MTB, NC>(buf, buf + S::kABytes, acc); });
 }
 
 // Lane (g, l16) of a wave holds D[4g+i][l16] of each 16x16 output tile.
 // Visits (token, column, value) of the wave's tiles for a block starting at token t0.
-template <int MTB, class F>
-__device__ __forceinline__ void mg_for_outputs(const f32x4_t (&acc)[Mg<MTB>::MTW][Mg<MTB>::NTW], int t0, int c0,
-                                               F&& f) {
-  using S = Mg<MTB>;
+template <int MTB, int NC = mg_cols(MTB), class F>
+__device__ __forceinline__ void mg_for_outputs(const f32x4_t (&acc)[Mg<MTB, NC>::MTW][Mg<MTB, NC>::NTW], int t0,
+                                               int c0, F&& f) {
+  using S = Mg<MTB, NC>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::WN, wn = wave % S::WN;
   const int g = lane >> 4, l16 = lane & 15;

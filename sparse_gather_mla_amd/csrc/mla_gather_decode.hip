@@ -37,24 +37,19 @@ __global__ __launch_bounds__(kBlock) void k_absorb(StepParams p) {
 
 template <int NT, int HG, int CS>
 __global__ __launch_bounds__(HG * CS * 64) void k_core(StepParams p) {
-  __shared__ __attribute__((aligned(16))) char ring[kCoreRing * core_buf_bytes(NT)];
-  __shared__ int ids[kMaxSplitRows];
-  __shared__ __attribute__((aligned(16))) char sink[1024];
-  __shared__ f32x4_t sx[HG * CS * 2 * 64];  // partial score tiles exchanged within a head group
-  core_phase<NT, HG, CS>(p, blockIdx.x, ring, ids, sink, sx);
+  __shared__ __attribute__((aligned(16))) char lds[core_lds_bytes(NT, HG, CS)];
+  core_phase<NT, HG, CS>(p, blockIdx.x, lds);
 }
 
-// fused variant: kv rows, absorption and core in one launch (phase_absorb_core)
+// fused variant: kv rows, absorption and core in one launch (phase_absorb_core);
+// the producers reuse the core's LDS
 template <int NT>
 __global__ __launch_bounds__(kBlock) void k_absorb_core(StepParams p) {
-  __shared__ __attribute__((aligned(16))) char ring[kCoreRing * core_buf_bytes(NT)];
-  __shared__ int ids[kMaxSplitRows];
-  __shared__ __attribute__((aligned(16))) char sink[1024];
-  __shared__ f32x4_t sx[1 * 4 * 2 * 64];
-  extern __shared__ float lds[];
-  constexpr bool kRingHolds = kCoreRing * core_buf_bytes(NT) >= kGemvLdsFloats * (int)sizeof(float);
-  float* plds = kRingHolds ? reinterpret_cast<float*>(ring) : lds;
-  phase_absorb_core<NT, 1, 4>(p, blockIdx.x, ring, ids, sink, sx, plds);
+  constexpr int kBytes = core_lds_bytes(NT, 1, 4) > kGemvLdsFloats * (int)sizeof(float)
+                             ? core_lds_bytes(NT, 1, 4)
+                             : kGemvLdsFloats * (int)sizeof(float);
+  __shared__ __attribute__((aligned(16))) char lds[kBytes];
+  phase_absorb_core<NT, 1, 4>(p, blockIdx.x, lds);
 }
 
 __global__ __launch_bounds__(kBlock) void k_oabsorb(StepParams p) {
@@ -194,27 +189,31 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   pl.mtb = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
   pl.ntb = cdiv(T, 16 * pl.mtb);
   pl.mt_pad = pl.ntb * pl.mtb;
-  // about one workgroup per CU with the 96 KB ring of 4 m-tiles, two otherwise
-  const int target = pl.mtb == 4 ? 256 : 512;
+  // about one workgroup per CU for the 128-column tiles (96-128 KB rings), two otherwise
+  const int nc = mg_cols(pl.mtb);
+  const int target = nc == 128 ? 256 : 512;
   pl.kt1 = cdiv(H, kMgK);
-  pl.ntq1m = cdiv(Q, kMgCols);
-  pl.nt1m = pl.ntq1m + cdiv(KVR, kMgCols);
+  pl.ntq1m = cdiv(Q, nc);
+  pl.nt1m = pl.ntq1m + cdiv(KVR, nc);
   split_m(pl.kt1, pl.nt1m * pl.ntb, target, &pl.s1, &pl.ks1m);
   pl.kt2 = cdiv(Q, kMgK);
-  pl.nt2m = cdiv(N2, kMgCols);
+  pl.nt2m = cdiv(N2, nc);
   split_m(pl.kt2, pl.nt2m * pl.ntb, target, &pl.s2, &pl.ks2m);
   pl.nct3 = R / kMgCols;
   pl.mtb3 = pl.mtb;
   while (pl.mtb3 > 1 && (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2048 > 96 * 1024) pl.mtb3 /= 2;
   pl.ntb3 = cdiv(T, 16 * pl.mtb3);
+  // as many tiles per workgroup as keep at least 128 workgroups busy
+  pl.tpw3 = pl.nct3;
+  while (pl.tpw3 > 1 && NH * pl.ntb3 * (pl.nct3 / pl.tpw3) < 128) pl.tpw3 /= 2;
   pl.mtb5 = 1;
   pl.ntb5 = cdiv(T, 16 * pl.mtb5);
   pl.nxc = cdiv(pl.kt1 * kMgK, kPrepChunk);
   pl.nqc = cdiv(Q, kQaChunk);
   pl.kt6 = cdiv(NH * DV, kMgK);
-  pl.nt6m = cdiv(H, kMgCols);
+  pl.nt6m = cdiv(H, nc);
   split_m(pl.kt6, pl.nt6m * pl.ntb, target, &pl.s6, &pl.ks6m);
-  pl.n7 = T * cdiv(H, 64);
+  pl.n7 = T * cdiv(H, kOutCols);
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -281,7 +280,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.nt5c = cdiv(T, pl.tc5);
   pl.nt6 = cdiv(H, kTile);
   choose_split(NH * DV, pl.nt6, &pl.s6, &pl.ks6);
-  pl.n7 = T * cdiv(H, 64);
+  pl.n7 = T * cdiv(H, kOutCols);
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -357,10 +356,6 @@ core_kernel_t pick_fused(int R) {
   }
 }
 
-size_t fused_dyn_lds(int R) {
-  return (size_t)kCoreRing * core_buf_bytes(R / 16) >= kGemvLdsFloats * sizeof(float) ? 0 : kGemvLdsFloats * sizeof(float);
-}
-
 core_kernel_t pick_core(const Plan& pl, int R) {
   return pl.core_hg == 1 ? pick_core_nt<1, 4>(R / 16) : pick_core_nt<4, 2>(R / 16);
 }
@@ -395,10 +390,6 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
   const void* gemv[] = {(const void*)k_down, (const void*)k_qup, (const void*)k_absorb, (const void*)k_oabsorb,
                         (const void*)k_oproj, (const void*)k_out, (const void*)k_prep, (const void*)k_qa};
   for (const void* k : gemv)
-    if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
-  // fused kernels whose ring is smaller than the producers' LDS take it as dynamic LDS
-  const void* fused[] = {(const void*)k_absorb_core<4>, (const void*)k_absorb_core<8>, (const void*)k_absorb_core<16>};
-  for (const void* k : fused)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
   const void* big[] = {(const void*)k_absorb_m<1>, (const void*)k_absorb_m<2>, (const void*)k_absorb_m<4>,
                        (const void*)k_oabsorb_m<1>};
@@ -555,7 +546,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
     mark(1);
     hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gl, s, p);
     mark(2);
-    hipLaunchKernelGGL(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, fused_dyn_lds(p.R), s, p);
+    hipLaunchKernelGGL(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, 0, s, p);
     mark(3);
     hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), blk, gl, s, p);
     mark(4);
@@ -588,7 +579,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
     mark(ev++);
     hipLaunchKernelGGL(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0, s, p);
     mark(ev++);
-    hipLaunchKernelGGL(pick_absorb_m(pl.mtb3), dim3(mg_grid(p.NH * pl.nct3, pl.ntb3)), blk,
+    hipLaunchKernelGGL(pick_absorb_m(pl.mtb3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk,
                        absorb_lds_bytes(pl, p.DN), s, p);
     mark(ev++);
     hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);

@@ -209,7 +209,8 @@ __device__ __forceinline__ void token_betas(const StepParams& p, int t0, int nt,
 // ---------------------------------------------------------------------------
 // k_absorb: q = beta * (sum of wq_b partials); q_lat[t,h,:] = q_nope[t,h,:] @
 // q_absorb_w[h] for a 64-column chunk; the chunk-0 workgroup also ropes q_pe.
-// Output: bf16 Qcat[t][h] = [q_lat | q_pe], laid out like a cache row.  Extra
+// Output: bf16 Qcat[t][h] = [q_lat | q_pe] * softmax_scale * log2(e), laid out
+// like a cache row (the core's scores come out in the log2 domain).  Extra
 // workgroups (one per token) finish the kv branch: kv-latent RMSNorm,
 // interleaved RoPE of the rotary part, bf16 write of the row at slot_mapping[t].
 // ---------------------------------------------------------------------------
@@ -256,7 +257,7 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
     gemv_tile(W, p.R, 0, p.DN, c0, 64, xs, p.DN, nt, qo - c0, 64, red, v);
     for (int idx = threadIdx.x; idx < nt * 64; idx += kBlock) {
       const int tt = idx / 64, c = idx % 64;
-      p.qcat[((size_t)(t0 + tt) * p.NH + h) * p.KVR + c0 + c] = f32_to_bf16(qo[tt * 64 + c]);
+      p.qcat[((size_t)(t0 + tt) * p.NH + h) * p.KVR + c0 + c] = f32_to_bf16(qo[tt * 64 + c] * p.scale_log2);
     }
     if (cc == 0) {
       reduce_parts(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH + p.DN, (size_t)T * p.N2, pl.s2, nt * p.DR,
@@ -264,7 +265,9 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
       const int half = p.DR / 2;
       for (int idx = threadIdx.x; idx < nt * half; idx += kBlock) {
         const int tt = idx / half, i = idx % half, t = t0 + tt;
-        const float x0 = beta[tt] * xs[tt * p.DR + 2 * i], x1 = beta[tt] * xs[tt * p.DR + 2 * i + 1];
+        // the query tile is stored pre-scaled by softmax_scale * log2(e)
+        const float bq = beta[tt] * p.scale_log2;
+        const float x0 = bq * xs[tt * p.DR + 2 * i], x1 = bq * xs[tt * p.DR + 2 * i + 1];
         const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
         bf16_t* q = p.qcat + ((size_t)t * p.NH + h) * p.KVR + p.R;
         q[2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
@@ -280,8 +283,7 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
 // rows, [T, T + NH*ncc3) run the absorption tiles, the rest run the core.  A
 // core workgroup waits for every kv row before it reads the cache (a token may
 // select its own position), issues its first row loads, then waits for its
-// heads' query tiles.  The producers work in `plds` (the core's ring when it
-// is large enough).
+// heads' query tiles.  The producers work in the same LDS array.
 // ---------------------------------------------------------------------------
 template <int NT, int HG, int CS>
 struct CoreWaitFused {
@@ -307,21 +309,20 @@ struct CoreWaitFused {
 };
 
 template <int NT, int HG, int CS>
-__device__ void phase_absorb_core(const StepParams& p, int b, char* ring, int* ids, char* sink, f32x4_t* sx,
-                                  float* plds) {
+__device__ void phase_absorb_core(const StepParams& p, int b, char* lds) {
   const Plan& pl = p.pl;
   const int T = pl.T, n_abs = p.NH * pl.ncc3;
   if (b < T) {  // kv row of token b
-    phase_absorb(p, n_abs + b, plds);
+    phase_absorb(p, n_abs + b, reinterpret_cast<float*>(lds));
     count_done(p.sync);
     return;
   }
   if (b < T + n_abs) {
-    phase_absorb(p, b - T, plds);
+    phase_absorb(p, b - T, reinterpret_cast<float*>(lds));
     count_done(p.sync + (2 + (b - T) / pl.ncc3) * kSyncStride);
     return;
   }
-  core_phase<NT, HG, CS>(p, b - T - n_abs, ring, ids, sink, sx, CoreWaitFused<NT, HG, CS>{p});
+  core_phase<NT, HG, CS>(p, b - T - n_abs, lds, CoreWaitFused<NT, HG, CS>{p});
 }
 
 // ---------------------------------------------------------------------------
@@ -453,17 +454,50 @@ __device__ void phase_oproj(const StepParams& p, int b, float* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// k_out: out[t][c] = bf16(sum over the o-projection's slabs), 64 columns per workgroup
+// k_out: out[t][c] = bf16(sum over the o-projection's slabs).  A workgroup
+// covers 256 columns of one token: four lanes per 4-column group each add
+// every fourth slab (in order), then the four partials are added in a fixed
+// order, so the result is reproducible.
 // ---------------------------------------------------------------------------
-__device__ void phase_out(const StepParams& p, int b, float* lds) {
+constexpr int kOutCols = kBlock;  // columns per k_out workgroup: kBlock/4 groups of four columns
+
+__device__ void phase_out(const StepParams& p, int b, float*) {
   const Plan& pl = p.pl;
-  const int ncg = (p.H + 63) / 64;
-  const int t = b / ncg, c0 = (b % ncg) * 64;
-  const int nc = min(64, p.H - c0);
-  float* sum = lds;
-  float* scratch = lds + 64;
-  reduce_parts4(p.part6 + (size_t)t * p.H + c0, (size_t)pl.T * p.H, pl.s6, nc / 4, nc / 4, 0, sum, scratch);
-  for (int c = threadIdx.x; c < nc; c += kBlock) p.out[(size_t)t * p.H + c0 + c] = f32_to_bf16(sum[c]);
+  const int ncg = (p.H + kOutCols - 1) / kOutCols;
+  const int t = b / ncg;
+  const int part = threadIdx.x & 3;
+  const int c = (b % ncg) * kOutCols + 4 * (threadIdx.x >> 2);
+  const bool ok = c < p.H;  // H % 8 == 0: a group of four is wholly inside or outside
+  const size_t stride = (size_t)pl.T * p.H;
+  const float* src = p.part6 + (size_t)t * p.H + (ok ? c : 0);
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = part;
+  for (; s + 12 < pl.s6; s += 16) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)(s + 4 * u) * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
+    }
+  }
+  for (; s < pl.s6; s += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)s * stride);
+    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  }
+  // partials of lanes 4i .. 4i+3: ((p0 + p1) + (p2 + p3))
+  float r[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] += __shfl_xor(r[i], 1, kWave);
+    r[i] += __shfl_xor(r[i], 2, kWave);
+  }
+  if (ok && part == 0) {
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
+    *reinterpret_cast<uint2*>(p.out + (size_t)t * p.H + c) = o;
+  }
 }
 
 }  // namespace mla

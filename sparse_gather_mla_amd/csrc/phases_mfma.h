@@ -92,7 +92,8 @@ __device__ void phase_down_m(const StepParams& p, int b, char* ring, char* sink)
   const bool is_q = tile < pl.ntq1m;
   const bf16_t* W = is_q ? p.wq_a : p.wkv_a;
   const int N = is_q ? p.Q : p.KVR;
-  const int c0 = (is_q ? tile : tile - pl.ntq1m) * kMgCols;
+  constexpr int NC = mg_cols(MTB);
+  const int c0 = (is_q ? tile : tile - pl.ntq1m) * NC;
   const int k0 = slab * pl.ks1m * kMgK;
   const int nks = min(pl.ks1m, pl.kt1 - slab * pl.ks1m);
   f32x4_t acc[Mg<MTB>::MTW][Mg<MTB>::NTW];
@@ -194,7 +195,8 @@ __device__ void phase_qup_m(const StepParams& p, int b, char* ring, char* sink) 
   int u, tb;
   if (!mg_unit(b, pl.nt2m * pl.s2, pl.ntb, u, tb)) return;
   const int tile = u % pl.nt2m, slab = u / pl.nt2m;
-  const int c0 = tile * kMgCols;
+  constexpr int NC = mg_cols(MTB);
+  const int c0 = tile * NC;
   const int k0 = slab * pl.ks2m * kMgK;
   const int nks = min(pl.ks2m, pl.kt2 - slab * pl.ks2m);
   f32x4_t acc[Mg<MTB>::MTW][Mg<MTB>::NTW];
@@ -207,28 +209,38 @@ __device__ void phase_qup_m(const StepParams& p, int b, char* ring, char* sink) 
 }
 
 // ---------------------------------------------------------------------------
-// k_absorb: workgroup (head h, 64-column tile of kv_lora_rank, token block).
-// The weight tile's loads are issued first; meanwhile A3 = beta * q_nope (wq_b
-// slabs summed in order) goes to LDS in fragment order.  q_lat lands in Qcat
-// as bf16.  The tile-0 workgroups also rope q_pe into Qcat.
+// k_absorb: workgroup (head h, group of tpw3 64-column tiles of kv_lora_rank,
+// token block).  The ring streams the group's tiles of q_absorb_w[h] (ceil(DN/32)
+// k-steps each) from the start; meanwhile A3 = beta * q_nope (wq_b slabs summed
+// in order) goes to LDS in fragment order, once for all the group's tiles.  Each tile's q_lat lands in Qcat
+// as bf16, pre-scaled by softmax_scale * log2(e); q_pe is roped into Qcat too.
 // LDS: ring (kMgDepth x 4 KB) | sink (1 KB) | beta (256 B) | A3 (ceil(DN/32) x MTB x 2 KB).
 // ---------------------------------------------------------------------------
 template <int MTB>
 __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
-  using S = Mg<MTB>;
+  using S = Mg<MTB, kMgCols>;
   const Plan& pl = p.pl;
+  const int ngrp = pl.nct3 / pl.tpw3;
   int u, tb;
-  if (!mg_unit(b, p.NH * pl.nct3, pl.ntb3, u, tb)) return;
-  const int h = u / pl.nct3, j = u % pl.nct3;
+  if (!mg_unit(b, p.NH * ngrp, pl.ntb3, u, tb)) return;
+  const int h = u / ngrp, j0 = (u % ngrp) * pl.tpw3;
   const int T = pl.T, tid = threadIdx.x;
   const int t0 = tb * MTB * 16;
   const int KS = (p.DN + kMgK - 1) / kMgK;
+  const int nsteps = pl.tpw3 * KS;
   char* ring = lds;
   float* beta = reinterpret_cast<float*>(lds + kMgDepth * S::kBBytes + 1024);
   char* ares = lds + kMgDepth * S::kBBytes + 1024 + 256;
-  const int c0 = j * kMgCols;
-  const BTileSrc bs = btile_src(p.w_qabs + (size_t)h * p.DN * p.R, p.DN, p.R, 0, c0);
-  auto issue = [&](int st, char* buf) { issue_btile(bs, st, st < KS, buf, p.zero16); };
+  // this lane's piece of a 32 x 64 weight tile (row r, swizzled 16-byte piece pc)
+  const bf16_t* W = p.w_qabs + (size_t)h * p.DN * p.R;
+  const int r = tid >> 3, pc = (tid & 7) ^ (r & 7);
+  auto issue = [&](int st, char* buf) {
+    const int j = j0 + st / KS, ks = st % KS;
+    const int row = ks * kMgK + r;
+    const void* src = p.zero16;
+    if (st < nsteps && row < p.DN) src = W + (size_t)row * p.R + j * kMgCols + 8 * pc;
+    dma16(src, buf + (tid >> 6) * 1024);
+  };
   mg_ring_prologue(ring, S::kBBytes, issue);
   if (tid < MTB * 16) beta[tid] = (t0 + tid < T) ? mfma_beta(p, t0 + tid) : 0.f;
   __syncthreads();
@@ -245,33 +257,40 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   }
   __syncthreads();
   f32x4_t acc[S::MTW][S::NTW];
+  auto zero = [&]() {
 #pragma unroll
-  for (int mt = 0; mt < S::MTW; ++mt)
+    for (int mt = 0; mt < S::MTW; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < S::NTW; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  mg_ring_loop<1>(KS, ring, S::kBBytes, issue,
-                  [&](int st, const char* buf) { mg_step<MTB>(ares + st * S::kABytes, buf, acc); });
-  mg_for_outputs<MTB>(acc, t0, c0, [&](int t, int c, float v) {
-    if (t < T) p.qcat[((size_t)t * p.NH + h) * p.KVR + c] = f32_to_bf16(v);
-  });
-  if (j == 0) {
-    const int half = p.DR / 2;
-    for (int idx = tid; idx < MTB * 16 * half; idx += kBlock) {
-      const int tt = idx / half, i = idx % half, t = t0 + tt;
-      if (t >= T) continue;
-      const float* src = p.part2 + (size_t)t * p.N2 + (size_t)h * p.QKH + p.DN + 2 * i;
-      float x0 = 0.f, x1 = 0.f;
-      for (int s2 = 0; s2 < pl.s2; ++s2) {
-        x0 += src[(size_t)s2 * T * p.N2];
-        x1 += src[(size_t)s2 * T * p.N2 + 1];
-      }
-      x0 *= beta[tt];
-      x1 *= beta[tt];
-      const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
-      bf16_t* q = p.qcat + ((size_t)t * p.NH + h) * p.KVR + p.R;
-      q[2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
-      q[2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
+      for (int nt = 0; nt < S::NTW; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  zero();
+  mg_ring_loop<1>(nsteps, ring, S::kBBytes, issue, [&](int st, const char* buf) {
+    const int j = j0 + st / KS, ks = st % KS;
+    mg_step<MTB, kMgCols>(ares + ks * S::kABytes, buf, acc);
+    if (ks == KS - 1) {  // tile j complete
+      mg_for_outputs<MTB, kMgCols>(acc, t0, j * kMgCols, [&](int t, int c, float v) {
+        if (t < T) p.qcat[((size_t)t * p.NH + h) * p.KVR + c] = f32_to_bf16(v * p.scale_log2);
+      });
+      zero();
     }
+  });
+  if (j0 != 0) return;  // the first tile group also ropes q_pe
+  const int half = p.DR / 2;
+  for (int idx = tid; idx < MTB * 16 * half; idx += kBlock) {
+    const int tt = idx / half, i = idx % half, t = t0 + tt;
+    if (t >= T) continue;
+    const float* src = p.part2 + (size_t)t * p.N2 + (size_t)h * p.QKH + p.DN + 2 * i;
+    float x0 = 0.f, x1 = 0.f;
+    for (int s2 = 0; s2 < pl.s2; ++s2) {
+      x0 += src[(size_t)s2 * T * p.N2];
+      x1 += src[(size_t)s2 * T * p.N2 + 1];
+    }
+    x0 *= beta[tt] * p.scale_log2;  // the query tile is stored pre-scaled
+    x1 *= beta[tt] * p.scale_log2;
+    const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
+    bf16_t* q = p.qcat + ((size_t)t * p.NH + h) * p.KVR + p.R;
+    q[2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
+    q[2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
   }
 }
 
@@ -416,7 +435,8 @@ __device__ void phase_oproj_m(const StepParams& p, int b, char* ring, char* sink
   int u, tb;
   if (!mg_unit(b, pl.nt6m * pl.s6, pl.ntb, u, tb)) return;
   const int tile = u % pl.nt6m, slab = u / pl.nt6m;
-  const int c0 = tile * kMgCols;
+  constexpr int NC = mg_cols(MTB);
+  const int c0 = tile * NC;
   const int k0 = slab * pl.ks6m * kMgK;
   const int nks = min(pl.ks6m, pl.kt6 - slab * pl.ks6m);
   f32x4_t acc[Mg<MTB>::MTW][Mg<MTB>::NTW];
