@@ -12,11 +12,13 @@ resident in HBM before timing starts.
 Timing: W warm-up steps, then K timed steps, every one of them preceded by a
 read and write of a 1 GiB buffer so that neither the L2s nor the 256 MB
 Infinity Cache hold the weights or the pool (cold-cache steps).  HIP events on
-the step's stream bracket the step (the flush is outside them) and each of its
-kernels; ``value`` is the mean step latency in microseconds.  Since every
-dispatch of the run is a cold one, a rocprofv3 kernel trace of the same
-command averages the same launches.  ``--extras`` adds warm (back-to-back) and
-HIP-graph timings.
+the step's stream bracket each step (the flush is outside them); ``value`` is
+the mean step latency in microseconds, kernels launched one by one
+(``--graph``: the library replays its captured HIP graph).  K more
+cold steps, launched kernel by kernel with an event before each, give the
+per-kernel breakdown.  Every dispatch of the run is a cold one, so a rocprofv3
+kernel trace of the same command averages the same launches.  ``--extras``
+adds warm (back-to-back) and torch-captured graph timings.
 
 ``roofline`` is for the kernel with the largest mean duration: algorithmic
 bytes per launch over its event-timed mean duration, against 8 TB/s.
@@ -65,6 +67,7 @@ def alg_bytes(sh, inp, names) -> dict:
         b = {"k_down": w_down + inputs, "k_qup": w_qb + kv_branch}
     b.update({"k_absorb": 2 * nh * dn * r, "k_core": 2 * kvr * uniq, "k_oabsorb": 2 * nh * dv * r,
               "k_oproj": 2 * nh * dv * H, "k_out": 2 * T * H})
+    b["k_absorb_core"] = b["k_absorb"] + b["k_core"]  # the fused variant's single launch
     b = {n: b.get(n, 0) for n in names}
     b["step"] = sum(b.values())
     return b
@@ -185,6 +188,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="ds32_slice")
     ap.add_argument("--fused", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="the library captures the step once and replays it")
     ap.add_argument("--extras", action="store_true", help="also time warm steps and a HIP graph of the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with four plain 512 MiB device copies (for counter calibration)")
@@ -214,7 +218,8 @@ def main() -> int:
     small_pool = sh.n_blocks * sh.block_size * sh.kv_row_dim * 2 <= (256 << 20)
     inp = make_inputs(wl, with_pool=small_pool)  # host copy of the pool only when small (CPU baseline)
     g = gpu_inputs(wl, inp, device=dev)
-    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens, device=0, fused=args.fused)
+    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens, device=0, fused=args.fused,
+                          graph=args.graph)
     names = mod.kernel_names(sh.n_tokens)
     nk = len(names)
     out = torch.empty((sh.n_tokens, sh.hidden), dtype=torch.bfloat16, device=dev)
@@ -223,21 +228,34 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     # --- warm-up and timed steps, all cold ----------------------------------
+    # The step as a caller runs it (kernels launched one by one; --graph: the
+    # library replays its captured HIP graph), bracketed by events on its stream.
     W, K = args.warmup, args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(W + K)]
+    bounds = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for _ in range(W):
+        flush.add_(1.0)  # read + write 1 GiB: evicts the L2s and the Infinity Cache
+        mod(g, out=out, stream=stream)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for k in range(W + K):
-        if k == W:
-            torch.cuda.synchronize()
-            wall0 = time.perf_counter()
-        flush.add_(1.0)  # read + write 1 GiB: evicts the L2s and the Infinity Cache
-        mod(g, out=out, events=evs[k], stream=stream)
+    for k in range(K):
+        flush.add_(1.0)
+        bounds[k][0].record(stream)
+        mod(g, out=out, stream=stream)
+        bounds[k][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    evs = evs[W:]
-    step_ms = [evs[k][0].elapsed_time(evs[k][nk]) for k in range(K)]
+    step_ms = [a.elapsed_time(b) for a, b in bounds]
+
+    # --- per-kernel breakdown: the same cold steps, kernels launched one by one
+    # with an event before each (these dispatches are the ones a kernel trace
+    # of this run averages too)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
+    for k in range(K):
+        flush.add_(1.0)
+        mod(g, out=out, events=evs[k], stream=stream)
+    torch.cuda.synchronize()
     stage_ms = {names[i]: [evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)] for i in range(nk)}
+    direct_ms = [evs[k][0].elapsed_time(evs[k][nk]) for k in range(K)]
 
     warm_us = graph_us = None
     if args.extras:
@@ -312,6 +330,8 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2),
         "alg_bytes_per_step": ab["step"],
         "step_us_p10_p50_p90": [round(x * 1e3, 3) for x in q],
+        "launch": "captured HIP graph, replayed" if args.graph else "kernels launched one by one",
+        "step_us_direct_launch_with_kernel_events": round(statistics.mean(direct_ms) * 1e3, 3),
         "wall_ms_per_step_incl_flush": round(wall / K * 1e3, 4),
         "stages": {n: {"us": round(stage_us[n], 3), "alg_bytes": ab.get(n, 0),
                        "GBps": round(ab.get(n, 0) / (stage_us[n] * 1e-6) / 1e9, 1)} for n in names},

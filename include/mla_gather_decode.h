@@ -50,6 +50,13 @@ extern "C" {
  * in the workspace instead of a kernel boundary.  Applies to steps of at most
  * 8 tokens with at most 16 heads; other steps run the separate kernels. */
 #define MLA_GD_FLAG_FUSED 1u
+/* Capture the step's launches once into a HIP graph (on a private stream of
+ * default priority, owned by the handle) and replay it on the caller's stream;
+ * the step is captured again whenever a tensor pointer, the workspace or
+ * n_tokens changes.  Profiled steps and steps enqueued on a stream that the
+ * caller is capturing launch directly.  Without the flag every step launches
+ * its kernels one by one (measured faster on MI355X for this step). */
+#define MLA_GD_FLAG_GRAPH 2u
 
 /*
  * Dimensions of the step, fixed when the handle is created.  The page passes

@@ -21,6 +21,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MLA_GD_LIBRARY") or os.path.join(_PKG, "libmla_gather_decode.so")
 
 MLA_GD_FLAG_FUSED = 1
+MLA_GD_FLAG_GRAPH = 2
 
 
 class MlaGdError(RuntimeError):
@@ -125,7 +126,10 @@ class MlaGatherDecode:
     """One handle of the C library plus a workspace, for up to ``max_tokens`` tokens."""
 
     def __init__(self, dims: Dims, max_tokens: int, device: int = 0, fused: bool = False,
-                 allocate_workspace: bool = True):
+                 allocate_workspace: bool = True, graph: bool = False):
+        """``fused``: the fused variant (kv rows, absorption and core in one launch).
+        ``graph``: capture the step once into a HIP graph and replay it (default:
+        kernels launched one by one)."""
         import torch
 
         self.lib = load_library()
@@ -133,12 +137,13 @@ class MlaGatherDecode:
         self.max_tokens = int(max_tokens)
         self.device = torch.device("cuda", device)
         self.fused = fused
+        self.graph = graph
         cd = _Dims(hidden=dims.hidden, q_lora_rank=dims.q_lora_rank, kv_lora_rank=dims.kv_lora_rank,
                    qk_nope_head_dim=dims.qk_nope_head_dim, qk_rope_head_dim=dims.qk_rope_head_dim,
                    v_head_dim=dims.v_head_dim, n_heads=dims.n_heads, block_size=dims.block_size,
                    max_blocks_per_seq=dims.max_blocks_per_seq, n_blocks=dims.n_blocks, n_prior=dims.n_prior,
                    max_tokens=self.max_tokens, softmax_scale=dims.softmax_scale, norm_eps=dims.norm_eps,
-                   flags=MLA_GD_FLAG_FUSED if fused else 0)
+                   flags=(MLA_GD_FLAG_FUSED if fused else 0) | (MLA_GD_FLAG_GRAPH if graph else 0))
         h = ctypes.c_void_p()
         rc = self.lib.mla_gather_decode_create(ctypes.byref(cd), int(device), ctypes.byref(h))
         if rc != 0:

@@ -6,8 +6,11 @@
 namespace mla {
 
 constexpr int kTile = 512;  // output columns per GEMV tile: 64 lanes x 8 bf16
-constexpr int kTT = 8;      // tokens per pass of the VALU GEMV
-constexpr int kUnroll = 8;  // 16-byte weight loads in flight per lane
+constexpr int kTT = 8;      // most tokens per pass of the VALU GEMV (and of the GEMV path)
+
+// 16-byte weight loads in flight per lane: a one-token pass holds few
+// accumulators, so it keeps twice as many loads in flight.
+__host__ __device__ constexpr int gemv_unroll(int ntt) { return ntt == 1 ? 16 : 8; }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -125,51 +128,53 @@ __device__ __forceinline__ GemvGeom gemv_geom(int nc) {
   return g;
 }
 
-// The first kUnroll weight loads of a tile, issued before the activations are ready.
+// The first UNR weight loads of a tile, issued before the activations are ready.
+template <int UNR>
 __device__ __forceinline__ void gemv_first(const bf16_t* __restrict__ W, int N, int k0, int ks, int c0, int nc,
                                            u32x4* v) {
   const GemvGeom g = gemv_geom(nc);
   const bf16_t* wp = W + (size_t)k0 * N + c0 + 8 * g.cg;
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < UNR; ++u) {
     const int r = g.r0 + u * g.rstep;
     if (g.active && r < ks) v[u] = ld_stream(wp + (size_t)r * N);
     else v[u] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-// One GEMV tile for up to kTT tokens:
+// One GEMV tile for up to NTT tokens:
 //   out[tt*ldo + c0 + c] = sum_{r < ks} xs[tt*xstride + r] * W[(k0 + r)*N + c0 + c],  c < nc <= 512.
 // W is [K, N] row-major bf16 (N and nc multiples of 8), xs is LDS.  `v` holds
-// the loads of gemv_first.  Lanes of equal column combine by shuffles, waves
-// through LDS (`red`: 3*kTT*512 floats).
+// the loads of gemv_first<UNR>.  Lanes of equal column combine by shuffles,
+// waves through LDS (`red`: 3*NTT*512 floats).
+template <int NTT, int UNR>
 __device__ __forceinline__ void gemv_tile(const bf16_t* __restrict__ W, int N, int k0, int ks, int c0, int nc,
                                           const float* xs, int xstride, int nt, float* __restrict__ out,
                                           size_t ldo, float* red, u32x4* v) {
   const GemvGeom g = gemv_geom(nc);
   const int wv = threadIdx.x >> 6;
-  float acc[kTT][8];
+  float acc[NTT][8];
 #pragma unroll
-  for (int tt = 0; tt < kTT; ++tt)
+  for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[tt][i] = 0.f;
   const bf16_t* wp = W + (size_t)k0 * N + c0 + 8 * g.cg;
-  for (int r0 = g.r0; r0 < ks; r0 += g.rstep * kUnroll) {
+  for (int r0 = g.r0; r0 < ks; r0 += g.rstep * UNR) {
     if (r0 != g.r0) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < UNR; ++u) {
         const int r = r0 + u * g.rstep;
         if (g.active && r < ks) v[u] = ld_stream(wp + (size_t)r * N);
         else v[u] = u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       const int r = min(r0 + u * g.rstep, ks - 1);  // rows past the slab carry zero weights
       float w[8];
       unpack8v(v[u], w);
 #pragma unroll
-      for (int tt = 0; tt < kTT; ++tt) {
+      for (int tt = 0; tt < NTT; ++tt) {
         if (tt < nt) {
           const float xv = xs[tt * xstride + r];
 #pragma unroll
@@ -180,27 +185,27 @@ __device__ __forceinline__ void gemv_tile(const bf16_t* __restrict__ W, int N, i
   }
   for (int off = g.lpr; off < 64; off <<= 1)
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt)
+    for (int tt = 0; tt < NTT; ++tt)
       if (tt < nt)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[tt][i] += __shfl_xor(acc[tt][i], off, kWave);
   if (wv > 0 && g.rsub == 0 && g.active) {
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt)
+    for (int tt = 0; tt < NTT; ++tt)
       if (tt < nt)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) red[((wv - 1) * kTT + tt) * kTile + 8 * g.cg + i] = acc[tt][i];
+        for (int i = 0; i < 8; ++i) red[((wv - 1) * NTT + tt) * kTile + 8 * g.cg + i] = acc[tt][i];
   }
   __syncthreads();
   if (wv == 0 && g.rsub == 0 && g.active) {
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
+    for (int tt = 0; tt < NTT; ++tt) {
       if (tt < nt) {
         float o[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          o[i] = acc[tt][i] + red[(0 * kTT + tt) * kTile + 8 * g.cg + i] + red[(1 * kTT + tt) * kTile + 8 * g.cg + i] +
-                 red[(2 * kTT + tt) * kTile + 8 * g.cg + i];
+          o[i] = acc[tt][i] + red[(0 * NTT + tt) * kTile + 8 * g.cg + i] + red[(1 * NTT + tt) * kTile + 8 * g.cg + i] +
+                 red[(2 * NTT + tt) * kTile + 8 * g.cg + i];
         float4* dst = reinterpret_cast<float4*>(out + (size_t)tt * ldo + c0 + 8 * g.cg);
         dst[0] = make_float4(o[0], o[1], o[2], o[3]);
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);

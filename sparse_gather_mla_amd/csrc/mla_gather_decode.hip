@@ -20,19 +20,22 @@ using namespace mla;
 // kernels: one phase each, launched in order on the caller's stream
 // ---------------------------------------------------------------------------
 
+template <int NTT>
 __global__ __launch_bounds__(kBlock) void k_down(StepParams p) {
   extern __shared__ float lds[];
-  phase_down(p, blockIdx.x, lds);
+  phase_down<NTT>(p, blockIdx.x, lds);
 }
 
+template <int NTT>
 __global__ __launch_bounds__(kBlock) void k_qup(StepParams p) {
   extern __shared__ float lds[];
-  phase_qup(p, blockIdx.x, lds);
+  phase_qup<NTT>(p, blockIdx.x, lds);
 }
 
+template <int NTT>
 __global__ __launch_bounds__(kBlock) void k_absorb(StepParams p) {
   extern __shared__ float lds[];
-  phase_absorb(p, blockIdx.x, lds);
+  phase_absorb<NTT>(p, blockIdx.x, lds);
 }
 
 template <int NT, int HG, int CS>
@@ -57,9 +60,10 @@ __global__ __launch_bounds__(kBlock) void k_oabsorb(StepParams p) {
   phase_oabsorb(p, blockIdx.x, lds);
 }
 
+template <int NTT>
 __global__ __launch_bounds__(kBlock) void k_oproj(StepParams p) {
   extern __shared__ float lds[];
-  phase_oproj(p, blockIdx.x, lds);
+  phase_oproj<NTT>(p, blockIdx.x, lds);
 }
 
 __global__ __launch_bounds__(kBlock) void k_out(StepParams p) {
@@ -127,6 +131,14 @@ struct mla_gd_handle {
   int device;
   int last_hip_error;
   bool lds_ready;  // dynamic-LDS limits of the kernels raised on this device
+  // With MLA_GD_FLAG_GRAPH: the step's launches captured once into a HIP graph
+  // on a private stream (default priority) and replayed on the caller's
+  // stream; captured again whenever any kernel argument differs.
+  hipStream_t cap_stream;
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+  bool graph_broken;        // a graph call failed once: launch directly from then on
+  unsigned char key[sizeof(mla::StepParams)];  // the captured kernel arguments
 };
 
 namespace {
@@ -316,7 +328,7 @@ int validate_dims(const mla_gd_dims& d) {
       d.max_blocks_per_seq <= 0 || d.n_blocks <= 0 || d.n_prior <= 0 || d.max_tokens <= 0)
     return MLA_GD_E_INVAL;
   if (d.qk_rope_head_dim % 2 != 0) return MLA_GD_E_INVAL;
-  if ((d.flags & ~MLA_GD_FLAG_FUSED) != 0u) return MLA_GD_E_INVAL;
+  if ((d.flags & ~(MLA_GD_FLAG_FUSED | MLA_GD_FLAG_GRAPH)) != 0u) return MLA_GD_E_INVAL;
   if (!isfinite(d.softmax_scale) || !isfinite(d.norm_eps) || d.norm_eps < 0.f) return MLA_GD_E_INVAL;
   const long long KVR = (long long)d.kv_lora_rank + d.qk_rope_head_dim;
   const long long N2 = (long long)d.n_heads * (d.qk_nope_head_dim + d.qk_rope_head_dim);
@@ -387,8 +399,10 @@ const char* kernel_name(const Plan& pl, int i) {
 
 hipError_t set_lds_limits(const mla_gd_dims& d) {
   hipError_t e = hipSuccess;
-  const void* gemv[] = {(const void*)k_down, (const void*)k_qup, (const void*)k_absorb, (const void*)k_oabsorb,
-                        (const void*)k_oproj, (const void*)k_out, (const void*)k_prep, (const void*)k_qa};
+  const void* gemv[] = {(const void*)k_down<8>, (const void*)k_qup<8>, (const void*)k_absorb<8>,
+                        (const void*)k_oproj<8>, (const void*)k_down<4>, (const void*)k_qup<4>,
+                        (const void*)k_absorb<4>, (const void*)k_oproj<4>, (const void*)k_oabsorb,
+                        (const void*)k_out, (const void*)k_prep, (const void*)k_qa};
   for (const void* k : gemv)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
   const void* big[] = {(const void*)k_absorb_m<1>, (const void*)k_absorb_m<2>, (const void*)k_absorb_m<4>,
@@ -399,6 +413,28 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
 }
 
 typedef void (*step_kernel_t)(StepParams);
+
+// GEMV-path kernels for NTT tokens per pass, and their dynamic LDS
+#define MLA_GD_NTT_PICK(fn, K)                                        \
+  step_kernel_t fn(int ntt) {                                         \
+    return ntt == 1 ? K<1> : (ntt == 2 ? K<2> : (ntt == 4 ? K<4> : K<8>)); \
+  }
+MLA_GD_NTT_PICK(pick_down, k_down)
+MLA_GD_NTT_PICK(pick_qup, k_qup)
+MLA_GD_NTT_PICK(pick_absorb, k_absorb)
+MLA_GD_NTT_PICK(pick_oproj, k_oproj)
+#undef MLA_GD_NTT_PICK
+
+size_t gemv_lds_bytes(int ntt) {
+  switch (ntt) {
+    case 1: return GemvLds<1>::floats * sizeof(float);
+    case 2: return GemvLds<2>::floats * sizeof(float);
+    case 4: return GemvLds<4>::floats * sizeof(float);
+    default: return GemvLds<8>::floats * sizeof(float);
+  }
+}
+
+int gemv_ntt(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)); }
 
 step_kernel_t pick_down_m(int mtb) { return mtb == 1 ? k_down_m<1> : (mtb == 2 ? k_down_m<2> : k_down_m<4>); }
 step_kernel_t pick_qup_m(int mtb) { return mtb == 1 ? k_qup_m<1> : (mtb == 2 ? k_qup_m<2> : k_qup_m<4>); }
@@ -436,11 +472,29 @@ int mla_gather_decode_create(const mla_gd_dims* dims, int device, mla_gd_handle*
   h->device = device;
   h->last_hip_error = 0;
   h->lds_ready = false;
+  h->cap_stream = nullptr;
+  h->graph = nullptr;
+  h->exec = nullptr;
+  h->graph_broken = false;
+  memset(h->key, 0, sizeof(h->key));
   *out_handle = h;
   return MLA_GD_OK;
 }
 
-void mla_gather_decode_destroy(mla_gd_handle* handle) { delete handle; }
+void mla_gather_decode_destroy(mla_gd_handle* handle) {
+  if (!handle) return;
+  if (handle->exec || handle->graph || handle->cap_stream) {
+    int cur = -1;
+    const bool restore = hipGetDevice(&cur) == hipSuccess && cur != handle->device;
+    if (hipSetDevice(handle->device) == hipSuccess) {
+      if (handle->exec) (void)hipGraphExecDestroy(handle->exec);
+      if (handle->graph) (void)hipGraphDestroy(handle->graph);
+      if (handle->cap_stream) (void)hipStreamDestroy(handle->cap_stream);
+    }
+    if (restore) (void)hipSetDevice(cur);
+  }
+  delete handle;
+}
 
 int mla_gather_decode_last_hip_error(const mla_gd_handle* handle) { return handle ? handle->last_hip_error : 0; }
 
@@ -469,6 +523,110 @@ int mla_gather_decode_workspace_init(const mla_gd_handle* handle, void* workspac
 }  // extern "C"
 
 namespace {
+
+// Enqueue the step's kernels on stream s; with `events`, record events[i]
+// before kernel i and after the last one.
+hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* events) {
+  const Plan& pl = p.pl;
+  const int T = pl.T;
+  hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], s);
+  };
+  const size_t gl = kGemvLdsBytes;
+  const int ntt = gemv_ntt(T);
+  const size_t gll = gemv_lds_bytes(ntt);  // GEMV phases passing over ntt tokens
+  const dim3 blk(kBlock);
+  const dim3 core_blk(64 * pl.core_hg * pl.core_cs);
+  mark(0);
+  if (pl.fused) {
+    hipLaunchKernelGGL(pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll, s, p);
+    mark(1);
+    hipLaunchKernelGGL(pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll, s, p);
+    mark(2);
+    hipLaunchKernelGGL(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, 0, s, p);
+    mark(3);
+    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), blk, gl, s, p);
+    mark(4);
+    hipLaunchKernelGGL(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll, s, p);
+    mark(5);
+    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
+    mark(6);
+  } else if (!pl.mfma) {
+    hipLaunchKernelGGL(pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll, s, p);
+    mark(1);
+    hipLaunchKernelGGL(pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll, s, p);
+    mark(2);
+    hipLaunchKernelGGL(pick_absorb(ntt), dim3(p.NH * pl.ncc3 + T), blk, gll, s, p);
+    mark(3);
+    hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
+    mark(4);
+    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), blk, gl, s, p);
+    mark(5);
+    hipLaunchKernelGGL(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll, s, p);
+    mark(6);
+    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
+    mark(7);
+  } else {
+    int ev = 1;
+    hipLaunchKernelGGL(k_prep, dim3(pl.n_idx_wg + T * pl.nxc), blk, 1024, s, p);
+    mark(ev++);
+    hipLaunchKernelGGL(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), blk, 0, s, p);
+    mark(ev++);
+    hipLaunchKernelGGL(k_qa, dim3(T * (pl.nqc + 1)), blk, gl, s, p);
+    mark(ev++);
+    hipLaunchKernelGGL(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0, s, p);
+    mark(ev++);
+    hipLaunchKernelGGL(pick_absorb_m(pl.mtb3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk,
+                       absorb_lds_bytes(pl, p.DN), s, p);
+    mark(ev++);
+    hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
+    mark(ev++);
+    if (pl.nsplit > 1) {
+      hipLaunchKernelGGL(k_combine, dim3(cdiv(T * p.NH * (p.R / 4), kBlock)), blk, 0, s, p);
+      mark(ev++);
+    }
+    hipLaunchKernelGGL(pick_oabsorb_m(pl.mtb5), dim3(mg_grid(p.NH, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R), s,
+                       p);
+    mark(ev++);
+    hipLaunchKernelGGL(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), blk, 0, s, p);
+    mark(ev++);
+    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
+    mark(ev++);
+  }
+  if (e == hipSuccess) e = hipGetLastError();
+  return e;
+}
+
+// Replay the captured graph of these kernel arguments on stream s, capturing
+// it first when the arguments differ from the last capture.
+hipError_t launch_graph(mla_gd_handle* h, const StepParams& p, hipStream_t s) {
+  static_assert(sizeof(h->key) == sizeof(StepParams), "graph key");
+  if (!h->exec || memcmp(h->key, &p, sizeof(p)) != 0) {
+    hipError_t e = hipSuccess;
+    if (!h->cap_stream) e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    if (e == hipSuccess) e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeRelaxed);
+    if (e == hipSuccess) {
+      const hipError_t el = launch_kernels(p, h->cap_stream, nullptr);
+      e = hipStreamEndCapture(h->cap_stream, &graph);
+      if (e == hipSuccess) e = el;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      (void)hipGetLastError();
+      return e;
+    }
+    if (h->exec) (void)hipGraphExecDestroy(h->exec);
+    if (h->graph) (void)hipGraphDestroy(h->graph);
+    h->exec = exec;
+    h->graph = graph;
+    memcpy(h->key, &p, sizeof(p));
+  }
+  return hipGraphLaunch(h->exec, s);
+}
 
 int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void* workspace,
              size_t workspace_bytes, void* stream, void* const* events, int n_events) {
@@ -533,68 +691,22 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   }
   if (e != hipSuccess) { h->last_hip_error = (int)e; return MLA_GD_E_HIP; }
   hipStream_t s = (hipStream_t)stream;
-  const int T = n_tokens;
-  auto mark = [&](int i) {
-    if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], s);
-  };
-  const size_t gl = kGemvLdsBytes;
-  const dim3 blk(kBlock);
-  const dim3 core_blk(64 * pl.core_hg * pl.core_cs);
-  mark(0);
-  if (pl.fused) {
-    hipLaunchKernelGGL(k_down, dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gl, s, p);
-    mark(1);
-    hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gl, s, p);
-    mark(2);
-    hipLaunchKernelGGL(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, 0, s, p);
-    mark(3);
-    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), blk, gl, s, p);
-    mark(4);
-    hipLaunchKernelGGL(k_oproj, dim3(pl.nt6 * pl.s6), blk, gl, s, p);
-    mark(5);
-    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
-    mark(6);
-  } else if (!pl.mfma) {
-    hipLaunchKernelGGL(k_down, dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gl, s, p);
-    mark(1);
-    hipLaunchKernelGGL(k_qup, dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gl, s, p);
-    mark(2);
-    hipLaunchKernelGGL(k_absorb, dim3(p.NH * pl.ncc3 + T), blk, gl, s, p);
-    mark(3);
-    hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
-    mark(4);
-    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), blk, gl, s, p);
-    mark(5);
-    hipLaunchKernelGGL(k_oproj, dim3(pl.nt6 * pl.s6), blk, gl, s, p);
-    mark(6);
-    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
-    mark(7);
-  } else {
-    int ev = 1;
-    hipLaunchKernelGGL(k_prep, dim3(pl.n_idx_wg + T * pl.nxc), blk, 1024, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), blk, 0, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(k_qa, dim3(T * (pl.nqc + 1)), blk, gl, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_absorb_m(pl.mtb3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk,
-                       absorb_lds_bytes(pl, p.DN), s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
-    mark(ev++);
-    if (pl.nsplit > 1) {
-      hipLaunchKernelGGL(k_combine, dim3(cdiv(T * p.NH * (p.R / 4), kBlock)), blk, 0, s, p);
-      mark(ev++);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (e == hipSuccess) e = hipStreamIsCapturing(s, &cap);
+  if (e != hipSuccess) { h->last_hip_error = (int)e; return MLA_GD_E_HIP; }
+  // replay the captured graph only when asked for, and never for the
+  // profiled step or inside the caller's own capture
+  const bool direct = events || cap != hipStreamCaptureStatusNone || !(d.flags & MLA_GD_FLAG_GRAPH) ||
+                      h->graph_broken;
+  if (!direct) {
+    e = launch_graph(h, p, s);
+    if (e != hipSuccess) {
+      h->graph_broken = true;  // fall back to direct launches for this handle
+      h->last_hip_error = (int)e;
+      e = launch_kernels(p, s, nullptr);
     }
-    hipLaunchKernelGGL(pick_oabsorb_m(pl.mtb5), dim3(mg_grid(p.NH, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R), s,
-                       p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), blk, 0, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
-    mark(ev++);
+  } else {
+    e = launch_kernels(p, s, events);
   }
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) { h->last_hip_error = (int)e; return MLA_GD_E_HIP; }

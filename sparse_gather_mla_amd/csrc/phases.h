@@ -26,12 +26,20 @@
 
 namespace mla {
 
-// LDS of the GEMV phases (floats): xs [kTT][512], red [3][kTT][512], scratch [1024], aux [1024]
-constexpr int kLdsXs = 0;
-constexpr int kLdsRed = kTT * kTile;
-constexpr int kLdsScratch = kLdsRed + 3 * kTT * kTile;
-constexpr int kLdsAux = kLdsScratch + 1024;
-constexpr int kGemvLdsFloats = kLdsAux + 1024;
+// LDS of a GEMV phase that passes over NTT tokens at a time (floats):
+// xs [NTT][512], red [3][NTT][512], scratch [1024], aux [1024]
+template <int NTT>
+struct GemvLds {
+  static constexpr int xs = 0;
+  static constexpr int red = NTT * kTile;
+  static constexpr int scratch = red + 3 * NTT * kTile;
+  static constexpr int aux = scratch + 1024;
+  static constexpr int floats = aux + 1024;
+};
+constexpr int kGemvLdsFloats = GemvLds<kTT>::floats;  // the largest (8 tokens per pass)
+// k_oabsorb's LDS layout (floats): split weights and maxima | o_lat [8][R] | scratch
+constexpr int kOabsOl = kTT * kTile;
+constexpr int kOabsScratch = kOabsOl + 4096;
 constexpr int kKvSlice = 64;  // kv-row columns reduced per kv-branch workgroup
 
 __device__ __forceinline__ float inv_rms(float sumsq, int n, float eps) {
@@ -88,6 +96,7 @@ __device__ __forceinline__ void wait_count(const unsigned* c, unsigned target, u
 // ---------------------------------------------------------------------------
 // k_down: index build; (x * g_in) @ [wq_a | wkv_a] split-K partials; sums of x^2
 // ---------------------------------------------------------------------------
+template <int NTT>
 __device__ void phase_down(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
   const int T = pl.T;
@@ -107,12 +116,12 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
   const int nc = min(kTile, N - c0);
   const int N1 = p.Q + p.KVR;
   const int k0 = slab * pl.ks1, ks = min(pl.ks1, p.H - k0);
-  float* xs = lds + kLdsXs;
-  float* red = lds + kLdsRed;
-  for (int t0 = 0; t0 < T; t0 += kTT) {
-    const int nt = min(kTT, T - t0);
-    u32x4 v[kUnroll];
-    gemv_first(W, N, k0, ks, c0, nc, v);
+  float* xs = lds + GemvLds<NTT>::xs;
+  float* red = lds + GemvLds<NTT>::red;
+  for (int t0 = 0; t0 < T; t0 += NTT) {
+    const int nt = min(NTT, T - t0);
+    u32x4 v[gemv_unroll(NTT)];
+    gemv_first<gemv_unroll(NTT)>(W, N, k0, ks, c0, nc, v);
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) {
       const int tt = idx / ks, r = idx % ks;
       xs[tt * kTile + r] = bf16_to_f32(p.x[(size_t)(t0 + tt) * p.H + k0 + r]) * p.g_in[k0 + r];
@@ -132,7 +141,7 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
     }
     __syncthreads();
     float* part = p.part1 + ((size_t)slab * T + t0) * N1 + (is_q ? 0 : p.Q);
-    gemv_tile(W, N, k0, ks, c0, nc, xs, kTile, nt, part, N1, red, v);
+    gemv_tile<NTT, gemv_unroll(NTT)>(W, N, k0, ks, c0, nc, xs, kTile, nt, part, N1, red, v);
   }
 }
 
@@ -141,14 +150,15 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
 // workgroups (token t, 64-column slice) reduce the kv row: kvr = alpha * acc_kv
 // and partial sums of squares of its latent columns.
 // ---------------------------------------------------------------------------
+template <int NTT>
 __device__ void phase_qup(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
   const int T = pl.T;
   const int N1 = p.Q + p.KVR;
   const int n_gemv = pl.nt2 * pl.s2;
-  float* xs = lds + kLdsXs;
-  float* red = lds + kLdsRed;
-  float* scratch = lds + kLdsScratch;
+  float* xs = lds + GemvLds<NTT>::xs;
+  float* red = lds + GemvLds<NTT>::red;
+  float* scratch = lds + GemvLds<NTT>::scratch;
   if (b >= n_gemv) {
     const int t = (b - n_gemv) / pl.nkv, sl = (b - n_gemv) % pl.nkv;
     const int c0 = sl * kKvSlice, nc = min(kKvSlice, p.KVR - c0);
@@ -170,10 +180,10 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
   const int slab = b / pl.nt2, tile = b % pl.nt2;
   const int c0 = tile * kTile, nc = min(kTile, p.N2 - c0);
   const int k0 = slab * pl.ks2, ks = min(pl.ks2, p.Q - k0);
-  for (int t0 = 0; t0 < T; t0 += kTT) {
-    const int nt = min(kTT, T - t0);
-    u32x4 v[kUnroll];
-    gemv_first(p.wq_b, p.N2, k0, ks, c0, nc, v);
+  for (int t0 = 0; t0 < T; t0 += NTT) {
+    const int nt = min(NTT, T - t0);
+    u32x4 v[gemv_unroll(NTT)];
+    gemv_first<gemv_unroll(NTT)>(p.wq_b, p.N2, k0, ks, c0, nc, v);
     // acc_a[t][k0 .. k0+ks) reduced over the down-projection's slabs
     reduce_parts4(p.part1 + (size_t)t0 * N1 + k0, (size_t)T * N1, pl.s1, nt * ks / 4, ks / 4, N1, xs, scratch);
     if (tile == 0) {
@@ -188,19 +198,20 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) xs[idx] *= p.g_q[k0 + idx % ks];
     __syncthreads();
-    gemv_tile(p.wq_b, p.N2, k0, ks, c0, nc, xs, ks, nt, p.part2 + ((size_t)slab * T + t0) * p.N2, p.N2, red, v);
+    gemv_tile<NTT, gemv_unroll(NTT)>(p.wq_b, p.N2, k0, ks, c0, nc, xs, ks, nt, p.part2 + ((size_t)slab * T + t0) * p.N2, p.N2, red, v);
   }
 }
 
 // per-token scalars: beta = alpha * inv_q (the scale of the wq_b output)
+template <int NTT>
 __device__ __forceinline__ void token_betas(const StepParams& p, int t0, int nt, float* beta, float* tmp,
                                             float* scratch) {
   const Plan& pl = p.pl;
   reduce_parts(p.ssx + t0, pl.T, pl.s1, nt, nt, 0, tmp, scratch);
-  reduce_parts(p.ssq + t0, pl.T, pl.s2, nt, nt, 0, tmp + kTT, scratch);
+  reduce_parts(p.ssq + t0, pl.T, pl.s2, nt, nt, 0, tmp + NTT, scratch);
   for (int tt = threadIdx.x; tt < nt; tt += kBlock) {
     const float a = inv_rms(tmp[tt], p.H, p.eps);
-    const float iq = 1.f / sqrtf(a * a * tmp[kTT + tt] / (float)p.Q + p.eps);
+    const float iq = 1.f / sqrtf(a * a * tmp[NTT + tt] / (float)p.Q + p.eps);
     beta[tt] = a * iq;
   }
   __syncthreads();
@@ -214,12 +225,13 @@ __device__ __forceinline__ void token_betas(const StepParams& p, int t0, int nt,
 // workgroups (one per token) finish the kv branch: kv-latent RMSNorm,
 // interleaved RoPE of the rotary part, bf16 write of the row at slot_mapping[t].
 // ---------------------------------------------------------------------------
+template <int NTT>
 __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
   const int T = pl.T;
-  float* xs = lds + kLdsXs;
-  float* red = lds + kLdsRed;
-  float* scratch = lds + kLdsScratch;
+  float* xs = lds + GemvLds<NTT>::xs;
+  float* red = lds + GemvLds<NTT>::red;
+  float* scratch = lds + GemvLds<NTT>::scratch;
   const int n_abs = p.NH * pl.ncc3;
   if (b >= n_abs) {
     const int t = b - n_abs;
@@ -241,20 +253,20 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
   }
   const int h = b / pl.ncc3, cc = b % pl.ncc3;
   const int c0 = cc * 64;
-  float* beta = lds + kLdsAux;
-  float* tmp = beta + kTT;          // [2*kTT]
-  float* qo = lds + kLdsAux + 512;  // [kTT][64]
+  float* beta = lds + GemvLds<NTT>::aux;
+  float* tmp = beta + NTT;          // [2*NTT]
+  float* qo = lds + GemvLds<NTT>::aux + 512;  // [NTT][64]
   const bf16_t* W = p.w_qabs + (size_t)h * p.DN * p.R;
-  for (int t0 = 0; t0 < T; t0 += kTT) {
-    const int nt = min(kTT, T - t0);
-    u32x4 v[kUnroll];
-    gemv_first(W, p.R, 0, p.DN, c0, 64, v);
-    token_betas(p, t0, nt, beta, tmp, scratch);
+  for (int t0 = 0; t0 < T; t0 += NTT) {
+    const int nt = min(NTT, T - t0);
+    u32x4 v[gemv_unroll(NTT)];
+    gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
+    token_betas<NTT>(p, t0, nt, beta, tmp, scratch);
     reduce_parts4(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH, (size_t)T * p.N2, pl.s2, nt * p.DN / 4,
                   p.DN / 4, p.N2, xs, scratch);
     for (int idx = threadIdx.x; idx < nt * p.DN; idx += kBlock) xs[idx] *= beta[idx / p.DN];
     __syncthreads();
-    gemv_tile(W, p.R, 0, p.DN, c0, 64, xs, p.DN, nt, qo - c0, 64, red, v);
+    gemv_tile<NTT, gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, xs, p.DN, nt, qo - c0, 64, red, v);
     for (int idx = threadIdx.x; idx < nt * 64; idx += kBlock) {
       const int tt = idx / 64, c = idx % 64;
       p.qcat[((size_t)(t0 + tt) * p.NH + h) * p.KVR + c0 + c] = f32_to_bf16(qo[tt * 64 + c] * p.scale_log2);
@@ -313,12 +325,12 @@ __device__ void phase_absorb_core(const StepParams& p, int b, char* lds) {
   const Plan& pl = p.pl;
   const int T = pl.T, n_abs = p.NH * pl.ncc3;
   if (b < T) {  // kv row of token b
-    phase_absorb(p, n_abs + b, reinterpret_cast<float*>(lds));
+    phase_absorb<kTT>(p, n_abs + b, reinterpret_cast<float*>(lds));
     count_done(p.sync);
     return;
   }
   if (b < T + n_abs) {
-    phase_absorb(p, b - T, reinterpret_cast<float*>(lds));
+    phase_absorb<kTT>(p, b - T, reinterpret_cast<float*>(lds));
     count_done(p.sync + (2 + (b - T) / pl.ncc3) * kSyncStride);
     return;
   }
@@ -352,8 +364,8 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
   float* pmL = lds;                  // [tc5][NSP]: maxima, then split weights
   float* plL = pmL + pl.tc5 * NSP;   // [tc5][NSP]
   float* linv = plL + pl.tc5 * NSP;  // [tc5]
-  float* ol = lds + kLdsRed;         // [tc5][R] (<= 4096 floats)
-  float* scratch = lds + kLdsRed + 4096;  // 256 float4
+  float* ol = lds + kOabsOl;            // [tc5][R] (<= 4096 floats)
+  float* scratch = lds + kOabsScratch;  // 256 float4
   for (int idx = tid; idx < nt * NSP; idx += kBlock) {
     const int tt = idx / NSP, s = idx % NSP;
     const size_t q = ((size_t)(t0 + tt) * NSP + s) * p.NH + h;
@@ -431,6 +443,7 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
 // ---------------------------------------------------------------------------
 // k_oproj: o_v @ o_proj_w split-K partials (this rank's partial output)
 // ---------------------------------------------------------------------------
+template <int NTT>
 __device__ void phase_oproj(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
   const int T = pl.T;
@@ -438,18 +451,18 @@ __device__ void phase_oproj(const StepParams& p, int b, float* lds) {
   const int slab = b / pl.nt6, tile = b % pl.nt6;
   const int c0 = tile * kTile, nc = min(kTile, p.H - c0);
   const int k0 = slab * pl.ks6, ks = min(pl.ks6, K - k0);
-  float* xs = lds + kLdsXs;
-  float* red = lds + kLdsRed;
-  for (int t0 = 0; t0 < T; t0 += kTT) {
-    const int nt = min(kTT, T - t0);
-    u32x4 v[kUnroll];
-    gemv_first(p.w_o, p.H, k0, ks, c0, nc, v);
+  float* xs = lds + GemvLds<NTT>::xs;
+  float* red = lds + GemvLds<NTT>::red;
+  for (int t0 = 0; t0 < T; t0 += NTT) {
+    const int nt = min(NTT, T - t0);
+    u32x4 v[gemv_unroll(NTT)];
+    gemv_first<gemv_unroll(NTT)>(p.w_o, p.H, k0, ks, c0, nc, v);
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) {
       const int tt = idx / ks, r = idx % ks;
       xs[tt * kTile + r] = p.ov[(size_t)(t0 + tt) * K + k0 + r];
     }
     __syncthreads();
-    gemv_tile(p.w_o, p.H, k0, ks, c0, nc, xs, kTile, nt, p.part6 + ((size_t)slab * T + t0) * p.H, p.H, red, v);
+    gemv_tile<NTT, gemv_unroll(NTT)>(p.w_o, p.H, k0, ks, c0, nc, xs, kTile, nt, p.part6 + ((size_t)slab * T + t0) * p.H, p.H, red, v);
   }
 }
 
