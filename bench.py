@@ -90,7 +90,8 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    ent = rec.get(workload, {}).get(kernel)
+    w = rec.get(workload, {})
+    ent = w.get(kernel) or w.get(kernel + "_m")  # matrix-core-path kernels carry an _m in their symbol
     if not ent or ent.get("source_digest") != source_digest():
         return None
     return ent.get("bytes_per_launch")
