@@ -262,13 +262,16 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   const int KVR = R + DR, QKH = d.qk_nope_head_dim + DR, N2 = d.n_heads * QKH, NH = d.n_heads;
   const int P = d.n_prior, DV = d.v_head_dim;
   pl.T = T;
-  pl.nt_q = cdiv(Q, kTile);
-  pl.nt_kv = cdiv(KVR, kTile);
+  pl.tw1 = 128;
+  pl.tw2 = 64;
+  pl.tw6 = 64;
+  pl.nt_q = cdiv(Q, pl.tw1);
+  pl.nt_kv = cdiv(KVR, pl.tw1);
   pl.nt1 = pl.nt_q + pl.nt_kv;
   choose_split(H, pl.nt1, &pl.s1, &pl.ks1);
   pl.n_idx_wg = cdiv(T * P, kBlock);
 
-  pl.nt2 = cdiv(N2, kTile);
+  pl.nt2 = cdiv(N2, pl.tw2);
   choose_split(Q, pl.nt2, &pl.s2, &pl.ks2);
   pl.nkv = cdiv(KVR, 64);
   pl.ncc3 = R / 64;
@@ -290,7 +293,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.nd5 = cdiv(DV, pl.dc5);
   pl.tc5 = std::min(T, kTT);
   pl.nt5c = cdiv(T, pl.tc5);
-  pl.nt6 = cdiv(H, kTile);
+  pl.nt6 = cdiv(H, pl.tw6);
   choose_split(NH * DV, pl.nt6, &pl.s6, &pl.ks6);
   pl.n7 = T * cdiv(H, kOutCols);
 

@@ -112,8 +112,8 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
   const bool is_q = tile < pl.nt_q;
   const bf16_t* W = is_q ? p.wq_a : p.wkv_a;
   const int N = is_q ? p.Q : p.KVR;
-  const int c0 = (is_q ? tile : tile - pl.nt_q) * kTile;
-  const int nc = min(kTile, N - c0);
+  const int c0 = (is_q ? tile : tile - pl.nt_q) * pl.tw1;
+  const int nc = min(pl.tw1, N - c0);
   const int N1 = p.Q + p.KVR;
   const int k0 = slab * pl.ks1, ks = min(pl.ks1, p.H - k0);
   float* xs = lds + GemvLds<NTT>::xs;
@@ -178,7 +178,7 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
     return;
   }
   const int slab = b / pl.nt2, tile = b % pl.nt2;
-  const int c0 = tile * kTile, nc = min(kTile, p.N2 - c0);
+  const int c0 = tile * pl.tw2, nc = min(pl.tw2, p.N2 - c0);
   const int k0 = slab * pl.ks2, ks = min(pl.ks2, p.Q - k0);
   for (int t0 = 0; t0 < T; t0 += NTT) {
     const int nt = min(NTT, T - t0);
@@ -449,7 +449,7 @@ __device__ void phase_oproj(const StepParams& p, int b, float* lds) {
   const int T = pl.T;
   const int K = p.NH * p.DV;
   const int slab = b / pl.nt6, tile = b % pl.nt6;
-  const int c0 = tile * kTile, nc = min(kTile, p.H - c0);
+  const int c0 = tile * pl.tw6, nc = min(pl.tw6, p.H - c0);
   const int k0 = slab * pl.ks6, ks = min(pl.ks6, K - k0);
   float* xs = lds + GemvLds<NTT>::xs;
   float* red = lds + GemvLds<NTT>::red;

@@ -10,9 +10,12 @@ namespace mla {
 // and n_tokens; every kernel reads the same copy.
 struct Plan {
   int T;  // tokens in this step
-  // k_down: index build + [wq_a | wkv_a] split-K GEMV (512-column tiles x slabs of hidden)
+  // GEMV-path tile widths (columns, <= 512) of the three split-K GEMVs: narrower
+  // tiles give as many workgroups with fewer slabs for the consumers to reduce
+  int tw1, tw2, tw6;
+  // k_down: index build + [wq_a | wkv_a] split-K GEMV (tw1-column tiles x slabs of hidden)
   int nt_q, nt_kv, nt1, s1, ks1, n_idx_wg;
-  // k_qup: wq_b split-K GEMV (tiles x slabs of q_lora_rank) + kv-row reduction (token x 64-column slice)
+  // k_qup: wq_b split-K GEMV (tw2-column tiles x slabs of q_lora_rank) + kv-row reduction (token x 64-column slice)
   int nt2, s2, ks2, nkv;
   // k_absorb: heads x 64-column chunks of kv_lora_rank, + one kv-finalise workgroup per token
   int ncc3;
@@ -20,7 +23,7 @@ struct Plan {
   int core_hg, core_cs, core_nhb, nsplit, ps;
   // k_oabsorb: heads x chunks of dc5 rows of v_head_dim x token chunks of tc5
   int dc5, nd5, tc5, nt5c;
-  // k_oproj: 512-column tiles over hidden x slabs of n_heads*v_head_dim
+  // k_oproj: tw6-column tiles over hidden x slabs of n_heads*v_head_dim
   int nt6, s6, ks6;
   // k_out: 64-column groups x token chunks
   int n7;
