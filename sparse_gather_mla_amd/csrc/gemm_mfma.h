@@ -8,13 +8,14 @@
 // meet the weight (two MFMAs per fragment): about 16 significant bits.  The
 // projections stay bound by the weight stream even with the matrix work doubled.
 //
-// Tiles: 16 tokens (an m-tile) x NC columns (64 or 128) x 32 k (a k-step).  A
+// Tiles: 16 tokens (an m-tile) x NC columns (64 to 256) x 32 k (a k-step).  A
 // workgroup of four waves owns one NC-column tile, one K slab and a block of
 // MTB m-tiles; the waves split the block 2 x 2 (1 x 4 for a single m-tile).
 //
-// Both operands reach LDS through direct global->LDS loads into a ring of
-// kMgDepth k-steps, so the main loop holds no compiler-visible global load and
-// its only waits are the ring's explicit vmcnt waits.
+// Both operands are loaded into registers several k-steps ahead of use (16-byte
+// global loads, non-temporal for the weight) and written to one of two LDS
+// stage buffers while the previous step's MFMAs run; the two small stages
+// leave room for several workgroups per CU.
 //   A comes from the previous kernel already in fragment order: for every
 //     (k-step, m-tile, half) a 1 KB block with lane l's eight bf16 at 16*l.
 //   B is the 32 x NC weight tile; row r keeps its 16-byte pieces XOR-swizzled
@@ -33,7 +34,6 @@ namespace mla {
 
 constexpr int kMgCols = 64;       // output columns per tile
 constexpr int kMgK = 32;          // k per step
-constexpr int kMgDepth = 8;       // ring depth in k-steps
 constexpr int kAFragElems = 512;  // bf16 per (k-step, m-tile, half) block
 
 // Offset of A[m][kk] (m < 16, kk < 32) in a 512-element fragment block.
@@ -83,9 +83,10 @@ __device__ __forceinline__ void put_a4_lds(char* ares, int mtb, int tt, int k, c
   *reinterpret_cast<uint2*>(blk + kAFragElems * 2 + e * 2) = lo;
 }
 
-// Columns per GEMM tile: 64 for one m-tile, 128 for larger token blocks (the
-// wider tile halves the activation bytes streamed per weight byte).
-__host__ __device__ constexpr int mg_cols(int mtb) { return mtb >= 2 ? 128 : 64; }
+// Columns per GEMM tile: 128 for one m-tile, 256 for larger token blocks.  A
+// wider tile streams fewer activation bytes per weight byte (the activation,
+// hi and lo, is as large per k as a 128-column weight row at 64 tokens).
+__host__ __device__ constexpr int mg_cols(int mtb) { return mtb >= 2 ? 256 : 128; }
 
 template <int MTB, int NC = mg_cols(MTB)>
 struct Mg {
@@ -96,9 +97,11 @@ struct Mg {
   static constexpr int kABytes = MTB * 2 * kAFragElems * 2;
   static constexpr int kBBytes = kMgK * NC * 2;
   static constexpr int kStep = kABytes + kBBytes;
-  static constexpr int kADma = (MTB * 128 + 255) / 256;  // A pieces per lane per step
-  static constexpr int kBDma = NC / 64;                  // B pieces per lane per step
-  static constexpr int kRing = kMgDepth * kStep;
+  static constexpr int kAPieces = (MTB * 128 + 255) / 256;  // A pieces per lane per step
+  static constexpr int kBPieces = NC / 64;                   // B pieces per lane per step
+  static constexpr int kPieces = kAPieces + kBPieces;
+  static constexpr int kAhead = NC >= 256 ? 3 : 6;           // k-steps loaded ahead into registers
+  static constexpr int kStage = 2 * kStep;                   // two LDS stage buffers
 };
 
 // Workgroup b -> (unit u, token block tb).  The token blocks of one unit sit
@@ -115,11 +118,26 @@ __device__ __forceinline__ bool mg_unit(int b, int nunits, int ntb, int& u, int&
 // bits are XORed with r mod 8 (transposing reads of four rows hit distinct banks).
 __device__ __forceinline__ int bswz(int pc, int r) { return (pc & ~7) | ((pc & 7) ^ (r & 7)); }
 
-// Sources of this lane's pieces of a 32 x NC weight tile at k-step 0.
+// Sixteen-byte operand pieces of one k-step held in registers.
+template <int NV>
+struct Pieces {
+  u32x4_t v[NV];
+};
+
+__device__ __forceinline__ u32x4_t load16(const bf16_t* src) { return *reinterpret_cast<const u32x4_t*>(src); }
+// Weights are read once per step: non-temporal loads, which stream from HBM at
+// more than twice the rate of cached ones on this chip.
+__device__ __forceinline__ u32x4_t load16_nt(const bf16_t* src) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+}
+__device__ __forceinline__ void store16(char* dst, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(dst) = v; }
+
+// This lane's pieces of a 32 x NC weight tile at k-step 0.  Piece i is LDS
+// slot q = 256 i + tid: row r = q / (NC/8), swizzled 16-byte column piece.
 template <int NC>
 struct BTileSrc {
   const bf16_t* p[NC / 64];  // nullptr: the piece's columns lie past N
-  int row[NC / 64];          // the piece's row at k-step 0; rows >= K read zeros
+  int row[NC / 64];          // the piece's row at k-step 0; rows >= K read as zeros
   size_t step;               // elements per k-step
   int K;
 };
@@ -129,7 +147,7 @@ __device__ __forceinline__ BTileSrc<NC> btile_src(const bf16_t* W, int K, int N,
   BTileSrc<NC> s;
 #pragma unroll
   for (int i = 0; i < NC / 64; ++i) {
-    const int q = i * 256 + threadIdx.x;  // LDS slot of this piece
+    const int q = i * 256 + threadIdx.x;
     const int r = q / (NC / 8), pc = bswz(q % (NC / 8), r);
     const int col = c0 + 8 * pc;
     s.p[i] = (col < N) ? W + (size_t)(k0 + r) * N + col : nullptr;
@@ -138,33 +156,6 @@ __device__ __forceinline__ BTileSrc<NC> btile_src(const bf16_t* W, int K, int N,
   s.step = (size_t)kMgK * N;
   s.K = K;
   return s;
-}
-
-// NC/64 direct loads per lane: k-step st of the weight tile into bufB.
-template <int NC>
-__device__ __forceinline__ void issue_btile(const BTileSrc<NC>& s, int st, bool live, char* bufB,
-                                            const void* zero16) {
-#pragma unroll
-  for (int i = 0; i < NC / 64; ++i) {
-    const void* src = zero16;
-    if (live && s.p[i] && s.row[i] + kMgK * st < s.K) src = s.p[i] + s.step * st;
-    dma16(src, bufB + (i * 256 + (threadIdx.x & ~63)) * 16);
-  }
-}
-
-// kADma direct loads per lane: the MTB m-tiles of k-step ks (both halves, contiguous) into bufA.
-template <int MTB>
-__device__ __forceinline__ void issue_atile(const bf16_t* A, int mt_pad, int mt0, int ks, bool live, char* bufA,
-                                            char* sink, const void* zero16) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < Mg<MTB>::kADma; ++i) {
-    const int q0 = i * 256 + wave * 64;  // first piece of this wave's load
-    const bool in = q0 < MTB * 128;
-    const void* src = zero16;
-    if (in && live) src = A + ((size_t)ks * mt_pad + mt0) * (2 * kAFragElems) + (size_t)(q0 + lane) * 8;
-    dma16(src, in ? bufA + q0 * 16 : sink);
-  }
 }
 
 // One k-step: B fragments by transposing reads, A fragments (hi, lo), MFMAs.
@@ -199,43 +190,55 @@ __device__ __forceinline__ void mg_step(const char* bufA, const char* bufB,
   }
 }
 
-// Pipelined loop over nsteps k-steps.  issue(st, buf) issues exactly NDMA
-// direct loads per lane for step st (loads of zeros once st >= nsteps);
-// step(st, buf) consumes a landed step.  Returns with every load landed and
-// the ring free.
-// The ring's first DEPTH-1 steps; issue them as early as possible (before
-// work the loop does not depend on), then run mg_ring_loop.
-template <int DEPTH = kMgDepth, class Issue>
-__device__ __forceinline__ void mg_ring_prologue(char* ring, int step_bytes, Issue&& issue) {
+// Pipelined loop over nsteps k-steps.  load(st) returns this lane's pieces of
+// step st (zeros once st >= nsteps; it must issue the same loads on every call,
+// reading a zero buffer where there is no data, or the compiler's waits for
+// the oldest loads degrade to waits for all of them); store(pieces,
+// buf) writes them to an LDS stage buffer; step(st, buf) consumes a stage.
+// Steps are loaded P ahead; stage st % 2 is written during step st - 1 and
+// read after the barrier that ends it.  Returns with both stages free.
+// The prologue (the first P loads) may be issued early, before work the loop
+// does not depend on.
+template <int NV, int P, class Load>
+__device__ __forceinline__ void mg_pipe_prologue(Pieces<NV> (&q)[P], Load&& load) {
 #pragma unroll
-  for (int s = 0; s < DEPTH - 1; ++s) issue(s, ring + s * step_bytes);
+  for (int j = 0; j < P; ++j) q[j] = load(j);
 }
 
-template <int NDMA, int DEPTH = kMgDepth, class Issue, class Step>
-__device__ __forceinline__ void mg_ring_loop(int nsteps, char* ring, int step_bytes, Issue&& issue, Step&& step) {
-  static_assert(NDMA * (DEPTH - 2) < 64, "vmcnt range");
-  for (int s = 0; s < nsteps; ++s) {
-    wait_vmcnt<NDMA * (DEPTH - 2)>();  // step s landed (this wave's oldest loads)
-    __syncthreads();                   // ... for every wave; buffer of step s-1 consumed
-    const int sn = s + DEPTH - 1;
-    issue(sn, ring + (sn % DEPTH) * step_bytes);
-    step(s, ring + (s % DEPTH) * step_bytes);
-  }
-  wait_vmcnt<0>();
+template <int NV, int P, class Load, class Store, class Step>
+__device__ __forceinline__ void mg_pipe_loop(Pieces<NV> (&q)[P], int nsteps, char* stage, int step_bytes,
+                                             Load&& load, Store&& store, Step&& step) {
+  store(q[0], stage);
+  q[0] = load(P);
   __syncthreads();
+  for (int s0 = 0; s0 < nsteps; s0 += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int s = s0 + j;
+      if (s >= nsteps) break;
+      step(s, stage + (s & 1) * step_bytes);
+      // unconditional, also past the last step: stage (s+1) % 2 was last read
+      // by step s-1, which every wave finished before the previous barrier
+      store(q[(j + 1) % P], stage + ((s + 1) & 1) * step_bytes);
+      q[(j + 1) % P] = load(s + 1 + P);
+      __syncthreads();
+    }
+  }
 }
 
-template <int NDMA, int DEPTH = kMgDepth, class Issue, class Step>
-__device__ __forceinline__ void mg_ring(int nsteps, char* ring, int step_bytes, Issue&& issue, Step&& step) {
-  mg_ring_prologue<DEPTH>(ring, step_bytes, issue);
-  mg_ring_loop<NDMA, DEPTH>(nsteps, ring, step_bytes, issue, step);
+template <int NV, int P, class Load, class Store, class Step>
+__device__ __forceinline__ void mg_pipe(int nsteps, char* stage, int step_bytes, Load&& load, Store&& store,
+                                        Step&& step) {
+  Pieces<NV> q[P];
+  mg_pipe_prologue(q, load);
+  mg_pipe_loop(q, nsteps, stage, step_bytes, load, store, step);
 }
 
 // acc = A[token block] @ W[k0 : k0 + 32*nks, c0 : c0 + NC] with A from a
 // global fragment-order buffer (its m-tiles mt0 .. mt0+MTB-1).
 template <int MTB, int NC = mg_cols(MTB)>
 __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, const bf16_t* W, int K, int N, int k0,
-                                      int nks, int c0, const void* zero16, char* ring, char* sink,
+                                      int nks, int c0, const bf16_t* zero16, char* stage,
                                       f32x4_t (&acc)[Mg<MTB, NC>::MTW][Mg<MTB, NC>::NTW]) {
   using S = Mg<MTB, NC>;
 #pragma unroll
@@ -244,12 +247,36 @@ __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, cons
     for (int nt = 0; nt < S::NTW; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const BTileSrc<NC> bs = btile_src<NC>(W, K, N, k0, c0);
   const int ks0 = k0 / kMgK;
-  mg_ring<S::kADma + S::kBDma>(
-      nks, ring, S::kStep,
-      [&](int st, char* buf) {
+  const int tid = threadIdx.x;
+  const bf16_t* Ab = A + ((size_t)ks0 * mt_pad + mt0) * (2 * kAFragElems) + (size_t)tid * 8;
+  const size_t astep = (size_t)mt_pad * 2 * kAFragElems;
+  mg_pipe<S::kPieces, S::kAhead>(
+      nks, stage, S::kStep,
+      [&](int st) {
+        // every piece is loaded (zeros from zero16 where there is no data), so
+        // the loads stay unconditional and the compiler's vmcnt waits exact
+        Pieces<S::kPieces> r;
         const bool live = st < nks;
-        issue_atile<MTB>(A, mt_pad, mt0, ks0 + st, live, buf, sink, zero16);
-        issue_btile<NC>(bs, st, live, buf + S::kABytes, zero16);
+#pragma unroll
+        for (int i = 0; i < S::kAPieces; ++i) {
+          const bf16_t* src = zero16;
+          if (live && i * 256 + tid < MTB * 128) src = Ab + astep * st + i * 256 * 8;
+          r.v[i] = load16(src);
+        }
+#pragma unroll
+        for (int i = 0; i < S::kBPieces; ++i) {
+          const bf16_t* src = zero16;
+          if (live && bs.p[i] && bs.row[i] + kMgK * st < bs.K) src = bs.p[i] + bs.step * st;
+          r.v[S::kAPieces + i] = load16_nt(src);
+        }
+        return r;
+      },
+      [&](const Pieces<S::kPieces>& r, char* buf) {
+#pragma unroll
+        for (int i = 0; i < S::kAPieces; ++i)
+          if (i * 256 + tid < MTB * 128) store16(buf + (i * 256 + tid) * 16, r.v[i]);
+#pragma unroll
+        for (int i = 0; i < S::kBPieces; ++i) store16(buf + S::kABytes + (i * 256 + tid) * 16, r.v[S::kAPieces + i]);
       },
       [&](int, const char* buf) { mg_step<MTB, NC>(buf, buf + S::kABytes, acc); });
 }

@@ -80,9 +80,8 @@ __global__ __launch_bounds__(kBlock) void k_prep(StepParams p) {
 
 template <int MTB>
 __global__ __launch_bounds__(kBlock) void k_down_m(StepParams p) {
-  __shared__ __attribute__((aligned(16))) char ring[Mg<MTB>::kRing];
-  __shared__ __attribute__((aligned(16))) char sink[1024];
-  phase_down_m<MTB>(p, blockIdx.x, ring, sink);
+  __shared__ __attribute__((aligned(16))) char stage[Mg<MTB>::kStage];
+  phase_down_m<MTB>(p, blockIdx.x, stage);
 }
 
 __global__ __launch_bounds__(kBlock) void k_qa(StepParams p) {
@@ -92,9 +91,8 @@ __global__ __launch_bounds__(kBlock) void k_qa(StepParams p) {
 
 template <int MTB>
 __global__ __launch_bounds__(kBlock) void k_qup_m(StepParams p) {
-  __shared__ __attribute__((aligned(16))) char ring[Mg<MTB>::kRing];
-  __shared__ __attribute__((aligned(16))) char sink[1024];
-  phase_qup_m<MTB>(p, blockIdx.x, ring, sink);
+  __shared__ __attribute__((aligned(16))) char stage[Mg<MTB>::kStage];
+  phase_qup_m<MTB>(p, blockIdx.x, stage);
 }
 
 template <int MTB>
@@ -113,9 +111,8 @@ __global__ __launch_bounds__(kBlock) void k_oabsorb_m(StepParams p) {
 
 template <int MTB>
 __global__ __launch_bounds__(kBlock) void k_oproj_m(StepParams p) {
-  __shared__ __attribute__((aligned(16))) char ring[Mg<MTB>::kRing];
-  __shared__ __attribute__((aligned(16))) char sink[1024];
-  phase_oproj_m<MTB>(p, blockIdx.x, ring, sink);
+  __shared__ __attribute__((aligned(16))) char stage[Mg<MTB>::kStage];
+  phase_oproj_m<MTB>(p, blockIdx.x, stage);
 }
 
 __global__ __launch_bounds__(kBlock) void k_zero_u32(uint32_t* p, size_t n) {
@@ -176,7 +173,8 @@ constexpr int kGemvMaxTokens = kTT;  // more tokens: projections on the matrix c
 // Matrix-core split-K: about `target` workgroups over `units` (tile, token
 // block) pairs, slabs of at least 8 k-steps.
 void split_m(int kt, int units, int target, int* s_out, int* ks_out) {
-  int s = cdiv(target, units);
+  // at most `target` workgroups: one more would start a second round on some CU
+  int s = target / units;
   s = clampi(s, 1, std::max(1, kt / 8));
   const int ks = cdiv(kt, s);
   *ks_out = ks;
@@ -186,7 +184,7 @@ void split_m(int kt, int units, int target, int* s_out, int* ks_out) {
 int mg_grid(int nunits, int ntb) { return cdiv(nunits, 8) * 8 * ntb; }
 
 size_t absorb_lds_bytes(const Plan& pl, int DN) {
-  return (size_t)kMgDepth * Mg<1>::kBBytes + 1024 + 256 + (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2 * kAFragElems * 2;
+  return (size_t)2 * Mg<1, kMgCols>::kBBytes + kAbsorbBetaBytes + (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2 * kAFragElems * 2;
 }
 
 size_t oabsorb_lds_bytes(const Plan& pl, int R) { return 256 + (size_t)(R / kMgK) * pl.mtb5 * 2 * kAFragElems * 2; }
@@ -198,12 +196,13 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   const int P = d.n_prior, DV = d.v_head_dim, DN = d.qk_nope_head_dim;
   const int T = pl.T;
   pl.mfma = 1;
-  pl.mtb = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
+  pl.mtb = T <= 16 ? 1 : (T <= 32 ? 2 : (T <= 64 ? 4 : 8));
   pl.ntb = cdiv(T, 16 * pl.mtb);
   pl.mt_pad = pl.ntb * pl.mtb;
-  // about one workgroup per CU for the 128-column tiles (96-128 KB rings), two otherwise
+  // about one workgroup per CU for the 256-column tiles, two for the narrower
+  // ones (more split-K slabs would add partial-sum traffic for little gain)
   const int nc = mg_cols(pl.mtb);
-  const int target = nc == 128 ? 256 : 512;
+  const int target = nc >= 256 ? 256 : 512;
   pl.kt1 = cdiv(H, kMgK);
   pl.ntq1m = cdiv(Q, nc);
   pl.nt1m = pl.ntq1m + cdiv(KVR, nc);
@@ -212,7 +211,7 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   pl.nt2m = cdiv(N2, nc);
   split_m(pl.kt2, pl.nt2m * pl.ntb, target, &pl.s2, &pl.ks2m);
   pl.nct3 = R / kMgCols;
-  pl.mtb3 = pl.mtb;
+  pl.mtb3 = std::min(pl.mtb, 4);  // 128-token blocks measured slower here
   while (pl.mtb3 > 1 && (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2048 > 96 * 1024) pl.mtb3 /= 2;
   pl.ntb3 = cdiv(T, 16 * pl.mtb3);
   // as many tiles per workgroup as keep at least 128 workgroups busy
@@ -439,9 +438,15 @@ size_t gemv_lds_bytes(int ntt) {
 
 int gemv_ntt(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)); }
 
-step_kernel_t pick_down_m(int mtb) { return mtb == 1 ? k_down_m<1> : (mtb == 2 ? k_down_m<2> : k_down_m<4>); }
-step_kernel_t pick_qup_m(int mtb) { return mtb == 1 ? k_qup_m<1> : (mtb == 2 ? k_qup_m<2> : k_qup_m<4>); }
-step_kernel_t pick_oproj_m(int mtb) { return mtb == 1 ? k_oproj_m<1> : (mtb == 2 ? k_oproj_m<2> : k_oproj_m<4>); }
+step_kernel_t pick_down_m(int mtb) {
+  return mtb == 1 ? k_down_m<1> : (mtb == 2 ? k_down_m<2> : (mtb == 4 ? k_down_m<4> : k_down_m<8>));
+}
+step_kernel_t pick_qup_m(int mtb) {
+  return mtb == 1 ? k_qup_m<1> : (mtb == 2 ? k_qup_m<2> : (mtb == 4 ? k_qup_m<4> : k_qup_m<8>));
+}
+step_kernel_t pick_oproj_m(int mtb) {
+  return mtb == 1 ? k_oproj_m<1> : (mtb == 2 ? k_oproj_m<2> : (mtb == 4 ? k_oproj_m<4> : k_oproj_m<8>));
+}
 step_kernel_t pick_absorb_m(int mtb) { return mtb == 1 ? k_absorb_m<1> : (mtb == 2 ? k_absorb_m<2> : k_absorb_m<4>); }
 step_kernel_t pick_oabsorb_m(int) { return k_oabsorb_m<1>; }
 

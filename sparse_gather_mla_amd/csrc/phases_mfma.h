@@ -84,7 +84,7 @@ __device__ __forceinline__ float mfma_beta(const StepParams& p, int t) {
 // k_down: split-K partials of A1 @ [wq_a | wkv_a] (wq_a's tiles first)
 // ---------------------------------------------------------------------------
 template <int MTB>
-__device__ void phase_down_m(const StepParams& p, int b, char* ring, char* sink) {
+__device__ void phase_down_m(const StepParams& p, int b, char* stage) {
   const Plan& pl = p.pl;
   int u, tb;
   if (!mg_unit(b, pl.nt1m * pl.s1, pl.ntb, u, tb)) return;
@@ -97,7 +97,7 @@ __device__ void phase_down_m(const StepParams& p, int b, char* ring, char* sink)
   const int k0 = slab * pl.ks1m * kMgK;
   const int nks = min(pl.ks1m, pl.kt1 - slab * pl.ks1m);
   f32x4_t acc[Mg<MTB>::MTW][Mg<MTB>::NTW];
-  mgemm<MTB>(p.a1, pl.mt_pad, tb * MTB, W, p.H, N, k0, nks, c0, p.zero16, ring, sink, acc);
+  mgemm<MTB>(p.a1, pl.mt_pad, tb * MTB, W, p.H, N, k0, nks, c0, reinterpret_cast<const bf16_t*>(p.zero16), stage, acc);
   const int N1 = p.Q + p.KVR, T = pl.T;
   float* out = p.part1 + (size_t)slab * T * N1 + (is_q ? 0 : p.Q);
   mg_for_outputs<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, float v) {
@@ -190,7 +190,7 @@ __device__ void phase_qa(const StepParams& p, int b, float* lds) {
 // k_qup: split-K partials of A2 @ wq_b
 // ---------------------------------------------------------------------------
 template <int MTB>
-__device__ void phase_qup_m(const StepParams& p, int b, char* ring, char* sink) {
+__device__ void phase_qup_m(const StepParams& p, int b, char* stage) {
   const Plan& pl = p.pl;
   int u, tb;
   if (!mg_unit(b, pl.nt2m * pl.s2, pl.ntb, u, tb)) return;
@@ -200,7 +200,7 @@ __device__ void phase_qup_m(const StepParams& p, int b, char* ring, char* sink) 
   const int k0 = slab * pl.ks2m * kMgK;
   const int nks = min(pl.ks2m, pl.kt2 - slab * pl.ks2m);
   f32x4_t acc[Mg<MTB>::MTW][Mg<MTB>::NTW];
-  mgemm<MTB>(p.a2, pl.mt_pad, tb * MTB, p.wq_b, p.Q, p.N2, k0, nks, c0, p.zero16, ring, sink, acc);
+  mgemm<MTB>(p.a2, pl.mt_pad, tb * MTB, p.wq_b, p.Q, p.N2, k0, nks, c0, reinterpret_cast<const bf16_t*>(p.zero16), stage, acc);
   const int T = pl.T;
   float* out = p.part2 + (size_t)slab * T * p.N2;
   mg_for_outputs<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, float v) {
@@ -210,12 +210,15 @@ __device__ void phase_qup_m(const StepParams& p, int b, char* ring, char* sink) 
 
 // ---------------------------------------------------------------------------
 // k_absorb: workgroup (head h, group of tpw3 64-column tiles of kv_lora_rank,
-// token block).  The ring streams the group's tiles of q_absorb_w[h] (ceil(DN/32)
-// k-steps each) from the start; meanwhile A3 = beta * q_nope (wq_b slabs summed
-// in order) goes to LDS in fragment order, once for all the group's tiles.  Each tile's q_lat lands in Qcat
-// as bf16, pre-scaled by softmax_scale * log2(e); q_pe is roped into Qcat too.
-// LDS: ring (kMgDepth x 4 KB) | sink (1 KB) | beta (256 B) | A3 (ceil(DN/32) x MTB x 2 KB).
+// token block).  The pipeline streams the group's tiles of q_absorb_w[h]
+// (ceil(DN/32) k-steps each); its first loads go out before A3 = beta * q_nope
+// (wq_b slabs summed in order) is written to LDS in fragment order, once for
+// all the group's tiles.  Each tile's q_lat lands in Qcat as bf16, pre-scaled
+// by softmax_scale * log2(e); q_pe is roped into Qcat too.
+// LDS: stages (2 x 4 KB) | beta (512 B) | A3 (ceil(DN/32) x MTB x 2 KB).
 // ---------------------------------------------------------------------------
+constexpr int kAbsorbBetaBytes = 512;  // beta of up to 128 tokens
+
 template <int MTB>
 __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   using S = Mg<MTB, kMgCols>;
@@ -228,20 +231,25 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   const int t0 = tb * MTB * 16;
   const int KS = (p.DN + kMgK - 1) / kMgK;
   const int nsteps = pl.tpw3 * KS;
-  char* ring = lds;
-  float* beta = reinterpret_cast<float*>(lds + kMgDepth * S::kBBytes + 1024);
-  char* ares = lds + kMgDepth * S::kBBytes + 1024 + 256;
+  static_assert(MTB * 16 * 4 <= kAbsorbBetaBytes, "beta region");
+  char* stage = lds;
+  float* beta = reinterpret_cast<float*>(lds + 2 * S::kBBytes);
+  char* ares = lds + 2 * S::kBBytes + kAbsorbBetaBytes;
   // this lane's piece of a 32 x 64 weight tile (row r, swizzled 16-byte piece pc)
   const bf16_t* W = p.w_qabs + (size_t)h * p.DN * p.R;
   const int r = tid >> 3, pc = (tid & 7) ^ (r & 7);
-  auto issue = [&](int st, char* buf) {
+  auto load = [&](int st) {
+    Pieces<1> q;
     const int j = j0 + st / KS, ks = st % KS;
     const int row = ks * kMgK + r;
-    const void* src = p.zero16;
+    const bf16_t* src = reinterpret_cast<const bf16_t*>(p.zero16);
     if (st < nsteps && row < p.DN) src = W + (size_t)row * p.R + j * kMgCols + 8 * pc;
-    dma16(src, buf + (tid >> 6) * 1024);
+    q.v[0] = load16_nt(src);
+    return q;
   };
-  mg_ring_prologue(ring, S::kBBytes, issue);
+  constexpr int P = 8;
+  Pieces<1> q[P];
+  mg_pipe_prologue(q, load);
   if (tid < MTB * 16) beta[tid] = (t0 + tid < T) ? mfma_beta(p, t0 + tid) : 0.f;
   __syncthreads();
   for (int idx = tid; idx < MTB * 16 * KS * 8; idx += kBlock) {
@@ -264,16 +272,18 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
       for (int nt = 0; nt < S::NTW; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
   zero();
-  mg_ring_loop<1>(nsteps, ring, S::kBBytes, issue, [&](int st, const char* buf) {
-    const int j = j0 + st / KS, ks = st % KS;
-    mg_step<MTB, kMgCols>(ares + ks * S::kABytes, buf, acc);
-    if (ks == KS - 1) {  // tile j complete
-      mg_for_outputs<MTB, kMgCols>(acc, t0, j * kMgCols, [&](int t, int c, float v) {
-        if (t < T) p.qcat[((size_t)t * p.NH + h) * p.KVR + c] = f32_to_bf16(v * p.scale_log2);
+  mg_pipe_loop(
+      q, nsteps, stage, S::kBBytes, load, [&](const Pieces<1>& v, char* buf) { store16(buf + tid * 16, v.v[0]); },
+      [&](int st, const char* buf) {
+        const int j = j0 + st / KS, ks = st % KS;
+        mg_step<MTB, kMgCols>(ares + ks * S::kABytes, buf, acc);
+        if (ks == KS - 1) {  // tile j complete
+          mg_for_outputs<MTB, kMgCols>(acc, t0, j * kMgCols, [&](int t, int c, float v) {
+            if (t < T) p.qcat[((size_t)t * p.NH + h) * p.KVR + c] = f32_to_bf16(v * p.scale_log2);
+          });
+          zero();
+        }
       });
-      zero();
-    }
-  });
   if (j0 != 0) return;  // the first tile group also ropes q_pe
   const int half = p.DR / 2;
   for (int idx = tid; idx < MTB * 16 * half; idx += kBlock) {
@@ -382,7 +392,7 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (dok && ks + q < KS) v = *reinterpret_cast<const u32x4_t*>(wrow + kMgK * (ks + q));
+        if (dok && ks + q < KS) v = load16_nt(wrow + kMgK * (ks + q));
         bfr[q] = __builtin_bit_cast(bf16x8_t, v);
       }
 #pragma unroll
@@ -430,7 +440,7 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
 // k_oproj: split-K partials of A5 @ o_proj_w
 // ---------------------------------------------------------------------------
 template <int MTB>
-__device__ void phase_oproj_m(const StepParams& p, int b, char* ring, char* sink) {
+__device__ void phase_oproj_m(const StepParams& p, int b, char* stage) {
   const Plan& pl = p.pl;
   int u, tb;
   if (!mg_unit(b, pl.nt6m * pl.s6, pl.ntb, u, tb)) return;
@@ -440,7 +450,7 @@ __device__ void phase_oproj_m(const StepParams& p, int b, char* ring, char* sink
   const int k0 = slab * pl.ks6m * kMgK;
   const int nks = min(pl.ks6m, pl.kt6 - slab * pl.ks6m);
   f32x4_t acc[Mg<MTB>::MTW][Mg<MTB>::NTW];
-  mgemm<MTB>(p.a5, pl.mt_pad, tb * MTB, p.w_o, p.NH * p.DV, p.H, k0, nks, c0, p.zero16, ring, sink, acc);
+  mgemm<MTB>(p.a5, pl.mt_pad, tb * MTB, p.w_o, p.NH * p.DV, p.H, k0, nks, c0, reinterpret_cast<const bf16_t*>(p.zero16), stage, acc);
   const int T = pl.T;
   float* out = p.part6 + (size_t)slab * T * p.H;
   mg_for_outputs<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, float v) {
