@@ -279,17 +279,18 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.core_cs = cs.cs;
   pl.core_nhb = cdiv(NH, 16 * cs.hg);
   {
-    // about one workgroup per CU, at most 16 splits (the combine reads every split)
+    // about one workgroup per CU.  The matrix-core path's combine kernel reads
+    // every split for every column, so it keeps at most 16; the GEMV path's
+    // output absorption reads each split once per column chunk.
     int ns = cdiv(256, T * pl.core_nhb);
-    ns = std::min(ns, 16);
+    ns = std::min(ns, T > kGemvMaxTokens ? 16 : 64);
     ns = clampi(ns, cdiv(P, kMaxSplitRows), cdiv(P, kCoreChunk));
     pl.ps = cdiv(cdiv(P, ns), kCoreChunk) * kCoreChunk;
     pl.nsplit = cdiv(P, pl.ps);
   }
   if (T > kGemvMaxTokens) return make_plan_mfma(d, pl);
   pl.fused = (d.flags & MLA_GD_FLAG_FUSED) && pl.core_hg == 1 && pl.core_cs == 4;
-  pl.dc5 = 16;
-  pl.nd5 = cdiv(DV, pl.dc5);
+  pl.nc5 = R / kOabsCols;
   pl.tc5 = std::min(T, kTT);
   pl.nt5c = cdiv(T, pl.tc5);
   pl.nt6 = cdiv(H, pl.tw6);
@@ -316,7 +317,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.off_pm = take((size_t)T * pl.nsplit * NH * f);
   pl.off_pl = take((size_t)T * pl.nsplit * NH * f);
   pl.off_po = take((size_t)T * pl.nsplit * NH * R * f);
-  pl.off_ov = take((size_t)T * NH * DV * f);
+  pl.off_ov = take((size_t)pl.nc5 * T * NH * DV * f);
   pl.off_part6 = take((size_t)pl.s6 * T * H * f);
   pl.total = off;
   return pl;
@@ -554,7 +555,7 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     mark(2);
     hipLaunchKernelGGL(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, 0, s, p);
     mark(3);
-    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), blk, gl, s, p);
+    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl, s, p);
     mark(4);
     hipLaunchKernelGGL(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll, s, p);
     mark(5);
@@ -569,7 +570,7 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     mark(3);
     hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
     mark(4);
-    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nd5 * pl.nt5c), blk, gl, s, p);
+    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl, s, p);
     mark(5);
     hipLaunchKernelGGL(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll, s, p);
     mark(6);

@@ -338,62 +338,71 @@ __device__ void phase_absorb_core(const StepParams& p, int b, char* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// k_oabsorb: combine the core's split partials of head h into o_lat (softmax
-// normalisation; a token with no valid entry gets zeros), then
-// o_v[t, h*DV + d] = out_absorb_w[h, d, :] . o_lat[t, h, :] for dc5 rows d.
-// The weight rows are loaded first; the combine runs in parallel over splits.
+// k_oabsorb: workgroup (head h, 64-column chunk j of kv_lora_rank, token
+// chunk).  It combines the core's split partials of its columns into o_lat
+// (softmax normalisation; a token with no valid entry gets zeros) and forms
+// the chunk's share of o_v for every row d:
+//   ovp[j][t][h*DV + d] = out_absorb_w[h, d, 64j : 64j+64] . o_lat[t, h, 64j : 64j+64]
+// k_oproj adds the chunks' shares in chunk order.  Splitting by latent column
+// keeps each split partial read once, however many splits the core made.
+// The first weight pieces are loaded before the combine.
 // ---------------------------------------------------------------------------
+constexpr int kOabsCols = 64;    // latent columns per workgroup
+constexpr int kOabsPieces = 4;   // 16-byte weight pieces per lane per pass: 128 rows x 8 pieces
+constexpr int kMaxOabsChunks = 8;  // kv_lora_rank <= 512
+
 __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
-  const int T = pl.T, NSP = pl.nsplit, R = p.R;
-  const int per_h = pl.nd5 * pl.nt5c;
+  const int T = pl.T, NSP = pl.nsplit, R = p.R, DV = p.DV;
+  const int per_h = pl.nc5 * pl.nt5c;
   const int h = b / per_h, rem = b % per_h;
-  const int dch = rem / pl.nt5c, tch = rem % pl.nt5c;
+  const int j = rem / pl.nt5c, tch = rem % pl.nt5c;
   const int t0 = tch * pl.tc5, nt = min(pl.tc5, T - t0);
-  const int d0 = dch * pl.dc5, nd = min(pl.dc5, p.DV - d0);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // weight rows d0 + wv + 4j, 8 columns per lane (R <= 512)
-  constexpr int kRowsPerWave = 4;  // dc5 = 16 rows over 4 waves
-  u32x4 wr[kRowsPerWave];
+  const int c0 = j * kOabsCols;
+  const int tid = threadIdx.x;
+  // piece q = i*256 + tid of a 128-row pass: row q / 8, columns c0 + 8*(q % 8) .. +8
+  const bf16_t* W = p.w_oabs + (size_t)h * DV * R + c0;
+  auto load_pass = [&](int d0, u32x4 (&wr)[kOabsPieces]) {
 #pragma unroll
-  for (int j = 0; j < kRowsPerWave; ++j) {
-    const int dd = wv + 4 * j, c = 8 * lane;
-    wr[j] = u32x4{0u, 0u, 0u, 0u};
-    if (dd < nd && c < R) wr[j] = ld_stream(p.w_oabs + ((size_t)h * p.DV + d0 + dd) * R + c);
-  }
-  float* pmL = lds;                  // [tc5][NSP]: maxima, then split weights
-  float* plL = pmL + pl.tc5 * NSP;   // [tc5][NSP]
-  float* linv = plL + pl.tc5 * NSP;  // [tc5]
-  float* ol = lds + kOabsOl;            // [tc5][R] (<= 4096 floats)
-  float* scratch = lds + kOabsScratch;  // 256 float4
-  for (int idx = tid; idx < nt * NSP; idx += kBlock) {
-    const int tt = idx / NSP, s = idx % NSP;
-    const size_t q = ((size_t)(t0 + tt) * NSP + s) * p.NH + h;
-    pmL[idx] = p.pm[q];
-    plL[idx] = p.pden[q];
-  }
-  __syncthreads();
-  if (tid < nt) {
-    float M = -INFINITY;
-    for (int s = 0; s < NSP; ++s) M = fmaxf(M, pmL[tid * NSP + s]);
-    float L = 0.f;
-    for (int s = 0; s < NSP; ++s) {
-      const float w = (M == -INFINITY) ? 0.f : exp2f(pmL[tid * NSP + s] - M);
-      pmL[tid * NSP + s] = w;
-      L = fmaf(plL[tid * NSP + s], w, L);
+    for (int i = 0; i < kOabsPieces; ++i) {
+      const int q = i * kBlock + tid, d = d0 + (q >> 3);
+      wr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (d < DV) wr[i] = ld_stream(W + (size_t)d * R + 8 * (q & 7));
     }
-    linv[tid] = (L > 0.f) ? 1.f / L : 0.f;
+  };
+  u32x4 wr[kOabsPieces];
+  load_pass(0, wr);
+  float* pmL = lds;                  // [tc5][NSP]: split weights
+  float* linv = pmL + pl.tc5 * NSP;  // [tc5]
+  float* ol = lds + kOabsOl;            // [tc5][64]
+  float* scratch = lds + kOabsScratch;  // 256 float4
+  // split weights w_s = 2^(m_s - M) and 1/L, L = sum_s w_s * l_s: a wave per
+  // token, a lane per split (at most 64 splits on this path); the butterfly
+  // sums leave the same value in every lane
+  {
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int tt = wv; tt < nt; tt += kBlock / kWave) {
+      const size_t q = ((size_t)(t0 + tt) * NSP + lane) * p.NH + h;
+      const float m = lane < NSP ? p.pm[q] : -INFINITY;
+      const float l = lane < NSP ? p.pden[q] : 0.f;
+      const float M = wave_max(m);
+      const float w = (M == -INFINITY || lane >= NSP) ? 0.f : exp2f(m - M);
+      const float L = wave_sum(l * w);
+      if (lane < NSP) pmL[tt * NSP + lane] = w;
+      if (lane == 0) linv[tt] = (L > 0.f) ? 1.f / L : 0.f;
+    }
   }
   __syncthreads();
-  // o_lat[tt][c] = linv * sum_s w_s * po[t][s][h][c]; float4 items, splits in parallel parts
+  // o_lat[tt][c] = linv * sum_s w_s * po[t][s][h][c0 + c]: float4 items, splits in parallel parts
   {
-    const int n4 = nt * (R / 4);
+    constexpr int C4 = kOabsCols / 4;
+    const int n4 = nt * C4;
     const int nsp = max(1, min(16, kBlock / n4));
     float4* out = reinterpret_cast<float4*>(nsp == 1 ? ol : scratch);
     for (int idx = tid; idx < n4 * nsp; idx += kBlock) {
       const int i = idx % n4, sp = idx / n4;
-      const int tt = i / (R / 4), c4 = i % (R / 4);
-      const float* src = p.po + ((size_t)(t0 + tt) * NSP * p.NH + h) * R + 4 * c4;
+      const int tt = i / C4, c4 = i % C4;
+      const float* src = p.po + ((size_t)(t0 + tt) * NSP * p.NH + h) * R + c0 + 4 * c4;
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int s = sp; s < NSP; s += nsp) {
         const float w = pmL[tt * NSP + s];
@@ -418,24 +427,28 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
       }
       __syncthreads();
     }
-    for (int i = tid; i < nt * R; i += kBlock) ol[i] *= linv[i / R];
+    for (int i = tid; i < nt * kOabsCols; i += kBlock) ol[i] *= linv[i / kOabsCols];
     __syncthreads();
   }
+  // the eight lanes of a row hold its eight pieces: dot products, then a
+  // fixed-order reduction over the eight lanes
+  float* ovp = p.ov + (size_t)j * T * p.NH * DV;
+  for (int d0 = 0; d0 < DV; d0 += kBlock * kOabsPieces / 8) {
+    if (d0 > 0) load_pass(d0, wr);
 #pragma unroll
-  for (int j = 0; j < kRowsPerWave; ++j) {
-    const int dd = wv + 4 * j;
-    if (dd >= nd) continue;  // wave-uniform
-    const int c = 8 * lane;
-    float w[8];
-    unpack8v(wr[j], w);
-    for (int tt = 0; tt < nt; ++tt) {
-      float a = 0.f;
-      if (c < R) {
+    for (int i = 0; i < kOabsPieces; ++i) {
+      const int q = i * kBlock + tid, d = d0 + (q >> 3), pc = q & 7;
+      float w[8];
+      unpack8v(wr[i], w);
+      for (int tt = 0; tt < nt; ++tt) {
+        float a = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = fmaf(w[i], ol[tt * R + c + i], a);
+        for (int e = 0; e < 8; ++e) a = fmaf(w[e], ol[tt * kOabsCols + 8 * pc + e], a);
+        a += __shfl_xor(a, 1, kWave);
+        a += __shfl_xor(a, 2, kWave);
+        a += __shfl_xor(a, 4, kWave);
+        if (pc == 0 && d < DV) ovp[(size_t)(t0 + tt) * p.NH * DV + (size_t)h * DV + d] = a;
       }
-      a = wave_sum(a);
-      if (lane == 0) p.ov[(size_t)(t0 + tt) * p.NH * p.DV + (size_t)h * p.DV + d0 + dd] = a;
     }
   }
 }
@@ -457,9 +470,18 @@ __device__ void phase_oproj(const StepParams& p, int b, float* lds) {
     const int nt = min(NTT, T - t0);
     u32x4 v[gemv_unroll(NTT)];
     gemv_first<gemv_unroll(NTT)>(p.w_o, p.H, k0, ks, c0, nc, v);
+    // o_v = the output absorption's column-chunk shares, added in chunk order
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) {
       const int tt = idx / ks, r = idx % ks;
-      xs[tt * kTile + r] = p.ov[(size_t)(t0 + tt) * K + k0 + r];
+      const float* src = p.ov + (size_t)(t0 + tt) * K + k0 + r;
+      float v[kMaxOabsChunks];
+#pragma unroll
+      for (int c = 0; c < kMaxOabsChunks; ++c) v[c] = c < pl.nc5 ? src[(size_t)c * T * K] : 0.f;
+      float a = v[0];
+#pragma unroll
+      for (int c = 1; c < kMaxOabsChunks; ++c)
+        if (c < pl.nc5) a += v[c];
+      xs[tt * kTile + r] = a;
     }
     __syncthreads();
     gemv_tile<NTT, gemv_unroll(NTT)>(p.w_o, p.H, k0, ks, c0, nc, xs, kTile, nt, p.part6 + ((size_t)slab * T + t0) * p.H, p.H, red, v);

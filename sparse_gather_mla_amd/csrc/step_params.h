@@ -21,8 +21,8 @@ struct Plan {
   int ncc3;
   // k_core: (token, split, head block); hg head groups of 16 x cs column splits per workgroup
   int core_hg, core_cs, core_nhb, nsplit, ps;
-  // k_oabsorb: heads x chunks of dc5 rows of v_head_dim x token chunks of tc5
-  int dc5, nd5, tc5, nt5c;
+  // k_oabsorb: heads x 64-column chunks of kv_lora_rank x token chunks of tc5
+  int nc5, tc5, nt5c;
   // k_oproj: tw6-column tiles over hidden x slabs of n_heads*v_head_dim
   int nt6, s6, ks6;
   // k_out: 64-column groups x token chunks
