@@ -101,7 +101,6 @@ __global__ __launch_bounds__(kBlock) void k_absorb_m(StepParams p) {
   phase_absorb_m<MTB>(p, blockIdx.x, reinterpret_cast<char*>(lds));
 }
 
-__global__ __launch_bounds__(kBlock) void k_combine(StepParams p) { phase_combine(p, blockIdx.x); }
 
 template <int MTB>
 __global__ __launch_bounds__(kBlock) void k_oabsorb_m(StepParams p) {
@@ -187,7 +186,9 @@ size_t absorb_lds_bytes(const Plan& pl, int DN) {
   return (size_t)2 * Mg<1, kMgCols>::kBBytes + kAbsorbBetaBytes + (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2 * kAFragElems * 2;
 }
 
-size_t oabsorb_lds_bytes(const Plan& pl, int R) { return 256 + (size_t)(R / kMgK) * pl.mtb5 * 2 * kAFragElems * 2; }
+size_t oabsorb_lds_bytes(const Plan& pl, int R) {
+  return oabsorb_hdr_bytes(pl.mtb5, pl.nsplit) + (size_t)(R / kMgK) * pl.mtb5 * 2 * kAFragElems * 2;
+}
 
 // Plan of the matrix-core path; `pl` already holds T, the index build and the core's split.
 Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
@@ -217,7 +218,9 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   // as many tiles per workgroup as keep at least 128 workgroups busy
   pl.tpw3 = pl.nct3;
   while (pl.tpw3 > 1 && NH * pl.ntb3 * (pl.nct3 / pl.tpw3) < 128) pl.tpw3 /= 2;
-  pl.mtb5 = 1;
+  // two m-tiles per workgroup when many heads give enough workgroups: half the
+  // weight re-reads across token blocks
+  pl.mtb5 = (NH >= 64 && T > 64) ? 2 : 1;
   pl.ntb5 = cdiv(T, 16 * pl.mtb5);
   pl.nxc = cdiv(pl.kt1 * kMgK, kPrepChunk);
   pl.nqc = cdiv(Q, kQaChunk);
@@ -247,7 +250,6 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   pl.off_pm = take((size_t)T * pl.nsplit * NH * f);
   pl.off_pl = take((size_t)T * pl.nsplit * NH * f);
   pl.off_po = take((size_t)T * pl.nsplit * NH * R * f);
-  pl.off_olat = take(pl.nsplit > 1 ? (size_t)T * NH * R * f : 0);
   pl.off_a5 = take((size_t)pl.kt6 * pl.mt_pad * frag);
   pl.off_part6 = take((size_t)pl.s6 * T * H * f);
   pl.total = off;
@@ -378,26 +380,23 @@ core_kernel_t pick_core(const Plan& pl, int R) {
 // Kernels of a step, in launch order: the GEMV path (few tokens) and the matrix-core path.
 const char* const kKernelNamesGemv[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"};
 const char* const kKernelNamesFused[] = {"k_down", "k_qup", "k_absorb_core", "k_oabsorb", "k_oproj", "k_out"};
-const char* const kKernelNamesMfma[] = {"k_prep", "k_down", "k_qa",      "k_qup",   "k_absorb",
-                                        "k_core", "k_combine", "k_oabsorb", "k_oproj", "k_out"};
-const char* const kKernelNamesMfma1[] = {"k_prep", "k_down",    "k_qa",    "k_qup", "k_absorb",
-                                         "k_core", "k_oabsorb", "k_oproj", "k_out"};
+const char* const kKernelNamesMfma[] = {"k_prep", "k_down",    "k_qa",    "k_qup", "k_absorb",
+                                        "k_core", "k_oabsorb", "k_oproj", "k_out"};
 constexpr int kNumKernelsGemv = 7;
-constexpr int kNumKernelsMfma = 10;  // with the split combine
-constexpr int kNumKernelsMfma1 = 9;  // the core runs one split per token
+constexpr int kNumKernelsMfma = 9;
 constexpr size_t kGemvLdsBytes = kGemvLdsFloats * sizeof(float);
 constexpr int kMaxLdsBytes = 160 * 1024;
 
 int num_kernels(const Plan& pl) {
   if (pl.fused) return kNumKernelsGemv - 1;
   if (!pl.mfma) return kNumKernelsGemv;
-  return pl.nsplit > 1 ? kNumKernelsMfma : kNumKernelsMfma1;
+  return kNumKernelsMfma;
 }
 
 const char* kernel_name(const Plan& pl, int i) {
   if (pl.fused) return kKernelNamesFused[i];
   if (!pl.mfma) return kKernelNamesGemv[i];
-  return pl.nsplit > 1 ? kKernelNamesMfma[i] : kKernelNamesMfma1[i];
+  return kKernelNamesMfma[i];
 }
 
 hipError_t set_lds_limits(const mla_gd_dims& d) {
@@ -409,7 +408,7 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
   for (const void* k : gemv)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
   const void* big[] = {(const void*)k_absorb_m<1>, (const void*)k_absorb_m<2>, (const void*)k_absorb_m<4>,
-                       (const void*)k_oabsorb_m<1>};
+                       (const void*)k_oabsorb_m<1>, (const void*)k_oabsorb_m<2>};
   for (const void* k : big)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   return e;
@@ -449,7 +448,7 @@ step_kernel_t pick_oproj_m(int mtb) {
   return mtb == 1 ? k_oproj_m<1> : (mtb == 2 ? k_oproj_m<2> : (mtb == 4 ? k_oproj_m<4> : k_oproj_m<8>));
 }
 step_kernel_t pick_absorb_m(int mtb) { return mtb == 1 ? k_absorb_m<1> : (mtb == 2 ? k_absorb_m<2> : k_absorb_m<4>); }
-step_kernel_t pick_oabsorb_m(int) { return k_oabsorb_m<1>; }
+step_kernel_t pick_oabsorb_m(int mtb) { return mtb == 2 ? k_oabsorb_m<2> : k_oabsorb_m<1>; }
 
 }  // namespace
 
@@ -591,10 +590,6 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     mark(ev++);
     hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
     mark(ev++);
-    if (pl.nsplit > 1) {
-      hipLaunchKernelGGL(k_combine, dim3(cdiv(T * p.NH * (p.R / 4), kBlock)), blk, 0, s, p);
-      mark(ev++);
-    }
     hipLaunchKernelGGL(pick_oabsorb_m(pl.mtb5), dim3(mg_grid(p.NH, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R), s,
                        p);
     mark(ev++);
@@ -688,7 +683,6 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
     p.kvr = nullptr; p.kvss = nullptr; p.ov = nullptr;
     p.a1 = (uint16_t*)(ws + pl.off_a1); p.a2 = (uint16_t*)(ws + pl.off_a2); p.a5 = (uint16_t*)(ws + pl.off_a5);
     p.ssq = (float*)(ws + pl.off_ssq);
-    p.olat = pl.nsplit > 1 ? (float*)(ws + pl.off_olat) : nullptr;
   }
   p.sync = (unsigned*)(ws + pl.off_sync);
   p.pl = pl;

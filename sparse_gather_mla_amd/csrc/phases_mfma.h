@@ -2,8 +2,8 @@
 // tokens.  The operations and their order are those of the GEMV path
 // (phases.h); the projections become hi/lo bf16 GEMMs on the matrix cores
 // (gemm_mfma.h).  Each producer writes the next GEMM's activation already in
-// fragment order, so the GEMM kernels stream both operands with direct
-// global->LDS loads:
+// fragment order, so the GEMM kernels stream both operands with plain 16-byte
+// loads:
 //   k_prep    index build; A1 = x * g_in; partial sums of x^2
 //   k_down    split-K partials of A1 @ [wq_a | wkv_a]
 //   k_qa      reduce them: A2 = acc_q * g_q and partial sums of acc_q^2 per
@@ -12,8 +12,7 @@
 //   k_absorb  q_lat = (beta * q_nope) @ q_absorb_w[h], beta = alpha * inv_q;
 //             RoPE of q_pe -> Qcat
 //   k_core    (shared with the GEMV path)
-//   k_combine the core's split partials -> normalised o_lat (only with splits)
-//   k_oabsorb o_v = out_absorb_w[h] . o_lat -> A5
+//   k_oabsorb combine the core's splits into o_lat; o_v = out_absorb_w[h] . o_lat -> A5
 //   k_oproj   split-K partials of A5 @ o_proj_w
 //   k_out     (shared) reduction to the bf16 output
 // Rows of a token block past the last token carry unspecified values; they
@@ -65,18 +64,31 @@ __device__ void phase_prep(const StepParams& p, int b, float* lds) {
   if (threadIdx.x == 0) p.ssx[(size_t)ch * pl.T + t] = ss;
 }
 
+// sum of n floats at p, p + stride, ... in index order; the loads of four
+// terms go out together
+__device__ __forceinline__ float sum_strided(const float* p, size_t stride, int n) {
+  float s = 0.f;
+  int c = 0;
+  for (; c + 4 <= n; c += 4) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = p[(size_t)(c + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s += v[u];
+  }
+  for (; c < n; ++c) s += p[(size_t)c * stride];
+  return s;
+}
+
 // alpha = 1/rms(x) of token t from the chunk sums (fixed order)
 __device__ __forceinline__ float mfma_alpha(const StepParams& p, int t) {
-  float s = 0.f;
-  for (int c = 0; c < p.pl.nxc; ++c) s += p.ssx[(size_t)c * p.pl.T + t];
-  return inv_rms(s, p.H, p.eps);
+  return inv_rms(sum_strided(p.ssx + t, p.pl.T, p.pl.nxc), p.H, p.eps);
 }
 
 // beta = alpha / rms(alpha * acc_q) of token t: the scale of the wq_b output
 __device__ __forceinline__ float mfma_beta(const StepParams& p, int t) {
   const float a = mfma_alpha(p, t);
-  float s = 0.f;
-  for (int c = 0; c < p.pl.nqc; ++c) s += p.ssq[(size_t)c * p.pl.T + t];
+  const float s = sum_strided(p.ssq + t, p.pl.T, p.pl.nqc);
   return a / sqrtf(a * a * s / (float)p.Q + p.eps);
 }
 
@@ -130,6 +142,39 @@ __device__ __forceinline__ float4 sum_slabs4(const float* src, size_t stride, in
     a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
   }
   return a;
+}
+
+// acc[i] = sum over S slabs (in slab order) of the float4 at src[i] + s*stride,
+// for NI items at once: every slab's NI loads go out together.  Items with a
+// null source give zeros.
+template <int NI>
+__device__ __forceinline__ void sum_slabs4_n(const float* const (&src)[NI], size_t stride, int S, float4 (&acc)[NI]) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = 0;
+  for (; s + 2 <= S; s += 2) {
+    float4 v[2][NI];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        v[u][i] = src[i] ? *reinterpret_cast<const float4*>(src[i] + (size_t)(s + u) * stride)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        acc[i].x += v[u][i].x; acc[i].y += v[u][i].y; acc[i].z += v[u][i].z; acc[i].w += v[u][i].w;
+      }
+  }
+  if (s < S) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (src[i]) {
+        const float4 v = *reinterpret_cast<const float4*>(src[i] + (size_t)s * stride);
+        acc[i].x += v.x; acc[i].y += v.y; acc[i].z += v.z; acc[i].w += v.w;
+      }
+  }
 }
 
 __device__ void phase_qa(const StepParams& p, int b, float* lds) {
@@ -219,6 +264,15 @@ __device__ void phase_qup_m(const StepParams& p, int b, char* stage) {
 // ---------------------------------------------------------------------------
 constexpr int kAbsorbBetaBytes = 512;  // beta of up to 128 tokens
 
+// interleaved RoPE of rotary pair i of the (pre-scaled) query of token t, head h, into Qcat
+__device__ __forceinline__ void rope_q(const StepParams& p, int t, int h, int i, float x0, float x1) {
+  const int half = p.DR / 2;
+  const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
+  bf16_t* q = p.qcat + ((size_t)t * p.NH + h) * p.KVR + p.R;
+  q[2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
+  q[2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
+}
+
 template <int MTB>
 __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   using S = Mg<MTB, kMgCols>;
@@ -252,16 +306,31 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   mg_pipe_prologue(q, load);
   if (tid < MTB * 16) beta[tid] = (t0 + tid < T) ? mfma_beta(p, t0 + tid) : 0.f;
   __syncthreads();
-  for (int idx = tid; idx < MTB * 16 * KS * 8; idx += kBlock) {
-    const int tt = idx / (KS * 8), k = 4 * (idx % (KS * 8));
-    const int t = t0 + tt;
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < T && k < p.DN) {  // DN % 8 == 0
-      const float4 v = sum_slabs4(p.part2 + (size_t)t * p.N2 + (size_t)h * p.QKH + k, (size_t)T * p.N2, pl.s2);
-      const float bt = beta[tt];
-      a[0] = bt * v.x; a[1] = bt * v.y; a[2] = bt * v.z; a[3] = bt * v.w;
+  // float4 items (token, 4 columns of q_nope), eight per thread per pass with
+  // their loads issued together
+  constexpr int NI = 8;
+  const int n_items = MTB * 16 * KS * 8;
+  for (int base = 0; base < n_items; base += NI * kBlock) {
+    const float* src[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = base + i * kBlock + tid;
+      const int tt = idx / (KS * 8), k = 4 * (idx % (KS * 8)), t = t0 + tt;
+      src[i] = (idx < n_items && t < T && k < p.DN)  // DN % 8 == 0
+                   ? p.part2 + (size_t)t * p.N2 + (size_t)h * p.QKH + k
+                   : nullptr;
     }
-    put_a4_lds<true>(ares, MTB, tt, k, a);
+    float4 v[NI];
+    sum_slabs4_n<NI>(src, (size_t)T * p.N2, pl.s2, v);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = base + i * kBlock + tid;
+      if (idx >= n_items) continue;
+      const int tt = idx / (KS * 8), k = 4 * (idx % (KS * 8));
+      const float bt = beta[tt];
+      const float a[4] = {bt * v[i].x, bt * v[i].y, bt * v[i].z, bt * v[i].w};
+      put_a4_lds<true>(ares, MTB, tt, k, a);
+    }
   }
   __syncthreads();
   f32x4_t acc[S::MTW][S::NTW];
@@ -286,143 +355,177 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
       });
   if (j0 != 0) return;  // the first tile group also ropes q_pe
   const int half = p.DR / 2;
-  for (int idx = tid; idx < MTB * 16 * half; idx += kBlock) {
-    const int tt = idx / half, i = idx % half, t = t0 + tt;
-    if (t >= T) continue;
-    const float* src = p.part2 + (size_t)t * p.N2 + (size_t)h * p.QKH + p.DN + 2 * i;
-    float x0 = 0.f, x1 = 0.f;
+  constexpr int NQ = 8;  // (token, rotary pair) items per thread per pass, loads issued together
+  for (int base = 0; base < MTB * 16 * half; base += NQ * kBlock) {
+    float2 x[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) x[j] = make_float2(0.f, 0.f);
     for (int s2 = 0; s2 < pl.s2; ++s2) {
-      x0 += src[(size_t)s2 * T * p.N2];
-      x1 += src[(size_t)s2 * T * p.N2 + 1];
+      float2 v[NQ];
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const int idx = base + j * kBlock + tid;
+        const int tt = idx / half, i = idx % half, t = t0 + tt;
+        v[j] = (idx < MTB * 16 * half && t < T)
+                   ? *reinterpret_cast<const float2*>(p.part2 + ((size_t)s2 * T + t) * p.N2 + (size_t)h * p.QKH +
+                                                      p.DN + 2 * i)
+                   : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        x[j].x += v[j].x;
+        x[j].y += v[j].y;
+      }
     }
-    x0 *= beta[tt] * p.scale_log2;  // the query tile is stored pre-scaled
-    x1 *= beta[tt] * p.scale_log2;
-    const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
-    bf16_t* q = p.qcat + ((size_t)t * p.NH + h) * p.KVR + p.R;
-    q[2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
-    q[2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int idx = base + j * kBlock + tid;
+      const int tt = idx / half, i = idx % half, t = t0 + tt;
+      if (idx >= MTB * 16 * half || t >= T) continue;
+      const float bq = beta[tt] * p.scale_log2;  // the query tile is stored pre-scaled
+      rope_q(p, t, h, i, x[j].x * bq, x[j].y * bq);
+    }
   }
 }
 
-// ---------------------------------------------------------------------------
-// k_combine (when the core splits the selected rows): one thread per
-// (token, head, 4 latent columns).  Weights w_s = 2^(m_s - M) over the splits,
-// L = sum_s w_s * l_s, o_lat = sum_s w_s * o_s / L in split order; a token
-// with no valid entry (L = 0) gets zeros.
-// ---------------------------------------------------------------------------
-__device__ void phase_combine(const StepParams& p, int b) {
-  const Plan& pl = p.pl;
-  const int R4 = p.R / 4, NSP = pl.nsplit;
-  const int i = b * kBlock + threadIdx.x;
-  if (i >= pl.T * p.NH * R4) return;
-  const int c4 = i % R4, th = i / R4, h = th % p.NH, t = th / p.NH;
-  const float* pm = p.pm + (size_t)t * NSP * p.NH + h;
-  const float* pd = p.pden + (size_t)t * NSP * p.NH + h;
-  float M = -INFINITY;
-  for (int s = 0; s < NSP; ++s) M = fmaxf(M, pm[(size_t)s * p.NH]);
-  float L = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (M != -INFINITY) {
-    const float* po = p.po + ((size_t)t * NSP * p.NH + h) * p.R + 4 * c4;
-    for (int s = 0; s < NSP; ++s) {
-      const float w = exp2f(pm[(size_t)s * p.NH] - M);
-      L = fmaf(pd[(size_t)s * p.NH], w, L);
-      const float4 v = *reinterpret_cast<const float4*>(po + (size_t)s * p.NH * p.R);
-      o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y); o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
-    }
-  }
-  const float li = (L > 0.f) ? 1.f / L : 0.f;
-  *reinterpret_cast<float4*>(p.olat + (size_t)th * p.R + 4 * c4) = make_float4(o.x * li, o.y * li, o.z * li, o.w * li);
-}
 
 // ---------------------------------------------------------------------------
-// k_oabsorb: workgroup (head h, token block).  o_lat (from k_combine, or the
-// core's single split divided by its denominator) goes to LDS as hi/lo
-// fragments in the plain order and meets out_absorb_w[h] ([DV, R],
-// k-contiguous: B fragments load straight from memory).  o_v goes to A5 in
+// k_oabsorb: workgroup (head h, token block).  o_lat, the core's split
+// partials combined (weights w_s = 2^(m_s - M) over the splits, L = sum_s w_s
+// l_s, o_lat = (sum_s w_s o_s) / L in split order; a token with no valid entry
+// gets zeros), goes to LDS as hi/lo fragments in the plain order and meets
+// out_absorb_w[h] ([DV, R], k-contiguous: B fragments load straight from
+// memory, every k-step of two output tiles at once).  o_v goes to A5 in
 // fragment order; the last head's workgroups write A5's K padding.
-// LDS: 1/L [16*MTB] (256 B) | A4 (R/32 x MTB x 2 KB).
+// LDS: split weights [16*MTB][nsplit] | 1/L [16*MTB] | A4 (R/32 x MTB x 2 KB).
 // ---------------------------------------------------------------------------
+__host__ __device__ constexpr int oabsorb_hdr_bytes(int mtb, int nsplit) {
+  return (16 * mtb * (nsplit + 1) * 4 + 255) / 256 * 256;
+}
+constexpr int kOabsMaxKs = 16;  // kv_lora_rank <= 512
+
 template <int MTB>
 __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
   const Plan& pl = p.pl;
   int u, tb;
   if (!mg_unit(b, p.NH, pl.ntb5, u, tb)) return;
   const int h = u;
-  const int T = pl.T, R = p.R, tid = threadIdx.x;
+  const int T = pl.T, R = p.R, tid = threadIdx.x, NSP = pl.nsplit;
   const int t0 = tb * MTB * 16;
   const int nt = min(MTB * 16, T - t0);
-  const bool split = pl.nsplit > 1;
-  float* linv = reinterpret_cast<float*>(lds);  // [16*MTB]
-  char* ares = lds + 256;
-  if (tid < nt) {
-    float li = 1.f;
-    if (!split) {
-      const float L = p.pden[(size_t)(t0 + tid) * p.NH + h];
-      li = (L > 0.f) ? 1.f / L : 0.f;
-    }
-    linv[tid] = li;
-  }
-  __syncthreads();
-  const float* src = split ? p.olat : p.po;  // both [T][NH][R] here
-  for (int idx = tid; idx < MTB * 16 * (R / 4); idx += kBlock) {
-    const int tt = idx / (R / 4), c = 4 * (idx % (R / 4));
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    if (tt < nt) {
-      const float4 v = *reinterpret_cast<const float4*>(src + ((size_t)(t0 + tt) * p.NH + h) * R + c);
-      const float li = linv[tt];
-      a[0] = v.x * li; a[1] = v.y * li; a[2] = v.z * li; a[3] = v.w * li;
-    }
-    put_a4_lds<false>(ares, MTB, tt, c, a);
-  }
-  __syncthreads();
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  float* wsp = reinterpret_cast<float*>(lds);  // [16*MTB][NSP]
+  float* linv = wsp + 16 * MTB * NSP;           // [16*MTB]
+  char* ares = lds + oabsorb_hdr_bytes(MTB, NSP);
+  // split weights and 1/L: a wave per token, a lane per split (NSP <= 64);
+  // the butterfly sums leave the same value in every lane
+  for (int tt = wave; tt < nt; tt += kBlock / kWave) {
+    const size_t q = ((size_t)(t0 + tt) * NSP + lane) * p.NH + h;
+    const float m = lane < NSP ? p.pm[q] : -INFINITY;
+    const float l = lane < NSP ? p.pden[q] : 0.f;
+    const float M = wave_max(m);
+    const float w = (M == -INFINITY || lane >= NSP) ? 0.f : exp2f(m - M);
+    const float L = wave_sum(l * w);
+    if (lane < NSP) wsp[tt * NSP + lane] = w;
+    if (lane == 0) linv[tt] = (L > 0.f) ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  // o_lat float4 items (token, 4 columns), eight per thread per pass; each
+  // split's eight loads go out together
+  {
+    constexpr int NI = 8;
+    const int n_items = MTB * 16 * (R / 4);
+    for (int base = 0; base < n_items; base += NI * kBlock) {
+      float4 o[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < NSP; ++s) {
+        float4 v[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int idx = base + i * kBlock + tid;
+          const int tt = idx / (R / 4), c = 4 * (idx % (R / 4));
+          v[i] = (idx < n_items && tt < nt)
+                     ? *reinterpret_cast<const float4*>(p.po + (((size_t)(t0 + tt) * NSP + s) * p.NH + h) * R + c)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int idx = base + i * kBlock + tid;
+          const int tt = idx / (R / 4);
+          const float w = (idx < n_items && tt < nt) ? wsp[tt * NSP + s] : 0.f;
+          o[i].x = fmaf(w, v[i].x, o[i].x);
+          o[i].y = fmaf(w, v[i].y, o[i].y);
+          o[i].z = fmaf(w, v[i].z, o[i].z);
+          o[i].w = fmaf(w, v[i].w, o[i].w);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int idx = base + i * kBlock + tid;
+        if (idx >= n_items) continue;
+        const int tt = idx / (R / 4), c = 4 * (idx % (R / 4));
+        const float li = tt < nt ? linv[tt] : 0.f;
+        const float a[4] = {o[i].x * li, o[i].y * li, o[i].z * li, o[i].w * li};
+        put_a4_lds<false>(ares, MTB, tt, c, a);
+      }
+    }
+  }
+  __syncthreads();
   const int KS = R / kMgK;
   const int ndt = (p.DV + 15) / 16;
   const int K5 = p.NH * p.DV;
-  for (int n = wave; n < ndt; n += 4) {
-    f32x4_t acc[MTB];
+  // output tiles n0 and n0 + 4 of this wave: all their B fragments first
+  for (int n0 = wave; n0 < ndt; n0 += 8) {
+    bf16x8_t bfr[2][kOabsMaxKs];
 #pragma unroll
-    for (int mt = 0; mt < MTB; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int d = 16 * n + l16;
-    const bool dok = d < p.DV;
-    const bf16_t* wrow = p.w_oabs + ((size_t)h * p.DV + (dok ? d : 0)) * R + 8 * g;
-    for (int ks = 0; ks < KS; ks += 4) {
-      bf16x8_t bfr[4];
+    for (int q = 0; q < 2; ++q) {
+      const int d = 16 * (n0 + 4 * q) + l16;
+      const bool dok = n0 + 4 * q < ndt && d < p.DV;
+      const bf16_t* wrow = p.w_oabs + ((size_t)h * p.DV + (dok ? d : 0)) * R + 8 * g;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int ks = 0; ks < kOabsMaxKs; ++ks) {
         u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (dok && ks + q < KS) v = load16_nt(wrow + kMgK * (ks + q));
-        bfr[q] = __builtin_bit_cast(bf16x8_t, v);
+        if (dok && ks < KS) v = load16_nt(wrow + kMgK * ks);
+        bfr[q][ks] = __builtin_bit_cast(bf16x8_t, v);
       }
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (ks + q >= KS) break;
-        const char* blk = ares + (size_t)((ks + q) * MTB) * 2 * (kAFragElems * 2);
+    for (int q = 0; q < 2; ++q) {
+      const int n = n0 + 4 * q;
+      if (n >= ndt) continue;  // wave-uniform
+      f32x4_t acc[MTB];
+#pragma unroll
+      for (int mt = 0; mt < MTB; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kOabsMaxKs; ++ks) {
+        if (ks >= KS) continue;  // uniform
+        const char* blk = ares + (size_t)(ks * MTB) * 2 * (kAFragElems * 2);
 #pragma unroll
         for (int mt = 0; mt < MTB; ++mt) {
           const bf16x8_t ahi = *reinterpret_cast<const bf16x8_t*>(blk + ((mt * 2) * 64 + lane) * 16);
           const bf16x8_t alo = *reinterpret_cast<const bf16x8_t*>(blk + ((mt * 2 + 1) * 64 + lane) * 16);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr[q], acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr[q], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr[q][ks], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr[q][ks], acc[mt], 0, 0, 0);
         }
       }
-    }
-    if (dok) {
-      const int k = h * p.DV + d;
+      const int d = 16 * n + l16;
+      if (d < p.DV) {
+        const int k = h * p.DV + d;
 #pragma unroll
-      for (int mt = 0; mt < MTB; ++mt)
+        for (int mt = 0; mt < MTB; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 16 * mt + 4 * g + i;
-          if (t < T) {
-            const float v = acc[mt][i];
-            const bf16_t hi = f32_to_bf16(v);
-            const size_t e = abuf_index(t, k, pl.mt_pad);
-            p.a5[e] = hi;
-            p.a5[e + kAFragElems] = f32_to_bf16(v - bf16_to_f32(hi));
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 16 * mt + 4 * g + i;
+            if (t < T) {
+              const float v = acc[mt][i];
+              const bf16_t hi = f32_to_bf16(v);
+              const size_t e = abuf_index(t, k, pl.mt_pad);
+              p.a5[e] = hi;
+              p.a5[e + kAFragElems] = f32_to_bf16(v - bf16_to_f32(hi));
+            }
           }
-        }
+      }
     }
   }
   if (h == p.NH - 1) {

@@ -43,7 +43,7 @@ struct Plan {
   // workspace layout (byte offsets)
   size_t off_zero, off_rows, off_part1, off_ssx, off_part2, off_ssq, off_kvr, off_kvss, off_qcat;
   size_t off_pm, off_pl, off_po, off_ov, off_part6;
-  size_t off_a1, off_a2, off_a5, off_olat;
+  size_t off_a1, off_a2, off_a5;
   size_t off_sync;  // fused variant's counters (same offset for every n_tokens)
   size_t total;
 };
@@ -92,7 +92,6 @@ struct StepParams {
   uint16_t* a1;     // x * g_in               [kt1][mt_pad][2][512]
   uint16_t* a2;     // acc_q * g_q            [kt2][mt_pad][2][512]
   uint16_t* a5;     // o_v                    [kt6][mt_pad][2][512]
-  float* olat;      // [T][NH][R] combined, normalised latent outputs (when nsplit > 1)
   // fused variant: counters kSyncStride words apart -- [0] kv rows written,
   // [1] error flag (a wait timed out), [2 + h] absorption tiles of head h done
   unsigned* sync;

@@ -159,11 +159,9 @@ def test_kernel_lists_of_both_paths(lib):
         gemv = names(8)
         mfma = names(9)
         assert gemv == ["k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"]
-        full = ["k_prep", "k_down", "k_qa", "k_qup", "k_absorb", "k_core", "k_combine", "k_oabsorb", "k_oproj",
-                "k_out"]
-        # k_combine runs only when the core splits a token's selected rows
-        assert mfma in (full, [k for k in full if k != "k_combine"])
-        assert names(40) in (full, [k for k in full if k != "k_combine"])
+        full = ["k_prep", "k_down", "k_qa", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"]
+        # the output absorption combines the core's splits itself
+        assert mfma == full and names(40) == full
         sizes = [lib.mla_gather_decode_workspace_size(h, t) for t in range(1, 41)]
         assert all(b >= a for a, b in zip(sizes, sizes[1:]))
     finally:
