@@ -337,4 +337,270 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
     }
 }
 
+// ---------------------------------------------------------------------------
+// Many heads: 64 heads per workgroup of eight waves, row-split scores.
+//
+// Wave w owns head tile ht = w/2 (16 heads) and row half rh = w%2 of each
+// 32-row chunk for the scores: S^T[16 rows x 16 heads] over the whole kv_row,
+// so no partial score tiles are exchanged.  The two waves of a head tile swap
+// their chunk maxima through LDS and so keep identical softmax references;
+// each keeps the row sum of its own rows (added at the end).  Each wave then
+// writes its probabilities into the PV operand of its head tile in LDS (rows
+// 4g+i of the half in slots 4*rh .. 4*rh+3, the order the transposing value
+// reads deliver) and, for the PV product, takes NT/8 output tiles (16 latent
+// columns each) for all 64 heads: every value fragment read from LDS serves
+// four MFMAs, and each gathered row is read from LDS once for the values.
+// LDS: ring | row ids | sink | bias | chunk maxima [2][4][16] | P [4][64 lanes][16 B]
+//      | rescale factors [4][16] | row sums [4][16].
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int core_rs_ofs_bias(int nt) { return core_ofs_sink(nt) + 1024; }
+__host__ __device__ constexpr int core_rs_ofs_max(int nt) { return core_rs_ofs_bias(nt) + kCoreRing * kCoreChunk * 4; }
+__host__ __device__ constexpr int core_rs_ofs_p(int nt) { return core_rs_ofs_max(nt) + 2 * 4 * 16 * 4; }
+__host__ __device__ constexpr int core_rs_ofs_alpha(int nt) { return core_rs_ofs_p(nt) + 4 * 64 * 16; }
+__host__ __device__ constexpr int core_rs_ofs_l(int nt) { return core_rs_ofs_alpha(nt) + 4 * 16 * 4; }
+__host__ __device__ constexpr int core_rs_lds_bytes(int nt) { return core_rs_ofs_l(nt) + 4 * 16 * 4; }
+
+template <int NT>
+__device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p, int b, char* lds) {
+  static_assert(NT % 8 == 0, "eight waves split the output tiles");
+  constexpr int NW = 8;
+  constexpr int NTW = NT / 8;        // output tiles per wave in the PV product
+  constexpr int KSMAX = NT / 2 + 2;  // 32-wide k-steps over kv_row = 16*NT + DR, DR <= 64
+  constexpr int NPMAX = core_row_pieces(NT);
+  constexpr int NI = (kCoreChunk * NPMAX + 64 * NW - 1) / (64 * NW);  // loads per wave per chunk
+  constexpr int BUF = core_buf_bytes(NT);
+  char* ring = lds;
+  int* ids = reinterpret_cast<int*>(lds + core_ofs_ids(NT));
+  char* sink = lds + core_ofs_sink(NT);
+  float* bias = reinterpret_cast<float*>(lds + core_rs_ofs_bias(NT));
+  float* cmax = reinterpret_cast<float*>(lds + core_rs_ofs_max(NT));     // [rh][ht][16]
+  char* pbuf = lds + core_rs_ofs_p(NT);                                  // [ht][lane][16 B]
+  float* alph = reinterpret_cast<float*>(lds + core_rs_ofs_alpha(NT));  // [ht][16]
+  float* lsum = reinterpret_cast<float*>(lds + core_rs_ofs_l(NT));      // [ht][16]
+  const Plan& pl = p.pl;
+  const int KVR = p.KVR;
+  const int ks = (KVR + 31) >> 5;  // score k-steps
+  const int npieces = KVR >> 3;    // 16-byte pieces of a cache row
+  const int npad = (4 * ks) | 1;   // LDS row stride in pieces (odd, <= NPMAX)
+  const int rstride = npad * 16;
+  const int slots = kCoreChunk * npad;
+
+  // workgroups of the same (token, split) but different head blocks sit 8
+  // block indices apart: same XCD, shared gathered rows in its L2
+  const int nhb = pl.core_nhb;
+  const int pair = (b / (8 * nhb)) * 8 + (b % 8);
+  const int hb = (b / 8) % nhb;
+  if (pair >= pl.T * pl.nsplit) return;  // padding workgroup (whole group exits before any barrier)
+  const int t = pair / pl.nsplit, split = pair % pl.nsplit;
+  const int j0 = split * pl.ps, j1 = min(p.P, j0 + pl.ps);
+  const int nrows = j1 - j0;
+  const int nchunks = (nrows + kCoreChunk - 1) / kCoreChunk;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ht = wave >> 1, rh = wave & 1;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int hblk = hb * 64;                   // first head of the workgroup
+  const int head = hblk + 16 * ht + l16;      // this lane's head in the score product
+
+  for (int i = tid; i < nchunks * kCoreChunk; i += NW * 64)
+    ids[i] = (i < nrows) ? p.rows[(size_t)t * p.P + j0 + i] : -1;
+  __syncthreads();
+
+  int lrow[NI], lofs[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int s = (i * NW + wave) * 64 + lane;
+    lrow[i] = -1;
+    lofs[i] = 0;
+    if (s < slots) {
+      const int r = s / npad, pc = s % npad;
+      if (pc < npieces) {
+        lrow[i] = r;
+        lofs[i] = pc * 16;
+      }
+    }
+  }
+  const unsigned row_bytes = (unsigned)KVR * 2u;
+  auto issue_chunk = [&](int c) {
+    const int bsel = c % kCoreRing;
+    char* buf = ring + bsel * BUF;
+    const bool live = c < nchunks;
+    const int* cid = ids + min(c, nchunks - 1) * kCoreChunk;
+    if (wave == 0 && lane < kCoreChunk) bias[bsel * kCoreChunk + lane] = (live && cid[lane] >= 0) ? 0.f : -INFINITY;
+    int rid[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) rid[i] = cid[max(lrow[i], 0)];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int s0 = (i * NW + wave) * 64;
+      const char* src = reinterpret_cast<const char*>(p.zero16);
+      if (live && lrow[i] >= 0 && rid[i] >= 0)
+        src = reinterpret_cast<const char*>(p.cache) + (size_t)(unsigned)rid[i] * row_bytes + lofs[i];
+      dma16(src, (s0 < slots) ? buf + s0 * 16 : sink);
+    }
+  };
+
+  f32x4_t o[4][NTW];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) o[q][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // per head l16 of head tile ht; l over this wave's rows
+
+#pragma unroll
+  for (int c = 0; c < kCoreRing - 1; ++c) issue_chunk(c);
+
+  // Q fragments of the whole kv_row: lane l holds Qcat[head][32*kk + 8*g .. +8]
+  bf16x8_t qf[KSMAX];
+#pragma unroll
+  for (int kk = 0; kk < KSMAX; ++kk) {
+    const int k = 32 * kk + 8 * g;
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (kk < ks && head < p.NH && k < KVR)
+      v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * p.NH + head) * KVR + k);
+    qf[kk] = __builtin_bit_cast(bf16x8_t, v);
+  }
+  wait_vmcnt<0>();
+
+  const lds_char_t* lring = (const lds_char_t*)ring;
+  const lds_char_t* lbias = (const lds_char_t*)bias;
+  // score fragments: row 16*rh + l16, pieces 4*kk + g
+  const int sofs = (16 * rh + l16) * rstride + 16 * g;
+  // value fragments: rows r1 and r1 + 16, this wave's output columns
+  const int r1 = 4 * g + (l16 >> 2);
+  const int vofs = r1 * rstride + 8 * (l16 & 3) + 32 * (wave * NTW);
+  const int rs16 = 16 * rstride;
+  const int px16 = (lane ^ 16) << 2, px32 = (lane ^ 32) << 2;
+
+  for (int c = 0; c < nchunks; ++c) {
+    wait_vmcnt<NI * (kCoreRing - 2)>();
+    __syncthreads();  // chunk c visible; the previous chunk's LDS buffers consumed
+    issue_chunk(c + kCoreRing - 1);
+    const int bsel = c % kCoreRing;
+    const lds_char_t* buf = lring + bsel * BUF;
+    // scores of this wave's 16 rows: two accumulators (even / odd k-steps),
+    // key fragments loaded two steps ahead
+    f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      const lds_char_t* pa = buf + sofs;
+      auto ld = [&](int kk) { return *(const lds_bf16x8_t*)(pa + 64 * kk); };
+      if (ks == KSMAX) {  // kv_row fills every k-step (uniform branch)
+        bf16x8_t f0 = ld(0), f1 = ld(1);
+#pragma unroll
+        for (int kk = 0; kk < KSMAX; ++kk) {
+          bf16x8_t f2 = f1;
+          if (kk + 2 < KSMAX) f2 = ld(kk + 2);
+          if (kk & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, qf[kk], sb, 0, 0, 0);
+          else sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, qf[kk], sa, 0, 0, 0);
+          f0 = f1;
+          f1 = f2;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KSMAX; ++kk) {
+          if (kk < ks) {
+            if (kk & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld(kk), qf[kk], sb, 0, 0, 0);
+            else sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld(kk), qf[kk], sa, 0, 0, 0);
+          }
+        }
+      }
+    }
+    // rows 16*rh + 4g + i: masked rows carry -inf
+    const f32x4_t bi = *(const lds_f32x4_t*)(lbias + 4 * (bsel * kCoreChunk + 16 * rh + 4 * g));
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = (sa[i] + sb[i]) + bi[i];
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, bperm(px16, mx));
+    mx = fmaxf(mx, bperm(px32, mx));
+    if (g == 0) cmax[(rh * 4 + ht) * 16 + l16] = mx;
+    __syncthreads();  // chunk maxima of both halves visible
+    mx = fmaxf(mx, cmax[((1 - rh) * 4 + ht) * 16 + l16]);  // the same value in both waves of the tile
+    // lazy rescaling as in core_phase: the reference moves only when the chunk
+    // maximum exceeds it by more than 8 (both waves decide alike)
+    float alpha = 1.f;
+    if (mx > m_run + 8.f) {
+      alpha = __builtin_amdgcn_exp2f(m_run - mx);  // m_run = -inf gives 0
+      m_run = mx;
+    }
+    float pr[4];
+    if (m_run != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = 0.f;
+    }
+    float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    ps += bperm(px16, ps);
+    ps += bperm(px32, ps);
+    l_run = l_run * alpha + ps;
+    // this half's probabilities into slots 4*rh .. 4*rh+3 of the head tile's PV operand
+    {
+      bf16_t pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = f32_to_bf16(pr[i]);
+      uint2 w;
+      w.x = (uint32_t)pb[0] | ((uint32_t)pb[1] << 16);
+      w.y = (uint32_t)pb[2] | ((uint32_t)pb[3] << 16);
+      *reinterpret_cast<uint2*>(pbuf + (ht * 64 + lane) * 16 + 8 * rh) = w;
+    }
+    if (rh == 0 && g == 0) alph[ht * 16 + l16] = alpha;
+    __syncthreads();  // probabilities and rescale factors of all head tiles visible
+    // PV: this wave's output tiles for all four head tiles
+    bf16x8_t pab[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pab[q] = *reinterpret_cast<const bf16x8_t*>(pbuf + (q * 64 + lane) * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // lane (g, l16) holds heads 4g+i of each output tile
+      const f32x4_t ai = *reinterpret_cast<const f32x4_t*>(alph + q * 16 + 4 * g);
+      const bool any = (ai[0] != 1.f) || (ai[1] != 1.f) || (ai[2] != 1.f) || (ai[3] != 1.f);
+      if (__builtin_amdgcn_ballot_w64(any) != 0) {  // wave-uniform
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[q][n][i] *= ai[i];
+      }
+    }
+    const unsigned av = (unsigned)(uintptr_t)(buf + vofs), av2 = av + (unsigned)rs16;
+    auto vfrag = [&](int n) {
+      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(av + 32u * n));
+      const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(av2 + 32u * n));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t vf = vfrag(0);
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) {
+      bf16x8_t vn = vf;
+      if (n + 1 < NTW) vn = vfrag(n + 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pab[q], vf, o[q][n], 0, 0, 0);
+      vf = vn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();  // the trailing loads (zero rows into unused buffers or the sink)
+
+  // (m, l): the waves of a head tile hold the same m; l adds the two halves
+  if (rh == 1 && g == 0) lsum[ht * 16 + l16] = l_run;
+  __syncthreads();
+  const size_t pb = ((size_t)t * pl.nsplit + split) * p.NH;
+  if (rh == 0 && g == 0 && head < p.NH) {
+    p.pm[pb + head] = m_run;
+    p.pden[pb + head] = l_run + lsum[ht * 16 + l16];
+  }
+  constexpr int R = 16 * NT;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int n = 0; n < NTW; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = hblk + 16 * q + 4 * g + i;
+        if (h < p.NH) p.po[(pb + h) * R + 16 * (wave * NTW + n) + l16] = o[q][n][i];
+      }
+}
+
 }  // namespace mla

@@ -44,6 +44,13 @@ __global__ __launch_bounds__(HG * CS * 64) void k_core(StepParams p) {
   core_phase<NT, HG, CS>(p, blockIdx.x, lds);
 }
 
+// many heads (64 per workgroup, eight waves): row-split scores (core_mfma.h)
+template <int NT>
+__global__ __launch_bounds__(512) void k_core_rs(StepParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[core_rs_lds_bytes(NT)];
+  core_phase_rs<NT>(p, blockIdx.x, lds);
+}
+
 // fused variant: kv rows, absorption and core in one launch (phase_absorb_core);
 // the producers reuse the core's LDS
 template <int NT>
@@ -280,6 +287,9 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.core_hg = cs.hg;
   pl.core_cs = cs.cs;
   pl.core_nhb = cdiv(NH, 16 * cs.hg);
+  // more than 16 heads and a latent width of 128 or more: the row-split core
+  // (the same 64 heads per workgroup in eight waves)
+  pl.core_rs = (cs.hg == 4 && cs.cs == 2 && R % 128 == 0) ? 1 : 0;
   {
     // about one workgroup per CU.  The matrix-core path's combine kernel reads
     // every split for every column, so it keeps at most 16; the GEMV path's
@@ -374,6 +384,13 @@ core_kernel_t pick_fused(int R) {
 }
 
 core_kernel_t pick_core(const Plan& pl, int R) {
+  if (pl.core_rs) {
+    switch (R / 16) {
+      case 8: return k_core_rs<8>;
+      case 16: return k_core_rs<16>;
+      default: return k_core_rs<32>;
+    }
+  }
   return pl.core_hg == 1 ? pick_core_nt<1, 4>(R / 16) : pick_core_nt<4, 2>(R / 16);
 }
 

@@ -21,6 +21,7 @@ struct Plan {
   int ncc3;
   // k_core: (token, split, head block); hg head groups of 16 x cs column splits per workgroup
   int core_hg, core_cs, core_nhb, nsplit, ps;
+  int core_rs;  // many heads: the row-split core (core_phase_rs)
   // k_oabsorb: heads x 64-column chunks of kv_lora_rank x token chunks of tc5
   int nc5, tc5, nt5c;
   // k_oproj: tw6-column tiles over hidden x slabs of n_heads*v_head_dim

@@ -110,6 +110,24 @@ def test_parity_ragged_shape_matrix_core_path(T):
     _run_and_check(wl)
 
 
+# More than 16 heads with a latent width of 128 or more run the row-split
+# core: 40 heads leave the third head tile half full and the fourth empty;
+# kv_row = 144 does not fill the last 32-wide k-step.  Both projection paths.
+MANY_HEADS = Workload(
+    name="ragged_heads40",
+    shape=MlaShape(n_tokens=5, hidden=1160, q_lora_rank=600, kv_lora_rank=128, qk_nope_head_dim=24,
+                   qk_rope_head_dim=16, v_head_dim=40, n_heads=40, block_size=16, max_blocks_per_seq=12,
+                   n_prior=100, softmax_scale=0.2, norm_eps=1e-6),
+    seed=91, context_range=(101, 180), n_duplicates=7, n_future=5,
+)
+
+
+@pytest.mark.parametrize("T", [5, 21])
+def test_parity_many_heads_row_split_core(T):
+    wl = replace(MANY_HEADS, name=f"ragged_heads40_T{T}", shape=replace(MANY_HEADS.shape, n_tokens=T), seed=91 + T)
+    _run_and_check(wl)
+
+
 # ---------------------------------------------------------------------------
 # the fused variant: kv rows, absorption and core in one launch (<= 16 heads, <= 8 tokens)
 # ---------------------------------------------------------------------------
