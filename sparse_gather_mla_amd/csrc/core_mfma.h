@@ -54,9 +54,36 @@ __host__ __device__ constexpr int core_lds_bytes(int nt, int hg, int cs) {
   return core_ofs_bias(nt, hg, cs) + kCoreRing * kCoreChunk * 4;
 }
 
-// Lane permutes with precomputed byte addresses (ds_bpermute).
-__device__ __forceinline__ float bperm(int addr, float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, v)));
+// Reductions over the lanes l, l^16, l^32, l^48 (the four row groups of an
+// MFMA output tile) with the lane-swap instructions: after a swap every lane
+// of a pair holds (lower lane's value, upper lane's value), so both lanes form
+// the same result in the same order, with no LDS round trip.  The operands
+// and both results pass through empty asm statements: the optimiser would
+// otherwise take the two results of swapping equal values as equal and fold
+// the pair reduction away.
+template <bool K32>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  const unsigned a = __builtin_bit_cast(unsigned, v);
+  unsigned b = a;
+  asm volatile("" : "+v"(b));
+  const auto r = K32 ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
+                     : __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  unsigned r0 = r[0], r1 = r[1];
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  lo = __builtin_bit_cast(float, r0);
+  hi = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max4groups(float v) {
+  float lo, hi;
+  lane_pair<false>(v, lo, hi);
+  lane_pair<true>(fmaxf(lo, hi), lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum4groups(float v) {
+  float lo, hi;
+  lane_pair<false>(v, lo, hi);
+  lane_pair<true>(lo + hi, lo, hi);
+  return lo + hi;
 }
 
 // Hooks of the separately launched core: every input is complete at kernel start.
@@ -196,7 +223,6 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   const int r1 = 4 * g + (l16 >> 2);
   const int vofs = r1 * rstride + 8 * (l16 & 3) + 32 * (cs * NTW);
   const int rs16 = 16 * rstride;
-  const int px16 = (lane ^ 16) << 2, px32 = (lane ^ 32) << 2;
 
   for (int c = 0; c < nchunks; ++c) {
     // chunk c's loads are this wave's oldest; the younger chunk may stay in flight
@@ -265,8 +291,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
       s[4 + i] = sb[i] + bb[i];
     }
     float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mx = fmaxf(mx, bperm(px16, mx));
-    mx = fmaxf(mx, bperm(px32, mx));
+    mx = max4groups(mx);
     // Lazy rescaling: the reference maximum m_run (log2 domain) moves only when
     // a chunk's maximum exceeds it by more than 8, so probabilities stay below
     // 2^8 and most chunks leave the accumulators alone.  The result is exact:
@@ -285,8 +310,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
       for (int i = 0; i < 8; ++i) pr[i] = 0.f;
     }
     float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-    ps += bperm(px16, ps);
-    ps += bperm(px32, ps);
+    ps = sum4groups(ps);
     l_run = l_run * alpha + ps;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // wave-uniform
       // rescale: lane l holds heads 4g+i of each output tile
@@ -350,11 +374,11 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
 // reads deliver) and, for the PV product, takes NT/8 output tiles (16 latent
 // columns each) for all 64 heads: every value fragment read from LDS serves
 // four MFMAs, and each gathered row is read from LDS once for the values.
-// LDS: ring | row ids | sink | bias | chunk maxima [2][4][16] | P [4][64 lanes][16 B]
-//      | rescale factors [4][16] | row sums [4][16].
+// LDS: ring | row ids | sink | chunk maxima [2][4][16] | P [4][64 lanes][16 B]
+//      | rescale factors [4][16] | row sums [4][16].  The validity of each
+// lane's score rows stays in registers from the chunk's issue to its use.
 // ---------------------------------------------------------------------------
-__host__ __device__ constexpr int core_rs_ofs_bias(int nt) { return core_ofs_sink(nt) + 1024; }
-__host__ __device__ constexpr int core_rs_ofs_max(int nt) { return core_rs_ofs_bias(nt) + kCoreRing * kCoreChunk * 4; }
+__host__ __device__ constexpr int core_rs_ofs_max(int nt) { return core_ofs_sink(nt) + 1024; }
 __host__ __device__ constexpr int core_rs_ofs_p(int nt) { return core_rs_ofs_max(nt) + 2 * 4 * 16 * 4; }
 __host__ __device__ constexpr int core_rs_ofs_alpha(int nt) { return core_rs_ofs_p(nt) + 4 * 64 * 16; }
 __host__ __device__ constexpr int core_rs_ofs_l(int nt) { return core_rs_ofs_alpha(nt) + 4 * 16 * 4; }
@@ -372,7 +396,6 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
   char* ring = lds;
   int* ids = reinterpret_cast<int*>(lds + core_ofs_ids(NT));
   char* sink = lds + core_ofs_sink(NT);
-  float* bias = reinterpret_cast<float*>(lds + core_rs_ofs_bias(NT));
   float* cmax = reinterpret_cast<float*>(lds + core_rs_ofs_max(NT));     // [rh][ht][16]
   char* pbuf = lds + core_rs_ofs_p(NT);                                  // [ht][lane][16 B]
   float* alph = reinterpret_cast<float*>(lds + core_rs_ofs_alpha(NT));  // [ht][16]
@@ -421,12 +444,17 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
     }
   }
   const unsigned row_bytes = (unsigned)KVR * 2u;
-  auto issue_chunk = [&](int c) {
+  // issues chunk c's row loads; returns the validity of this lane's score
+  // rows 16*rh + 4g + i (bit i), kept in registers until the chunk is used
+  auto issue_chunk = [&](int c) -> unsigned {
     const int bsel = c % kCoreRing;
     char* buf = ring + bsel * BUF;
     const bool live = c < nchunks;
     const int* cid = ids + min(c, nchunks - 1) * kCoreChunk;
-    if (wave == 0 && lane < kCoreChunk) bias[bsel * kCoreChunk + lane] = (live && cid[lane] >= 0) ? 0.f : -INFINITY;
+    const int4 mine = *reinterpret_cast<const int4*>(cid + 16 * rh + 4 * g);
+    const unsigned valid = live ? ((mine.x >= 0 ? 1u : 0u) | (mine.y >= 0 ? 2u : 0u) | (mine.z >= 0 ? 4u : 0u) |
+                                   (mine.w >= 0 ? 8u : 0u))
+                                : 0u;
     int rid[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) rid[i] = cid[max(lrow[i], 0)];
@@ -438,6 +466,7 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
         src = reinterpret_cast<const char*>(p.cache) + (size_t)(unsigned)rid[i] * row_bytes + lofs[i];
       dma16(src, (s0 < slots) ? buf + s0 * 16 : sink);
     }
+    return valid;
   };
 
   f32x4_t o[4][NTW];
@@ -447,8 +476,8 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
     for (int n = 0; n < NTW; ++n) o[q][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;  // per head l16 of head tile ht; l over this wave's rows
 
-#pragma unroll
-  for (int c = 0; c < kCoreRing - 1; ++c) issue_chunk(c);
+  static_assert(kCoreRing == 3, "the validity masks rotate through three registers");
+  unsigned vm0 = issue_chunk(0), vm1 = issue_chunk(1);
 
   // Q fragments of the whole kv_row: lane l holds Qcat[head][32*kk + 8*g .. +8]
   bf16x8_t qf[KSMAX];
@@ -463,19 +492,16 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
   wait_vmcnt<0>();
 
   const lds_char_t* lring = (const lds_char_t*)ring;
-  const lds_char_t* lbias = (const lds_char_t*)bias;
   // score fragments: row 16*rh + l16, pieces 4*kk + g
   const int sofs = (16 * rh + l16) * rstride + 16 * g;
   // value fragments: rows r1 and r1 + 16, this wave's output columns
   const int r1 = 4 * g + (l16 >> 2);
   const int vofs = r1 * rstride + 8 * (l16 & 3) + 32 * (wave * NTW);
   const int rs16 = 16 * rstride;
-  const int px16 = (lane ^ 16) << 2, px32 = (lane ^ 32) << 2;
 
   for (int c = 0; c < nchunks; ++c) {
     wait_vmcnt<NI * (kCoreRing - 2)>();
     __syncthreads();  // chunk c visible; the previous chunk's LDS buffers consumed
-    issue_chunk(c + kCoreRing - 1);
     const int bsel = c % kCoreRing;
     const lds_char_t* buf = lring + bsel * BUF;
     // scores of this wave's 16 rows: two accumulators (even / odd k-steps),
@@ -506,14 +532,17 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
         }
       }
     }
+    // the loads of chunk c+2 go out after this chunk's score reads; its ring
+    // buffer was last read by chunk c-1, finished by every wave before the barrier
+    const unsigned vm2 = issue_chunk(c + kCoreRing - 1);
     // rows 16*rh + 4g + i: masked rows carry -inf
-    const f32x4_t bi = *(const lds_f32x4_t*)(lbias + 4 * (bsel * kCoreChunk + 16 * rh + 4 * g));
     float s[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = (sa[i] + sb[i]) + bi[i];
+    for (int i = 0; i < 4; ++i) s[i] = ((vm0 >> i) & 1u) ? sa[i] + sb[i] : -INFINITY;
+    vm0 = vm1;
+    vm1 = vm2;
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, bperm(px16, mx));
-    mx = fmaxf(mx, bperm(px32, mx));
+    mx = max4groups(mx);
     if (g == 0) cmax[(rh * 4 + ht) * 16 + l16] = mx;
     __syncthreads();  // chunk maxima of both halves visible
     mx = fmaxf(mx, cmax[((1 - rh) * 4 + ht) * 16 + l16]);  // the same value in both waves of the tile
@@ -533,8 +562,7 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
       for (int i = 0; i < 4; ++i) pr[i] = 0.f;
     }
     float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    ps += bperm(px16, ps);
-    ps += bperm(px32, ps);
+    ps = sum4groups(ps);
     l_run = l_run * alpha + ps;
     // this half's probabilities into slots 4*rh .. 4*rh+3 of the head tile's PV operand
     {
