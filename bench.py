@@ -91,7 +91,8 @@ def measured_traffic(kernel: str, workload: str):
     with open(path) as f:
         rec = json.load(f)
     w = rec.get(workload, {})
-    ent = w.get(kernel) or w.get(kernel + "_m")  # matrix-core-path kernels carry an _m in their symbol
+    # matrix-core-path kernels carry an _m in their symbol, the many-heads core an _rs
+    ent = w.get(kernel) or w.get(kernel + "_m") or w.get(kernel + "_rs")
     if not ent or ent.get("source_digest") != source_digest():
         return None
     return ent.get("bytes_per_launch")
