@@ -217,6 +217,10 @@ __device__ __forceinline__ void token_betas(const StepParams& p, int t0, int nt,
   __syncthreads();
 }
 
+// q_nope slab terms per thread loaded ahead of the token scales (one token per
+// pass leaves one or two terms per thread)
+__host__ __device__ constexpr int abs_pre(int ntt) { return ntt == 1 ? 2 : 8; }
+
 // ---------------------------------------------------------------------------
 // k_absorb: q = beta * (sum of wq_b partials); q_lat[t,h,:] = q_nope[t,h,:] @
 // q_absorb_w[h] for a 64-column chunk; the chunk-0 workgroup also ropes q_pe.
@@ -261,9 +265,55 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
     const int nt = min(NTT, T - t0);
     u32x4 v[gemv_unroll(NTT)];
     gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
+    // q_nope summed over the wq_b slabs: this thread's item (token, 4 columns)
+    // and slab part sp (s = sp, sp + nsp, ...); the first kAbsPre terms are
+    // loaded before the token scales are reduced, so the loads overlap
+    const int n4 = nt * p.DN / 4, w4 = p.DN / 4;
+    const int nsp = max(1, min(16, kBlock / n4));
+    const bool one_item = n4 * nsp <= kBlock;
+    const int item = threadIdx.x % n4, sp = threadIdx.x / n4;
+    const bool has_item = one_item && (int)threadIdx.x < n4 * nsp;
+    const float* src = p.part2 + (size_t)(t0 + item / w4) * p.N2 + (size_t)h * p.QKH + 4 * (item % w4);
+    const size_t sstride = (size_t)T * p.N2;
+    constexpr int kAbsPre = abs_pre(NTT);
+    float4 xpre[kAbsPre];
+#pragma unroll
+    for (int k = 0; k < kAbsPre; ++k) {
+      const int sl = sp + k * nsp;
+      xpre[k] = (has_item && sl < pl.s2) ? *reinterpret_cast<const float4*>(src + (size_t)sl * sstride)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     token_betas<NTT>(p, t0, nt, beta, tmp, scratch);
-    reduce_parts4(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH, (size_t)T * p.N2, pl.s2, nt * p.DN / 4,
-                  p.DN / 4, p.N2, xs, scratch);
+    if (one_item) {
+      float4* out = reinterpret_cast<float4*>(nsp == 1 ? xs : scratch);
+      if (has_item) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < kAbsPre; ++k) {
+          a.x += xpre[k].x; a.y += xpre[k].y; a.z += xpre[k].z; a.w += xpre[k].w;  // zeros past the last slab
+        }
+        for (int sl = sp + kAbsPre * nsp; sl < pl.s2; sl += nsp) {
+          const float4 x = *reinterpret_cast<const float4*>(src + (size_t)sl * sstride);
+          a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+        }
+        out[sp * n4 + item] = a;
+      }
+      __syncthreads();
+      if (nsp > 1) {
+        for (int i = threadIdx.x; i < n4; i += kBlock) {
+          float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+          for (int q = 0; q < nsp; ++q) {
+            const float4 x = reinterpret_cast<const float4*>(scratch)[q * n4 + i];
+            a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+          }
+          reinterpret_cast<float4*>(xs)[i] = a;
+        }
+        __syncthreads();
+      }
+    } else {
+      reduce_parts4(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH, (size_t)T * p.N2, pl.s2, nt * p.DN / 4,
+                    p.DN / 4, p.N2, xs, scratch);
+    }
     for (int idx = threadIdx.x; idx < nt * p.DN; idx += kBlock) xs[idx] *= beta[idx / p.DN];
     __syncthreads();
     gemv_tile<NTT, gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, xs, p.DN, nt, qo - c0, 64, red, v);
@@ -350,6 +400,7 @@ __device__ void phase_absorb_core(const StepParams& p, int b, char* lds) {
 constexpr int kOabsCols = 64;    // latent columns per workgroup
 constexpr int kOabsPieces = 4;   // 16-byte weight pieces per lane per pass: 128 rows x 8 pieces
 constexpr int kMaxOabsChunks = 8;  // kv_lora_rank <= 512
+constexpr int kOabsPre = 8;  // split partials per thread loaded ahead of the split weights
 
 __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
@@ -376,6 +427,24 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
   float* linv = pmL + pl.tc5 * NSP;  // [tc5]
   float* ol = lds + kOabsOl;            // [tc5][64]
   float* scratch = lds + kOabsScratch;  // 256 float4
+  // this thread's combine item (token, 4 columns) and part sp of the splits
+  // (s = sp, sp + nsp, ...): its first kOabsPre split partials are loaded
+  // before the split weights are known, so the two loads overlap
+  constexpr int C4 = kOabsCols / 4;
+  const int n4 = nt * C4;
+  const int nsp = max(1, min(16, kBlock / n4));
+  const bool has_item = tid < n4 * nsp;
+  const int item = tid % n4, sp = tid / n4;
+  const int tti = item / C4, c4i = item % C4;
+  const float* src = p.po + ((size_t)(t0 + tti) * NSP * p.NH + h) * R + c0 + 4 * c4i;
+  const size_t sstride = (size_t)p.NH * R;
+  float4 xpre[kOabsPre];
+#pragma unroll
+  for (int k = 0; k < kOabsPre; ++k) {
+    const int s = sp + k * nsp;
+    xpre[k] = (has_item && s < NSP) ? *reinterpret_cast<const float4*>(src + (size_t)s * sstride)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   // split weights w_s = 2^(m_s - M) and 1/L, L = sum_s w_s * l_s: a wave per
   // token, a lane per split (at most 64 splits on this path); the butterfly
   // sums leave the same value in every lane
@@ -393,34 +462,39 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
     }
   }
   __syncthreads();
-  // o_lat[tt][c] = linv * sum_s w_s * po[t][s][h][c0 + c]: float4 items, splits in parallel parts
+  // o_lat[tt][c] = linv * sum_s w_s * po[t][s][h][c0 + c], each part in split order
   {
-    constexpr int C4 = kOabsCols / 4;
-    const int n4 = nt * C4;
-    const int nsp = max(1, min(16, kBlock / n4));
     float4* out = reinterpret_cast<float4*>(nsp == 1 ? ol : scratch);
-    for (int idx = tid; idx < n4 * nsp; idx += kBlock) {
-      const int i = idx % n4, sp = idx / n4;
-      const int tt = i / C4, c4 = i % C4;
-      const float* src = p.po + ((size_t)(t0 + tt) * NSP * p.NH + h) * R + c0 + 4 * c4;
+    if (has_item) {
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = sp; s < NSP; s += nsp) {
-        const float w = pmL[tt * NSP + s];
-        const float4 x = *reinterpret_cast<const float4*>(src + (size_t)s * p.NH * R);
+#pragma unroll
+      for (int k = 0; k < kOabsPre; ++k) {
+        const int s = sp + k * nsp;
+        if (s < NSP) {
+          const float w = pmL[tti * NSP + s];
+          a.x = fmaf(w, xpre[k].x, a.x);
+          a.y = fmaf(w, xpre[k].y, a.y);
+          a.z = fmaf(w, xpre[k].z, a.z);
+          a.w = fmaf(w, xpre[k].w, a.w);
+        }
+      }
+      for (int s = sp + kOabsPre * nsp; s < NSP; s += nsp) {  // more splits than prefetched
+        const float w = pmL[tti * NSP + s];
+        const float4 x = *reinterpret_cast<const float4*>(src + (size_t)s * sstride);
         a.x = fmaf(w, x.x, a.x);
         a.y = fmaf(w, x.y, a.y);
         a.z = fmaf(w, x.z, a.z);
         a.w = fmaf(w, x.w, a.w);
       }
-      out[sp * n4 + i] = a;
+      out[sp * n4 + item] = a;
     }
     __syncthreads();
     if (nsp > 1) {
       const float4* sc = reinterpret_cast<const float4*>(scratch);
       for (int i = tid; i < n4; i += kBlock) {
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int sp = 0; sp < nsp; ++sp) {
-          const float4 x = sc[sp * n4 + i];
+        for (int q = 0; q < nsp; ++q) {
+          const float4 x = sc[q * n4 + i];
           a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
         }
         reinterpret_cast<float4*>(ol)[i] = a;
