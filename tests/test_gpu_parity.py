@@ -177,6 +177,20 @@ def test_parity_tiny_shape_matrix_core_path():
     _run_and_check(wl)
 
 
+def _mostly_future(inp):
+    gi = inp["gather_indices"]
+    pos = int(inp["positions"][0])
+    n = gi.shape[1]
+    gi[0, 200:] = pos + 1 + torch.arange(n - 200, dtype=gi.dtype) % 50  # masked (future)
+
+
+def test_one_token_mostly_masked_many_splits():
+    """ds32_slice shape (one token: 64 row splits of 32) with only the first 200
+    entries valid, so most splits hold no valid row and combine as zeros."""
+    wl = next(c for c in CONFIGS if c.name == "ds32_slice")
+    _run_and_check(wl, mutate=_mostly_future)
+
+
 # ---------------------------------------------------------------------------
 # special inputs on the tiny shape
 # ---------------------------------------------------------------------------
