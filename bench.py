@@ -15,13 +15,15 @@ Infinity Cache hold the weights or the pool (cold-cache steps).  HIP events on
 the step's stream bracket each step (the flush is outside them); ``value`` is
 the mean step latency in microseconds, kernels launched one by one
 (``--graph``: the library replays its captured HIP graph).  K more
-cold steps, launched kernel by kernel with an event before each, give the
-per-kernel breakdown.  Every dispatch of the run is a cold one, so a rocprofv3
-kernel trace of the same command averages the same launches.  ``--extras``
+cold steps, each kernel launched with its own start and stop events (they
+stamp the kernel's execution, not the dispatch gaps), give the per-kernel
+breakdown.  Every dispatch of the run is a cold one, so a rocprofv3 kernel
+trace of the same command averages the same launches.  ``--extras``
 adds warm (back-to-back) and torch-captured graph timings.
 
 ``roofline`` is for the kernel with the largest mean duration: algorithmic
-bytes per launch over its event-timed mean duration, against 8 TB/s.
+bytes per launch over its mean duration between its start and stop events,
+against 8 TB/s.
 ``traffic`` is that kernel's HBM bytes per launch from two rocprofv3 counter
 runs (FETCH_SIZE, WRITE_SIZE), scaled by what the same counters read for a
 plain 512 MiB device copy, recorded by ``--traffic`` in profiles/traffic.json
@@ -248,16 +250,16 @@ def main() -> int:
     wall = time.perf_counter() - wall0
     step_ms = [a.elapsed_time(b) for a, b in bounds]
 
-    # --- per-kernel breakdown: the same cold steps, kernels launched one by one
-    # with an event before each (these dispatches are the ones a kernel trace
-    # of this run averages too)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
+    # --- per-kernel breakdown: the same cold steps, each kernel launched with a
+    # start and a stop event that stamp its own execution (no dispatch gaps);
+    # these dispatches are the ones a kernel trace of this run averages too
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(K)]
     for k in range(K):
         flush.add_(1.0)
         mod(g, out=out, events=evs[k], stream=stream)
     torch.cuda.synchronize()
-    stage_ms = {names[i]: [evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)] for i in range(nk)}
-    direct_ms = [evs[k][0].elapsed_time(evs[k][nk]) for k in range(K)]
+    stage_ms = {names[i]: [evs[k][2 * i].elapsed_time(evs[k][2 * i + 1]) for k in range(K)] for i in range(nk)}
+    direct_ms = [evs[k][0].elapsed_time(evs[k][2 * nk - 1]) for k in range(K)]
 
     warm_us = graph_us = None
     if args.extras:

@@ -176,11 +176,15 @@ int mla_gather_decode_step(mla_gd_handle* handle, const mla_gd_tensors* tensors,
  * mla_gather_decode_kernel_count(handle, n_tokens) kernel launches (steps of
  * more than 8 tokens run the projections on the matrix cores, with two more
  * kernels; 0 for an invalid handle or n_tokens).
- * mla_gather_decode_step_profiled() is mla_gather_decode_step() plus
- * hipEventRecord(events[i], stream) before kernel i and events[count] after
- * the last one.  `events` holds n_events >= count + 1 created hipEvent_t
- * handles (owned by the caller).  Kernel names are static strings ("" for an
- * index out of range).
+ * mla_gather_decode_step_profiled() is mla_gather_decode_step() with timing
+ * events (created hipEvent_t handles owned by the caller), in one of two forms:
+ *   n_events >= 2*count: kernel i is launched with events[2i] and events[2i+1]
+ *     as its start and stop events (hipExtLaunchKernel), which stamp the
+ *     kernel's own execution, without the dispatch gaps between kernels;
+ *   count + 1 <= n_events < 2*count: hipEventRecord(events[i], stream) before
+ *     kernel i and events[count] after the last one.
+ * Fewer events, or a null handle among those used, give MLA_GD_E_INVAL.
+ * Kernel names are static strings ("" for an index out of range).
  */
 int mla_gather_decode_kernel_count(const mla_gd_handle* handle, int32_t n_tokens);
 const char* mla_gather_decode_kernel_name(const mla_gd_handle* handle, int32_t n_tokens, int index);

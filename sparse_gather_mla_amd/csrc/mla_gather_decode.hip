@@ -1,6 +1,7 @@
 // MLA gather-decode step for MI355X (gfx950): kernels and the C ABI declared
 // in include/mla_gather_decode.h.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <math.h>
 #include <stdio.h>
@@ -551,70 +552,72 @@ namespace {
 
 // Enqueue the step's kernels on stream s; with `events`, record events[i]
 // before kernel i and after the last one.
-hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* events) {
+// Launches the kernels of a step one by one.  A profiled step either records
+// events[i] before kernel i and events[count] after the last (bracket false),
+// or hands events[2i] and events[2i+1] to kernel i's launch, which stamps the
+// kernel's own start and end (bracket true: the intervals exclude the
+// dispatch gaps between kernels).
+struct Launcher {
+  const StepParams* p;
+  hipStream_t s;
+  void* const* events;
+  bool bracket;
+  hipError_t e = hipSuccess;
+  int i = 0;
+  void operator()(step_kernel_t k, dim3 grid, dim3 block, size_t lds) {
+    if (e != hipSuccess) return;
+    void* args[] = {const_cast<StepParams*>(p)};
+    if (events && bracket) {
+      e = hipExtLaunchKernel((const void*)k, grid, block, args, lds, s, (hipEvent_t)events[2 * i],
+                             (hipEvent_t)events[2 * i + 1], 0);
+    } else {
+      if (events) e = hipEventRecord((hipEvent_t)events[i], s);
+      if (e == hipSuccess) e = hipLaunchKernel((const void*)k, grid, block, args, lds, s);
+    }
+    ++i;
+  }
+  hipError_t finish() {
+    if (e == hipSuccess && events && !bracket) e = hipEventRecord((hipEvent_t)events[i], s);
+    return e;
+  }
+};
+
+hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* events, bool bracket = false) {
   const Plan& pl = p.pl;
   const int T = pl.T;
-  hipError_t e = hipSuccess;
-  auto mark = [&](int i) {
-    if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], s);
-  };
+  Launcher L{&p, s, events, bracket};
   const size_t gl = kGemvLdsBytes;
   const int ntt = gemv_ntt(T);
   const size_t gll = gemv_lds_bytes(ntt);  // GEMV phases passing over ntt tokens
   const dim3 blk(kBlock);
   const dim3 core_blk(64 * pl.core_hg * pl.core_cs);
-  mark(0);
   if (pl.fused) {
-    hipLaunchKernelGGL(pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll, s, p);
-    mark(1);
-    hipLaunchKernelGGL(pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll, s, p);
-    mark(2);
-    hipLaunchKernelGGL(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, 0, s, p);
-    mark(3);
-    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl, s, p);
-    mark(4);
-    hipLaunchKernelGGL(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll, s, p);
-    mark(5);
-    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
-    mark(6);
+    L(pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll);
+    L(pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll);
+    L(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, 0);
+    L(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl);
+    L(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll);
+    L(k_out, dim3(pl.n7), blk, gl);
   } else if (!pl.mfma) {
-    hipLaunchKernelGGL(pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll, s, p);
-    mark(1);
-    hipLaunchKernelGGL(pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll, s, p);
-    mark(2);
-    hipLaunchKernelGGL(pick_absorb(ntt), dim3(p.NH * pl.ncc3 + T), blk, gll, s, p);
-    mark(3);
-    hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
-    mark(4);
-    hipLaunchKernelGGL(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl, s, p);
-    mark(5);
-    hipLaunchKernelGGL(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll, s, p);
-    mark(6);
-    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
-    mark(7);
+    L(pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll);
+    L(pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll);
+    L(pick_absorb(ntt), dim3(p.NH * pl.ncc3 + T), blk, gll);
+    L(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0);
+    L(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl);
+    L(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll);
+    L(k_out, dim3(pl.n7), blk, gl);
   } else {
-    int ev = 1;
-    hipLaunchKernelGGL(k_prep, dim3(pl.n_idx_wg + T * pl.nxc), blk, 1024, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), blk, 0, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(k_qa, dim3(T * (pl.nqc + 1)), blk, gl, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_absorb_m(pl.mtb3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk,
-                       absorb_lds_bytes(pl, p.DN), s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_oabsorb_m(pl.mtb5), dim3(mg_grid(p.NH, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R), s,
-                       p);
-    mark(ev++);
-    hipLaunchKernelGGL(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), blk, 0, s, p);
-    mark(ev++);
-    hipLaunchKernelGGL(k_out, dim3(pl.n7), blk, gl, s, p);
-    mark(ev++);
+    L(k_prep, dim3(pl.n_idx_wg + T * pl.nxc), blk, 1024);
+    L(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), blk, 0);
+    L(k_qa, dim3(T * (pl.nqc + 1)), blk, gl);
+    L(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0);
+    L(pick_absorb_m(pl.mtb3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk, absorb_lds_bytes(pl, p.DN));
+    L(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0);
+    L(pick_oabsorb_m(pl.mtb5), dim3(mg_grid(p.NH, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R));
+    L(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), blk, 0);
+    L(k_out, dim3(pl.n7), blk, gl);
   }
+  hipError_t e = L.finish();
   if (e == hipSuccess) e = hipGetLastError();
   return e;
 }
@@ -656,8 +659,9 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   if (n_tokens < 1 || n_tokens > d.max_tokens) return MLA_GD_E_INVAL;
   const int nk = num_kernels(make_plan(d, n_tokens));
   if (events && n_events < nk + 1) return MLA_GD_E_INVAL;
+  const bool bracket = events && n_events >= 2 * nk;  // a start and an end event per kernel
   if (events)
-    for (int i = 0; i <= nk; ++i)
+    for (int i = 0; i < (bracket ? 2 * nk : nk + 1); ++i)
       if (!events[i]) return MLA_GD_E_INVAL;
   const void* bf[] = {tn->hidden_states, tn->wq_a, tn->wq_b, tn->wkv_a, tn->q_absorb_w, tn->out_absorb_w,
                       tn->o_proj_w, tn->kv_cache, tn->out};
@@ -726,7 +730,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
       e = launch_kernels(p, s, nullptr);
     }
   } else {
-    e = launch_kernels(p, s, events);
+    e = launch_kernels(p, s, events, bracket);
   }
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) { h->last_hip_error = (int)e; return MLA_GD_E_HIP; }
