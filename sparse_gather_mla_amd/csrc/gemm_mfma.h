@@ -32,7 +32,6 @@
 
 namespace mla {
 
-constexpr int kMgCols = 64;       // output columns per tile
 constexpr int kMgK = 32;          // k per step
 constexpr int kAFragElems = 512;  // bf16 per (k-step, m-tile, half) block
 

@@ -103,10 +103,10 @@ __global__ __launch_bounds__(kBlock) void k_qup_m(StepParams p) {
   phase_qup_m<MTB>(p, blockIdx.x, stage);
 }
 
-template <int MTB>
+template <int MTB, int NCA>
 __global__ __launch_bounds__(kBlock) void k_absorb_m(StepParams p) {
   extern __shared__ float lds[];
-  phase_absorb_m<MTB>(p, blockIdx.x, reinterpret_cast<char*>(lds));
+  phase_absorb_m<MTB, NCA>(p, blockIdx.x, reinterpret_cast<char*>(lds));
 }
 
 
@@ -191,7 +191,7 @@ void split_m(int kt, int units, int target, int* s_out, int* ks_out) {
 int mg_grid(int nunits, int ntb) { return cdiv(nunits, 8) * 8 * ntb; }
 
 size_t absorb_lds_bytes(const Plan& pl, int DN) {
-  return (size_t)2 * Mg<1, kMgCols>::kBBytes + kAbsorbBetaBytes + (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2 * kAFragElems * 2;
+  return (size_t)2 * kMgK * pl.nca3 * 2 + kAbsorbBetaBytes + (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2 * kAFragElems * 2;
 }
 
 size_t oabsorb_lds_bytes(const Plan& pl, int R) {
@@ -219,10 +219,13 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   pl.kt2 = cdiv(Q, kMgK);
   pl.nt2m = cdiv(N2, nc);
   split_m(pl.kt2, pl.nt2m * pl.ntb, target, &pl.s2, &pl.ks2m);
-  pl.nct3 = R / kMgCols;
   pl.mtb3 = std::min(pl.mtb, 4);  // 128-token blocks measured slower here
   while (pl.mtb3 > 1 && (size_t)cdiv(DN, kMgK) * pl.mtb3 * 2048 > 96 * 1024) pl.mtb3 /= 2;
   pl.ntb3 = cdiv(T, 16 * pl.mtb3);
+  // 128-column absorption tiles (256-byte weight row segments) where the latent
+  // width allows and the tiles still give two workgroups per CU; 64 otherwise
+  pl.nca3 = (R % 128 == 0 && NH * pl.ntb3 * (R / 128) >= 256) ? 128 : 64;
+  pl.nct3 = R / pl.nca3;
   // as many tiles per workgroup as keep at least 128 workgroups busy
   pl.tpw3 = pl.nct3;
   while (pl.tpw3 > 1 && NH * pl.ntb3 * (pl.nct3 / pl.tpw3) < 128) pl.tpw3 /= 2;
@@ -425,7 +428,8 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
                         (const void*)k_out, (const void*)k_prep, (const void*)k_qa};
   for (const void* k : gemv)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
-  const void* big[] = {(const void*)k_absorb_m<1>, (const void*)k_absorb_m<2>, (const void*)k_absorb_m<4>,
+  const void* big[] = {(const void*)k_absorb_m<1, 64>, (const void*)k_absorb_m<2, 64>, (const void*)k_absorb_m<4, 64>,
+                       (const void*)k_absorb_m<1, 128>, (const void*)k_absorb_m<2, 128>, (const void*)k_absorb_m<4, 128>,
                        (const void*)k_oabsorb_m<1>, (const void*)k_oabsorb_m<2>};
   for (const void* k : big)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
@@ -465,7 +469,10 @@ step_kernel_t pick_qup_m(int mtb) {
 step_kernel_t pick_oproj_m(int mtb) {
   return mtb == 1 ? k_oproj_m<1> : (mtb == 2 ? k_oproj_m<2> : (mtb == 4 ? k_oproj_m<4> : k_oproj_m<8>));
 }
-step_kernel_t pick_absorb_m(int mtb) { return mtb == 1 ? k_absorb_m<1> : (mtb == 2 ? k_absorb_m<2> : k_absorb_m<4>); }
+step_kernel_t pick_absorb_m(int mtb, int nca) {
+  if (nca == 128) return mtb == 1 ? k_absorb_m<1, 128> : (mtb == 2 ? k_absorb_m<2, 128> : k_absorb_m<4, 128>);
+  return mtb == 1 ? k_absorb_m<1, 64> : (mtb == 2 ? k_absorb_m<2, 64> : k_absorb_m<4, 64>);
+}
 step_kernel_t pick_oabsorb_m(int mtb) { return mtb == 2 ? k_oabsorb_m<2> : k_oabsorb_m<1>; }
 
 }  // namespace
@@ -611,7 +618,7 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     L(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), blk, 0);
     L(k_qa, dim3(T * (pl.nqc + 1)), blk, gl);
     L(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0);
-    L(pick_absorb_m(pl.mtb3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk, absorb_lds_bytes(pl, p.DN));
+    L(pick_absorb_m(pl.mtb3, pl.nca3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk, absorb_lds_bytes(pl, p.DN));
     L(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0);
     L(pick_oabsorb_m(pl.mtb5), dim3(mg_grid(p.NH, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R));
     L(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), blk, 0);

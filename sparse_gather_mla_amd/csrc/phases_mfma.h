@@ -254,13 +254,14 @@ __device__ void phase_qup_m(const StepParams& p, int b, char* stage) {
 }
 
 // ---------------------------------------------------------------------------
-// k_absorb: workgroup (head h, group of tpw3 64-column tiles of kv_lora_rank,
+// k_absorb: workgroup (head h, group of tpw3 NCA-column tiles of kv_lora_rank,
 // token block).  The pipeline streams the group's tiles of q_absorb_w[h]
 // (ceil(DN/32) k-steps each); its first loads go out before A3 = beta * q_nope
 // (wq_b slabs summed in order) is written to LDS in fragment order, once for
 // all the group's tiles.  Each tile's q_lat lands in Qcat as bf16, pre-scaled
 // by softmax_scale * log2(e); q_pe is roped into Qcat too.
-// LDS: stages (2 x 4 KB) | beta (512 B) | A3 (ceil(DN/32) x MTB x 2 KB).
+// NCA = 128 where kv_lora_rank allows (each weight row segment is 256 bytes), else 64.
+// LDS: stages (2 x NCA/16 KB) | beta (512 B) | A3 (ceil(DN/32) x MTB x 2 KB).
 // ---------------------------------------------------------------------------
 constexpr int kAbsorbBetaBytes = 512;  // beta of up to 128 tokens
 
@@ -273,9 +274,10 @@ __device__ __forceinline__ void rope_q(const StepParams& p, int t, int h, int i,
   q[2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
 }
 
-template <int MTB>
+template <int MTB, int NCA>
 __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
-  using S = Mg<MTB, kMgCols>;
+  using S = Mg<MTB, NCA>;
+  constexpr int NV = NCA / 64;  // 16-byte weight pieces per lane per step
   const Plan& pl = p.pl;
   const int ngrp = pl.nct3 / pl.tpw3;
   int u, tb;
@@ -289,20 +291,30 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   char* stage = lds;
   float* beta = reinterpret_cast<float*>(lds + 2 * S::kBBytes);
   char* ares = lds + 2 * S::kBBytes + kAbsorbBetaBytes;
-  // this lane's piece of a 32 x 64 weight tile (row r, swizzled 16-byte piece pc)
+  // this lane's pieces of a 32 x NCA weight tile: piece q = 256 i + tid is
+  // row q / (NCA/8), swizzled 16-byte column piece
   const bf16_t* W = p.w_qabs + (size_t)h * p.DN * p.R;
-  const int r = tid >> 3, pc = (tid & 7) ^ (r & 7);
+  int pr[NV], ppc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int qq = i * kBlock + tid;
+    pr[i] = qq / (NCA / 8);
+    ppc[i] = bswz(qq % (NCA / 8), pr[i]);
+  }
   auto load = [&](int st) {
-    Pieces<1> q;
+    Pieces<NV> q;
     const int j = j0 + st / KS, ks = st % KS;
-    const int row = ks * kMgK + r;
-    const bf16_t* src = reinterpret_cast<const bf16_t*>(p.zero16);
-    if (st < nsteps && row < p.DN) src = W + (size_t)row * p.R + j * kMgCols + 8 * pc;
-    q.v[0] = load16_nt(src);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int row = ks * kMgK + pr[i];
+      const bf16_t* src = reinterpret_cast<const bf16_t*>(p.zero16);
+      if (st < nsteps && row < p.DN) src = W + (size_t)row * p.R + j * NCA + 8 * ppc[i];
+      q.v[i] = load16_nt(src);
+    }
     return q;
   };
-  constexpr int P = 8;
-  Pieces<1> q[P];
+  constexpr int P = NV == 1 ? 8 : 6;
+  Pieces<NV> q[P];
   mg_pipe_prologue(q, load);
   if (tid < MTB * 16) beta[tid] = (t0 + tid < T) ? mfma_beta(p, t0 + tid) : 0.f;
   __syncthreads();
@@ -342,12 +354,16 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   };
   zero();
   mg_pipe_loop(
-      q, nsteps, stage, S::kBBytes, load, [&](const Pieces<1>& v, char* buf) { store16(buf + tid * 16, v.v[0]); },
+      q, nsteps, stage, S::kBBytes, load,
+      [&](const Pieces<NV>& v, char* buf) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) store16(buf + (i * kBlock + tid) * 16, v.v[i]);
+      },
       [&](int st, const char* buf) {
         const int j = j0 + st / KS, ks = st % KS;
-        mg_step<MTB, kMgCols>(ares + ks * S::kABytes, buf, acc);
+        mg_step<MTB, NCA>(ares + ks * S::kABytes, buf, acc);
         if (ks == KS - 1) {  // tile j complete
-          mg_for_outputs<MTB, kMgCols>(acc, t0, j * kMgCols, [&](int t, int c, float v) {
+          mg_for_outputs<MTB, NCA>(acc, t0, j * NCA, [&](int t, int c, float v) {
             if (t < T) p.qcat[((size_t)t * p.NH + h) * p.KVR + c] = f32_to_bf16(v * p.scale_log2);
           });
           zero();
