@@ -110,10 +110,10 @@ __global__ __launch_bounds__(kBlock) void k_absorb_m(StepParams p) {
 }
 
 
-template <int MTB>
+template <int MTB, int Q5>
 __global__ __launch_bounds__(kBlock) void k_oabsorb_m(StepParams p) {
   extern __shared__ float lds[];
-  phase_oabsorb_m<MTB>(p, blockIdx.x, reinterpret_cast<char*>(lds));
+  phase_oabsorb_m<MTB, Q5>(p, blockIdx.x, reinterpret_cast<char*>(lds));
 }
 
 template <int MTB>
@@ -233,6 +233,13 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   // weight re-reads across token blocks
   pl.mtb5 = (NH >= 64 && T > 64) ? 2 : 1;
   pl.ntb5 = cdiv(T, 16 * pl.mtb5);
+  // few (head, token block) pairs: split each pair's output tiles over
+  // workgroups of four tiles (one per wave), each combining the splits itself
+  {
+    const int ndt = cdiv(DV, 16);
+    pl.nq5 = (NH * pl.ntb5 < 128 && ndt > 4) ? cdiv(ndt, 4) : 1;
+    pl.q5 = pl.nq5 > 1 ? 1 : 2;
+  }
   pl.nxc = cdiv(pl.kt1 * kMgK, kPrepChunk);
   pl.nqc = cdiv(Q, kQaChunk);
   pl.kt6 = cdiv(NH * DV, kMgK);
@@ -430,7 +437,8 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
   const void* big[] = {(const void*)k_absorb_m<1, 64>, (const void*)k_absorb_m<2, 64>, (const void*)k_absorb_m<4, 64>,
                        (const void*)k_absorb_m<1, 128>, (const void*)k_absorb_m<2, 128>, (const void*)k_absorb_m<4, 128>,
-                       (const void*)k_oabsorb_m<1>, (const void*)k_oabsorb_m<2>};
+                       (const void*)k_oabsorb_m<1, 1>, (const void*)k_oabsorb_m<2, 1>,
+                       (const void*)k_oabsorb_m<1, 2>, (const void*)k_oabsorb_m<2, 2>};
   for (const void* k : big)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   return e;
@@ -473,7 +481,10 @@ step_kernel_t pick_absorb_m(int mtb, int nca) {
   if (nca == 128) return mtb == 1 ? k_absorb_m<1, 128> : (mtb == 2 ? k_absorb_m<2, 128> : k_absorb_m<4, 128>);
   return mtb == 1 ? k_absorb_m<1, 64> : (mtb == 2 ? k_absorb_m<2, 64> : k_absorb_m<4, 64>);
 }
-step_kernel_t pick_oabsorb_m(int mtb) { return mtb == 2 ? k_oabsorb_m<2> : k_oabsorb_m<1>; }
+step_kernel_t pick_oabsorb_m(int mtb, int q5) {
+  if (q5 == 1) return mtb == 2 ? k_oabsorb_m<2, 1> : k_oabsorb_m<1, 1>;
+  return mtb == 2 ? k_oabsorb_m<2, 2> : k_oabsorb_m<1, 2>;
+}
 
 }  // namespace
 
@@ -620,7 +631,7 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     L(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0);
     L(pick_absorb_m(pl.mtb3, pl.nca3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk, absorb_lds_bytes(pl, p.DN));
     L(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0);
-    L(pick_oabsorb_m(pl.mtb5), dim3(mg_grid(p.NH, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R));
+    L(pick_oabsorb_m(pl.mtb5, pl.q5), dim3(mg_grid(p.NH * pl.nq5, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R));
     L(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), blk, 0);
     L(k_out, dim3(pl.n7), blk, gl);
   }

@@ -579,20 +579,19 @@ __device__ void phase_out(const StepParams& p, int b, float*) {
   const bool ok = c < p.H;  // H % 8 == 0: a group of four is wholly inside or outside
   const size_t stride = (size_t)pl.T * p.H;
   const float* src = p.part6 + (size_t)t * p.H + (ok ? c : 0);
+  // this lane's slabs, eight loads at a time (an index past the last slab
+  // reloads the last and is dropped)
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = part;
-  for (; s + 12 < pl.s6; s += 16) {
-    float4 v[4];
+  const int S = pl.s6;
+  for (int s = part; s < S; s += 32) {
+    float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)(s + 4 * u) * stride);
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)min(s + 4 * u, S - 1) * stride);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
-    }
-  }
-  for (; s < pl.s6; s += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)s * stride);
-    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    for (int u = 0; u < 8; ++u)
+      if (s + 4 * u < S) {
+        a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
+      }
   }
   // partials of lanes 4i .. 4i+3: ((p0 + p1) + (p2 + p3))
   float r[4] = {a.x, a.y, a.z, a.w};

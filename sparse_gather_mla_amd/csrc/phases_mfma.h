@@ -125,55 +125,49 @@ __device__ void phase_down_m(const StepParams& p, int b, char* stage) {
 // y = alpha * acc_kv, RMSNorm of its latent part, RoPE of its rotary part,
 // bf16 row at slot_mapping[t].
 // ---------------------------------------------------------------------------
+// Sums over S split-K slabs, in slab order, of partials written by the
+// previous kernel.  G slabs' loads go out together (a slab index past S-1
+// reloads slab S-1 and is dropped), so a reduction costs ceil(S/G) memory
+// round trips, and every load is unconditional.
+template <int G>
 __device__ __forceinline__ float4 sum_slabs4(const float* src, size_t stride, int S) {
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = 0;
-  for (; s + 4 <= S; s += 4) {
-    float4 v[4];
+  for (int s = 0; s < S; s += G) {
+    float4 v[G];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)(s + u) * stride);
+    for (int u = 0; u < G; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)min(s + u, S - 1) * stride);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
-    }
-  }
-  for (; s < S; ++s) {
-    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)s * stride);
-    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    for (int u = 0; u < G; ++u)
+      if (s + u < S) {
+        a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
+      }
   }
   return a;
 }
 
 // acc[i] = sum over S slabs (in slab order) of the float4 at src[i] + s*stride,
-// for NI items at once: every slab's NI loads go out together.  Items with a
-// null source give zeros.
-template <int NI>
+// for NI items at once: G slabs' loads of all NI items go out together.
+// Items with a null source give zeros.
+template <int NI, int G>
 __device__ __forceinline__ void sum_slabs4_n(const float* const (&src)[NI], size_t stride, int S, float4 (&acc)[NI]) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = 0;
-  for (; s + 2 <= S; s += 2) {
-    float4 v[2][NI];
+  for (int s = 0; s < S; s += G) {
+    float4 v[G][NI];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < G; ++u) {
+      const size_t o = (size_t)min(s + u, S - 1) * stride;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        v[u][i] = src[i] ? *reinterpret_cast<const float4*>(src[i] + (size_t)(s + u) * stride)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[u][i] = src[i] ? *reinterpret_cast<const float4*>(src[i] + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < G; ++u)
+      if (s + u < S)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        acc[i].x += v[u][i].x; acc[i].y += v[u][i].y; acc[i].z += v[u][i].z; acc[i].w += v[u][i].w;
-      }
-  }
-  if (s < S) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if (src[i]) {
-        const float4 v = *reinterpret_cast<const float4*>(src[i] + (size_t)s * stride);
-        acc[i].x += v.x; acc[i].y += v.y; acc[i].z += v.z; acc[i].w += v.w;
-      }
+        for (int i = 0; i < NI; ++i) {
+          acc[i].x += v[u][i].x; acc[i].y += v[u][i].y; acc[i].z += v[u][i].z; acc[i].w += v[u][i].w;
+        }
   }
 }
 
@@ -191,7 +185,7 @@ __device__ void phase_qa(const StepParams& p, int b, float* lds) {
     if (k < KP) {
       float a[4] = {0.f, 0.f, 0.f, 0.f};
       if (k < p.Q) {  // Q % 8 == 0
-        const float4 v = sum_slabs4(src + k, sstride, pl.s1);
+        const float4 v = sum_slabs4<16>(src + k, sstride, pl.s1);
         const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -209,7 +203,7 @@ __device__ void phase_qa(const StepParams& p, int b, float* lds) {
   float* scratch = lds + ((p.KVR + 63) & ~63);
   const float alpha = mfma_alpha(p, t);
   for (int c4 = tid; c4 < p.KVR / 4; c4 += kBlock) {
-    const float4 v = sum_slabs4(src + p.Q + 4 * c4, sstride, pl.s1);
+    const float4 v = sum_slabs4<16>(src + p.Q + 4 * c4, sstride, pl.s1);
     y[4 * c4 + 0] = alpha * v.x;
     y[4 * c4 + 1] = alpha * v.y;
     y[4 * c4 + 2] = alpha * v.z;
@@ -318,9 +312,11 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
   mg_pipe_prologue(q, load);
   if (tid < MTB * 16) beta[tid] = (t0 + tid < T) ? mfma_beta(p, t0 + tid) : 0.f;
   __syncthreads();
-  // float4 items (token, 4 columns of q_nope), eight per thread per pass with
-  // their loads issued together
-  constexpr int NI = 8;
+  // float4 items (token, 4 columns of q_nope), NI per thread per pass, with
+  // the loads of GS slabs issued together (fewer registers for the largest
+  // token blocks, whose pipeline holds more)
+  constexpr int NI = MTB <= 2 ? 4 : 8;
+  constexpr int GS = MTB <= 2 ? 8 : 2;
   const int n_items = MTB * 16 * KS * 8;
   for (int base = 0; base < n_items; base += NI * kBlock) {
     const float* src[NI];
@@ -333,7 +329,7 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
                    : nullptr;
     }
     float4 v[NI];
-    sum_slabs4_n<NI>(src, (size_t)T * p.N2, pl.s2, v);
+    sum_slabs4_n<NI, GS>(src, (size_t)T * p.N2, pl.s2, v);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int idx = base + i * kBlock + tid;
@@ -371,27 +367,36 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
       });
   if (j0 != 0) return;  // the first tile group also ropes q_pe
   const int half = p.DR / 2;
-  constexpr int NQ = 8;  // (token, rotary pair) items per thread per pass, loads issued together
+  constexpr int NQ = MTB <= 2 ? 4 : 8;  // (token, rotary pair) items per thread per pass
+  constexpr int GQ = MTB <= 2 ? 8 : 1;  // slabs whose loads go out together
   for (int base = 0; base < MTB * 16 * half; base += NQ * kBlock) {
     float2 x[NQ];
+    const float* src[NQ];
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) x[j] = make_float2(0.f, 0.f);
-    for (int s2 = 0; s2 < pl.s2; ++s2) {
-      float2 v[NQ];
+    for (int j = 0; j < NQ; ++j) {
+      x[j] = make_float2(0.f, 0.f);
+      const int idx = base + j * kBlock + tid;
+      const int tt = idx / half, i = idx % half, t = t0 + tt;
+      src[j] = (idx < MTB * 16 * half && t < T) ? p.part2 + (size_t)t * p.N2 + (size_t)h * p.QKH + p.DN + 2 * i
+                                                 : nullptr;
+    }
+    for (int s2 = 0; s2 < pl.s2; s2 += GQ) {
+      float2 v[GQ][NQ];
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        const int idx = base + j * kBlock + tid;
-        const int tt = idx / half, i = idx % half, t = t0 + tt;
-        v[j] = (idx < MTB * 16 * half && t < T)
-                   ? *reinterpret_cast<const float2*>(p.part2 + ((size_t)s2 * T + t) * p.N2 + (size_t)h * p.QKH +
-                                                      p.DN + 2 * i)
-                   : make_float2(0.f, 0.f);
+      for (int u = 0; u < GQ; ++u) {
+        const size_t o = (size_t)min(s2 + u, pl.s2 - 1) * T * p.N2;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+          v[u][j] = src[j] ? *reinterpret_cast<const float2*>(src[j] + o) : make_float2(0.f, 0.f);
       }
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        x[j].x += v[j].x;
-        x[j].y += v[j].y;
-      }
+      for (int u = 0; u < GQ; ++u)
+        if (s2 + u < pl.s2)
+#pragma unroll
+          for (int j = 0; j < NQ; ++j) {
+            x[j].x += v[u][j].x;
+            x[j].y += v[u][j].y;
+          }
     }
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
@@ -420,16 +425,43 @@ __host__ __device__ constexpr int oabsorb_hdr_bytes(int mtb, int nsplit) {
 }
 constexpr int kOabsMaxKs = 16;  // kv_lora_rank <= 512
 
-template <int MTB>
+// Q5 output tiles per wave.  With nq5 > 1 parts per (head, token block) each
+// workgroup takes 4*Q5 of the 16-row output tiles (and combines the splits
+// itself), so few heads and tokens still fill the chip.
+template <int MTB, int Q5>
 __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
   const Plan& pl = p.pl;
   int u, tb;
-  if (!mg_unit(b, p.NH, pl.ntb5, u, tb)) return;
-  const int h = u;
+  if (!mg_unit(b, p.NH * pl.nq5, pl.ntb5, u, tb)) return;
+  const int h = u / pl.nq5, pq = u % pl.nq5;
   const int T = pl.T, R = p.R, tid = threadIdx.x, NSP = pl.nsplit;
   const int t0 = tb * MTB * 16;
   const int nt = min(MTB * 16, T - t0);
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int KS = R / kMgK;
+  const int ndt = (p.DV + 15) / 16;
+  const int nlo = pl.nq5 == 1 ? 0 : pq * 4 * Q5;
+  const int nhi = pl.nq5 == 1 ? ndt : min(ndt, nlo + 4 * Q5);
+  // this wave's tiles n0 + 4q: every B fragment straight from the k-contiguous weight
+  bf16x8_t bfr[Q5][kOabsMaxKs];
+  auto load_b = [&](int n0) {
+#pragma unroll
+    for (int q = 0; q < Q5; ++q) {
+      const int d = 16 * (n0 + 4 * q) + l16;
+      const bool dok = n0 + 4 * q < nhi && d < p.DV;
+      const bf16_t* wrow = p.w_oabs + ((size_t)h * p.DV + (dok ? d : 0)) * R + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < kOabsMaxKs; ++ks) {
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (dok && ks < KS) v = load16_nt(wrow + kMgK * ks);
+        bfr[q][ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+  };
+  // one tile per wave: its fragments load before the combine (two would hold
+  // too many registers across it)
+  const int nfirst = nlo + wave;
+  if (Q5 == 1 && nfirst < nhi) load_b(nfirst);
   float* wsp = reinterpret_cast<float*>(lds);  // [16*MTB][NSP]
   float* linv = wsp + 16 * MTB * NSP;           // [16*MTB]
   char* ares = lds + oabsorb_hdr_bytes(MTB, NSP);
@@ -446,34 +478,46 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
     if (lane == 0) linv[tt] = (L > 0.f) ? 1.f / L : 0.f;
   }
   __syncthreads();
-  // o_lat float4 items (token, 4 columns), eight per thread per pass; each
-  // split's eight loads go out together
+  // o_lat float4 items (token, 4 columns), eight per thread per pass; the
+  // loads of G splits go out together (a split index past the last reloads
+  // the last and is dropped).  Two tiles per wave keep G = 1: the registers
+  // of four splits cost more than the round trips they save.
   {
     constexpr int NI = 8;
+    constexpr int G = Q5 == 1 ? 4 : 1;
     const int n_items = MTB * 16 * (R / 4);
     for (int base = 0; base < n_items; base += NI * kBlock) {
       float4 o[NI];
+      const float* src[NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = 0; s < NSP; ++s) {
-        float4 v[NI];
+      for (int i = 0; i < NI; ++i) {
+        o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int idx = base + i * kBlock + tid;
+        const int tt = idx / (R / 4), c = 4 * (idx % (R / 4));
+        src[i] = (idx < n_items && tt < nt) ? p.po + ((size_t)(t0 + tt) * NSP * p.NH + h) * R + c : nullptr;
+      }
+      for (int s = 0; s < NSP; s += G) {
+        float4 v[G][NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int idx = base + i * kBlock + tid;
-          const int tt = idx / (R / 4), c = 4 * (idx % (R / 4));
-          v[i] = (idx < n_items && tt < nt)
-                     ? *reinterpret_cast<const float4*>(p.po + (((size_t)(t0 + tt) * NSP + s) * p.NH + h) * R + c)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int u = 0; u < G; ++u) {
+          const size_t off = (size_t)min(s + u, NSP - 1) * p.NH * R;
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+            v[u][i] = src[i] ? *reinterpret_cast<const float4*>(src[i] + off) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int idx = base + i * kBlock + tid;
-          const int tt = idx / (R / 4);
-          const float w = (idx < n_items && tt < nt) ? wsp[tt * NSP + s] : 0.f;
-          o[i].x = fmaf(w, v[i].x, o[i].x);
-          o[i].y = fmaf(w, v[i].y, o[i].y);
-          o[i].z = fmaf(w, v[i].z, o[i].z);
-          o[i].w = fmaf(w, v[i].w, o[i].w);
+        for (int u = 0; u < G; ++u) {
+          if (s + u >= NSP) continue;  // uniform
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const int idx = base + i * kBlock + tid;
+            const int tt = idx / (R / 4);
+            const float w = src[i] ? wsp[tt * NSP + s + u] : 0.f;
+            o[i].x = fmaf(w, v[u][i].x, o[i].x);
+            o[i].y = fmaf(w, v[u][i].y, o[i].y);
+            o[i].z = fmaf(w, v[u][i].z, o[i].z);
+            o[i].w = fmaf(w, v[u][i].w, o[i].w);
+          }
         }
       }
 #pragma unroll
@@ -488,28 +532,13 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
     }
   }
   __syncthreads();
-  const int KS = R / kMgK;
-  const int ndt = (p.DV + 15) / 16;
   const int K5 = p.NH * p.DV;
-  // output tiles n0 and n0 + 4 of this wave: all their B fragments first
-  for (int n0 = wave; n0 < ndt; n0 += 8) {
-    bf16x8_t bfr[2][kOabsMaxKs];
+  for (int n0 = nfirst; n0 < nhi; n0 += 4 * Q5) {
+    if (Q5 != 1 || n0 != nfirst) load_b(n0);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int d = 16 * (n0 + 4 * q) + l16;
-      const bool dok = n0 + 4 * q < ndt && d < p.DV;
-      const bf16_t* wrow = p.w_oabs + ((size_t)h * p.DV + (dok ? d : 0)) * R + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < kOabsMaxKs; ++ks) {
-        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (dok && ks < KS) v = load16_nt(wrow + kMgK * ks);
-        bfr[q][ks] = __builtin_bit_cast(bf16x8_t, v);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < Q5; ++q) {
       const int n = n0 + 4 * q;
-      if (n >= ndt) continue;  // wave-uniform
+      if (n >= nhi) continue;  // wave-uniform
       f32x4_t acc[MTB];
 #pragma unroll
       for (int mt = 0; mt < MTB; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -544,7 +573,7 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
       }
     }
   }
-  if (h == p.NH - 1) {
+  if (h == p.NH - 1 && pq == 0) {
     const int KP = pl.kt6 * kMgK;
     for (int idx = tid; idx < nt * (KP - K5); idx += kBlock) {
       const int t = t0 + idx / (KP - K5), k = K5 + idx % (KP - K5);

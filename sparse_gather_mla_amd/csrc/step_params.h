@@ -39,7 +39,7 @@ struct Plan {
   int kt1, ks1m, nt1m, ntq1m;  // [wq_a | wkv_a]: slabs in s1
   int kt2, ks2m, nt2m;         // wq_b: slabs in s2
   int mtb3, ntb3, nca3, nct3, tpw3;  // absorption: token blocks, nca3-column tiles of kv_lora_rank (nct3), tiles per workgroup
-  int mtb5, ntb5;              // output absorption: token blocks
+  int mtb5, ntb5, nq5, q5;     // output absorption: token blocks, parts per (head, block), tiles per wave
   int nxc, nqc;                // k_prep chunks of hidden; k_qa chunks of q_lora_rank (per token)
   int kt6, ks6m, nt6m;         // o_proj: slabs in s6
   // workspace layout (byte offsets)

@@ -128,6 +128,15 @@ def test_parity_many_heads_row_split_core(T):
     _run_and_check(wl)
 
 
+# 72-wide value heads give five 16-row output tiles: with few (head, token
+# block) pairs the output absorption splits them over two workgroups per pair,
+# the second holding one tile (three of its waves idle), and K5 = 1440 leaves
+# A5 padding.
+def test_parity_output_absorption_parts():
+    wl = replace(RAGGED, name="ragged_dv72_T21", shape=replace(RAGGED.shape, n_tokens=21, v_head_dim=72), seed=121)
+    _run_and_check(wl)
+
+
 # ---------------------------------------------------------------------------
 # the fused variant: kv rows, absorption and core in one launch (<= 16 heads, <= 8 tokens)
 # ---------------------------------------------------------------------------
