@@ -202,16 +202,49 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
   }
 }
 
-// per-token scalars: beta = alpha * inv_q (the scale of the wq_b output)
-template <int NTT>
-__device__ __forceinline__ void token_betas(const StepParams& p, int t0, int nt, float* beta, float* tmp,
-                                            float* scratch) {
+// Per-token scalars beta = alpha * inv_q (the scale of the wq_b output) from
+// the partial sums of squares: pairs q < nt*(s1 + s2), the down-projection's
+// slabs of sum(x^2) first, then the up-projection's slabs of sum(acc_a^2).
+// tscale_load issues this thread's pairs q = tid + k*kBlock; a workgroup
+// calls it before its weight loads, so the answers are not queued behind the
+// weight stream (loads return in order).  tscale_finish stages the pairs in
+// `scr` (nt*(s1 + s2) floats of LDS) and adds each token's slabs in order.
+constexpr int kTsPre = 2;
+
+__device__ __forceinline__ float tscale_at(const StepParams& p, int t0, int nt, int q) {
+  const int n1 = nt * p.pl.s1;
+  if (q < n1) return p.ssx[(size_t)(q / nt) * p.pl.T + t0 + q % nt];
+  q -= n1;
+  return p.ssq[(size_t)(q / nt) * p.pl.T + t0 + q % nt];
+}
+
+__device__ __forceinline__ void tscale_load(const StepParams& p, int t0, int nt, float (&v)[kTsPre]) {
+  const int nq = nt * (p.pl.s1 + p.pl.s2);
+#pragma unroll
+  for (int k = 0; k < kTsPre; ++k) {
+    const int q = threadIdx.x + k * kBlock;
+    v[k] = q < nq ? tscale_at(p, t0, nt, q) : 0.f;
+  }
+}
+
+__device__ __forceinline__ void tscale_finish(const StepParams& p, int t0, int nt, const float (&v)[kTsPre],
+                                              float* beta, float* scr) {
   const Plan& pl = p.pl;
-  reduce_parts(p.ssx + t0, pl.T, pl.s1, nt, nt, 0, tmp, scratch);
-  reduce_parts(p.ssq + t0, pl.T, pl.s2, nt, nt, 0, tmp + NTT, scratch);
-  for (int tt = threadIdx.x; tt < nt; tt += kBlock) {
-    const float a = inv_rms(tmp[tt], p.H, p.eps);
-    const float iq = 1.f / sqrtf(a * a * tmp[NTT + tt] / (float)p.Q + p.eps);
+  const int nq = nt * (pl.s1 + pl.s2);
+#pragma unroll
+  for (int k = 0; k < kTsPre; ++k) {
+    const int q = threadIdx.x + k * kBlock;
+    if (q < nq) scr[q] = v[k];
+  }
+  for (int q = threadIdx.x + kTsPre * kBlock; q < nq; q += kBlock) scr[q] = tscale_at(p, t0, nt, q);
+  __syncthreads();
+  if ((int)threadIdx.x < nt) {
+    const int tt = threadIdx.x;
+    float sx = 0.f, sq = 0.f;
+    for (int sl = 0; sl < pl.s1; ++sl) sx += scr[sl * nt + tt];
+    for (int sl = 0; sl < pl.s2; ++sl) sq += scr[(pl.s1 + sl) * nt + tt];
+    const float a = inv_rms(sx, p.H, p.eps);
+    const float iq = 1.f / sqrtf(a * a * sq / (float)p.Q + p.eps);
     beta[tt] = a * iq;
   }
   __syncthreads();
@@ -258,16 +291,16 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
   const int h = b / pl.ncc3, cc = b % pl.ncc3;
   const int c0 = cc * 64;
   float* beta = lds + GemvLds<NTT>::aux;
-  float* tmp = beta + NTT;          // [2*NTT]
   float* qo = lds + GemvLds<NTT>::aux + 512;  // [NTT][64]
   const bf16_t* W = p.w_qabs + (size_t)h * p.DN * p.R;
   for (int t0 = 0; t0 < T; t0 += NTT) {
     const int nt = min(NTT, T - t0);
-    u32x4 v[gemv_unroll(NTT)];
-    gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
-    // q_nope summed over the wq_b slabs: this thread's item (token, 4 columns)
-    // and slab part sp (s = sp, sp + nsp, ...); the first kAbsPre terms are
-    // loaded before the token scales are reduced, so the loads overlap
+    // the small loads go out before the weight stream: the token-scale
+    // partials, then q_nope summed over the wq_b slabs: this thread's item
+    // (token, 4 columns) and slab part sp (s = sp, sp + nsp, ...), its first
+    // kAbsPre terms
+    float tsv[kTsPre];
+    tscale_load(p, t0, nt, tsv);
     const int n4 = nt * p.DN / 4, w4 = p.DN / 4;
     const int nsp = max(1, min(16, kBlock / n4));
     const bool one_item = n4 * nsp <= kBlock;
@@ -283,7 +316,26 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
       xpre[k] = (has_item && sl < pl.s2) ? *reinterpret_cast<const float4*>(src + (size_t)sl * sstride)
                                           : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    token_betas<NTT>(p, t0, nt, beta, tmp, scratch);
+    // the chunk-0 workgroup's q_pe partials: (slab, item) pairs q = s*nr + i,
+    // staged in the reduction area after the GEMV and added in slab order
+    // (when they fit it)
+    constexpr int kRopePre = 4;
+    const int nr = nt * p.DR, nrs = nr * pl.s2;
+    const bool rope_lds = cc == 0 && nrs <= 3 * NTT * kTile;
+    const float* rsrc = p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH + p.DN;
+    auto rope_at = [&](int q) {
+      const int sl = q / nr, i = q % nr;
+      return rsrc[((size_t)sl * T + i / p.DR) * p.N2 + i % p.DR];
+    };
+    float rp[kRopePre];
+#pragma unroll
+    for (int k = 0; k < kRopePre; ++k) {
+      const int q = threadIdx.x + k * kBlock;
+      rp[k] = (rope_lds && q < nrs) ? rope_at(q) : 0.f;
+    }
+    u32x4 v[gemv_unroll(NTT)];
+    gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
+    tscale_finish(p, t0, nt, tsv, beta, red);  // `red` is free until the GEMV
     if (one_item) {
       float4* out = reinterpret_cast<float4*>(nsp == 1 ? xs : scratch);
       if (has_item) {
@@ -322,8 +374,24 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
       p.qcat[((size_t)(t0 + tt) * p.NH + h) * p.KVR + c0 + c] = f32_to_bf16(qo[tt * 64 + c] * p.scale_log2);
     }
     if (cc == 0) {
-      reduce_parts(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH + p.DN, (size_t)T * p.N2, pl.s2, nt * p.DR,
-                   p.DR, p.N2, xs, scratch);
+      if (rope_lds) {
+#pragma unroll
+        for (int k = 0; k < kRopePre; ++k) {
+          const int q = threadIdx.x + k * kBlock;
+          if (q < nrs) red[q] = rp[k];
+        }
+        for (int q = threadIdx.x + kRopePre * kBlock; q < nrs; q += kBlock) red[q] = rope_at(q);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nr; i += kBlock) {
+          float a = 0.f;
+          for (int sl = 0; sl < pl.s2; ++sl) a += red[sl * nr + i];
+          xs[i] = a;
+        }
+        __syncthreads();
+      } else {
+        reduce_parts(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH + p.DN, (size_t)T * p.N2, pl.s2, nt * p.DR,
+                     p.DR, p.N2, xs, scratch);
+      }
       const int half = p.DR / 2;
       for (int idx = threadIdx.x; idx < nt * half; idx += kBlock) {
         const int tt = idx / half, i = idx % half, t = t0 + tt;
