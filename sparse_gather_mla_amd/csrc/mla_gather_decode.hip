@@ -274,6 +274,14 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   return pl;
 }
 
+// Rows of one batch of weight loads of a GEMV tile nc columns wide (the lane
+// geometry of gemv_geom): a slab no longer than this streams in one round trip.
+int gemv_batch_rows(int nc, int ntt) {
+  int lpr = 64;
+  while (lpr > 8 && (lpr >> 1) >= nc / 8) lpr >>= 1;
+  return (kBlock / 64) * (64 / lpr) * gemv_unroll(ntt);
+}
+
 Plan make_plan(const mla_gd_dims& d, int T) {
   Plan pl;
   memset(&pl, 0, sizeof(pl));
@@ -288,6 +296,12 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.nt_kv = cdiv(KVR, pl.tw1);
   pl.nt1 = pl.nt_q + pl.nt_kv;
   choose_split(H, pl.nt1, &pl.s1, &pl.ks1);
+  // one token: slabs of the down-projection no longer than one batch of loads
+  // (a second batch would wait for the first one's products)
+  if (T == 1 && pl.ks1 > gemv_batch_rows(pl.tw1, 1)) {
+    pl.ks1 = gemv_batch_rows(pl.tw1, 1);
+    pl.s1 = cdiv(H, pl.ks1);
+  }
   pl.n_idx_wg = cdiv(T * P, kBlock);
 
   pl.nt2 = cdiv(N2, pl.tw2);
