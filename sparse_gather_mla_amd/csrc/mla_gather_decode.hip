@@ -291,7 +291,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.T = T;
   pl.tw1 = 128;
   pl.tw2 = 64;
-  pl.tw6 = 64;
+  pl.tw6 = T == 1 ? 128 : 64;  // one token: 256-byte row segments of o_proj_w
   pl.nt_q = cdiv(Q, pl.tw1);
   pl.nt_kv = cdiv(KVR, pl.tw1);
   pl.nt1 = pl.nt_q + pl.nt_kv;
@@ -332,6 +332,10 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.nt5c = cdiv(T, pl.tc5);
   pl.nt6 = cdiv(H, pl.tw6);
   choose_split(NH * DV, pl.nt6, &pl.s6, &pl.ks6);
+  if (T == 1 && pl.ks6 > gemv_batch_rows(pl.tw6, 1)) {  // as for the down-projection
+    pl.ks6 = gemv_batch_rows(pl.tw6, 1);
+    pl.s6 = cdiv(NH * DV, pl.ks6);
+  }
   pl.n7 = T * cdiv(H, kOutCols);
 
   size_t off = 0;
