@@ -82,10 +82,11 @@ __device__ __forceinline__ void put_a4_lds(char* ares, int mtb, int tt, int k, c
   *reinterpret_cast<uint2*>(blk + kAFragElems * 2 + e * 2) = lo;
 }
 
-// Columns per GEMM tile: 128 for one m-tile, 256 for larger token blocks.  A
-// wider tile streams fewer activation bytes per weight byte (the activation,
-// hi and lo, is as large per k as a 128-column weight row at 64 tokens).
-__host__ __device__ constexpr int mg_cols(int mtb) { return mtb >= 2 ? 256 : 128; }
+// Columns per GEMM tile: 128 for blocks of up to 32 tokens (twice the
+// workgroups), 256 for 64 and 128 tokens, where a wider tile streams fewer
+// activation bytes per weight byte (the activation, hi and lo, is as large per
+// k as a 128-column weight row at 64 tokens).
+__host__ __device__ constexpr int mg_cols(int mtb) { return mtb >= 4 ? 256 : 128; }
 
 template <int MTB, int NC = mg_cols(MTB)>
 struct Mg {

@@ -33,7 +33,7 @@ struct Plan {
   // Matrix-core path (more than a few tokens).  Token blocks of mtb m-tiles
   // (16 tokens each), ntb blocks, m-tiles padded to mt_pad = ntb*mtb.  For each
   // projection: kt* k-steps of 32 in all, ks* per slab, column tiles of
-  // mg_cols(mtb) weight columns (128 for one m-tile, 256 otherwise).
+  // mg_cols(mtb) weight columns (128 for up to two m-tiles, 256 otherwise).
   int mfma;
   int mtb, ntb, mt_pad;
   int kt1, ks1m, nt1m, ntq1m;  // [wq_a | wkv_a]: slabs in s1
