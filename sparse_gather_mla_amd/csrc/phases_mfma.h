@@ -66,17 +66,18 @@ __device__ void phase_prep(const StepParams& p, int b, float* lds) {
 
 // sum of n floats at p, p + stride, ... in index order; the loads of four
 // terms go out together
+// sum_{c < n} p[c*stride] in order, eight loads at a time (an index past the
+// last reloads the last and is dropped), n >= 1
 __device__ __forceinline__ float sum_strided(const float* p, size_t stride, int n) {
   float s = 0.f;
-  int c = 0;
-  for (; c + 4 <= n; c += 4) {
-    float v[4];
+  for (int c = 0; c < n; c += 8) {
+    float v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = p[(size_t)(c + u) * stride];
+    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)min(c + u, n - 1) * stride];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s += v[u];
+    for (int u = 0; u < 8; ++u)
+      if (c + u < n) s += v[u];
   }
-  for (; c < n; ++c) s += p[(size_t)c * stride];
   return s;
 }
 
@@ -86,9 +87,27 @@ __device__ __forceinline__ float mfma_alpha(const StepParams& p, int t) {
 }
 
 // beta = alpha / rms(alpha * acc_q) of token t: the scale of the wq_b output
+// (both chunk-sum lists are loaded before either is added)
 __device__ __forceinline__ float mfma_beta(const StepParams& p, int t) {
+  const Plan& pl = p.pl;
+  if (pl.nxc <= 8 && pl.nqc <= 8) {
+    float vx[8], vq[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      vx[u] = p.ssx[(size_t)min(u, pl.nxc - 1) * pl.T + t];
+      vq[u] = p.ssq[(size_t)min(u, pl.nqc - 1) * pl.T + t];
+    }
+    float sx = 0.f, sq = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < pl.nxc) sx += vx[u];
+      if (u < pl.nqc) sq += vq[u];
+    }
+    const float a = inv_rms(sx, p.H, p.eps);
+    return a / sqrtf(a * a * sq / (float)p.Q + p.eps);
+  }
   const float a = mfma_alpha(p, t);
-  const float s = sum_strided(p.ssq + t, p.pl.T, p.pl.nqc);
+  const float s = sum_strided(p.ssq + t, pl.T, pl.nqc);
   return a / sqrtf(a * a * s / (float)p.Q + p.eps);
 }
 
@@ -465,12 +484,24 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
   float* wsp = reinterpret_cast<float*>(lds);  // [16*MTB][NSP]
   float* linv = wsp + 16 * MTB * NSP;           // [16*MTB]
   char* ares = lds + oabsorb_hdr_bytes(MTB, NSP);
-  // split weights and 1/L: a wave per token, a lane per split (NSP <= 64);
-  // the butterfly sums leave the same value in every lane
-  for (int tt = wave; tt < nt; tt += kBlock / kWave) {
-    const size_t q = ((size_t)(t0 + tt) * NSP + lane) * p.NH + h;
-    const float m = lane < NSP ? p.pm[q] : -INFINITY;
-    const float l = lane < NSP ? p.pden[q] : 0.f;
+  // split weights and 1/L: a wave per token (tokens wave + 4j), a lane per
+  // split (NSP <= 64), every token's loads issued together; the butterfly
+  // sums leave the same value in every lane
+  constexpr int TPW = MTB * 16 / (kBlock / kWave);
+  float mj[TPW], lj[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int tt = wave + j * (kBlock / kWave);
+    const bool ok = tt < nt && lane < NSP;
+    const size_t q = ((size_t)(t0 + (ok ? tt : 0)) * NSP + (ok ? lane : 0)) * p.NH + h;
+    mj[j] = ok ? p.pm[q] : -INFINITY;
+    lj[j] = ok ? p.pden[q] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int tt = wave + j * (kBlock / kWave);
+    if (tt >= nt) continue;  // wave-uniform
+    const float m = mj[j], l = lj[j];
     const float M = wave_max(m);
     const float w = (M == -INFINITY || lane >= NSP) ? 0.f : exp2f(m - M);
     const float L = wave_sum(l * w);
