@@ -86,6 +86,31 @@ __device__ __forceinline__ float sum4groups(float v) {
   return lo + hi;
 }
 
+// Reductions over all 64 lanes with no LDS round trip: within each row of 16
+// lanes by DPP moves (the two quad swaps, then the half-row and row mirrors;
+// after each step every lane of the group holds the same partial, formed in
+// the same order), then over the four rows with the lane swaps above.  Every
+// lane returns the same value.  All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_mov<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
+  return max4groups(v);
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_mov<kDppQuadXor1>(v);
+  v += dpp_mov<kDppQuadXor2>(v);
+  v += dpp_mov<kDppRowHalfMirror>(v);
+  v += dpp_mov<kDppRowMirror>(v);
+  return sum4groups(v);
+}
+
 // Hooks of the separately launched core: every input is complete at kernel start.
 struct CoreNoWait {
   __device__ void before_rows(int) const {}

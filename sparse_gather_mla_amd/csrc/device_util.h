@@ -32,12 +32,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
-
 // Sum over the workgroup; every thread gets the result.  `scratch` holds >= 4 floats
 // and must not be in use by the caller across this call.
 __device__ __forceinline__ float block_sum(float v, float* scratch) {

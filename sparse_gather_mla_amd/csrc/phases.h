@@ -522,9 +522,9 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
       const size_t q = ((size_t)(t0 + tt) * NSP + lane) * p.NH + h;
       const float m = lane < NSP ? p.pm[q] : -INFINITY;
       const float l = lane < NSP ? p.pden[q] : 0.f;
-      const float M = wave_max(m);
+      const float M = wave_max_dpp(m);
       const float w = (M == -INFINITY || lane >= NSP) ? 0.f : exp2f(m - M);
-      const float L = wave_sum(l * w);
+      const float L = wave_sum_dpp(l * w);
       if (lane < NSP) pmL[tt * NSP + lane] = w;
       if (lane == 0) linv[tt] = (L > 0.f) ? 1.f / L : 0.f;
     }

@@ -502,9 +502,9 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
     const int tt = wave + j * (kBlock / kWave);
     if (tt >= nt) continue;  // wave-uniform
     const float m = mj[j], l = lj[j];
-    const float M = wave_max(m);
+    const float M = wave_max_dpp(m);
     const float w = (M == -INFINITY || lane >= NSP) ? 0.f : exp2f(m - M);
-    const float L = wave_sum(l * w);
+    const float L = wave_sum_dpp(l * w);
     if (lane < NSP) wsp[tt * NSP + lane] = w;
     if (lane == 0) linv[tt] = (L > 0.f) ? 1.f / L : 0.f;
   }
