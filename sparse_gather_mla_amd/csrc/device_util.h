@@ -46,25 +46,4 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
   return s;
 }
 
-// Arrival counter for "the last workgroup to finish reduces" patterns.
-// Every thread of the workgroup calls it after writing its partial results.
-// Release: the agent-scope fence writes this workgroup's stores back past its
-// XCD's L2 before the counter moves.  Acquire: the last arriver fences again
-// before it reads the others' partials, so it does not see stale L2 lines.
-// The last arriver resets the counter to zero for the next use.
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned n, int* flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(counter, 1u);
-    const int last = (prev == n - 1u);
-    if (last) atomicExch(counter, 0u);
-    *flag = last;
-  }
-  __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
-}
-
 }  // namespace mla

@@ -100,6 +100,20 @@ def test_parity_ragged_shape():
     _run_and_check(RAGGED)
 
 
+# The GEMV path's token passes: 3 tokens in a 4-token pass, 8 in a full one.
+@pytest.mark.parametrize("T", [3, 8])
+def test_parity_ragged_shape_gemv_token_passes(T):
+    wl = replace(RAGGED, name=f"ragged_T{T}", shape=replace(RAGGED.shape, n_tokens=T), seed=177 + T)
+    _run_and_check(wl)
+
+
+# More than 128 tokens: two 128-token blocks on the matrix cores (the second
+# one ragged) in every GEMM, the absorptions and the index build.
+def test_parity_ragged_shape_two_token_blocks():
+    wl = replace(RAGGED, name="ragged_T150", shape=replace(RAGGED.shape, n_tokens=150), seed=227)
+    _run_and_check(wl, tokens=[0, 63, 127, 128, 149])
+
+
 # Steps of more than 8 tokens run the projections on the matrix cores.  Token
 # counts that give one m-tile (9), a ragged block of two (21), a ragged block
 # of four (37) and two blocks of four (70); the ragged shape also gives K not
