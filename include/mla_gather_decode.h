@@ -43,6 +43,7 @@ extern "C" {
 #define MLA_GD_E_WORKSPACE 3    /* workspace smaller than mla_gather_decode_workspace_size() */
 #define MLA_GD_E_UNSUPPORTED 4  /* dimensions outside what the kernels handle (see create) */
 #define MLA_GD_E_HIP 5          /* a HIP runtime call or kernel launch failed */
+#define MLA_GD_E_DEVICE_CHECK 6 /* with MLA_GD_FLAG_DEBUG_CHECKS: an earlier step found invalid index data */
 
 /* flags (mla_gd_dims.flags) */
 /* Fused variant (ablation): the kv-row write, the absorption and the gather
@@ -57,6 +58,26 @@ extern "C" {
  * caller is capturing launch directly.  Without the flag every step launches
  * its kernels one by one (measured faster on MI355X for this step). */
 #define MLA_GD_FLAG_GRAPH 2u
+/* Device-side checks of the caller's index data, which the page leaves to the
+ * caller: slot_mapping[t] inside the pool and distinct across the step's
+ * tokens, and for every selected position that passes the causal mask a
+ * block-table column inside max_blocks_per_seq and a block id inside
+ * n_blocks.  A failing token row is not written and a failing gathered entry
+ * is treated as masked (no out-of-range access either way); the kernels set
+ * bits of an error word in the workspace (MLA_GD_CHECK_*).  With the flag,
+ * mla_gather_decode_step() first waits for the steps enqueued before it on
+ * `stream`, reads and clears that word, and returns MLA_GD_E_DEVICE_CHECK
+ * without launching anything if it was set; mla_gather_decode_debug_status()
+ * reads and clears it on demand.  Off by default: the checks cost a
+ * synchronisation per step, and a step with them cannot be enqueued on a
+ * stream under capture (MLA_GD_E_INVAL). */
+#define MLA_GD_FLAG_DEBUG_CHECKS 4u
+
+/* bits of the debug error word */
+#define MLA_GD_CHECK_SLOT_RANGE 1u     /* slot_mapping[t] outside [0, n_blocks * block_size): row not written */
+#define MLA_GD_CHECK_BLOCK_RANGE 2u    /* a block_table entry outside [0, n_blocks): entry masked */
+#define MLA_GD_CHECK_TABLE_COLUMN 4u   /* position / block_size >= max_blocks_per_seq: entry masked */
+#define MLA_GD_CHECK_SLOT_SHARED 8u    /* two tokens share a slot: both write it, one value survives */
 
 /*
  * Dimensions of the step, fixed when the handle is created.  The page passes
@@ -191,6 +212,15 @@ const char* mla_gather_decode_kernel_name(const mla_gd_handle* handle, int32_t n
 int mla_gather_decode_step_profiled(mla_gd_handle* handle, const mla_gd_tensors* tensors, int32_t n_tokens,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     void* const* events, int n_events);
+
+/*
+ * Debug checks (MLA_GD_FLAG_DEBUG_CHECKS): wait for the work enqueued on
+ * `stream`, store the workspace's error word (MLA_GD_CHECK_* bits) in *bits
+ * and clear it.  Returns MLA_GD_E_DEVICE_CHECK if any bit was set,
+ * MLA_GD_E_INVAL for a NULL handle, workspace or bits pointer or a handle
+ * created without the flag.  Not for use while `stream` is being captured.
+ */
+int mla_gather_decode_debug_status(const mla_gd_handle* handle, void* workspace, uint32_t* bits, void* stream);
 
 /* Human-readable name of an error code (never NULL). */
 const char* mla_gather_decode_strerror(int code);

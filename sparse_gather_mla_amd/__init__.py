@@ -22,6 +22,8 @@ LIB_PATH = os.environ.get("MLA_GD_LIBRARY") or os.path.join(_PKG, "libmla_gather
 
 MLA_GD_FLAG_FUSED = 1
 MLA_GD_FLAG_GRAPH = 2
+MLA_GD_FLAG_DEBUG_CHECKS = 4
+MLA_GD_CHECK_SLOT_RANGE, MLA_GD_CHECK_BLOCK_RANGE, MLA_GD_CHECK_TABLE_COLUMN, MLA_GD_CHECK_SLOT_SHARED = 1, 2, 4, 8
 
 
 class MlaGdError(RuntimeError):
@@ -77,6 +79,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                                     ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.mla_gather_decode_step_profiled.restype = ctypes.c_int
+    lib.mla_gather_decode_debug_status.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32),
+                                                   ctypes.c_void_p]
+    lib.mla_gather_decode_debug_status.restype = ctypes.c_int
     lib.mla_gather_decode_kernel_count.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     lib.mla_gather_decode_kernel_count.restype = ctypes.c_int
     lib.mla_gather_decode_kernel_name.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int]
@@ -126,10 +131,12 @@ class MlaGatherDecode:
     """One handle of the C library plus a workspace, for up to ``max_tokens`` tokens."""
 
     def __init__(self, dims: Dims, max_tokens: int, device: int = 0, fused: bool = False,
-                 allocate_workspace: bool = True, graph: bool = False):
+                 allocate_workspace: bool = True, graph: bool = False, debug_checks: bool = False):
         """``fused``: the fused variant (kv rows, absorption and core in one launch).
         ``graph``: capture the step once into a HIP graph and replay it (default:
-        kernels launched one by one)."""
+        kernels launched one by one).  ``debug_checks``: device-side checks of
+        the index data (slot range and sharing, block-table column and block id
+        ranges); see debug_status()."""
         import torch
 
         self.lib = load_library()
@@ -143,7 +150,8 @@ class MlaGatherDecode:
                    v_head_dim=dims.v_head_dim, n_heads=dims.n_heads, block_size=dims.block_size,
                    max_blocks_per_seq=dims.max_blocks_per_seq, n_blocks=dims.n_blocks, n_prior=dims.n_prior,
                    max_tokens=self.max_tokens, softmax_scale=dims.softmax_scale, norm_eps=dims.norm_eps,
-                   flags=(MLA_GD_FLAG_FUSED if fused else 0) | (MLA_GD_FLAG_GRAPH if graph else 0))
+                   flags=(MLA_GD_FLAG_FUSED if fused else 0) | (MLA_GD_FLAG_GRAPH if graph else 0)
+                   | (MLA_GD_FLAG_DEBUG_CHECKS if debug_checks else 0))
         h = ctypes.c_void_p()
         rc = self.lib.mla_gather_decode_create(ctypes.byref(cd), int(device), ctypes.byref(h))
         if rc != 0:
@@ -192,6 +200,20 @@ class MlaGatherDecode:
 
     def __call__(self, inp: Dict[str, object], **kw):
         return self.step(inp, **kw)
+
+    def debug_status(self, workspace=None) -> int:
+        """Error bits (MLA_GD_CHECK_*) the debug checks recorded since the last
+        read, after the work enqueued on the current stream; clears them."""
+        import torch
+
+        ws = self.workspace if workspace is None else workspace
+        bits = ctypes.c_uint32(0)
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        rc = self.lib.mla_gather_decode_debug_status(self.handle, ctypes.c_void_p(ws.data_ptr()), ctypes.byref(bits),
+                                                     ctypes.c_void_p(stream))
+        if rc not in (0, 6):  # MLA_GD_OK, MLA_GD_E_DEVICE_CHECK
+            raise MlaGdError(rc, "mla_gather_decode_debug_status", self.lib.mla_gather_decode_last_hip_error(self.handle))
+        return int(bits.value)
 
     def kernel_names(self, n_tokens: int):
         """Names of the kernels a step of ``n_tokens`` tokens launches, in order."""

@@ -256,6 +256,7 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   const size_t f = sizeof(float);
   const size_t frag = 2 * kAFragElems * sizeof(uint16_t);  // one (k-step, m-tile): both halves
   pl.off_zero = take(256);
+  pl.off_err = take(256);  // debug error word: the same offset for every n_tokens
   pl.off_sync = take((size_t)(NH + 2) * 64);
   pl.off_rows = take((size_t)T * P * sizeof(int32_t));
   pl.off_a1 = take((size_t)pl.kt1 * pl.mt_pad * frag);
@@ -346,6 +347,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   };
   const size_t f = sizeof(float);
   pl.off_zero = take(256);
+  pl.off_err = take(256);  // debug error word: the same offset for every n_tokens
   pl.off_sync = take((size_t)(NH + 2) * 64);
   pl.off_rows = take((size_t)T * P * sizeof(int32_t));
   pl.off_part1 = take((size_t)pl.s1 * T * (Q + KVR) * f);
@@ -372,7 +374,7 @@ int validate_dims(const mla_gd_dims& d) {
       d.max_blocks_per_seq <= 0 || d.n_blocks <= 0 || d.n_prior <= 0 || d.max_tokens <= 0)
     return MLA_GD_E_INVAL;
   if (d.qk_rope_head_dim % 2 != 0) return MLA_GD_E_INVAL;
-  if ((d.flags & ~(MLA_GD_FLAG_FUSED | MLA_GD_FLAG_GRAPH)) != 0u) return MLA_GD_E_INVAL;
+  if ((d.flags & ~(MLA_GD_FLAG_FUSED | MLA_GD_FLAG_GRAPH | MLA_GD_FLAG_DEBUG_CHECKS)) != 0u) return MLA_GD_E_INVAL;
   if (!isfinite(d.softmax_scale) || !isfinite(d.norm_eps) || d.norm_eps < 0.f) return MLA_GD_E_INVAL;
   const long long KVR = (long long)d.kv_lora_rank + d.qk_rope_head_dim;
   const long long N2 = (long long)d.n_heads * (d.qk_nope_head_dim + d.qk_rope_head_dim);
@@ -432,6 +434,7 @@ constexpr int kNumKernelsGemv = 7;
 constexpr int kNumKernelsMfma = 9;
 constexpr size_t kGemvLdsBytes = kGemvLdsFloats * sizeof(float);
 constexpr int kMaxLdsBytes = 160 * 1024;
+constexpr size_t kErrOffset = 256;  // Plan::off_err in every plan (right after the zero bytes)
 
 int num_kernels(const Plan& pl) {
   if (pl.fused) return kNumKernelsGemv - 1;
@@ -518,6 +521,7 @@ const char* mla_gather_decode_strerror(int code) {
     case MLA_GD_E_WORKSPACE: return "workspace too small";
     case MLA_GD_E_UNSUPPORTED: return "unsupported dimensions";
     case MLA_GD_E_HIP: return "HIP runtime error";
+    case MLA_GD_E_DEVICE_CHECK: return "device check failed (invalid index data in an earlier step)";
     default: return "unknown error";
   }
 }
@@ -688,6 +692,30 @@ hipError_t launch_graph(mla_gd_handle* h, const StepParams& p, hipStream_t s) {
   return hipGraphLaunch(h->exec, s);
 }
 
+// Debug checks: wait for the work on `stream`, read the workspace's error
+// word into *bits and clear it (with a fill kernel, so the call stays free of
+// memset nodes).
+int read_clear_err(mla_gd_handle* h, void* workspace, hipStream_t s, uint32_t* bits) {
+  unsigned* err = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + kErrOffset);
+  uint32_t w = 0;
+  hipError_t e = hipSetDevice(h->device);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (e == hipSuccess) e = hipStreamIsCapturing(s, &cap);
+  if (e == hipSuccess && cap != hipStreamCaptureStatusNone) return MLA_GD_E_INVAL;  // a read-back cannot be captured
+  if (e == hipSuccess) e = hipMemcpyAsync(&w, err, sizeof(w), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && w != 0u) {
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(kBlock), 0, s, err, (size_t)1);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) {
+    h->last_hip_error = (int)e;
+    return MLA_GD_E_HIP;
+  }
+  *bits = w;
+  return w ? MLA_GD_E_DEVICE_CHECK : MLA_GD_OK;
+}
+
 int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void* workspace,
              size_t workspace_bytes, void* stream, void* const* events, int n_events) {
   if (!h || !tn || !workspace) return MLA_GD_E_INVAL;
@@ -712,6 +740,11 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
 
   const Plan pl = make_plan(d, n_tokens);
   if (workspace_bytes < pl.total) return MLA_GD_E_WORKSPACE;
+  if (d.flags & MLA_GD_FLAG_DEBUG_CHECKS) {
+    uint32_t bits = 0;
+    const int rc = read_clear_err(h, workspace, (hipStream_t)stream, &bits);
+    if (rc != MLA_GD_OK) return rc;
+  }
 
   StepParams p;
   memset(&p, 0, sizeof(p));
@@ -719,6 +752,8 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   p.DR = d.qk_rope_head_dim; p.DV = d.v_head_dim; p.NH = d.n_heads; p.BS = d.block_size;
   p.MB = d.max_blocks_per_seq; p.P = d.n_prior; p.KVR = p.R + p.DR; p.QKH = p.DN + p.DR;
   p.N2 = p.NH * p.QKH;
+  p.NBLK = d.n_blocks;
+  p.dbg = (d.flags & MLA_GD_FLAG_DEBUG_CHECKS) ? 1 : 0;
   p.scale_log2 = d.softmax_scale * 1.4426950408889634f;
   p.eps = d.norm_eps;
   p.x = (const uint16_t*)tn->hidden_states; p.g_in = tn->input_norm_w; p.wq_a = (const uint16_t*)tn->wq_a;
@@ -742,6 +777,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
     p.ssq = (float*)(ws + pl.off_ssq);
   }
   p.sync = (unsigned*)(ws + pl.off_sync);
+  p.err = (unsigned*)(ws + pl.off_err);
   p.pl = pl;
 
   hipError_t e = hipSetDevice(h->device);
@@ -780,6 +816,11 @@ extern "C" {
 int mla_gather_decode_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void* workspace,
                            size_t workspace_bytes, void* stream) {
   return run_step(h, tn, n_tokens, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+int mla_gather_decode_debug_status(const mla_gd_handle* handle, void* workspace, uint32_t* bits, void* stream) {
+  if (!handle || !workspace || !bits || !(handle->d.flags & MLA_GD_FLAG_DEBUG_CHECKS)) return MLA_GD_E_INVAL;
+  return read_clear_err(const_cast<mla_gd_handle*>(handle), workspace, (hipStream_t)stream, bits);
 }
 
 int mla_gather_decode_step_profiled(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens,

@@ -23,6 +23,7 @@
 #include "device_util.h"
 #include "gemv.h"
 #include "step_params.h"
+#include "mla_gather_decode.h"
 
 namespace mla {
 
@@ -48,16 +49,44 @@ __device__ __forceinline__ float inv_rms(float sumsq, int n, float eps) {
 
 // Index build for entry idx = t*P + j: selected position -> flat cache row,
 // -1 where causally masked.  Masked entries touch neither the block table nor
-// the cache.
+// the cache.  With the debug checks, an entry whose block-table column or
+// block id is out of range is masked too, and reported.
 __device__ __forceinline__ void index_build(const StepParams& p, int idx) {
   if (idx >= p.pl.T * p.P) return;
   const int t = idx / p.P;
   const int g = p.gidx[idx];
   const int ps = p.pos[t];
   int row = -1;
-  if (g >= 0 && g <= ps) row = p.btab[(size_t)t * p.MB + g / p.BS] * p.BS + g % p.BS;
+  if (g >= 0 && g <= ps) {
+    const int col = g / p.BS;
+    if (p.dbg && col >= p.MB) {
+      atomicOr(p.err, MLA_GD_CHECK_TABLE_COLUMN);
+    } else {
+      const int blk = p.btab[(size_t)t * p.MB + col];
+      if (p.dbg && (unsigned)blk >= (unsigned)p.NBLK) atomicOr(p.err, MLA_GD_CHECK_BLOCK_RANGE);
+      else row = blk * p.BS + g % p.BS;
+    }
+  }
   p.rows[idx] = row;
   if (p.rows_out) p.rows_out[idx] = row;
+}
+
+// Whether token t's cache row may be written: always without the debug
+// checks; with them, when slot_mapping[t] lies in the pool (a slot shared
+// with another token is reported and still written).  Every thread of the
+// workgroup calls it.
+__device__ __forceinline__ bool slot_ok(const StepParams& p, int t) {
+  if (!p.dbg) return true;
+  const int s = p.slot[t];
+  const bool in_range = (unsigned)s < (unsigned)p.NBLK * (unsigned)p.BS;
+  int shared = 0;
+  for (int u = threadIdx.x; u < p.pl.T; u += blockDim.x) shared |= (u != t && p.slot[u] == s);
+  shared = __syncthreads_or(shared);
+  if (threadIdx.x == 0) {
+    if (!in_range) atomicOr(p.err, MLA_GD_CHECK_SLOT_RANGE);
+    if (shared) atomicOr(p.err, MLA_GD_CHECK_SLOT_SHARED);
+  }
+  return in_range;
 }
 
 // ---------------------------------------------------------------------------
@@ -277,6 +306,7 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
     for (int i = threadIdx.x; i < pl.nkv; i += kBlock) ss += p.kvss[(size_t)t * pl.nkv + i];
     ss = block_sum(ss, scratch);
     const float inv = inv_rms(ss, p.R, p.eps);
+    if (!slot_ok(p, t)) return;
     bf16_t* row = p.cache + (size_t)p.slot[t] * p.KVR;
     for (int c = threadIdx.x; c < p.R; c += kBlock) row[c] = f32_to_bf16(kv[c] * inv * p.g_kv[c]);
     const int half = p.DR / 2;

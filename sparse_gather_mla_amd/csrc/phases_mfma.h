@@ -233,6 +233,7 @@ __device__ void phase_qa(const StepParams& p, int b, float* lds) {
   for (int c = tid; c < p.R; c += kBlock) sk = fmaf(y[c], y[c], sk);
   sk = block_sum(sk, scratch);
   const float inv = inv_rms(sk, p.R, p.eps);
+  if (!slot_ok(p, t)) return;
   bf16_t* crow = p.cache + (size_t)p.slot[t] * p.KVR;
   for (int c = tid; c < p.R; c += kBlock) crow[c] = f32_to_bf16(y[c] * inv * p.g_kv[c]);
   const int half = p.DR / 2;

@@ -43,7 +43,7 @@ struct Plan {
   int nxc, nqc;                // k_prep chunks of hidden; k_qa chunks of q_lora_rank (per token)
   int kt6, ks6m, nt6m;         // o_proj: slabs in s6
   // workspace layout (byte offsets)
-  size_t off_zero, off_rows, off_part1, off_ssx, off_part2, off_ssq, off_kvr, off_kvss, off_qcat;
+  size_t off_zero, off_err, off_rows, off_part1, off_ssx, off_part2, off_ssq, off_kvr, off_kvss, off_qcat;
   size_t off_pm, off_pl, off_po, off_ov, off_part6;
   size_t off_a1, off_a2, off_a5;
   size_t off_sync;  // fused variant's counters (same offset for every n_tokens)
@@ -53,6 +53,8 @@ struct Plan {
 struct StepParams {
   // dimensions
   int H, Q, R, DN, DR, DV, NH, BS, MB, P, KVR, QKH, N2;
+  int NBLK;  // n_blocks (pool blocks)
+  int dbg;   // debug checks of the index data (MLA_GD_FLAG_DEBUG_CHECKS)
   float scale_log2;  // softmax_scale * log2(e): scores live in the log2 domain
   float eps;
   // inputs (device pointers)
@@ -97,6 +99,7 @@ struct StepParams {
   // fused variant: counters kSyncStride words apart -- [0] kv rows written,
   // [1] error flag (a wait timed out), [2 + h] absorption tiles of head h done
   unsigned* sync;
+  unsigned* err;  // debug error word (MLA_GD_CHECK_* bits)
   Plan pl;
 };
 

@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -42,7 +42,7 @@ def test_abi_version_and_strerror(lib):
     assert lib.mla_gather_decode_abi_version() == c["MLA_GD_ABI_VERSION"]
     seen = set()
     for name in ("MLA_GD_OK", "MLA_GD_E_INVAL", "MLA_GD_E_ALIGN", "MLA_GD_E_WORKSPACE", "MLA_GD_E_UNSUPPORTED",
-                 "MLA_GD_E_HIP"):
+                 "MLA_GD_E_HIP", "MLA_GD_E_DEVICE_CHECK"):
         s = lib.mla_gather_decode_strerror(c[name]).decode()
         assert s and s not in seen
         seen.add(s)
@@ -200,3 +200,35 @@ def test_fused_flag_kernel_list(lib):
         assert "k_core" in names(h, 1) and "k_absorb_core" not in names(h, 1)
     finally:
         lib.mla_gather_decode_destroy(h)
+
+
+def test_debug_checks_flag_and_status_arguments(lib):
+    """The debug-checks flag is accepted; the status query rejects a handle
+    created without it and null arguments before any GPU call."""
+    c = _codes()
+    rc, h = _create(lib, _dims(flags=c["MLA_GD_FLAG_DEBUG_CHECKS"]))
+    assert rc == 0
+    bits = ctypes.c_uint32(0)
+    try:
+        assert lib.mla_gather_decode_debug_status(h, None, ctypes.byref(bits), None) == c["MLA_GD_E_INVAL"]
+        assert lib.mla_gather_decode_debug_status(h, ctypes.c_void_p(4096), None, None) == c["MLA_GD_E_INVAL"]
+    finally:
+        lib.mla_gather_decode_destroy(h)
+    rc, h = _create(lib, _dims())
+    assert rc == 0
+    try:
+        assert lib.mla_gather_decode_debug_status(h, ctypes.c_void_p(4096), ctypes.byref(bits), None) == c["MLA_GD_E_INVAL"]
+    finally:
+        lib.mla_gather_decode_destroy(h)
+    assert lib.mla_gather_decode_debug_status(None, ctypes.c_void_p(4096), ctypes.byref(bits), None) == c["MLA_GD_E_INVAL"]
+    # distinct check bits
+    bits_def = [c[k] for k in ("MLA_GD_CHECK_SLOT_RANGE", "MLA_GD_CHECK_BLOCK_RANGE", "MLA_GD_CHECK_TABLE_COLUMN",
+                               "MLA_GD_CHECK_SLOT_SHARED")]
+    assert sorted(bits_def) == [1, 2, 4, 8]
+
+
+def test_binding_constants_match_the_header():
+    c = _codes()
+    for k in ("MLA_GD_FLAG_FUSED", "MLA_GD_FLAG_GRAPH", "MLA_GD_FLAG_DEBUG_CHECKS", "MLA_GD_CHECK_SLOT_RANGE",
+              "MLA_GD_CHECK_BLOCK_RANGE", "MLA_GD_CHECK_TABLE_COLUMN", "MLA_GD_CHECK_SLOT_SHARED"):
+        assert getattr(sgm, k) == c[k], k
