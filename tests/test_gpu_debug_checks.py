@@ -219,3 +219,42 @@ def test_shared_slot_is_reported(path):
     # each element of the shared row is token 0's or token 1's; token 1's own slot is untouched
     assert bool(((flat[s0] == ref[s0]) | (flat[s0] == ref[s1])).all())
     assert torch.equal(flat[s1], pool0.view(-1, kvr)[s1])
+
+
+def test_debug_checks_with_graph_replay():
+    """With the graph flag the error word is read before each replay; index data
+    changed in place (same pointers) reach the replayed kernels."""
+    wl = TINY
+    sh = wl.shape
+    bs = sh.block_size
+    _say(f"[debug] graph replay, T={sh.n_tokens}")
+    inp = make_inputs(wl, with_pool=False)
+    g = gpu_inputs(wl, inp)
+    dims = Dims.from_shape(sh)
+    mod = MlaGatherDecode(dims, max_tokens=sh.n_tokens, graph=True, debug_checks=True)
+    plain = MlaGatherDecode(dims, max_tokens=sh.n_tokens)
+    pool0 = g["kv_cache"].clone()
+    out1 = mod(g).clone()
+    out2 = mod(g).clone()
+    torch.cuda.synchronize()
+    assert mod.debug_status() == 0
+    g["kv_cache"].copy_(pool0)
+    ref = plain(g).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, ref) and torch.equal(out2, ref)
+    # an out-of-range block id written in place into the captured block table
+    pos = int(inp["positions"][0])
+    col = [int(x) for x in inp["gather_indices"][0] if 0 <= int(x) <= pos][0] // bs
+    masked, n = _mask_entries(inp, 0, lambda x: x // bs == col)
+    assert n > 0
+    g["block_table"][0, col] = sh.n_blocks + 3
+    out3 = mod(g).clone()
+    torch.cuda.synchronize()
+    _say("[debug] graph replay with a bad block id done")
+    assert mod.debug_status() == MLA_GD_CHECK_BLOCK_RANGE
+    ok, err, bound = within_tol(bf16_to_f64(out3), oracle_reference(wl, masked, list(range(sh.n_tokens)))["out"])
+    assert ok, (err, bound)
+    mod(g)
+    with pytest.raises(MlaGdError) as ei:
+        mod(g)
+    assert ei.value.code == E_DEVICE_CHECK
