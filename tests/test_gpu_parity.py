@@ -317,3 +317,23 @@ def test_graph_replay_matches_direct_launches_and_recaptures():
     torch.cuda.synchronize()
     for o in outs + [other]:
         assert torch.equal(o, ref)
+
+
+# ---------------------------------------------------------------------------
+# the documented size limits, on the small dims: n_prior = 262144 (64 core
+# splits of 4096 rows, the most row ids a core workgroup stages) and
+# max_tokens = 4096 (32 blocks of 128 tokens on the matrix cores)
+# ---------------------------------------------------------------------------
+MAX_PRIOR = replace(CONFIGS[0], name="tiny_max_prior",
+                    shape=replace(CONFIGS[0].shape, n_tokens=1, n_prior=262144, max_blocks_per_seq=18760),
+                    contexts=(300000,), context_range=None, n_duplicates=1000, n_future=1000, seed=2101)
+MAX_TOKENS = replace(CONFIGS[0], name="tiny_max_tokens", shape=replace(CONFIGS[0].shape, n_tokens=4096),
+                     contexts=None, context_range=(40, 120), seed=2102)
+
+
+def test_parity_largest_n_prior():
+    _run_and_check(MAX_PRIOR)
+
+
+def test_parity_largest_token_count():
+    _run_and_check(MAX_TOKENS, tokens=[0, 1, 2047, 4095])
