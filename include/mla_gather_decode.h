@@ -20,7 +20,11 @@
  *   - mla_gather_decode_step() only enqueues work on the given HIP stream and
  *     never synchronises the host; errors inside kernels are not reported
  *     (device data validity -- slot and block ids in range, distinct slots --
- *     is the caller's contract, as on the page).
+ *     is the caller's contract, as on the page).  A handle created with
+ *     MLA_GD_FLAG_DEBUG_CHECKS is the exception: its steps check that data
+ *     on the device and wait for the stream once per step (see the flag).
+ *   - Calls that touch the device make the handle's device current on the
+ *     calling thread.
  *   - A handle may be used from one thread at a time.  Two steps that overlap
  *     in time must use different workspaces.
  */
