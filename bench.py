@@ -185,6 +185,80 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, workload: str) -> int:
     return 0
 
 
+def router_bench(args) -> int:
+    """Cold latency of the fused RMSNorm + router top-K (two kernels), with the
+    roofline of its GEMV kernel and the oracle timed on the host."""
+    import json as _json
+    import statistics
+    import time
+
+    import numpy as np
+    import torch
+
+    from oracle import router_oracle as ro
+    from sparse_gather_mla_amd.router import rmsnorm_router_topk, workspace_size
+    from workload import ROUTER_CONFIGS, make_router_inputs
+
+    T, H, E, K = ROUTER_CONFIGS[args.router]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = make_router_inputs(T, H, E, seed=31, with_bias=True)
+    g = {k: v.to(dev) for k, v in inp.items()}
+    out = (torch.empty((T, H), dtype=torch.bfloat16, device=dev), torch.empty((T, K), dtype=torch.int32, device=dev),
+           torch.empty((T, E), dtype=torch.bfloat16, device=dev))
+    ws = torch.empty(workspace_size(T, H, E), dtype=torch.uint8, device=dev)
+    flush = torch.zeros((1 << 30) // 4, dtype=torch.float32, device=dev)
+
+    def run():
+        rmsnorm_router_topk(g["hidden_states"], g["gamma"], g["router_weights"], g["router_bias"], 1e-6, K,
+                            "sigmoid", workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        flush.add_(1.0)
+        run()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(args.steps):
+        flush.add_(1.0)  # cold: evicts the L2s and the Infinity Cache
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    us = statistics.mean(a.elapsed_time(b) for a, b in ev) * 1e3
+    # algorithmic bytes: weights, hidden states (read twice: GEMV and the normalised
+    # write), gamma, bias, and the three outputs
+    alg = 2 * H * E + 2 * 2 * T * H + 2 * H + 4 * E + 2 * T * H + 4 * T * K + 2 * T * E
+    gemv_alg = 2 * H * E + 2 * T * H + 2 * H
+    x = inp["hidden_states"].to(torch.float64).numpy()
+    gam, w = inp["gamma"].to(torch.float64).numpy(), inp["router_weights"].to(torch.float64).numpy()
+    bias = inp["router_bias"].to(torch.float64).numpy()
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < min(args.cpu_budget, 10.0) or n == 0:
+        ro.rmsnorm_router_topk(x, gam, w, bias, 1e-6, K, ro.SIGMOID)
+        n += 1
+    cpu_us = (time.perf_counter() - t0) / n * 1e6
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    line = {"metric": "rmsnorm_router_topk_latency", "value": round(us, 3), "unit": "us", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": us / 1e3, "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{args.router}: T={T}, H={H}, E={E}, top_k={K}, sigmoid, bias",
+                       "cache_state": "cold (1 GiB flush per call)"},
+            "roofline": {"bound": "hbm", "kernel": "whole call (k_rt_partial + k_rt_select)",
+                         "achieved": round(alg / us / 1e3, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(alg / us / 1e3 / 8000.0, 4), "traffic": None, "alg_bytes": alg,
+                         "gemv_alg_bytes": gemv_alg},
+            "cpu_baseline": {"value": round(cpu_us, 1), "unit": "us", "cores": cores, "kind": "oracle",
+                             "sample": f"{n} whole calls, fp64 numpy"}}
+    print(_json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +273,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--router", default=None, metavar="NAME",
+                    help="time the fused RMSNorm + router top-K instead (router_t1 or router_t128)")
     args = ap.parse_args()
 
     if args.traffic:
@@ -207,6 +283,9 @@ def main() -> int:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the step is single-GPU; the multi-GPU design is documented, not built)", file=sys.stderr)
         return 2
+
+    if args.router:
+        return router_bench(args)
 
     import numpy as np
     import torch

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libmla_gather_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "mla_gather_decode.hip")]
+SOURCES = [os.path.join(CSRC, "mla_gather_decode.hip"), os.path.join(PKG, "router", "rmsnorm_router_topk.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("device_util.h", "phases.h", "step_params.h")] + [
     os.path.join(ROOT, "include", "mla_gather_decode.h")]
 

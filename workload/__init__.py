@@ -6,6 +6,8 @@ and the GPU path can be fed from it without sharing any method code.
 """
 from .gen import (  # noqa: F401
     CONFIGS,
+    ROUTER_CONFIGS,
+    make_router_inputs,
     MlaShape,
     Workload,
     config_by_name,

@@ -151,6 +151,7 @@ _TAGS: Dict[str, int] = {
     "hidden_states": 1, "input_norm_w": 2, "wq_a": 3, "q_norm_w": 4, "wq_b": 5,
     "wkv_a": 6, "kv_norm_w": 7, "q_absorb_w": 8, "out_absorb_w": 9, "o_proj_w": 10,
     "contexts": 11, "block_table": 12, "gather_indices": 13, "kv_pool": 14,
+    "router_hidden": 21, "router_gamma": 22, "router_weights": 23, "router_bias": 24,
 }
 
 
@@ -364,4 +365,31 @@ def make_inputs(wl: Workload, device="cpu", with_pool: bool = True,
         pdev = torch.device(pool_device) if pool_device is not None else dev
         pool = torch.empty((sh.n_blocks, 1, bs, kvr), dtype=torch.bfloat16, device=pdev)
         out["kv_cache"] = fill_pool_(wl, pool)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# the fused RMSNorm + router top-K (the MoE block's first step)
+# ----------------------------------------------------------------------------
+
+# (n_tokens, hidden, n_experts, top_k): DeepSeek-V3-sized routers at one and at
+# the page's largest token count
+ROUTER_CONFIGS = {
+    "router_t1": (1, 7168, 256, 8),
+    "router_t128": (128, 7168, 256, 8),
+}
+
+
+def make_router_inputs(n_tokens: int, hidden: int, n_experts: int, seed: int, with_bias: bool = True):
+    """hidden_states [T, H] bf16 ~ N(0, 1), gamma [H] bf16 ~ 1 + 0.1 N, router
+    weights [H, E] bf16 ~ N(0, 1/H) (logits of unit scale), bias [E] fp32 ~ 0.1 N."""
+    out = {
+        "hidden_states": _normal_bf16(seed, "router_hidden", (n_tokens, hidden), 1.0),
+        "gamma": _bf16(1.0 + 0.1 * _rng(seed, "router_gamma").standard_normal(size=(hidden,))),
+        "router_weights": _normal_bf16(seed, "router_weights", (hidden, n_experts), 1.0 / math.sqrt(hidden)),
+        "router_bias": None,
+    }
+    if with_bias:
+        b = 0.1 * _rng(seed, "router_bias").standard_normal(size=(n_experts,))
+        out["router_bias"] = torch.from_numpy(b).to(torch.float32)
     return out
