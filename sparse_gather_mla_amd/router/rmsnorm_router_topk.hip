@@ -28,7 +28,7 @@ constexpr int kTW = 64;      // experts per GEMV tile (128-byte weight row segme
 constexpr int kMaxKs = 256;  // slab rows: one batch of weight loads per lane at 64 columns
 constexpr int kNtt = kTT;    // tokens per GEMV pass
 constexpr int kMaxT = 128, kMaxH = 65536, kMaxE = 1024, kMaxK = 32;
-constexpr int kTargetWG = 384;
+constexpr int kTargetWG = 112;  // GEMV workgroups before token groups: few slabs keep the select reduction short
 
 struct RtPlan {
   int ntile, s, ks;
