@@ -2,7 +2,9 @@
 
 Bars: gathered row addresses / mask bits and the set of written cache slots
 bit-exact; the bf16 output and the bf16 written cache-row values within
-max |err| <= 2e-2 * RMS(reference) (fp32 accumulation on the GPU).
+|err| <= 2e-2 * RMS(reference) per element, plus half the bf16 spacing at the
+reference value (the format's floor; it matters only beyond about 5 RMS),
+with fp32 accumulation on the GPU.  Every token is compared.
 """
 import sys
 from dataclasses import replace
@@ -13,7 +15,7 @@ import torch
 
 import oracle
 from sparse_gather_mla_amd import Dims, MlaGatherDecode
-from tests.harness import (TOL, bf16_to_f64, gpu_inputs, index_build_all, oracle_reference, rms,
+from tests.harness import (TOL, bf16_half_ulp, bf16_to_f64, gpu_inputs, index_build_all, oracle_reference, rms,
                            token_slice, within_tol)
 from workload import CONFIGS, MlaShape, Workload, make_inputs, pool_rows
 
@@ -61,11 +63,20 @@ def _run_and_check(wl: Workload, tokens=None, fused=False, mutate=None, pool_che
     ref = oracle_reference(wl, inp, tokens)
     got_out = bf16_to_f64(out[torch.as_tensor(tokens, device="cuda")])
     ok, err, bound = within_tol(got_out, ref["out"])
-    _say(f"[parity] {wl.name} out: max err {err:.3e} bound {bound:.3e} (rms {rms(ref['out']):.3e})")
+    excess = float(np.max(np.abs(got_out - ref["out"]) - bf16_half_ulp(ref["out"]))) / bound
+    _say(f"[parity] {wl.name} out ({len(tokens)} of {T} tokens): max err {err:.3e} bound {bound:.3e} "
+         f"err/bound {err / bound:.3f}, (err - bf16 floor)/bound {excess:.3f} (rms {rms(ref['out']):.3e})")
     assert ok
+    # the worst token on its own scale too (a token whose output is much smaller
+    # than the batch RMS must not hide behind the others)
+    per_tok = [float(np.max(np.abs(got_out[i] - ref["out"][i]))) / (TOL * rms(ref["out"][i]))
+               for i in range(len(tokens)) if rms(ref["out"][i]) > 0]
+    if per_tok:
+        worst = int(np.argmax(per_tok))
+        _say(f"[parity] {wl.name} worst token {tokens[worst]}: err/(2e-2*rms of that token) {per_tok[worst]:.3f}")
     got_rows = bf16_to_f64(pool.view(-1, kvr)[slots[torch.as_tensor(tokens, device="cuda")]])
     ok, err, bound = within_tol(got_rows, ref["new_row"])
-    _say(f"[parity] {wl.name} cache rows: max err {err:.3e} bound {bound:.3e}")
+    _say(f"[parity] {wl.name} cache rows: max err {err:.3e} bound {bound:.3e} err/bound {err / bound:.3f}")
     assert ok
     # the GPU's stored row is a bf16 rounding of a value within tolerance of the exact row
     return out, ref, inp, g
@@ -77,10 +88,11 @@ def test_parity_small_and_medium(name):
     _run_and_check(wl)
 
 
-@pytest.mark.parametrize("name,tokens", [("fullhead64", [0, 17, 40, 63]), ("large128", [0, 77, 127])])
-def test_parity_full_head_sampled_tokens(name, tokens):
+# the 128-head configurations at full size, every token compared with the oracle
+@pytest.mark.parametrize("name", ["fullhead64", "large128"])
+def test_parity_full_head_all_tokens(name):
     wl = next(w for w in CONFIGS if w.name == name)
-    _run_and_check(wl, tokens=tokens)
+    _run_and_check(wl)
 
 
 # ---------------------------------------------------------------------------
@@ -111,7 +123,7 @@ def test_parity_ragged_shape_gemv_token_passes(T):
 # one ragged) in every GEMM, the absorptions and the index build.
 def test_parity_ragged_shape_two_token_blocks():
     wl = replace(RAGGED, name="ragged_T150", shape=replace(RAGGED.shape, n_tokens=150), seed=227)
-    _run_and_check(wl, tokens=[0, 63, 127, 128, 149])
+    _run_and_check(wl)
 
 
 # Steps of more than 8 tokens run the projections on the matrix cores.  Token
@@ -336,4 +348,4 @@ def test_parity_largest_n_prior():
 
 
 def test_parity_largest_token_count():
-    _run_and_check(MAX_TOKENS, tokens=[0, 1, 2047, 4095])
+    _run_and_check(MAX_TOKENS)

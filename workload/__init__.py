@@ -16,4 +16,5 @@ from .gen import (  # noqa: F401
     pool_rows,
     splitmix64_np,
     splitmix64_torch,
+    to_device,
 )

@@ -368,6 +368,19 @@ def make_inputs(wl: Workload, device="cpu", with_pool: bool = True,
     return out
 
 
+def to_device(wl: Workload, inp: Dict[str, object], device="cuda") -> Dict[str, object]:
+    """Copy the tensors of a host input set to ``device``; the cache pool is
+    copied if the set holds one, else allocated and filled there in place."""
+    sh = wl.shape
+    g = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items() if k != "kv_cache"}
+    if "kv_cache" in inp:
+        g["kv_cache"] = inp["kv_cache"].to(device)
+    else:
+        pool = torch.empty((sh.n_blocks, 1, sh.block_size, sh.kv_row_dim), dtype=torch.bfloat16, device=device)
+        g["kv_cache"] = fill_pool_(wl, pool)
+    return g
+
+
 # ----------------------------------------------------------------------------
 # the fused RMSNorm + router top-K (the MoE block's first step)
 # ----------------------------------------------------------------------------
