@@ -218,6 +218,35 @@ int mla_gather_decode_step_profiled(mla_gd_handle* handle, const mla_gd_tensors*
                                     void* const* events, int n_events);
 
 /*
+ * Allocation-free step, for callers that cannot allocate device memory or
+ * create runtime objects: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same step as
+ * mla_gather_decode_step(), with the workspace taken from a static device
+ * array of MLA_GD_STATIC_SCRATCH_BYTES bytes inside the library (one copy per
+ * GPU, held from the first such call on that GPU until the process ends).
+ * The caller passes the tensors and `out` as usual.
+ *   - Returns MLA_GD_E_WORKSPACE, without launching anything, when a step of
+ *     n_tokens tokens needs more workspace than that (16 heads of the
+ *     DeepSeek-V3.2 dims fit up to 32 tokens; 128 heads do not fit).
+ *   - Calls no hipMalloc/hipFree and creates no stream, event or graph: the
+ *     kernels are launched one by one on `stream` (MLA_GD_FLAG_GRAPH is
+ *     ignored).  Handles created with MLA_GD_FLAG_DEBUG_CHECKS get
+ *     MLA_GD_E_INVAL (their read-back is a synchronising copy).
+ *   - The first call on a GPU looks up that GPU's copy of the array
+ *     (hipGetSymbolAddress) with the handle's device current; MLA_GD_E_HIP if
+ *     that fails.
+ *   - Every call on one GPU, from every handle, shares that GPU's array, and
+ *     the array keeps the last step's contents (each step rewrites what it
+ *     reads; its first kernel clears the part that must start at zero).  Two
+ *     steps that may overlap in time on one GPU (different streams, threads
+ *     or handles) race on it: serialise them, or give them
+ *     mla_gather_decode_step() with separate workspaces.
+ */
+#define MLA_GD_STATIC_SCRATCH_BYTES (32u << 20)
+int mla_gather_decode_step_noalloc(mla_gd_handle* handle, const mla_gd_tensors* tensors, int32_t n_tokens,
+                                   void* stream);
+
+/*
  * Debug checks (MLA_GD_FLAG_DEBUG_CHECKS): wait for the work enqueued on
  * `stream`, store the workspace's error word (MLA_GD_CHECK_* bits) in *bits
  * and clear it.  Returns MLA_GD_E_DEVICE_CHECK if any bit was set,

@@ -86,6 +86,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_gather_decode_kernel_count.restype = ctypes.c_int
     lib.mla_gather_decode_kernel_name.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int]
     lib.mla_gather_decode_kernel_name.restype = ctypes.c_char_p
+    lib.mla_gather_decode_step_noalloc.argtypes = [ctypes.c_void_p, ctypes.POINTER(_Tensors), ctypes.c_int32,
+                                                   ctypes.c_void_p]
+    lib.mla_gather_decode_step_noalloc.restype = ctypes.c_int
     lib.mla_gather_decode_abi_version.argtypes = []
     lib.mla_gather_decode_abi_version.restype = ctypes.c_int
     _lib = lib
@@ -221,11 +224,14 @@ class MlaGatherDecode:
         return [self.lib.mla_gather_decode_kernel_name(self.handle, n_tokens, i).decode() for i in range(n)]
 
     def step(self, inp: Dict[str, object], out=None, gather_rows_out=None, workspace=None, stream=None,
-             events=None):
+             events=None, noalloc=False):
         """Enqueue one step on ``stream`` (default: torch's current stream); returns ``out``.
 
         ``events``: optional list of len(kernel_names(T))+1 torch.cuda.Event(enable_timing=True)
-        recorded around each kernel of the step on that stream."""
+        recorded around each kernel of the step on that stream.  ``noalloc``:
+        the allocation-free entry point (mla_gather_decode_step_noalloc), whose
+        workspace is the library's static device array (``workspace`` and
+        ``events`` must be None; pass ``out``, or a new tensor is allocated here)."""
         import torch
 
         d = self.dims
@@ -268,11 +274,20 @@ class MlaGatherDecode:
             setattr(tn, name, self._check(name, t, dt, shp))
         if gather_rows_out is not None:
             tn.gather_rows_out = self._check("gather_rows_out", gather_rows_out, i32, (T, d.n_prior))
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        if noalloc:
+            if workspace is not None or events is not None:
+                raise ValueError("noalloc steps take neither a workspace nor events")
+            rc = self.lib.mla_gather_decode_step_noalloc(self.handle, ctypes.byref(tn), T,
+                                                         ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise MlaGdError(rc, "mla_gather_decode_step_noalloc",
+                                 self.lib.mla_gather_decode_last_hip_error(self.handle))
+            return out
         ws = workspace if workspace is not None else self.workspace
         if ws is None:
             raise ValueError("no workspace")
-        if stream is None:
-            stream = torch.cuda.current_stream(self.device)
         ws_ptr = ctypes.c_void_p(ws.data_ptr())
         ws_bytes = ctypes.c_size_t(ws.numel() * ws.element_size())
         st = ctypes.c_void_p(stream.cuda_stream)

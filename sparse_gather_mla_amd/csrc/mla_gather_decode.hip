@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "../../include/mla_gather_decode.h"
@@ -717,7 +718,7 @@ int read_clear_err(mla_gd_handle* h, void* workspace, hipStream_t s, uint32_t* b
 }
 
 int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void* workspace,
-             size_t workspace_bytes, void* stream, void* const* events, int n_events) {
+             size_t workspace_bytes, void* stream, void* const* events, int n_events, bool force_direct = false) {
   if (!h || !tn || !workspace) return MLA_GD_E_INVAL;
   const mla_gd_dims& d = h->d;
   if (n_tokens < 1 || n_tokens > d.max_tokens) return MLA_GD_E_INVAL;
@@ -792,8 +793,8 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   if (e != hipSuccess) { h->last_hip_error = (int)e; return MLA_GD_E_HIP; }
   // replay the captured graph only when asked for, and never for the
   // profiled step or inside the caller's own capture
-  const bool direct = events || cap != hipStreamCaptureStatusNone || !(d.flags & MLA_GD_FLAG_GRAPH) ||
-                      h->graph_broken;
+  const bool direct = force_direct || events || cap != hipStreamCaptureStatusNone ||
+                      !(d.flags & MLA_GD_FLAG_GRAPH) || h->graph_broken;
   if (!direct) {
     e = launch_graph(h, p, s);
     if (e != hipSuccess) {
@@ -828,6 +829,56 @@ int mla_gather_decode_step_profiled(mla_gd_handle* h, const mla_gd_tensors* tn, 
                                     int n_events) {
   if (!events) return MLA_GD_E_INVAL;
   return run_step(h, tn, n_tokens, workspace, workspace_bytes, stream, events, n_events);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The allocation-free entry point's workspace: one static device array.  Host
+// code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory); each device's copy is looked up once with
+// hipGetSymbolAddress and that pointer is what the kernels get.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MLA_GD_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// This device's copy of `scratch` (the device must be current).
+hipError_t scratch_on_device(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_gather_decode_step_noalloc(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void* stream) {
+  if (!h || !tn) return MLA_GD_E_INVAL;
+  if (h->d.flags & MLA_GD_FLAG_DEBUG_CHECKS) return MLA_GD_E_INVAL;
+  if (n_tokens < 1 || n_tokens > h->d.max_tokens) return MLA_GD_E_INVAL;
+  if (h->device >= kMaxScratchDevices) return MLA_GD_E_INVAL;
+  if (make_plan(h->d, n_tokens).total > (size_t)MLA_GD_STATIC_SCRATCH_BYTES) return MLA_GD_E_WORKSPACE;
+  hipError_t e = hipSetDevice(h->device);
+  void* ws = nullptr;
+  if (e == hipSuccess) e = scratch_on_device(h->device, &ws);
+  if (e != hipSuccess) {
+    h->last_hip_error = (int)e;
+    return MLA_GD_E_HIP;
+  }
+  return run_step(h, tn, n_tokens, ws, MLA_GD_STATIC_SCRATCH_BYTES, stream, nullptr, 0, /*direct=*/true);
 }
 
 int mla_gather_decode_kernel_count(const mla_gd_handle* h, int32_t n_tokens) {

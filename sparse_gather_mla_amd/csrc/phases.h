@@ -71,6 +71,15 @@ __device__ __forceinline__ void index_build(const StepParams& p, int idx) {
   if (p.rows_out) p.rows_out[idx] = row;
 }
 
+// The workspace's 256-byte zero region (the source of padding loads) must
+// read as zeros.  Workgroup 0 of a step's first kernel rewrites it, so a
+// workspace whose earlier contents are unknown (a reused buffer, the static
+// scratch of the allocation-free entry point) needs no separate clearing; no
+// workgroup of a first kernel reads the region.
+__device__ __forceinline__ void clear_zero_region(const StepParams& p, int b) {
+  if (b == 0 && threadIdx.x < 64) const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(p.zero16))[threadIdx.x] = 0u;
+}
+
 // Whether token t's cache row may be written: always without the debug
 // checks; with them, when slot_mapping[t] lies in the pool (a slot shared
 // with another token is reported and still written).  Every thread of the
@@ -133,6 +142,7 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
   // the fused variant's counters start each step at zero (this step's later
   // kernels run after this one; the previous step's have finished)
   if (pl.fused && b == 0 && (int)threadIdx.x < p.NH + 2) p.sync[threadIdx.x * kSyncStride] = 0u;
+  clear_zero_region(p, b);
   if (b >= n_gemv) {
     index_build(p, (b - n_gemv) * kBlock + threadIdx.x);
     return;

@@ -36,6 +36,7 @@ constexpr int kQaChunk = 4 * kBlock;        // q_lora_rank columns per k_qa work
 // ---------------------------------------------------------------------------
 __device__ void phase_prep(const StepParams& p, int b, float* lds) {
   const Plan& pl = p.pl;
+  clear_zero_region(p, b);
   if (b < pl.n_idx_wg) {
     index_build(p, b * kBlock + threadIdx.x);
     return;

@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -232,3 +232,40 @@ def test_binding_constants_match_the_header():
     for k in ("MLA_GD_FLAG_FUSED", "MLA_GD_FLAG_GRAPH", "MLA_GD_FLAG_DEBUG_CHECKS", "MLA_GD_CHECK_SLOT_RANGE",
               "MLA_GD_CHECK_BLOCK_RANGE", "MLA_GD_CHECK_TABLE_COLUMN", "MLA_GD_CHECK_SLOT_SHARED"):
         assert getattr(sgm, k) == c[k], k
+
+
+def test_noalloc_step_rejections_before_any_device_work(lib):
+    """The allocation-free step rejects a null handle or tensors, a handle with
+    debug checks, an out-of-range token count, and a step whose workspace would
+    exceed the static scratch (128 heads of the DeepSeek-V3.2 dims), all before
+    it touches a GPU."""
+    c = _codes()
+    tn = sgm._Tensors()
+    assert lib.mla_gather_decode_step_noalloc(None, ctypes.byref(tn), 1, None) == c["MLA_GD_E_INVAL"]
+    rc, h = _create(lib, _dims(flags=c["MLA_GD_FLAG_DEBUG_CHECKS"]))
+    assert rc == 0
+    try:
+        assert lib.mla_gather_decode_step_noalloc(h, ctypes.byref(tn), 1, None) == c["MLA_GD_E_INVAL"]
+    finally:
+        lib.mla_gather_decode_destroy(h)
+    rc, h = _create(lib, _dims(max_tokens=2))
+    assert rc == 0
+    try:
+        assert lib.mla_gather_decode_step_noalloc(h, None, 1, None) == c["MLA_GD_E_INVAL"]
+        assert lib.mla_gather_decode_step_noalloc(h, ctypes.byref(tn), 0, None) == c["MLA_GD_E_INVAL"]
+        assert lib.mla_gather_decode_step_noalloc(h, ctypes.byref(tn), 3, None) == c["MLA_GD_E_INVAL"]
+    finally:
+        lib.mla_gather_decode_destroy(h)
+    big = _dims(hidden=7168, q_lora_rank=1536, kv_lora_rank=512, qk_nope_head_dim=128, qk_rope_head_dim=64,
+                v_head_dim=128, n_heads=128, block_size=64, max_blocks_per_seq=2048, n_blocks=262144,
+                n_prior=2048, max_tokens=128)
+    rc, h = _create(lib, big)
+    assert rc == 0
+    try:
+        limit = 32 << 20
+        assert lib.mla_gather_decode_workspace_size(h, 128) > limit
+        assert lib.mla_gather_decode_step_noalloc(h, ctypes.byref(tn), 128, None) == c["MLA_GD_E_WORKSPACE"]
+    finally:
+        lib.mla_gather_decode_destroy(h)
+    src = open(HEADER).read()
+    assert "#define MLA_GD_STATIC_SCRATCH_BYTES (32u << 20)" in src
