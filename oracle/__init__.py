@@ -4,6 +4,7 @@ from .mla_oracle import (  # noqa: F401
     bf16_round,
     dense_row_reader,
     front_fold,
+    gather_keys,
     mla_gather_decode_step,
     output_projection,
     resolve_row,

@@ -180,12 +180,34 @@ def output_projection(o_lat: np.ndarray, out_absorb_w: np.ndarray, o_proj_w: np.
 RowReader = Callable[[np.ndarray], np.ndarray]
 
 
+def gather_keys(rows_t: np.ndarray, written: Dict[int, np.ndarray], read_rows: RowReader, kv_row: int) -> np.ndarray:
+    """The cache rows one token attends over: one row per valid selected entry
+    (duplicates kept, masked entries -1 skipped).  A row this step wrote reads
+    the stored value, every other row the pool as it was before the step
+    ("API Reference", ``kv_cache``: the front-fold writes this step's rows,
+    then the core reads selected rows back)."""
+    valid = rows_t[rows_t >= 0]
+    keys = np.empty((len(valid), kv_row))
+    need = [i for i, rr in enumerate(valid.tolist()) if rr not in written]
+    if need:
+        keys[need] = read_rows(valid[need])
+    for i, rr in enumerate(valid.tolist()):
+        if rr in written:
+            keys[i] = written[rr]
+    return keys
+
+
 def mla_gather_decode_step(inp: Dict[str, np.ndarray], read_rows: RowReader,
                            trace: Optional[dict] = None) -> Dict[str, np.ndarray]:
     """One decode step for every token of the batch.
 
     ``inp`` maps the page's parameter names to float64 (values) / int64
-    (indices) numpy arrays, plus the scalar parameters.  ``read_rows(idx)``
+    (indices) numpy arrays, plus the scalar parameters.  An optional
+    ``token_seq`` [T] lets several tokens of one sequence share a step: token
+    t resolves its selected positions through row ``token_seq[t]`` of
+    ``block_table`` (then ``[n_seqs, max_blocks_per_seq]``); without it token
+    t uses row t, one sequence per token as on the page ("Dimensions",
+    ``n_tokens``).  ``read_rows(idx)``
     returns the pool's flat rows ``idx`` as float64 ``[len(idx), kv_row]``
     before this step; the rows the step writes are kept in an overlay, so the
     caller's pool is never modified.
@@ -193,7 +215,10 @@ def mla_gather_decode_step(inp: Dict[str, np.ndarray], read_rows: RowReader,
     Order of effects: the front-fold of every token writes its row into the
     cache first, then the core gathers ("API Reference", ``kv_cache``: the
     front-fold writes this step's row, and the core reads the selected prior
-    rows back).
+    rows back).  So a token that selects the position of another token of its
+    sequence in this step (an earlier one; later ones are causally masked)
+    reads that token's stored row, exactly as if the tokens had run as
+    successive single-token steps in position order.
 
     Returns ``out [T, hidden]``, ``new_row [T, kv_row]`` (exact), ``stored_row``
     ``[T, kv_row]`` (bf16-rounded, as written), ``rows [T, n_prior]`` (flat row
@@ -227,20 +252,15 @@ def mla_gather_decode_step(inp: Dict[str, np.ndarray], read_rows: RowReader,
         written[int(inp["slot_mapping"][t])] = stored[t]
 
     # index build, gather, attention core, output projection
+    seq = inp.get("token_seq")
     rows = np.full((T, P), -1, dtype=np.int64)
     out = np.empty((T, H))
     for t in range(T):
         pos = int(inp["positions"][t])
+        table_row = inp["block_table"][t if seq is None else int(seq[t])]
         for j in range(P):
-            rows[t, j] = resolve_row(int(gi[t, j]), pos, inp["block_table"][t], bs)
-        valid = rows[t][rows[t] >= 0]
-        keys = np.empty((len(valid), kv_row))
-        need = [i for i, rr in enumerate(valid.tolist()) if rr not in written]
-        if need:
-            keys[need] = read_rows(valid[need])
-        for i, rr in enumerate(valid.tolist()):
-            if rr in written:
-                keys[i] = written[rr]
+            rows[t, j] = resolve_row(int(gi[t, j]), pos, table_row, bs)
+        keys = gather_keys(rows[t], written, read_rows, kv_row)
         o_lat = attention_core(q_lat[t], q_pe[t], keys, scale, r)
         out[t] = output_projection(o_lat, w["out_absorb_w"], w["o_proj_w"])
         if trace is not None:

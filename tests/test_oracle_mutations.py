@@ -27,6 +27,8 @@ PIN_TESTS = [
     pins.test_masked_rows_are_never_read,
     pins.test_cache_write_row_and_locality,
     pins.test_bf16_round_matches_torch_conversion,
+    pins.test_index_build_multi_token_fixture,
+    pins.test_multi_token_batch_equals_successive_single_token_steps,
 ]
 
 
@@ -115,6 +117,10 @@ def _ff_heads_split(x_t, w, cos_t, sin_t, n_heads, dn, dr, r, eps):
     return q_lat, q_pe, q_nope, row
 
 
+def _gather_ignores_this_steps_rows(rows_t, written, read_rows, kv_row):
+    return _ORIG["gather_keys"](rows_t, {}, read_rows, kv_row)
+
+
 def _bf16_truncate(x):
     x = np.asarray(x, dtype=np.float64).astype(np.float32)
     b = x.view(np.uint32) & np.uint32(0xFFFF0000)
@@ -122,7 +128,7 @@ def _bf16_truncate(x):
 
 
 _ORIG = {k: getattr(om, k) for k in ("rms_norm", "rope_interleaved", "resolve_row", "attention_core",
-                                     "output_projection", "front_fold", "bf16_round")}
+                                     "output_projection", "front_fold", "bf16_round", "gather_keys")}
 
 MUTANTS = {
     "rope_sign": ("rope_interleaved", _rope_sign),
@@ -139,6 +145,7 @@ MUTANTS = {
     "cache_row_rope_first": ("front_fold", _ff_row_swapped),
     "wq_b_not_head_major": ("front_fold", _ff_heads_split),
     "bf16_truncation": ("bf16_round", _bf16_truncate),
+    "rows_written_this_step_invisible": ("gather_keys", _gather_ignores_this_steps_rows),
 }
 
 

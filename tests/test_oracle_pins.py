@@ -127,6 +127,95 @@ def test_index_build_hand_worked_fixture():
         assert got == g["rows"][t]
 
 
+def _case_with_tables(block_table, token_seq, positions, gather_indices, block_size, seed=0, n_blocks=None,
+                      H=40, Q=16, r=16, dn=8, dr=8, dv=12, nh=3):
+    """Random weights and pool around given index tensors (several tokens may
+    share a sequence's block-table row through token_seq)."""
+    rng = np.random.default_rng(seed)
+    bt = np.asarray(block_table, dtype=np.int64)
+    seq = np.asarray(token_seq, dtype=np.int64)
+    pos = np.asarray(positions, dtype=np.int64)
+    T = len(pos)
+    if n_blocks is None:
+        n_blocks = int(bt.max()) + 1
+    inp = dict(
+        hidden_states=rng.standard_normal((T, H)),
+        input_norm_w=1 + 0.1 * rng.standard_normal(H),
+        wq_a=rng.standard_normal((H, Q)) / math.sqrt(H),
+        q_norm_w=1 + 0.1 * rng.standard_normal(Q),
+        wq_b=rng.standard_normal((Q, nh * (dn + dr))) / math.sqrt(Q),
+        wkv_a=rng.standard_normal((H, r + dr)) / math.sqrt(H),
+        kv_norm_w=1 + 0.1 * rng.standard_normal(r),
+        q_absorb_w=rng.standard_normal((nh, dn, r)) / math.sqrt(r),
+        out_absorb_w=rng.standard_normal((nh, dv, r)) / math.sqrt(r),
+        o_proj_w=rng.standard_normal((nh * dv, H)) / math.sqrt(nh * dv),
+        n_heads=nh, qk_nope_head_dim=dn, qk_rope_head_dim=dr, kv_lora_rank=r,
+        softmax_scale=1 / math.sqrt(dn + dr), norm_eps=1e-6, kv_cache_block_size=block_size,
+    )
+    ang = pos[:, None] * np.power(10000.0, -2.0 * np.arange(dr // 2) / dr)[None, :]
+    inp["cos"], inp["sin"] = np.cos(ang), np.sin(ang)
+    inp["block_table"] = bt
+    inp["token_seq"] = seq
+    inp["positions"] = pos
+    inp["slot_mapping"] = bt[seq, pos // block_size] * block_size + pos % block_size
+    inp["gather_indices"] = np.asarray(gather_indices, dtype=np.int64)
+    pool = rng.standard_normal((n_blocks * block_size, r + dr))
+    return inp, pool
+
+
+def test_index_build_multi_token_fixture():
+    """Several tokens of one sequence: each resolves through its sequence's
+    table row; earlier tokens' positions are valid, later ones masked."""
+    with open(os.path.join(GOLDEN, "index_build_multi_token.json")) as f:
+        g = json.load(f)
+    inp, pool = _case_with_tables(g["block_table"], g["token_seq"], g["positions"], g["gather_indices"],
+                                  g["block_size"])
+    assert inp["slot_mapping"].tolist() == g["slot_mapping"]
+    res = _run(inp, pool)
+    assert res["rows"].tolist() == g["rows"]
+
+
+def test_multi_token_batch_equals_successive_single_token_steps():
+    """Two sequences, three and two tokens at consecutive positions, each
+    selecting its sequence's other tokens' positions (and masked later ones):
+    one batched step equals single-token steps run in position order, each
+    writing its row into the pool before the next one runs."""
+    bs, MB = 4, 6
+    rng = np.random.default_rng(8)
+    bt = rng.permutation(2 * MB).reshape(2, MB)
+    seq = np.array([0, 1, 0, 1, 0])
+    pos = np.array([13, 9, 14, 10, 15])
+    P = 9
+    gi = np.empty((5, P), dtype=np.int64)
+    for t in range(5):
+        mine = [int(p) for p, s in zip(pos, seq) if s == seq[t]]  # its sequence's tokens, earlier and later
+        rest = rng.choice(int(pos[t]) - 2, size=P - len(mine), replace=False)
+        row = np.concatenate([mine, rest])
+        rng.shuffle(row)
+        gi[t] = row
+    inp, pool = _case_with_tables(bt, seq, pos, gi, bs, seed=3, n_blocks=2 * MB)
+    batched = _run(inp, pool)
+    cur = pool.copy()
+    per_token = ("hidden_states", "cos", "sin", "slot_mapping", "positions", "gather_indices")
+    for t in np.argsort(pos, kind="stable"):
+        one = {k: (v[[t]] if k in per_token else v) for k, v in inp.items() if k not in ("token_seq", "block_table")}
+        one["block_table"] = bt[[seq[t]]]
+        res = _run(one, cur)
+        assert np.array_equal(res["rows"][0], batched["rows"][t])
+        np.testing.assert_allclose(res["out"][0], batched["out"][t], rtol=1e-12, atol=1e-14)
+        assert np.array_equal(res["stored_row"][0], batched["stored_row"][t])
+        cur[int(inp["slot_mapping"][t])] = res["stored_row"][0]
+    # the case exercises the cross-token reads: without the pool updates
+    # between the single-token steps, the later tokens' outputs change
+    changed = 0
+    for t in range(5):
+        one = {k: (v[[t]] if k in per_token else v) for k, v in inp.items() if k not in ("token_seq", "block_table")}
+        one["block_table"] = bt[[seq[t]]]
+        stale = _run(one, pool)
+        changed += not np.allclose(stale["out"][0], batched["out"][t], rtol=1e-9)
+    assert changed == 3  # every token but the first of each sequence
+
+
 # ---------------------------------------------------------------------------
 # layouts of the projections (one-hot probes with closed forms)
 # ---------------------------------------------------------------------------
