@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MLA_GD_ABI_VERSION 2
+#define MLA_GD_ABI_VERSION 3
 
 /* error codes */
 #define MLA_GD_OK 0
@@ -82,6 +82,7 @@ extern "C" {
 #define MLA_GD_CHECK_BLOCK_RANGE 2u    /* a block_table entry outside [0, n_blocks): entry masked */
 #define MLA_GD_CHECK_TABLE_COLUMN 4u   /* position / block_size >= max_blocks_per_seq: entry masked */
 #define MLA_GD_CHECK_SLOT_SHARED 8u    /* two tokens share a slot: both write it, one value survives */
+#define MLA_GD_CHECK_SEQ_RANGE 16u     /* token_seq[t] outside [0, n_tokens): the token's entries masked */
 
 /*
  * Dimensions of the step, fixed when the handle is created.  The page passes
@@ -141,8 +142,9 @@ typedef struct mla_gd_tensors {
   const float* sin_table;      /* [T, dr/2] fp32: sine table of interleaved RoPE */
   void* kv_cache;              /* [n_blocks, 1, block_size, kv_row] bf16, MUTATED IN PLACE:
                                   row slot_mapping[t] is overwritten with token t's row */
-  const int32_t* slot_mapping; /* [T] int32: flat cache row each token's own key is written to */
-  const int32_t* block_table;  /* [T, max_blocks_per_seq] int32: logical-to-physical block map */
+  const int32_t* slot_mapping; /* [T] int32: flat cache row that receives token t's new row */
+  const int32_t* block_table;  /* [n_seqs, max_blocks_per_seq] int32: per sequence, logical block ->
+                                  physical block; n_seqs = T without token_seq */
   const int32_t* positions;    /* [T] int32: this step's absolute position per token */
   const int32_t* gather_indices; /* [T, n_prior] int32: selected absolute prior positions, unsorted */
   void* out;                   /* [T, hidden] bf16, written: this rank's attention-block output
@@ -150,6 +152,10 @@ typedef struct mla_gd_tensors {
   int32_t* gather_rows_out;    /* optional (may be NULL) [T, n_prior] int32, written: the flat cache
                                   row each selected position resolved to, or -1 where the causal
                                   mask removed it */
+  const int32_t* token_seq;    /* optional (may be NULL) [T] int32: the block_table row (sequence) of
+                                  token t, in [0, n_tokens).  NULL: row t, one sequence per token.
+                                  Several tokens of one sequence (multi-token or speculative decode)
+                                  share a row; see mla_gather_decode_step() for what they see. */
 } mla_gd_tensors;
 
 typedef struct mla_gd_handle mla_gd_handle;
@@ -189,9 +195,14 @@ int mla_gather_decode_workspace_init(const mla_gd_handle* handle, void* workspac
  * Enqueue one decode step for n_tokens tokens (1 <= n_tokens <= max_tokens) on
  * `stream` (hipStream_t; NULL = default stream).  Reads every input tensor,
  * writes `out`, row slot_mapping[t] of kv_cache for every token, the optional
- * gather_rows_out, and the workspace.  The row a token writes is visible to
- * the gather of every token in the same step (a token that selects its own
- * position reads this step's row).
+ * gather_rows_out, and the workspace.  Every token's row is written before
+ * any token gathers, so the row a token writes is visible to the gather of
+ * every token in the same step: a token that selects its own position reads
+ * this step's row, and with token_seq a token that selects the position of
+ * an earlier token of its sequence reads the row that token wrote in this
+ * step (later tokens' positions are causally masked).  The result equals
+ * running the tokens of each sequence as successive single-token steps in
+ * position order.  The tokens of one step must have distinct slots.
  */
 int mla_gather_decode_step(mla_gd_handle* handle, const mla_gd_tensors* tensors, int32_t n_tokens,
                            void* workspace, size_t workspace_bytes, void* stream);

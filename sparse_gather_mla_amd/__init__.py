@@ -24,6 +24,7 @@ MLA_GD_FLAG_FUSED = 1
 MLA_GD_FLAG_GRAPH = 2
 MLA_GD_FLAG_DEBUG_CHECKS = 4
 MLA_GD_CHECK_SLOT_RANGE, MLA_GD_CHECK_BLOCK_RANGE, MLA_GD_CHECK_TABLE_COLUMN, MLA_GD_CHECK_SLOT_SHARED = 1, 2, 4, 8
+MLA_GD_CHECK_SEQ_RANGE = 16
 
 
 class MlaGdError(RuntimeError):
@@ -42,7 +43,8 @@ class _Dims(ctypes.Structure):
 
 TENSOR_FIELDS = ("hidden_states", "input_norm_w", "wq_a", "q_norm_w", "wq_b", "wkv_a", "kv_norm_w",
                  "q_absorb_w", "out_absorb_w", "o_proj_w", "cos_table", "sin_table", "kv_cache",
-                 "slot_mapping", "block_table", "positions", "gather_indices", "out", "gather_rows_out")
+                 "slot_mapping", "block_table", "positions", "gather_indices", "out", "gather_rows_out",
+                 "token_seq")
 
 
 class _Tensors(ctypes.Structure):
@@ -264,7 +266,10 @@ class MlaGatherDecode:
             "sin_table": (inp["sin"], f32, (T, dr // 2)),
             "kv_cache": (inp["kv_cache"], bf, (d.n_blocks, 1, d.block_size, kvr)),
             "slot_mapping": (inp["slot_mapping"], i32, (T,)),
-            "block_table": (inp["block_table"], i32, (T, d.max_blocks_per_seq)),
+            # with token_seq the table has one row per sequence of the step (at most T)
+            "block_table": (inp["block_table"], i32,
+                            ((int(inp["block_table"].shape[0]) if inp.get("token_seq") is not None else T),
+                             d.max_blocks_per_seq)),
             "positions": (inp["positions"], i32, (T,)),
             "gather_indices": (inp["gather_indices"], i32, (T, d.n_prior)),
             "out": (out, bf, (T, H)),
@@ -274,6 +279,10 @@ class MlaGatherDecode:
             setattr(tn, name, self._check(name, t, dt, shp))
         if gather_rows_out is not None:
             tn.gather_rows_out = self._check("gather_rows_out", gather_rows_out, i32, (T, d.n_prior))
+        if inp.get("token_seq") is not None:
+            if not 1 <= int(inp["block_table"].shape[0]) <= T:
+                raise ValueError("block_table with token_seq: one row per sequence, at most n_tokens rows")
+            tn.token_seq = self._check("token_seq", inp["token_seq"], i32, (T,))
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         if noalloc:

@@ -737,6 +737,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   for (const void* q : bf) if (!aligned(q, 16)) return MLA_GD_E_ALIGN;
   for (const void* q : w4) if (!aligned(q, 4)) return MLA_GD_E_ALIGN;
   if (tn->gather_rows_out && !aligned(tn->gather_rows_out, 4)) return MLA_GD_E_ALIGN;
+  if (tn->token_seq && !aligned(tn->token_seq, 4)) return MLA_GD_E_ALIGN;
   if (!aligned(workspace, 256)) return MLA_GD_E_ALIGN;
 
   const Plan pl = make_plan(d, n_tokens);
@@ -763,6 +764,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   p.w_o = (const uint16_t*)tn->o_proj_w; p.cos_t = tn->cos_table; p.sin_t = tn->sin_table;
   p.cache = (uint16_t*)tn->kv_cache; p.slot = tn->slot_mapping; p.btab = tn->block_table; p.pos = tn->positions;
   p.gidx = tn->gather_indices; p.out = (uint16_t*)tn->out; p.rows_out = tn->gather_rows_out;
+  p.tseq = tn->token_seq;
   char* ws = (char*)workspace;
   p.zero16 = (const uint16_t*)(ws + pl.off_zero);
   p.rows = (int32_t*)(ws + pl.off_rows);

@@ -49,8 +49,9 @@ __device__ __forceinline__ float inv_rms(float sumsq, int n, float eps) {
 
 // Index build for entry idx = t*P + j: selected position -> flat cache row,
 // -1 where causally masked.  Masked entries touch neither the block table nor
-// the cache.  With the debug checks, an entry whose block-table column or
-// block id is out of range is masked too, and reported.
+// the cache.  Token t resolves through block-table row token_seq[t] (row t
+// without token_seq).  With the debug checks, an entry whose sequence,
+// block-table column or block id is out of range is masked too, and reported.
 __device__ __forceinline__ void index_build(const StepParams& p, int idx) {
   if (idx >= p.pl.T * p.P) return;
   const int t = idx / p.P;
@@ -59,10 +60,13 @@ __device__ __forceinline__ void index_build(const StepParams& p, int idx) {
   int row = -1;
   if (g >= 0 && g <= ps) {
     const int col = g / p.BS;
-    if (p.dbg && col >= p.MB) {
+    const int sq = p.tseq ? p.tseq[t] : t;
+    if (p.dbg && (unsigned)sq >= (unsigned)p.pl.T) {
+      atomicOr(p.err, MLA_GD_CHECK_SEQ_RANGE);
+    } else if (p.dbg && col >= p.MB) {
       atomicOr(p.err, MLA_GD_CHECK_TABLE_COLUMN);
     } else {
-      const int blk = p.btab[(size_t)t * p.MB + col];
+      const int blk = p.btab[(size_t)sq * p.MB + col];
       if (p.dbg && (unsigned)blk >= (unsigned)p.NBLK) atomicOr(p.err, MLA_GD_CHECK_BLOCK_RANGE);
       else row = blk * p.BS + g % p.BS;
     }

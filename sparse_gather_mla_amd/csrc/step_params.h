@@ -77,6 +77,7 @@ struct StepParams {
   const int32_t* gidx;
   uint16_t* out;
   int32_t* rows_out;  // optional
+  const int32_t* tseq;  // optional [T]: block-table row of each token (NULL: row t)
   // workspace views
   const uint16_t* zero16;  // 256 zero bytes (source of padding loads)
   int32_t* rows;    // [T][P] flat cache row or -1

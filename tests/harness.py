@@ -46,9 +46,12 @@ def within_tol(got: np.ndarray, ref: np.ndarray, tol: float = TOL):
 
 
 def token_slice(inp: Dict[str, object], tokens: Iterable[int]) -> Dict[str, object]:
-    """Inputs restricted to some tokens (tokens are independent sequences)."""
+    """Inputs restricted to some tokens.  With token_seq the block table is
+    per sequence and stays whole (the kept tokens index into it)."""
     idx = torch.as_tensor(list(tokens), dtype=torch.long)
-    per_token = ("hidden_states", "cos", "sin", "slot_mapping", "block_table", "positions", "gather_indices")
+    per_token = ("hidden_states", "cos", "sin", "slot_mapping", "positions", "gather_indices", "token_seq")
+    if "token_seq" not in inp:
+        per_token = per_token + ("block_table",)
     out = {}
     for k, v in inp.items():
         if k == "kv_cache":
@@ -86,11 +89,12 @@ def index_build_all(inp_cpu: Dict[str, object], block_size: int) -> np.ndarray:
     pos = inp_cpu["positions"].numpy()
     bt = inp_cpu["block_table"].numpy()
     T, P = gi.shape
+    seq = inp_cpu["token_seq"].numpy() if inp_cpu.get("token_seq") is not None else np.arange(T)
     rows = np.empty((T, P), dtype=np.int64)
     for t in range(T):
         p = int(pos[t])
         for j in range(P):
-            rows[t, j] = oracle.resolve_row(int(gi[t, j]), p, bt[t], block_size)
+            rows[t, j] = oracle.resolve_row(int(gi[t, j]), p, bt[int(seq[t])], block_size)
     return rows
 
 

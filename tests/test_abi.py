@@ -119,6 +119,9 @@ def test_workspace_size_and_step_argument_checks(lib):
         tn.positions = 4096 + 2
         assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 1, ws, sizes[0], None) == c["MLA_GD_E_ALIGN"]
         tn.positions = 4096
+        tn.token_seq = 4096 + 2  # optional, but 4-byte aligned when given
+        assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 1, ws, sizes[0], None) == c["MLA_GD_E_ALIGN"]
+        tn.token_seq = None
         assert lib.mla_gather_decode_step(h, ctypes.byref(tn), 1, ctypes.c_void_p((1 << 20) + 16), sizes[0],
                                           None) == c["MLA_GD_E_ALIGN"]
         assert lib.mla_gather_decode_workspace_init(h, None, 1024, None) == c["MLA_GD_E_INVAL"]
@@ -223,14 +226,15 @@ def test_debug_checks_flag_and_status_arguments(lib):
     assert lib.mla_gather_decode_debug_status(None, ctypes.c_void_p(4096), ctypes.byref(bits), None) == c["MLA_GD_E_INVAL"]
     # distinct check bits
     bits_def = [c[k] for k in ("MLA_GD_CHECK_SLOT_RANGE", "MLA_GD_CHECK_BLOCK_RANGE", "MLA_GD_CHECK_TABLE_COLUMN",
-                               "MLA_GD_CHECK_SLOT_SHARED")]
-    assert sorted(bits_def) == [1, 2, 4, 8]
+                               "MLA_GD_CHECK_SLOT_SHARED", "MLA_GD_CHECK_SEQ_RANGE")]
+    assert sorted(bits_def) == [1, 2, 4, 8, 16]
 
 
 def test_binding_constants_match_the_header():
     c = _codes()
     for k in ("MLA_GD_FLAG_FUSED", "MLA_GD_FLAG_GRAPH", "MLA_GD_FLAG_DEBUG_CHECKS", "MLA_GD_CHECK_SLOT_RANGE",
-              "MLA_GD_CHECK_BLOCK_RANGE", "MLA_GD_CHECK_TABLE_COLUMN", "MLA_GD_CHECK_SLOT_SHARED"):
+              "MLA_GD_CHECK_BLOCK_RANGE", "MLA_GD_CHECK_TABLE_COLUMN", "MLA_GD_CHECK_SLOT_SHARED",
+              "MLA_GD_CHECK_SEQ_RANGE"):
         assert getattr(sgm, k) == c[k], k
 
 

@@ -258,3 +258,21 @@ def test_debug_checks_with_graph_replay():
     with pytest.raises(MlaGdError) as ei:
         mod(g)
     assert ei.value.code == E_DEVICE_CHECK
+
+
+def test_sequence_id_out_of_range_is_masked_and_reported():
+    """Several tokens per sequence (token_seq): a token whose sequence id lies
+    outside [0, n_tokens) has every entry masked (the block table is never
+    read for it) and MLA_GD_CHECK_SEQ_RANGE is reported."""
+    from sparse_gather_mla_amd import MLA_GD_CHECK_SEQ_RANGE
+
+    wl = replace(CONFIGS[0], name="tiny_mt_dbg", shape=replace(CONFIGS[0].shape, n_tokens=6), contexts=None,
+                 context_range=(60, 120), tokens_per_seq=3, seed=3101)
+    sh = wl.shape
+    _say(f"[debug] sequence id out of range, T={sh.n_tokens}")
+    inp = make_inputs(wl, with_pool=False)
+    bad = copy.deepcopy(inp)
+    bad["token_seq"][1] = sh.n_tokens  # past the last allowed row
+    ref, n = _mask_entries(inp, 1, lambda g: True)
+    assert n > 0
+    _check_masked_run("gemv", wl, False, bad, ref, MLA_GD_CHECK_SEQ_RANGE)

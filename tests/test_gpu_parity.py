@@ -95,6 +95,8 @@ def test_parity_full_head_all_tokens(name):
     _run_and_check(wl)
 
 
+TINY_BASE = CONFIGS[0]
+
 # ---------------------------------------------------------------------------
 # a ragged shape: several column tiles with tails, 2 head groups (16 + 4),
 # n_prior not a multiple of the row chunk
@@ -349,3 +351,59 @@ def test_parity_largest_n_prior():
 
 def test_parity_largest_token_count():
     _run_and_check(MAX_TOKENS)
+
+
+# ---------------------------------------------------------------------------
+# several tokens of one sequence in one step (multi-token / speculative
+# decode): tokens of a sequence share its block-table row through token_seq,
+# sit at its last positions, and each selects every other one of them
+# (earlier ones read this step's rows, later ones are masked)
+# ---------------------------------------------------------------------------
+def _mt(base, name, T, k, seed, **shape_kw):
+    return replace(base, name=name, shape=replace(base.shape, n_tokens=T, **shape_kw), contexts=None,
+                   context_range=base.context_range or (60, 120), tokens_per_seq=k, seed=seed)
+
+
+MULTI_TOKEN = [
+    _mt(TINY_BASE, "tiny_mt_T6_k3", 6, 3, 3001),                      # GEMV path
+    _mt(RAGGED, "ragged_mt_T21_k3", 21, 3, 3002),                     # matrix-core path
+    _mt(MANY_HEADS, "heads40_mt_T20_k4", 20, 4, 3003),                # row-split core
+    _mt(next(c for c in CONFIGS if c.name == "batch32"), "batch32_mt_k4", 32, 4, 3004),  # DeepSeek dims
+]
+
+
+@pytest.mark.parametrize("wl", MULTI_TOKEN, ids=[w.name for w in MULTI_TOKEN])
+def test_parity_multi_token_sequences(wl):
+    out, ref, inp, g = _run_and_check(wl)
+    assert int(inp["token_seq"].max()) == wl.shape.n_tokens // wl.tokens_per_seq - 1
+
+
+def test_parity_multi_token_fused_variant():
+    _run_and_check(MULTI_TOKEN[0], fused=True)
+
+
+def test_multi_token_batch_matches_successive_single_token_steps():
+    """The batched step equals the tokens run one by one in position order,
+    each single-token step seeing the rows the earlier ones wrote."""
+    wl = MULTI_TOKEN[0]
+    sh = wl.shape
+    inp = make_inputs(wl, with_pool=False)
+    g = gpu_inputs(wl, inp)
+    pool0 = g["kv_cache"].clone()
+    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens)
+    batched = mod(g).clone()
+    pool_batched = g["kv_cache"].clone()
+    g["kv_cache"].copy_(pool0)
+    seq = inp["token_seq"].long()
+    for t in torch.argsort(inp["positions"], stable=True).tolist():
+        one = token_slice(g, [t])
+        del one["token_seq"]
+        one["block_table"] = g["block_table"][seq[t]:seq[t] + 1].contiguous()
+        one["kv_cache"] = g["kv_cache"]
+        o = mod(one)
+        torch.cuda.synchronize()
+        ok, err, bound = within_tol(bf16_to_f64(o[0]), bf16_to_f64(batched[t]))
+        _say(f"[multi-token] token {t}: successive vs batched max err {err:.3e} bound {bound:.3e}")
+        assert ok
+    ok, err, bound = within_tol(bf16_to_f64(g["kv_cache"]), bf16_to_f64(pool_batched))
+    assert ok

@@ -87,6 +87,10 @@ class Workload:
     n_duplicates: int = 0  # entries that repeat an already selected position
     n_future: int = 0  # entries past the token's position (causally masked)
     description: str = ""
+    # tokens per sequence in the step (speculative / multi-token decode): the
+    # tokens of a sequence sit at its last positions, share its block-table
+    # row (token_seq), and each selects every other one of them
+    tokens_per_seq: int = 1
 
     def with_tokens(self, n_tokens: int) -> "Workload":
         """Same recipe with fewer tokens (used by tests to sample a big shape)."""
@@ -272,17 +276,24 @@ def _contexts(wl: Workload) -> np.ndarray:
     return _rng(wl.seed, "contexts").integers(lo, hi, size=T, endpoint=True)
 
 
-def _gather_indices(wl: Workload, positions: np.ndarray) -> np.ndarray:
+def _gather_indices(wl: Workload, positions: np.ndarray, step_positions=None) -> np.ndarray:
+    """step_positions[t]: positions of the other tokens of t's sequence in this
+    step, each selected once (earlier ones valid, later ones masked)."""
     sh = wl.shape
     P = sh.n_prior
     seq_cap = sh.max_blocks_per_seq * sh.block_size  # positions a block-table row can address
     rng = _rng(wl.seed, "gather_indices")
     out = np.empty((sh.n_tokens, P), dtype=np.int64)
     for t, pos in enumerate(positions.tolist()):
-        n_dist = P - wl.n_duplicates - wl.n_future
+        forced = np.asarray([] if step_positions is None else step_positions[t], dtype=np.int64)
+        n_dist = P - wl.n_duplicates - wl.n_future - len(forced)
+        early = forced[forced <= pos]
         n_avail = pos + 1
-        take = min(n_dist, n_avail)
-        distinct = rng.choice(n_avail, size=take, replace=False)
+        take = min(n_dist, n_avail - len(early))
+        pool = np.setdiff1d(np.arange(n_avail), early) if len(early) else None
+        distinct = (rng.choice(pool, size=take, replace=False) if pool is not None
+                    else rng.choice(n_avail, size=take, replace=False))
+        distinct = np.concatenate([distinct, early]).astype(np.int64)
         n_fut = wl.n_future + (n_dist - take)  # short sequences pad with masked future positions
         dups = rng.choice(distinct, size=wl.n_duplicates, replace=False) if wl.n_duplicates else np.empty(0, np.int64)
         if n_fut:
@@ -290,7 +301,7 @@ def _gather_indices(wl: Workload, positions: np.ndarray) -> np.ndarray:
             fut = rng.integers(pos + 1, seq_cap - 1, size=n_fut, endpoint=True)
         else:
             fut = np.empty(0, np.int64)
-        row = np.concatenate([distinct, dups, fut]).astype(np.int64)
+        row = np.concatenate([distinct, dups, fut, forced[forced > pos]]).astype(np.int64)
         rng.shuffle(row)
         out[t] = row
     return out
@@ -334,10 +345,25 @@ def make_inputs(wl: Workload, device="cpu", with_pool: bool = True,
     assert np.all(positions < MB * bs), "context longer than the block table can address"
     perm = _rng(s, "block_table").permutation(sh.n_blocks).astype(np.int64)
     block_table = perm.reshape(T, MB)
+    k = wl.tokens_per_seq
+    step_positions = None
+    if k > 1:
+        # token j of sequence q = t // k sits k - 1 - j positions before the
+        # end of that sequence's context; the table has one row per sequence
+        assert T % k == 0, "tokens_per_seq must divide n_tokens"
+        seq = np.arange(T) // k
+        positions = ctx[seq * k + k - 1] - 1 - (k - 1 - np.arange(T) % k)
+        assert np.all(positions >= 0)
+        block_table = block_table[: T // k]
+        out["token_seq"] = torch.from_numpy(seq.astype(np.int32))
+        step_positions = [[int(positions[u]) for u in range(q * k, q * k + k) if u != t]
+                          for t, q in enumerate(seq.tolist())]
+    else:
+        seq = np.arange(T)
     # this token's own key lives at logical position `pos` of its sequence:
-    # physical block block_table[t, pos // bs], offset pos % bs in that block
-    slot = block_table[np.arange(T), positions // bs] * bs + positions % bs
-    gi = _gather_indices(wl, positions)
+    # physical block block_table[seq, pos // bs], offset pos % bs in that block
+    slot = block_table[seq, positions // bs] * bs + positions % bs
+    gi = _gather_indices(wl, positions, step_positions)
 
     # rotary tables evaluated at the token's position, theta_i = pos * 10000^(-2i/dr)
     i = np.arange(dr // 2, dtype=np.float64)
