@@ -407,3 +407,61 @@ def test_multi_token_batch_matches_successive_single_token_steps():
         assert ok
     ok, err, bound = within_tol(bf16_to_f64(g["kv_cache"]), bf16_to_f64(pool_batched))
     assert ok
+
+
+# ---------------------------------------------------------------------------
+# A score far above the rest, late in a split: for three tokens one gathered
+# row, past the first 32-row chunk of its split, is replaced by the token's
+# own head-0 query (from the oracle's front-fold) with the other heads' query
+# directions projected out, scaled so that head 0 scores it +100 (log2 units)
+# and every other head about 0.  The core's online softmax must move head 0's
+# reference by about 95 units in mid-split (rescaling what it accumulated).
+# Only one head sees the outsized score: a large |q||k| in many heads would
+# turn the bf16 query tile's rounding into score errors of a tenth of a unit
+# and fail the bar for any bf16-query design, so the case tests the softmax
+# and nothing else.  The oracle reads the same pool.
+# ---------------------------------------------------------------------------
+FAR_SCORE = Workload(
+    name="heads40_far_score",
+    shape=MlaShape(n_tokens=32, hidden=1160, q_lora_rank=600, kv_lora_rank=128, qk_nope_head_dim=24,
+                   qk_rope_head_dim=16, v_head_dim=40, n_heads=40, block_size=16, max_blocks_per_seq=48,
+                   n_prior=512, softmax_scale=0.2, norm_eps=1e-6),
+    seed=4242, context_range=(600, 760), n_duplicates=7, n_future=5,
+)
+
+
+def test_parity_one_far_larger_score_late_in_a_split():
+    wl = FAR_SCORE
+    sh = wl.shape
+    r = sh.kv_lora_rank
+    inp = make_inputs(wl, with_pool=False)
+    g = gpu_inputs(wl, inp)
+    flat = g["kv_cache"].view(-1, sh.kv_row_dim)
+    rows = index_build_all(inp, sh.block_size)
+    o64 = oracle.to_f64_inputs({k: v for k, v in inp.items() if k != "kv_cache"}, block_size=sh.block_size)
+    w = {k: o64[k] for k in ("input_norm_w", "wq_a", "q_norm_w", "wq_b", "wkv_a", "kv_norm_w", "q_absorb_w",
+                             "out_absorb_w", "o_proj_w")}
+    placed = []
+    for t in (0, 5, 31):
+        q_lat, q_pe, _, _ = oracle.front_fold(o64["hidden_states"][t], w, o64["cos"][t], o64["sin"][t], sh.n_heads,
+                                              sh.qk_nope_head_dim, sh.qk_rope_head_dim, r, sh.norm_eps)
+        qall = np.concatenate([q_lat, q_pe], axis=1)
+        basis, _ = np.linalg.qr(qall[1:].T)  # the other heads' query directions
+        d = qall[0] - basis @ (basis.T @ qall[0])
+        # head 0's score (log2 units) = softmax_scale * log2(e) * (q0 . row) = 100
+        row = d * (100.0 / (sh.softmax_scale * 1.4426950408889634 * float(qall[0] @ d)))
+        own = int(inp["slot_mapping"][t])
+        # a position in the second half of a 64-row split; its row is selected nowhere else
+        j = next(j for j in range(96, sh.n_prior) if j % 64 >= 32 and rows[t, j] >= 0 and rows[t, j] != own
+                 and int(np.count_nonzero(rows[t] == rows[t, j])) == 1)
+        flat[int(rows[t, j])] = torch.from_numpy(row).to(torch.bfloat16).cuda()
+        placed.append((t, j, int(rows[t, j])))
+    pool_cpu = g["kv_cache"].cpu()
+    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens)
+    out = mod(g)
+    torch.cuda.synchronize()
+    # the pool copy predates the step: the oracle overlays this step's rows itself
+    ref = oracle_reference(wl, inp, list(range(sh.n_tokens)), pool_cpu=pool_cpu)
+    ok, err, bound = within_tol(bf16_to_f64(out), ref["out"])
+    _say(f"[far score] (token, position, row) {placed}: max err {err:.3e} bound {bound:.3e} err/bound {err / bound:.3f}")
+    assert ok
