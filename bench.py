@@ -76,6 +76,7 @@ def alg_bytes(sh, inp, names) -> dict:
     b.update({"k_absorb": 2 * nh * dn * r, "k_core": 2 * kvr * uniq, "k_oabsorb": 2 * nh * dv * r,
               "k_oproj": 2 * nh * dv * H, "k_out": 2 * T * H})
     b["k_absorb_core"] = b["k_absorb"] + b["k_core"]  # the fused variant's single launch
+    b["k_step"] = sum(b[n] for n in ("k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"))
     b = {n: b.get(n, 0) for n in names}
     b["step"] = sum(b.values())
     return b
@@ -326,11 +327,13 @@ def core_flops(sh, inp) -> int:
 
 
 def measure_config(name: str, steps: int, warmup: int, fused: bool = False, graph: bool = False,
-                   extras: bool = False, cpu_budget: float = 0.0, calibrate_copy: bool = False) -> dict:
-    """Cold steps of one workload: step latency (median, p10, p90, mean), the
-    per-kernel breakdown from start/stop events on each kernel launch, the
-    dominant kernel's roofline, the core's matrix-core utilisation and,
-    with a budget, the oracle's host time."""
+                   extras: bool = False, cpu_budget: float = 0.0, calibrate_copy: bool = False,
+                   single: bool = False, tokens: int = 0) -> dict:
+    """Cold steps of one workload (its first ``tokens`` tokens if given): step
+    latency (median, p10, p90, mean), the per-kernel breakdown from start/stop
+    events on each kernel launch, the dominant kernel's roofline, the core's
+    matrix-core utilisation and, with a budget, the oracle's host time.
+    ``single``: the single-launch variant."""
     import numpy as np
     import torch
 
@@ -338,12 +341,15 @@ def measure_config(name: str, steps: int, warmup: int, fused: bool = False, grap
     from workload import config_by_name, make_inputs, to_device
 
     wl = config_by_name(name)
+    if tokens:
+        wl = wl.with_tokens(tokens)
     sh = wl.shape
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = make_inputs(wl, with_pool=False)  # the pool is filled on the GPU
     g = to_device(wl, inp, device=dev)
-    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens, device=0, fused=fused, graph=graph)
+    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=sh.n_tokens, device=0, fused=fused, graph=graph,
+                          single_launch=single)
     names = mod.kernel_names(sh.n_tokens)
     nk = len(names)
     out = torch.empty((sh.n_tokens, sh.hidden), dtype=torch.bfloat16, device=dev)
@@ -493,6 +499,7 @@ def main() -> int:
     ap.add_argument("--config", default="all",
                     help="one workload, or 'all': ds32_slice as the headline plus the other n_prior=2048 configs")
     ap.add_argument("--fused", action="store_true")
+    ap.add_argument("--single", action="store_true", help="the single-launch variant (whole step, one kernel)")
     ap.add_argument("--graph", action="store_true", help="the library captures the step once and replays it")
     ap.add_argument("--extras", action="store_true", help="also time warm steps and a HIP graph of the step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -520,7 +527,7 @@ def main() -> int:
     print(f"[bench] {head_name}: {args.warmup} + {args.steps} cold steps", file=sys.stderr, flush=True)
     head = measure_config(head_name, args.steps, args.warmup, fused=args.fused, graph=args.graph,
                           extras=args.extras, cpu_budget=budget,
-                          calibrate_copy=args.calibrate_copy and args.config != "all")
+                          calibrate_copy=args.calibrate_copy and args.config != "all", single=args.single)
     res = {
         "metric": METRIC,
         "value": head["us"],
@@ -535,7 +542,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": head["workload"], "n_tokens": head["n_tokens"], "n_heads": head["n_heads"],
-                   "n_prior": 2048, "variant": "fused" if args.fused else "separate",
+                   "n_prior": 2048,
+                   "variant": "fused" if args.fused else ("single launch" if args.single else "separate"),
                    "cache_state": "cold (1 GiB flush per step)",
                    "statistic": "median of the timed steps"},
         "launch": "captured HIP graph, replayed" if args.graph else "kernels launched one by one",
@@ -552,7 +560,7 @@ def main() -> int:
         copy_gbps = copy_bandwidth_gbps()
         res["copy_GBps"] = round(copy_gbps, 1)
         res["pct_of_copy_bandwidth"] = round(100 * head["achieved_GBps"] / copy_gbps, 2)
-        if not args.fused:
+        if not args.fused and not args.single:
             # the ablation of the pages: kv-row write, absorption and core fused in one launch
             print("[bench] ds32_slice fused variant", file=sys.stderr, flush=True)
             fz = measure_config(head_name, args.steps, args.warmup, fused=True)
@@ -561,6 +569,19 @@ def main() -> int:
                                      "fused_stages": {n: v["us"] for n, v in fz["stages"].items()},
                                      "pages_context_us": {"separate": 385.8, "fused": 340.2,
                                                           "hardware": "AWS Neuron, unstated shape"}}
+            # the whole step as one launch, against the separate kernels: ds32_slice
+            # and the batch32 workload cut to 8 tokens (the most the variant takes)
+            sl = {}
+            for name, tok, sep_us in ((head_name, 0, head["us"]), ("batch32", 8, None)):
+                label = name if not tok else f"{name}_T{tok}"
+                if sep_us is None:
+                    print(f"[bench] {label} separate kernels", file=sys.stderr, flush=True)
+                    sep_us = measure_config(name, args.steps, args.warmup, tokens=tok)["us"]
+                print(f"[bench] {label} single launch", file=sys.stderr, flush=True)
+                one = measure_config(name, args.steps, args.warmup, single=True, tokens=tok)
+                sl[label] = {"separate_us": sep_us, "single_launch_us": one["us"],
+                             "single_launch_us_p10_p50_p90": one["us_p10_p50_p90"]}
+            res["single_launch_ablation"] = sl
         res["configs"] = {}
         for name in BENCH_CONFIGS[1:]:
             # the 128-head workloads keep the run short: fewer steps

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MLA_GD_ABI_VERSION 3
+#define MLA_GD_ABI_VERSION 4
 
 /* error codes */
 #define MLA_GD_OK 0
@@ -76,6 +76,21 @@ extern "C" {
  * synchronisation per step, and a step with them cannot be enqueued on a
  * stream under capture (MLA_GD_E_INVAL). */
 #define MLA_GD_FLAG_DEBUG_CHECKS 4u
+/* Single-launch step (ablation): every phase of the step -- the index build
+ * first, then the down-projections, the query up-projection, the absorption
+ * with the kv-row write, the gather core, the output absorption, the
+ * o-projection and the output sum -- runs as workgroups of ONE kernel launch,
+ * in that order of workgroup index.  A workgroup issues its first weight
+ * loads, then waits on device-scope arrival flags in the workspace for the
+ * workgroups whose results it reads (never for a later one, so in-order
+ * dispatch always makes progress); results pass through device-scope
+ * (write-through) stores.  Applies to steps of at most 8 tokens with at most
+ * 16 heads and n_prior <= 131072; other steps run the separate kernels.
+ * Cannot be combined with MLA_GD_FLAG_FUSED (MLA_GD_E_INVAL).  Needs a
+ * workspace zeroed by mla_gather_decode_workspace_init (as every workspace
+ * does); if a wait ever times out (MLA_GD_CHECK_WAIT_TIMEOUT), zero the
+ * workspace again before the next step. */
+#define MLA_GD_FLAG_SINGLE_LAUNCH 8u
 
 /* bits of the debug error word */
 #define MLA_GD_CHECK_SLOT_RANGE 1u     /* slot_mapping[t] outside [0, n_blocks * block_size): row not written */
@@ -83,6 +98,8 @@ extern "C" {
 #define MLA_GD_CHECK_TABLE_COLUMN 4u   /* position / block_size >= max_blocks_per_seq: entry masked */
 #define MLA_GD_CHECK_SLOT_SHARED 8u    /* two tokens share a slot: both write it, one value survives */
 #define MLA_GD_CHECK_SEQ_RANGE 16u     /* token_seq[t] outside [0, n_tokens): the token's entries masked */
+#define MLA_GD_CHECK_WAIT_TIMEOUT 32u  /* fused or single-launch variant: a wait for another workgroup's
+                                          results gave up (set whether or not the debug checks are on) */
 
 /*
  * Dimensions of the step, fixed when the handle is created.  The page passes
@@ -244,11 +261,13 @@ int mla_gather_decode_step_profiled(mla_gd_handle* handle, const mla_gd_tensors*
  *     ignored).  Handles created with MLA_GD_FLAG_DEBUG_CHECKS get
  *     MLA_GD_E_INVAL (their read-back is a synchronising copy).
  *   - The first call on a GPU looks up that GPU's copy of the array
- *     (hipGetSymbolAddress) with the handle's device current; MLA_GD_E_HIP if
- *     that fails.
+ *     (hipGetSymbolAddress) with the handle's device current, and clears the
+ *     array's first 64 KB + 512 bytes (as mla_gather_decode_workspace_init
+ *     would) with a fill kernel on `stream`; MLA_GD_E_HIP if either fails.
  *   - Every call on one GPU, from every handle, shares that GPU's array, and
  *     the array keeps the last step's contents (each step rewrites what it
- *     reads; its first kernel clears the part that must start at zero).  Two
+ *     reads, clears at its start what must start at zero, and leaves the
+ *     single-launch flags ready for the next step of any handle).  Two
  *     steps that may overlap in time on one GPU (different streams, threads
  *     or handles) race on it: serialise them, or give them
  *     mla_gather_decode_step() with separate workspaces.

@@ -23,8 +23,10 @@ LIB_PATH = os.environ.get("MLA_GD_LIBRARY") or os.path.join(_PKG, "libmla_gather
 MLA_GD_FLAG_FUSED = 1
 MLA_GD_FLAG_GRAPH = 2
 MLA_GD_FLAG_DEBUG_CHECKS = 4
+MLA_GD_FLAG_SINGLE_LAUNCH = 8
 MLA_GD_CHECK_SLOT_RANGE, MLA_GD_CHECK_BLOCK_RANGE, MLA_GD_CHECK_TABLE_COLUMN, MLA_GD_CHECK_SLOT_SHARED = 1, 2, 4, 8
 MLA_GD_CHECK_SEQ_RANGE = 16
+MLA_GD_CHECK_WAIT_TIMEOUT = 32
 
 
 class MlaGdError(RuntimeError):
@@ -136,8 +138,10 @@ class MlaGatherDecode:
     """One handle of the C library plus a workspace, for up to ``max_tokens`` tokens."""
 
     def __init__(self, dims: Dims, max_tokens: int, device: int = 0, fused: bool = False,
-                 allocate_workspace: bool = True, graph: bool = False, debug_checks: bool = False):
+                 allocate_workspace: bool = True, graph: bool = False, debug_checks: bool = False,
+                 single_launch: bool = False):
         """``fused``: the fused variant (kv rows, absorption and core in one launch).
+        ``single_launch``: the whole step as one launch (few tokens, at most 16 heads).
         ``graph``: capture the step once into a HIP graph and replay it (default:
         kernels launched one by one).  ``debug_checks``: device-side checks of
         the index data (slot range and sharing, block-table column and block id
@@ -149,6 +153,7 @@ class MlaGatherDecode:
         self.max_tokens = int(max_tokens)
         self.device = torch.device("cuda", device)
         self.fused = fused
+        self.single_launch = single_launch
         self.graph = graph
         cd = _Dims(hidden=dims.hidden, q_lora_rank=dims.q_lora_rank, kv_lora_rank=dims.kv_lora_rank,
                    qk_nope_head_dim=dims.qk_nope_head_dim, qk_rope_head_dim=dims.qk_rope_head_dim,
@@ -156,7 +161,8 @@ class MlaGatherDecode:
                    max_blocks_per_seq=dims.max_blocks_per_seq, n_blocks=dims.n_blocks, n_prior=dims.n_prior,
                    max_tokens=self.max_tokens, softmax_scale=dims.softmax_scale, norm_eps=dims.norm_eps,
                    flags=(MLA_GD_FLAG_FUSED if fused else 0) | (MLA_GD_FLAG_GRAPH if graph else 0)
-                   | (MLA_GD_FLAG_DEBUG_CHECKS if debug_checks else 0))
+                   | (MLA_GD_FLAG_DEBUG_CHECKS if debug_checks else 0)
+                   | (MLA_GD_FLAG_SINGLE_LAUNCH if single_launch else 0))
         h = ctypes.c_void_p()
         rc = self.lib.mla_gather_decode_create(ctypes.byref(cd), int(device), ctypes.byref(h))
         if rc != 0:

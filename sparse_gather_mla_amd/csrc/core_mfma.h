@@ -44,14 +44,21 @@ constexpr int kMaxSplitRows = 4096;  // row ids staged in LDS per core workgroup
 __host__ __device__ constexpr int core_row_pieces(int nt) { return (2 * nt + 8) | 1; }
 __host__ __device__ constexpr int core_buf_bytes(int nt) { return (kCoreChunk * core_row_pieces(nt) * 16 + 1023) / 1024 * 1024; }
 
-// LDS of a core workgroup, carved from one array: ring | row ids | sink |
-// partial score tiles (HG*CS*128 x 16 B) | score bias (kCoreRing x 32 floats).
-__host__ __device__ constexpr int core_ofs_ids(int nt) { return kCoreRing * core_buf_bytes(nt); }
-__host__ __device__ constexpr int core_ofs_sink(int nt) { return core_ofs_ids(nt) + kMaxSplitRows * 4; }
-__host__ __device__ constexpr int core_ofs_sx(int nt) { return core_ofs_sink(nt) + 1024; }
-__host__ __device__ constexpr int core_ofs_bias(int nt, int hg, int cs) { return core_ofs_sx(nt) + hg * cs * 128 * 16; }
-__host__ __device__ constexpr int core_lds_bytes(int nt, int hg, int cs) {
-  return core_ofs_bias(nt, hg, cs) + kCoreRing * kCoreChunk * 4;
+// LDS of a core workgroup, carved from one array: ring (`ring` chunk buffers)
+// | row ids (`maxr`) | sink | partial score tiles (HG*CS*128 x 16 B) | score
+// bias (ring x 32 floats).
+__host__ __device__ constexpr int core_ofs_ids(int nt, int ring = kCoreRing) { return ring * core_buf_bytes(nt); }
+__host__ __device__ constexpr int core_ofs_sink(int nt, int ring = kCoreRing, int maxr = kMaxSplitRows) {
+  return core_ofs_ids(nt, ring) + maxr * 4;
+}
+__host__ __device__ constexpr int core_ofs_sx(int nt, int ring = kCoreRing, int maxr = kMaxSplitRows) {
+  return core_ofs_sink(nt, ring, maxr) + 1024;
+}
+__host__ __device__ constexpr int core_ofs_bias(int nt, int hg, int cs, int ring = kCoreRing, int maxr = kMaxSplitRows) {
+  return core_ofs_sx(nt, ring, maxr) + hg * cs * 128 * 16;
+}
+__host__ __device__ constexpr int core_lds_bytes(int nt, int hg, int cs, int ring = kCoreRing, int maxr = kMaxSplitRows) {
+  return core_ofs_bias(nt, hg, cs, ring, maxr) + ring * kCoreChunk * 4;
 }
 
 // Reductions over the lanes l, l^16, l^32, l^48 (the four row groups of an
@@ -111,29 +118,35 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return sum4groups(v);
 }
 
-// Hooks of the separately launched core: every input is complete at kernel start.
+// Hooks of the separately launched core: every input is complete at kernel
+// start, and the results are read by a later kernel.
 struct CoreNoWait {
   __device__ void before_rows(int) const {}
   __device__ void before_q(int) const {}
+  __device__ __forceinline__ void st(float* p, float v) const { *p = v; }
 };
 
 // Hooks: before_rows(token) runs before the first read of the row ids or the
 // cache; before_q(first head) after the first row loads are issued and before
 // the query tiles are read.  Every thread of the workgroup calls both.
+// st(p, v) stores one of the split's results (m, l, o).
+// RING chunk buffers are in flight (1: each chunk is loaded after the previous
+// one is consumed); MAXR is the most rows a split may hold.
 // NT: latent width / 16.  HG: head groups of 16 per workgroup.  CS: column
 // splits.  The CS waves of a head group each own NT/CS output tiles; they
 // split the score's k-steps between them and add their partial score tiles
 // through LDS (`sx`), so every wave of the group holds the same scores and
 // the same softmax state.  The workgroup has HG*CS waves.  `lds` holds
 // core_lds_bytes(NT, HG, CS) bytes, 16-byte aligned.
-template <int NT, int HG, int CS, class Hooks = CoreNoWait>
+template <int NT, int HG, int CS, class Hooks = CoreNoWait, int RING = kCoreRing, int MAXR = kMaxSplitRows>
 __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, int b, char* lds,
                                                           const Hooks& hooks = Hooks()) {
+  static_assert(RING >= 1 && RING <= 3, "ring depth");
   char* ring = lds;
-  int* ids = reinterpret_cast<int*>(lds + core_ofs_ids(NT));
-  char* sink = lds + core_ofs_sink(NT);
-  f32x4_t* sx = reinterpret_cast<f32x4_t*>(lds + core_ofs_sx(NT));
-  float* bias = reinterpret_cast<float*>(lds + core_ofs_bias(NT, HG, CS));
+  int* ids = reinterpret_cast<int*>(lds + core_ofs_ids(NT, RING));
+  char* sink = lds + core_ofs_sink(NT, RING, MAXR);
+  f32x4_t* sx = reinterpret_cast<f32x4_t*>(lds + core_ofs_sx(NT, RING, MAXR));
+  float* bias = reinterpret_cast<float*>(lds + core_ofs_bias(NT, HG, CS, RING, MAXR));
   constexpr int NW = HG * CS;
   constexpr int NTW = NT / CS;       // output tiles (16 columns) per wave
   constexpr int KSMAX = NT / 2 + 2;  // 32-wide k-steps over kv_row = 16*NT + DR, DR <= 64
@@ -177,7 +190,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   const int kb = cs * KSW;
   const int nj = min(KSW, ks - kb);
 
-  // Direct global->LDS loads of chunk c into ring buffer c % kCoreRing.  Every
+  // Direct global->LDS loads of chunk c into ring buffer c % RING.  Every
   // wave issues exactly NI loads per chunk (slots past the buffer go to the
   // sink) so that the vmcnt arithmetic below is static.  Per-lane geometry,
   // the same for every chunk: the row inside the chunk of the piece this lane
@@ -198,7 +211,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   }
   const unsigned row_bytes = (unsigned)KVR * 2u;
   auto issue_chunk = [&](int c) {
-    const int bsel = c % kCoreRing;
+    const int bsel = c % RING;
     char* buf = ring + bsel * BUF;
     const bool live = c < nchunks;
     const int* cid = ids + min(c, nchunks - 1) * kCoreChunk;
@@ -222,7 +235,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   float m_run = -INFINITY, l_run = 0.f;
 
 #pragma unroll
-  for (int c = 0; c < kCoreRing - 1; ++c) issue_chunk(c);
+  for (int c = 0; c < (RING > 1 ? RING - 1 : 1); ++c) issue_chunk(c);
 
   hooks.before_q(hb * HG * 16);
   // Q fragments: lane l holds Qcat[head][32*kk + 8*g .. +8] (B operand of the score product)
@@ -250,11 +263,20 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   const int rs16 = 16 * rstride;
 
   for (int c = 0; c < nchunks; ++c) {
-    // chunk c's loads are this wave's oldest; the younger chunk may stay in flight
-    wait_vmcnt<NI * (kCoreRing - 2)>();
-    __syncthreads();  // chunk c visible to every wave; buffer (c-1) % ring consumed
-    issue_chunk(c + kCoreRing - 1);
-    const int bsel = c % kCoreRing;
+    if constexpr (RING > 1) {
+      // chunk c's loads are this wave's oldest; the younger chunk may stay in flight
+      wait_vmcnt<NI * (RING - 2)>();
+      __syncthreads();  // chunk c visible to every wave; buffer (c-1) % ring consumed
+      issue_chunk(c + RING - 1);
+    } else {
+      if (c > 0) {  // chunk 0 was issued before the query tiles were read
+        __syncthreads();  // every wave is done with chunk c-1's buffer and bias
+        issue_chunk(c);
+        wait_vmcnt<0>();
+      }
+      __syncthreads();  // chunk c visible to every wave
+    }
+    const int bsel = c % RING;
     const lds_char_t* buf = lring + bsel * BUF;
     // scores: tile A rows 0-15, tile B rows 16-31, fragments loaded two steps ahead
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -373,8 +395,8 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   // this split's partial result; waves of one head group hold identical (m, l)
   const size_t pb = ((size_t)t * pl.nsplit + split) * p.NH;
   if (cs == 0 && g == 0 && head < p.NH) {
-    p.pm[pb + head] = m_run;
-    p.pden[pb + head] = l_run;
+    hooks.st(p.pm + pb + head, m_run);
+    hooks.st(p.pden + pb + head, l_run);
   }
   constexpr int R = 16 * NT;
 #pragma unroll
@@ -382,7 +404,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = hbase + 4 * g + i;
-      if (h < p.NH) p.po[(pb + h) * R + 16 * (cs * NTW + n) + l16] = o[n][i];
+      if (h < p.NH) hooks.st(p.po + (pb + h) * R + 16 * (cs * NTW + n) + l16, o[n][i]);
     }
 }
 

@@ -2,6 +2,7 @@
 #pragma once
 
 #include "device_util.h"
+#include "handoff.h"
 
 namespace mla {
 
@@ -29,9 +30,10 @@ __device__ __forceinline__ void unpack8v(const u32x4 v, float* w) {
 // dst[i] = sum_{s < S} src[s*sstride + (i / w)*tstride + (i % w)] for i < n (floats).
 // Deterministic: part sp of nsp sums s = sp, sp+nsp, ... in order, then the
 // parts are added in order.  dst and scratch (256 floats) are LDS.  Every
-// thread of the workgroup must call it.
+// thread of the workgroup must call it.  `sy` loads the partials (handoff.h).
+template <class Sy = HandoffNone>
 __device__ __forceinline__ void reduce_parts(const float* __restrict__ src, size_t sstride, int S, int n, int w,
-                                             size_t tstride, float* dst, float* scratch) {
+                                             size_t tstride, float* dst, float* scratch, const Sy& sy = Sy()) {
   const int tid = threadIdx.x;
   int nsp = (n > 0) ? kBlock / n : 1;
   nsp = max(1, min(nsp, 16));
@@ -45,8 +47,8 @@ __device__ __forceinline__ void reduce_parts(const float* __restrict__ src, size
     int s = sp;
     for (; s + 7 * nsp < S; s += 8 * nsp)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] += s0[(size_t)(s + u * nsp) * sstride];
-    for (; s < S; s += nsp) a[0] += s0[(size_t)s * sstride];
+      for (int u = 0; u < 8; ++u) a[u] += sy.ld(s0 + (size_t)(s + u * nsp) * sstride);
+    for (; s < S; s += nsp) a[0] += sy.ld(s0 + (size_t)s * sstride);
     out[sp * n + i] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   }
   __syncthreads();
@@ -63,8 +65,9 @@ __device__ __forceinline__ void reduce_parts(const float* __restrict__ src, size
 // As reduce_parts for groups of 4 floats: items are float4 at element offset
 // (i / w4)*tstride + 4*(i % w4); tstride and the source must be 16-byte
 // aligned.  scratch holds 256 float4.
+template <class Sy = HandoffNone>
 __device__ __forceinline__ void reduce_parts4(const float* __restrict__ src, size_t sstride, int S, int n4, int w4,
-                                              size_t tstride, float* dst, float* scratch) {
+                                              size_t tstride, float* dst, float* scratch, const Sy& sy = Sy()) {
   const int tid = threadIdx.x;
   int nsp = (n4 > 0) ? kBlock / n4 : 1;
   nsp = max(1, min(nsp, 16));
@@ -79,12 +82,12 @@ __device__ __forceinline__ void reduce_parts4(const float* __restrict__ src, siz
     for (; s + 3 * nsp < S; s += 4 * nsp) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float4 v = *reinterpret_cast<const float4*>(s0 + (size_t)(s + u * nsp) * sstride);
+        const float4 v = sy.ld4(s0 + (size_t)(s + u * nsp) * sstride);
         a[u].x += v.x; a[u].y += v.y; a[u].z += v.z; a[u].w += v.w;
       }
     }
     for (; s < S; s += nsp) {
-      const float4 v = *reinterpret_cast<const float4*>(s0 + (size_t)s * sstride);
+      const float4 v = sy.ld4(s0 + (size_t)s * sstride);
       a[0].x += v.x; a[0].y += v.y; a[0].z += v.z; a[0].w += v.w;
     }
     out[sp * n4 + i] = make_float4((a[0].x + a[1].x) + (a[2].x + a[3].x), (a[0].y + a[1].y) + (a[2].y + a[3].y),
@@ -146,11 +149,12 @@ __device__ __forceinline__ void gemv_first(const bf16_t* __restrict__ W, int N, 
 //   out[tt*ldo + c0 + c] = sum_{r < ks} xs[tt*xstride + r] * W[(k0 + r)*N + c0 + c],  c < nc <= 512.
 // W is [K, N] row-major bf16 (N and nc multiples of 8), xs is LDS.  `v` holds
 // the loads of gemv_first<UNR>.  Lanes of equal column combine by shuffles,
-// waves through LDS (`red`: 3*NTT*512 floats).
-template <int NTT, int UNR>
+// waves through LDS (`red`: 3*NTT*512 floats).  The output goes out through
+// the hand-off policy `sy` (handoff.h).
+template <int NTT, int UNR, class Sy = HandoffNone>
 __device__ __forceinline__ void gemv_tile(const bf16_t* __restrict__ W, int N, int k0, int ks, int c0, int nc,
                                           const float* xs, int xstride, int nt, float* __restrict__ out,
-                                          size_t ldo, float* red, u32x4* v) {
+                                          size_t ldo, float* red, u32x4* v, const Sy& sy = Sy()) {
   const GemvGeom g = gemv_geom(nc);
   const int wv = threadIdx.x >> 6;
   float acc[NTT][8];
@@ -206,9 +210,9 @@ __device__ __forceinline__ void gemv_tile(const bf16_t* __restrict__ W, int N, i
         for (int i = 0; i < 8; ++i)
           o[i] = acc[tt][i] + red[(0 * NTT + tt) * kTile + 8 * g.cg + i] + red[(1 * NTT + tt) * kTile + 8 * g.cg + i] +
                  red[(2 * NTT + tt) * kTile + 8 * g.cg + i];
-        float4* dst = reinterpret_cast<float4*>(out + (size_t)tt * ldo + c0 + 8 * g.cg);
-        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        float* dst = out + (size_t)tt * ldo + c0 + 8 * g.cg;
+        sy.st4(dst, make_float4(o[0], o[1], o[2], o[3]));
+        sy.st4(dst + 4, make_float4(o[4], o[5], o[6], o[7]));
       }
     }
   }

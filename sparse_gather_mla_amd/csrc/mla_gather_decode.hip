@@ -15,6 +15,7 @@
 #include "../../include/mla_gather_decode.h"
 #include "phases.h"
 #include "phases_mfma.h"
+#include "single_launch.h"
 
 using namespace mla;
 
@@ -25,6 +26,10 @@ using namespace mla;
 template <int NTT>
 __global__ __launch_bounds__(kBlock) void k_down(StepParams p) {
   extern __shared__ float lds[];
+  // the fused variant's counters start each step at zero (this step's later
+  // kernels run after this one; the previous step's have finished)
+  if (p.pl.fused && blockIdx.x == 0 && (int)threadIdx.x < p.NH + 2) p.sync[threadIdx.x * kSyncStride] = 0u;
+  clear_zero_region(p, blockIdx.x);
   phase_down<NTT>(p, blockIdx.x, lds);
 }
 
@@ -51,6 +56,13 @@ template <int NT>
 __global__ __launch_bounds__(512) void k_core_rs(StepParams p) {
   __shared__ __attribute__((aligned(16))) char lds[core_rs_lds_bytes(NT)];
   core_phase_rs<NT>(p, blockIdx.x, lds);
+}
+
+// single-launch variant: the whole step as one launch (single_launch.h)
+template <int NTT, int NT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_step(StepParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[single_lds_bytes<NTT, NT>()];
+  step_single<NTT, NT>(p, blockIdx.x, lds);
 }
 
 // fused variant: kv rows, absorption and core in one launch (phase_absorb_core);
@@ -258,6 +270,7 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   const size_t frag = 2 * kAFragElems * sizeof(uint16_t);  // one (k-step, m-tile): both halves
   pl.off_zero = take(256);
   pl.off_err = take(256);  // debug error word: the same offset for every n_tokens
+  pl.off_flags = take((size_t)kFlagRegionWords * 4);  // the same offset and size in every plan
   pl.off_sync = take((size_t)(NH + 2) * 64);
   pl.off_rows = take((size_t)T * P * sizeof(int32_t));
   pl.off_a1 = take((size_t)pl.kt1 * pl.mt_pad * frag);
@@ -329,6 +342,17 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   }
   if (T > kGemvMaxTokens) return make_plan_mfma(d, pl);
   pl.fused = (d.flags & MLA_GD_FLAG_FUSED) && pl.core_hg == 1 && pl.core_cs == 4;
+  pl.single = (d.flags & MLA_GD_FLAG_SINGLE_LAUNCH) && pl.core_hg == 1 && pl.core_cs == 4;
+  if (pl.single) {
+    // splits of at most kSingleMaxRows rows (the single launch's core stages fewer row ids)
+    const int ns = std::max(pl.nsplit, cdiv(P, kSingleMaxRows));
+    if (ns > 64) {
+      pl.single = 0;
+    } else {
+      pl.ps = cdiv(cdiv(P, ns), kCoreChunk) * kCoreChunk;
+      pl.nsplit = cdiv(P, pl.ps);
+    }
+  }
   pl.nc5 = R / kOabsCols;
   pl.tc5 = std::min(T, kTT);
   pl.nt5c = cdiv(T, pl.tc5);
@@ -339,6 +363,17 @@ Plan make_plan(const mla_gd_dims& d, int T) {
     pl.s6 = cdiv(NH * DV, pl.ks6);
   }
   pl.n7 = T * cdiv(H, kOutCols);
+  if (pl.single) {
+    pl.i_down = pl.n_idx_wg;
+    pl.i_qup = pl.i_down + pl.nt1 * pl.s1;
+    pl.i_abs = pl.i_qup + pl.nt2 * pl.s2 + T * pl.nkv;
+    pl.i_core = pl.i_abs + NH * pl.ncc3 + T;
+    pl.i_oabs = pl.i_core + core_grid(pl);
+    pl.i_oproj = pl.i_oabs + NH * pl.nc5 * pl.nt5c;
+    pl.i_out = pl.i_oproj + pl.nt6 * pl.s6;
+    pl.n_items = pl.i_out + pl.n7;
+    if (pl.n_items > kSingleMaxItems) pl.single = 0;  // then the separate kernels (same split)
+  }
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -349,6 +384,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   const size_t f = sizeof(float);
   pl.off_zero = take(256);
   pl.off_err = take(256);  // debug error word: the same offset for every n_tokens
+  pl.off_flags = take((size_t)kFlagRegionWords * 4);  // the same offset and size in every plan
   pl.off_sync = take((size_t)(NH + 2) * 64);
   pl.off_rows = take((size_t)T * P * sizeof(int32_t));
   pl.off_part1 = take((size_t)pl.s1 * T * (Q + KVR) * f);
@@ -375,7 +411,9 @@ int validate_dims(const mla_gd_dims& d) {
       d.max_blocks_per_seq <= 0 || d.n_blocks <= 0 || d.n_prior <= 0 || d.max_tokens <= 0)
     return MLA_GD_E_INVAL;
   if (d.qk_rope_head_dim % 2 != 0) return MLA_GD_E_INVAL;
-  if ((d.flags & ~(MLA_GD_FLAG_FUSED | MLA_GD_FLAG_GRAPH | MLA_GD_FLAG_DEBUG_CHECKS)) != 0u) return MLA_GD_E_INVAL;
+  if ((d.flags & ~(MLA_GD_FLAG_FUSED | MLA_GD_FLAG_GRAPH | MLA_GD_FLAG_DEBUG_CHECKS | MLA_GD_FLAG_SINGLE_LAUNCH)) != 0u)
+    return MLA_GD_E_INVAL;
+  if ((d.flags & MLA_GD_FLAG_FUSED) && (d.flags & MLA_GD_FLAG_SINGLE_LAUNCH)) return MLA_GD_E_INVAL;
   if (!isfinite(d.softmax_scale) || !isfinite(d.norm_eps) || d.norm_eps < 0.f) return MLA_GD_E_INVAL;
   const long long KVR = (long long)d.kv_lora_rank + d.qk_rope_head_dim;
   const long long N2 = (long long)d.n_heads * (d.qk_nope_head_dim + d.qk_rope_head_dim);
@@ -415,6 +453,25 @@ core_kernel_t pick_fused(int R) {
   }
 }
 
+template <int NTT>
+core_kernel_t pick_step_nt(int R) {
+  switch (R / 16) {
+    case 4: return k_step<NTT, 4>;
+    case 8: return k_step<NTT, 8>;
+    case 16: return k_step<NTT, 16>;
+    default: return k_step<NTT, 32>;
+  }
+}
+
+core_kernel_t pick_step(int ntt, int R) {
+  switch (ntt) {
+    case 1: return pick_step_nt<1>(R);
+    case 2: return pick_step_nt<2>(R);
+    case 4: return pick_step_nt<4>(R);
+    default: return pick_step_nt<8>(R);
+  }
+}
+
 core_kernel_t pick_core(const Plan& pl, int R) {
   if (pl.core_rs) {
     switch (R / 16) {
@@ -436,14 +493,17 @@ constexpr int kNumKernelsMfma = 9;
 constexpr size_t kGemvLdsBytes = kGemvLdsFloats * sizeof(float);
 constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr size_t kErrOffset = 256;  // Plan::off_err in every plan (right after the zero bytes)
+constexpr size_t kFlagsOffset = 512;  // Plan::off_flags in every plan (right after the error word)
 
 int num_kernels(const Plan& pl) {
+  if (pl.single) return 1;
   if (pl.fused) return kNumKernelsGemv - 1;
   if (!pl.mfma) return kNumKernelsGemv;
   return kNumKernelsMfma;
 }
 
 const char* kernel_name(const Plan& pl, int i) {
+  if (pl.single) return "k_step";
   if (pl.fused) return kKernelNamesFused[i];
   if (!pl.mfma) return kKernelNamesGemv[i];
   return kKernelNamesMfma[i];
@@ -632,7 +692,9 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
   const size_t gll = gemv_lds_bytes(ntt);  // GEMV phases passing over ntt tokens
   const dim3 blk(kBlock);
   const dim3 core_blk(64 * pl.core_hg * pl.core_cs);
-  if (pl.fused) {
+  if (pl.single) {
+    L(pick_step(ntt, p.R), dim3(pl.n_items), blk, 0);
+  } else if (pl.fused) {
     L(pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll);
     L(pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll);
     L(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, 0);
@@ -741,6 +803,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   if (!aligned(workspace, 256)) return MLA_GD_E_ALIGN;
 
   const Plan pl = make_plan(d, n_tokens);
+  if (pl.off_err != kErrOffset || pl.off_flags != kFlagsOffset) return MLA_GD_E_INVAL;  // layout invariant
   if (workspace_bytes < pl.total) return MLA_GD_E_WORKSPACE;
   if (d.flags & MLA_GD_FLAG_DEBUG_CHECKS) {
     uint32_t bits = 0;
@@ -781,6 +844,8 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   }
   p.sync = (unsigned*)(ws + pl.off_sync);
   p.err = (unsigned*)(ws + pl.off_err);
+  p.epoch = (unsigned*)(ws + pl.off_flags);
+  p.flags = p.epoch + kFlagHeaderWords;
   p.pl = pl;
 
   hipError_t e = hipSetDevice(h->device);
@@ -849,14 +914,22 @@ constexpr int kMaxScratchDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxScratchDevices] = {};
 
-// This device's copy of `scratch` (the device must be current).
-hipError_t scratch_on_device(int device, void** out) {
+// This device's copy of `scratch` (the device must be current).  At the first
+// lookup on a device, the array's fixed head (zero bytes, error word and the
+// single-launch epoch and flags, the same bytes in every plan) is cleared on
+// `stream` with a fill kernel, as a fresh workspace would be.
+hipError_t scratch_on_device(int device, hipStream_t stream, void** out) {
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[device]) {
     void* ptr = nullptr;
-    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return e;
     if (!ptr) return hipErrorInvalidSymbol;
+    const size_t words = (kFlagsOffset + (size_t)kFlagRegionWords * 4) / 4;
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((words + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream,
+                       (uint32_t*)ptr, words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     g_scratch_ptr[device] = ptr;
   }
   *out = g_scratch_ptr[device];
@@ -875,7 +948,7 @@ int mla_gather_decode_step_noalloc(mla_gd_handle* h, const mla_gd_tensors* tn, i
   if (make_plan(h->d, n_tokens).total > (size_t)MLA_GD_STATIC_SCRATCH_BYTES) return MLA_GD_E_WORKSPACE;
   hipError_t e = hipSetDevice(h->device);
   void* ws = nullptr;
-  if (e == hipSuccess) e = scratch_on_device(h->device, &ws);
+  if (e == hipSuccess) e = scratch_on_device(h->device, (hipStream_t)stream, &ws);
   if (e != hipSuccess) {
     h->last_hip_error = (int)e;
     return MLA_GD_E_HIP;

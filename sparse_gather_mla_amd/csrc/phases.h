@@ -22,6 +22,7 @@
 #include "mfma_util.h"
 #include "device_util.h"
 #include "gemv.h"
+#include "handoff.h"
 #include "step_params.h"
 #include "mla_gather_decode.h"
 
@@ -52,7 +53,8 @@ __device__ __forceinline__ float inv_rms(float sumsq, int n, float eps) {
 // the cache.  Token t resolves through block-table row token_seq[t] (row t
 // without token_seq).  With the debug checks, an entry whose sequence,
 // block-table column or block id is out of range is masked too, and reported.
-__device__ __forceinline__ void index_build(const StepParams& p, int idx) {
+template <class Sy = HandoffNone>
+__device__ __forceinline__ void index_build(const StepParams& p, int idx, const Sy& sy = Sy()) {
   if (idx >= p.pl.T * p.P) return;
   const int t = idx / p.P;
   const int g = p.gidx[idx];
@@ -71,7 +73,7 @@ __device__ __forceinline__ void index_build(const StepParams& p, int idx) {
       else row = blk * p.BS + g % p.BS;
     }
   }
-  p.rows[idx] = row;
+  sy.st(p.rows + idx, row);
   if (p.rows_out) p.rows_out[idx] = row;
 }
 
@@ -105,8 +107,9 @@ __device__ __forceinline__ bool slot_ok(const StepParams& p, int t) {
 // ---------------------------------------------------------------------------
 // Counters of the fused variant.  A producer workgroup publishes its stores
 // with a device-scope release and one atomic increment; a consumer polls with
-// relaxed device-scope loads (bounded: after kSpinLimit polls it raises the
-// error flag and goes on, so no wait can hang) and then fences before reading.
+// relaxed device-scope loads (bounded: after kSpinLimit polls it sets
+// MLA_GD_CHECK_WAIT_TIMEOUT in the error word and goes on, so no wait can
+// hang) and then fences before reading.
 // Producers always have lower workgroup indices than their consumers and never
 // wait themselves, so in-order dispatch guarantees progress.
 // ---------------------------------------------------------------------------
@@ -128,7 +131,7 @@ __device__ __forceinline__ void count_done(unsigned* c) {
 __device__ __forceinline__ void wait_count(const unsigned* c, unsigned target, unsigned* err) {
   for (int it = 0; __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++it) {
     if (it >= kSpinLimit) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      atomicOr(err, MLA_GD_CHECK_WAIT_TIMEOUT);
       break;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -138,15 +141,11 @@ __device__ __forceinline__ void wait_count(const unsigned* c, unsigned target, u
 // ---------------------------------------------------------------------------
 // k_down: index build; (x * g_in) @ [wq_a | wkv_a] split-K partials; sums of x^2
 // ---------------------------------------------------------------------------
-template <int NTT>
-__device__ void phase_down(const StepParams& p, int b, float* lds) {
+template <int NTT, class Sy = HandoffNone>
+__device__ __attribute__((always_inline)) void phase_down(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
   const int T = pl.T;
   const int n_gemv = pl.nt1 * pl.s1;
-  // the fused variant's counters start each step at zero (this step's later
-  // kernels run after this one; the previous step's have finished)
-  if (pl.fused && b == 0 && (int)threadIdx.x < p.NH + 2) p.sync[threadIdx.x * kSyncStride] = 0u;
-  clear_zero_region(p, b);
   if (b >= n_gemv) {
     index_build(p, (b - n_gemv) * kBlock + threadIdx.x);
     return;
@@ -180,11 +179,11 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
         }
 #pragma unroll
       for (int off = 16; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
-      if (tt < nt && rp == 0) p.ssx[(size_t)slab * T + t0 + tt] = s;
+      if (tt < nt && rp == 0) sy.st(p.ssx + (size_t)slab * T + t0 + tt, s);
     }
     __syncthreads();
     float* part = p.part1 + ((size_t)slab * T + t0) * N1 + (is_q ? 0 : p.Q);
-    gemv_tile<NTT, gemv_unroll(NTT)>(W, N, k0, ks, c0, nc, xs, kTile, nt, part, N1, red, v);
+    gemv_tile<NTT, gemv_unroll(NTT)>(W, N, k0, ks, c0, nc, xs, kTile, nt, part, N1, red, v, sy);
   }
 }
 
@@ -193,8 +192,8 @@ __device__ void phase_down(const StepParams& p, int b, float* lds) {
 // workgroups (token t, 64-column slice) reduce the kv row: kvr = alpha * acc_kv
 // and partial sums of squares of its latent columns.
 // ---------------------------------------------------------------------------
-template <int NTT>
-__device__ void phase_qup(const StepParams& p, int b, float* lds) {
+template <int NTT, class Sy = HandoffNone>
+__device__ __attribute__((always_inline)) void phase_qup(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
   const int T = pl.T;
   const int N1 = p.Q + p.KVR;
@@ -207,17 +206,18 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
     const int c0 = sl * kKvSlice, nc = min(kKvSlice, p.KVR - c0);
     float* kv = xs;  // [64]
     float* sx = xs + kKvSlice;
-    reduce_parts4(p.part1 + (size_t)t * N1 + p.Q + c0, (size_t)T * N1, pl.s1, nc / 4, nc / 4, 0, kv, scratch);
-    reduce_parts(p.ssx + t, T, pl.s1, 1, 1, 0, sx, scratch);
+    sy.wait();
+    reduce_parts4(p.part1 + (size_t)t * N1 + p.Q + c0, (size_t)T * N1, pl.s1, nc / 4, nc / 4, 0, kv, scratch, sy);
+    reduce_parts(p.ssx + t, T, pl.s1, 1, 1, 0, sx, scratch, sy);
     const float alpha = inv_rms(sx[0], p.H, p.eps);
     float ss = 0.f;
     for (int c = threadIdx.x; c < nc; c += kBlock) {
       const float y = alpha * kv[c];
-      p.kvr[(size_t)t * p.KVR + c0 + c] = y;
+      sy.st(p.kvr + (size_t)t * p.KVR + c0 + c, y);
       if (c0 + c < p.R) ss = fmaf(y, y, ss);
     }
     ss = block_sum(ss, scratch);
-    if (threadIdx.x == 0) p.kvss[(size_t)t * pl.nkv + sl] = ss;
+    if (threadIdx.x == 0) sy.st(p.kvss + (size_t)t * pl.nkv + sl, ss);
     return;
   }
   const int slab = b / pl.nt2, tile = b % pl.nt2;
@@ -227,8 +227,9 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
     const int nt = min(NTT, T - t0);
     u32x4 v[gemv_unroll(NTT)];
     gemv_first<gemv_unroll(NTT)>(p.wq_b, p.N2, k0, ks, c0, nc, v);
+    sy.wait();
     // acc_a[t][k0 .. k0+ks) reduced over the down-projection's slabs
-    reduce_parts4(p.part1 + (size_t)t0 * N1 + k0, (size_t)T * N1, pl.s1, nt * ks / 4, ks / 4, N1, xs, scratch);
+    reduce_parts4(p.part1 + (size_t)t0 * N1 + k0, (size_t)T * N1, pl.s1, nt * ks / 4, ks / 4, N1, xs, scratch, sy);
     if (tile == 0) {
       const int tt = threadIdx.x >> 5, rp = threadIdx.x & 31;
       float s = 0.f;
@@ -236,12 +237,12 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
         for (int r = rp; r < ks; r += 32) s = fmaf(xs[tt * ks + r], xs[tt * ks + r], s);
 #pragma unroll
       for (int off = 16; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
-      if (tt < nt && rp == 0) p.ssq[(size_t)slab * T + t0 + tt] = s;
+      if (tt < nt && rp == 0) sy.st(p.ssq + (size_t)slab * T + t0 + tt, s);
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) xs[idx] *= p.g_q[k0 + idx % ks];
     __syncthreads();
-    gemv_tile<NTT, gemv_unroll(NTT)>(p.wq_b, p.N2, k0, ks, c0, nc, xs, ks, nt, p.part2 + ((size_t)slab * T + t0) * p.N2, p.N2, red, v);
+    gemv_tile<NTT, gemv_unroll(NTT)>(p.wq_b, p.N2, k0, ks, c0, nc, xs, ks, nt, p.part2 + ((size_t)slab * T + t0) * p.N2, p.N2, red, v, sy);
   }
 }
 
@@ -254,24 +255,27 @@ __device__ void phase_qup(const StepParams& p, int b, float* lds) {
 // `scr` (nt*(s1 + s2) floats of LDS) and adds each token's slabs in order.
 constexpr int kTsPre = 2;
 
-__device__ __forceinline__ float tscale_at(const StepParams& p, int t0, int nt, int q) {
+template <class Sy>
+__device__ __forceinline__ float tscale_at(const StepParams& p, int t0, int nt, int q, const Sy& sy) {
   const int n1 = nt * p.pl.s1;
-  if (q < n1) return p.ssx[(size_t)(q / nt) * p.pl.T + t0 + q % nt];
+  if (q < n1) return sy.ld(p.ssx + (size_t)(q / nt) * p.pl.T + t0 + q % nt);
   q -= n1;
-  return p.ssq[(size_t)(q / nt) * p.pl.T + t0 + q % nt];
+  return sy.ld(p.ssq + (size_t)(q / nt) * p.pl.T + t0 + q % nt);
 }
 
-__device__ __forceinline__ void tscale_load(const StepParams& p, int t0, int nt, float (&v)[kTsPre]) {
+template <class Sy>
+__device__ __forceinline__ void tscale_load(const StepParams& p, int t0, int nt, float (&v)[kTsPre], const Sy& sy) {
   const int nq = nt * (p.pl.s1 + p.pl.s2);
 #pragma unroll
   for (int k = 0; k < kTsPre; ++k) {
     const int q = threadIdx.x + k * kBlock;
-    v[k] = q < nq ? tscale_at(p, t0, nt, q) : 0.f;
+    v[k] = q < nq ? tscale_at(p, t0, nt, q, sy) : 0.f;
   }
 }
 
+template <class Sy>
 __device__ __forceinline__ void tscale_finish(const StepParams& p, int t0, int nt, const float (&v)[kTsPre],
-                                              float* beta, float* scr) {
+                                              float* beta, float* scr, const Sy& sy) {
   const Plan& pl = p.pl;
   const int nq = nt * (pl.s1 + pl.s2);
 #pragma unroll
@@ -279,7 +283,7 @@ __device__ __forceinline__ void tscale_finish(const StepParams& p, int t0, int n
     const int q = threadIdx.x + k * kBlock;
     if (q < nq) scr[q] = v[k];
   }
-  for (int q = threadIdx.x + kTsPre * kBlock; q < nq; q += kBlock) scr[q] = tscale_at(p, t0, nt, q);
+  for (int q = threadIdx.x + kTsPre * kBlock; q < nq; q += kBlock) scr[q] = tscale_at(p, t0, nt, q, sy);
   __syncthreads();
   if ((int)threadIdx.x < nt) {
     const int tt = threadIdx.x;
@@ -305,8 +309,8 @@ __host__ __device__ constexpr int abs_pre(int ntt) { return ntt == 1 ? 2 : 8; }
 // workgroups (one per token) finish the kv branch: kv-latent RMSNorm,
 // interleaved RoPE of the rotary part, bf16 write of the row at slot_mapping[t].
 // ---------------------------------------------------------------------------
-template <int NTT>
-__device__ void phase_absorb(const StepParams& p, int b, float* lds) {
+template <int NTT, class Sy = HandoffNone>
+__device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
   const int T = pl.T;
   float* xs = lds + GemvLds<NTT>::xs;
@@ -316,19 +320,20 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
   if (b >= n_abs) {
     const int t = b - n_abs;
     const float* kv = p.kvr + (size_t)t * p.KVR;
+    sy.wait();
     float ss = 0.f;
-    for (int i = threadIdx.x; i < pl.nkv; i += kBlock) ss += p.kvss[(size_t)t * pl.nkv + i];
+    for (int i = threadIdx.x; i < pl.nkv; i += kBlock) ss += sy.ld(p.kvss + (size_t)t * pl.nkv + i);
     ss = block_sum(ss, scratch);
     const float inv = inv_rms(ss, p.R, p.eps);
     if (!slot_ok(p, t)) return;
     bf16_t* row = p.cache + (size_t)p.slot[t] * p.KVR;
-    for (int c = threadIdx.x; c < p.R; c += kBlock) row[c] = f32_to_bf16(kv[c] * inv * p.g_kv[c]);
+    for (int c = threadIdx.x; c < p.R; c += kBlock) sy.st(row + c, f32_to_bf16(sy.ld(kv + c) * inv * p.g_kv[c]));
     const int half = p.DR / 2;
     for (int i = threadIdx.x; i < half; i += kBlock) {
-      const float x0 = kv[p.R + 2 * i], x1 = kv[p.R + 2 * i + 1];
+      const float x0 = sy.ld(kv + p.R + 2 * i), x1 = sy.ld(kv + p.R + 2 * i + 1);
       const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
-      row[p.R + 2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
-      row[p.R + 2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
+      sy.st(row + p.R + 2 * i, f32_to_bf16(x0 * cs - x1 * sn));
+      sy.st(row + p.R + 2 * i + 1, f32_to_bf16(x0 * sn + x1 * cs));
     }
     return;
   }
@@ -339,12 +344,18 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
   const bf16_t* W = p.w_qabs + (size_t)h * p.DN * p.R;
   for (int t0 = 0; t0 < T; t0 += NTT) {
     const int nt = min(NTT, T - t0);
-    // the small loads go out before the weight stream: the token-scale
-    // partials, then q_nope summed over the wq_b slabs: this thread's item
-    // (token, 4 columns) and slab part sp (s = sp, sp + nsp, ...), its first
-    // kAbsPre terms
+    // the small loads go out before the weight stream (in one launch with
+    // the producers: after it, since they wait for the producers): the
+    // token-scale partials, then q_nope summed over the wq_b slabs: this
+    // thread's item (token, 4 columns) and slab part sp (s = sp, sp + nsp,
+    // ...), its first kAbsPre terms
+    u32x4 v[gemv_unroll(NTT)];
+    if constexpr (Sy::kWeightsFirst) {
+      gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
+      sy.wait();
+    }
     float tsv[kTsPre];
-    tscale_load(p, t0, nt, tsv);
+    tscale_load(p, t0, nt, tsv, sy);
     const int n4 = nt * p.DN / 4, w4 = p.DN / 4;
     const int nsp = max(1, min(16, kBlock / n4));
     const bool one_item = n4 * nsp <= kBlock;
@@ -357,8 +368,7 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
 #pragma unroll
     for (int k = 0; k < kAbsPre; ++k) {
       const int sl = sp + k * nsp;
-      xpre[k] = (has_item && sl < pl.s2) ? *reinterpret_cast<const float4*>(src + (size_t)sl * sstride)
-                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      xpre[k] = (has_item && sl < pl.s2) ? sy.ld4(src + (size_t)sl * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     // the chunk-0 workgroup's q_pe partials: (slab, item) pairs q = s*nr + i,
     // staged in the reduction area after the GEMV and added in slab order
@@ -369,7 +379,7 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
     const float* rsrc = p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH + p.DN;
     auto rope_at = [&](int q) {
       const int sl = q / nr, i = q % nr;
-      return rsrc[((size_t)sl * T + i / p.DR) * p.N2 + i % p.DR];
+      return sy.ld(rsrc + ((size_t)sl * T + i / p.DR) * p.N2 + i % p.DR);
     };
     float rp[kRopePre];
 #pragma unroll
@@ -377,9 +387,8 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
       const int q = threadIdx.x + k * kBlock;
       rp[k] = (rope_lds && q < nrs) ? rope_at(q) : 0.f;
     }
-    u32x4 v[gemv_unroll(NTT)];
-    gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
-    tscale_finish(p, t0, nt, tsv, beta, red);  // `red` is free until the GEMV
+    if constexpr (!Sy::kWeightsFirst) gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
+    tscale_finish(p, t0, nt, tsv, beta, red, sy);  // `red` is free until the GEMV
     if (one_item) {
       float4* out = reinterpret_cast<float4*>(nsp == 1 ? xs : scratch);
       if (has_item) {
@@ -389,7 +398,7 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
           a.x += xpre[k].x; a.y += xpre[k].y; a.z += xpre[k].z; a.w += xpre[k].w;  // zeros past the last slab
         }
         for (int sl = sp + kAbsPre * nsp; sl < pl.s2; sl += nsp) {
-          const float4 x = *reinterpret_cast<const float4*>(src + (size_t)sl * sstride);
+          const float4 x = sy.ld4(src + (size_t)sl * sstride);
           a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
         }
         out[sp * n4 + item] = a;
@@ -408,14 +417,14 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
       }
     } else {
       reduce_parts4(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH, (size_t)T * p.N2, pl.s2, nt * p.DN / 4,
-                    p.DN / 4, p.N2, xs, scratch);
+                    p.DN / 4, p.N2, xs, scratch, sy);
     }
     for (int idx = threadIdx.x; idx < nt * p.DN; idx += kBlock) xs[idx] *= beta[idx / p.DN];
     __syncthreads();
     gemv_tile<NTT, gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, xs, p.DN, nt, qo - c0, 64, red, v);
     for (int idx = threadIdx.x; idx < nt * 64; idx += kBlock) {
       const int tt = idx / 64, c = idx % 64;
-      p.qcat[((size_t)(t0 + tt) * p.NH + h) * p.KVR + c0 + c] = f32_to_bf16(qo[tt * 64 + c] * p.scale_log2);
+      sy.st(p.qcat + ((size_t)(t0 + tt) * p.NH + h) * p.KVR + c0 + c, f32_to_bf16(qo[tt * 64 + c] * p.scale_log2));
     }
     if (cc == 0) {
       if (rope_lds) {
@@ -434,7 +443,7 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
         __syncthreads();
       } else {
         reduce_parts(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH + p.DN, (size_t)T * p.N2, pl.s2, nt * p.DR,
-                     p.DR, p.N2, xs, scratch);
+                     p.DR, p.N2, xs, scratch, sy);
       }
       const int half = p.DR / 2;
       for (int idx = threadIdx.x; idx < nt * half; idx += kBlock) {
@@ -444,8 +453,8 @@ __device__ void phase_absorb(const StepParams& p, int b, float* lds) {
         const float x0 = bq * xs[tt * p.DR + 2 * i], x1 = bq * xs[tt * p.DR + 2 * i + 1];
         const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
         bf16_t* q = p.qcat + ((size_t)t * p.NH + h) * p.KVR + p.R;
-        q[2 * i] = f32_to_bf16(x0 * cs - x1 * sn);
-        q[2 * i + 1] = f32_to_bf16(x0 * sn + x1 * cs);
+        sy.st(q + 2 * i, f32_to_bf16(x0 * cs - x1 * sn));
+        sy.st(q + 2 * i + 1, f32_to_bf16(x0 * sn + x1 * cs));
       }
     }
     __syncthreads();
@@ -480,6 +489,8 @@ struct CoreWaitFused {
     }
     __syncthreads();
   }
+  // results are read by the next kernel
+  __device__ __forceinline__ void st(float* q, float v) const { *q = v; }
 };
 
 template <int NT, int HG, int CS>
@@ -514,7 +525,8 @@ constexpr int kOabsPieces = 4;   // 16-byte weight pieces per lane per pass: 128
 constexpr int kMaxOabsChunks = 8;  // kv_lora_rank <= 512
 constexpr int kOabsPre = 8;  // split partials per thread loaded ahead of the split weights
 
-__device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
+template <class Sy = HandoffNone>
+__device__ __attribute__((always_inline)) void phase_oabsorb(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
   const int T = pl.T, NSP = pl.nsplit, R = p.R, DV = p.DV;
   const int per_h = pl.nc5 * pl.nt5c;
@@ -535,6 +547,7 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
   };
   u32x4 wr[kOabsPieces];
   load_pass(0, wr);
+  sy.wait();
   float* pmL = lds;                  // [tc5][NSP]: split weights
   float* linv = pmL + pl.tc5 * NSP;  // [tc5]
   float* ol = lds + kOabsOl;            // [tc5][64]
@@ -633,7 +646,7 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
         a += __shfl_xor(a, 1, kWave);
         a += __shfl_xor(a, 2, kWave);
         a += __shfl_xor(a, 4, kWave);
-        if (pc == 0 && d < DV) ovp[(size_t)(t0 + tt) * p.NH * DV + (size_t)h * DV + d] = a;
+        if (pc == 0 && d < DV) sy.st(ovp + (size_t)(t0 + tt) * p.NH * DV + (size_t)h * DV + d, a);
       }
     }
   }
@@ -642,8 +655,8 @@ __device__ void phase_oabsorb(const StepParams& p, int b, float* lds) {
 // ---------------------------------------------------------------------------
 // k_oproj: o_v @ o_proj_w split-K partials (this rank's partial output)
 // ---------------------------------------------------------------------------
-template <int NTT>
-__device__ void phase_oproj(const StepParams& p, int b, float* lds) {
+template <int NTT, class Sy = HandoffNone>
+__device__ __attribute__((always_inline)) void phase_oproj(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
   const int T = pl.T;
   const int K = p.NH * p.DV;
@@ -656,13 +669,14 @@ __device__ void phase_oproj(const StepParams& p, int b, float* lds) {
     const int nt = min(NTT, T - t0);
     u32x4 v[gemv_unroll(NTT)];
     gemv_first<gemv_unroll(NTT)>(p.w_o, p.H, k0, ks, c0, nc, v);
+    sy.wait();
     // o_v = the output absorption's column-chunk shares, added in chunk order
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) {
       const int tt = idx / ks, r = idx % ks;
       const float* src = p.ov + (size_t)(t0 + tt) * K + k0 + r;
       float v[kMaxOabsChunks];
 #pragma unroll
-      for (int c = 0; c < kMaxOabsChunks; ++c) v[c] = c < pl.nc5 ? src[(size_t)c * T * K] : 0.f;
+      for (int c = 0; c < kMaxOabsChunks; ++c) v[c] = c < pl.nc5 ? sy.ld(src + (size_t)c * T * K) : 0.f;
       float a = v[0];
 #pragma unroll
       for (int c = 1; c < kMaxOabsChunks; ++c)
@@ -670,7 +684,7 @@ __device__ void phase_oproj(const StepParams& p, int b, float* lds) {
       xs[tt * kTile + r] = a;
     }
     __syncthreads();
-    gemv_tile<NTT, gemv_unroll(NTT)>(p.w_o, p.H, k0, ks, c0, nc, xs, kTile, nt, p.part6 + ((size_t)slab * T + t0) * p.H, p.H, red, v);
+    gemv_tile<NTT, gemv_unroll(NTT)>(p.w_o, p.H, k0, ks, c0, nc, xs, kTile, nt, p.part6 + ((size_t)slab * T + t0) * p.H, p.H, red, v, sy);
   }
 }
 
@@ -682,8 +696,10 @@ __device__ void phase_oproj(const StepParams& p, int b, float* lds) {
 // ---------------------------------------------------------------------------
 constexpr int kOutCols = kBlock;  // columns per k_out workgroup: kBlock/4 groups of four columns
 
-__device__ void phase_out(const StepParams& p, int b, float*) {
+template <class Sy = HandoffNone>
+__device__ __attribute__((always_inline)) void phase_out(const StepParams& p, int b, float*, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
+  sy.wait();
   const int ncg = (p.H + kOutCols - 1) / kOutCols;
   const int t = b / ncg;
   const int part = threadIdx.x & 3;
@@ -698,7 +714,7 @@ __device__ void phase_out(const StepParams& p, int b, float*) {
   for (int s = part; s < S; s += 32) {
     float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)min(s + 4 * u, S - 1) * stride);
+    for (int u = 0; u < 8; ++u) v[u] = sy.ld4(src + (size_t)min(s + 4 * u, S - 1) * stride);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (s + 4 * u < S) {

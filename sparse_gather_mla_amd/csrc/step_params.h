@@ -30,6 +30,13 @@ struct Plan {
   int n7;
   // fused variant: one launch for the kv-row write, the absorption and the core
   int fused;
+  // single-launch variant: the whole step as one launch; item (workgroup)
+  // ranges of its phases: index build [0, i_down), down-projections [i_down,
+  // i_qup), up-projection [i_qup, i_abs), absorption [i_abs, i_core), core
+  // [i_core, i_oabs), output absorption [i_oabs, i_oproj), o-projection
+  // [i_oproj, i_out), output sum [i_out, n_items)
+  int single;
+  int i_down, i_qup, i_abs, i_core, i_oabs, i_oproj, i_out, n_items;
   // Matrix-core path (more than a few tokens).  Token blocks of mtb m-tiles
   // (16 tokens each), ntb blocks, m-tiles padded to mt_pad = ntb*mtb.  For each
   // projection: kt* k-steps of 32 in all, ks* per slab, column tiles of
@@ -47,6 +54,7 @@ struct Plan {
   size_t off_pm, off_pl, off_po, off_ov, off_part6;
   size_t off_a1, off_a2, off_a5;
   size_t off_sync;  // fused variant's counters (same offset for every n_tokens)
+  size_t off_flags;  // single-launch epoch and arrival flags (the same offset and size in every plan)
   size_t total;
 };
 
@@ -101,6 +109,11 @@ struct StepParams {
   // [1] error flag (a wait timed out), [2 + h] absorption tiles of head h done
   unsigned* sync;
   unsigned* err;  // debug error word (MLA_GD_CHECK_* bits)
+  // single-launch variant: epoch[0] = the last completed step's number,
+  // epoch[16] = output workgroups done in this step; flags[item] = the step
+  // number that item last completed
+  unsigned* epoch;
+  unsigned* flags;
   Plan pl;
 };
 

@@ -68,7 +68,8 @@ def _create(lib, d):
     ({"hidden": 0}, "MLA_GD_E_INVAL"),
     ({"n_prior": -1}, "MLA_GD_E_INVAL"),
     ({"qk_rope_head_dim": 15}, "MLA_GD_E_INVAL"),
-    ({"flags": 8}, "MLA_GD_E_INVAL"),
+    ({"flags": 16}, "MLA_GD_E_INVAL"),
+    ({"flags": 1 | 8}, "MLA_GD_E_INVAL"),  # fused and single launch together
     ({"norm_eps": -1.0}, "MLA_GD_E_INVAL"),
     ({"softmax_scale": float("nan")}, "MLA_GD_E_INVAL"),
     ({"hidden": 260}, "MLA_GD_E_UNSUPPORTED"),
@@ -203,6 +204,34 @@ def test_fused_flag_kernel_list(lib):
         assert "k_core" in names(h, 1) and "k_absorb_core" not in names(h, 1)
     finally:
         lib.mla_gather_decode_destroy(h)
+
+
+def test_single_launch_flag_kernel_list(lib):
+    """The single-launch variant runs the whole step as one kernel on the GEMV
+    path (up to 8 tokens, up to 16 heads); larger steps, more heads or more
+    prior positions than its splits hold keep the separate kernels."""
+    c = _codes()
+
+    def names(h, T):
+        n = lib.mla_gather_decode_kernel_count(h, T)
+        return [lib.mla_gather_decode_kernel_name(h, T, i).decode() for i in range(n)]
+
+    rc, h = _create(lib, _dims(max_tokens=12, flags=c["MLA_GD_FLAG_SINGLE_LAUNCH"]))
+    assert rc == 0
+    try:
+        assert names(h, 1) == ["k_step"] and names(h, 8) == ["k_step"]
+        assert names(h, 9)[0] == "k_prep" and "k_step" not in names(h, 9)
+        sizes = [lib.mla_gather_decode_workspace_size(h, t) for t in range(1, 13)]
+        assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+    finally:
+        lib.mla_gather_decode_destroy(h)
+    for kw in ({"n_heads": 20}, {"n_prior": 64 * 2048 + 32, "max_blocks_per_seq": 8300, "n_blocks": 16600}):
+        rc, h = _create(lib, _dims(flags=c["MLA_GD_FLAG_SINGLE_LAUNCH"], **kw))
+        assert rc == 0, kw
+        try:
+            assert names(h, 1)[0] == "k_down", kw
+        finally:
+            lib.mla_gather_decode_destroy(h)
 
 
 def test_debug_checks_flag_and_status_arguments(lib):

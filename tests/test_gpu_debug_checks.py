@@ -1,5 +1,6 @@
 """Device-side checks of the caller's index data (MLA_GD_FLAG_DEBUG_CHECKS),
-through the C ABI, on the GEMV path, the matrix-core path and the fused variant.
+through the C ABI, on the GEMV path, the matrix-core path, the fused variant
+and the single-launch variant.
 
 Valid inputs give the same bits as a handle without the checks.  A block-table
 column or block id out of range masks that entry (the index build and the
@@ -26,8 +27,9 @@ pytestmark = pytest.mark.gpu
 TINY = CONFIGS[0]
 TINY24 = replace(CONFIGS[0], name="tiny_T24", shape=replace(CONFIGS[0].shape, n_tokens=24),
                  contexts=None, context_range=(40, 120), seed=1024)
-# path -> (workload, fused)
-PATHS = {"gemv": (TINY, False), "mfma": (TINY24, False), "fused": (TINY, True)}
+# path -> (workload, handle options)
+PATHS = {"gemv": (TINY, {}), "mfma": (TINY24, {}), "fused": (TINY, {"fused": True}),
+         "single": (TINY, {"single_launch": True})}
 E_DEVICE_CHECK = 6
 
 
@@ -36,10 +38,10 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _handles(wl, fused):
+def _handles(wl, opts):
     dims, T = Dims.from_shape(wl.shape), wl.shape.n_tokens
-    return (MlaGatherDecode(dims, max_tokens=T, fused=fused, debug_checks=True),
-            MlaGatherDecode(dims, max_tokens=T, fused=fused))
+    return (MlaGatherDecode(dims, max_tokens=T, debug_checks=True, **opts),
+            MlaGatherDecode(dims, max_tokens=T, **opts))
 
 
 def _rows_buf(sh):
@@ -60,11 +62,11 @@ def _mask_entries(inp, t, pred):
     return ref, n
 
 
-def _check_masked_run(path, wl, fused, bad, ref, bit):
+def _check_masked_run(path, wl, opts, bad, ref, bit):
     """Run `bad` with the checks; it must index, and compute, as `ref` (the
     offending entries masked), report `bit`, and make the next step fail."""
     sh = wl.shape
-    dbg, _ = _handles(wl, fused)
+    dbg, _ = _handles(wl, opts)
     g_bad = gpu_inputs(wl, bad)
     rows = _rows_buf(sh)
     out = dbg(g_bad, gather_rows_out=rows).clone()
@@ -89,12 +91,12 @@ def _check_masked_run(path, wl, fused, bad, ref, bit):
 
 @pytest.mark.parametrize("path", list(PATHS))
 def test_valid_inputs_same_bits_without_error(path):
-    wl, fused = PATHS[path]
+    wl, opts = PATHS[path]
     sh = wl.shape
     _say(f"[debug] valid inputs, {path} T={sh.n_tokens}")
     inp = make_inputs(wl, with_pool=False)
     g = gpu_inputs(wl, inp)
-    dbg, plain = _handles(wl, fused)
+    dbg, plain = _handles(wl, opts)
     pool0 = g["kv_cache"].clone()
     rows_d, rows_p = _rows_buf(sh), _rows_buf(sh)
     out_d = dbg(g, gather_rows_out=rows_d).clone()
@@ -112,7 +114,7 @@ def test_valid_inputs_same_bits_without_error(path):
 
 @pytest.mark.parametrize("path", list(PATHS))
 def test_block_id_out_of_range_is_masked_and_reported(path):
-    wl, fused = PATHS[path]
+    wl, opts = PATHS[path]
     sh = wl.shape
     bs = sh.block_size
     _say(f"[debug] block id out of range, {path} T={sh.n_tokens}")
@@ -131,14 +133,14 @@ def test_block_id_out_of_range_is_masked_and_reported(path):
     ref, n_t = _mask_entries(ref, t, lambda g: g // bs == col_t)
     assert n_t > 0
     bad["block_table"][t, col_t] = -2
-    _check_masked_run(path, wl, fused, bad, ref, MLA_GD_CHECK_BLOCK_RANGE)
+    _check_masked_run(path, wl, opts, bad, ref, MLA_GD_CHECK_BLOCK_RANGE)
 
 
 @pytest.mark.parametrize("path", list(PATHS))
 def test_block_table_column_out_of_range_is_masked_and_reported(path):
     """A position past the table (position // block_size >= max_blocks_per_seq)
     that passes the causal mask."""
-    wl, fused = PATHS[path]
+    wl, opts = PATHS[path]
     sh = wl.shape
     span = sh.max_blocks_per_seq * sh.block_size
     _say(f"[debug] table column out of range, {path} T={sh.n_tokens}")
@@ -153,19 +155,19 @@ def test_block_table_column_out_of_range_is_masked_and_reported(path):
     gi[0, 7] = span + 5  # the token's own position
     ref, n = _mask_entries(bad, 0, lambda g: g >= span)
     assert n == 2
-    _check_masked_run(path, wl, fused, bad, ref, MLA_GD_CHECK_TABLE_COLUMN)
+    _check_masked_run(path, wl, opts, bad, ref, MLA_GD_CHECK_TABLE_COLUMN)
 
 
 @pytest.mark.parametrize("path", list(PATHS))
 def test_slot_out_of_range_leaves_the_pool_unwritten(path):
-    wl, fused = PATHS[path]
+    wl, opts = PATHS[path]
     sh = wl.shape
     kvr, T = sh.kv_row_dim, sh.n_tokens
     bad_t = T - 1
     _say(f"[debug] slot out of range, {path} T={T}")
     inp = make_inputs(wl, with_pool=False)
     g = gpu_inputs(wl, inp)
-    dbg, plain = _handles(wl, fused)
+    dbg, plain = _handles(wl, opts)
     pool0 = g["kv_cache"].clone()
     g_bad = dict(g)
     g_bad["slot_mapping"] = g["slot_mapping"].clone()
@@ -195,13 +197,13 @@ def test_slot_out_of_range_leaves_the_pool_unwritten(path):
 
 @pytest.mark.parametrize("path", list(PATHS))
 def test_shared_slot_is_reported(path):
-    wl, fused = PATHS[path]
+    wl, opts = PATHS[path]
     sh = wl.shape
     kvr = sh.kv_row_dim
     _say(f"[debug] shared slot, {path} T={sh.n_tokens}")
     inp = make_inputs(wl, with_pool=False)
     g = gpu_inputs(wl, inp)
-    dbg, plain = _handles(wl, fused)
+    dbg, plain = _handles(wl, opts)
     pool0 = g["kv_cache"].clone()
     s0, s1 = int(g["slot_mapping"][0]), int(g["slot_mapping"][1])
     g_sh = dict(g)

@@ -27,10 +27,16 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run_and_check(wl: Workload, tokens=None, fused=False, mutate=None, pool_check_rows=64):
+def _err_word(mod, ws=None):
+    """The workspace's error word (MLA_GD_CHECK_* bits; right after the 256 zero bytes)."""
+    ws = mod.workspace if ws is None else ws
+    return int(ws.view(torch.int32)[256 // 4].item())
+
+
+def _run_and_check(wl: Workload, tokens=None, fused=False, mutate=None, pool_check_rows=64, single=False):
     sh = wl.shape
     T, P, kvr = sh.n_tokens, sh.n_prior, sh.kv_row_dim
-    _say(f"[parity] {wl.name} T={T} nh={sh.n_heads} P={P} fused={fused}")
+    _say(f"[parity] {wl.name} T={T} nh={sh.n_heads} P={P} fused={fused} single={single}")
     inp = make_inputs(wl, with_pool=False)
     if mutate is not None:
         mutate(inp)
@@ -41,11 +47,14 @@ def _run_and_check(wl: Workload, tokens=None, fused=False, mutate=None, pool_che
     probe = np.random.default_rng(0).integers(0, flat.shape[0], size=pool_check_rows)
     assert torch.equal(flat[torch.from_numpy(probe).cuda()].cpu(), pool_rows(wl, probe))
     before = pool.clone()
-    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=T, fused=fused)
+    mod = MlaGatherDecode(Dims.from_shape(sh), max_tokens=T, fused=fused, single_launch=single)
+    if single:
+        assert mod.kernel_names(T) == ["k_step"]
     rows = torch.full((T, P), -7, dtype=torch.int32, device="cuda")
     out = mod(g, gather_rows_out=rows)
     torch.cuda.synchronize()
     _say(f"[parity] {wl.name} step done")
+    assert _err_word(mod) == 0  # no wait of the fused or single-launch variant timed out
 
     # index build: bit-exact for every token
     ref_rows = index_build_all(inp, sh.block_size)
@@ -168,12 +177,6 @@ def test_parity_output_absorption_parts():
 # ---------------------------------------------------------------------------
 # the fused variant: kv rows, absorption and core in one launch (<= 16 heads, <= 8 tokens)
 # ---------------------------------------------------------------------------
-def _fused_error_word(mod):
-    # the fused counters sit right after the workspace's first 256 bytes, 64 bytes apart;
-    # the second one is the error flag a timed-out wait raises
-    return int(mod.workspace.view(torch.int32)[(256 + 64) // 4].item())
-
-
 @pytest.mark.parametrize("name", ["tiny", "ds32_slice"])
 def test_parity_fused_variant(name):
     wl = next(w for w in CONFIGS if w.name == name)
@@ -201,7 +204,7 @@ def test_fused_variant_counters_and_repeat():
     outs = [mod(g).clone() for _ in range(3)]
     ref = sep(g).clone()
     torch.cuda.synchronize()
-    assert _fused_error_word(mod) == 0
+    assert _err_word(mod) == 0
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
     ok, err, bound = within_tol(bf16_to_f64(outs[0]), bf16_to_f64(ref))
     assert ok, (err, bound)
@@ -465,3 +468,83 @@ def test_parity_one_far_larger_score_late_in_a_split():
     ok, err, bound = within_tol(bf16_to_f64(out), ref["out"])
     _say(f"[far score] (token, position, row) {placed}: max err {err:.3e} bound {bound:.3e} err/bound {err / bound:.3f}")
     assert ok
+
+
+# ---------------------------------------------------------------------------
+# the single-launch variant: the whole step as one kernel (<= 8 tokens,
+# <= 16 heads).  Its arithmetic is the separate kernels' (the same splits and
+# reduction orders), so besides the oracle bar it must give the same bits.
+# ---------------------------------------------------------------------------
+_BATCH32 = next(c for c in CONFIGS if c.name == "batch32")
+RAGGED13 = replace(RAGGED, name="ragged_nh13", shape=replace(RAGGED.shape, n_heads=13), seed=4401)
+SINGLE_CASES = [
+    TINY_BASE,
+    next(c for c in CONFIGS if c.name == "ds32_slice"),
+    replace(_BATCH32.with_tokens(8), name="batch32_T8"),
+    RAGGED13,                                                                              # 5 tokens: an 8-token pass
+    replace(RAGGED13, name="ragged_nh13_T2", shape=replace(RAGGED13.shape, n_tokens=2), seed=4402),
+    MULTI_TOKEN[0],                                                                        # 2 sequences x 3 tokens
+]
+
+
+@pytest.mark.parametrize("wl", SINGLE_CASES, ids=[w.name for w in SINGLE_CASES])
+def test_parity_single_launch(wl):
+    out, ref, inp, g = _run_and_check(wl, single=True)
+    # the separate kernels on the same inputs (the step rewrites the same rows
+    # with the same values) give the same bits
+    sep = MlaGatherDecode(Dims.from_shape(wl.shape), max_tokens=wl.shape.n_tokens)
+    assert sep.kernel_names(wl.shape.n_tokens)[0] == "k_down"
+    out_sep = sep(g)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_sep)
+
+
+def test_single_launch_self_row_and_all_masked():
+    """A token that selects its own position must see this step's row: the
+    single launch's core waits for every kv-row workgroup before it reads a row id."""
+    out, ref, inp, g = _run_and_check(TINY, single=True, mutate=_self_row_and_all_masked)
+    assert torch.count_nonzero(out[1]).item() == 0
+
+
+def test_single_launch_repeated_steps_of_varying_size():
+    """One handle and workspace run steps of 8, 3, 1, 8 and 1 tokens in a row:
+    flags of an earlier (larger) step never satisfy a later step's waits (the
+    epoch advances every step), each step gives the separate kernels' bits, and
+    no wait times out."""
+    wl = _BATCH32.with_tokens(8)
+    sh = wl.shape
+    inp = make_inputs(wl, with_pool=False)
+    g = gpu_inputs(wl, inp)
+    single = MlaGatherDecode(Dims.from_shape(sh), max_tokens=8, single_launch=True)
+    sep = MlaGatherDecode(Dims.from_shape(sh), max_tokens=8)
+    for T in (8, 3, 1, 8, 1):
+        sub = token_slice(g, list(range(T)))
+        sub["kv_cache"] = g["kv_cache"]
+        a = single(sub).clone()
+        b = sep(sub).clone()
+        torch.cuda.synchronize()
+        _say(f"[single] steps of {T} tokens: equal {torch.equal(a, b)}")
+        assert torch.equal(a, b)
+    assert _err_word(single) == 0
+
+
+def test_single_launch_noalloc_and_graph_replay():
+    """The single launch through the allocation-free entry point (the static
+    device array) and replayed from a captured graph, three times each: the
+    same bits as the separate kernels every time."""
+    wl = CONFIGS[1]  # ds32_slice
+    sh = wl.shape
+    inp = make_inputs(wl, with_pool=False)
+    g = gpu_inputs(wl, inp)
+    dims = Dims.from_shape(sh)
+    ref = MlaGatherDecode(dims, max_tokens=1)(g).clone()
+    single = MlaGatherDecode(dims, max_tokens=1, single_launch=True)
+    graphed = MlaGatherDecode(dims, max_tokens=1, single_launch=True, graph=True)
+    fixed = torch.empty_like(ref)
+    for i in range(3):
+        a = single(g, noalloc=True).clone()
+        graphed(g, out=fixed)
+        torch.cuda.synchronize()  # eager work and synchronisation between replays
+        _say(f"[single] noalloc / graph replay {i}")
+        assert torch.equal(a, ref) and torch.equal(fixed, ref)
+    assert _err_word(graphed) == 0
