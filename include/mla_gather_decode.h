@@ -53,7 +53,8 @@ extern "C" {
 /* Fused variant (ablation): the kv-row write, the absorption and the gather
  * core run as one launch whose core workgroups wait on device-scope counters
  * in the workspace instead of a kernel boundary.  Applies to steps of at most
- * 8 tokens with at most 16 heads; other steps run the separate kernels. */
+ * 3 tokens (the GEMV path) with at most 16 heads; other steps run the
+ * separate kernels. */
 #define MLA_GD_FLAG_FUSED 1u
 /* Capture the step's launches once into a HIP graph (on a private stream of
  * default priority, owned by the handle) and replay it on the caller's stream;
@@ -84,7 +85,7 @@ extern "C" {
  * loads, then waits on device-scope arrival flags in the workspace for the
  * workgroups whose results it reads (never for a later one, so in-order
  * dispatch always makes progress); results pass through device-scope
- * (write-through) stores.  Applies to steps of at most 8 tokens with at most
+ * (write-through) stores.  Applies to steps of at most 3 tokens with at most
  * 16 heads and n_prior <= 131072; other steps run the separate kernels.
  * Cannot be combined with MLA_GD_FLAG_FUSED (MLA_GD_E_INVAL).  Needs a
  * workspace zeroed by mla_gather_decode_workspace_init (as every workspace
@@ -227,7 +228,7 @@ int mla_gather_decode_step(mla_gd_handle* handle, const mla_gd_tensors* tensors,
 /*
  * Per-kernel timing.  A step of n_tokens tokens runs as
  * mla_gather_decode_kernel_count(handle, n_tokens) kernel launches (steps of
- * more than 8 tokens run the projections on the matrix cores, with two more
+ * more than 3 tokens run the projections on the matrix cores, with two more
  * kernels; 0 for an invalid handle or n_tokens).
  * mla_gather_decode_step_profiled() is mla_gather_decode_step() with timing
  * events (created hipEvent_t handles owned by the caller), in one of two forms:

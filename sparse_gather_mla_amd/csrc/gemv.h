@@ -7,7 +7,7 @@
 namespace mla {
 
 constexpr int kTile = 512;  // output columns per GEMV tile: 64 lanes x 8 bf16
-constexpr int kTT = 8;      // most tokens per pass of the VALU GEMV (and of the GEMV path)
+constexpr int kTT = 4;      // most tokens per pass of the VALU GEMV (the GEMV path takes up to 3)
 
 // 16-byte weight loads in flight per lane: a one-token pass holds few
 // accumulators, so it keeps twice as many loads in flight.
@@ -28,7 +28,8 @@ __device__ __forceinline__ void unpack8v(const u32x4 v, float* w) {
 }
 
 // dst[i] = sum_{s < S} src[s*sstride + (i / w)*tstride + (i % w)] for i < n (floats).
-// Deterministic: part sp of nsp sums s = sp, sp+nsp, ... in order, then the
+// Deterministic: part sp of nsp sums s = sp, sp+nsp, ... in order (loaded
+// eight at a time, so that up to 8*nsp slabs take one round trip), then the
 // parts are added in order.  dst and scratch (256 floats) are LDS.  Every
 // thread of the workgroup must call it.  `sy` loads the partials (handoff.h).
 template <class Sy = HandoffNone>
@@ -41,15 +42,15 @@ __device__ __forceinline__ void reduce_parts(const float* __restrict__ src, size
   for (int idx = tid; idx < n * nsp; idx += kBlock) {
     const int i = idx % n, sp = idx / n;
     const float* s0 = src + (size_t)(i / w) * tstride + (i % w);
-    float a[8];
+    float a = 0.f;
+    for (int s = sp; s < S; s += 8 * nsp) {
+      float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] = 0.f;
-    int s = sp;
-    for (; s + 7 * nsp < S; s += 8 * nsp)
+      for (int u = 0; u < 8; ++u) v[u] = (s + u * nsp < S) ? sy.ld(s0 + (size_t)(s + u * nsp) * sstride) : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] += sy.ld(s0 + (size_t)(s + u * nsp) * sstride);
-    for (; s < S; s += nsp) a[0] += sy.ld(s0 + (size_t)s * sstride);
-    out[sp * n + i] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+      for (int u = 0; u < 8; ++u) a += v[u];
+    }
+    out[sp * n + i] = a;
   }
   __syncthreads();
   if (nsp > 1) {
@@ -75,23 +76,18 @@ __device__ __forceinline__ void reduce_parts4(const float* __restrict__ src, siz
   for (int idx = tid; idx < n4 * nsp; idx += kBlock) {
     const int i = idx % n4, sp = idx / n4;
     const float* s0 = src + (size_t)(i / w4) * tstride + 4 * (i % w4);
-    float4 a[4];
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = sp; s < S; s += 8 * nsp) {
+      float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = sp;
-    for (; s + 3 * nsp < S; s += 4 * nsp) {
+      for (int u = 0; u < 8; ++u)
+        v[u] = (s + u * nsp < S) ? sy.ld4(s0 + (size_t)(s + u * nsp) * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 v = sy.ld4(s0 + (size_t)(s + u * nsp) * sstride);
-        a[u].x += v.x; a[u].y += v.y; a[u].z += v.z; a[u].w += v.w;
+      for (int u = 0; u < 8; ++u) {
+        a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
       }
     }
-    for (; s < S; s += nsp) {
-      const float4 v = sy.ld4(s0 + (size_t)s * sstride);
-      a[0].x += v.x; a[0].y += v.y; a[0].z += v.z; a[0].w += v.w;
-    }
-    out[sp * n4 + i] = make_float4((a[0].x + a[1].x) + (a[2].x + a[3].x), (a[0].y + a[1].y) + (a[2].y + a[3].y),
-                                   (a[0].z + a[1].z) + (a[2].z + a[3].z), (a[0].w + a[1].w) + (a[2].w + a[3].w));
+    out[sp * n4 + i] = a;
   }
   __syncthreads();
   if (nsp > 1) {

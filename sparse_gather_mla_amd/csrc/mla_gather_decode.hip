@@ -188,7 +188,12 @@ CoreShape core_shape(int n_heads) { return n_heads <= 16 ? CoreShape{1, 4} : Cor
 
 int core_grid(const Plan& pl) { return cdiv(pl.T * pl.nsplit, 8) * 8 * pl.core_nhb; }
 
-constexpr int kGemvMaxTokens = kTT;  // more tokens: projections on the matrix cores
+// More tokens: projections on the matrix cores.  Cold steps of the
+// DeepSeek-V3.2 dims (16 heads, n_prior 2048) took, GEMV path against
+// matrix-core path: 2 tokens 65 / 83 us, 3 tokens 79 / 83, 4 tokens 89 / 84,
+// 8 tokens 136 / 86.
+constexpr int kGemvMaxTokens = 3;
+static_assert(kGemvMaxTokens <= kTT, "one GEMV pass per step");
 
 // Matrix-core split-K: about `target` workgroups over `units` (tile, token
 // block) pairs, slabs of at least 8 k-steps.
@@ -467,8 +472,7 @@ core_kernel_t pick_step(int ntt, int R) {
   switch (ntt) {
     case 1: return pick_step_nt<1>(R);
     case 2: return pick_step_nt<2>(R);
-    case 4: return pick_step_nt<4>(R);
-    default: return pick_step_nt<8>(R);
+    default: return pick_step_nt<4>(R);
   }
 }
 
@@ -511,8 +515,7 @@ const char* kernel_name(const Plan& pl, int i) {
 
 hipError_t set_lds_limits(const mla_gd_dims& d) {
   hipError_t e = hipSuccess;
-  const void* gemv[] = {(const void*)k_down<8>, (const void*)k_qup<8>, (const void*)k_absorb<8>,
-                        (const void*)k_oproj<8>, (const void*)k_down<4>, (const void*)k_qup<4>,
+  const void* gemv[] = {(const void*)k_down<4>, (const void*)k_qup<4>,
                         (const void*)k_absorb<4>, (const void*)k_oproj<4>, (const void*)k_oabsorb,
                         (const void*)k_out, (const void*)k_prep, (const void*)k_qa};
   for (const void* k : gemv)
@@ -529,10 +532,8 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
 typedef void (*step_kernel_t)(StepParams);
 
 // GEMV-path kernels for NTT tokens per pass, and their dynamic LDS
-#define MLA_GD_NTT_PICK(fn, K)                                        \
-  step_kernel_t fn(int ntt) {                                         \
-    return ntt == 1 ? K<1> : (ntt == 2 ? K<2> : (ntt == 4 ? K<4> : K<8>)); \
-  }
+#define MLA_GD_NTT_PICK(fn, K) \
+  step_kernel_t fn(int ntt) { return ntt == 1 ? K<1> : (ntt == 2 ? K<2> : K<4>); }
 MLA_GD_NTT_PICK(pick_down, k_down)
 MLA_GD_NTT_PICK(pick_qup, k_qup)
 MLA_GD_NTT_PICK(pick_absorb, k_absorb)
@@ -543,12 +544,11 @@ size_t gemv_lds_bytes(int ntt) {
   switch (ntt) {
     case 1: return GemvLds<1>::floats * sizeof(float);
     case 2: return GemvLds<2>::floats * sizeof(float);
-    case 4: return GemvLds<4>::floats * sizeof(float);
-    default: return GemvLds<8>::floats * sizeof(float);
+    default: return GemvLds<4>::floats * sizeof(float);
   }
 }
 
-int gemv_ntt(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)); }
+int gemv_ntt(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : 4); }
 
 step_kernel_t pick_down_m(int mtb) {
   return mtb == 1 ? k_down_m<1> : (mtb == 2 ? k_down_m<2> : (mtb == 4 ? k_down_m<4> : k_down_m<8>));

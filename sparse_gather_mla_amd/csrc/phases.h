@@ -38,7 +38,7 @@ struct GemvLds {
   static constexpr int aux = scratch + 1024;
   static constexpr int floats = aux + 1024;
 };
-constexpr int kGemvLdsFloats = GemvLds<kTT>::floats;  // the largest (8 tokens per pass)
+constexpr int kGemvLdsFloats = GemvLds<kTT>::floats;  // the largest (kTT tokens per pass)
 // k_oabsorb's LDS layout (floats): split weights and maxima | o_lat [8][R] | scratch
 constexpr int kOabsOl = kTT * kTile;
 constexpr int kOabsScratch = kOabsOl + 4096;
@@ -227,6 +227,14 @@ __device__ __attribute__((always_inline)) void phase_qup(const StepParams& p, in
     const int nt = min(NTT, T - t0);
     u32x4 v[gemv_unroll(NTT)];
     gemv_first<gemv_unroll(NTT)>(p.wq_b, p.N2, k0, ks, c0, nc, v);
+    // g_q of this thread's columns r = tid + 256k, before the partials (an
+    // input, so before any wait too)
+    float gq[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = threadIdx.x + k * kBlock;
+      gq[k] = r < ks ? p.g_q[k0 + r] : 0.f;
+    }
     sy.wait();
     // acc_a[t][k0 .. k0+ks) reduced over the down-projection's slabs
     reduce_parts4(p.part1 + (size_t)t0 * N1 + k0, (size_t)T * N1, pl.s1, nt * ks / 4, ks / 4, N1, xs, scratch, sy);
@@ -240,7 +248,16 @@ __device__ __attribute__((always_inline)) void phase_qup(const StepParams& p, in
       if (tt < nt && rp == 0) sy.st(p.ssq + (size_t)slab * T + t0 + tt, s);
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) xs[idx] *= p.g_q[k0 + idx % ks];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = threadIdx.x + k * kBlock;
+      if (r < ks)
+        for (int tt = 0; tt < nt; ++tt) xs[tt * ks + r] *= gq[k];
+    }
+    for (int r = threadIdx.x + 2 * kBlock; r < ks; r += kBlock) {
+      const float g = p.g_q[k0 + r];
+      for (int tt = 0; tt < nt; ++tt) xs[tt * ks + r] *= g;
+    }
     __syncthreads();
     gemv_tile<NTT, gemv_unroll(NTT)>(p.wq_b, p.N2, k0, ks, c0, nc, xs, ks, nt, p.part2 + ((size_t)slab * T + t0) * p.N2, p.N2, red, v, sy);
   }
@@ -309,6 +326,8 @@ __host__ __device__ constexpr int abs_pre(int ntt) { return ntt == 1 ? 2 : 8; }
 // workgroups (one per token) finish the kv branch: kv-latent RMSNorm,
 // interleaved RoPE of the rotary part, bf16 write of the row at slot_mapping[t].
 // ---------------------------------------------------------------------------
+static_assert(kTT * 32 <= kBlock, "one RoPE pair per thread for every token of a pass (qk_rope_head_dim <= 64)");
+
 template <int NTT, class Sy = HandoffNone>
 __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
@@ -320,6 +339,19 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
   if (b >= n_abs) {
     const int t = b - n_abs;
     const float* kv = p.kvr + (size_t)t * p.KVR;
+    // inputs first: g_kv of columns tid + 256k (kv_lora_rank <= 512) and
+    // the RoPE table of pair tid (qk_rope_head_dim <= 64)
+    const int half = p.DR / 2;
+    float gk[2], rc = 0.f, rs = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = threadIdx.x + k * kBlock;
+      gk[k] = c < p.R ? p.g_kv[c] : 0.f;
+    }
+    if ((int)threadIdx.x < half) {
+      rc = p.cos_t[(size_t)t * half + threadIdx.x];
+      rs = p.sin_t[(size_t)t * half + threadIdx.x];
+    }
     sy.wait();
     float ss = 0.f;
     for (int i = threadIdx.x; i < pl.nkv; i += kBlock) ss += sy.ld(p.kvss + (size_t)t * pl.nkv + i);
@@ -327,13 +359,16 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
     const float inv = inv_rms(ss, p.R, p.eps);
     if (!slot_ok(p, t)) return;
     bf16_t* row = p.cache + (size_t)p.slot[t] * p.KVR;
-    for (int c = threadIdx.x; c < p.R; c += kBlock) sy.st(row + c, f32_to_bf16(sy.ld(kv + c) * inv * p.g_kv[c]));
-    const int half = p.DR / 2;
-    for (int i = threadIdx.x; i < half; i += kBlock) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = threadIdx.x + k * kBlock;
+      if (c < p.R) sy.st(row + c, f32_to_bf16(sy.ld(kv + c) * inv * gk[k]));
+    }
+    if ((int)threadIdx.x < half) {
+      const int i = threadIdx.x;
       const float x0 = sy.ld(kv + p.R + 2 * i), x1 = sy.ld(kv + p.R + 2 * i + 1);
-      const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
-      sy.st(row + p.R + 2 * i, f32_to_bf16(x0 * cs - x1 * sn));
-      sy.st(row + p.R + 2 * i + 1, f32_to_bf16(x0 * sn + x1 * cs));
+      sy.st(row + p.R + 2 * i, f32_to_bf16(x0 * rc - x1 * rs));
+      sy.st(row + p.R + 2 * i + 1, f32_to_bf16(x0 * rs + x1 * rc));
     }
     return;
   }
@@ -350,10 +385,17 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
     // thread's item (token, 4 columns) and slab part sp (s = sp, sp + nsp,
     // ...), its first kAbsPre terms
     u32x4 v[gemv_unroll(NTT)];
-    if constexpr (Sy::kWeightsFirst) {
-      gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
-      sy.wait();
+    if constexpr (Sy::kWeightsFirst) gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
+    // the chunk-0 workgroup's RoPE tables: pair idx = tid of token idx / half
+    // (nt * half <= kTT * 32 <= kBlock), inputs, so before any wait
+    const int half = p.DR / 2;
+    float rc = 0.f, rs = 0.f;
+    if (cc == 0 && (int)threadIdx.x < nt * half) {
+      const int t = t0 + (int)threadIdx.x / half, i = (int)threadIdx.x % half;
+      rc = p.cos_t[(size_t)t * half + i];
+      rs = p.sin_t[(size_t)t * half + i];
     }
+    if constexpr (Sy::kWeightsFirst) sy.wait();
     float tsv[kTsPre];
     tscale_load(p, t0, nt, tsv, sy);
     const int n4 = nt * p.DN / 4, w4 = p.DN / 4;
@@ -445,16 +487,14 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
         reduce_parts(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH + p.DN, (size_t)T * p.N2, pl.s2, nt * p.DR,
                      p.DR, p.N2, xs, scratch, sy);
       }
-      const int half = p.DR / 2;
-      for (int idx = threadIdx.x; idx < nt * half; idx += kBlock) {
-        const int tt = idx / half, i = idx % half, t = t0 + tt;
+      if ((int)threadIdx.x < nt * half) {
+        const int tt = threadIdx.x / half, i = threadIdx.x % half, t = t0 + tt;
         // the query tile is stored pre-scaled by softmax_scale * log2(e)
         const float bq = beta[tt] * p.scale_log2;
         const float x0 = bq * xs[tt * p.DR + 2 * i], x1 = bq * xs[tt * p.DR + 2 * i + 1];
-        const float cs = p.cos_t[(size_t)t * half + i], sn = p.sin_t[(size_t)t * half + i];
         bf16_t* q = p.qcat + ((size_t)t * p.NH + h) * p.KVR + p.R;
-        sy.st(q + 2 * i, f32_to_bf16(x0 * cs - x1 * sn));
-        sy.st(q + 2 * i + 1, f32_to_bf16(x0 * sn + x1 * cs));
+        sy.st(q + 2 * i, f32_to_bf16(x0 * rc - x1 * rs));
+        sy.st(q + 2 * i + 1, f32_to_bf16(x0 * rs + x1 * rc));
       }
     }
     __syncthreads();

@@ -152,7 +152,7 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
 
 
 def test_kernel_lists_of_both_paths(lib):
-    """Steps of up to 8 tokens run the GEMV path; larger ones the matrix-core
+    """Steps of up to 3 tokens run the GEMV path; larger ones the matrix-core
     path with its two extra kernels.  The workspace covers both."""
     rc, h = _create(lib, _dims(max_tokens=40))
     assert rc == 0
@@ -160,8 +160,8 @@ def test_kernel_lists_of_both_paths(lib):
         def names(T):
             n = lib.mla_gather_decode_kernel_count(h, T)
             return [lib.mla_gather_decode_kernel_name(h, T, i).decode() for i in range(n)]
-        gemv = names(8)
-        mfma = names(9)
+        gemv = names(3)
+        mfma = names(4)
         assert gemv == ["k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"]
         full = ["k_prep", "k_down", "k_qa", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"]
         # the output absorption combines the core's splits itself
@@ -187,8 +187,8 @@ def test_fused_flag_kernel_list(lib):
     assert rc == 0
     try:
         assert names(h, 1) == ["k_down", "k_qup", "k_absorb_core", "k_oabsorb", "k_oproj", "k_out"]
-        assert names(h, 8) == names(h, 1)
-        assert "k_absorb_core" not in names(h, 9) and "k_core" in names(h, 9)
+        assert names(h, 3) == names(h, 1)
+        assert "k_absorb_core" not in names(h, 4) and "k_core" in names(h, 4)
         # the counters live in the workspace, so fused and separate sizes agree
         rc2, h2 = _create(lib, _dims(max_tokens=12))
         assert rc2 == 0
@@ -208,7 +208,7 @@ def test_fused_flag_kernel_list(lib):
 
 def test_single_launch_flag_kernel_list(lib):
     """The single-launch variant runs the whole step as one kernel on the GEMV
-    path (up to 8 tokens, up to 16 heads); larger steps, more heads or more
+    path (up to 3 tokens, up to 16 heads); larger steps, more heads or more
     prior positions than its splits hold keep the separate kernels."""
     c = _codes()
 
@@ -219,8 +219,8 @@ def test_single_launch_flag_kernel_list(lib):
     rc, h = _create(lib, _dims(max_tokens=12, flags=c["MLA_GD_FLAG_SINGLE_LAUNCH"]))
     assert rc == 0
     try:
-        assert names(h, 1) == ["k_step"] and names(h, 8) == ["k_step"]
-        assert names(h, 9)[0] == "k_prep" and "k_step" not in names(h, 9)
+        assert names(h, 1) == ["k_step"] and names(h, 3) == ["k_step"]
+        assert names(h, 4)[0] == "k_prep" and "k_step" not in names(h, 4)
         sizes = [lib.mla_gather_decode_workspace_size(h, t) for t in range(1, 13)]
         assert all(b >= a for a, b in zip(sizes, sizes[1:]))
     finally:

@@ -277,4 +277,4 @@ def test_sequence_id_out_of_range_is_masked_and_reported():
     bad["token_seq"][1] = sh.n_tokens  # past the last allowed row
     ref, n = _mask_entries(inp, 1, lambda g: True)
     assert n > 0
-    _check_masked_run("gemv", wl, False, bad, ref, MLA_GD_CHECK_SEQ_RANGE)
+    _check_masked_run("gemv", wl, {}, bad, ref, MLA_GD_CHECK_SEQ_RANGE)

@@ -123,8 +123,8 @@ def test_parity_ragged_shape():
     _run_and_check(RAGGED)
 
 
-# The GEMV path's token passes: 3 tokens in a 4-token pass, 8 in a full one.
-@pytest.mark.parametrize("T", [3, 8])
+# The GEMV path's token passes: 2 tokens in a 2-token pass, 3 in a 4-token pass.
+@pytest.mark.parametrize("T", [2, 3])
 def test_parity_ragged_shape_gemv_token_passes(T):
     wl = replace(RAGGED, name=f"ragged_T{T}", shape=replace(RAGGED.shape, n_tokens=T), seed=177 + T)
     _run_and_check(wl)
@@ -137,11 +137,12 @@ def test_parity_ragged_shape_two_token_blocks():
     _run_and_check(wl)
 
 
-# Steps of more than 8 tokens run the projections on the matrix cores.  Token
-# counts that give one m-tile (9), a ragged block of two (21), a ragged block
-# of four (37) and two blocks of four (70); the ragged shape also gives K not
-# a multiple of the 32-wide k-step and column tiles with tails in every GEMM.
-@pytest.mark.parametrize("T", [9, 21, 37, 70])
+# Steps of more than 3 tokens run the projections on the matrix cores.  Token
+# counts that give one m-tile (4: the fewest, 12 padding rows; 9), a ragged
+# block of two (21), a ragged block of four (37) and two blocks of four (70);
+# the ragged shape also gives K not a multiple of the 32-wide k-step and
+# column tiles with tails in every GEMM.
+@pytest.mark.parametrize("T", [4, 9, 21, 37, 70])
 def test_parity_ragged_shape_matrix_core_path(T):
     wl = replace(RAGGED, name=f"ragged_T{T}", shape=replace(RAGGED.shape, n_tokens=T), seed=77 + T)
     _run_and_check(wl)
@@ -175,7 +176,7 @@ def test_parity_output_absorption_parts():
 
 
 # ---------------------------------------------------------------------------
-# the fused variant: kv rows, absorption and core in one launch (<= 16 heads, <= 8 tokens)
+# the fused variant: kv rows, absorption and core in one launch (<= 16 heads, <= 3 tokens)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["tiny", "ds32_slice"])
 def test_parity_fused_variant(name):
@@ -367,8 +368,10 @@ def _mt(base, name, T, k, seed, **shape_kw):
                    context_range=base.context_range or (60, 120), tokens_per_seq=k, seed=seed)
 
 
+MT_GEMV = _mt(TINY_BASE, "tiny_mt_T3_k3", 3, 3, 3005)              # GEMV path: one sequence of 3
 MULTI_TOKEN = [
-    _mt(TINY_BASE, "tiny_mt_T6_k3", 6, 3, 3001),                      # GEMV path
+    _mt(TINY_BASE, "tiny_mt_T6_k3", 6, 3, 3001),                      # matrix-core path, fewest tokens
+    MT_GEMV,
     _mt(RAGGED, "ragged_mt_T21_k3", 21, 3, 3002),                     # matrix-core path
     _mt(MANY_HEADS, "heads40_mt_T20_k4", 20, 4, 3003),                # row-split core
     _mt(next(c for c in CONFIGS if c.name == "batch32"), "batch32_mt_k4", 32, 4, 3004),  # DeepSeek dims
@@ -382,7 +385,7 @@ def test_parity_multi_token_sequences(wl):
 
 
 def test_parity_multi_token_fused_variant():
-    _run_and_check(MULTI_TOKEN[0], fused=True)
+    _run_and_check(MT_GEMV, fused=True)
 
 
 def test_multi_token_batch_matches_successive_single_token_steps():
@@ -471,7 +474,7 @@ def test_parity_one_far_larger_score_late_in_a_split():
 
 
 # ---------------------------------------------------------------------------
-# the single-launch variant: the whole step as one kernel (<= 8 tokens,
+# the single-launch variant: the whole step as one kernel (<= 3 tokens,
 # <= 16 heads).  Its arithmetic is the separate kernels' (the same splits and
 # reduction orders), so besides the oracle bar it must give the same bits.
 # ---------------------------------------------------------------------------
@@ -480,10 +483,10 @@ RAGGED13 = replace(RAGGED, name="ragged_nh13", shape=replace(RAGGED.shape, n_hea
 SINGLE_CASES = [
     TINY_BASE,
     next(c for c in CONFIGS if c.name == "ds32_slice"),
-    replace(_BATCH32.with_tokens(8), name="batch32_T8"),
-    RAGGED13,                                                                              # 5 tokens: an 8-token pass
+    replace(_BATCH32.with_tokens(3), name="batch32_T3"),
+    replace(RAGGED13, name="ragged_nh13_T3", shape=replace(RAGGED13.shape, n_tokens=3), seed=4403),  # a 4-token pass
     replace(RAGGED13, name="ragged_nh13_T2", shape=replace(RAGGED13.shape, n_tokens=2), seed=4402),
-    MULTI_TOKEN[0],                                                                        # 2 sequences x 3 tokens
+    MT_GEMV,                                                                               # 1 sequence x 3 tokens
 ]
 
 
@@ -507,17 +510,18 @@ def test_single_launch_self_row_and_all_masked():
 
 
 def test_single_launch_repeated_steps_of_varying_size():
-    """One handle and workspace run steps of 8, 3, 1, 8 and 1 tokens in a row:
-    flags of an earlier (larger) step never satisfy a later step's waits (the
-    epoch advances every step), each step gives the separate kernels' bits, and
-    no wait times out."""
+    """One handle and workspace run steps of 8 (matrix-core path), 3, 1, 8, 1
+    and 2 tokens in a row: flags of an earlier (larger) step never satisfy a
+    later step's waits (the epoch advances every step, and the other path's
+    steps leave the flag region alone), each step gives the separate kernels'
+    bits, and no wait times out."""
     wl = _BATCH32.with_tokens(8)
     sh = wl.shape
     inp = make_inputs(wl, with_pool=False)
     g = gpu_inputs(wl, inp)
     single = MlaGatherDecode(Dims.from_shape(sh), max_tokens=8, single_launch=True)
     sep = MlaGatherDecode(Dims.from_shape(sh), max_tokens=8)
-    for T in (8, 3, 1, 8, 1):
+    for T in (8, 3, 1, 8, 1, 2):
         sub = token_slice(g, list(range(T)))
         sub["kv_cache"] = g["kv_cache"]
         a = single(sub).clone()
