@@ -77,6 +77,8 @@ def alg_bytes(sh, inp, names) -> dict:
               "k_oproj": 2 * nh * dv * H, "k_out": 2 * T * H})
     b["k_absorb_core"] = b["k_absorb"] + b["k_core"]  # the fused variant's single launch
     b["k_step"] = sum(b[n] for n in ("k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"))
+    if "k_out" not in names:  # the GEMV path's o-projection writes the output itself
+        b["k_oproj"] += b["k_out"]
     b = {n: b.get(n, 0) for n in names}
     b["step"] = sum(b.values())
     return b

@@ -66,6 +66,23 @@ __device__ __forceinline__ float4 ld_dev4(const float* p) {
                      __uint_as_float((uint32_t)(b >> 32)));
 }
 
+// Stores that a later workgroup of the same kernel reads (no waits): the
+// o-projection's slab partials, which the last slab of a column tile to
+// arrive adds up.
+struct HandoffDevStores {
+  static constexpr bool kWeightsFirst = false;
+  __device__ __forceinline__ void wait() const {}
+  template <class T>
+  __device__ __forceinline__ void st(T* p, T v) const { st_dev(p, v); }
+  __device__ __forceinline__ void st4(float* p, float4 v) const {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    st_dev(q, (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32));
+    st_dev(q + 1, (uint64_t)__float_as_uint(v.z) | ((uint64_t)__float_as_uint(v.w) << 32));
+  }
+  __device__ __forceinline__ float ld(const float* p) const { return *p; }
+  __device__ __forceinline__ float4 ld4(const float* p) const { return *reinterpret_cast<const float4*>(p); }
+};
+
 // Up to three ranges of arrival flags: flags[lo[r] .. lo[r] + n[r]).
 struct FlagSet {
   int lo[3] = {0, 0, 0};

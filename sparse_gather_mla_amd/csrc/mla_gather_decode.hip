@@ -26,9 +26,13 @@ using namespace mla;
 template <int NTT>
 __global__ __launch_bounds__(kBlock) void k_down(StepParams p) {
   extern __shared__ float lds[];
-  // the fused variant's counters start each step at zero (this step's later
-  // kernels run after this one; the previous step's have finished)
-  if (p.pl.fused && blockIdx.x == 0 && (int)threadIdx.x < p.NH + 2) p.sync[threadIdx.x * kSyncStride] = 0u;
+  // the fused variant's counters and the o-projection tiles' arrival counters
+  // start each step at zero (this step's later kernels run after this one;
+  // the previous step's have finished)
+  if (blockIdx.x == 0) {
+    if (p.pl.fused && (int)threadIdx.x < p.NH + 2) p.sync[threadIdx.x * kSyncStride] = 0u;
+    for (int i = threadIdx.x; i < p.pl.nt6; i += kBlock) p.tcnt[i * kSyncStride] = 0u;
+  }
   clear_zero_region(p, blockIdx.x);
   phase_down<NTT>(p, blockIdx.x, lds);
 }
@@ -81,10 +85,13 @@ __global__ __launch_bounds__(kBlock) void k_oabsorb(StepParams p) {
   phase_oabsorb(p, blockIdx.x, lds);
 }
 
+// o-projection slabs; the last slab of each column tile to arrive writes the
+// tile's output (oproj_fold_out)
 template <int NTT>
 __global__ __launch_bounds__(kBlock) void k_oproj(StepParams p) {
   extern __shared__ float lds[];
-  phase_oproj<NTT>(p, blockIdx.x, lds);
+  phase_oproj<NTT>(p, blockIdx.x, lds, HandoffDevStores());
+  oproj_fold_out(p, blockIdx.x % p.pl.nt6, lds);
 }
 
 __global__ __launch_bounds__(kBlock) void k_out(StepParams p) {
@@ -367,7 +374,8 @@ Plan make_plan(const mla_gd_dims& d, int T) {
     pl.ks6 = gemv_batch_rows(pl.tw6, 1);
     pl.s6 = cdiv(NH * DV, pl.ks6);
   }
-  pl.n7 = T * cdiv(H, kOutCols);
+  pl.n7 = 0;  // the output sum runs in the o-projection's last-arriving slabs
+  pl.fold_out = 1;
   if (pl.single) {
     pl.i_down = pl.n_idx_wg;
     pl.i_qup = pl.i_down + pl.nt1 * pl.s1;
@@ -376,7 +384,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
     pl.i_oabs = pl.i_core + core_grid(pl);
     pl.i_oproj = pl.i_oabs + NH * pl.nc5 * pl.nt5c;
     pl.i_out = pl.i_oproj + pl.nt6 * pl.s6;
-    pl.n_items = pl.i_out + pl.n7;
+    pl.n_items = pl.i_out;
     if (pl.n_items > kSingleMaxItems) pl.single = 0;  // then the separate kernels (same split)
   }
 
@@ -404,6 +412,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   pl.off_po = take((size_t)T * pl.nsplit * NH * R * f);
   pl.off_ov = take((size_t)pl.nc5 * T * NH * DV * f);
   pl.off_part6 = take((size_t)pl.s6 * T * H * f);
+  pl.off_tcnt = take((size_t)pl.nt6 * kSyncStride * 4);
   pl.total = off;
   return pl;
 }
@@ -488,11 +497,11 @@ core_kernel_t pick_core(const Plan& pl, int R) {
 }
 
 // Kernels of a step, in launch order: the GEMV path (few tokens) and the matrix-core path.
-const char* const kKernelNamesGemv[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"};
-const char* const kKernelNamesFused[] = {"k_down", "k_qup", "k_absorb_core", "k_oabsorb", "k_oproj", "k_out"};
+const char* const kKernelNamesGemv[] = {"k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj"};
+const char* const kKernelNamesFused[] = {"k_down", "k_qup", "k_absorb_core", "k_oabsorb", "k_oproj"};
 const char* const kKernelNamesMfma[] = {"k_prep", "k_down",    "k_qa",    "k_qup", "k_absorb",
                                         "k_core", "k_oabsorb", "k_oproj", "k_out"};
-constexpr int kNumKernelsGemv = 7;
+constexpr int kNumKernelsGemv = 6;
 constexpr int kNumKernelsMfma = 9;
 constexpr size_t kGemvLdsBytes = kGemvLdsFloats * sizeof(float);
 constexpr int kMaxLdsBytes = 160 * 1024;
@@ -700,7 +709,6 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     L(pick_fused(p.R), dim3(T + p.NH * pl.ncc3 + core_grid(pl)), blk, 0);
     L(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl);
     L(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll);
-    L(k_out, dim3(pl.n7), blk, gl);
   } else if (!pl.mfma) {
     L(pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll);
     L(pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll);
@@ -708,7 +716,6 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     L(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0);
     L(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl);
     L(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll);
-    L(k_out, dim3(pl.n7), blk, gl);
   } else {
     L(k_prep, dim3(pl.n_idx_wg + T * pl.nxc), blk, 1024);
     L(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), blk, 0);
@@ -846,6 +853,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   p.err = (unsigned*)(ws + pl.off_err);
   p.epoch = (unsigned*)(ws + pl.off_flags);
   p.flags = p.epoch + kFlagHeaderWords;
+  p.tcnt = pl.fold_out ? (unsigned*)(ws + pl.off_tcnt) : nullptr;
   p.pl = pl;
 
   hipError_t e = hipSetDevice(h->device);

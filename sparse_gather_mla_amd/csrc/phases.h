@@ -776,4 +776,50 @@ __device__ __attribute__((always_inline)) void phase_out(const StepParams& p, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// GEMV path: the output sum folded into the o-projection.  Each o-projection
+// workgroup (column tile `tile`, one slab) has stored its partials with
+// device scope; once they are complete it counts itself in the tile's
+// arrival counter, and the last of the tile's s6 slabs to arrive adds the
+// tile's slabs, in slab order whichever arrives last (so the result is
+// reproducible), and writes the bf16 output of the tile's columns.  Returns
+// whether this workgroup was the last.  The counters start each step at zero
+// (the step's first kernel or item clears them).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool oproj_fold_out(const StepParams& p, int tile, float* lds) {
+  const Plan& pl = p.pl;
+  const int T = pl.T, S = pl.s6;
+  const int c0 = tile * pl.tw6, nc = min(pl.tw6, p.H - c0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  unsigned* arrived = reinterpret_cast<unsigned*>(lds);
+  if (threadIdx.x == 0)
+    arrived[0] = __hip_atomic_fetch_add(p.tcnt + tile * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (arrived[0] != (unsigned)S - 1u) return false;
+  const int n4 = nc / 4;  // H % 8 == 0 and tw6 % 8 == 0
+  const size_t sstride = (size_t)T * p.H;
+  for (int it = threadIdx.x; it < T * n4; it += kBlock) {
+    const int tt = it / n4, c = c0 + 4 * (it % n4);
+    const float* src = p.part6 + (size_t)tt * p.H + c;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < S; s += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = s + u < S ? ld_dev4(src + (size_t)(s + u) * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
+      }
+    }
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+    o.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+    *reinterpret_cast<uint2*>(p.out + (size_t)tt * p.H + c) = o;
+  }
+  return true;
+}
+
 }  // namespace mla

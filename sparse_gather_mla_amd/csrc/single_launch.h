@@ -2,15 +2,15 @@
 // kernel, in the order of the MLA attention block gather decode API page's
 // description -- the index build first (its inputs are tiny and every gather
 // depends on them), then the down-projections, the query up-projection, the
-// absorption with the kv-row write, the gather core, the output absorption,
-// the o-projection and the output sum.
+// absorption with the kv-row write, the gather core, the output absorption
+// and the o-projection, whose last-arriving slab of each column tile writes
+// the output (oproj_fold_out).
 //
 // Workgroup b runs item b of that list.  An item waits only for the items of
 // earlier phases whose results it reads (HandoffFlags, handoff.h): a
 // q up-projection slab for the down-projection tiles over its rows, an
 // absorption tile for its head's up-projection tiles, an o-projection slab
-// for the output absorption of its heads, an output group for the
-// o-projection tiles over its columns.  The hardware dispatches workgroups in
+// for the output absorption of its heads.  The hardware dispatches workgroups in
 // index order, so the lowest unfinished phase always runs: no wait can
 // deadlock.  Each GEMV item issues its first weight loads before it waits, so
 // a phase's weight stream overlaps the tail of the phase before it, and a
@@ -27,7 +27,7 @@ namespace mla {
 
 constexpr int kSingleRing = 1;
 constexpr int kSingleMaxRows = 2048;
-// the flag region: [0] epoch, [16] completed output workgroups, flags from word 64
+// the flag region: [0] epoch, [16] completed o-projection column tiles, flags from word 64
 constexpr int kFlagHeaderWords = 64;
 constexpr int kFlagRegionWords = 16384;
 constexpr int kSingleMaxItems = kFlagRegionWords - kFlagHeaderWords;
@@ -79,7 +79,10 @@ __device__ __attribute__((always_inline)) void step_single(const StepParams& p, 
   const int T = pl.T;
   auto sync = [&](const FlagSet& fs) { return HandoffFlags{p.flags, p.err, e, fs}; };
   if (b < pl.i_down) {
-    if (b == 0 && threadIdx.x < 64) st_dev(const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(p.zero16)) + threadIdx.x, 0u);
+    if (b == 0) {  // the zero region and the o-projection tiles' arrival counters
+      if (threadIdx.x < 64) st_dev(const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(p.zero16)) + threadIdx.x, 0u);
+      for (int i = threadIdx.x; i < pl.nt6; i += kBlock) st_dev(p.tcnt + i * kSyncStride, 0u);
+    }
     index_build(p, b * kBlock + threadIdx.x, sync(FlagSet()));
   } else if (b < pl.i_qup) {
     phase_down<NTT>(p, slab_major(b - pl.i_down, pl.s1, pl.nt1), fl, sync(FlagSet()));
@@ -122,31 +125,26 @@ __device__ __attribute__((always_inline)) void step_single(const StepParams& p, 
     const int tch = (b - pl.i_oabs) % pl.nt5c, t0 = tch * pl.tc5, nt = min(pl.tc5, T - t0);
     const int lo = pl.i_core + t0 * pl.nsplit, hi = tch == pl.nt5c - 1 ? pl.i_oabs : lo + nt * pl.nsplit;
     phase_oabsorb(p, b - pl.i_oabs, fl, sync(FlagSet().add(lo, hi - lo)));
-  } else if (b < pl.i_out) {
+  } else {
     // o_v rows [k0, k0 + ks): the output absorption of their heads
-    const int i = b - pl.i_oproj, slab = i % pl.s6;
+    const int i = b - pl.i_oproj, slab = i % pl.s6, tile = i / pl.s6;
     const int k0 = slab * pl.ks6, ks = min(pl.ks6, p.NH * p.DV - k0);
     const int ha = k0 / p.DV, hb = (k0 + ks - 1) / p.DV, per_h = pl.nc5 * pl.nt5c;
-    phase_oproj<NTT>(p, slab_major(i, pl.s6, pl.nt6), fl,
-                     sync(FlagSet().add(pl.i_oabs + ha * per_h, (hb - ha + 1) * per_h)));
-  } else {
-    // columns [c0, c1) of one token: the o-projection's tiles over them
-    const int i = b - pl.i_out, ncg = (p.H + kOutCols - 1) / kOutCols;
-    const int c0 = (i % ncg) * kOutCols, c1 = min(p.H, c0 + kOutCols);
-    const int ta = c0 / pl.tw6, tb = (c1 - 1) / pl.tw6;
-    phase_out(p, i, fl, sync(FlagSet().add(pl.i_oproj + ta * pl.s6, (tb - ta + 1) * pl.s6)));
-    // Every other item has raised its flag before the last output item gets
-    // here (the output items wait on every o-projection item, and so on back:
-    // each phase's items together wait on every item of the phases they
-    // read), so every workgroup of the step has read the epoch: the last one
-    // advances it.
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned* done = p.epoch + 16;
-      const unsigned old = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == (unsigned)(pl.n_items - pl.i_out) - 1u) {
-        st_dev(done, 0u);
-        st_dev(p.epoch, e);
+    phase_oproj<NTT>(p, slab * pl.nt6 + tile, fl, sync(FlagSet().add(pl.i_oabs + ha * per_h, (hb - ha + 1) * per_h)));
+    // The last slab of each tile writes the tile's output; the last tile to
+    // be written ends the step.  Every other item has finished reading the
+    // epoch by then (each item's results are waited for, directly or through
+    // its consumers, by some o-projection slab, and every slab is counted),
+    // so that one advances it.
+    if (oproj_fold_out(p, tile, fl)) {
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        unsigned* done = p.epoch + 16;
+        const unsigned old = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == (unsigned)pl.nt6 - 1u) {
+          st_dev(done, 0u);
+          st_dev(p.epoch, e);
+        }
       }
     }
     return;

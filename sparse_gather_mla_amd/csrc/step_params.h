@@ -28,6 +28,9 @@ struct Plan {
   int nt6, s6, ks6;
   // k_out: 64-column groups x token chunks
   int n7;
+  // GEMV path: the output sum is folded into the o-projection (no k_out); the
+  // last slab of each column tile to arrive adds the tile's slabs
+  int fold_out;
   // fused variant: one launch for the kv-row write, the absorption and the core
   int fused;
   // single-launch variant: the whole step as one launch; item (workgroup)
@@ -55,6 +58,7 @@ struct Plan {
   size_t off_a1, off_a2, off_a5;
   size_t off_sync;  // fused variant's counters (same offset for every n_tokens)
   size_t off_flags;  // single-launch epoch and arrival flags (the same offset and size in every plan)
+  size_t off_tcnt;   // GEMV path: per o-projection column tile arrival counters (kSyncStride words apart)
   size_t total;
 };
 
@@ -114,6 +118,7 @@ struct StepParams {
   // number that item last completed
   unsigned* epoch;
   unsigned* flags;
+  unsigned* tcnt;  // GEMV path: o-projection column tiles' arrival counters
   Plan pl;
 };
 

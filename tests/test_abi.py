@@ -131,7 +131,7 @@ def test_workspace_size_and_step_argument_checks(lib):
             assert n >= 1
             names = [lib.mla_gather_decode_kernel_name(h, T, i).decode() for i in range(n)]
             assert all(names) and len(set(names)) == len(names)
-            assert "k_core" in names and names[-1] == "k_out"
+            assert "k_core" in names and names[-1] == ("k_oproj" if T <= 3 else "k_out")
             assert lib.mla_gather_decode_kernel_name(h, T, n) == b""
         assert lib.mla_gather_decode_kernel_count(h, 0) == 0
         assert lib.mla_gather_decode_kernel_count(h, 5) == 0
@@ -162,7 +162,8 @@ def test_kernel_lists_of_both_paths(lib):
             return [lib.mla_gather_decode_kernel_name(h, T, i).decode() for i in range(n)]
         gemv = names(3)
         mfma = names(4)
-        assert gemv == ["k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"]
+        # the GEMV path's o-projection writes the output itself (no k_out)
+        assert gemv == ["k_down", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj"]
         full = ["k_prep", "k_down", "k_qa", "k_qup", "k_absorb", "k_core", "k_oabsorb", "k_oproj", "k_out"]
         # the output absorption combines the core's splits itself
         assert mfma == full and names(40) == full
@@ -186,7 +187,7 @@ def test_fused_flag_kernel_list(lib):
     rc, h = _create(lib, _dims(max_tokens=12, flags=c["MLA_GD_FLAG_FUSED"]))
     assert rc == 0
     try:
-        assert names(h, 1) == ["k_down", "k_qup", "k_absorb_core", "k_oabsorb", "k_oproj", "k_out"]
+        assert names(h, 1) == ["k_down", "k_qup", "k_absorb_core", "k_oabsorb", "k_oproj"]
         assert names(h, 3) == names(h, 1)
         assert "k_absorb_core" not in names(h, 4) and "k_core" in names(h, 4)
         # the counters live in the workspace, so fused and separate sizes agree
