@@ -2,11 +2,13 @@
  * mla_gather_decode.h -- C ABI of one MLA gather-decode step on an MI355X (gfx950).
  *
  * The step is the operation of the "MLA Attention Block Gather Decode Kernel
- * API Reference" page (awsdocs-neuron, nkilib experimental deepseek_v32): one
- * DeepSeek-V3.2 MLA decode step from the residual stream to this rank's
- * attention-block output, attending only over the prior positions a lightning
- * indexer selected.  Tensor names, shapes and meanings are the page's
- * ("API Reference" parameter list; "Notes"; "Dimensions").
+ * API Reference" page (awsdocs-neuron, nkilib experimental deepseek_v32).  For
+ * each decode token it applies the input norm and the low-rank query and
+ * key/value projections, writes the token's row into the paged latent cache,
+ * attends over the earlier positions listed for that token, and projects the
+ * result back to the hidden width (this rank's heads only; no residual add).
+ * Tensor names, shapes and meanings follow the page ("API Reference"
+ * parameter list; "Notes"; "Dimensions").
  *
  * Conventions for every call:
  *   - Every tensor pointer is a DEVICE pointer on the handle's device, in

@@ -184,8 +184,8 @@ def gather_keys(rows_t: np.ndarray, written: Dict[int, np.ndarray], read_rows: R
     """The cache rows one token attends over: one row per valid selected entry
     (duplicates kept, masked entries -1 skipped).  A row this step wrote reads
     the stored value, every other row the pool as it was before the step
-    ("API Reference", ``kv_cache``: the front-fold writes this step's rows,
-    then the core reads selected rows back)."""
+    ("API Reference", ``kv_cache``: the cache is updated in place before the
+    gather, so rows of this step are seen by it)."""
     valid = rows_t[rows_t >= 0]
     keys = np.empty((len(valid), kv_row))
     need = [i for i, rr in enumerate(valid.tolist()) if rr not in written]
