@@ -13,8 +13,8 @@
  *   indices[t]     = the top_k experts by logit, descending (ties: lower index first)
  *   affinities[t]  = zero except at indices[t]: sigmoid(logit), or the softmax
  *                    over the top_k selected logits
- * The logits are accumulated in fp32 from the bf16 inputs; x_hat is stored as
- * bf16 but the router consumes it unrounded.
+ * The logits are accumulated in fp32 from the bf16 (or fp16) inputs; x_hat is
+ * stored in the input type but the router consumes it unrounded.
  *
  * Conventions: every tensor pointer is a device pointer on the current HIP
  * device, row-major; bf16 tensors and the workspace are 16-byte aligned, fp32
@@ -41,13 +41,15 @@ extern "C" {
 
 #define RT_ACT_SIGMOID 0
 #define RT_ACT_SOFTMAX 1
+#define RT_DTYPE_BF16 0 /* hidden_states, gamma, router_weights and normed_out in bf16 */
+#define RT_DTYPE_FP16 1 /* ... in fp16 (the page's second input type) */
 
 /*
  * Device workspace bytes for (n_tokens, hidden, n_experts), 0 if the shape is
  * unsupported.  Limits: 1 <= n_tokens <= 128 (the page's single-tile bound),
  * hidden a multiple of 128 (the page's) up to 65536, n_experts a multiple of 8
- * up to 1024.  The workspace holds split-K partial logits and sums of squares;
- * it needs no initialisation.
+ * up to 1024.  The workspace holds split-K partial logits; it needs no
+ * initialisation.
  */
 size_t rmsnorm_router_topk_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_experts);
 
@@ -65,6 +67,19 @@ int rmsnorm_router_topk(const void* hidden_states, const void* gamma, const void
                         const float* router_bias, int32_t n_tokens, int32_t hidden, int32_t n_experts,
                         int32_t top_k, float eps, int32_t act, void* normed_out, int32_t* topk_indices,
                         void* affinities, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same call with the input type chosen: dtype RT_DTYPE_BF16 (as
+ * rmsnorm_router_topk) or RT_DTYPE_FP16, which the page allows for
+ * hidden_states, gamma and router_weights ("API Reference": bf16/fp16).  The
+ * three inputs share the type, normed_out has it too (rounded to nearest
+ * even), and affinities stay bf16 as the page returns them.  RT_E_INVAL for
+ * another dtype.
+ */
+int rmsnorm_router_topk_typed(int32_t dtype, const void* hidden_states, const void* gamma, const void* router_weights,
+                              const float* router_bias, int32_t n_tokens, int32_t hidden, int32_t n_experts,
+                              int32_t top_k, float eps, int32_t act, void* normed_out, int32_t* topk_indices,
+                              void* affinities, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

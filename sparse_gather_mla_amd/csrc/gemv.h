@@ -20,6 +20,18 @@ __device__ __forceinline__ u32x4 ld_stream(const bf16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// fp16 words of a 32-bit pair
+__device__ __forceinline__ float f16lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu)); }
+__device__ __forceinline__ float f16hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
+
+// eight fp16 values of a 16-byte piece
+__device__ __forceinline__ void unpack8vh(const u32x4 v, float* w) {
+  w[0] = f16lo(v[0]); w[1] = f16hi(v[0]);
+  w[2] = f16lo(v[1]); w[3] = f16hi(v[1]);
+  w[4] = f16lo(v[2]); w[5] = f16hi(v[2]);
+  w[6] = f16lo(v[3]); w[7] = f16hi(v[3]);
+}
+
 __device__ __forceinline__ void unpack8v(const u32x4 v, float* w) {
   w[0] = bf16lo(v[0]); w[1] = bf16hi(v[0]);
   w[2] = bf16lo(v[1]); w[3] = bf16hi(v[1]);
@@ -146,8 +158,8 @@ __device__ __forceinline__ void gemv_first(const bf16_t* __restrict__ W, int N, 
 // W is [K, N] row-major bf16 (N and nc multiples of 8), xs is LDS.  `v` holds
 // the loads of gemv_first<UNR>.  Lanes of equal column combine by shuffles,
 // waves through LDS (`red`: 3*NTT*512 floats).  The output goes out through
-// the hand-off policy `sy` (handoff.h).
-template <int NTT, int UNR, class Sy = HandoffNone>
+// the hand-off policy `sy` (handoff.h).  kHalf: W holds fp16 instead of bf16.
+template <int NTT, int UNR, class Sy = HandoffNone, bool kHalf = false>
 __device__ __forceinline__ void gemv_tile(const bf16_t* __restrict__ W, int N, int k0, int ks, int c0, int nc,
                                           const float* xs, int xstride, int nt, float* __restrict__ out,
                                           size_t ldo, float* red, u32x4* v, const Sy& sy = Sy()) {
@@ -172,7 +184,8 @@ __device__ __forceinline__ void gemv_tile(const bf16_t* __restrict__ W, int N, i
     for (int u = 0; u < UNR; ++u) {
       const int r = min(r0 + u * g.rstep, ks - 1);  // rows past the slab carry zero weights
       float w[8];
-      unpack8v(v[u], w);
+      if constexpr (kHalf) unpack8vh(v[u], w);
+      else unpack8v(v[u], w);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         if (tt < nt) {

@@ -2,22 +2,25 @@
 // "RMSNorm Router Top-K A2AV Kernel API Reference" page ("API Reference";
 // "Notes": top-K on the raw logits, the activation on the selected experts).
 //
-// Two kernels:
+// Two kernels, each templated on the input type (bf16 or fp16, the page's two):
 //   k_rt_partial  split-K GEMV over router_weights with the RMSNorm scale folded
 //                 out: workgroup (64-expert tile, slab of hidden, group of 8
 //                 tokens) loads its weight slab (16-byte non-temporal loads)
-//                 while it stages its tokens' activations, and writes partial
-//                 logits of (x * gamma) @ W and, on tile 0, partial sums of x^2;
-//   k_rt_select   one workgroup per token: 1/rms from the partial sums, the
-//                 normalised bf16 row, logits = (1/rms) * sum of partials + bias
-//                 (the slabs summed in a fixed order, many loads in flight),
-//                 top-K by K rounds of a block-wide argmax (ties to the lower
-//                 expert), the activation on the selected logits, and the
-//                 indices and masked affinities.
+//                 while it stages its tokens' activations x * gamma, and writes
+//                 partial logits of (x * gamma) @ W;
+//   k_rt_select   one workgroup per token.  Its loads go out together (the x
+//                 and gamma row, the bias and the partial logits, many in
+//                 flight), then 1/rms from the row it holds, the logits
+//                 (1/rms) * sum of partials + bias (slabs in a fixed order).
+//                 Wave 0 then runs top-K on registers (E/64 keys a lane, a DPP
+//                 argmax per round, ties to the lower expert, no barriers) and
+//                 the activation of the selected logits, lane by lane, while
+//                 the other waves write the normalised row.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 
+#include "../csrc/core_mfma.h"
 #include "../csrc/gemv.h"
 #include "rmsnorm_router_topk.h"
 
@@ -29,6 +32,8 @@ constexpr int kMaxKs = 256;  // slab rows: one batch of weight loads per lane at
 constexpr int kNtt = 8;      // tokens per GEMV pass
 constexpr int kMaxT = 128, kMaxH = 65536, kMaxE = 1024, kMaxK = 32;
 constexpr int kTargetWG = 112;  // GEMV workgroups before token groups: few slabs keep the select reduction short
+constexpr int kEPL = kMaxE / kWave;  // logits per lane of the top-K wave
+constexpr int kXPre = 4;             // 16-byte pieces of x (and gamma) per thread loaded with the partials
 
 struct RtPlan {
   int ntile, s, ks;
@@ -58,147 +63,241 @@ int shape_code(int T, int H, int E) {
   return RT_OK;
 }
 
-__global__ __launch_bounds__(kBlock) void k_rt_partial(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
-                                                      const bf16_t* __restrict__ W, int T, int H, int E, int ks,
-                                                      int ntile, int s, float* __restrict__ part,
-                                                      float* __restrict__ ssq) {
+// eight input values of a 16-byte piece, and their rounding back
+template <bool F16>
+__device__ __forceinline__ void unpack8in(const uint4 v, float* w) {
+  if constexpr (F16) {
+    unpack8vh(u32x4{v.x, v.y, v.z, v.w}, w);
+  } else {
+    unpack8(v, w);
+  }
+}
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2out(float a, float b) {
+  if constexpr (F16) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+  } else {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  }
+}
+
+template <bool F16>
+__global__ __launch_bounds__(kBlock) void k_rt_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                                      const uint16_t* __restrict__ W, int T, int H, int E, int ks,
+                                                      int ntile, int s, float* __restrict__ part) {
   __shared__ float xs[kNtt * kMaxKs];
   __shared__ float red[3 * kNtt * kTile];
-  __shared__ float sq8[kBlock];
   const int tile = blockIdx.x % ntile, slab = (blockIdx.x / ntile) % s, tg = blockIdx.x / (ntile * s);
   const int c0 = tile * kTW, nc = min(kTW, E - c0);
   const int k0 = slab * ks, kss = min(ks, H - k0);
   // the slab fits one batch of loads: gemv_tile issues no further weight loads
   u32x4 v[gemv_unroll(kNtt)];
   gemv_first<gemv_unroll(kNtt)>(W, E, k0, kss, c0, nc, v);
-  {
-    const int t0 = tg * kNtt, nt = min(kNtt, T - t0);
-    // one 16-byte piece of x and of gamma per thread (nt * kss / 8 <= 256 pieces)
-    const int g8 = kss / 8;
-    const int tt = threadIdx.x / g8, r8 = threadIdx.x % g8;
-    float q = 0.f;
-    if (tt < nt) {
-      float xv[8], gv[8];
-      unpack8(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * H + k0 + 8 * r8), xv);
-      unpack8(*reinterpret_cast<const uint4*>(gamma + k0 + 8 * r8), gv);
+  const int t0 = tg * kNtt, nt = min(kNtt, T - t0);
+  // one 16-byte piece of x and of gamma per thread (nt * kss / 8 <= 256 pieces)
+  const int g8 = kss / 8;
+  const int tt = threadIdx.x / g8, r8 = threadIdx.x % g8;
+  if (tt < nt) {
+    float xv[8], gv[8];
+    unpack8in<F16>(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * H + k0 + 8 * r8), xv);
+    unpack8in<F16>(*reinterpret_cast<const uint4*>(gamma + k0 + 8 * r8), gv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xs[tt * kMaxKs + 8 * r8 + i] = xv[i] * gv[i];
-        q = fmaf(xv[i], xv[i], q);
-      }
-    }
-    sq8[threadIdx.x] = q;
-    __syncthreads();
-    if (tile == 0 && (int)threadIdx.x < nt) {  // sum of x^2 over the slab, pieces in order
-      float a = 0.f;
-      for (int i = 0; i < g8; ++i) a += sq8[threadIdx.x * g8 + i];
-      ssq[(size_t)slab * T + t0 + threadIdx.x] = a;
-    }
-    gemv_tile<kNtt, gemv_unroll(kNtt)>(W, E, k0, kss, c0, nc, xs, kMaxKs, nt,
-                                       part + ((size_t)slab * T + t0) * E, (size_t)E, red, v);
+    for (int i = 0; i < 8; ++i) xs[tt * kMaxKs + 8 * r8 + i] = xv[i] * gv[i];
   }
+  __syncthreads();
+  gemv_tile<kNtt, gemv_unroll(kNtt), HandoffNone, F16>(W, E, k0, kss, c0, nc, xs, kMaxKs, nt,
+                                                      part + ((size_t)slab * T + t0) * E, (size_t)E, red, v);
 }
 
-__global__ __launch_bounds__(kBlock) void k_rt_select(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
+// Top-K keys: the logit mapped to an unsigned number of the same order (NaN
+// ranks as -inf, -0 as +0); 0 is below every expert's key and marks an empty
+// slot.  A round takes the largest key of the wave and, among lanes holding
+// it, the lowest expert: two reductions on 32-bit values (v_max_u32 /
+// v_min_u32 after DPP moves within rows of 16 and lane swaps across them),
+// with no LDS round trips.
+__device__ __forceinline__ unsigned order_key(float v) {
+  if (v != v) v = -INFINITY;
+  if (v == 0.f) v = 0.f;
+  const unsigned u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u(unsigned v) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+// lanes l and l^16 (K32 false) or l and l^32 (true) both get (lower lane's
+// value, upper lane's value), as in core_mfma.h's lane_pair
+template <bool K32>
+__device__ __forceinline__ void pair_u(unsigned a, unsigned& lo, unsigned& hi) {
+  unsigned b = a;
+  asm volatile("" : "+v"(b));
+  const auto r = K32 ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
+                     : __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  lo = r[0];
+  hi = r[1];
+  asm volatile("" : "+v"(lo), "+v"(hi));
+}
+template <bool kMax>
+__device__ __forceinline__ unsigned wave_reduce_u(unsigned v) {
+  auto op = [](unsigned a, unsigned b) { return kMax ? max(a, b) : min(a, b); };
+  v = op(v, dpp_u<kDppQuadXor1>(v));
+  v = op(v, dpp_u<kDppQuadXor2>(v));
+  v = op(v, dpp_u<kDppRowHalfMirror>(v));
+  v = op(v, dpp_u<kDppRowMirror>(v));
+  unsigned lo, hi;
+  pair_u<false>(v, lo, hi);
+  v = op(lo, hi);
+  pair_u<true>(v, lo, hi);
+  return op(lo, hi);
+}
+
+template <bool F16>
+__global__ __launch_bounds__(kBlock) void k_rt_select(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
                                                      const float* __restrict__ bias, int T, int H, int E, int K,
                                                      int s, float eps, int act, const float* __restrict__ part,
-                                                     const float* __restrict__ ssq, bf16_t* __restrict__ normed,
-                                                     int32_t* __restrict__ idx, bf16_t* __restrict__ aff) {
+                                                     uint16_t* __restrict__ normed, int32_t* __restrict__ idx,
+                                                     uint16_t* __restrict__ aff) {
   __shared__ __attribute__((aligned(16))) float zl[kMaxE];  // float4 stores of the partial reduction
-  __shared__ unsigned char taken[kMaxE];
-  __shared__ float wv[kBlock / kWave];
-  __shared__ int we[kBlock / kWave];
-  __shared__ int sel[kMaxK];
-  __shared__ float val[kMaxK];
   __shared__ float scratch[kBlock / kWave];
   __shared__ float4 rscratch[kBlock];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const uint16_t* xr = x + (size_t)t * H;
+  const int nv = H / 8;  // 16-byte pieces of the row
 
-  float sq = 0.f;
-  for (int i = tid; i < s; i += kBlock) sq += ssq[(size_t)i * T + t];
-  sq = block_sum(sq, scratch);
-  const float inv = 1.f / sqrtf(sq / (float)H + eps);
-  // the normalised row, 16-byte pieces, four per thread in flight
-  const int nv = H / 8;
-  for (int i0 = tid; i0 < nv; i0 += 4 * kBlock) {
-    uint4 xv[4], gv[4];
+  // the first kXPre pieces of x and gamma per thread and the bias, issued
+  // before the partial logits so that all of them share one round trip
+  uint4 xv[kXPre], gv[kXPre];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = min(i0 + u * kBlock, nv - 1);
-      xv[u] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + 8 * i);
-      gv[u] = *reinterpret_cast<const uint4*>(gamma + 8 * i);
-    }
+  for (int u = 0; u < kXPre; ++u) {
+    const int i = min(tid + u * kBlock, nv - 1);
+    xv[u] = *reinterpret_cast<const uint4*>(xr + 8 * i);
+    gv[u] = *reinterpret_cast<const uint4*>(gamma + 8 * i);
+  }
+  float bz[kMaxE / kBlock];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kBlock;
-      if (i >= nv) continue;
-      float a[8], b[8];
-      unpack8(xv[u], a);
-      unpack8(gv[u], b);
-      uint4 o;
-      o.x = (uint32_t)f32_to_bf16(a[0] * inv * b[0]) | ((uint32_t)f32_to_bf16(a[1] * inv * b[1]) << 16);
-      o.y = (uint32_t)f32_to_bf16(a[2] * inv * b[2]) | ((uint32_t)f32_to_bf16(a[3] * inv * b[3]) << 16);
-      o.z = (uint32_t)f32_to_bf16(a[4] * inv * b[4]) | ((uint32_t)f32_to_bf16(a[5] * inv * b[5]) << 16);
-      o.w = (uint32_t)f32_to_bf16(a[6] * inv * b[6]) | ((uint32_t)f32_to_bf16(a[7] * inv * b[7]) << 16);
-      *reinterpret_cast<uint4*>(normed + (size_t)t * H + 8 * i) = o;
-    }
+  for (int u = 0; u < kMaxE / kBlock; ++u) {
+    const int e = tid + u * kBlock;
+    bz[u] = (bias && e < E) ? bias[e] : 0.f;
   }
   reduce_parts4(part + (size_t)t * E, (size_t)T * E, s, E / 4, E / 4, 0, zl, reinterpret_cast<float*>(rscratch));
-  for (int e = tid; e < E; e += kBlock) {
-    zl[e] = zl[e] * inv + (bias ? bias[e] : 0.f);
-    taken[e] = 0;
-  }
-  __syncthreads();
 
-  // K rounds of a block-wide argmax over the untaken experts (NaN ranks as -inf,
-  // so every round finds an expert)
-  for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-    for (int e = tid; e < E; e += kBlock) {
-      if (taken[e]) continue;
-      float z = zl[e];
-      if (z != z) z = -INFINITY;
-      if (z > bv || (z == bv && e < be)) { bv = z; be = e; }
-    }
+  // sum of x^2 over the row (pieces past the first kXPre per thread loaded now)
+  float sq = 0.f;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oe = __shfl_xor(be, off, kWave);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+  for (int u = 0; u < kXPre; ++u) {
+    if (tid + u * kBlock < nv) {
+      float a[8];
+      unpack8in<F16>(xv[u], a);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sq = fmaf(a[k], a[k], sq);
     }
-    if ((tid & 63) == 0) { wv[tid >> 6] = bv; we[tid >> 6] = be; }
-    __syncthreads();
-    if (tid == 0) {
-      float b = wv[0];
-      int e0 = we[0];
-      for (int w = 1; w < kBlock / kWave; ++w)
-        if (wv[w] > b || (wv[w] == b && we[w] < e0)) { b = wv[w]; e0 = we[w]; }
-      sel[k] = e0;
-      taken[e0] = 1;
-    }
-    __syncthreads();
   }
-  if (tid == 0) {
-    if (act == RT_ACT_SIGMOID) {
-      for (int k = 0; k < K; ++k) val[k] = 1.f / (1.f + expf(-zl[sel[k]]));
-    } else {  // softmax over the selected logits; sel[0] holds the largest
-      const float m = zl[sel[0]];
-      float sum = 0.f;
-      for (int k = 0; k < K; ++k) {
-        val[k] = expf(zl[sel[k]] - m);
-        sum += val[k];
+  for (int i = tid + kXPre * kBlock; i < nv; i += kBlock) {
+    float a[8];
+    unpack8in<F16>(*reinterpret_cast<const uint4*>(xr + 8 * i), a);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sq = fmaf(a[k], a[k], sq);
+  }
+  sq = block_sum(sq, scratch);  // its barriers also make zl visible
+  const float inv = 1.f / sqrtf(sq / (float)H + eps);
+#pragma unroll
+  for (int u = 0; u < kMaxE / kBlock; ++u) {
+    const int e = tid + u * kBlock;
+    if (e < E) zl[e] = zl[e] * inv + bz[u];
+  }
+  __syncthreads();  // the logits
+  // the normalised row: each thread its own pieces (H % 8 == 0); wave 0
+  // writes its pieces after the top-K, so that no store of its own is in
+  // flight while it ranks (the compiler waits for outstanding stores there)
+  auto put = [&](int i, const uint4& xa, const uint4& ga) {
+    float a[8], b[8];
+    unpack8in<F16>(xa, a);
+    unpack8in<F16>(ga, b);
+    uint4 o;
+    o.x = pack2out<F16>(a[0] * inv * b[0], a[1] * inv * b[1]);
+    o.y = pack2out<F16>(a[2] * inv * b[2], a[3] * inv * b[3]);
+    o.z = pack2out<F16>(a[4] * inv * b[4], a[5] * inv * b[5]);
+    o.w = pack2out<F16>(a[6] * inv * b[6], a[7] * inv * b[7]);
+    *reinterpret_cast<uint4*>(normed + (size_t)t * H + 8 * i) = o;
+  };
+  auto put_mine = [&]() {
+#pragma unroll
+    for (int u = 0; u < kXPre; ++u)
+      if (tid + u * kBlock < nv) put(tid + u * kBlock, xv[u], gv[u]);
+    for (int i = tid + kXPre * kBlock; i < nv; i += kBlock)
+      put(i, *reinterpret_cast<const uint4*>(xr + 8 * i), *reinterpret_cast<const uint4*>(gamma + 8 * i));
+  };
+  if (tid >= kWave) {
+    put_mine();
+    return;
+  }
+
+  // top-K in one wave: lane l holds the keys of experts l + 64 j (j < kEPL),
+  // 0 past E, so every round finds a real expert (K <= E).  Each lane keeps
+  // its best untaken (key, expert); only the lane whose expert a round takes
+  // looks for its next best.
+  unsigned kh[kEPL];
+#pragma unroll
+  for (int j = 0; j < kEPL; ++j) {
+    const int e = lane + kWave * j;
+    kh[j] = e < E ? order_key(zl[e]) : 0u;
+  }
+  unsigned taken = 0u, bv = 0u, be = 0xffffffffu;
+  auto lane_best = [&]() {
+    bv = 0u;
+    be = 0xffffffffu;
+#pragma unroll
+    for (int j = kEPL - 1; j >= 0; --j)  // downwards: among equal keys the lower expert stays
+      if (!((taken >> j) & 1u) && kh[j] != 0u && kh[j] >= bv) {
+        bv = kh[j];
+        be = (unsigned)(lane + kWave * j);
       }
-      for (int k = 0; k < K; ++k) val[k] /= sum;
+  };
+  lane_best();
+  int my_sel = 0;
+  for (int k = 0; k < K; ++k) {
+    const unsigned vmax = wave_reduce_u<true>(bv);
+    const int e = (int)wave_reduce_u<false>(bv == vmax ? be : 0xffffffffu);
+    if (lane == k) my_sel = e;
+    if ((e & 63) == lane) {
+      taken |= 1u << (e >> 6);
+      lane_best();
     }
   }
-  __syncthreads();
-  if (tid < K) idx[(size_t)t * K + tid] = sel[tid];
-  for (int e = tid; e < E; e += kBlock) zl[e] = 0.f;
-  __syncthreads();
-  if (tid < K) zl[sel[tid]] = val[tid];
-  __syncthreads();
-  for (int e = tid; e < E; e += kBlock) aff[(size_t)t * E + e] = f32_to_bf16(zl[e]);
+  // the activation of every selected logit, by the lane that holds it:
+  // sigmoid on its own; softmax against the largest selected logit, divided
+  // by the sum over the selected (wave reductions)
+  float zmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kEPL; ++j)
+    if ((taken >> j) & 1u) zmax = fmaxf(zmax, zl[lane + kWave * j]);
+  zmax = wave_max_dpp(zmax);
+  float ex[kEPL];
+  float esum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kEPL; ++j) {
+    ex[j] = 0.f;
+    if ((taken >> j) & 1u) {
+      const float zj = zl[lane + kWave * j];
+      ex[j] = act == RT_ACT_SIGMOID ? 1.f / (1.f + expf(-zj)) : expf(zj - zmax);
+      esum += ex[j];
+    }
+  }
+  if (act != RT_ACT_SIGMOID) {
+    const float r = 1.f / wave_sum_dpp(esum);
+#pragma unroll
+    for (int j = 0; j < kEPL; ++j) ex[j] *= r;
+  }
+  // the masked affinity row through LDS (this wave alone: its LDS accesses
+  // run in order), written as pairs of bf16
+#pragma unroll
+  for (int j = 0; j < kEPL; ++j)
+    if (lane + kWave * j < E) zl[lane + kWave * j] = ex[j];
+  for (int e0 = 2 * lane; e0 < E; e0 += 2 * kWave)
+    *reinterpret_cast<uint32_t*>(aff + (size_t)t * E + e0) =
+        (uint32_t)f32_to_bf16(zl[e0]) | ((uint32_t)f32_to_bf16(zl[e0 + 1]) << 16);
+  if (lane < K) idx[(size_t)t * K + lane] = my_sel;
+  put_mine();
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -210,15 +309,15 @@ extern "C" {
 size_t rmsnorm_router_topk_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_experts) {
   if (rt::shape_code(n_tokens, hidden, n_experts) != RT_OK) return 0;
   const rt::RtPlan pl = rt::rt_plan(n_tokens, hidden, n_experts);
-  return rt::align256((size_t)pl.s * n_tokens * n_experts * sizeof(float)) +
-         rt::align256((size_t)pl.s * n_tokens * sizeof(float));
+  return rt::align256((size_t)pl.s * n_tokens * n_experts * sizeof(float));
 }
 
-int rmsnorm_router_topk(const void* hidden_states, const void* gamma, const void* router_weights,
-                        const float* router_bias, int32_t n_tokens, int32_t hidden, int32_t n_experts,
-                        int32_t top_k, float eps, int32_t act, void* normed_out, int32_t* topk_indices,
-                        void* affinities, void* workspace, size_t workspace_bytes, void* stream) {
+int rmsnorm_router_topk_typed(int32_t dtype, const void* hidden_states, const void* gamma, const void* router_weights,
+                              const float* router_bias, int32_t n_tokens, int32_t hidden, int32_t n_experts,
+                              int32_t top_k, float eps, int32_t act, void* normed_out, int32_t* topk_indices,
+                              void* affinities, void* workspace, size_t workspace_bytes, void* stream) {
   using namespace rt;
+  if (dtype != RT_DTYPE_BF16 && dtype != RT_DTYPE_FP16) return RT_E_INVAL;
   if (!hidden_states || !gamma || !router_weights || !normed_out || !topk_indices || !affinities || !workspace)
     return RT_E_INVAL;
   const int sc = shape_code(n_tokens, hidden, n_experts);
@@ -233,19 +332,29 @@ int rmsnorm_router_topk(const void* hidden_states, const void* gamma, const void
 
   const RtPlan pl = rt_plan(n_tokens, hidden, n_experts);
   float* part = static_cast<float*>(workspace);
-  float* ssq = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        align256((size_t)pl.s * n_tokens * n_experts * sizeof(float)));
   hipStream_t s = (hipStream_t)stream;
   const int ntg = (n_tokens + kNtt - 1) / kNtt;
-  hipLaunchKernelGGL(k_rt_partial, dim3(pl.ntile * pl.s * ntg), dim3(kBlock), 0, s, (const bf16_t*)hidden_states,
-                     (const bf16_t*)gamma, (const bf16_t*)router_weights, n_tokens, hidden, n_experts, pl.ks, pl.ntile,
-                     pl.s, part, ssq);
+  const bool f16 = dtype == RT_DTYPE_FP16;
+  const auto* xh = (const uint16_t*)hidden_states;
+  const auto* gh = (const uint16_t*)gamma;
+  const auto* wh = (const uint16_t*)router_weights;
+  hipLaunchKernelGGL(f16 ? k_rt_partial<true> : k_rt_partial<false>, dim3(pl.ntile * pl.s * ntg), dim3(kBlock), 0, s,
+                     xh, gh, wh, n_tokens, hidden, n_experts, pl.ks, pl.ntile, pl.s, part);
   if (hipGetLastError() != hipSuccess) return RT_E_HIP;
-  hipLaunchKernelGGL(k_rt_select, dim3(n_tokens), dim3(kBlock), 0, s, (const bf16_t*)hidden_states,
-                     (const bf16_t*)gamma, router_bias, n_tokens, hidden, n_experts, top_k, pl.s, eps, act, part,
-                     ssq, (bf16_t*)normed_out, topk_indices, (bf16_t*)affinities);
+  hipLaunchKernelGGL(f16 ? k_rt_select<true> : k_rt_select<false>, dim3(n_tokens), dim3(kBlock), 0, s, xh, gh,
+                     router_bias, n_tokens, hidden, n_experts, top_k, pl.s, eps, act, part, (uint16_t*)normed_out,
+                     topk_indices, (uint16_t*)affinities);
   if (hipGetLastError() != hipSuccess) return RT_E_HIP;
   return RT_OK;
+}
+
+int rmsnorm_router_topk(const void* hidden_states, const void* gamma, const void* router_weights,
+                        const float* router_bias, int32_t n_tokens, int32_t hidden, int32_t n_experts,
+                        int32_t top_k, float eps, int32_t act, void* normed_out, int32_t* topk_indices,
+                        void* affinities, void* workspace, size_t workspace_bytes, void* stream) {
+  return rmsnorm_router_topk_typed(RT_DTYPE_BF16, hidden_states, gamma, router_weights, router_bias, n_tokens, hidden,
+                                   n_experts, top_k, eps, act, normed_out, topk_indices, affinities, workspace,
+                                   workspace_bytes, stream);
 }
 
 }  // extern "C"

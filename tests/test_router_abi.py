@@ -18,7 +18,7 @@ def _codes():
 def test_router_symbols_exported():
     src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(rmsnorm_router_topk\w*)\s*\(", src)))
-    assert names == ["rmsnorm_router_topk", "rmsnorm_router_topk_workspace_size"]
+    assert names == ["rmsnorm_router_topk", "rmsnorm_router_topk_typed", "rmsnorm_router_topk_workspace_size"]
     lib = sgm.load_library()
     for n in names:
         assert hasattr(lib, n)
@@ -50,3 +50,15 @@ def test_router_argument_errors_before_any_launch():
     assert call(eps=-1.0) == c["RT_E_INVAL"]
     assert call(w=ctypes.c_void_p(4098)) == c["RT_E_ALIGN"]
     assert call(ws=16) == c["RT_E_WORKSPACE"]
+
+
+def test_router_typed_entry_rejects_unknown_dtype_first():
+    c = _codes()
+    lib = router._lib()
+    p = ctypes.c_void_p(4096)
+    for dt in (2, -1):
+        assert lib.rmsnorm_router_topk_typed(dt, p, p, p, None, 1, 256, 16, 2, 1e-6, 0, p, p, p, p, 1 << 20,
+                                             None) == c["RT_E_INVAL"]
+    # a known dtype reaches the ordinary checks
+    assert lib.rmsnorm_router_topk_typed(c["RT_DTYPE_FP16"], p, p, p, None, 0, 256, 16, 2, 1e-6, 0, p, p, p, p,
+                                         1 << 20, None) == c["RT_E_INVAL"]

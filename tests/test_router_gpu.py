@@ -27,10 +27,10 @@ def _f64(t):
     return t.detach().cpu().to(torch.float64).numpy()
 
 
-def _check(T, H, E, K, act, with_bias, seed, zero_weights=False):
-    print(f"[router] T={T} H={H} E={E} K={K} act={act} bias={with_bias}", flush=True)
+def _check(T, H, E, K, act, with_bias, seed, zero_weights=False, dtype=torch.bfloat16):
+    print(f"[router] T={T} H={H} E={E} K={K} act={act} bias={with_bias} dtype={dtype}", flush=True)
     sys.stdout.flush()
-    inp = make_router_inputs(T, H, E, seed, with_bias)
+    inp = make_router_inputs(T, H, E, seed, with_bias, dtype=dtype)
     if zero_weights:
         inp["router_weights"].zero_()
     g = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
@@ -42,8 +42,11 @@ def _check(T, H, E, K, act, with_bias, seed, zero_weights=False):
     a = ro.SIGMOID if act == "sigmoid" else ro.SOFTMAX
     x_hat, ref_idx, _ = ro.rmsnorm_router_topk(x, gam, w, b, 1e-6, K, a)
     z = ro.router_logits(x_hat, w, b)
+    assert normed.dtype == dtype and aff.dtype == torch.bfloat16
     ok, err, bound = within_tol(_f64(normed), x_hat)
     assert ok, ("normed", err, bound)
+    if dtype == torch.float16:  # fp16 keeps 3 more mantissa bits than bf16: a tighter floor holds
+        assert np.max(np.abs(_f64(normed) - x_hat)) <= 2.0 ** -10 * np.max(np.abs(x_hat)), "normed (fp16 rounding)"
     got = idx.cpu().numpy().astype(np.int64)
     ref_aff = np.zeros((T, E))
     n_exact = 0
@@ -86,6 +89,20 @@ def test_router_full_size(name, act):
 ])
 def test_router_ragged_and_limits(T, H, E, K, act, bias):
     _check(T, H, E, K, act, bias, seed=41 + T)
+
+
+@pytest.mark.parametrize("T,H,E,K,act", [
+    (1, 7168, 256, 8, "sigmoid"),   # router_t1 in fp16
+    (37, 1152, 72, 5, "softmax"),   # ragged, fp16
+])
+def test_router_fp16_inputs(T, H, E, K, act):
+    _check(T, H, E, K, act, True, seed=61 + T, dtype=torch.float16)
+
+
+def test_router_largest_expert_count():
+    """n_experts = 1024 (16 logits per lane of the top-K wave, 16 expert tiles)
+    with the largest top_k."""
+    _check(3, 256, 1024, 32, "sigmoid", True, seed=71)
 
 
 def test_router_exact_ties_pick_lower_experts():

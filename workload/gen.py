@@ -419,13 +419,20 @@ ROUTER_CONFIGS = {
 }
 
 
-def make_router_inputs(n_tokens: int, hidden: int, n_experts: int, seed: int, with_bias: bool = True):
-    """hidden_states [T, H] bf16 ~ N(0, 1), gamma [H] bf16 ~ 1 + 0.1 N, router
-    weights [H, E] bf16 ~ N(0, 1/H) (logits of unit scale), bias [E] fp32 ~ 0.1 N."""
+def make_router_inputs(n_tokens: int, hidden: int, n_experts: int, seed: int, with_bias: bool = True,
+                       dtype=torch.bfloat16):
+    """hidden_states [T, H] ~ N(0, 1), gamma [H] ~ 1 + 0.1 N, router weights
+    [H, E] ~ N(0, 1/H) (logits of unit scale), all three in `dtype` (bf16 or
+    fp16, the page's two input types; the same draws either way), bias [E]
+    fp32 ~ 0.1 N."""
+    def cast(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(torch.float32).to(dtype)
+
     out = {
-        "hidden_states": _normal_bf16(seed, "router_hidden", (n_tokens, hidden), 1.0),
-        "gamma": _bf16(1.0 + 0.1 * _rng(seed, "router_gamma").standard_normal(size=(hidden,))),
-        "router_weights": _normal_bf16(seed, "router_weights", (hidden, n_experts), 1.0 / math.sqrt(hidden)),
+        "hidden_states": cast(_rng(seed, "router_hidden").standard_normal(size=(n_tokens, hidden))),
+        "gamma": cast(1.0 + 0.1 * _rng(seed, "router_gamma").standard_normal(size=(hidden,))),
+        "router_weights": cast(_rng(seed, "router_weights").standard_normal(size=(hidden, n_experts))
+                               * (1.0 / math.sqrt(hidden))),
         "router_bias": None,
     }
     if with_bias:
