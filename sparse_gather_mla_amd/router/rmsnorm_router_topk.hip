@@ -8,6 +8,12 @@
 //                 tokens) loads its weight slab (16-byte non-temporal loads)
 //                 while it stages its tokens' activations x * gamma, and writes
 //                 partial logits of (x * gamma) @ W;
+// From 9 tokens on (bf16 inputs) the logits run on the matrix cores instead:
+//   k_rt_prep     x * gamma in fp32, split into bf16 hi and lo halves, in the
+//                 fragment order of the attention step's matrix-core GEMM;
+//   k_rt_partial_m  split-K GEMM (x * gamma) @ W on v_mfma_f32_16x16x32_bf16
+//                 (gemm_mfma.h: both halves meet the weight, about 16
+//                 significant bits), partial logits per K slab.
 //   k_rt_select   one workgroup per token.  Its loads go out together (the x
 //                 and gamma row, the bias and the partial logits, many in
 //                 flight), then 1/rms from the row it holds, the logits
@@ -21,6 +27,7 @@
 #include <algorithm>
 
 #include "../csrc/core_mfma.h"
+#include "../csrc/gemm_mfma.h"
 #include "../csrc/gemv.h"
 #include "rmsnorm_router_topk.h"
 
@@ -39,6 +46,14 @@ struct RtPlan {
   int ntile, s, ks;
 };
 
+// Matrix-core plan: token blocks of kMtb m-tiles (32 tokens), 128-expert
+// tiles, K slabs of ks k-steps (at least 8), about 512 workgroups.
+constexpr int kMtb = 2;
+constexpr int kMfmaMinT = 9;
+struct RtPlanM {
+  int ntile, ntb, mt_pad, kt, ks, s;
+};
+
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 RtPlan rt_plan(int T, int H, int E) {
@@ -55,7 +70,22 @@ RtPlan rt_plan(int T, int H, int E) {
   return pl;
 }
 
+RtPlanM rt_plan_m(int T, int H, int E) {
+  RtPlanM pl;
+  pl.ntile = cdiv(E, mg_cols(kMtb));
+  pl.ntb = cdiv(T, 16 * kMtb);
+  pl.mt_pad = pl.ntb * kMtb;
+  pl.kt = H / kMgK;
+  const int s = std::max(1, std::min(512 / (pl.ntile * pl.ntb), std::max(1, pl.kt / 8)));
+  pl.ks = cdiv(pl.kt, s);
+  pl.s = cdiv(pl.kt, pl.ks);
+  return pl;
+}
+
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// matrix-core workspace: zero bytes | activations in fragment order | partial logits
+size_t abuf_bytes(const RtPlanM& pl) { return (size_t)pl.kt * pl.mt_pad * 2 * kAFragElems * sizeof(uint16_t); }
 
 int shape_code(int T, int H, int E) {
   if (T < 1 || H < 1 || E < 1) return RT_E_INVAL;
@@ -107,6 +137,44 @@ __global__ __launch_bounds__(kBlock) void k_rt_partial(const uint16_t* __restric
   __syncthreads();
   gemv_tile<kNtt, gemv_unroll(kNtt), HandoffNone, F16>(W, E, k0, kss, c0, nc, xs, kMaxKs, nt,
                                                       part + ((size_t)slab * T + t0) * E, (size_t)E, red, v);
+}
+
+// x * gamma (fp32) split into bf16 hi / lo in fragment order, four k per
+// thread; workgroup 0 also clears the zero bytes the GEMM reads for padding.
+// Rows of the last token block past T are left as they are: an output row
+// depends only on its own activation row, and those rows are not written.
+__global__ __launch_bounds__(kBlock) void k_rt_prep(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                                   int T, int H, int mt_pad, uint16_t* __restrict__ abuf,
+                                                   uint32_t* __restrict__ zero) {
+  if (blockIdx.x == 0 && threadIdx.x < 64) zero[threadIdx.x] = 0u;
+  const int nq = H / 4;
+  for (int i = blockIdx.x * kBlock + threadIdx.x; i < T * nq; i += gridDim.x * kBlock) {
+    const int t = i / nq, k = 4 * (i % nq);
+    const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * H + k);
+    const uint2 gv = *reinterpret_cast<const uint2*>(gamma + k);
+    float a[4] = {bf16lo(xv.x) * bf16lo(gv.x), bf16hi(xv.x) * bf16hi(gv.x), bf16lo(xv.y) * bf16lo(gv.y),
+                  bf16hi(xv.y) * bf16hi(gv.y)};
+    put_a4(abuf, mt_pad, t, k, a);
+  }
+}
+
+// Partial logits of one (128-expert tile, K slab, 32-token block).
+__global__ __launch_bounds__(kBlock) void k_rt_partial_m(const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ W,
+                                                        int T, int H, int E, int ntile, int ntb, int mt_pad, int kt,
+                                                        int ks, int s, const uint16_t* __restrict__ zero16,
+                                                        float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) char stage[Mg<kMtb>::kStage];
+  int u, tb;
+  if (!mg_unit(blockIdx.x, ntile * s, ntb, u, tb)) return;
+  const int tile = u % ntile, slab = u / ntile;
+  constexpr int NC = mg_cols(kMtb);
+  const int c0 = tile * NC, k0 = slab * ks * kMgK, nks = min(ks, kt - slab * ks);
+  f32x4_t acc[Mg<kMtb>::MTW][Mg<kMtb>::NTW];
+  mgemm<kMtb>(abuf, mt_pad, tb * kMtb, W, H, E, k0, nks, c0, zero16, stage, acc);
+  float* out = part + (size_t)slab * T * E;
+  mg_for_outputs<kMtb>(acc, tb * kMtb * 16, c0, [&](int t, int c, float v) {
+    if (t < T && c < E) out[(size_t)t * E + c] = v;
+  });
 }
 
 // Top-K keys: the logit mapped to an unsigned number of the same order (NaN
@@ -309,7 +377,13 @@ extern "C" {
 size_t rmsnorm_router_topk_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_experts) {
   if (rt::shape_code(n_tokens, hidden, n_experts) != RT_OK) return 0;
   const rt::RtPlan pl = rt::rt_plan(n_tokens, hidden, n_experts);
-  return rt::align256((size_t)pl.s * n_tokens * n_experts * sizeof(float));
+  size_t b = rt::align256((size_t)pl.s * n_tokens * n_experts * sizeof(float));
+  if (n_tokens >= rt::kMfmaMinT) {  // the matrix-core plan (bf16 inputs)
+    const rt::RtPlanM pm = rt::rt_plan_m(n_tokens, hidden, n_experts);
+    b = std::max(b, 256 + rt::align256(rt::abuf_bytes(pm)) +
+                        rt::align256((size_t)pm.s * n_tokens * n_experts * sizeof(float)));
+  }
+  return b;
 }
 
 int rmsnorm_router_topk_typed(int32_t dtype, const void* hidden_states, const void* gamma, const void* router_weights,
@@ -330,19 +404,36 @@ int rmsnorm_router_topk_typed(int32_t dtype, const void* hidden_states, const vo
   if (!aligned(topk_indices, 4) || (router_bias && !aligned(router_bias, 4))) return RT_E_ALIGN;
   if (workspace_bytes < rmsnorm_router_topk_workspace_size(n_tokens, hidden, n_experts)) return RT_E_WORKSPACE;
 
-  const RtPlan pl = rt_plan(n_tokens, hidden, n_experts);
-  float* part = static_cast<float*>(workspace);
   hipStream_t s = (hipStream_t)stream;
-  const int ntg = (n_tokens + kNtt - 1) / kNtt;
   const bool f16 = dtype == RT_DTYPE_FP16;
   const auto* xh = (const uint16_t*)hidden_states;
   const auto* gh = (const uint16_t*)gamma;
   const auto* wh = (const uint16_t*)router_weights;
-  hipLaunchKernelGGL(f16 ? k_rt_partial<true> : k_rt_partial<false>, dim3(pl.ntile * pl.s * ntg), dim3(kBlock), 0, s,
-                     xh, gh, wh, n_tokens, hidden, n_experts, pl.ks, pl.ntile, pl.s, part);
+  float* part = static_cast<float*>(workspace);
+  int slabs;
+  if (!f16 && n_tokens >= kMfmaMinT) {
+    const RtPlanM pm = rt_plan_m(n_tokens, hidden, n_experts);
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* zero = reinterpret_cast<uint32_t*>(ws);
+    uint16_t* abuf = reinterpret_cast<uint16_t*>(ws + 256);
+    part = reinterpret_cast<float*>(ws + 256 + align256(abuf_bytes(pm)));
+    const int nprep = std::min(2048, cdiv(n_tokens * hidden / 4, kBlock));
+    hipLaunchKernelGGL(k_rt_prep, dim3(nprep), dim3(kBlock), 0, s, xh, gh, n_tokens, hidden, pm.mt_pad, abuf, zero);
+    if (hipGetLastError() != hipSuccess) return RT_E_HIP;
+    const int nwg = cdiv(pm.ntile * pm.s, 8) * 8 * pm.ntb;
+    hipLaunchKernelGGL(k_rt_partial_m, dim3(nwg), dim3(kBlock), 0, s, abuf, wh, n_tokens, hidden, n_experts, pm.ntile,
+                       pm.ntb, pm.mt_pad, pm.kt, pm.ks, pm.s, reinterpret_cast<const uint16_t*>(zero), part);
+    slabs = pm.s;
+  } else {
+    const RtPlan pl = rt_plan(n_tokens, hidden, n_experts);
+    const int ntg = (n_tokens + kNtt - 1) / kNtt;
+    hipLaunchKernelGGL(f16 ? k_rt_partial<true> : k_rt_partial<false>, dim3(pl.ntile * pl.s * ntg), dim3(kBlock), 0,
+                       s, xh, gh, wh, n_tokens, hidden, n_experts, pl.ks, pl.ntile, pl.s, part);
+    slabs = pl.s;
+  }
   if (hipGetLastError() != hipSuccess) return RT_E_HIP;
   hipLaunchKernelGGL(f16 ? k_rt_select<true> : k_rt_select<false>, dim3(n_tokens), dim3(kBlock), 0, s, xh, gh,
-                     router_bias, n_tokens, hidden, n_experts, top_k, pl.s, eps, act, part, (uint16_t*)normed_out,
+                     router_bias, n_tokens, hidden, n_experts, top_k, slabs, eps, act, part, (uint16_t*)normed_out,
                      topk_indices, (uint16_t*)affinities);
   if (hipGetLastError() != hipSuccess) return RT_E_HIP;
   return RT_OK;

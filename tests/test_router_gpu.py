@@ -86,6 +86,8 @@ def test_router_full_size(name, act):
     (37, 1152, 72, 5, "sigmoid", True),    # ragged: 4 passes + 5 tokens, a 64 + 8 expert split
     (3, 256, 64, 32, "softmax", True),     # the largest top_k
     (128, 128, 8, 8, "sigmoid", False),    # every expert selected, the smallest hidden
+    (9, 7168, 256, 8, "sigmoid", True),    # the fewest tokens on the matrix cores: one padded token block
+    (65, 384, 1000, 16, "softmax", True),  # three token blocks, eight expert tiles with a 104-expert tail
 ])
 def test_router_ragged_and_limits(T, H, E, K, act, bias):
     _check(T, H, E, K, act, bias, seed=41 + T)
