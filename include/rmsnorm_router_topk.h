@@ -14,7 +14,10 @@
  *   affinities[t]  = zero except at indices[t]: sigmoid(logit), or the softmax
  *                    over the top_k selected logits
  * The logits are accumulated in fp32 from the bf16 (or fp16) inputs; x_hat is
- * stored in the input type but the router consumes it unrounded.
+ * stored in the input type but the router consumes it unrounded.  From 9
+ * tokens on with bf16 inputs the products run on the matrix cores, with
+ * hidden * gamma carried as two bf16 halves (about 16 significant bits, a
+ * relative error near 2^-17 per product) against the bf16 weight.
  *
  * Conventions: every tensor pointer is a device pointer on the current HIP
  * device, row-major; bf16 tensors and the workspace are 16-byte aligned, fp32
@@ -48,8 +51,9 @@ extern "C" {
  * Device workspace bytes for (n_tokens, hidden, n_experts), 0 if the shape is
  * unsupported.  Limits: 1 <= n_tokens <= 128 (the page's single-tile bound),
  * hidden a multiple of 128 (the page's) up to 65536, n_experts a multiple of 8
- * up to 1024.  The workspace holds split-K partial logits; it needs no
- * initialisation.
+ * up to 1024.  The workspace holds split-K partial logits and, on the
+ * matrix-core path, hidden * gamma in the GEMM's operand order and a small zero
+ * region; it needs no initialisation.
  */
 size_t rmsnorm_router_topk_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_experts);
 
