@@ -51,9 +51,8 @@ extern "C" {
  * Device workspace bytes for (n_tokens, hidden, n_experts), 0 if the shape is
  * unsupported.  Limits: 1 <= n_tokens <= 128 (the page's single-tile bound),
  * hidden a multiple of 128 (the page's) up to 65536, n_experts a multiple of 8
- * up to 1024.  The workspace holds split-K partial logits and, on the
- * matrix-core path, hidden * gamma in the GEMM's operand order and a small zero
- * region; it needs no initialisation.
+ * up to 1024.  The workspace holds split-K partial logits; it needs no
+ * initialisation.
  */
 size_t rmsnorm_router_topk_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_experts);
 

@@ -9,11 +9,13 @@
 //                 while it stages its tokens' activations x * gamma, and writes
 //                 partial logits of (x * gamma) @ W;
 // From 9 tokens on (bf16 inputs) the logits run on the matrix cores instead:
-//   k_rt_prep     x * gamma in fp32, split into bf16 hi and lo halves, in the
-//                 fragment order of the attention step's matrix-core GEMM;
-//   k_rt_partial_m  split-K GEMM (x * gamma) @ W on v_mfma_f32_16x16x32_bf16
-//                 (gemm_mfma.h: both halves meet the weight, about 16
-//                 significant bits), partial logits per K slab.
+//   k_rt_partial_m  split-K GEMM (x * gamma) @ W on v_mfma_f32_16x16x32_bf16,
+//                 partial logits per K slab.  Each k-step's x and gamma
+//                 pieces ride in the same register pipeline as its weight
+//                 pieces; x * gamma is formed in fp32 and split into bf16 hi
+//                 and lo halves as it is written to LDS in fragment order, and
+//                 both halves meet the weight (gemm_mfma.h: about 16
+//                 significant bits).
 //   k_rt_select   one workgroup per token.  Its loads go out together (the x
 //                 and gamma row, the bias and the partial logits, many in
 //                 flight), then 1/rms from the row it holds, the logits
@@ -47,11 +49,13 @@ struct RtPlan {
 };
 
 // Matrix-core plan: token blocks of kMtb m-tiles (32 tokens), 128-expert
-// tiles, K slabs of ks k-steps (at least 8), about 512 workgroups.
+// tiles, K slabs of ks k-steps (at least 8 where that still gives 512
+// workgroups).
 constexpr int kMtb = 2;
+constexpr int kRtMinKs = 8;  // 4 (twice the workgroups and partials) measured slower at 128 tokens
 constexpr int kMfmaMinT = 9;
 struct RtPlanM {
-  int ntile, ntb, mt_pad, kt, ks, s;
+  int ntile, ntb, kt, ks, s;
 };
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -74,9 +78,8 @@ RtPlanM rt_plan_m(int T, int H, int E) {
   RtPlanM pl;
   pl.ntile = cdiv(E, mg_cols(kMtb));
   pl.ntb = cdiv(T, 16 * kMtb);
-  pl.mt_pad = pl.ntb * kMtb;
   pl.kt = H / kMgK;
-  const int s = std::max(1, std::min(512 / (pl.ntile * pl.ntb), std::max(1, pl.kt / 8)));
+  const int s = std::max(1, std::min(512 / (pl.ntile * pl.ntb), std::max(1, pl.kt / kRtMinKs)));
   pl.ks = cdiv(pl.kt, s);
   pl.s = cdiv(pl.kt, pl.ks);
   return pl;
@@ -84,8 +87,6 @@ RtPlanM rt_plan_m(int T, int H, int E) {
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-// matrix-core workspace: zero bytes | activations in fragment order | partial logits
-size_t abuf_bytes(const RtPlanM& pl) { return (size_t)pl.kt * pl.mt_pad * 2 * kAFragElems * sizeof(uint16_t); }
 
 int shape_code(int T, int H, int E) {
   if (T < 1 || H < 1 || E < 1) return RT_E_INVAL;
@@ -139,40 +140,60 @@ __global__ __launch_bounds__(kBlock) void k_rt_partial(const uint16_t* __restric
                                                       part + ((size_t)slab * T + t0) * E, (size_t)E, red, v);
 }
 
-// x * gamma (fp32) split into bf16 hi / lo in fragment order, four k per
-// thread; workgroup 0 also clears the zero bytes the GEMM reads for padding.
-// Rows of the last token block past T are left as they are: an output row
-// depends only on its own activation row, and those rows are not written.
-__global__ __launch_bounds__(kBlock) void k_rt_prep(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
-                                                   int T, int H, int mt_pad, uint16_t* __restrict__ abuf,
-                                                   uint32_t* __restrict__ zero) {
-  if (blockIdx.x == 0 && threadIdx.x < 64) zero[threadIdx.x] = 0u;
-  const int nq = H / 4;
-  for (int i = blockIdx.x * kBlock + threadIdx.x; i < T * nq; i += gridDim.x * kBlock) {
-    const int t = i / nq, k = 4 * (i % nq);
-    const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * H + k);
-    const uint2 gv = *reinterpret_cast<const uint2*>(gamma + k);
-    float a[4] = {bf16lo(xv.x) * bf16lo(gv.x), bf16hi(xv.x) * bf16hi(gv.x), bf16lo(xv.y) * bf16lo(gv.y),
-                  bf16hi(xv.y) * bf16hi(gv.y)};
-    put_a4(abuf, mt_pad, t, k, a);
-  }
-}
+// Sixteen zero bytes for the GEMM's padding loads (never written).
+__device__ __attribute__((aligned(16))) uint16_t g_zero16[8] = {};
 
-// Partial logits of one (128-expert tile, K slab, 32-token block).
-__global__ __launch_bounds__(kBlock) void k_rt_partial_m(const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ W,
-                                                        int T, int H, int E, int ntile, int ntb, int mt_pad, int kt,
-                                                        int ks, int s, const uint16_t* __restrict__ zero16,
-                                                        float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) char stage[Mg<kMtb>::kStage];
+// Partial logits of one (128-expert tile, K slab, 32-token block).  Per
+// k-step each thread loads two 16-byte weight pieces and four k of one token's
+// x and gamma (tokens past T and k-steps past the slab read zeros).
+__global__ __launch_bounds__(kBlock) void k_rt_partial_m(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                                        const uint16_t* __restrict__ W, int T, int H, int E, int ntile,
+                                                        int ntb, int kt, int ks, int s, float* __restrict__ part) {
+  using S = Mg<kMtb>;
+  constexpr int NC = mg_cols(kMtb);
+  static_assert(S::kBPieces == 2 && kMtb * 16 * kMgK == 4 * kBlock, "one x piece per thread and k-step");
+  __shared__ __attribute__((aligned(16))) char stage[S::kStage];
   int u, tb;
   if (!mg_unit(blockIdx.x, ntile * s, ntb, u, tb)) return;
-  const int tile = u % ntile, slab = u / ntile;
-  constexpr int NC = mg_cols(kMtb);
+  const int tile = u % ntile, slab = u / ntile, tid = threadIdx.x;
   const int c0 = tile * NC, k0 = slab * ks * kMgK, nks = min(ks, kt - slab * ks);
-  f32x4_t acc[Mg<kMtb>::MTW][Mg<kMtb>::NTW];
-  mgemm<kMtb>(abuf, mt_pad, tb * kMtb, W, H, E, k0, nks, c0, zero16, stage, acc);
+  const int t0 = tb * kMtb * 16, tt = tid >> 3, k4 = 4 * (tid & 7);
+  const bool row_ok = t0 + tt < T;
+  const uint16_t* xs = x + (size_t)(row_ok ? t0 + tt : 0) * H + k0 + k4;
+  const uint16_t* gs = gamma + k0 + k4;
+  const BTileSrc<NC> bs = btile_src<NC>(W, H, E, k0, c0);
+  f32x4_t acc[S::MTW][S::NTW];
+#pragma unroll
+  for (int mt = 0; mt < S::MTW; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < S::NTW; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  mg_pipe<3, S::kAhead>(
+      nks, stage, S::kStep,
+      [&](int st) {
+        Pieces<3> r;
+        const bool live = st < nks;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint16_t* src = g_zero16;
+          if (live && bs.p[i]) src = bs.p[i] + bs.step * st;
+          r.v[i] = load16_nt(src);
+        }
+        const uint2 xa = *reinterpret_cast<const uint2*>(live && row_ok ? xs + kMgK * st : g_zero16);
+        const uint2 ga = *reinterpret_cast<const uint2*>(live ? gs + kMgK * st : g_zero16);
+        r.v[2] = u32x4_t{xa.x, xa.y, ga.x, ga.y};
+        return r;
+      },
+      [&](const Pieces<3>& r, char* buf) {
+        const u32x4_t v = r.v[2];
+        const float a[4] = {bf16lo(v[0]) * bf16lo(v[2]), bf16hi(v[0]) * bf16hi(v[2]), bf16lo(v[1]) * bf16lo(v[3]),
+                            bf16hi(v[1]) * bf16hi(v[3])};
+        put_a4_lds<true>(buf, kMtb, tt, k4, a);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) store16(buf + S::kABytes + (i * kBlock + tid) * 16, r.v[i]);
+      },
+      [&](int, const char* buf) { mg_step<kMtb, NC>(buf, buf + S::kABytes, acc); });
   float* out = part + (size_t)slab * T * E;
-  mg_for_outputs<kMtb>(acc, tb * kMtb * 16, c0, [&](int t, int c, float v) {
+  mg_for_outputs<kMtb>(acc, t0, c0, [&](int t, int c, float v) {
     if (t < T && c < E) out[(size_t)t * E + c] = v;
   });
 }
@@ -228,6 +249,7 @@ __global__ __launch_bounds__(kBlock) void k_rt_select(const uint16_t* __restrict
   __shared__ __attribute__((aligned(16))) float zl[kMaxE];  // float4 stores of the partial reduction
   __shared__ float scratch[kBlock / kWave];
   __shared__ float4 rscratch[kBlock];
+  static_assert(kBlock * 8 + kMaxK * 8 <= sizeof(float4) * kBlock, "rank top-K scratch");
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const uint16_t* xr = x + (size_t)t * H;
   const int nv = H / 8;  // 16-byte pieces of the row
@@ -295,12 +317,64 @@ __global__ __launch_bounds__(kBlock) void k_rt_select(const uint16_t* __restrict
     for (int i = tid + kXPre * kBlock; i < nv; i += kBlock)
       put(i, *reinterpret_cast<const uint4*>(xr + 8 * i), *reinterpret_cast<const uint4*>(gamma + 8 * i));
   };
+  if (E <= kBlock) {
+    // top-K by rank, one expert per thread: expert e's rank is the number of
+    // experts before it (a larger key, or the same key and a lower index),
+    // counted against every key at once as one 64-bit comparison of (key,
+    // kMaxE - 1 - expert); the experts of rank < K are the selection, in
+    // order.  (The keys and the selection reuse the reduction's scratch.)
+    unsigned long long* ck = reinterpret_cast<unsigned long long*>(rscratch);
+    float* selz = reinterpret_cast<float*>(ck + kBlock);
+    int* sele = reinterpret_cast<int*>(selz + kMaxK);
+    const unsigned long long mine =
+        tid < E ? ((unsigned long long)order_key(zl[tid]) << 32) | (unsigned)(kMaxE - 1 - tid) : 0ull;
+    ck[tid] = mine;
+    __syncthreads();
+    int rank = 0;
+#pragma unroll 4
+    for (int j = 0; j < E; j += 2) {  // E % 8 == 0
+      const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(ck + j);
+      rank += (c.x > mine ? 1 : 0) + (c.y > mine ? 1 : 0);
+    }
+    if (tid < E) {
+      if (rank < K) {
+        selz[rank] = zl[tid];
+        sele[rank] = tid;
+      }
+      zl[tid] = 0.f;  // the affinity row, selected entries filled in below
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // the activations, lane k for the k-th selected expert; the masked
+      // affinity row through LDS (this wave's LDS accesses run in order)
+      const bool on = lane < K;
+      const float z = on ? selz[lane] : -INFINITY;
+      const int e = on ? sele[lane] : 0;
+      float a;
+      if (act == RT_ACT_SIGMOID) {
+        a = 1.f / (1.f + expf(-z));
+      } else {
+        const float zmax = wave_max_dpp(z);
+        const float ex = on ? expf(z - zmax) : 0.f;
+        a = ex * (1.f / wave_sum_dpp(ex));
+      }
+      if (on) {
+        zl[e] = a;
+        idx[(size_t)t * K + lane] = e;
+      }
+      for (int e0 = 2 * lane; e0 < E; e0 += 2 * kWave)
+        *reinterpret_cast<uint32_t*>(aff + (size_t)t * E + e0) =
+            (uint32_t)f32_to_bf16(zl[e0]) | ((uint32_t)f32_to_bf16(zl[e0 + 1]) << 16);
+    }
+    put_mine();
+    return;
+  }
   if (tid >= kWave) {
     put_mine();
     return;
   }
 
-  // top-K in one wave: lane l holds the keys of experts l + 64 j (j < kEPL),
+  // more than kBlock experts: top-K in one wave: lane l holds the keys of experts l + 64 j (j < kEPL),
   // 0 past E, so every round finds a real expert (K <= E).  Each lane keeps
   // its best untaken (key, expert); only the lane whose expert a round takes
   // looks for its next best.
@@ -380,8 +454,7 @@ size_t rmsnorm_router_topk_workspace_size(int32_t n_tokens, int32_t hidden, int3
   size_t b = rt::align256((size_t)pl.s * n_tokens * n_experts * sizeof(float));
   if (n_tokens >= rt::kMfmaMinT) {  // the matrix-core plan (bf16 inputs)
     const rt::RtPlanM pm = rt::rt_plan_m(n_tokens, hidden, n_experts);
-    b = std::max(b, 256 + rt::align256(rt::abuf_bytes(pm)) +
-                        rt::align256((size_t)pm.s * n_tokens * n_experts * sizeof(float)));
+    b = std::max(b, rt::align256((size_t)pm.s * n_tokens * n_experts * sizeof(float)));
   }
   return b;
 }
@@ -413,16 +486,9 @@ int rmsnorm_router_topk_typed(int32_t dtype, const void* hidden_states, const vo
   int slabs;
   if (!f16 && n_tokens >= kMfmaMinT) {
     const RtPlanM pm = rt_plan_m(n_tokens, hidden, n_experts);
-    char* ws = static_cast<char*>(workspace);
-    uint32_t* zero = reinterpret_cast<uint32_t*>(ws);
-    uint16_t* abuf = reinterpret_cast<uint16_t*>(ws + 256);
-    part = reinterpret_cast<float*>(ws + 256 + align256(abuf_bytes(pm)));
-    const int nprep = std::min(2048, cdiv(n_tokens * hidden / 4, kBlock));
-    hipLaunchKernelGGL(k_rt_prep, dim3(nprep), dim3(kBlock), 0, s, xh, gh, n_tokens, hidden, pm.mt_pad, abuf, zero);
-    if (hipGetLastError() != hipSuccess) return RT_E_HIP;
     const int nwg = cdiv(pm.ntile * pm.s, 8) * 8 * pm.ntb;
-    hipLaunchKernelGGL(k_rt_partial_m, dim3(nwg), dim3(kBlock), 0, s, abuf, wh, n_tokens, hidden, n_experts, pm.ntile,
-                       pm.ntb, pm.mt_pad, pm.kt, pm.ks, pm.s, reinterpret_cast<const uint16_t*>(zero), part);
+    hipLaunchKernelGGL(k_rt_partial_m, dim3(nwg), dim3(kBlock), 0, s, xh, gh, wh, n_tokens, hidden, n_experts, pm.ntile,
+                       pm.ntb, pm.kt, pm.ks, pm.s, part);
     slabs = pm.s;
   } else {
     const RtPlan pl = rt_plan(n_tokens, hidden, n_experts);
