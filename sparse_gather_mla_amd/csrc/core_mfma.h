@@ -678,4 +678,231 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
       }
 }
 
+
+// ---------------------------------------------------------------------------
+// Many heads, one head tile per wave: 128 heads per workgroup of eight waves.
+//
+// Wave w owns heads 16w .. 16w+15 of the workgroup's block for the whole
+// chunk: both score tiles (rows 0-15 and 16-31) over the whole kv_row, the
+// softmax of its heads, and the PV product over every latent column.  No wave
+// reads another wave's results, so the ring's barrier is the only one per
+// chunk, and every gathered row is loaded once for all 128 heads.  The PV
+// product is taken transposed, O^T[c, head] += sum_row V^T[c, row] P^T[row, head]:
+// the value fragments are the A operand and the probabilities, which stay in
+// the lanes the score tiles left them in, the B operand.  Lane l's
+// accumulators then all belong to head l%16, so a rescale is a per-lane
+// multiply with no cross-lane moves.
+// LDS: ring | row ids | sink | score bias (ring x 32 floats).
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int core_wide_ofs_bias(int nt) { return core_ofs_sink(nt) + 1024; }
+__host__ __device__ constexpr int core_wide_lds_bytes(int nt) {
+  return core_wide_ofs_bias(nt) + kCoreRing * kCoreChunk * 4;
+}
+
+template <int NT>
+__device__ __attribute__((always_inline)) void core_phase_wide(const StepParams& p, int b, char* lds) {
+  constexpr int NW = 8;
+  constexpr int KSMAX = NT / 2 + 2;  // 32-wide k-steps over kv_row = 16*NT + DR, DR <= 64
+  constexpr int NPMAX = core_row_pieces(NT);
+  constexpr int NI = (kCoreChunk * NPMAX + 64 * NW - 1) / (64 * NW);  // loads per wave per chunk
+  constexpr int BUF = core_buf_bytes(NT);
+  char* ring = lds;
+  int* ids = reinterpret_cast<int*>(lds + core_ofs_ids(NT));
+  char* sink = lds + core_ofs_sink(NT);
+  float* bias = reinterpret_cast<float*>(lds + core_wide_ofs_bias(NT));
+  const Plan& pl = p.pl;
+  const int KVR = p.KVR;
+  const int ks = (KVR + 31) >> 5;  // score k-steps
+  const int npieces = KVR >> 3;    // 16-byte pieces of a cache row
+  const int npad = (4 * ks) | 1;   // LDS row stride in pieces (odd, <= NPMAX)
+  const int rstride = npad * 16;
+  const int slots = kCoreChunk * npad;
+
+  // workgroups of the same (token, split) but different head blocks sit 8
+  // block indices apart: same XCD, shared gathered rows in its L2
+  const int nhb = pl.core_nhb;
+  const int pair = (b / (8 * nhb)) * 8 + (b % 8);
+  const int hb = (b / 8) % nhb;
+  if (pair >= pl.T * pl.nsplit) return;  // padding workgroup (whole group exits before any barrier)
+  const int t = pair / pl.nsplit, split = pair % pl.nsplit;
+  const int j0 = split * pl.ps, j1 = min(p.P, j0 + pl.ps);
+  const int nrows = j1 - j0;
+  const int nchunks = (nrows + kCoreChunk - 1) / kCoreChunk;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar arithmetic below
+  const int g = lane >> 4, l16 = lane & 15;
+  const int head = hb * (16 * NW) + 16 * wave + l16;  // this lane's head (scores, softmax, output)
+
+  for (int i = tid; i < nchunks * kCoreChunk; i += NW * 64)
+    ids[i] = (i < nrows) ? p.rows[(size_t)t * p.P + j0 + i] : -1;
+  __syncthreads();
+
+  // Per-lane geometry of the ring loads, the same for every chunk: load i of
+  // this wave fills slots (i*NW + wave)*64 + lane; geo[i] = (row in the chunk
+  // << 16) | byte offset in the cache row, or -1 for a padding piece (zeros).
+  int geo[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int s = (i * NW + wave) * 64 + lane;
+    const int r = s / npad, pc = s % npad;
+    geo[i] = (s < slots && pc < npieces) ? ((r << 16) | (pc * 16)) : -1;
+  }
+  const unsigned row_bytes = (unsigned)KVR * 2u;
+  const char* cache = reinterpret_cast<const char*>(p.cache);
+  const char* zsrc = reinterpret_cast<const char*>(p.zero16);
+  auto issue_chunk = [&](int c) {
+    const int bsel = c % kCoreRing;
+    char* buf = ring + bsel * BUF;
+    const bool live = c < nchunks;  // wave-uniform
+    const int* cid = ids + min(c, nchunks - 1) * kCoreChunk;
+    if (wave == 0 && lane < kCoreChunk) bias[bsel * kCoreChunk + lane] = (live && cid[lane] >= 0) ? 0.f : -INFINITY;
+    int rid[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) rid[i] = cid[max(geo[i] >> 16, 0)];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int s0 = (i * NW + wave) * 64;  // first slot of this load (scalar)
+      int gi = geo[i];
+      asm volatile("" : "+v"(gi));  // keep the row offset 32-bit; no hoisted 64-bit bases
+      const char* src = zsrc;
+      if (live && gi >= 0 && rid[i] >= 0)
+        src = cache + ((uint64_t)(unsigned)rid[i] * row_bytes + (unsigned)(gi & 0xffff));
+      dma16(src, (s0 < slots) ? buf + s0 * 16 : sink);  // lanes past `slots` stay inside the 1 KB-rounded buffer
+    }
+  };
+
+  f32x4_t o[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // head l16; l over this lane's rows (groups added at the end)
+
+  issue_chunk(0);
+  issue_chunk(1);
+
+  // Q fragments of the whole kv_row: lane l holds Qcat[head][32*kk + 8*g .. +8]
+  // (loaded from a clamped address and zeroed past the heads or the row)
+  bf16x8_t qf[KSMAX];
+  {
+    const bool hl = head < p.NH;
+    const uint16_t* qrow = p.qcat + ((size_t)t * p.NH + (hl ? head : 0)) * KVR;
+#pragma unroll
+    for (int kk = 0; kk < KSMAX; ++kk) {
+      const int k = 32 * kk + 8 * g;
+      const bool ok = hl && kk < ks && k < KVR;
+      u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + (ok ? k : 0));
+      if (!ok) v = u32x4_t{0u, 0u, 0u, 0u};
+      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  wait_vmcnt<0>();
+
+  const lds_char_t* lring = (const lds_char_t*)ring;
+  const lds_char_t* lbias = (const lds_char_t*)bias;
+  // score fragments: rows l16 and 16+l16, pieces 4*kk+g
+  const int sofs = l16 * rstride + 16 * g;
+  // value fragments: rows r1 and r1+16, columns 16n + 4*(l16&3) .. +3 of each tile
+  const int r1 = 4 * g + (l16 >> 2);
+  const int vofs = r1 * rstride + 8 * (l16 & 3);
+  const int rs16 = 16 * rstride;
+
+  for (int c = 0; c < nchunks; ++c) {
+    wait_vmcnt<NI>();  // chunk c's loads are this wave's oldest; chunk c+1 may stay in flight
+    __syncthreads();   // chunk c visible to every wave; buffer (c-1) % ring consumed
+    issue_chunk(c + kCoreRing - 1);
+    const int bsel = c % kCoreRing;
+    const lds_char_t* buf = lring + bsel * BUF;
+    // scores: tile A rows 0-15, tile B rows 16-31, key fragments one step ahead
+    f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      const lds_char_t* pa = buf + sofs;
+      const lds_char_t* pb = pa + rs16;
+      auto ld = [&](const lds_char_t* q, int kk) { return *(const lds_bf16x8_t*)(q + 64 * kk); };
+      if (ks == KSMAX) {  // kv_row fills every k-step (uniform branch)
+        bf16x8_t fa = ld(pa, 0), fb = ld(pb, 0);
+#pragma unroll
+        for (int kk = 0; kk < KSMAX; ++kk) {
+          bf16x8_t na = fa, nb = fb;
+          if (kk + 1 < KSMAX) {
+            na = ld(pa, kk + 1);
+            nb = ld(pb, kk + 1);
+          }
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, qf[kk], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, qf[kk], sb, 0, 0, 0);
+          fa = na;
+          fb = nb;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KSMAX; ++kk) {
+          if (kk < ks) {
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld(pa, kk), qf[kk], sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld(pb, kk), qf[kk], sb, 0, 0, 0);
+          }
+        }
+      }
+    }
+    // rows 4g+i (tile A) and 16+4g+i (tile B): masked rows carry -inf
+    const f32x4_t ba = *(const lds_f32x4_t*)(lbias + 4 * (bsel * kCoreChunk + 4 * g));
+    const f32x4_t bb = *(const lds_f32x4_t*)(lbias + 4 * (bsel * kCoreChunk + 16 + 4 * g));
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = sa[i] + ba[i];
+      s[4 + i] = sb[i] + bb[i];
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    mx = max4groups(mx);  // the chunk maximum of head l16, the same in its four lanes
+    // lazy rescaling, per head: the reference moves only when the chunk
+    // maximum exceeds it by more than 8 (log2 units)
+    float alpha = 1.f;
+    if (mx > m_run + 8.f) {
+      alpha = __builtin_amdgcn_exp2f(m_run - mx);  // m_run = -inf gives 0
+      m_run = mx;
+    }
+    float pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = (m_run != -INFINITY) ? __builtin_amdgcn_exp2f(s[i] - m_run) : 0.f;
+    l_run = l_run * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // wave-uniform
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] *= alpha;
+    }
+    // B operand of the PV product: k-slots 0-3 = rows 4g+i, 4-7 = rows 16+4g+i
+    bf16x8_t pab;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pab[i] = (__bf16)pr[i];
+    const unsigned av = (unsigned)(uintptr_t)(buf + vofs), av2 = av + (unsigned)rs16;
+    auto vfrag = [&](int n) {
+      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(av + 32u * n));
+      const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(av2 + 32u * n));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t vf = vfrag(0);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      bf16x8_t vn = vf;
+      if (n + 1 < NT) vn = vfrag(n + 1);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pab, o[n], 0, 0, 0);
+      vf = vn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();  // the trailing loads (zero rows into unused buffers or the sink)
+
+  const float l_tot = sum4groups(l_run);
+  const size_t pb = ((size_t)t * pl.nsplit + split) * p.NH;
+  if (head < p.NH) {
+    if (g == 0) {
+      p.pm[pb + head] = m_run;
+      p.pden[pb + head] = l_tot;
+    }
+    constexpr int R = 16 * NT;
+    // lane (g, l16) holds columns 16n + 4g + i of head l16
+#pragma unroll
+    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t*>(p.po + (pb + head) * R + 16 * n + 4 * g) = o[n];
+  }
+}
+
 }  // namespace mla

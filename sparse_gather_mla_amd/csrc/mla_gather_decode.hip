@@ -62,6 +62,13 @@ __global__ __launch_bounds__(512) void k_core_rs(StepParams p) {
   core_phase_rs<NT>(p, blockIdx.x, lds);
 }
 
+// more heads (128 per workgroup, eight waves): one head tile per wave (core_mfma.h)
+template <int NT>
+__global__ __launch_bounds__(512) void k_core_wide(StepParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[core_wide_lds_bytes(NT)];
+  core_phase_wide<NT>(p, blockIdx.x, lds);
+}
+
 // single-launch variant: the whole step as one launch (single_launch.h)
 template <int NTT, int NT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_step(StepParams p) {
@@ -191,7 +198,9 @@ struct CoreShape {
 // <= 16 heads: one head group, four waves splitting the latent columns;
 // otherwise four head groups (64 heads) per workgroup, two waves per group
 // splitting the latent columns.
-CoreShape core_shape(int n_heads) { return n_heads <= 16 ? CoreShape{1, 4} : CoreShape{4, 2}; }
+CoreShape core_shape(int n_heads) {
+  return n_heads <= 16 ? CoreShape{1, 4} : (n_heads <= 64 ? CoreShape{4, 2} : CoreShape{8, 1});
+}
 
 int core_grid(const Plan& pl) { return cdiv(pl.T * pl.nsplit, 8) * 8 * pl.core_nhb; }
 
@@ -486,6 +495,14 @@ core_kernel_t pick_step(int ntt, int R) {
 }
 
 core_kernel_t pick_core(const Plan& pl, int R) {
+  if (pl.core_hg == 8) {
+    switch (R / 16) {
+      case 4: return k_core_wide<4>;
+      case 8: return k_core_wide<8>;
+      case 16: return k_core_wide<16>;
+      default: return k_core_wide<32>;
+    }
+  }
   if (pl.core_rs) {
     switch (R / 16) {
       case 8: return k_core_rs<8>;

@@ -166,6 +166,17 @@ def test_parity_many_heads_row_split_core(T):
     _run_and_check(wl)
 
 
+# More than 64 heads: the core gives each wave one 16-head tile, 128 heads per
+# workgroup.  72 heads leave half a tile and three waves without heads; 136
+# heads make a second head block holding one half-empty tile.  Two tokens run
+# the GEMV path, the others the matrix-core path.
+@pytest.mark.parametrize("nh,T", [(72, 2), (72, 21), (136, 5)])
+def test_parity_many_heads_one_tile_per_wave(nh, T):
+    wl = replace(MANY_HEADS, name=f"ragged_heads{nh}_T{T}", shape=replace(MANY_HEADS.shape, n_tokens=T, n_heads=nh),
+                 seed=300 + nh + T)
+    _run_and_check(wl)
+
+
 # 72-wide value heads give five 16-row output tiles: with few (head, token
 # block) pairs the output absorption splits them over two workgroups per pair,
 # the second holding one tile (three of its waves idle), and K5 = 1440 leaves
