@@ -692,9 +692,18 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
 // the lanes the score tiles left them in, the B operand.  Lane l's
 // accumulators then all belong to head l%16, so a rescale is a per-lane
 // multiply with no cross-lane moves.
+// A buffer row spans 4*ks + 2 16-byte pieces: at that stride (2 mod 4) the
+// score fragments' 16-byte reads ran 16 % faster than at the odd stride of
+// the other shapes, and the transposing value reads 3 % slower.
 // LDS: ring | row ids | sink | score bias (ring x 32 floats).
 // ---------------------------------------------------------------------------
-__host__ __device__ constexpr int core_wide_ofs_bias(int nt) { return core_ofs_sink(nt) + 1024; }
+__host__ __device__ constexpr int core_wide_row_pieces(int nt) { return 2 * nt + 10; }
+__host__ __device__ constexpr int core_wide_buf_bytes(int nt) {
+  return (kCoreChunk * core_wide_row_pieces(nt) * 16 + 1023) / 1024 * 1024;
+}
+__host__ __device__ constexpr int core_wide_ofs_ids(int nt) { return kCoreRing * core_wide_buf_bytes(nt); }
+__host__ __device__ constexpr int core_wide_ofs_sink(int nt) { return core_wide_ofs_ids(nt) + kMaxSplitRows * 4; }
+__host__ __device__ constexpr int core_wide_ofs_bias(int nt) { return core_wide_ofs_sink(nt) + 1024; }
 __host__ __device__ constexpr int core_wide_lds_bytes(int nt) {
   return core_wide_ofs_bias(nt) + kCoreRing * kCoreChunk * 4;
 }
@@ -703,18 +712,18 @@ template <int NT>
 __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams& p, int b, char* lds) {
   constexpr int NW = 8;
   constexpr int KSMAX = NT / 2 + 2;  // 32-wide k-steps over kv_row = 16*NT + DR, DR <= 64
-  constexpr int NPMAX = core_row_pieces(NT);
+  constexpr int NPMAX = core_wide_row_pieces(NT);
   constexpr int NI = (kCoreChunk * NPMAX + 64 * NW - 1) / (64 * NW);  // loads per wave per chunk
-  constexpr int BUF = core_buf_bytes(NT);
+  constexpr int BUF = core_wide_buf_bytes(NT);
   char* ring = lds;
-  int* ids = reinterpret_cast<int*>(lds + core_ofs_ids(NT));
-  char* sink = lds + core_ofs_sink(NT);
+  int* ids = reinterpret_cast<int*>(lds + core_wide_ofs_ids(NT));
+  char* sink = lds + core_wide_ofs_sink(NT);
   float* bias = reinterpret_cast<float*>(lds + core_wide_ofs_bias(NT));
   const Plan& pl = p.pl;
   const int KVR = p.KVR;
   const int ks = (KVR + 31) >> 5;  // score k-steps
   const int npieces = KVR >> 3;    // 16-byte pieces of a cache row
-  const int npad = (4 * ks) | 1;   // LDS row stride in pieces (odd, <= NPMAX)
+  const int npad = 4 * ks + 2;     // LDS row stride in pieces (<= NPMAX)
   const int rstride = npad * 16;
   const int slots = kCoreChunk * npad;
 
