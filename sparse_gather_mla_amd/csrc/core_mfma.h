@@ -711,6 +711,8 @@ __host__ __device__ constexpr int core_wide_lds_bytes(int nt) {
 template <int NT>
 __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams& p, int b, char* lds) {
   constexpr int NW = 8;
+  constexpr int KD = 2;                 // key-fragment k-steps in flight
+  constexpr int VD = NT >= 4 ? 4 : NT;  // value-fragment tiles in flight
   constexpr int KSMAX = NT / 2 + 2;  // 32-wide k-steps over kv_row = 16*NT + DR, DR <= 64
   constexpr int NPMAX = core_wide_row_pieces(NT);
   constexpr int NI = (kCoreChunk * NPMAX + 64 * NW - 1) / (64 * NW);  // loads per wave per chunk
@@ -815,31 +817,39 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
   const int vofs = r1 * rstride + 8 * (l16 & 3);
   const int rs16 = 16 * rstride;
 
+  const bool late_issue = wave >= NW / 2;  // the second wave of each SIMD (scalar)
   for (int c = 0; c < nchunks; ++c) {
     wait_vmcnt<NI>();  // chunk c's loads are this wave's oldest; chunk c+1 may stay in flight
     __syncthreads();   // chunk c visible to every wave; buffer (c-1) % ring consumed
-    issue_chunk(c + kCoreRing - 1);
+    // The loads of chunk c+2 stall the issuing wave until the memory system
+    // takes them (they go out at the gather's rate), so the two waves of a
+    // SIMD issue them at different points: waves 0-3 first, waves 4-7 after
+    // their softmax.  Each wave's stall then overlaps the other's products.
+    if (!late_issue) issue_chunk(c + kCoreRing - 1);
     const int bsel = c % kCoreRing;
     const lds_char_t* buf = lring + bsel * BUF;
-    // scores: tile A rows 0-15, tile B rows 16-31, key fragments one step ahead
+    // scores: tile A rows 0-15, tile B rows 16-31, key fragments KD k-steps ahead
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
       const lds_char_t* pa = buf + sofs;
       const lds_char_t* pb = pa + rs16;
       auto ld = [&](const lds_char_t* q, int kk) { return *(const lds_bf16x8_t*)(q + 64 * kk); };
       if (ks == KSMAX) {  // kv_row fills every k-step (uniform branch)
-        bf16x8_t fa = ld(pa, 0), fb = ld(pb, 0);
+        bf16x8_t fa[KD], fb[KD];
+#pragma unroll
+        for (int j = 0; j < KD; ++j) {
+          fa[j] = ld(pa, j);
+          fb[j] = ld(pb, j);
+        }
 #pragma unroll
         for (int kk = 0; kk < KSMAX; ++kk) {
-          bf16x8_t na = fa, nb = fb;
-          if (kk + 1 < KSMAX) {
-            na = ld(pa, kk + 1);
-            nb = ld(pb, kk + 1);
+          const bf16x8_t ca = fa[kk % KD], cb = fb[kk % KD];
+          if (kk + KD < KSMAX) {
+            fa[kk % KD] = ld(pa, kk + KD);
+            fb[kk % KD] = ld(pb, kk + KD);
           }
-          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, qf[kk], sa, 0, 0, 0);
-          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, qf[kk], sb, 0, 0, 0);
-          fa = na;
-          fb = nb;
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca, qf[kk], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb, qf[kk], sb, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
@@ -878,6 +888,7 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] *= alpha;
     }
+    if (late_issue) issue_chunk(c + kCoreRing - 1);
     // B operand of the PV product: k-slots 0-3 = rows 4g+i, 4-7 = rows 16+4g+i
     bf16x8_t pab;
 #pragma unroll
@@ -888,13 +899,15 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
       const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(av2 + 32u * n));
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    bf16x8_t vf = vfrag(0);
+    // value fragments VD tiles ahead
+    bf16x8_t vq[VD];
+#pragma unroll
+    for (int j = 0; j < VD; ++j) vq[j] = vfrag(j);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      bf16x8_t vn = vf;
-      if (n + 1 < NT) vn = vfrag(n + 1);
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pab, o[n], 0, 0, 0);
-      vf = vn;
+      const bf16x8_t cv = vq[n % VD];
+      if (n + VD < NT) vq[n % VD] = vfrag(n + VD);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv, pab, o[n], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
