@@ -184,8 +184,10 @@ __device__ __forceinline__ void mg_step(const char* bufA, const char* bufB,
     const bf16x8_t alo = *reinterpret_cast<const bf16x8_t*>(bufA + ((m * 2 + 1) * 64 + lane) * 16);
 #pragma unroll
     for (int nt = 0; nt < S::NTW; ++nt) {
-      acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr[nt], acc[mt][nt], 0, 0, 0);
-      acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr[nt], acc[mt][nt], 0, 0, 0);
+      // transposed product (weight fragment as the A operand): lane (g, l16)
+      // gets columns 4g..4g+3 of token l16, stored four at a time
+      acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nt], ahi, acc[mt][nt], 0, 0, 0);
+      acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nt], alo, acc[mt][nt], 0, 0, 0);
     }
   }
 }
@@ -281,11 +283,12 @@ __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, cons
       [&](int, const char* buf) { mg_step<MTB, NC>(buf, buf + S::kABytes, acc); });
 }
 
-// Lane (g, l16) of a wave holds D[4g+i][l16] of each 16x16 output tile.
-// Visits (token, column, value) of the wave's tiles for a block starting at token t0.
+// Lane (g, l16) of a wave holds out[token l16][columns 4g .. 4g+3] of each
+// 16x16 output tile (the products are taken transposed).  Visits (token,
+// first column, four values) of the wave's tiles for a block starting at token t0.
 template <int MTB, int NC = mg_cols(MTB), class F>
-__device__ __forceinline__ void mg_for_outputs(const f32x4_t (&acc)[Mg<MTB, NC>::MTW][Mg<MTB, NC>::NTW], int t0,
-                                               int c0, F&& f) {
+__device__ __forceinline__ void mg_for_outputs4(const f32x4_t (&acc)[Mg<MTB, NC>::MTW][Mg<MTB, NC>::NTW], int t0,
+                                                int c0, F&& f) {
   using S = Mg<MTB, NC>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::WN, wn = wave % S::WN;
@@ -294,9 +297,18 @@ __device__ __forceinline__ void mg_for_outputs(const f32x4_t (&acc)[Mg<MTB, NC>:
   for (int mt = 0; mt < S::MTW; ++mt)
 #pragma unroll
     for (int nt = 0; nt < S::NTW; ++nt)
+      f(t0 + 16 * (wm * S::MTW + mt) + l16, c0 + 16 * (wn * S::NTW + nt) + 4 * g, acc[mt][nt]);
+}
+
+// Four consecutive fp32 outputs out[c .. c+3] (c % 4 == 0), columns from n on dropped.
+__device__ __forceinline__ void store_f32x4(float* out, int c, int n, const f32x4_t& v) {
+  if (c + 4 <= n) {
+    *reinterpret_cast<f32x4_t*>(out + c) = v;
+  } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        f(t0 + 16 * (wm * S::MTW + mt) + 4 * g + i, c0 + 16 * (wn * S::NTW + nt) + l16, acc[mt][nt][i]);
+    for (int i = 0; i < 4; ++i)
+      if (c + i < n) out[c + i] = v[i];
+  }
 }
 
 }  // namespace mla

@@ -132,8 +132,8 @@ __device__ void phase_down_m(const StepParams& p, int b, char* stage) {
   mgemm<MTB>(p.a1, pl.mt_pad, tb * MTB, W, p.H, N, k0, nks, c0, reinterpret_cast<const bf16_t*>(p.zero16), stage, acc);
   const int N1 = p.Q + p.KVR, T = pl.T;
   float* out = p.part1 + (size_t)slab * T * N1 + (is_q ? 0 : p.Q);
-  mg_for_outputs<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, float v) {
-    if (t < T && c < N) out[(size_t)t * N1 + c] = v;
+  mg_for_outputs4<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, const f32x4_t& v) {
+    if (t < T) store_f32x4(out + (size_t)t * N1, c, N, v);
   });
 }
 
@@ -263,8 +263,8 @@ __device__ void phase_qup_m(const StepParams& p, int b, char* stage) {
   mgemm<MTB>(p.a2, pl.mt_pad, tb * MTB, p.wq_b, p.Q, p.N2, k0, nks, c0, reinterpret_cast<const bf16_t*>(p.zero16), stage, acc);
   const int T = pl.T;
   float* out = p.part2 + (size_t)slab * T * p.N2;
-  mg_for_outputs<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, float v) {
-    if (t < T && c < p.N2) out[(size_t)t * p.N2 + c] = v;
+  mg_for_outputs4<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, const f32x4_t& v) {
+    if (t < T) store_f32x4(out + (size_t)t * p.N2, c, p.N2, v);
   });
 }
 
@@ -380,8 +380,13 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
         const int j = j0 + st / KS, ks = st % KS;
         mg_step<MTB, NCA>(ares + ks * S::kABytes, buf, acc);
         if (ks == KS - 1) {  // tile j complete
-          mg_for_outputs<MTB, NCA>(acc, t0, j * NCA, [&](int t, int c, float v) {
-            if (t < T) p.qcat[((size_t)t * p.NH + h) * p.KVR + c] = f32_to_bf16(v * p.scale_log2);
+          mg_for_outputs4<MTB, NCA>(acc, t0, j * NCA, [&](int t, int c, const f32x4_t& v) {
+            if (t < T) {  // four bf16 in one 8-byte store (KVR % 8 == 0, c % 4 == 0)
+              const float sl = p.scale_log2;
+              const uint2 w = make_uint2(pack_bf16x2(f32_to_bf16(v[0] * sl), f32_to_bf16(v[1] * sl)),
+                                         pack_bf16x2(f32_to_bf16(v[2] * sl), f32_to_bf16(v[3] * sl)));
+              *reinterpret_cast<uint2*>(p.qcat + ((size_t)t * p.NH + h) * p.KVR + c) = w;
+            }
           });
           zero();
         }
@@ -583,26 +588,29 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
         for (int mt = 0; mt < MTB; ++mt) {
           const bf16x8_t ahi = *reinterpret_cast<const bf16x8_t*>(blk + ((mt * 2) * 64 + lane) * 16);
           const bf16x8_t alo = *reinterpret_cast<const bf16x8_t*>(blk + ((mt * 2 + 1) * 64 + lane) * 16);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr[q][ks], acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr[q][ks], acc[mt], 0, 0, 0);
+          // transposed product: lane (g, l16) gets o_v columns 4g..4g+3 of token l16
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[q][ks], ahi, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[q][ks], alo, acc[mt], 0, 0, 0);
         }
       }
-      const int d = 16 * n + l16;
-      if (d < p.DV) {
-        const int k = h * p.DV + d;
+      const int d0 = 16 * n + 4 * g;
 #pragma unroll
-        for (int mt = 0; mt < MTB; ++mt)
+      for (int mt = 0; mt < MTB; ++mt) {
+        const int t = t0 + 16 * mt + l16;
+        if (t >= T) continue;
+        const float a[4] = {acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]};
+        if ((p.DV & 3) == 0 && d0 + 3 < p.DV) {
+          put_a4(p.a5, pl.mt_pad, t, h * p.DV + d0, a);  // one 8-byte run per half
+        } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 16 * mt + 4 * g + i;
-            if (t < T) {
-              const float v = acc[mt][i];
-              const bf16_t hi = f32_to_bf16(v);
-              const size_t e = abuf_index(t, k, pl.mt_pad);
-              p.a5[e] = hi;
-              p.a5[e + kAFragElems] = f32_to_bf16(v - bf16_to_f32(hi));
-            }
+            if (d0 + i >= p.DV) continue;
+            const bf16_t hi = f32_to_bf16(a[i]);
+            const size_t e = abuf_index(t, h * p.DV + d0 + i, pl.mt_pad);
+            p.a5[e] = hi;
+            p.a5[e + kAFragElems] = f32_to_bf16(a[i] - bf16_to_f32(hi));
           }
+        }
       }
     }
   }
@@ -634,8 +642,8 @@ __device__ void phase_oproj_m(const StepParams& p, int b, char* stage) {
   mgemm<MTB>(p.a5, pl.mt_pad, tb * MTB, p.w_o, p.NH * p.DV, p.H, k0, nks, c0, reinterpret_cast<const bf16_t*>(p.zero16), stage, acc);
   const int T = pl.T;
   float* out = p.part6 + (size_t)slab * T * p.H;
-  mg_for_outputs<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, float v) {
-    if (t < T && c < p.H) out[(size_t)t * p.H + c] = v;
+  mg_for_outputs4<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, const f32x4_t& v) {
+    if (t < T) store_f32x4(out + (size_t)t * p.H, c, p.H, v);
   });
 }
 

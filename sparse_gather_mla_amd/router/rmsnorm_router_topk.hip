@@ -193,8 +193,8 @@ __global__ __launch_bounds__(kBlock) void k_rt_partial_m(const uint16_t* __restr
       },
       [&](int, const char* buf) { mg_step<kMtb, NC>(buf, buf + S::kABytes, acc); });
   float* out = part + (size_t)slab * T * E;
-  mg_for_outputs<kMtb>(acc, t0, c0, [&](int t, int c, float v) {
-    if (t < T && c < E) out[(size_t)t * E + c] = v;
+  mg_for_outputs4<kMtb>(acc, t0, c0, [&](int t, int c, const f32x4_t& v) {
+    if (t < T) store_f32x4(out + (size_t)t * E, c, E, v);
   });
 }
 
