@@ -188,8 +188,8 @@ typedef struct mla_gd_handle mla_gd_handle;
  * n_heads*(dn+dr) must be multiples of 8; kv_lora_rank one of 64, 128, 256,
  * 512; qk_rope_head_dim even and at most 64; qk_nope_head_dim at most 512;
  * qk_nope_head_dim + qk_rope_head_dim a multiple of 4; q_lora_rank +
- * kv_lora_rank + qk_rope_head_dim at most 16384; n_prior at most 262144;
- * max_tokens at most 4096.
+ * kv_lora_rank + qk_rope_head_dim at most 16384; n_prior at most 262144
+ * (163840 with more than 64 heads); max_tokens at most 4096.
  */
 int mla_gather_decode_create(const mla_gd_dims* dims, int device, mla_gd_handle** out_handle);
 

@@ -701,12 +701,17 @@ __host__ __device__ constexpr int core_wide_row_pieces(int nt) { return 2 * nt +
 __host__ __device__ constexpr int core_wide_buf_bytes(int nt) {
   return (kCoreChunk * core_wide_row_pieces(nt) * 16 + 1023) / 1024 * 1024;
 }
-__host__ __device__ constexpr int core_wide_ofs_ids(int nt) { return kCoreRing * core_wide_buf_bytes(nt); }
-__host__ __device__ constexpr int core_wide_ofs_sink(int nt) { return core_wide_ofs_ids(nt) + kMaxSplitRows * 4; }
+// Four chunk buffers keep three chunks' loads in flight (3 % faster than
+// three buffers at large128); the row ids of a split then get the 10 KB left.
+constexpr int kWideRing = 4;
+constexpr int kWideMaxSplitRows = 2560;  // row ids staged per workgroup
+__host__ __device__ constexpr int core_wide_ofs_ids(int nt) { return kWideRing * core_wide_buf_bytes(nt); }
+__host__ __device__ constexpr int core_wide_ofs_sink(int nt) { return core_wide_ofs_ids(nt) + kWideMaxSplitRows * 4; }
 __host__ __device__ constexpr int core_wide_ofs_bias(int nt) { return core_wide_ofs_sink(nt) + 1024; }
 __host__ __device__ constexpr int core_wide_lds_bytes(int nt) {
-  return core_wide_ofs_bias(nt) + kCoreRing * kCoreChunk * 4;
+  return core_wide_ofs_bias(nt) + kWideRing * kCoreChunk * 4;
 }
+static_assert(core_wide_lds_bytes(32) <= 160 * 1024, "one workgroup's LDS");
 
 template <int NT>
 __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams& p, int b, char* lds) {
@@ -763,7 +768,7 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
   const char* cache = reinterpret_cast<const char*>(p.cache);
   const char* zsrc = reinterpret_cast<const char*>(p.zero16);
   auto issue_chunk = [&](int c) {
-    const int bsel = c % kCoreRing;
+    const int bsel = c % kWideRing;
     char* buf = ring + bsel * BUF;
     const bool live = c < nchunks;  // wave-uniform
     const int* cid = ids + min(c, nchunks - 1) * kCoreChunk;
@@ -788,8 +793,8 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
   for (int n = 0; n < NT; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;  // head l16; l over this lane's rows (groups added at the end)
 
-  issue_chunk(0);
-  issue_chunk(1);
+#pragma unroll
+  for (int c = 0; c + 1 < kWideRing; ++c) issue_chunk(c);
 
   // Q fragments of the whole kv_row: lane l holds Qcat[head][32*kk + 8*g .. +8]
   // (loaded from a clamped address and zeroed past the heads or the row)
@@ -819,14 +824,14 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
 
   const bool late_issue = wave >= NW / 2;  // the second wave of each SIMD (scalar)
   for (int c = 0; c < nchunks; ++c) {
-    wait_vmcnt<NI>();  // chunk c's loads are this wave's oldest; chunk c+1 may stay in flight
+    wait_vmcnt<NI * (kWideRing - 2)>();  // chunk c's loads are this wave's oldest; c+1 and c+2 may stay in flight
     __syncthreads();   // chunk c visible to every wave; buffer (c-1) % ring consumed
-    // The loads of chunk c+2 stall the issuing wave until the memory system
+    // The loads of chunk c+3 stall the issuing wave until the memory system
     // takes them (they go out at the gather's rate), so the two waves of a
     // SIMD issue them at different points: waves 0-3 first, waves 4-7 after
     // their softmax.  Each wave's stall then overlaps the other's products.
-    if (!late_issue) issue_chunk(c + kCoreRing - 1);
-    const int bsel = c % kCoreRing;
+    if (!late_issue) issue_chunk(c + kWideRing - 1);
+    const int bsel = c % kWideRing;
     const lds_char_t* buf = lring + bsel * BUF;
     // scores: tile A rows 0-15, tile B rows 16-31, key fragments KD k-steps ahead
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -888,7 +893,7 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] *= alpha;
     }
-    if (late_issue) issue_chunk(c + kCoreRing - 1);
+    if (late_issue) issue_chunk(c + kWideRing - 1);
     // B operand of the PV product: k-slots 0-3 = rows 4g+i, 4-7 = rows 16+4g+i
     bf16x8_t pab;
 #pragma unroll

@@ -357,7 +357,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
     // output absorption reads each split once per column chunk.
     int ns = cdiv(256, T * pl.core_nhb);
     ns = std::min(ns, T > kGemvMaxTokens ? 16 : 64);
-    ns = clampi(ns, cdiv(P, kMaxSplitRows), cdiv(P, kCoreChunk));
+    ns = clampi(ns, cdiv(P, cs.hg == 8 ? kWideMaxSplitRows : kMaxSplitRows), cdiv(P, kCoreChunk));
     pl.ps = cdiv(cdiv(P, ns), kCoreChunk) * kCoreChunk;
     pl.nsplit = cdiv(P, pl.ps);
   }
@@ -449,6 +449,8 @@ int validate_dims(const mla_gd_dims& d) {
   // one token's down-projection row is reduced in LDS; the core's split partials fit its combine
   if ((long long)d.q_lora_rank + KVR > 16384) return MLA_GD_E_UNSUPPORTED;
   if (d.n_prior > 64 * kMaxSplitRows) return MLA_GD_E_UNSUPPORTED;
+  // more than 64 heads: the core stages fewer row ids per split (at most 64 splits)
+  if (d.n_heads > 64 && d.n_prior > 64 * kWideMaxSplitRows) return MLA_GD_E_UNSUPPORTED;
   // flat cache rows and element offsets must fit the kernels' index arithmetic
   if ((long long)d.n_blocks * d.block_size > (1LL << 31) - 1) return MLA_GD_E_UNSUPPORTED;
   if ((long long)d.max_tokens * d.n_prior > (1LL << 31) - 1) return MLA_GD_E_UNSUPPORTED;

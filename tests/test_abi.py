@@ -81,6 +81,10 @@ def _create(lib, d):
     ({"max_tokens": 5000}, "MLA_GD_E_UNSUPPORTED"),
     ({"q_lora_rank": 16384}, "MLA_GD_E_UNSUPPORTED"),
     ({"n_prior": 262144 + 1}, "MLA_GD_E_UNSUPPORTED"),
+    # more than 64 heads: at most 64 core splits of 2560 row ids
+    ({"n_heads": 72, "n_prior": 163840}, "MLA_GD_OK"),
+    ({"n_heads": 72, "n_prior": 163840 + 1}, "MLA_GD_E_UNSUPPORTED"),
+    ({"n_heads": 64, "n_prior": 163840 + 1}, "MLA_GD_OK"),
 ])
 def test_create_validates_dims(lib, kw, code):
     rc, h = _create(lib, _dims(**kw))

@@ -364,6 +364,22 @@ def test_parity_largest_n_prior():
     _run_and_check(MAX_PRIOR)
 
 
+# more than 64 heads: 64 core splits of 2560 rows, the most row ids the
+# 128-head core stages; two tokens (GEMV path) and five (matrix cores)
+MAX_PRIOR_WIDE = replace(MANY_HEADS, name="heads72_max_prior",
+                         shape=replace(MANY_HEADS.shape, n_tokens=2, n_heads=72, n_prior=163840,
+                                       max_blocks_per_seq=11250),
+                         contexts=(170000, 179000), context_range=None, n_duplicates=1000, n_future=1000, seed=2103)
+
+
+@pytest.mark.parametrize("T", [2, 5])
+def test_parity_largest_n_prior_many_heads(T):
+    wl = MAX_PRIOR_WIDE if T == 2 else replace(MAX_PRIOR_WIDE, name="heads72_max_prior_T5",
+                                                shape=replace(MAX_PRIOR_WIDE.shape, n_tokens=5),
+                                                contexts=(170000, 179000, 171000, 175000, 163900), seed=2104)
+    _run_and_check(wl)
+
+
 def test_parity_largest_token_count():
     _run_and_check(MAX_TOKENS)
 
