@@ -263,6 +263,20 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   // as many tiles per workgroup as keep at least 128 workgroups busy
   pl.tpw3 = pl.nct3;
   while (pl.tpw3 > 1 && NH * pl.ntb3 * (pl.nct3 / pl.tpw3) < 128) pl.tpw3 /= 2;
+  // Many heads at a 512-wide latent: one tile of every column, so each weight
+  // row is read whole (1 KB) instead of in 256-byte pieces, with the largest
+  // token block that still gives one workgroup per CU.
+  if (R == 512 && (size_t)cdiv(DN, kMgK) * 2048 <= 48 * 1024) {
+    int m = std::min(pl.mtb, 4);
+    while (m > 1 && NH * cdiv(T, 16 * m) < 256) m /= 2;
+    if (NH * cdiv(T, 16 * m) >= 256 && (size_t)cdiv(DN, kMgK) * m * 2048 <= 48 * 1024) {
+      pl.mtb3 = m;
+      pl.ntb3 = cdiv(T, 16 * m);
+      pl.nca3 = 512;
+      pl.nct3 = 1;
+      pl.tpw3 = 1;
+    }
+  }
   // two m-tiles per workgroup when many heads give enough workgroups: half the
   // weight re-reads across token blocks
   pl.mtb5 = (NH >= 64 && T > 64) ? 2 : 1;
@@ -550,6 +564,7 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsBytes);
   const void* big[] = {(const void*)k_absorb_m<1, 64>, (const void*)k_absorb_m<2, 64>, (const void*)k_absorb_m<4, 64>,
                        (const void*)k_absorb_m<1, 128>, (const void*)k_absorb_m<2, 128>, (const void*)k_absorb_m<4, 128>,
+                       (const void*)k_absorb_m<1, 512>, (const void*)k_absorb_m<2, 512>, (const void*)k_absorb_m<4, 512>,
                        (const void*)k_oabsorb_m<1, 1>, (const void*)k_oabsorb_m<2, 1>,
                        (const void*)k_oabsorb_m<1, 2>, (const void*)k_oabsorb_m<2, 2>};
   for (const void* k : big)
@@ -588,6 +603,7 @@ step_kernel_t pick_oproj_m(int mtb) {
   return mtb == 1 ? k_oproj_m<1> : (mtb == 2 ? k_oproj_m<2> : (mtb == 4 ? k_oproj_m<4> : k_oproj_m<8>));
 }
 step_kernel_t pick_absorb_m(int mtb, int nca) {
+  if (nca == 512) return mtb == 1 ? k_absorb_m<1, 512> : (mtb == 2 ? k_absorb_m<2, 512> : k_absorb_m<4, 512>);
   if (nca == 128) return mtb == 1 ? k_absorb_m<1, 128> : (mtb == 2 ? k_absorb_m<2, 128> : k_absorb_m<4, 128>);
   return mtb == 1 ? k_absorb_m<1, 64> : (mtb == 2 ? k_absorb_m<2, 64> : k_absorb_m<4, 64>);
 }

@@ -328,7 +328,7 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
     }
     return q;
   };
-  constexpr int P = NV == 1 ? 8 : 6;
+  constexpr int P = NV == 1 ? 8 : (NV == 2 ? 6 : 2);  // k-steps of weight pieces loaded ahead
   Pieces<NV> q[P];
   mg_pipe_prologue(q, load);
   if (tid < MTB * 16) beta[tid] = (t0 + tid < T) ? mfma_beta(p, t0 + tid) : 0.f;
