@@ -190,6 +190,9 @@ typedef struct mla_gd_handle mla_gd_handle;
  * qk_nope_head_dim + qk_rope_head_dim a multiple of 4; q_lora_rank +
  * kv_lora_rank + qk_rope_head_dim at most 16384; n_prior at most 262144
  * (163840 with more than 64 heads); max_tokens at most 4096.
+ * If the environment variable MLA_GD_LOG is set (and not "0") at creation,
+ * the first step of each size prints its work decomposition (kernel path,
+ * core shape and splits, GEMM slabs, workspace bytes) to stderr.
  */
 int mla_gather_decode_create(const mla_gd_dims* dims, int device, mla_gd_handle** out_handle);
 

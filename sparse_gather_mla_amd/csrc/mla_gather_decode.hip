@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "../../include/mla_gather_decode.h"
 #include "phases.h"
@@ -170,6 +171,12 @@ struct mla_gd_handle {
   hipGraphExec_t exec;
   bool graph_broken;        // a graph call failed once: launch directly from then on
   unsigned char key[sizeof(mla::StepParams)];  // the captured kernel arguments
+  // workspace_size: ws_most[t] = the largest plan total over steps of 1..t
+  // tokens, filled on first use
+  std::vector<size_t> ws_most;
+  // MLA_GD_LOG set at create: each step size's plan is printed to stderr once
+  bool log_plans;
+  std::vector<bool> logged;
 };
 
 namespace {
@@ -648,6 +655,8 @@ int mla_gather_decode_create(const mla_gd_dims* dims, int device, mla_gd_handle*
   h->exec = nullptr;
   h->graph_broken = false;
   memset(h->key, 0, sizeof(h->key));
+  const char* lg = getenv("MLA_GD_LOG");
+  h->log_plans = lg && *lg && strcmp(lg, "0") != 0;
   *out_handle = h;
   return MLA_GD_OK;
 }
@@ -671,9 +680,13 @@ int mla_gather_decode_last_hip_error(const mla_gd_handle* handle) { return handl
 
 size_t mla_gather_decode_workspace_size(const mla_gd_handle* handle, int32_t n_tokens) {
   if (!handle || n_tokens < 1 || n_tokens > handle->d.max_tokens) return 0;
-  size_t most = 0;
-  for (int t = 1; t <= n_tokens; ++t) most = std::max(most, make_plan(handle->d, t).total);
-  return most;
+  mla_gd_handle* h = const_cast<mla_gd_handle*>(handle);
+  if (h->ws_most.empty()) {  // one plan per step size, once per handle
+    std::vector<size_t> most((size_t)h->d.max_tokens + 1, 0);
+    for (int t = 1; t <= h->d.max_tokens; ++t) most[t] = std::max(most[t - 1], make_plan(h->d, t).total);
+    h->ws_most.swap(most);
+  }
+  return h->ws_most[n_tokens];
 }
 
 int mla_gather_decode_workspace_init(const mla_gd_handle* handle, void* workspace, size_t bytes, void* stream) {
@@ -821,12 +834,35 @@ int read_clear_err(mla_gd_handle* h, void* workspace, hipStream_t s, uint32_t* b
   return w ? MLA_GD_E_DEVICE_CHECK : MLA_GD_OK;
 }
 
+// MLA_GD_LOG: the work decomposition of a step size, once per handle and size.
+void log_plan(mla_gd_handle* h, const Plan& pl) {
+  if (h->logged.size() != (size_t)h->d.max_tokens + 1) h->logged.assign((size_t)h->d.max_tokens + 1, false);
+  if (h->logged[pl.T]) return;
+  h->logged[pl.T] = true;
+  const char* core = pl.core_hg == 8 ? "one 16-head tile per wave, 128 heads per workgroup"
+                                     : (pl.core_rs ? "row-split, 64 heads per workgroup"
+                                                   : (pl.core_hg == 1 ? "16 heads, 4 waves" : "64 heads, 8 waves"));
+  fprintf(stderr, "[mla_gd] T=%d: %s path%s%s; core: %s, %d split(s) of %d rows x %d head block(s) = %d workgroups; workspace %zu bytes\n",
+          pl.T, pl.mfma ? "matrix-core" : "GEMV", pl.single ? ", single launch" : "", pl.fused ? ", fused" : "", core,
+          pl.nsplit, pl.ps, pl.core_nhb, core_grid(pl), pl.total);
+  if (pl.mfma)
+    fprintf(stderr, "[mla_gd]   token blocks of %d x 16 (%d); down %d slabs x %d k-steps; up %d slabs x %d; "
+                    "absorption %d-column tiles, %d per workgroup, blocks of %d x 16; output absorption blocks of %d x 16, "
+                    "%d part(s); o-projection %d slabs x %d\n",
+            pl.mtb, pl.ntb, pl.s1, pl.ks1m, pl.s2, pl.ks2m, pl.nca3, pl.tpw3, pl.mtb3, pl.mtb5, pl.nq5, pl.s6, pl.ks6m);
+  else
+    fprintf(stderr, "[mla_gd]   down %d tiles x %d slabs of %d rows; up %d tiles x %d slabs of %d rows; "
+                    "o-projection %d tiles x %d slabs of %d rows\n",
+            pl.nt1, pl.s1, pl.ks1, pl.nt2, pl.s2, pl.ks2, pl.nt6, pl.s6, pl.ks6);
+}
+
 int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void* workspace,
              size_t workspace_bytes, void* stream, void* const* events, int n_events, bool force_direct = false) {
   if (!h || !tn || !workspace) return MLA_GD_E_INVAL;
   const mla_gd_dims& d = h->d;
   if (n_tokens < 1 || n_tokens > d.max_tokens) return MLA_GD_E_INVAL;
-  const int nk = num_kernels(make_plan(d, n_tokens));
+  const Plan pl = make_plan(d, n_tokens);
+  const int nk = num_kernels(pl);
   if (events && n_events < nk + 1) return MLA_GD_E_INVAL;
   const bool bracket = events && n_events >= 2 * nk;  // a start and an end event per kernel
   if (events)
@@ -844,7 +880,7 @@ int run_step(mla_gd_handle* h, const mla_gd_tensors* tn, int32_t n_tokens, void*
   if (tn->token_seq && !aligned(tn->token_seq, 4)) return MLA_GD_E_ALIGN;
   if (!aligned(workspace, 256)) return MLA_GD_E_ALIGN;
 
-  const Plan pl = make_plan(d, n_tokens);
+  if (h->log_plans) log_plan(h, pl);
   if (pl.off_err != kErrOffset || pl.off_flags != kFlagsOffset) return MLA_GD_E_INVAL;  // layout invariant
   if (workspace_bytes < pl.total) return MLA_GD_E_WORKSPACE;
   if (d.flags & MLA_GD_FLAG_DEBUG_CHECKS) {

@@ -307,3 +307,40 @@ def test_noalloc_step_rejections_before_any_device_work(lib):
         lib.mla_gather_decode_destroy(h)
     src = open(HEADER).read()
     assert "#define MLA_GD_STATIC_SCRATCH_BYTES (32u << 20)" in src
+
+
+def test_plan_log_prints_each_step_size_once():
+    """MLA_GD_LOG set at create: the first step of each size prints its work
+    decomposition to stderr (here steps rejected for a short workspace, after
+    planning and before any device work)."""
+    import subprocess
+    import sys
+    import textwrap
+
+    code = textwrap.dedent("""
+        import ctypes
+        import sparse_gather_mla_amd as sgm
+        from tests.test_abi import _codes, _dims
+        lib = sgm.load_library()
+        h = ctypes.c_void_p()
+        d = _dims(max_tokens=8, n_heads=72, kv_lora_rank=128)
+        assert lib.mla_gather_decode_create(ctypes.byref(d), 0, ctypes.byref(h)) == 0
+        tn = sgm._Tensors()
+        for f in sgm.TENSOR_FIELDS:
+            if f != "gather_rows_out":
+                setattr(tn, f, 4096)
+        ws = ctypes.c_void_p(1 << 20)
+        for T in (1, 5, 1, 5):
+            assert lib.mla_gather_decode_step(h, ctypes.byref(tn), T, ws, 256, None) == _codes()["MLA_GD_E_WORKSPACE"]
+        lib.mla_gather_decode_destroy(h)
+    """)
+    import os
+
+    env = dict(os.environ, MLA_GD_LOG="1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[mla_gd] T=")]
+    assert len(lines) == 2, r.stderr
+    assert lines[0].startswith("[mla_gd] T=1: GEMV path") and "one 16-head tile per wave" in lines[0]
+    assert lines[1].startswith("[mla_gd] T=5: matrix-core path")
