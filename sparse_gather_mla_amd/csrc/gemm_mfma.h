@@ -9,8 +9,9 @@
 // projections stay bound by the weight stream even with the matrix work doubled.
 //
 // Tiles: 16 tokens (an m-tile) x NC columns (64 to 256) x 32 k (a k-step).  A
-// workgroup of four waves owns one NC-column tile, one K slab and a block of
-// MTB m-tiles; the waves split the block 2 x 2 (1 x 4 for a single m-tile).
+// workgroup owns one NC-column tile, one K slab and a block of MTB m-tiles;
+// four waves split the block 2 x 2 (1 x 4 for a single m-tile), eight waves
+// (128-token blocks) 2 x 4.
 //
 // Both operands are loaded into registers several k-steps ahead of use (16-byte
 // global loads, non-temporal for the weight) and written to one of two LDS
@@ -87,18 +88,23 @@ __device__ __forceinline__ void put_a4_lds(char* ares, int mtb, int tt, int k, c
 // activation bytes per weight byte (the activation, hi and lo, is as large per
 // k as a 128-column weight row at 64 tokens).
 __host__ __device__ constexpr int mg_cols(int mtb) { return mtb >= 4 ? 256 : 128; }
+// Waves per GEMM workgroup: eight for 128-token blocks (two per SIMD, so one
+// wave's loads, stores and barrier waits overlap the other's products; four
+// waves held 368 registers each and ran one per SIMD), four otherwise.
+__host__ __device__ constexpr int mg_waves(int mtb) { return mtb >= 8 ? 8 : 4; }
 
-template <int MTB, int NC = mg_cols(MTB)>
+template <int MTB, int NC = mg_cols(MTB), int NW = mg_waves(MTB)>
 struct Mg {
+  static constexpr int kThreads = 64 * NW;
   static constexpr int WM = MTB >= 2 ? 2 : 1;  // waves along tokens
-  static constexpr int WN = 4 / WM;            // waves along columns
+  static constexpr int WN = NW / WM;           // waves along columns
   static constexpr int MTW = MTB / WM;         // m-tiles per wave
   static constexpr int NTW = NC / 16 / WN;     // 16-column n-tiles per wave
   static constexpr int kABytes = MTB * 2 * kAFragElems * 2;
   static constexpr int kBBytes = kMgK * NC * 2;
   static constexpr int kStep = kABytes + kBBytes;
-  static constexpr int kAPieces = (MTB * 128 + 255) / 256;  // A pieces per lane per step
-  static constexpr int kBPieces = NC / 64;                   // B pieces per lane per step
+  static constexpr int kAPieces = (MTB * 128 + kThreads - 1) / kThreads;  // A pieces per lane per step
+  static constexpr int kBPieces = NC * 4 / kThreads;                       // B pieces per lane per step
   static constexpr int kPieces = kAPieces + kBPieces;
   static constexpr int kAhead = NC >= 256 ? 3 : 6;           // k-steps loaded ahead into registers
   static constexpr int kStage = 2 * kStep;                   // two LDS stage buffers
@@ -133,21 +139,21 @@ __device__ __forceinline__ u32x4_t load16_nt(const bf16_t* src) {
 __device__ __forceinline__ void store16(char* dst, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(dst) = v; }
 
 // This lane's pieces of a 32 x NC weight tile at k-step 0.  Piece i is LDS
-// slot q = 256 i + tid: row r = q / (NC/8), swizzled 16-byte column piece.
-template <int NC>
+// slot q = NTHR i + tid: row r = q / (NC/8), swizzled 16-byte column piece.
+template <int NC, int NTHR = kBlock>
 struct BTileSrc {
-  const bf16_t* p[NC / 64];  // nullptr: the piece's columns lie past N
-  int row[NC / 64];          // the piece's row at k-step 0; rows >= K read as zeros
-  size_t step;               // elements per k-step
+  const bf16_t* p[NC * 4 / NTHR];  // nullptr: the piece's columns lie past N
+  int row[NC * 4 / NTHR];          // the piece's row at k-step 0; rows >= K read as zeros
+  size_t step;                     // elements per k-step
   int K;
 };
 
-template <int NC>
-__device__ __forceinline__ BTileSrc<NC> btile_src(const bf16_t* W, int K, int N, int k0, int c0) {
-  BTileSrc<NC> s;
+template <int NC, int NTHR = kBlock>
+__device__ __forceinline__ BTileSrc<NC, NTHR> btile_src(const bf16_t* W, int K, int N, int k0, int c0) {
+  BTileSrc<NC, NTHR> s;
 #pragma unroll
-  for (int i = 0; i < NC / 64; ++i) {
-    const int q = i * 256 + threadIdx.x;
+  for (int i = 0; i < NC * 4 / NTHR; ++i) {
+    const int q = i * NTHR + threadIdx.x;
     const int r = q / (NC / 8), pc = bswz(q % (NC / 8), r);
     const int col = c0 + 8 * pc;
     s.p[i] = (col < N) ? W + (size_t)(k0 + r) * N + col : nullptr;
@@ -159,10 +165,10 @@ __device__ __forceinline__ BTileSrc<NC> btile_src(const bf16_t* W, int K, int N,
 }
 
 // One k-step: B fragments by transposing reads, A fragments (hi, lo), MFMAs.
-template <int MTB, int NC>
+template <int MTB, int NC, int NW = mg_waves(MTB)>
 __device__ __forceinline__ void mg_step(const char* bufA, const char* bufB,
-                                        f32x4_t (&acc)[Mg<MTB, NC>::MTW][Mg<MTB, NC>::NTW]) {
-  using S = Mg<MTB, NC>;
+                                        f32x4_t (&acc)[Mg<MTB, NC, NW>::MTW][Mg<MTB, NC, NW>::NTW]) {
+  using S = Mg<MTB, NC, NW>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::WN, wn = wave % S::WN;
   const int g = lane >> 4, l16 = lane & 15;
@@ -238,16 +244,17 @@ __device__ __forceinline__ void mg_pipe(int nsteps, char* stage, int step_bytes,
 
 // acc = A[token block] @ W[k0 : k0 + 32*nks, c0 : c0 + NC] with A from a
 // global fragment-order buffer (its m-tiles mt0 .. mt0+MTB-1).
-template <int MTB, int NC = mg_cols(MTB)>
+template <int MTB, int NC = mg_cols(MTB), int NW = mg_waves(MTB)>
 __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, const bf16_t* W, int K, int N, int k0,
                                       int nks, int c0, const bf16_t* zero16, char* stage,
-                                      f32x4_t (&acc)[Mg<MTB, NC>::MTW][Mg<MTB, NC>::NTW]) {
-  using S = Mg<MTB, NC>;
+                                      f32x4_t (&acc)[Mg<MTB, NC, NW>::MTW][Mg<MTB, NC, NW>::NTW]) {
+  using S = Mg<MTB, NC, NW>;
+  constexpr int NTHR = S::kThreads;
 #pragma unroll
   for (int mt = 0; mt < S::MTW; ++mt)
 #pragma unroll
     for (int nt = 0; nt < S::NTW; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const BTileSrc<NC> bs = btile_src<NC>(W, K, N, k0, c0);
+  const BTileSrc<NC, NTHR> bs = btile_src<NC, NTHR>(W, K, N, k0, c0);
   const int ks0 = k0 / kMgK;
   const int tid = threadIdx.x;
   const bf16_t* Ab = A + ((size_t)ks0 * mt_pad + mt0) * (2 * kAFragElems) + (size_t)tid * 8;
@@ -262,7 +269,7 @@ __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, cons
 #pragma unroll
         for (int i = 0; i < S::kAPieces; ++i) {
           const bf16_t* src = zero16;
-          if (live && i * 256 + tid < MTB * 128) src = Ab + astep * st + i * 256 * 8;
+          if (live && i * NTHR + tid < MTB * 128) src = Ab + astep * st + i * NTHR * 8;
           r.v[i] = load16(src);
         }
 #pragma unroll
@@ -276,20 +283,20 @@ __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, cons
       [&](const Pieces<S::kPieces>& r, char* buf) {
 #pragma unroll
         for (int i = 0; i < S::kAPieces; ++i)
-          if (i * 256 + tid < MTB * 128) store16(buf + (i * 256 + tid) * 16, r.v[i]);
+          if (i * NTHR + tid < MTB * 128) store16(buf + (i * NTHR + tid) * 16, r.v[i]);
 #pragma unroll
-        for (int i = 0; i < S::kBPieces; ++i) store16(buf + S::kABytes + (i * 256 + tid) * 16, r.v[S::kAPieces + i]);
+        for (int i = 0; i < S::kBPieces; ++i) store16(buf + S::kABytes + (i * NTHR + tid) * 16, r.v[S::kAPieces + i]);
       },
-      [&](int, const char* buf) { mg_step<MTB, NC>(buf, buf + S::kABytes, acc); });
+      [&](int, const char* buf) { mg_step<MTB, NC, NW>(buf, buf + S::kABytes, acc); });
 }
 
 // Lane (g, l16) of a wave holds out[token l16][columns 4g .. 4g+3] of each
 // 16x16 output tile (the products are taken transposed).  Visits (token,
 // first column, four values) of the wave's tiles for a block starting at token t0.
-template <int MTB, int NC = mg_cols(MTB), class F>
-__device__ __forceinline__ void mg_for_outputs4(const f32x4_t (&acc)[Mg<MTB, NC>::MTW][Mg<MTB, NC>::NTW], int t0,
-                                                int c0, F&& f) {
-  using S = Mg<MTB, NC>;
+template <int MTB, int NC = mg_cols(MTB), int NW = mg_waves(MTB), class F>
+__device__ __forceinline__ void mg_for_outputs4(const f32x4_t (&acc)[Mg<MTB, NC, NW>::MTW][Mg<MTB, NC, NW>::NTW],
+                                                int t0, int c0, F&& f) {
+  using S = Mg<MTB, NC, NW>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::WN, wn = wave % S::WN;
   const int g = lane >> 4, l16 = lane & 15;

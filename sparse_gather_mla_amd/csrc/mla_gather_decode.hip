@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kBlock) void k_prep(StepParams p) {
 }
 
 template <int MTB>
-__global__ __launch_bounds__(kBlock) void k_down_m(StepParams p) {
+__global__ __launch_bounds__(64 * mg_waves(MTB)) void k_down_m(StepParams p) {
   __shared__ __attribute__((aligned(16))) char stage[Mg<MTB>::kStage];
   phase_down_m<MTB>(p, blockIdx.x, stage);
 }
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kBlock) void k_qa(StepParams p) {
 }
 
 template <int MTB>
-__global__ __launch_bounds__(kBlock) void k_qup_m(StepParams p) {
+__global__ __launch_bounds__(64 * mg_waves(MTB)) void k_qup_m(StepParams p) {
   __shared__ __attribute__((aligned(16))) char stage[Mg<MTB>::kStage];
   phase_qup_m<MTB>(p, blockIdx.x, stage);
 }
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kBlock) void k_oabsorb_m(StepParams p) {
 }
 
 template <int MTB>
-__global__ __launch_bounds__(kBlock) void k_oproj_m(StepParams p) {
+__global__ __launch_bounds__(64 * mg_waves(MTB)) void k_oproj_m(StepParams p) {
   __shared__ __attribute__((aligned(16))) char stage[Mg<MTB>::kStage];
   phase_oproj_m<MTB>(p, blockIdx.x, stage);
 }
@@ -766,13 +766,14 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     L(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll);
   } else {
     L(k_prep, dim3(pl.n_idx_wg + T * pl.nxc), blk, 1024);
-    L(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), blk, 0);
+    const dim3 gblk(64 * mg_waves(pl.mtb));  // GEMM workgroups: eight waves for 128-token blocks
+    L(pick_down_m(pl.mtb), dim3(mg_grid(pl.nt1m * pl.s1, pl.ntb)), gblk, 0);
     L(k_qa, dim3(T * (pl.nqc + 1)), blk, gl);
-    L(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), blk, 0);
+    L(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), gblk, 0);
     L(pick_absorb_m(pl.mtb3, pl.nca3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk, absorb_lds_bytes(pl, p.DN));
     L(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0);
     L(pick_oabsorb_m(pl.mtb5, pl.q5), dim3(mg_grid(p.NH * pl.nq5, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R));
-    L(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), blk, 0);
+    L(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), gblk, 0);
     L(k_out, dim3(pl.n7), blk, gl);
   }
   hipError_t e = L.finish();
