@@ -88,10 +88,11 @@ __device__ __forceinline__ void put_a4_lds(char* ares, int mtb, int tt, int k, c
 // activation bytes per weight byte (the activation, hi and lo, is as large per
 // k as a 128-column weight row at 64 tokens).
 __host__ __device__ constexpr int mg_cols(int mtb) { return mtb >= 4 ? 256 : 128; }
-// Waves per GEMM workgroup: eight for 128-token blocks (two per SIMD, so one
-// wave's loads, stores and barrier waits overlap the other's products; four
-// waves held 368 registers each and ran one per SIMD), four otherwise.
-__host__ __device__ constexpr int mg_waves(int mtb) { return mtb >= 8 ? 8 : 4; }
+// Waves per GEMM workgroup: eight for blocks of 64 and 128 tokens (two per
+// SIMD, so one wave's loads, stores and barrier waits overlap the other's
+// products; with four waves a 128-token block held 368 registers a wave and
+// ran one wave per SIMD), four for smaller blocks.
+__host__ __device__ constexpr int mg_waves(int mtb) { return mtb >= 4 ? 8 : 4; }
 
 template <int MTB, int NC = mg_cols(MTB), int NW = mg_waves(MTB)>
 struct Mg {

@@ -291,7 +291,7 @@ __device__ __forceinline__ void rope_q(const StepParams& p, int t, int h, int i,
 
 template <int MTB, int NCA>
 __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
-  using S = Mg<MTB, NCA>;
+  using S = Mg<MTB, NCA, 4>;  // four waves: the loads below index by kBlock
   constexpr int NV = NCA / 64;  // 16-byte weight pieces per lane per step
   const Plan& pl = p.pl;
   const int ngrp = pl.nct3 / pl.tpw3;
@@ -378,9 +378,9 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
       },
       [&](int st, const char* buf) {
         const int j = j0 + st / KS, ks = st % KS;
-        mg_step<MTB, NCA>(ares + ks * S::kABytes, buf, acc);
+        mg_step<MTB, NCA, 4>(ares + ks * S::kABytes, buf, acc);
         if (ks == KS - 1) {  // tile j complete
-          mg_for_outputs4<MTB, NCA>(acc, t0, j * NCA, [&](int t, int c, const f32x4_t& v) {
+          mg_for_outputs4<MTB, NCA, 4>(acc, t0, j * NCA, [&](int t, int c, const f32x4_t& v) {
             if (t < T) {  // four bf16 in one 8-byte store (KVR % 8 == 0, c % 4 == 0)
               const float sl = p.scale_log2;
               const uint2 w = make_uint2(pack_bf16x2(f32_to_bf16(v[0] * sl), f32_to_bf16(v[1] * sl)),

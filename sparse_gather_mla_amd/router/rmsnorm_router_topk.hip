@@ -149,7 +149,7 @@ __device__ __attribute__((aligned(16))) uint16_t g_zero16[8] = {};
 __global__ __launch_bounds__(kBlock) void k_rt_partial_m(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
                                                         const uint16_t* __restrict__ W, int T, int H, int E, int ntile,
                                                         int ntb, int kt, int ks, int s, float* __restrict__ part) {
-  using S = Mg<kMtb>;
+  using S = Mg<kMtb, mg_cols(kMtb), 4>;
   constexpr int NC = mg_cols(kMtb);
   static_assert(S::kBPieces == 2 && kMtb * 16 * kMgK == 4 * kBlock, "one x piece per thread and k-step");
   __shared__ __attribute__((aligned(16))) char stage[S::kStage];
@@ -191,9 +191,9 @@ __global__ __launch_bounds__(kBlock) void k_rt_partial_m(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < 2; ++i) store16(buf + S::kABytes + (i * kBlock + tid) * 16, r.v[i]);
       },
-      [&](int, const char* buf) { mg_step<kMtb, NC>(buf, buf + S::kABytes, acc); });
+      [&](int, const char* buf) { mg_step<kMtb, NC, 4>(buf, buf + S::kABytes, acc); });
   float* out = part + (size_t)slab * T * E;
-  mg_for_outputs4<kMtb>(acc, t0, c0, [&](int t, int c, const f32x4_t& v) {
+  mg_for_outputs4<kMtb, NC, 4>(acc, t0, c0, [&](int t, int c, const f32x4_t& v) {
     if (t < T) store_f32x4(out + (size_t)t * E, c, E, v);
   });
 }
