@@ -11,7 +11,9 @@ resident in HBM before timing starts.  By default the line's ``value`` is the
 DeepSeek-V3.2 slice (one token, 16 heads, n_prior 2048); ``configs`` holds the
 same measurements for the other n_prior = 2048 workloads (32 tokens x 16
 heads, 64 and 128 tokens x 128 heads), ``fused_ablation`` the single-launch
-kv-row/absorption/core variant, ``copy_GBps`` a plain device copy's bandwidth.
+kv-row/absorption/core variant, ``single_launch_ablation`` the whole step as
+one launch, ``router`` the fused RMSNorm + router top-K at one and 128 tokens,
+``copy_GBps`` a plain device copy's bandwidth.
 
 Timing: W warm-up steps, then K timed steps, every one of them preceded by a
 read and write of a 1 GiB buffer so that neither the L2s nor the 256 MB
@@ -239,8 +241,15 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, workload: str) -> int:
 
 def router_bench(args) -> int:
     """Cold latency of the fused RMSNorm + router top-K (two kernels), with the
-    roofline of its GEMV kernel and the oracle timed on the host."""
+    roofline of the whole call and the oracle timed on the host: one JSON line."""
     import json as _json
+
+    print(_json.dumps(router_measure(args.router, args.steps, args.warmup, args.cpu_budget)), flush=True)
+    return 0
+
+
+def router_measure(name: str, steps: int, warmup: int, cpu_budget: float) -> dict:
+    """The router line of ``router_bench`` as a dict (also nested in the default run's line)."""
     import statistics
     import time
 
@@ -251,7 +260,7 @@ def router_bench(args) -> int:
     from sparse_gather_mla_amd.router import rmsnorm_router_topk, workspace_size
     from workload import ROUTER_CONFIGS, make_router_inputs
 
-    T, H, E, K = ROUTER_CONFIGS[args.router]
+    T, H, E, K = ROUTER_CONFIGS[name]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = make_router_inputs(T, H, E, seed=31, with_bias=True)
@@ -265,12 +274,12 @@ def router_bench(args) -> int:
         rmsnorm_router_topk(g["hidden_states"], g["gamma"], g["router_weights"], g["router_bias"], 1e-6, K,
                             "sigmoid", workspace=ws, out=out)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         flush.add_(1.0)
         run()
     torch.cuda.synchronize()
     ev = []
-    for _ in range(args.steps):
+    for _ in range(steps):
         flush.add_(1.0)  # cold: evicts the L2s and the Infinity Cache
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -278,7 +287,8 @@ def router_bench(args) -> int:
         b.record()
         ev.append((a, b))
     torch.cuda.synchronize()
-    us = statistics.mean(a.elapsed_time(b) for a, b in ev) * 1e3
+    call_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    us = statistics.mean(call_us)
     # algorithmic bytes: weights, hidden states (read twice: GEMV and the normalised
     # write), gamma, bias, and the three outputs
     alg = 2 * H * E + 2 * 2 * T * H + 2 * H + 4 * E + 2 * T * H + 4 * T * K + 2 * T * E
@@ -287,7 +297,7 @@ def router_bench(args) -> int:
     gam, w = inp["gamma"].to(torch.float64).numpy(), inp["router_weights"].to(torch.float64).numpy()
     bias = inp["router_bias"].to(torch.float64).numpy()
     t0, n = time.perf_counter(), 0
-    while time.perf_counter() - t0 < min(args.cpu_budget, 10.0) or n == 0:
+    while time.perf_counter() - t0 < min(cpu_budget, 10.0) or n == 0:
         ro.rmsnorm_router_topk(x, gam, w, bias, 1e-6, K, ro.SIGMOID)
         n += 1
     cpu_us = (time.perf_counter() - t0) / n * 1e6
@@ -296,10 +306,12 @@ def router_bench(args) -> int:
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = 1
+    q = np.percentile(call_us, [10, 50, 90])
     line = {"metric": "rmsnorm_router_topk_latency", "value": round(us, 3), "unit": "us", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": us / 1e3, "higher_is_better": False,
+            "steps": steps, "warmup": warmup, "ms_per_step": us / 1e3, "higher_is_better": False,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": f"{args.router}: T={T}, H={H}, E={E}, top_k={K}, sigmoid, bias",
+            "us_p10_p50_p90": [round(x, 3) for x in q],
+            "config": {"workload": f"{name}: T={T}, H={H}, E={E}, top_k={K}, sigmoid, bias",
                        "cache_state": "cold (1 GiB flush per call)"},
             "roofline": {"bound": "hbm", "kernel": "whole call (k_rt_partial + k_rt_select)",
                          "achieved": round(alg / us / 1e3, 1), "peak": 8000.0, "unit": "GB/s",
@@ -307,8 +319,9 @@ def router_bench(args) -> int:
                          "gemv_alg_bytes": gemv_alg},
             "cpu_baseline": {"value": round(cpu_us, 1), "unit": "us", "cores": cores, "kind": "oracle",
                              "sample": f"{n} whole calls, fp64 numpy"}}
-    print(_json.dumps(line), flush=True)
-    return 0
+    del g, out, ws, flush
+    torch.cuda.empty_cache()
+    return line
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -592,6 +605,13 @@ def main() -> int:
             c = measure_config(name, k, args.warmup, cpu_budget=budget / 2)
             c["pct_of_copy_bandwidth"] = round(100 * c["achieved_GBps"] / copy_gbps, 2)
             res["configs"][name] = c
+        # the widening beside the step: the fused RMSNorm + MoE router top-K (mean of cold calls)
+        res["router"] = {}
+        for name in ("router_t1", "router_t128"):
+            print(f"[bench] {name}: {args.warmup} + {args.steps} cold calls", file=sys.stderr, flush=True)
+            r = router_measure(name, args.steps, args.warmup, min(budget, 2.0))
+            res["router"][name] = {k: r[k] for k in ("value", "unit", "us_p10_p50_p90", "config", "roofline",
+                                                     "cpu_baseline")}
     print(json.dumps(res), flush=True)
     return 0
 
