@@ -121,6 +121,7 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 // Hooks of the separately launched core: every input is complete at kernel
 // start, and the results are read by a later kernel.
 struct CoreNoWait {
+  static constexpr bool kEarlyQ = true;  // the query tiles may load before the row ids
   __device__ void before_rows(int) const {}
   __device__ void before_q(int) const {}
   __device__ __forceinline__ void st(float* p, float v) const { *p = v; }
@@ -128,7 +129,9 @@ struct CoreNoWait {
 
 // Hooks: before_rows(token) runs before the first read of the row ids or the
 // cache; before_q(first head) after the first row loads are issued and before
-// the query tiles are read.  Every thread of the workgroup calls both.
+// the query tiles are read (kEarlyQ: the tiles are complete at kernel start, so
+// they load first, before the row ids).  Every thread of the workgroup calls
+// both.
 // st(p, v) stores one of the split's results (m, l, o).
 // RING chunk buffers are in flight (1: each chunk is loaded after the previous
 // one is consumed); MAXR is the most rows a split may hold.
@@ -180,19 +183,37 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   const int hbase = (hb * HG + hg) * 16;
   const int head = hbase + l16;  // this lane's head for Q fragments and softmax state
 
+  // this wave's k-steps: kk = kb + j for j < nj (nj may be smaller than KSW,
+  // or not positive for the last waves of a short row)
+  const int kb = cs * KSW;
+  const int nj = min(KSW, ks - kb);
+  const int nlive = (ks + KSW - 1) / KSW;  // waves holding score k-steps
+  // Q fragments: lane l holds Qcat[head][32*kk + 8*g .. +8] (B operand of the score product)
+  bf16x8_t qf[KSW];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int j = 0; j < KSW; ++j) {
+      const int k = 32 * (kb + j) + 8 * g;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (j < nj && head < p.NH && k < KVR)
+        v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * p.NH + head) * KVR + k);
+      qf[j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  };
+  if constexpr (Hooks::kEarlyQ) load_q();  // its round trip overlaps the row ids'
+
   hooks.before_rows(t);
   // this split's flat row ids (-1: causally masked, or past the split)
   for (int i = tid; i < nchunks * kCoreChunk; i += NW * 64)
     ids[i] = (i < nrows) ? p.rows[(size_t)t * p.P + j0 + i] : -1;
   __syncthreads();  // row ids visible
 
-  // this wave's k-steps: kk = kb + j for j < nj (nj may be smaller than KSW)
-  const int kb = cs * KSW;
-  const int nj = min(KSW, ks - kb);
-
   // Direct global->LDS loads of chunk c into ring buffer c % RING.  Every
   // wave issues exactly NI loads per chunk (slots past the buffer go to the
-  // sink) so that the vmcnt arithmetic below is static.  Per-lane geometry,
+  // sink) so that the vmcnt arithmetic below is static.  Chunks past the
+  // split's last are not loaded (each DMA instruction holds the issuing wave
+  // for about as long whatever it reads); the waits below count only the
+  // chunks that were.  Per-lane geometry,
   // the same for every chunk: the row inside the chunk of the piece this lane
   // loads (-1: zeros) and its byte offset in the cache row.
   int lrow[NI], lofs[NI];
@@ -235,21 +256,12 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   float m_run = -INFINITY, l_run = 0.f;
 
 #pragma unroll
-  for (int c = 0; c < (RING > 1 ? RING - 1 : 1); ++c) issue_chunk(c);
+  for (int c = 0; c < (RING > 1 ? RING - 1 : 1); ++c)
+    if (c < nchunks) issue_chunk(c);
 
   hooks.before_q(hb * HG * 16);
-  // Q fragments: lane l holds Qcat[head][32*kk + 8*g .. +8] (B operand of the score product)
-  bf16x8_t qf[KSW];
-#pragma unroll
-  for (int j = 0; j < KSW; ++j) {
-    const int k = 32 * (kb + j) + 8 * g;
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (j < nj && head < p.NH && k < KVR)
-      v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * p.NH + head) * KVR + k);
-    qf[j] = __builtin_bit_cast(bf16x8_t, v);
-  }
-  // loads return in order: the Q fragments land after the first ring chunks,
-  // so nothing but ring loads is outstanding below
+  if constexpr (!Hooks::kEarlyQ) load_q();
+  // nothing but ring loads is outstanding below
   wait_vmcnt<0>();
 
   // LDS-space views (addresses fold into the instructions' offset fields)
@@ -264,10 +276,14 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
 
   for (int c = 0; c < nchunks; ++c) {
     if constexpr (RING > 1) {
-      // chunk c's loads are this wave's oldest; the younger chunk may stay in flight
-      wait_vmcnt<NI * (RING - 2)>();
+      // chunk c's loads are this wave's oldest; the younger chunk, if it was
+      // loaded, may stay in flight
+      if (c + RING - 2 < nchunks)
+        wait_vmcnt<NI * (RING - 2)>();
+      else
+        wait_vmcnt<0>();
       __syncthreads();  // chunk c visible to every wave; buffer (c-1) % ring consumed
-      issue_chunk(c + RING - 1);
+      if (c + RING - 1 < nchunks) issue_chunk(c + RING - 1);
     } else {
       if (c > 0) {  // chunk 0 was issued before the query tiles were read
         __syncthreads();  // every wave is done with chunk c-1's buffer and bias
@@ -303,29 +319,50 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
           fa1 = fa2; fb1 = fb2;
           __builtin_amdgcn_sched_barrier(0);
         }
-      } else {  // the last column split of a short row: fewer live k-steps
+      } else {  // the last column splits of a short row: fewer live k-steps
+        // (fragments past the last live one reload it: every read stays in
+        // the buffer, and only live k-steps reach the matrix cores)
+        const int jl = max(nj - 1, 0);
+        bf16x8_t fa0 = ld(pa, 0), fb0 = ld(pb, 0), fa1 = fa0, fb1 = fb0;
+        if (KSW > 1) {
+          fa1 = ld(pa, min(1, jl));
+          fb1 = ld(pb, min(1, jl));
+        }
 #pragma unroll
         for (int j = 0; j < KSW; ++j) {
-          if (j < nj) {
-            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld(pa, j), qf[j], sa, 0, 0, 0);
-            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld(pb, j), qf[j], sb, 0, 0, 0);
+          bf16x8_t fa2 = fa1, fb2 = fb1;
+          if (j + 2 < KSW) {
+            fa2 = ld(pa, min(j + 2, jl));
+            fb2 = ld(pb, min(j + 2, jl));
           }
+          if (j < nj) {
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, qf[j], sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb0, qf[j], sb, 0, 0, 0);
+          }
+          fa0 = fa1; fb0 = fb1;
+          fa1 = fa2; fb1 = fb2;
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
     if constexpr (CS > 1) {
-      // add the group's partial score tiles, in wave order (identical in every wave)
+      // add the group's partial score tiles, in wave order (identical in every
+      // wave); waves past the last k-step hold none
       f32x4_t* mine = sx + ((hg * CS + cs) * 2) * 64;
-      mine[lane] = sa;
-      mine[64 + lane] = sb;
+      if (cs < nlive) {
+        mine[lane] = sa;
+        mine[64 + lane] = sb;
+      }
       __syncthreads();
       const f32x4_t* grp = sx + (hg * CS * 2) * 64;
       sa = grp[lane];
       sb = grp[64 + lane];
 #pragma unroll
       for (int w = 1; w < CS; ++w) {
-        sa += grp[w * 128 + lane];
-        sb += grp[w * 128 + 64 + lane];
+        if (w < nlive) {
+          sa += grp[w * 128 + lane];
+          sb += grp[w * 128 + 64 + lane];
+        }
       }
     }
     // rows 4g+i (tile A) and 16+4g+i (tile B): masked rows carry -inf
@@ -390,7 +427,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  wait_vmcnt<0>();  // the trailing loads (zero rows into unused buffers or the sink)
+  wait_vmcnt<0>();  // every chunk loaded was waited for; kept as a guard
 
   // this split's partial result; waves of one head group hold identical (m, l)
   const size_t pb = ((size_t)t * pl.nsplit + split) * p.NH;

@@ -202,11 +202,14 @@ struct CoreShape {
   int hg, cs;
 };
 
-// <= 16 heads: one head group, four waves splitting the latent columns;
-// otherwise four head groups (64 heads) per workgroup, two waves per group
-// splitting the latent columns.
-CoreShape core_shape(int n_heads) {
-  return n_heads <= 16 ? CoreShape{1, 4} : (n_heads <= 64 ? CoreShape{4, 2} : CoreShape{8, 1});
+// <= 16 heads: one head group, eight waves (four below a 512-wide latent)
+// splitting the latent columns and the score k-steps; 17-64 heads: four head
+// groups per workgroup, two waves per group; more: eight head groups, one
+// wave each.  Eight waves against four for 16 heads at the 512-wide latent
+// (cold kernel time): 7.3 against 8.4 us at one token, 23.0 against 23.4 at
+// 32 tokens.
+CoreShape core_shape(int n_heads, int R) {
+  return n_heads <= 16 ? CoreShape{1, R >= 512 ? 8 : 4} : (n_heads <= 64 ? CoreShape{4, 2} : CoreShape{8, 1});
 }
 
 int core_grid(const Plan& pl) { return cdiv(pl.T * pl.nsplit, 8) * 8 * pl.core_nhb; }
@@ -365,7 +368,7 @@ Plan make_plan(const mla_gd_dims& d, int T) {
   choose_split(Q, pl.nt2, &pl.s2, &pl.ks2);
   pl.nkv = cdiv(KVR, 64);
   pl.ncc3 = R / 64;
-  const CoreShape cs = core_shape(NH);
+  const CoreShape cs = core_shape(NH, R);
   pl.core_hg = cs.hg;
   pl.core_cs = cs.cs;
   pl.core_nhb = cdiv(NH, 16 * cs.hg);
@@ -383,8 +386,9 @@ Plan make_plan(const mla_gd_dims& d, int T) {
     pl.nsplit = cdiv(P, pl.ps);
   }
   if (T > kGemvMaxTokens) return make_plan_mfma(d, pl);
-  pl.fused = (d.flags & MLA_GD_FLAG_FUSED) && pl.core_hg == 1 && pl.core_cs == 4;
-  pl.single = (d.flags & MLA_GD_FLAG_SINGLE_LAUNCH) && pl.core_hg == 1 && pl.core_cs == 4;
+  pl.fused = (d.flags & MLA_GD_FLAG_FUSED) && pl.core_hg == 1;
+  pl.single = (d.flags & MLA_GD_FLAG_SINGLE_LAUNCH) && pl.core_hg == 1;
+  if (pl.fused || pl.single) pl.core_cs = 4;  // their core runs in 256-thread workgroups
   if (pl.single) {
     // splits of at most kSingleMaxRows rows (the single launch's core stages fewer row ids)
     const int ns = std::max(pl.nsplit, cdiv(P, kSingleMaxRows));
@@ -533,7 +537,8 @@ core_kernel_t pick_core(const Plan& pl, int R) {
       default: return k_core_rs<32>;
     }
   }
-  return pl.core_hg == 1 ? pick_core_nt<1, 4>(R / 16) : pick_core_nt<4, 2>(R / 16);
+  if (pl.core_hg == 1) return pl.core_cs == 8 ? k_core<32, 1, 8> : pick_core_nt<1, 4>(R / 16);
+  return pick_core_nt<4, 2>(R / 16);
 }
 
 // Kernels of a step, in launch order: the GEMV path (few tokens) and the matrix-core path.

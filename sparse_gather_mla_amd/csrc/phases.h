@@ -510,6 +510,7 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
 // ---------------------------------------------------------------------------
 template <int NT, int HG, int CS>
 struct CoreWaitFused {
+  static constexpr bool kEarlyQ = false;  // the query tiles are produced in the same launch
   const StepParams& p;
   // one wave polls, fences (invalidating the CU's L1 and stale L2 lines for
   // every wave of the workgroup), then releases the others at the barrier

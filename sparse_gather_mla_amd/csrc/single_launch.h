@@ -46,6 +46,7 @@ constexpr int single_lds_bytes() {
 // are out.  All of them are read with ordinary loads: each wait covers every
 // producer of the lines read.
 struct CoreWaitSingle {
+  static constexpr bool kEarlyQ = false;  // the query tiles are produced in the same launch
   const StepParams& p;
   unsigned e;
   __device__ void before_rows(int) const {

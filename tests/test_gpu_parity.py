@@ -502,8 +502,9 @@ def test_parity_one_far_larger_score_late_in_a_split():
 
 # ---------------------------------------------------------------------------
 # the single-launch variant: the whole step as one kernel (<= 3 tokens,
-# <= 16 heads).  Its arithmetic is the separate kernels' (the same splits and
-# reduction orders), so besides the oracle bar it must give the same bits.
+# <= 16 heads).  Its arithmetic is the fused variant's (the same phases,
+# splits, reduction orders and four-wave core), so besides the oracle bar it
+# must give the same bits; below a 512-wide latent also the separate kernels'.
 # ---------------------------------------------------------------------------
 _BATCH32 = next(c for c in CONFIGS if c.name == "batch32")
 RAGGED13 = replace(RAGGED, name="ragged_nh13", shape=replace(RAGGED.shape, n_heads=13), seed=4401)
@@ -520,13 +521,20 @@ SINGLE_CASES = [
 @pytest.mark.parametrize("wl", SINGLE_CASES, ids=[w.name for w in SINGLE_CASES])
 def test_parity_single_launch(wl):
     out, ref, inp, g = _run_and_check(wl, single=True)
-    # the separate kernels on the same inputs (the step rewrites the same rows
-    # with the same values) give the same bits
-    sep = MlaGatherDecode(Dims.from_shape(wl.shape), max_tokens=wl.shape.n_tokens)
-    assert sep.kernel_names(wl.shape.n_tokens)[0] == "k_down"
-    out_sep = sep(g)
+    # the fused variant on the same inputs (the step rewrites the same rows
+    # with the same values) gives the same bits: the same phases, splits and
+    # four-wave core.  (The separately launched core takes eight waves at a
+    # 512-wide latent, so its score sums round in another order.)
+    fz = MlaGatherDecode(Dims.from_shape(wl.shape), max_tokens=wl.shape.n_tokens, fused=True)
+    assert fz.kernel_names(wl.shape.n_tokens)[2] == "k_absorb_core"
+    out_fz = fz(g)
     torch.cuda.synchronize()
-    assert torch.equal(out, out_sep)
+    assert torch.equal(out, out_fz)
+    if wl.shape.kv_lora_rank < 512:  # the separate kernels' core has four waves too
+        sep = MlaGatherDecode(Dims.from_shape(wl.shape), max_tokens=wl.shape.n_tokens)
+        out_sep = sep(g)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_sep)
 
 
 def test_single_launch_self_row_and_all_masked():
@@ -540,14 +548,14 @@ def test_single_launch_repeated_steps_of_varying_size():
     """One handle and workspace run steps of 8 (matrix-core path), 3, 1, 8, 1
     and 2 tokens in a row: flags of an earlier (larger) step never satisfy a
     later step's waits (the epoch advances every step, and the other path's
-    steps leave the flag region alone), each step gives the separate kernels'
-    bits, and no wait times out."""
+    steps leave the flag region alone), each step gives the bits of the fused
+    variant (the separate kernels at 8 tokens), and no wait times out."""
     wl = _BATCH32.with_tokens(8)
     sh = wl.shape
     inp = make_inputs(wl, with_pool=False)
     g = gpu_inputs(wl, inp)
     single = MlaGatherDecode(Dims.from_shape(sh), max_tokens=8, single_launch=True)
-    sep = MlaGatherDecode(Dims.from_shape(sh), max_tokens=8)
+    sep = MlaGatherDecode(Dims.from_shape(sh), max_tokens=8, fused=True)
     for T in (8, 3, 1, 8, 1, 2):
         sub = token_slice(g, list(range(T)))
         sub["kv_cache"] = g["kv_cache"]
@@ -562,13 +570,13 @@ def test_single_launch_repeated_steps_of_varying_size():
 def test_single_launch_noalloc_and_graph_replay():
     """The single launch through the allocation-free entry point (the static
     device array) and replayed from a captured graph, three times each: the
-    same bits as the separate kernels every time."""
+    same bits as the fused variant every time."""
     wl = CONFIGS[1]  # ds32_slice
     sh = wl.shape
     inp = make_inputs(wl, with_pool=False)
     g = gpu_inputs(wl, inp)
     dims = Dims.from_shape(sh)
-    ref = MlaGatherDecode(dims, max_tokens=1)(g).clone()
+    ref = MlaGatherDecode(dims, max_tokens=1, fused=True)(g).clone()
     single = MlaGatherDecode(dims, max_tokens=1, single_launch=True)
     graphed = MlaGatherDecode(dims, max_tokens=1, single_launch=True, graph=True)
     fixed = torch.empty_like(ref)
