@@ -830,8 +830,11 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
   for (int n = 0; n < NT; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;  // head l16; l over this lane's rows (groups added at the end)
 
+  // chunks past the split's last are not loaded (a DMA instruction holds its
+  // wave about as long whatever it reads); the waits count only those that were
 #pragma unroll
-  for (int c = 0; c + 1 < kWideRing; ++c) issue_chunk(c);
+  for (int c = 0; c + 1 < kWideRing; ++c)
+    if (c < nchunks) issue_chunk(c);
 
   // Q fragments of the whole kv_row: lane l holds Qcat[head][32*kk + 8*g .. +8]
   // (loaded from a clamped address and zeroed past the heads or the row)
@@ -861,13 +864,21 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
 
   const bool late_issue = wave >= NW / 2;  // the second wave of each SIMD (scalar)
   for (int c = 0; c < nchunks; ++c) {
-    wait_vmcnt<NI * (kWideRing - 2)>();  // chunk c's loads are this wave's oldest; c+1 and c+2 may stay in flight
+    // chunk c's loads are this wave's oldest; those of c+1 and c+2, if loaded, may stay in flight
+    static_assert(kWideRing == 4, "the waits below count three chunks in flight");
+    if (c + 2 < nchunks)
+      wait_vmcnt<2 * NI>();
+    else if (c + 1 < nchunks)
+      wait_vmcnt<NI>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();   // chunk c visible to every wave; buffer (c-1) % ring consumed
     // The loads of chunk c+3 stall the issuing wave until the memory system
     // takes them (they go out at the gather's rate), so the two waves of a
     // SIMD issue them at different points: waves 0-3 first, waves 4-7 after
     // their softmax.  Each wave's stall then overlaps the other's products.
-    if (!late_issue) issue_chunk(c + kWideRing - 1);
+    const bool more = c + kWideRing - 1 < nchunks;  // uniform
+    if (!late_issue && more) issue_chunk(c + kWideRing - 1);
     const int bsel = c % kWideRing;
     const lds_char_t* buf = lring + bsel * BUF;
     // scores: tile A rows 0-15, tile B rows 16-31, key fragments KD k-steps ahead
@@ -930,7 +941,7 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] *= alpha;
     }
-    if (late_issue) issue_chunk(c + kWideRing - 1);
+    if (late_issue && more) issue_chunk(c + kWideRing - 1);
     // B operand of the PV product: k-slots 0-3 = rows 4g+i, 4-7 = rows 16+4g+i
     bf16x8_t pab;
 #pragma unroll
@@ -953,7 +964,7 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  wait_vmcnt<0>();  // the trailing loads (zero rows into unused buffers or the sink)
+  wait_vmcnt<0>();  // every chunk loaded was waited for; kept as a guard
 
   const float l_tot = sum4groups(l_run);
   const size_t pb = ((size_t)t * pl.nsplit + split) * p.NH;
