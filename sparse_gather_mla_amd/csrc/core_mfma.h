@@ -975,8 +975,19 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
     }
     constexpr int R = 16 * NT;
     // lane (g, l16) holds columns 16n + 4g + i of head l16
+    if (pl.po16) {  // o / l in fp16, four columns in one 8-byte store
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      _Float16* po16 = reinterpret_cast<_Float16*>(p.po) + (pb + head) * R + 4 * g;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t*>(p.po + (pb + head) * R + 16 * n + 4 * g) = o[n];
+      for (int n = 0; n < NT; ++n) {
+        const f16x4_t v = f16x4_t{(_Float16)(o[n][0] * inv), (_Float16)(o[n][1] * inv), (_Float16)(o[n][2] * inv),
+                                  (_Float16)(o[n][3] * inv)};
+        *reinterpret_cast<f16x4_t*>(po16 + 16 * n) = v;
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t*>(p.po + (pb + head) * R + 16 * n + 4 * g) = o[n];
+    }
   }
 }
 

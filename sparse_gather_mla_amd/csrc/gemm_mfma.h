@@ -5,8 +5,10 @@
 // W is a bf16 [K, N] weight, row-major (columns contiguous); A is an fp32
 // activation.  Rounding A to bf16 would cost 8 bits on every product, so each
 // activation is split into hi = bf16(a) and lo = bf16(a - hi) and both halves
-// meet the weight (two MFMAs per fragment): about 16 significant bits.  The
-// projections stay bound by the weight stream even with the matrix work doubled.
+// meet the weight (two MFMAs per fragment): about 16 significant bits.  Up to
+// 32 tokens the projections stay bound by the weight stream even with the
+// matrix work doubled.  A GEMM can also read the hi halves alone (AH = 1),
+// which the o-projection of 64- and 128-token blocks does (phases_mfma.h).
 //
 // Tiles: 16 tokens (an m-tile) x NC columns (64 to 256) x 32 k (a k-step).  A
 // workgroup owns one NC-column tile, one K slab and a block of MTB m-tiles;
@@ -64,12 +66,13 @@ __device__ __forceinline__ void split4(const float* a, uint2& hi, uint2& lo) {
 
 // A[t][k..k+3] (k % 4 == 0) into a global fragment-order buffer.  In both
 // orders four consecutive k of one token are one 8-byte run of each half.
-__device__ __forceinline__ void put_a4(bf16_t* buf, int mt_pad, int t, int k, const float* a) {
+// Without `lo` the lo half is left unwritten (its consumer reads hi alone).
+__device__ __forceinline__ void put_a4(bf16_t* buf, int mt_pad, int t, int k, const float* a, bool lo_too = true) {
   uint2 hi, lo;
   split4(a, hi, lo);
   const size_t i = abuf_index(t, k, mt_pad);
   *reinterpret_cast<uint2*>(buf + i) = hi;
-  *reinterpret_cast<uint2*>(buf + i + kAFragElems) = lo;
+  if (lo_too) *reinterpret_cast<uint2*>(buf + i + kAFragElems) = lo;
 }
 
 // The same into an LDS block array [k-step][m-tile < mtb][half][512], either order.
@@ -94,17 +97,19 @@ __host__ __device__ constexpr int mg_cols(int mtb) { return mtb >= 4 ? 256 : 128
 // ran one wave per SIMD), four for smaller blocks.
 __host__ __device__ constexpr int mg_waves(int mtb) { return mtb >= 4 ? 8 : 4; }
 
-template <int MTB, int NC = mg_cols(MTB), int NW = mg_waves(MTB)>
+// Activation halves a GEMM reads: 2 (hi and lo) or 1 (hi alone, a plain bf16
+// activation).
+template <int MTB, int NC = mg_cols(MTB), int NW = mg_waves(MTB), int AH = 2>
 struct Mg {
   static constexpr int kThreads = 64 * NW;
   static constexpr int WM = MTB >= 2 ? 2 : 1;  // waves along tokens
   static constexpr int WN = NW / WM;           // waves along columns
   static constexpr int MTW = MTB / WM;         // m-tiles per wave
   static constexpr int NTW = NC / 16 / WN;     // 16-column n-tiles per wave
-  static constexpr int kABytes = MTB * 2 * kAFragElems * 2;
+  static constexpr int kABytes = MTB * AH * kAFragElems * 2;
   static constexpr int kBBytes = kMgK * NC * 2;
   static constexpr int kStep = kABytes + kBBytes;
-  static constexpr int kAPieces = (MTB * 128 + kThreads - 1) / kThreads;  // A pieces per lane per step
+  static constexpr int kAPieces = (MTB * 64 * AH + kThreads - 1) / kThreads;  // A pieces per lane per step
   static constexpr int kBPieces = NC * 4 / kThreads;                       // B pieces per lane per step
   static constexpr int kPieces = kAPieces + kBPieces;
   static constexpr int kAhead = NC >= 256 ? 3 : 6;           // k-steps loaded ahead into registers
@@ -165,11 +170,12 @@ __device__ __forceinline__ BTileSrc<NC, NTHR> btile_src(const bf16_t* W, int K, 
   return s;
 }
 
-// One k-step: B fragments by transposing reads, A fragments (hi, lo), MFMAs.
-template <int MTB, int NC, int NW = mg_waves(MTB)>
+// One k-step: B fragments by transposing reads, A fragments (hi, and lo when
+// AH == 2; the stage holds AH blocks per m-tile), MFMAs.
+template <int MTB, int NC, int NW = mg_waves(MTB), int AH = 2>
 __device__ __forceinline__ void mg_step(const char* bufA, const char* bufB,
                                         f32x4_t (&acc)[Mg<MTB, NC, NW>::MTW][Mg<MTB, NC, NW>::NTW]) {
-  using S = Mg<MTB, NC, NW>;
+  using S = Mg<MTB, NC, NW, AH>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::WN, wn = wave % S::WN;
   const int g = lane >> 4, l16 = lane & 15;
@@ -187,14 +193,15 @@ __device__ __forceinline__ void mg_step(const char* bufA, const char* bufB,
 #pragma unroll
   for (int mt = 0; mt < S::MTW; ++mt) {
     const int m = wm * S::MTW + mt;
-    const bf16x8_t ahi = *reinterpret_cast<const bf16x8_t*>(bufA + ((m * 2) * 64 + lane) * 16);
-    const bf16x8_t alo = *reinterpret_cast<const bf16x8_t*>(bufA + ((m * 2 + 1) * 64 + lane) * 16);
+    const bf16x8_t ahi = *reinterpret_cast<const bf16x8_t*>(bufA + ((m * AH) * 64 + lane) * 16);
+    bf16x8_t alo = ahi;
+    if constexpr (AH == 2) alo = *reinterpret_cast<const bf16x8_t*>(bufA + ((m * 2 + 1) * 64 + lane) * 16);
 #pragma unroll
     for (int nt = 0; nt < S::NTW; ++nt) {
       // transposed product (weight fragment as the A operand): lane (g, l16)
       // gets columns 4g..4g+3 of token l16, stored four at a time
       acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nt], ahi, acc[mt][nt], 0, 0, 0);
-      acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nt], alo, acc[mt][nt], 0, 0, 0);
+      if constexpr (AH == 2) acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nt], alo, acc[mt][nt], 0, 0, 0);
     }
   }
 }
@@ -244,12 +251,13 @@ __device__ __forceinline__ void mg_pipe(int nsteps, char* stage, int step_bytes,
 }
 
 // acc = A[token block] @ W[k0 : k0 + 32*nks, c0 : c0 + NC] with A from a
-// global fragment-order buffer (its m-tiles mt0 .. mt0+MTB-1).
-template <int MTB, int NC = mg_cols(MTB), int NW = mg_waves(MTB)>
+// global fragment-order buffer (its m-tiles mt0 .. mt0+MTB-1); with AH == 1
+// only the hi blocks are read, so A enters as plain bf16.
+template <int MTB, int NC = mg_cols(MTB), int NW = mg_waves(MTB), int AH = 2>
 __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, const bf16_t* W, int K, int N, int k0,
                                       int nks, int c0, const bf16_t* zero16, char* stage,
                                       f32x4_t (&acc)[Mg<MTB, NC, NW>::MTW][Mg<MTB, NC, NW>::NTW]) {
-  using S = Mg<MTB, NC, NW>;
+  using S = Mg<MTB, NC, NW, AH>;
   constexpr int NTHR = S::kThreads;
 #pragma unroll
   for (int mt = 0; mt < S::MTW; ++mt)
@@ -258,7 +266,7 @@ __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, cons
   const BTileSrc<NC, NTHR> bs = btile_src<NC, NTHR>(W, K, N, k0, c0);
   const int ks0 = k0 / kMgK;
   const int tid = threadIdx.x;
-  const bf16_t* Ab = A + ((size_t)ks0 * mt_pad + mt0) * (2 * kAFragElems) + (size_t)tid * 8;
+  const bf16_t* Ab = A + ((size_t)ks0 * mt_pad + mt0) * (2 * kAFragElems);
   const size_t astep = (size_t)mt_pad * 2 * kAFragElems;
   mg_pipe<S::kPieces, S::kAhead>(
       nks, stage, S::kStep,
@@ -269,8 +277,12 @@ __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, cons
         const bool live = st < nks;
 #pragma unroll
         for (int i = 0; i < S::kAPieces; ++i) {
+          // piece q: block q / 64 of the stage (m-tile, half), lane q % 64;
+          // with AH == 1 block m is the hi block of m-tile m in global memory
+          const int q = i * NTHR + tid;
           const bf16_t* src = zero16;
-          if (live && i * NTHR + tid < MTB * 128) src = Ab + astep * st + i * NTHR * 8;
+          if (live && q < MTB * 64 * AH)
+            src = Ab + astep * st + (AH == 2 ? (size_t)q * 8 : (size_t)(q >> 6) * 2 * kAFragElems + (q & 63) * 8);
           r.v[i] = load16(src);
         }
 #pragma unroll
@@ -284,11 +296,11 @@ __device__ __forceinline__ void mgemm(const bf16_t* A, int mt_pad, int mt0, cons
       [&](const Pieces<S::kPieces>& r, char* buf) {
 #pragma unroll
         for (int i = 0; i < S::kAPieces; ++i)
-          if (i * NTHR + tid < MTB * 128) store16(buf + (i * NTHR + tid) * 16, r.v[i]);
+          if (i * NTHR + tid < MTB * 64 * AH) store16(buf + (i * NTHR + tid) * 16, r.v[i]);
 #pragma unroll
         for (int i = 0; i < S::kBPieces; ++i) store16(buf + S::kABytes + (i * NTHR + tid) * 16, r.v[S::kAPieces + i]);
       },
-      [&](int, const char* buf) { mg_step<MTB, NC, NW>(buf, buf + S::kABytes, acc); });
+      [&](int, const char* buf) { mg_step<MTB, NC, NW, AH>(buf, buf + S::kABytes, acc); });
 }
 
 // Lane (g, l16) of a wave holds out[token l16][columns 4g .. 4g+3] of each

@@ -138,15 +138,15 @@ __global__ __launch_bounds__(kBlock) void k_absorb_m(StepParams p) {
 }
 
 
-template <int MTB, int Q5>
+template <int MTB, int Q5, bool PO16>
 __global__ __launch_bounds__(kBlock) void k_oabsorb_m(StepParams p) {
   extern __shared__ float lds[];
-  phase_oabsorb_m<MTB, Q5>(p, blockIdx.x, reinterpret_cast<char*>(lds));
+  phase_oabsorb_m<MTB, Q5, PO16>(p, blockIdx.x, reinterpret_cast<char*>(lds));
 }
 
 template <int MTB>
 __global__ __launch_bounds__(64 * mg_waves(MTB)) void k_oproj_m(StepParams p) {
-  __shared__ __attribute__((aligned(16))) char stage[Mg<MTB>::kStage];
+  __shared__ __attribute__((aligned(16))) char stage[Mg<MTB, mg_cols(MTB), mg_waves(MTB), oproj_ah(MTB)>::kStage];
   phase_oproj_m<MTB>(p, blockIdx.x, stage);
 }
 
@@ -249,6 +249,7 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   const int P = d.n_prior, DV = d.v_head_dim, DN = d.qk_nope_head_dim;
   const int T = pl.T;
   pl.mfma = 1;
+  pl.po16 = pl.core_hg == 8 ? 1 : 0;  // the one-head-tile-per-wave core (more than 64 heads)
   pl.mtb = T <= 16 ? 1 : (T <= 32 ? 2 : (T <= 64 ? 4 : 8));
   pl.ntb = cdiv(T, 16 * pl.mtb);
   pl.mt_pad = pl.ntb * pl.mtb;
@@ -577,8 +578,10 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
   const void* big[] = {(const void*)k_absorb_m<1, 64>, (const void*)k_absorb_m<2, 64>, (const void*)k_absorb_m<4, 64>,
                        (const void*)k_absorb_m<1, 128>, (const void*)k_absorb_m<2, 128>, (const void*)k_absorb_m<4, 128>,
                        (const void*)k_absorb_m<1, 512>, (const void*)k_absorb_m<2, 512>, (const void*)k_absorb_m<4, 512>,
-                       (const void*)k_oabsorb_m<1, 1>, (const void*)k_oabsorb_m<2, 1>,
-                       (const void*)k_oabsorb_m<1, 2>, (const void*)k_oabsorb_m<2, 2>};
+                       (const void*)k_oabsorb_m<1, 1, false>, (const void*)k_oabsorb_m<2, 1, false>,
+                       (const void*)k_oabsorb_m<1, 2, false>, (const void*)k_oabsorb_m<2, 2, false>,
+                       (const void*)k_oabsorb_m<1, 1, true>, (const void*)k_oabsorb_m<2, 1, true>,
+                       (const void*)k_oabsorb_m<1, 2, true>, (const void*)k_oabsorb_m<2, 2, true>};
   for (const void* k : big)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   return e;
@@ -619,9 +622,14 @@ step_kernel_t pick_absorb_m(int mtb, int nca) {
   if (nca == 128) return mtb == 1 ? k_absorb_m<1, 128> : (mtb == 2 ? k_absorb_m<2, 128> : k_absorb_m<4, 128>);
   return mtb == 1 ? k_absorb_m<1, 64> : (mtb == 2 ? k_absorb_m<2, 64> : k_absorb_m<4, 64>);
 }
-step_kernel_t pick_oabsorb_m(int mtb, int q5) {
-  if (q5 == 1) return mtb == 2 ? k_oabsorb_m<2, 1> : k_oabsorb_m<1, 1>;
-  return mtb == 2 ? k_oabsorb_m<2, 2> : k_oabsorb_m<1, 2>;
+template <bool PO16>
+step_kernel_t pick_oabsorb_m_t(int mtb, int q5) {
+  if (q5 == 1) return mtb == 2 ? k_oabsorb_m<2, 1, PO16> : k_oabsorb_m<1, 1, PO16>;
+  return mtb == 2 ? k_oabsorb_m<2, 2, PO16> : k_oabsorb_m<1, 2, PO16>;
+}
+
+step_kernel_t pick_oabsorb_m(const Plan& pl) {
+  return pl.po16 ? pick_oabsorb_m_t<true>(pl.mtb5, pl.q5) : pick_oabsorb_m_t<false>(pl.mtb5, pl.q5);
 }
 
 }  // namespace
@@ -777,7 +785,7 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     L(pick_qup_m(pl.mtb), dim3(mg_grid(pl.nt2m * pl.s2, pl.ntb)), gblk, 0);
     L(pick_absorb_m(pl.mtb3, pl.nca3), dim3(mg_grid(p.NH * (pl.nct3 / pl.tpw3), pl.ntb3)), blk, absorb_lds_bytes(pl, p.DN));
     L(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0);
-    L(pick_oabsorb_m(pl.mtb5, pl.q5), dim3(mg_grid(p.NH * pl.nq5, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R));
+    L(pick_oabsorb_m(pl), dim3(mg_grid(p.NH * pl.nq5, pl.ntb5)), blk, oabsorb_lds_bytes(pl, p.R));
     L(pick_oproj_m(pl.mtb), dim3(mg_grid(pl.nt6m * pl.s6, pl.ntb)), gblk, 0);
     L(k_out, dim3(pl.n7), blk, gl);
   }
@@ -848,9 +856,10 @@ void log_plan(mla_gd_handle* h, const Plan& pl) {
   const char* core = pl.core_hg == 8 ? "one 16-head tile per wave, 128 heads per workgroup"
                                      : (pl.core_rs ? "row-split, 64 heads per workgroup"
                                                    : (pl.core_hg == 1 ? "16 heads, 4 waves" : "64 heads, 8 waves"));
-  fprintf(stderr, "[mla_gd] T=%d: %s path%s%s; core: %s, %d split(s) of %d rows x %d head block(s) = %d workgroups; workspace %zu bytes\n",
+  fprintf(stderr, "[mla_gd] T=%d: %s path%s%s; core: %s, %d split(s) of %d rows x %d head block(s) = %d workgroups, "
+                  "%s split partials; workspace %zu bytes\n",
           pl.T, pl.mfma ? "matrix-core" : "GEMV", pl.single ? ", single launch" : "", pl.fused ? ", fused" : "", core,
-          pl.nsplit, pl.ps, pl.core_nhb, core_grid(pl), pl.total);
+          pl.nsplit, pl.ps, pl.core_nhb, core_grid(pl), pl.po16 ? "fp16 o/l" : "fp32", pl.total);
   if (pl.mfma)
     fprintf(stderr, "[mla_gd]   token blocks of %d x 16 (%d); down %d slabs x %d k-steps; up %d slabs x %d; "
                     "absorption %d-column tiles, %d per workgroup, blocks of %d x 16; output absorption blocks of %d x 16, "

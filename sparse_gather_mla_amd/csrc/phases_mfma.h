@@ -19,6 +19,8 @@
 // only reach output rows that are never stored.  K padding is written as zeros.
 #pragma once
 
+#include <type_traits>
+
 #include "device_util.h"
 #include "gemm_mfma.h"
 #include "phases.h"
@@ -451,11 +453,19 @@ __host__ __device__ constexpr int oabsorb_hdr_bytes(int mtb, int nsplit) {
 }
 constexpr int kOabsMaxKs = 16;  // kv_lora_rank <= 512
 
+// Activation halves the o-projection reads (gemm_mfma.h): blocks of 64 and
+// 128 tokens take o_v as plain bf16 (its hi half).  There the doubled matrix
+// work of the hi/lo products outweighs the weight stream, and o_v is the
+// path's last activation: its rounding reaches the output only through the
+// sum over n_heads * v_head_dim products.
+__host__ __device__ constexpr int oproj_ah(int mtb) { return mtb >= 4 ? 1 : 2; }
+
 // Q5 output tiles per wave.  With nq5 > 1 parts per (head, token block) each
 // workgroup takes 4*Q5 of the 16-row output tiles (and combines the splits
 // itself), so few heads and tokens still fill the chip.
-template <int MTB, int Q5>
+template <int MTB, int Q5, bool PO16>
 __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
+  using ElemT = std::conditional_t<PO16, _Float16, float>;  // the core's partials (pl.po16)
   const Plan& pl = p.pl;
   int u, tb;
   if (!mg_unit(b, p.NH * pl.nq5, pl.ntb5, u, tb)) return;
@@ -512,36 +522,41 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
     const float M = wave_max_dpp(m);
     const float w = (M == -INFINITY || lane >= NSP) ? 0.f : exp2f(m - M);
     const float L = wave_sum_dpp(l * w);
-    if (lane < NSP) wsp[tt * NSP + lane] = w;
+    // normalised fp16 partials (o / l) weigh in with w * l
+    if (lane < NSP) wsp[tt * NSP + lane] = PO16 ? w * l : w;
     if (lane == 0) linv[tt] = (L > 0.f) ? 1.f / L : 0.f;
   }
   __syncthreads();
   // o_lat float4 items (token, 4 columns), eight per thread per pass; the
   // loads of G splits go out together (a split index past the last reloads
   // the last and is dropped).  Two tiles per wave keep G = 1: the registers
-  // of four splits cost more than the round trips they save.
+  // of four splits cost more than the round trips they save.  Partials in
+  // fp16 (PO16) are four halves, 8 bytes, per item.
   {
+    using VT = std::conditional_t<PO16, f16x4_t, float4>;
     constexpr int NI = 8;
-    constexpr int G = Q5 == 1 ? 4 : 1;
+    constexpr int G = Q5 == 1 ? 4 : (PO16 ? 2 : 1);
     const int n_items = MTB * 16 * (R / 4);
     for (int base = 0; base < n_items; base += NI * kBlock) {
       float4 o[NI];
-      const float* src[NI];
+      const VT* src[NI];
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         const int idx = base + i * kBlock + tid;
         const int tt = idx / (R / 4), c = 4 * (idx % (R / 4));
-        src[i] = (idx < n_items && tt < nt) ? p.po + ((size_t)(t0 + tt) * NSP * p.NH + h) * R + c : nullptr;
+        src[i] = (idx < n_items && tt < nt)
+                     ? reinterpret_cast<const VT*>(reinterpret_cast<const ElemT*>(p.po) +
+                                                   ((size_t)(t0 + tt) * NSP * p.NH + h) * R + c)
+                     : nullptr;
       }
       for (int s = 0; s < NSP; s += G) {
-        float4 v[G][NI];
+        VT v[G][NI];
 #pragma unroll
         for (int u = 0; u < G; ++u) {
-          const size_t off = (size_t)min(s + u, NSP - 1) * p.NH * R;
+          const size_t off = (size_t)min(s + u, NSP - 1) * p.NH * R / 4;  // in items
 #pragma unroll
-          for (int i = 0; i < NI; ++i)
-            v[u][i] = src[i] ? *reinterpret_cast<const float4*>(src[i] + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+          for (int i = 0; i < NI; ++i) v[u][i] = src[i] ? src[i][off] : VT{};
         }
 #pragma unroll
         for (int u = 0; u < G; ++u) {
@@ -551,10 +566,10 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
             const int idx = base + i * kBlock + tid;
             const int tt = idx / (R / 4);
             const float w = src[i] ? wsp[tt * NSP + s + u] : 0.f;
-            o[i].x = fmaf(w, v[u][i].x, o[i].x);
-            o[i].y = fmaf(w, v[u][i].y, o[i].y);
-            o[i].z = fmaf(w, v[u][i].z, o[i].z);
-            o[i].w = fmaf(w, v[u][i].w, o[i].w);
+            o[i].x = fmaf(w, (float)v[u][i].x, o[i].x);
+            o[i].y = fmaf(w, (float)v[u][i].y, o[i].y);
+            o[i].z = fmaf(w, (float)v[u][i].z, o[i].z);
+            o[i].w = fmaf(w, (float)v[u][i].w, o[i].w);
           }
         }
       }
@@ -571,6 +586,7 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
   }
   __syncthreads();
   const int K5 = p.NH * p.DV;
+  const bool a5_lo = oproj_ah(pl.mtb) == 2;  // the o-projection reads A5's lo half
   for (int n0 = nfirst; n0 < nhi; n0 += 4 * Q5) {
     if (Q5 != 1 || n0 != nfirst) load_b(n0);
 #pragma unroll
@@ -600,7 +616,7 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
         if (t >= T) continue;
         const float a[4] = {acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]};
         if ((p.DV & 3) == 0 && d0 + 3 < p.DV) {
-          put_a4(p.a5, pl.mt_pad, t, h * p.DV + d0, a);  // one 8-byte run per half
+          put_a4(p.a5, pl.mt_pad, t, h * p.DV + d0, a, a5_lo);  // one 8-byte run per half
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -626,8 +642,9 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// k_oproj: split-K partials of A5 @ o_proj_w
+// k_oproj: split-K partials of A5 @ o_proj_w (oproj_ah(MTB) halves of A5)
 // ---------------------------------------------------------------------------
+
 template <int MTB>
 __device__ void phase_oproj_m(const StepParams& p, int b, char* stage) {
   const Plan& pl = p.pl;
@@ -639,7 +656,8 @@ __device__ void phase_oproj_m(const StepParams& p, int b, char* stage) {
   const int k0 = slab * pl.ks6m * kMgK;
   const int nks = min(pl.ks6m, pl.kt6 - slab * pl.ks6m);
   f32x4_t acc[Mg<MTB>::MTW][Mg<MTB>::NTW];
-  mgemm<MTB>(p.a5, pl.mt_pad, tb * MTB, p.w_o, p.NH * p.DV, p.H, k0, nks, c0, reinterpret_cast<const bf16_t*>(p.zero16), stage, acc);
+  mgemm<MTB, mg_cols(MTB), mg_waves(MTB), oproj_ah(MTB)>(p.a5, pl.mt_pad, tb * MTB, p.w_o, p.NH * p.DV, p.H, k0, nks,
+                                                        c0, reinterpret_cast<const bf16_t*>(p.zero16), stage, acc);
   const int T = pl.T;
   float* out = p.part6 + (size_t)slab * T * p.H;
   mg_for_outputs4<MTB>(acc, tb * MTB * 16, c0, [&](int t, int c, const f32x4_t& v) {

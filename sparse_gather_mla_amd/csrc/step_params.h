@@ -31,6 +31,10 @@ struct Plan {
   // GEMV path: the output sum is folded into the o-projection (no k_out); the
   // last slab of each column tile to arrive adds the tile's slabs
   int fold_out;
+  // matrix-core path with more than 64 heads: the core stores each split's
+  // latent output normalised by its own denominator (o / l) in fp16, half the
+  // bytes of the fp32 partials it otherwise writes
+  int po16;
   // fused variant: one launch for the kv-row write, the absorption and the core
   int fused;
   // single-launch variant: the whole step as one launch; item (workgroup)
@@ -102,7 +106,8 @@ struct StepParams {
   uint16_t* qcat;   // [T][NH][KVR] bf16: per head [q_lat | roped q_pe]
   float* pm;        // [T][nsplit][NH] running max (log2 domain) per split
   float* pden;      // [T][nsplit][NH] softmax denominators per split
-  float* po;        // [T][nsplit][NH][R] unnormalised latent outputs per split
+  float* po;        // [T][nsplit][NH][R] unnormalised latent outputs per split (fp32), or
+                    // with pl.po16 normalised ones (fp16, o / l; zeros where l = 0)
   float* ov;        // [T][NH*DV] output-absorbed values
   float* part6;     // [s6][T][H] split-K partials of the o-projection
   // matrix-core path: activations in fragment order (hi/lo bf16), per-token scales

@@ -177,6 +177,22 @@ def test_parity_many_heads_one_tile_per_wave(nh, T):
     _run_and_check(wl)
 
 
+def _masked_splits(inp):
+    gi = inp["gather_indices"]
+    gi[1, :] = -1  # token 1: nothing valid, every split empty
+    gi[2, 10:] = 2**30  # token 2: only its first ten entries valid, the later splits empty
+
+
+# The many-heads core on the matrix-core path stores each split's output
+# normalised by its own denominator; a split without a valid row must combine
+# as zeros (and an all-masked token give a zero output row).
+def test_many_heads_matrix_core_empty_splits_and_all_masked_token():
+    wl = replace(MANY_HEADS, name="ragged_heads72_T5_masked", shape=replace(MANY_HEADS.shape, n_tokens=5, n_heads=72),
+                 seed=411)
+    out, ref, inp, g = _run_and_check(wl, mutate=_masked_splits)
+    assert torch.count_nonzero(out[1]).item() == 0
+
+
 # 72-wide value heads give five 16-row output tiles: with few (head, token
 # block) pairs the output absorption splits them over two workgroups per pair,
 # the second holding one tile (three of its waves idle), and K5 = 1440 leaves
