@@ -436,13 +436,32 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
     hooks.st(p.pden + pb + head, l_run);
   }
   constexpr int R = 16 * NT;
-#pragma unroll
-  for (int n = 0; n < NTW; ++n)
+  if (pl.po16) {
+    // o / l in fp16 (the matrix-core path, whose hooks store plainly): lane
+    // (g, l16) holds heads hbase + 4g + i, whose l lane 4g + i holds
+    float inv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = hbase + 4 * g + i;
-      if (h < p.NH) hooks.st(p.po + (pb + h) * R + 16 * (cs * NTW + n) + l16, o[n][i]);
+      const float li = __shfl(l_run, 4 * g + i, 64);
+      inv[i] = li > 0.f ? 1.f / li : 0.f;
     }
+    _Float16* po16 = reinterpret_cast<_Float16*>(p.po);
+#pragma unroll
+    for (int n = 0; n < NTW; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = hbase + 4 * g + i;
+        if (h < p.NH) po16[(pb + h) * R + 16 * (cs * NTW + n) + l16] = (_Float16)(o[n][i] * inv[i]);
+      }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NTW; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = hbase + 4 * g + i;
+        if (h < p.NH) hooks.st(p.po + (pb + h) * R + 16 * (cs * NTW + n) + l16, o[n][i]);
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------

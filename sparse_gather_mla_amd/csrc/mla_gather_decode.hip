@@ -249,7 +249,7 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   const int P = d.n_prior, DV = d.v_head_dim, DN = d.qk_nope_head_dim;
   const int T = pl.T;
   pl.mfma = 1;
-  pl.po16 = pl.core_hg == 8 ? 1 : 0;  // the one-head-tile-per-wave core (more than 64 heads)
+  pl.po16 = pl.core_rs ? 0 : 1;  // every core shape but the row-split one (17-64 heads)
   pl.mtb = T <= 16 ? 1 : (T <= 32 ? 2 : (T <= 64 ? 4 : 8));
   pl.ntb = cdiv(T, 16 * pl.mtb);
   pl.mt_pad = pl.ntb * pl.mtb;

@@ -31,9 +31,9 @@ struct Plan {
   // GEMV path: the output sum is folded into the o-projection (no k_out); the
   // last slab of each column tile to arrive adds the tile's slabs
   int fold_out;
-  // matrix-core path with more than 64 heads: the core stores each split's
-  // latent output normalised by its own denominator (o / l) in fp16, half the
-  // bytes of the fp32 partials it otherwise writes
+  // matrix-core path, every core shape but the row-split one: the core stores
+  // each split's latent output normalised by its own denominator (o / l) in
+  // fp16, half the bytes of the fp32 partials it otherwise writes
   int po16;
   // fused variant: one launch for the kv-row write, the absorption and the core
   int fused;

@@ -183,12 +183,15 @@ def _masked_splits(inp):
     gi[2, 10:] = 2**30  # token 2: only its first ten entries valid, the later splits empty
 
 
-# The many-heads core on the matrix-core path stores each split's output
-# normalised by its own denominator; a split without a valid row must combine
-# as zeros (and an all-masked token give a zero output row).
-def test_many_heads_matrix_core_empty_splits_and_all_masked_token():
-    wl = replace(MANY_HEADS, name="ragged_heads72_T5_masked", shape=replace(MANY_HEADS.shape, n_tokens=5, n_heads=72),
-                 seed=411)
+# On the matrix-core path the core stores each split's output normalised by
+# its own denominator; a split without a valid row must combine as zeros (and
+# an all-masked token give a zero output row).  Both core shapes that do so:
+# one 16-head tile (13 heads) and one tile per wave (72 heads).
+@pytest.mark.parametrize("nh", [13, 72])
+def test_matrix_core_empty_splits_and_all_masked_token(nh):
+    base = MANY_HEADS if nh > 64 else RAGGED
+    wl = replace(base, name=f"ragged_heads{nh}_T5_masked", shape=replace(base.shape, n_tokens=5, n_heads=nh),
+                 seed=411 + nh)
     out, ref, inp, g = _run_and_check(wl, mutate=_masked_splits)
     assert torch.count_nonzero(out[1]).item() == 0
 
