@@ -748,19 +748,20 @@ __device__ __attribute__((always_inline)) void phase_out(const StepParams& p, in
   const bool ok = c < p.H;  // H % 8 == 0: a group of four is wholly inside or outside
   const size_t stride = (size_t)pl.T * p.H;
   const float* src = p.part6 + (size_t)t * p.H + (ok ? c : 0);
-  // this lane's slabs, eight loads at a time (an index past the last slab
-  // reloads the last and is dropped)
+  // this lane's slabs s = part, part + 4, ..., eight loads at a time; a lane
+  // loads only slabs that exist (with eight or nine slabs a lane needs two or
+  // three, and an unconditional reload of the last would triple the loads)
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   const int S = pl.s6;
   for (int s = part; s < S; s += 32) {
     float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = sy.ld4(src + (size_t)min(s + 4 * u, S - 1) * stride);
-#pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (s + 4 * u < S) {
-        a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
-      }
+      v[u] = s + 4 * u < S ? sy.ld4(src + (size_t)(s + 4 * u) * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
+    }
   }
   // partials of lanes 4i .. 4i+3: ((p0 + p1) + (p2 + p3))
   float r[4] = {a.x, a.y, a.z, a.w};
