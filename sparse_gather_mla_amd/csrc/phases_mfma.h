@@ -148,16 +148,17 @@ __device__ void phase_down_m(const StepParams& p, int b, char* stage) {
 // bf16 row at slot_mapping[t].
 // ---------------------------------------------------------------------------
 // Sums over S split-K slabs, in slab order, of partials written by the
-// previous kernel.  G slabs' loads go out together (a slab index past S-1
-// reloads slab S-1 and is dropped), so a reduction costs ceil(S/G) memory
-// round trips, and every load is unconditional.
+// previous kernel.  G slabs' loads go out together, so a reduction costs
+// ceil(S/G) memory round trips; slabs past S - 1 are not loaded (the
+// condition is the same in every lane).
 template <int G>
 __device__ __forceinline__ float4 sum_slabs4(const float* src, size_t stride, int S) {
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < S; s += G) {
     float4 v[G];
 #pragma unroll
-    for (int u = 0; u < G; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)min(s + u, S - 1) * stride);
+    for (int u = 0; u < G; ++u)
+      v[u] = s + u < S ? *reinterpret_cast<const float4*>(src + (size_t)(s + u) * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < G; ++u)
       if (s + u < S) {
@@ -178,10 +179,10 @@ __device__ __forceinline__ void sum_slabs4_n(const float* const (&src)[NI], size
     float4 v[G][NI];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const size_t o = (size_t)min(s + u, S - 1) * stride;
+      const size_t o = (size_t)(s + u) * stride;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        v[u][i] = src[i] ? *reinterpret_cast<const float4*>(src[i] + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[u][i] = (src[i] && s + u < S) ? *reinterpret_cast<const float4*>(src[i] + o) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < G; ++u)
@@ -412,10 +413,10 @@ __device__ void phase_absorb_m(const StepParams& p, int b, char* lds) {
       float2 v[GQ][NQ];
 #pragma unroll
       for (int u = 0; u < GQ; ++u) {
-        const size_t o = (size_t)min(s2 + u, pl.s2 - 1) * T * p.N2;
+        const size_t o = (size_t)(s2 + u) * T * p.N2;
 #pragma unroll
         for (int j = 0; j < NQ; ++j)
-          v[u][j] = src[j] ? *reinterpret_cast<const float2*>(src[j] + o) : make_float2(0.f, 0.f);
+          v[u][j] = (src[j] && s2 + u < pl.s2) ? *reinterpret_cast<const float2*>(src[j] + o) : make_float2(0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < GQ; ++u)
@@ -528,8 +529,7 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
   }
   __syncthreads();
   // o_lat float4 items (token, 4 columns), eight per thread per pass; the
-  // loads of G splits go out together (a split index past the last reloads
-  // the last and is dropped).  Two tiles per wave keep G = 1: the registers
+  // loads of G splits go out together (splits past the last are not loaded).  Two tiles per wave keep G = 1: the registers
   // of four splits cost more than the round trips they save.  Partials in
   // fp16 (PO16) are four halves, 8 bytes, per item.
   {
@@ -554,9 +554,9 @@ __device__ void phase_oabsorb_m(const StepParams& p, int b, char* lds) {
         VT v[G][NI];
 #pragma unroll
         for (int u = 0; u < G; ++u) {
-          const size_t off = (size_t)min(s + u, NSP - 1) * p.NH * R / 4;  // in items
+          const size_t off = (size_t)(s + u) * p.NH * R / 4;  // in items
 #pragma unroll
-          for (int i = 0; i < NI; ++i) v[u][i] = src[i] ? src[i][off] : VT{};
+          for (int i = 0; i < NI; ++i) v[u][i] = (src[i] && s + u < NSP) ? src[i][off] : VT{};
         }
 #pragma unroll
         for (int u = 0; u < G; ++u) {
