@@ -253,10 +253,12 @@ Plan make_plan_mfma(const mla_gd_dims& d, Plan pl) {
   pl.mtb = T <= 16 ? 1 : (T <= 32 ? 2 : (T <= 64 ? 4 : 8));
   pl.ntb = cdiv(T, 16 * pl.mtb);
   pl.mt_pad = pl.ntb * pl.mtb;
-  // about one workgroup per CU for the 256-column tiles, two for the narrower
-  // ones (more split-K slabs would add partial-sum traffic for little gain)
+  // about one workgroup per CU, for the 128-column tiles too: at 32 tokens
+  // (cold steps) 256 workgroups against 512 took the down-projection from
+  // 12.3 to 11.3 us, the q-latent reduction (half the slabs) from 7.4 to 6.4
+  // and the o-projection from 11.7 to 10.7; 192 and 128 were slower again
   const int nc = mg_cols(pl.mtb);
-  const int target = nc >= 256 ? 256 : 512;
+  const int target = 256;
   pl.kt1 = cdiv(H, kMgK);
   pl.ntq1m = cdiv(Q, nc);
   pl.nt1m = pl.ntq1m + cdiv(KVR, nc);
