@@ -267,7 +267,7 @@ def router_measure(name: str, steps: int, warmup: int, cpu_budget: float) -> dic
     g = {k: v.to(dev) for k, v in inp.items()}
     out = (torch.empty((T, H), dtype=torch.bfloat16, device=dev), torch.empty((T, K), dtype=torch.int32, device=dev),
            torch.empty((T, E), dtype=torch.bfloat16, device=dev))
-    ws = torch.empty(workspace_size(T, H, E), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(workspace_size(T, H, E), dtype=torch.uint8, device=dev)
     flush = torch.zeros((1 << 30) // 4, dtype=torch.float32, device=dev)
 
     def run():

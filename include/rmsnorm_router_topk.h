@@ -17,7 +17,9 @@
  * stored in the input type but the router consumes it unrounded.  From 9
  * tokens on with bf16 inputs the products run on the matrix cores, with
  * hidden * gamma carried as two bf16 halves (about 16 significant bits, a
- * relative error near 2^-17 per product) against the bf16 weight.
+ * relative error near 2^-17 per product) against the bf16 weight.  A single
+ * token runs as one launch: the last workgroup to finish its share of the
+ * logits (an arrival counter in the workspace) selects the experts.
  *
  * Conventions: every tensor pointer is a device pointer on the current HIP
  * device, row-major; bf16 tensors and the workspace are 16-byte aligned, fp32
@@ -51,8 +53,10 @@ extern "C" {
  * Device workspace bytes for (n_tokens, hidden, n_experts), 0 if the shape is
  * unsupported.  Limits: 1 <= n_tokens <= 128 (the page's single-tile bound),
  * hidden a multiple of 128 (the page's) up to 65536, n_experts a multiple of 8
- * up to 1024.  The workspace holds split-K partial logits; it needs no
- * initialisation.
+ * up to 1024.  The workspace holds an arrival counter and the split-K
+ * partial logits.  It must be zero-filled before its first call; every call
+ * leaves the counter at zero again.  Calls that may overlap in time need
+ * separate workspaces.
  */
 size_t rmsnorm_router_topk_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_experts);
 

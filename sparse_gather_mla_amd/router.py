@@ -60,7 +60,7 @@ def rmsnorm_router_topk(hidden_states, gamma, router_weights, router_bias=None, 
     normed, idx, aff = out
     nbytes = workspace_size(T, H, E)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)  # the counter starts at zero
     s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
     dtype = RT_DTYPE_FP16 if dt_in == torch.float16 else RT_DTYPE_BF16
     rc = lib.rmsnorm_router_topk_typed(dtype, hidden_states.data_ptr(), gamma.data_ptr(), router_weights.data_ptr(),

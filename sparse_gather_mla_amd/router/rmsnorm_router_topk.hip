@@ -2,7 +2,8 @@
 // "RMSNorm Router Top-K A2AV Kernel API Reference" page ("API Reference";
 // "Notes": top-K on the raw logits, the activation on the selected experts).
 //
-// Two kernels, each templated on the input type (bf16 or fp16, the page's two):
+// Two kernels, each templated on the input type (bf16 or fp16, the page's two);
+// a single token runs both in one launch, k_rt_one_token (below):
 //   k_rt_partial  split-K GEMV over router_weights with the RMSNorm scale folded
 //                 out: workgroup (64-expert tile, slab of hidden, group of 8
 //                 tokens) loads its weight slab (16-byte non-temporal loads)
@@ -43,6 +44,7 @@ constexpr int kMaxT = 128, kMaxH = 65536, kMaxE = 1024, kMaxK = 32;
 constexpr int kTargetWG = 112;  // GEMV workgroups before token groups: few slabs keep the select reduction short
 constexpr int kEPL = kMaxE / kWave;  // logits per lane of the top-K wave
 constexpr int kXPre = 4;             // 16-byte pieces of x (and gamma) per thread loaded with the partials
+constexpr size_t kCounterBytes = 256;  // workspace head: the one-token launch's arrival counter
 
 struct RtPlan {
   int ntile, s, ks;
@@ -112,19 +114,20 @@ __device__ __forceinline__ uint32_t pack2out(float a, float b) {
   }
 }
 
-template <bool F16>
-__global__ __launch_bounds__(kBlock) void k_rt_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
-                                                      const uint16_t* __restrict__ W, int T, int H, int E, int ks,
-                                                      int ntile, int s, float* __restrict__ part) {
-  __shared__ float xs[kNtt * kMaxKs];
-  __shared__ float red[3 * kNtt * kTile];
+// NTT: tokens per pass (and the width of the LDS stages).
+template <bool F16, int NTT = kNtt, class Sy = HandoffNone>
+__device__ __forceinline__ void rt_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                           const uint16_t* __restrict__ W, int T, int H, int E, int ks, int ntile,
+                                           int s, float* __restrict__ part, const Sy& sy = Sy()) {
+  __shared__ float xs[NTT * kMaxKs];
+  __shared__ float red[3 * NTT * kTile];
   const int tile = blockIdx.x % ntile, slab = (blockIdx.x / ntile) % s, tg = blockIdx.x / (ntile * s);
   const int c0 = tile * kTW, nc = min(kTW, E - c0);
   const int k0 = slab * ks, kss = min(ks, H - k0);
   // the slab fits one batch of loads: gemv_tile issues no further weight loads
-  u32x4 v[gemv_unroll(kNtt)];
-  gemv_first<gemv_unroll(kNtt)>(W, E, k0, kss, c0, nc, v);
-  const int t0 = tg * kNtt, nt = min(kNtt, T - t0);
+  u32x4 v[gemv_unroll(NTT)];
+  gemv_first<gemv_unroll(NTT)>(W, E, k0, kss, c0, nc, v);
+  const int t0 = tg * NTT, nt = min(NTT, T - t0);
   // one 16-byte piece of x and of gamma per thread (nt * kss / 8 <= 256 pieces)
   const int g8 = kss / 8;
   const int tt = threadIdx.x / g8, r8 = threadIdx.x % g8;
@@ -136,8 +139,15 @@ __global__ __launch_bounds__(kBlock) void k_rt_partial(const uint16_t* __restric
     for (int i = 0; i < 8; ++i) xs[tt * kMaxKs + 8 * r8 + i] = xv[i] * gv[i];
   }
   __syncthreads();
-  gemv_tile<kNtt, gemv_unroll(kNtt), HandoffNone, F16>(W, E, k0, kss, c0, nc, xs, kMaxKs, nt,
-                                                      part + ((size_t)slab * T + t0) * E, (size_t)E, red, v);
+  gemv_tile<NTT, gemv_unroll(NTT), Sy, F16>(W, E, k0, kss, c0, nc, xs, kMaxKs, nt,
+                                             part + ((size_t)slab * T + t0) * E, (size_t)E, red, v, sy);
+}
+
+template <bool F16>
+__global__ __launch_bounds__(kBlock) void k_rt_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                                      const uint16_t* __restrict__ W, int T, int H, int E, int ks,
+                                                      int ntile, int s, float* __restrict__ part) {
+  rt_partial<F16>(x, gamma, W, T, H, E, ks, ntile, s, part);
 }
 
 // Sixteen zero bytes for the GEMM's padding loads (never written).
@@ -240,17 +250,17 @@ __device__ __forceinline__ unsigned wave_reduce_u(unsigned v) {
   return op(lo, hi);
 }
 
-template <bool F16>
-__global__ __launch_bounds__(kBlock) void k_rt_select(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
-                                                     const float* __restrict__ bias, int T, int H, int E, int K,
-                                                     int s, float eps, int act, const float* __restrict__ part,
-                                                     uint16_t* __restrict__ normed, int32_t* __restrict__ idx,
-                                                     uint16_t* __restrict__ aff) {
+template <bool F16, class Sy = HandoffNone>
+__device__ __forceinline__ void rt_select(int t, const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                          const float* __restrict__ bias, int T, int H, int E, int K, int s,
+                                          float eps, int act, const float* __restrict__ part,
+                                          uint16_t* __restrict__ normed, int32_t* __restrict__ idx,
+                                          uint16_t* __restrict__ aff, const Sy& sy = Sy()) {
   __shared__ __attribute__((aligned(16))) float zl[kMaxE];  // float4 stores of the partial reduction
   __shared__ float scratch[kBlock / kWave];
   __shared__ float4 rscratch[kBlock];
-  static_assert(kBlock * 8 + kMaxK * 8 <= sizeof(float4) * kBlock, "rank top-K scratch");
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  static_assert(kBlock * 8 + (kBlock / kWave) * kMaxK * 8 + kMaxK * 8 <= sizeof(float4) * kBlock, "top-K scratch");
+  const int tid = threadIdx.x, lane = tid & 63;
   const uint16_t* xr = x + (size_t)t * H;
   const int nv = H / 8;  // 16-byte pieces of the row
 
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(kBlock) void k_rt_select(const uint16_t* __restrict
     const int e = tid + u * kBlock;
     bz[u] = (bias && e < E) ? bias[e] : 0.f;
   }
-  reduce_parts4(part + (size_t)t * E, (size_t)T * E, s, E / 4, E / 4, 0, zl, reinterpret_cast<float*>(rscratch));
+  reduce_parts4(part + (size_t)t * E, (size_t)T * E, s, E / 4, E / 4, 0, zl, reinterpret_cast<float*>(rscratch), sy);
 
   // sum of x^2 over the row (pieces past the first kXPre per thread loaded now)
   float sq = 0.f;
@@ -318,31 +328,60 @@ __global__ __launch_bounds__(kBlock) void k_rt_select(const uint16_t* __restrict
       put(i, *reinterpret_cast<const uint4*>(xr + 8 * i), *reinterpret_cast<const uint4*>(gamma + 8 * i));
   };
   if (E <= kBlock) {
-    // top-K by rank, one expert per thread: expert e's rank is the number of
-    // experts before it (a larger key, or the same key and a lower index),
-    // counted against every key at once as one 64-bit comparison of (key,
-    // kMaxE - 1 - expert); the experts of rank < K are the selection, in
-    // order.  (The keys and the selection reuse the reduction's scratch.)
-    unsigned long long* ck = reinterpret_cast<unsigned long long*>(rscratch);
-    float* selz = reinterpret_cast<float*>(ck + kBlock);
+    // Two levels by rank, one expert per thread.  A key is the 64-bit (order
+    // key of the logit, kMaxE - 1 - expert), unique per expert, so ranks need
+    // no tie rule; 0 marks no expert.  Each expert is first ranked within its
+    // wave's 64 (the number of larger keys there); the K best of each wave are
+    // the candidates, which hold the global top K.  Wave 0 then ranks the 4K
+    // candidates; those of rank < K are the selection, in order.  Every LDS
+    // read of a pass is issued before its compares (one wave per SIMD: a
+    // read's latency is not hidden by another wave).  (Keys, candidates and
+    // selection reuse the reduction's scratch.)
+    unsigned long long* ck = reinterpret_cast<unsigned long long*>(rscratch);   // [kBlock] keys
+    unsigned long long* cand = ck + kBlock;                                     // [waves * K]
+    float* selz = reinterpret_cast<float*>(cand + (kBlock / kWave) * kMaxK);
     int* sele = reinterpret_cast<int*>(selz + kMaxK);
-    const unsigned long long mine =
+    const int wv = tid >> 6;
+    const unsigned long long key =
         tid < E ? ((unsigned long long)order_key(zl[tid]) << 32) | (unsigned)(kMaxE - 1 - tid) : 0ull;
-    ck[tid] = mine;
+    ck[tid] = key;
+    if (tid < (kBlock / kWave) * K) cand[tid] = 0ull;
     __syncthreads();
-    int rank = 0;
-#pragma unroll 4
-    for (int j = 0; j < E; j += 2) {  // E % 8 == 0
-      const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(ck + j);
-      rank += (c.x > mine ? 1 : 0) + (c.y > mine ? 1 : 0);
-    }
-    if (tid < E) {
-      if (rank < K) {
-        selz[rank] = zl[tid];
-        sele[rank] = tid;
+    // rank of this expert within its wave
+    {
+      const ulonglong2* w = reinterpret_cast<const ulonglong2*>(ck + kWave * wv);
+      int lr = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        ulonglong2 c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) c[u] = w[16 * h + u];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) lr += (c[u].x > key ? 1 : 0) + (c[u].y > key ? 1 : 0);
       }
-      zl[tid] = 0.f;  // the affinity row, selected entries filled in below
+      if (lr < K) cand[wv * K + lr] = key;  // a wave with fewer than K experts leaves zero keys
     }
+    __syncthreads();
+    const int nc = (kBlock / kWave) * K;  // <= 128, even
+    const unsigned long long mine = tid < nc && tid < kWave * 2 ? cand[tid] : 0ull;
+    int rank = 0;
+    if (tid < kWave * 2) {  // waves 0 and 1 (nc <= 128)
+      for (int j0 = 0; j0 < nc; j0 += 32) {
+        ulonglong2 c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) c[u] = j0 + 2 * u < nc ? reinterpret_cast<const ulonglong2*>(cand + j0)[u]
+                                                             : ulonglong2{0ull, 0ull};
+#pragma unroll
+        for (int u = 0; u < 16; ++u) rank += (c[u].x > mine ? 1 : 0) + (c[u].y > mine ? 1 : 0);
+      }
+    }
+    if (mine != 0ull && rank < K) {
+      const int e = kMaxE - 1 - (int)(unsigned)(mine & 0xffffffffu);
+      selz[rank] = zl[e];
+      sele[rank] = e;
+    }
+    __syncthreads();
+    if (tid < E) zl[tid] = 0.f;  // the affinity row, selected entries filled in below
     __syncthreads();
     if (tid < kWave) {
       // the activations, lane k for the k-th selected expert; the masked
@@ -442,6 +481,51 @@ __global__ __launch_bounds__(kBlock) void k_rt_select(const uint16_t* __restrict
   put_mine();
 }
 
+template <bool F16>
+__global__ __launch_bounds__(kBlock) void k_rt_select(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                                     const float* __restrict__ bias, int T, int H, int E, int K,
+                                                     int s, float eps, int act, const float* __restrict__ part,
+                                                     uint16_t* __restrict__ normed, int32_t* __restrict__ idx,
+                                                     uint16_t* __restrict__ aff) {
+  rt_select<F16>(blockIdx.x, x, gamma, bias, T, H, E, K, s, eps, act, part, normed, idx, aff);
+}
+
+// Partial logits read back by the last workgroup of the same launch:
+// device-scope loads (they bypass this XCD's L2, which may hold stale lines).
+struct DevLoads {
+  static constexpr bool kWeightsFirst = false;
+  __device__ __forceinline__ void wait() const {}
+  __device__ __forceinline__ float ld(const float* p) const { return ld_dev(p); }
+  __device__ __forceinline__ float4 ld4(const float* p) const { return ld_dev4(p); }
+};
+
+// One token in one launch.  Every workgroup computes its tile and slab of the
+// partial logits (as k_rt_partial) and stores them with device scope, waits
+// for those stores, then counts itself in the arrival counter (a device-scope
+// atomic); the last to arrive resets the counter to zero and runs the select
+// of the token (as k_rt_select), reading the partials with device-scope loads.
+// The partials are added in slab order whichever workgroup is last, so the
+// result is the two-kernel path's, bit for bit.
+template <bool F16>
+__global__ __launch_bounds__(kBlock) void k_rt_one_token(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                                        const uint16_t* __restrict__ W, const float* __restrict__ bias,
+                                                        int H, int E, int K, int ks, int ntile, int s, float eps,
+                                                        int act, float* __restrict__ part, unsigned* __restrict__ cnt,
+                                                        uint16_t* __restrict__ normed, int32_t* __restrict__ idx,
+                                                        uint16_t* __restrict__ aff) {
+  __shared__ unsigned arrived;
+  rt_partial<F16, 1>(x, gamma, W, 1, H, E, ks, ntile, s, part, HandoffDevStores());
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmcnt<0>();  // this workgroup's partial stores are complete
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (arrived != (unsigned)(ntile * s) - 1u) return;
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  rt_select<F16>(0, x, gamma, bias, 1, H, E, K, s, eps, act, part, normed, idx, aff, DevLoads());
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace rt
@@ -456,7 +540,7 @@ size_t rmsnorm_router_topk_workspace_size(int32_t n_tokens, int32_t hidden, int3
     const rt::RtPlanM pm = rt::rt_plan_m(n_tokens, hidden, n_experts);
     b = std::max(b, rt::align256((size_t)pm.s * n_tokens * n_experts * sizeof(float)));
   }
-  return b;
+  return rt::kCounterBytes + b;
 }
 
 int rmsnorm_router_topk_typed(int32_t dtype, const void* hidden_states, const void* gamma, const void* router_weights,
@@ -482,7 +566,15 @@ int rmsnorm_router_topk_typed(int32_t dtype, const void* hidden_states, const vo
   const auto* xh = (const uint16_t*)hidden_states;
   const auto* gh = (const uint16_t*)gamma;
   const auto* wh = (const uint16_t*)router_weights;
-  float* part = static_cast<float*>(workspace);
+  unsigned* cnt = static_cast<unsigned*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+  if (n_tokens == 1) {
+    const RtPlan pl = rt_plan(1, hidden, n_experts);
+    hipLaunchKernelGGL(f16 ? k_rt_one_token<true> : k_rt_one_token<false>, dim3(pl.ntile * pl.s), dim3(kBlock), 0, s,
+                       xh, gh, wh, router_bias, hidden, n_experts, top_k, pl.ks, pl.ntile, pl.s, eps, act, part, cnt,
+                       (uint16_t*)normed_out, topk_indices, (uint16_t*)affinities);
+    return hipGetLastError() == hipSuccess ? RT_OK : RT_E_HIP;
+  }
   int slabs;
   if (!f16 && n_tokens >= kMfmaMinT) {
     const RtPlanM pm = rt_plan_m(n_tokens, hidden, n_experts);

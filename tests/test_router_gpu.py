@@ -113,3 +113,34 @@ def test_router_exact_ties_pick_lower_experts():
     got, aff = _check(4, 256, 32, 6, "sigmoid", False, seed=5, zero_weights=True)
     assert np.array_equal(got, np.tile(np.arange(6), (4, 1)))
     assert np.all(aff[:, :6] == 0.5) and np.all(aff[:, 6:] == 0)
+
+
+@pytest.mark.parametrize("H,E,K,act", [
+    (1152, 72, 5, "softmax"),   # a 64 + 8 expert split
+    (256, 1024, 32, "sigmoid"),  # the top-K wave (more than 256 experts)
+])
+def test_router_one_token_shapes(H, E, K, act):
+    """One token runs as a single launch whose last workgroup selects."""
+    _check(1, H, E, K, act, True, seed=81 + E)
+
+
+def test_router_one_token_repeats_on_one_workspace():
+    """The single-token launch counts its workgroups in the workspace and the
+    last one resets the counter: three calls on one workspace give the same
+    bits, agree with the oracle, and leave the counter at zero."""
+    from sparse_gather_mla_amd.router import workspace_size
+
+    T, H, E, K = ROUTER_CONFIGS["router_t1"]
+    _check(T, H, E, K, "sigmoid", True, seed=91)
+    inp = make_router_inputs(T, H, E, 91, True)
+    g = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    ws = torch.zeros(workspace_size(T, H, E), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        normed, idx, aff = rmsnorm_router_topk(g["hidden_states"], g["gamma"], g["router_weights"], g["router_bias"],
+                                               1e-6, K, "sigmoid", workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((normed.clone(), idx.clone(), aff.clone()))
+        assert int(ws[:4].view(torch.int32).item()) == 0
+    for o in outs[1:]:
+        assert all(torch.equal(a, b) for a, b in zip(o, outs[0]))
