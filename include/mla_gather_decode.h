@@ -166,7 +166,7 @@ typedef struct mla_gd_tensors {
   const float* kv_norm_w;      /* [r] fp32: RMSNorm gamma of the KV latent */
   const void* q_absorb_w;      /* [nh, dn, r] bf16: nope half of wkv_b (nope query -> latent) */
   const void* out_absorb_w;    /* [nh, dv, r] bf16: value half of wkv_b (latent output -> value width) */
-  const void* o_proj_w;        /* [nh*dv, hidden] bf16: this rank's shard of the o-projection */
+  const void* o_proj_w;        /* [nh*dv, hidden] bf16: o-projection rows of this rank's heads */
   const float* cos_table;      /* [T, dr/2] fp32: cosine table of interleaved RoPE */
   const float* sin_table;      /* [T, dr/2] fp32: sine table of interleaved RoPE */
   void* kv_cache;              /* [n_blocks, 1, block_size, kv_row] bf16, MUTATED IN PLACE:
@@ -174,7 +174,7 @@ typedef struct mla_gd_tensors {
   const int32_t* slot_mapping; /* [T] int32: flat cache row that receives token t's new row */
   const int32_t* block_table;  /* [n_seqs, max_blocks_per_seq] int32: per sequence, logical block ->
                                   physical block; n_seqs = T without token_seq */
-  const int32_t* positions;    /* [T] int32: this step's absolute position per token */
+  const int32_t* positions;    /* [T] int32: absolute position of each token in its sequence */
   const int32_t* gather_indices; /* [T, n_prior] int32: selected absolute prior positions, unsorted */
   void* out;                   /* [T, hidden] bf16, written: this rank's attention-block output
                                   (partial o-projection; no residual add, no cross-rank reduction) */

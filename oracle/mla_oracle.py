@@ -46,8 +46,8 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float64 values to the nearest bfloat16 value, ties to even.
 
     bfloat16 keeps 8 significant bits and fp32's exponent range.  Used only
-    for the cache row the step stores ("API Reference", ``kv_cache``: the
-    front-fold writes this step's row and the core reads rows back).
+    for the cache row the step stores (the ``kv_cache`` parameter of "API
+    Reference": the cache is updated in place and later gathered from).
     """
     x = np.asarray(x, dtype=F64)
     out = np.array(x, copy=True)
@@ -64,9 +64,9 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm over the last axis: ``x / sqrt(mean(x^2) + eps) * gamma``.
 
-    The page gives an fp32 RMSNorm gamma for the layer input, the query latent
-    and the KV latent, and one ``norm_eps`` "for every RMSNorm in the
-    front-fold" ("API Reference": ``input_norm_w``, ``q_norm_w``,
+    The page gives fp32 RMSNorm scales for three places (the layer input, the
+    query latent and the KV latent) and a single ``norm_eps`` that all three
+    norms share ("API Reference": ``input_norm_w``, ``q_norm_w``,
     ``kv_norm_w``, ``norm_eps``).
     """
     x = np.asarray(x, dtype=F64)
@@ -164,8 +164,8 @@ def attention_core(q_lat: np.ndarray, q_pe: np.ndarray, keys: np.ndarray, scale:
 
 def output_projection(o_lat: np.ndarray, out_absorb_w: np.ndarray, o_proj_w: np.ndarray) -> np.ndarray:
     """``out_absorb_w`` maps each head's latent output to ``v_head_dim``; the
-    heads are concatenated (head-major) and multiplied by this rank's shard of
-    the o-projection ("API Reference": ``out_absorb_w``, ``o_proj_w``)."""
+    heads are concatenated (head-major) and multiplied by the o-projection
+    rows of this rank's heads ("API Reference": ``out_absorb_w``, ``o_proj_w``)."""
     nh, dv, r = out_absorb_w.shape
     o_v = np.empty((nh, dv), dtype=F64)
     for h in range(nh):
@@ -213,9 +213,9 @@ def mla_gather_decode_step(inp: Dict[str, np.ndarray], read_rows: RowReader,
     caller's pool is never modified.
 
     Order of effects: the front-fold of every token writes its row into the
-    cache first, then the core gathers ("API Reference", ``kv_cache``: the
-    front-fold writes this step's row, and the core reads the selected prior
-    rows back).  So a token that selects the position of another token of its
+    cache first, then the core gathers (the ``kv_cache`` parameter of "API
+    Reference": the in-place update comes before the gather, so the gathered
+    rows can include the ones stored in this step).  So a token that selects the position of another token of its
     sequence in this step (an earlier one; later ones are causally masked)
     reads that token's stored row, exactly as if the tokens had run as
     successive single-token steps in position order.
