@@ -32,7 +32,7 @@
  *   - Arithmetic: bf16 operands, fp32 accumulation.  Projections of steps
  *     with more than 3 tokens carry each fp32 activation as two bf16 halves
  *     (about 16 significant bits), except the o-projection of steps with more
- *     than 32 tokens, which takes its input as plain bf16.  In steps of more
+ *     than 16 tokens, which takes its input as plain bf16.  In steps of more
  *     than 3 tokens the attention core hands its per-split latent outputs,
  *     each a weighted mean of cache rows, to the output absorption in fp16
  *     (except with 17 to 64 heads at kv_lora_rank >= 128): latent cache values

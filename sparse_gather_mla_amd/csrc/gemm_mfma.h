@@ -8,7 +8,7 @@
 // meet the weight (two MFMAs per fragment): about 16 significant bits.  Up to
 // 32 tokens the projections stay bound by the weight stream even with the
 // matrix work doubled.  A GEMM can also read the hi halves alone (AH = 1),
-// which the o-projection of 64- and 128-token blocks does (phases_mfma.h).
+// which the o-projection of 32- to 128-token blocks does (phases_mfma.h).
 //
 // Tiles: 16 tokens (an m-tile) x NC columns (64 to 256) x 32 k (a k-step).  A
 // workgroup owns one NC-column tile, one K slab and a block of MTB m-tiles;

@@ -454,12 +454,13 @@ __host__ __device__ constexpr int oabsorb_hdr_bytes(int mtb, int nsplit) {
 }
 constexpr int kOabsMaxKs = 16;  // kv_lora_rank <= 512
 
-// Activation halves the o-projection reads (gemm_mfma.h): blocks of 64 and
-// 128 tokens take o_v as plain bf16 (its hi half).  There the doubled matrix
-// work of the hi/lo products outweighs the weight stream, and o_v is the
+// Activation halves the o-projection reads (gemm_mfma.h): blocks of 32 to
+// 128 tokens take o_v as plain bf16 (its hi half).  There the hi/lo products
+// and the second half's loads cost more than the weight stream can hide
+// (at 128 tokens the doubled matrix work alone outweighs it), and o_v is the
 // path's last activation: its rounding reaches the output only through the
 // sum over n_heads * v_head_dim products.
-__host__ __device__ constexpr int oproj_ah(int mtb) { return mtb >= 4 ? 1 : 2; }
+__host__ __device__ constexpr int oproj_ah(int mtb) { return mtb >= 2 ? 1 : 2; }
 
 // Q5 output tiles per wave.  With nq5 > 1 parts per (head, token block) each
 // workgroup takes 4*Q5 of the 16-row output tiles (and combines the splits
