@@ -509,7 +509,7 @@ def copy_bandwidth_gbps(nbytes: int = 1 << 30, reps: int = 10) -> float:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="all",
                     help="one workload, or 'all': ds32_slice as the headline plus the other n_prior=2048 configs")
