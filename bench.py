@@ -104,8 +104,10 @@ def measured_traffic(kernel: str, workload: str):
     with open(path) as f:
         rec = json.load(f)
     w = rec.get(workload, {})
-    # matrix-core-path kernels carry an _m in their symbol, the many-heads cores an _rs or _wide
-    ent = w.get(kernel) or w.get(kernel + "_m") or w.get(kernel + "_rs") or w.get(kernel + "_wide")
+    # matrix-core-path kernels carry an _m in their symbol, the many-heads cores an _rs or _wide, the
+    # one-token kernels compiled for the DeepSeek-V3.2 shape an _fx
+    ent = (w.get(kernel) or w.get(kernel + "_m") or w.get(kernel + "_rs") or w.get(kernel + "_wide")
+           or w.get(kernel + "_fx"))
     if not ent or ent.get("source_digest") != source_digest():
         return None
     return ent.get("bytes_per_launch")

@@ -30,7 +30,8 @@
 #include "mfma_util.h"
 #include "step_params.h"
 
-namespace mla {
+namespace MLA_PHASE_NS {
+using namespace ::mla;
 
 constexpr int kCoreChunk = 32;  // gathered rows per step
 constexpr int kCoreRing = 3;    // chunk buffers in flight
@@ -158,7 +159,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   constexpr int NI = (kCoreChunk * NPMAX + 64 * NW - 1) / (64 * NW);  // loads per wave per chunk
   constexpr int BUF = core_buf_bytes(NT);
   const Plan& pl = p.pl;
-  const int KVR = p.KVR;
+  const int KVR = MLA_D(KVR);
   const int ks = (KVR + 31) >> 5;    // score k-steps
   const int npieces = KVR >> 3;      // 16-byte pieces of a cache row
   const int npad = (4 * ks) | 1;     // LDS row stride in pieces (odd, <= NPMAX)
@@ -171,8 +172,8 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   const int nhb = pl.core_nhb;
   const int pair = (b / (8 * nhb)) * 8 + (b % 8);
   const int hb = (b / 8) % nhb;
-  if (pair >= pl.T * pl.nsplit) return;  // padding workgroup (whole group exits before any barrier)
-  const int t = pair / pl.nsplit, split = pair % pl.nsplit;
+  if (pair >= MLA_PL(T) * MLA_PL(nsplit)) return;  // padding workgroup (whole group exits before any barrier)
+  const int t = pair / MLA_PL(nsplit), split = pair % MLA_PL(nsplit);
   const int j0 = split * pl.ps, j1 = min(p.P, j0 + pl.ps);
   const int nrows = j1 - j0;
   const int nchunks = (nrows + kCoreChunk - 1) / kCoreChunk;
@@ -195,8 +196,8 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
     for (int j = 0; j < KSW; ++j) {
       const int k = 32 * (kb + j) + 8 * g;
       u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (j < nj && head < p.NH && k < KVR)
-        v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * p.NH + head) * KVR + k);
+      if (j < nj && head < MLA_D(NH) && k < KVR)
+        v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * MLA_D(NH) + head) * KVR + k);
       qf[j] = __builtin_bit_cast(bf16x8_t, v);
     }
   };
@@ -430,8 +431,8 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
   wait_vmcnt<0>();  // every chunk loaded was waited for; kept as a guard
 
   // this split's partial result; waves of one head group hold identical (m, l)
-  const size_t pb = ((size_t)t * pl.nsplit + split) * p.NH;
-  if (cs == 0 && g == 0 && head < p.NH) {
+  const size_t pb = ((size_t)t * MLA_PL(nsplit) + split) * MLA_D(NH);
+  if (cs == 0 && g == 0 && head < MLA_D(NH)) {
     hooks.st(p.pm + pb + head, m_run);
     hooks.st(p.pden + pb + head, l_run);
   }
@@ -451,7 +452,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = hbase + 4 * g + i;
-        if (h < p.NH) po16[(pb + h) * R + 16 * (cs * NTW + n) + l16] = (_Float16)(o[n][i] * inv[i]);
+        if (h < MLA_D(NH)) po16[(pb + h) * R + 16 * (cs * NTW + n) + l16] = (_Float16)(o[n][i] * inv[i]);
       }
   } else {
 #pragma unroll
@@ -459,7 +460,7 @@ __device__ __attribute__((always_inline)) void core_phase(const StepParams& p, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = hbase + 4 * g + i;
-        if (h < p.NH) hooks.st(p.po + (pb + h) * R + 16 * (cs * NTW + n) + l16, o[n][i]);
+        if (h < MLA_D(NH)) hooks.st(p.po + (pb + h) * R + 16 * (cs * NTW + n) + l16, o[n][i]);
       }
   }
 }
@@ -504,7 +505,7 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
   float* alph = reinterpret_cast<float*>(lds + core_rs_ofs_alpha(NT));  // [ht][16]
   float* lsum = reinterpret_cast<float*>(lds + core_rs_ofs_l(NT));      // [ht][16]
   const Plan& pl = p.pl;
-  const int KVR = p.KVR;
+  const int KVR = MLA_D(KVR);
   const int ks = (KVR + 31) >> 5;  // score k-steps
   const int npieces = KVR >> 3;    // 16-byte pieces of a cache row
   const int npad = (4 * ks) | 1;   // LDS row stride in pieces (odd, <= NPMAX)
@@ -516,8 +517,8 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
   const int nhb = pl.core_nhb;
   const int pair = (b / (8 * nhb)) * 8 + (b % 8);
   const int hb = (b / 8) % nhb;
-  if (pair >= pl.T * pl.nsplit) return;  // padding workgroup (whole group exits before any barrier)
-  const int t = pair / pl.nsplit, split = pair % pl.nsplit;
+  if (pair >= MLA_PL(T) * MLA_PL(nsplit)) return;  // padding workgroup (whole group exits before any barrier)
+  const int t = pair / MLA_PL(nsplit), split = pair % MLA_PL(nsplit);
   const int j0 = split * pl.ps, j1 = min(p.P, j0 + pl.ps);
   const int nrows = j1 - j0;
   const int nchunks = (nrows + kCoreChunk - 1) / kCoreChunk;
@@ -588,8 +589,8 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
   for (int kk = 0; kk < KSMAX; ++kk) {
     const int k = 32 * kk + 8 * g;
     u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (kk < ks && head < p.NH && k < KVR)
-      v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * p.NH + head) * KVR + k);
+    if (kk < ks && head < MLA_D(NH) && k < KVR)
+      v = *reinterpret_cast<const u32x4_t*>(p.qcat + ((size_t)t * MLA_D(NH) + head) * KVR + k);
     qf[kk] = __builtin_bit_cast(bf16x8_t, v);
   }
   wait_vmcnt<0>();
@@ -717,8 +718,8 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
   // (m, l): the waves of a head tile hold the same m; l adds the two halves
   if (rh == 1 && g == 0) lsum[ht * 16 + l16] = l_run;
   __syncthreads();
-  const size_t pb = ((size_t)t * pl.nsplit + split) * p.NH;
-  if (rh == 0 && g == 0 && head < p.NH) {
+  const size_t pb = ((size_t)t * MLA_PL(nsplit) + split) * MLA_D(NH);
+  if (rh == 0 && g == 0 && head < MLA_D(NH)) {
     p.pm[pb + head] = m_run;
     p.pden[pb + head] = l_run + lsum[ht * 16 + l16];
   }
@@ -730,7 +731,7 @@ __device__ __attribute__((always_inline)) void core_phase_rs(const StepParams& p
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = hblk + 16 * q + 4 * g + i;
-        if (h < p.NH) p.po[(pb + h) * R + 16 * (wave * NTW + n) + l16] = o[q][n][i];
+        if (h < MLA_D(NH)) p.po[(pb + h) * R + 16 * (wave * NTW + n) + l16] = o[q][n][i];
       }
 }
 
@@ -783,7 +784,7 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
   char* sink = lds + core_wide_ofs_sink(NT);
   float* bias = reinterpret_cast<float*>(lds + core_wide_ofs_bias(NT));
   const Plan& pl = p.pl;
-  const int KVR = p.KVR;
+  const int KVR = MLA_D(KVR);
   const int ks = (KVR + 31) >> 5;  // score k-steps
   const int npieces = KVR >> 3;    // 16-byte pieces of a cache row
   const int npad = 4 * ks + 2;     // LDS row stride in pieces (<= NPMAX)
@@ -795,8 +796,8 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
   const int nhb = pl.core_nhb;
   const int pair = (b / (8 * nhb)) * 8 + (b % 8);
   const int hb = (b / 8) % nhb;
-  if (pair >= pl.T * pl.nsplit) return;  // padding workgroup (whole group exits before any barrier)
-  const int t = pair / pl.nsplit, split = pair % pl.nsplit;
+  if (pair >= MLA_PL(T) * MLA_PL(nsplit)) return;  // padding workgroup (whole group exits before any barrier)
+  const int t = pair / MLA_PL(nsplit), split = pair % MLA_PL(nsplit);
   const int j0 = split * pl.ps, j1 = min(p.P, j0 + pl.ps);
   const int nrows = j1 - j0;
   const int nchunks = (nrows + kCoreChunk - 1) / kCoreChunk;
@@ -859,8 +860,8 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
   // (loaded from a clamped address and zeroed past the heads or the row)
   bf16x8_t qf[KSMAX];
   {
-    const bool hl = head < p.NH;
-    const uint16_t* qrow = p.qcat + ((size_t)t * p.NH + (hl ? head : 0)) * KVR;
+    const bool hl = head < MLA_D(NH);
+    const uint16_t* qrow = p.qcat + ((size_t)t * MLA_D(NH) + (hl ? head : 0)) * KVR;
 #pragma unroll
     for (int kk = 0; kk < KSMAX; ++kk) {
       const int k = 32 * kk + 8 * g;
@@ -986,8 +987,8 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
   wait_vmcnt<0>();  // every chunk loaded was waited for; kept as a guard
 
   const float l_tot = sum4groups(l_run);
-  const size_t pb = ((size_t)t * pl.nsplit + split) * p.NH;
-  if (head < p.NH) {
+  const size_t pb = ((size_t)t * MLA_PL(nsplit) + split) * MLA_D(NH);
+  if (head < MLA_D(NH)) {
     if (g == 0) {
       p.pm[pb + head] = m_run;
       p.pden[pb + head] = l_tot;
@@ -1010,4 +1011,4 @@ __device__ __attribute__((always_inline)) void core_phase_wide(const StepParams&
   }
 }
 
-}  // namespace mla
+}  // namespace MLA_PHASE_NS

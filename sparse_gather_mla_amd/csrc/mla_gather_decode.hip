@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "../../include/mla_gather_decode.h"
+#include "fixed_shape.h"
 #include "phases.h"
 #include "phases_mfma.h"
 #include "single_launch.h"
@@ -586,6 +587,7 @@ hipError_t set_lds_limits(const mla_gd_dims& d) {
                        (const void*)k_oabsorb_m<1, 2, true>, (const void*)k_oabsorb_m<2, 2, true>};
   for (const void* k : big)
     if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
+  if (e == hipSuccess) e = fixed_shape_init();
   return e;
 }
 
@@ -773,12 +775,16 @@ hipError_t launch_kernels(const StepParams& p, hipStream_t s, void* const* event
     L(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl);
     L(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll);
   } else if (!pl.mfma) {
-    L(pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll);
-    L(pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll);
-    L(pick_absorb(ntt), dim3(p.NH * pl.ncc3 + T), blk, gll);
-    L(pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0);
-    L(k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl);
-    L(pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll);
+    // the DeepSeek-V3.2 one-token shape runs the same phases compiled with
+    // its sizes as constants (fixed_shape.h), the same grids and LDS
+    const bool fx = fixed_shape_applies(p);
+    const FixedShapeKernels& F = fixed_shape_kernels();
+    L(fx ? F.down : pick_down(ntt), dim3(pl.nt1 * pl.s1 + pl.n_idx_wg), blk, gll);
+    L(fx ? F.qup : pick_qup(ntt), dim3(pl.nt2 * pl.s2 + T * pl.nkv), blk, gll);
+    L(fx ? F.absorb : pick_absorb(ntt), dim3(p.NH * pl.ncc3 + T), blk, gll);
+    L(fx ? F.core : pick_core(pl, p.R), dim3(core_grid(pl)), core_blk, 0);
+    L(fx ? F.oabsorb : k_oabsorb, dim3(p.NH * pl.nc5 * pl.nt5c), blk, gl);
+    L(fx ? F.oproj : pick_oproj(ntt), dim3(pl.nt6 * pl.s6), blk, gll);
   } else {
     L(k_prep, dim3(pl.n_idx_wg + T * pl.nxc), blk, 1024);
     const dim3 gblk(64 * mg_waves(pl.mtb));  // GEMM workgroups: eight waves for 128-token blocks

@@ -26,7 +26,8 @@
 #include "step_params.h"
 #include "mla_gather_decode.h"
 
-namespace mla {
+namespace MLA_PHASE_NS {
+using namespace ::mla;
 
 // LDS of a GEMV phase that passes over NTT tokens at a time (floats):
 // xs [NTT][512], red [3][NTT][512], scratch [1024], aux [1024]
@@ -55,7 +56,7 @@ __device__ __forceinline__ float inv_rms(float sumsq, int n, float eps) {
 // block-table column or block id is out of range is masked too, and reported.
 template <class Sy = HandoffNone>
 __device__ __forceinline__ void index_build(const StepParams& p, int idx, const Sy& sy = Sy()) {
-  if (idx >= p.pl.T * p.P) return;
+  if (idx >= MLA_PL(T) * p.P) return;
   const int t = idx / p.P;
   const int g = p.gidx[idx];
   const int ps = p.pos[t];
@@ -63,7 +64,7 @@ __device__ __forceinline__ void index_build(const StepParams& p, int idx, const 
   if (g >= 0 && g <= ps) {
     const int col = g / p.BS;
     const int sq = p.tseq ? p.tseq[t] : t;
-    if (p.dbg && (unsigned)sq >= (unsigned)p.pl.T) {
+    if (p.dbg && (unsigned)sq >= (unsigned)MLA_PL(T)) {
       atomicOr(p.err, MLA_GD_CHECK_SEQ_RANGE);
     } else if (p.dbg && col >= p.MB) {
       atomicOr(p.err, MLA_GD_CHECK_TABLE_COLUMN);
@@ -95,7 +96,7 @@ __device__ __forceinline__ bool slot_ok(const StepParams& p, int t) {
   const int s = p.slot[t];
   const bool in_range = (unsigned)s < (unsigned)p.NBLK * (unsigned)p.BS;
   int shared = 0;
-  for (int u = threadIdx.x; u < p.pl.T; u += blockDim.x) shared |= (u != t && p.slot[u] == s);
+  for (int u = threadIdx.x; u < MLA_PL(T); u += blockDim.x) shared |= (u != t && p.slot[u] == s);
   shared = __syncthreads_or(shared);
   if (threadIdx.x == 0) {
     if (!in_range) atomicOr(p.err, MLA_GD_CHECK_SLOT_RANGE);
@@ -144,8 +145,8 @@ __device__ __forceinline__ void wait_count(const unsigned* c, unsigned target, u
 template <int NTT, class Sy = HandoffNone>
 __device__ __attribute__((always_inline)) void phase_down(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
-  const int T = pl.T;
-  const int n_gemv = pl.nt1 * pl.s1;
+  const int T = MLA_PL(T);
+  const int n_gemv = pl.nt1 * MLA_PL(s1);
   if (b >= n_gemv) {
     index_build(p, (b - n_gemv) * kBlock + threadIdx.x);
     return;
@@ -153,11 +154,11 @@ __device__ __attribute__((always_inline)) void phase_down(const StepParams& p, i
   const int slab = b / pl.nt1, tile = b % pl.nt1;
   const bool is_q = tile < pl.nt_q;
   const bf16_t* W = is_q ? p.wq_a : p.wkv_a;
-  const int N = is_q ? p.Q : p.KVR;
-  const int c0 = (is_q ? tile : tile - pl.nt_q) * pl.tw1;
-  const int nc = min(pl.tw1, N - c0);
-  const int N1 = p.Q + p.KVR;
-  const int k0 = slab * pl.ks1, ks = min(pl.ks1, p.H - k0);
+  const int N = is_q ? MLA_D(Q) : MLA_D(KVR);
+  const int c0 = (is_q ? tile : tile - pl.nt_q) * MLA_PL(tw1);
+  const int nc = min(MLA_PL(tw1), N - c0);
+  const int N1 = MLA_D(Q) + MLA_D(KVR);
+  const int k0 = slab * MLA_PL(ks1), ks = min(MLA_PL(ks1), MLA_D(H) - k0);
   float* xs = lds + GemvLds<NTT>::xs;
   float* red = lds + GemvLds<NTT>::red;
   for (int t0 = 0; t0 < T; t0 += NTT) {
@@ -166,7 +167,7 @@ __device__ __attribute__((always_inline)) void phase_down(const StepParams& p, i
     gemv_first<gemv_unroll(NTT)>(W, N, k0, ks, c0, nc, v);
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) {
       const int tt = idx / ks, r = idx % ks;
-      xs[tt * kTile + r] = bf16_to_f32(p.x[(size_t)(t0 + tt) * p.H + k0 + r]) * p.g_in[k0 + r];
+      xs[tt * kTile + r] = bf16_to_f32(p.x[(size_t)(t0 + tt) * MLA_D(H) + k0 + r]) * p.g_in[k0 + r];
     }
     if (tile == 0) {
       // sum of x^2 over this slab, one 32-lane group per token
@@ -174,7 +175,7 @@ __device__ __attribute__((always_inline)) void phase_down(const StepParams& p, i
       float s = 0.f;
       if (tt < nt)
         for (int r = rp; r < ks; r += 32) {
-          const float xv = bf16_to_f32(p.x[(size_t)(t0 + tt) * p.H + k0 + r]);
+          const float xv = bf16_to_f32(p.x[(size_t)(t0 + tt) * MLA_D(H) + k0 + r]);
           s = fmaf(xv, xv, s);
         }
 #pragma unroll
@@ -182,7 +183,7 @@ __device__ __attribute__((always_inline)) void phase_down(const StepParams& p, i
       if (tt < nt && rp == 0) sy.st(p.ssx + (size_t)slab * T + t0 + tt, s);
     }
     __syncthreads();
-    float* part = p.part1 + ((size_t)slab * T + t0) * N1 + (is_q ? 0 : p.Q);
+    float* part = p.part1 + ((size_t)slab * T + t0) * N1 + (is_q ? 0 : MLA_D(Q));
     gemv_tile<NTT, gemv_unroll(NTT)>(W, N, k0, ks, c0, nc, xs, kTile, nt, part, N1, red, v, sy);
   }
 }
@@ -195,38 +196,38 @@ __device__ __attribute__((always_inline)) void phase_down(const StepParams& p, i
 template <int NTT, class Sy = HandoffNone>
 __device__ __attribute__((always_inline)) void phase_qup(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
-  const int T = pl.T;
-  const int N1 = p.Q + p.KVR;
-  const int n_gemv = pl.nt2 * pl.s2;
+  const int T = MLA_PL(T);
+  const int N1 = MLA_D(Q) + MLA_D(KVR);
+  const int n_gemv = pl.nt2 * MLA_PL(s2);
   float* xs = lds + GemvLds<NTT>::xs;
   float* red = lds + GemvLds<NTT>::red;
   float* scratch = lds + GemvLds<NTT>::scratch;
   if (b >= n_gemv) {
-    const int t = (b - n_gemv) / pl.nkv, sl = (b - n_gemv) % pl.nkv;
-    const int c0 = sl * kKvSlice, nc = min(kKvSlice, p.KVR - c0);
+    const int t = (b - n_gemv) / MLA_PL(nkv), sl = (b - n_gemv) % MLA_PL(nkv);
+    const int c0 = sl * kKvSlice, nc = min(kKvSlice, MLA_D(KVR) - c0);
     float* kv = xs;  // [64]
     float* sx = xs + kKvSlice;
     sy.wait();
-    reduce_parts4(p.part1 + (size_t)t * N1 + p.Q + c0, (size_t)T * N1, pl.s1, nc / 4, nc / 4, 0, kv, scratch, sy);
-    reduce_parts(p.ssx + t, T, pl.s1, 1, 1, 0, sx, scratch, sy);
-    const float alpha = inv_rms(sx[0], p.H, p.eps);
+    reduce_parts4(p.part1 + (size_t)t * N1 + MLA_D(Q) + c0, (size_t)T * N1, MLA_PL(s1), nc / 4, nc / 4, 0, kv, scratch, sy);
+    reduce_parts(p.ssx + t, T, MLA_PL(s1), 1, 1, 0, sx, scratch, sy);
+    const float alpha = inv_rms(sx[0], MLA_D(H), p.eps);
     float ss = 0.f;
     for (int c = threadIdx.x; c < nc; c += kBlock) {
       const float y = alpha * kv[c];
-      sy.st(p.kvr + (size_t)t * p.KVR + c0 + c, y);
-      if (c0 + c < p.R) ss = fmaf(y, y, ss);
+      sy.st(p.kvr + (size_t)t * MLA_D(KVR) + c0 + c, y);
+      if (c0 + c < MLA_D(R)) ss = fmaf(y, y, ss);
     }
     ss = block_sum(ss, scratch);
-    if (threadIdx.x == 0) sy.st(p.kvss + (size_t)t * pl.nkv + sl, ss);
+    if (threadIdx.x == 0) sy.st(p.kvss + (size_t)t * MLA_PL(nkv) + sl, ss);
     return;
   }
   const int slab = b / pl.nt2, tile = b % pl.nt2;
-  const int c0 = tile * pl.tw2, nc = min(pl.tw2, p.N2 - c0);
-  const int k0 = slab * pl.ks2, ks = min(pl.ks2, p.Q - k0);
+  const int c0 = tile * MLA_PL(tw2), nc = min(MLA_PL(tw2), MLA_D(N2) - c0);
+  const int k0 = slab * MLA_PL(ks2), ks = min(MLA_PL(ks2), MLA_D(Q) - k0);
   for (int t0 = 0; t0 < T; t0 += NTT) {
     const int nt = min(NTT, T - t0);
     u32x4 v[gemv_unroll(NTT)];
-    gemv_first<gemv_unroll(NTT)>(p.wq_b, p.N2, k0, ks, c0, nc, v);
+    gemv_first<gemv_unroll(NTT)>(p.wq_b, MLA_D(N2), k0, ks, c0, nc, v);
     // g_q of this thread's columns r = tid + 256k, before the partials (an
     // input, so before any wait too)
     float gq[2];
@@ -237,7 +238,7 @@ __device__ __attribute__((always_inline)) void phase_qup(const StepParams& p, in
     }
     sy.wait();
     // acc_a[t][k0 .. k0+ks) reduced over the down-projection's slabs
-    reduce_parts4(p.part1 + (size_t)t0 * N1 + k0, (size_t)T * N1, pl.s1, nt * ks / 4, ks / 4, N1, xs, scratch, sy);
+    reduce_parts4(p.part1 + (size_t)t0 * N1 + k0, (size_t)T * N1, MLA_PL(s1), nt * ks / 4, ks / 4, N1, xs, scratch, sy);
     if (tile == 0) {
       const int tt = threadIdx.x >> 5, rp = threadIdx.x & 31;
       float s = 0.f;
@@ -259,7 +260,7 @@ __device__ __attribute__((always_inline)) void phase_qup(const StepParams& p, in
       for (int tt = 0; tt < nt; ++tt) xs[tt * ks + r] *= g;
     }
     __syncthreads();
-    gemv_tile<NTT, gemv_unroll(NTT)>(p.wq_b, p.N2, k0, ks, c0, nc, xs, ks, nt, p.part2 + ((size_t)slab * T + t0) * p.N2, p.N2, red, v, sy);
+    gemv_tile<NTT, gemv_unroll(NTT)>(p.wq_b, MLA_D(N2), k0, ks, c0, nc, xs, ks, nt, p.part2 + ((size_t)slab * T + t0) * MLA_D(N2), MLA_D(N2), red, v, sy);
   }
 }
 
@@ -274,15 +275,15 @@ constexpr int kTsPre = 2;
 
 template <class Sy>
 __device__ __forceinline__ float tscale_at(const StepParams& p, int t0, int nt, int q, const Sy& sy) {
-  const int n1 = nt * p.pl.s1;
-  if (q < n1) return sy.ld(p.ssx + (size_t)(q / nt) * p.pl.T + t0 + q % nt);
+  const int n1 = nt * MLA_PL(s1);
+  if (q < n1) return sy.ld(p.ssx + (size_t)(q / nt) * MLA_PL(T) + t0 + q % nt);
   q -= n1;
-  return sy.ld(p.ssq + (size_t)(q / nt) * p.pl.T + t0 + q % nt);
+  return sy.ld(p.ssq + (size_t)(q / nt) * MLA_PL(T) + t0 + q % nt);
 }
 
 template <class Sy>
 __device__ __forceinline__ void tscale_load(const StepParams& p, int t0, int nt, float (&v)[kTsPre], const Sy& sy) {
-  const int nq = nt * (p.pl.s1 + p.pl.s2);
+  const int nq = nt * (MLA_PL(s1) + MLA_PL(s2));
 #pragma unroll
   for (int k = 0; k < kTsPre; ++k) {
     const int q = threadIdx.x + k * kBlock;
@@ -294,7 +295,7 @@ template <class Sy>
 __device__ __forceinline__ void tscale_finish(const StepParams& p, int t0, int nt, const float (&v)[kTsPre],
                                               float* beta, float* scr, const Sy& sy) {
   const Plan& pl = p.pl;
-  const int nq = nt * (pl.s1 + pl.s2);
+  const int nq = nt * (MLA_PL(s1) + MLA_PL(s2));
 #pragma unroll
   for (int k = 0; k < kTsPre; ++k) {
     const int q = threadIdx.x + k * kBlock;
@@ -305,10 +306,10 @@ __device__ __forceinline__ void tscale_finish(const StepParams& p, int t0, int n
   if ((int)threadIdx.x < nt) {
     const int tt = threadIdx.x;
     float sx = 0.f, sq = 0.f;
-    for (int sl = 0; sl < pl.s1; ++sl) sx += scr[sl * nt + tt];
-    for (int sl = 0; sl < pl.s2; ++sl) sq += scr[(pl.s1 + sl) * nt + tt];
-    const float a = inv_rms(sx, p.H, p.eps);
-    const float iq = 1.f / sqrtf(a * a * sq / (float)p.Q + p.eps);
+    for (int sl = 0; sl < MLA_PL(s1); ++sl) sx += scr[sl * nt + tt];
+    for (int sl = 0; sl < MLA_PL(s2); ++sl) sq += scr[(MLA_PL(s1) + sl) * nt + tt];
+    const float a = inv_rms(sx, MLA_D(H), p.eps);
+    const float iq = 1.f / sqrtf(a * a * sq / (float)MLA_D(Q) + p.eps);
     beta[tt] = a * iq;
   }
   __syncthreads();
@@ -331,22 +332,22 @@ static_assert(kTT * 32 <= kBlock, "one RoPE pair per thread for every token of a
 template <int NTT, class Sy = HandoffNone>
 __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
-  const int T = pl.T;
+  const int T = MLA_PL(T);
   float* xs = lds + GemvLds<NTT>::xs;
   float* red = lds + GemvLds<NTT>::red;
   float* scratch = lds + GemvLds<NTT>::scratch;
-  const int n_abs = p.NH * pl.ncc3;
+  const int n_abs = MLA_D(NH) * MLA_PL(ncc3);
   if (b >= n_abs) {
     const int t = b - n_abs;
-    const float* kv = p.kvr + (size_t)t * p.KVR;
+    const float* kv = p.kvr + (size_t)t * MLA_D(KVR);
     // inputs first: g_kv of columns tid + 256k (kv_lora_rank <= 512) and
     // the RoPE table of pair tid (qk_rope_head_dim <= 64)
-    const int half = p.DR / 2;
+    const int half = MLA_D(DR) / 2;
     float gk[2], rc = 0.f, rs = 0.f;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int c = threadIdx.x + k * kBlock;
-      gk[k] = c < p.R ? p.g_kv[c] : 0.f;
+      gk[k] = c < MLA_D(R) ? p.g_kv[c] : 0.f;
     }
     if ((int)threadIdx.x < half) {
       rc = p.cos_t[(size_t)t * half + threadIdx.x];
@@ -354,29 +355,29 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
     }
     sy.wait();
     float ss = 0.f;
-    for (int i = threadIdx.x; i < pl.nkv; i += kBlock) ss += sy.ld(p.kvss + (size_t)t * pl.nkv + i);
+    for (int i = threadIdx.x; i < MLA_PL(nkv); i += kBlock) ss += sy.ld(p.kvss + (size_t)t * MLA_PL(nkv) + i);
     ss = block_sum(ss, scratch);
-    const float inv = inv_rms(ss, p.R, p.eps);
+    const float inv = inv_rms(ss, MLA_D(R), p.eps);
     if (!slot_ok(p, t)) return;
-    bf16_t* row = p.cache + (size_t)p.slot[t] * p.KVR;
+    bf16_t* row = p.cache + (size_t)p.slot[t] * MLA_D(KVR);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int c = threadIdx.x + k * kBlock;
-      if (c < p.R) sy.st(row + c, f32_to_bf16(sy.ld(kv + c) * inv * gk[k]));
+      if (c < MLA_D(R)) sy.st(row + c, f32_to_bf16(sy.ld(kv + c) * inv * gk[k]));
     }
     if ((int)threadIdx.x < half) {
       const int i = threadIdx.x;
-      const float x0 = sy.ld(kv + p.R + 2 * i), x1 = sy.ld(kv + p.R + 2 * i + 1);
-      sy.st(row + p.R + 2 * i, f32_to_bf16(x0 * rc - x1 * rs));
-      sy.st(row + p.R + 2 * i + 1, f32_to_bf16(x0 * rs + x1 * rc));
+      const float x0 = sy.ld(kv + MLA_D(R) + 2 * i), x1 = sy.ld(kv + MLA_D(R) + 2 * i + 1);
+      sy.st(row + MLA_D(R) + 2 * i, f32_to_bf16(x0 * rc - x1 * rs));
+      sy.st(row + MLA_D(R) + 2 * i + 1, f32_to_bf16(x0 * rs + x1 * rc));
     }
     return;
   }
-  const int h = b / pl.ncc3, cc = b % pl.ncc3;
+  const int h = b / MLA_PL(ncc3), cc = b % MLA_PL(ncc3);
   const int c0 = cc * 64;
   float* beta = lds + GemvLds<NTT>::aux;
   float* qo = lds + GemvLds<NTT>::aux + 512;  // [NTT][64]
-  const bf16_t* W = p.w_qabs + (size_t)h * p.DN * p.R;
+  const bf16_t* W = p.w_qabs + (size_t)h * MLA_D(DN) * MLA_D(R);
   for (int t0 = 0; t0 < T; t0 += NTT) {
     const int nt = min(NTT, T - t0);
     // the small loads go out before the weight stream (in one launch with
@@ -385,10 +386,10 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
     // thread's item (token, 4 columns) and slab part sp (s = sp, sp + nsp,
     // ...), its first kAbsPre terms
     u32x4 v[gemv_unroll(NTT)];
-    if constexpr (Sy::kWeightsFirst) gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
+    if constexpr (Sy::kWeightsFirst) gemv_first<gemv_unroll(NTT)>(W, MLA_D(R), 0, MLA_D(DN), c0, 64, v);
     // the chunk-0 workgroup's RoPE tables: pair idx = tid of token idx / half
     // (nt * half <= kTT * 32 <= kBlock), inputs, so before any wait
-    const int half = p.DR / 2;
+    const int half = MLA_D(DR) / 2;
     float rc = 0.f, rs = 0.f;
     if (cc == 0 && (int)threadIdx.x < nt * half) {
       const int t = t0 + (int)threadIdx.x / half, i = (int)threadIdx.x % half;
@@ -398,30 +399,30 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
     if constexpr (Sy::kWeightsFirst) sy.wait();
     float tsv[kTsPre];
     tscale_load(p, t0, nt, tsv, sy);
-    const int n4 = nt * p.DN / 4, w4 = p.DN / 4;
+    const int n4 = nt * MLA_D(DN) / 4, w4 = MLA_D(DN) / 4;
     const int nsp = max(1, min(16, kBlock / n4));
     const bool one_item = n4 * nsp <= kBlock;
     const int item = threadIdx.x % n4, sp = threadIdx.x / n4;
     const bool has_item = one_item && (int)threadIdx.x < n4 * nsp;
-    const float* src = p.part2 + (size_t)(t0 + item / w4) * p.N2 + (size_t)h * p.QKH + 4 * (item % w4);
-    const size_t sstride = (size_t)T * p.N2;
+    const float* src = p.part2 + (size_t)(t0 + item / w4) * MLA_D(N2) + (size_t)h * MLA_D(QKH) + 4 * (item % w4);
+    const size_t sstride = (size_t)T * MLA_D(N2);
     constexpr int kAbsPre = abs_pre(NTT);
     float4 xpre[kAbsPre];
 #pragma unroll
     for (int k = 0; k < kAbsPre; ++k) {
       const int sl = sp + k * nsp;
-      xpre[k] = (has_item && sl < pl.s2) ? sy.ld4(src + (size_t)sl * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      xpre[k] = (has_item && sl < MLA_PL(s2)) ? sy.ld4(src + (size_t)sl * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     // the chunk-0 workgroup's q_pe partials: (slab, item) pairs q = s*nr + i,
     // staged in the reduction area after the GEMV and added in slab order
     // (when they fit it)
     constexpr int kRopePre = 4;
-    const int nr = nt * p.DR, nrs = nr * pl.s2;
+    const int nr = nt * MLA_D(DR), nrs = nr * MLA_PL(s2);
     const bool rope_lds = cc == 0 && nrs <= 3 * NTT * kTile;
-    const float* rsrc = p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH + p.DN;
+    const float* rsrc = p.part2 + (size_t)t0 * MLA_D(N2) + (size_t)h * MLA_D(QKH) + MLA_D(DN);
     auto rope_at = [&](int q) {
       const int sl = q / nr, i = q % nr;
-      return sy.ld(rsrc + ((size_t)sl * T + i / p.DR) * p.N2 + i % p.DR);
+      return sy.ld(rsrc + ((size_t)sl * T + i / MLA_D(DR)) * MLA_D(N2) + i % MLA_D(DR));
     };
     float rp[kRopePre];
 #pragma unroll
@@ -429,7 +430,7 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
       const int q = threadIdx.x + k * kBlock;
       rp[k] = (rope_lds && q < nrs) ? rope_at(q) : 0.f;
     }
-    if constexpr (!Sy::kWeightsFirst) gemv_first<gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, v);
+    if constexpr (!Sy::kWeightsFirst) gemv_first<gemv_unroll(NTT)>(W, MLA_D(R), 0, MLA_D(DN), c0, 64, v);
     tscale_finish(p, t0, nt, tsv, beta, red, sy);  // `red` is free until the GEMV
     if (one_item) {
       float4* out = reinterpret_cast<float4*>(nsp == 1 ? xs : scratch);
@@ -439,7 +440,7 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
         for (int k = 0; k < kAbsPre; ++k) {
           a.x += xpre[k].x; a.y += xpre[k].y; a.z += xpre[k].z; a.w += xpre[k].w;  // zeros past the last slab
         }
-        for (int sl = sp + kAbsPre * nsp; sl < pl.s2; sl += nsp) {
+        for (int sl = sp + kAbsPre * nsp; sl < MLA_PL(s2); sl += nsp) {
           const float4 x = sy.ld4(src + (size_t)sl * sstride);
           a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
         }
@@ -458,15 +459,15 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
         __syncthreads();
       }
     } else {
-      reduce_parts4(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH, (size_t)T * p.N2, pl.s2, nt * p.DN / 4,
-                    p.DN / 4, p.N2, xs, scratch, sy);
+      reduce_parts4(p.part2 + (size_t)t0 * MLA_D(N2) + (size_t)h * MLA_D(QKH), (size_t)T * MLA_D(N2), MLA_PL(s2), nt * MLA_D(DN) / 4,
+                    MLA_D(DN) / 4, MLA_D(N2), xs, scratch, sy);
     }
-    for (int idx = threadIdx.x; idx < nt * p.DN; idx += kBlock) xs[idx] *= beta[idx / p.DN];
+    for (int idx = threadIdx.x; idx < nt * MLA_D(DN); idx += kBlock) xs[idx] *= beta[idx / MLA_D(DN)];
     __syncthreads();
-    gemv_tile<NTT, gemv_unroll(NTT)>(W, p.R, 0, p.DN, c0, 64, xs, p.DN, nt, qo - c0, 64, red, v);
+    gemv_tile<NTT, gemv_unroll(NTT)>(W, MLA_D(R), 0, MLA_D(DN), c0, 64, xs, MLA_D(DN), nt, qo - c0, 64, red, v);
     for (int idx = threadIdx.x; idx < nt * 64; idx += kBlock) {
       const int tt = idx / 64, c = idx % 64;
-      sy.st(p.qcat + ((size_t)(t0 + tt) * p.NH + h) * p.KVR + c0 + c, f32_to_bf16(qo[tt * 64 + c] * p.scale_log2));
+      sy.st(p.qcat + ((size_t)(t0 + tt) * MLA_D(NH) + h) * MLA_D(KVR) + c0 + c, f32_to_bf16(qo[tt * 64 + c] * p.scale_log2));
     }
     if (cc == 0) {
       if (rope_lds) {
@@ -479,20 +480,20 @@ __device__ __attribute__((always_inline)) void phase_absorb(const StepParams& p,
         __syncthreads();
         for (int i = threadIdx.x; i < nr; i += kBlock) {
           float a = 0.f;
-          for (int sl = 0; sl < pl.s2; ++sl) a += red[sl * nr + i];
+          for (int sl = 0; sl < MLA_PL(s2); ++sl) a += red[sl * nr + i];
           xs[i] = a;
         }
         __syncthreads();
       } else {
-        reduce_parts(p.part2 + (size_t)t0 * p.N2 + (size_t)h * p.QKH + p.DN, (size_t)T * p.N2, pl.s2, nt * p.DR,
-                     p.DR, p.N2, xs, scratch, sy);
+        reduce_parts(p.part2 + (size_t)t0 * MLA_D(N2) + (size_t)h * MLA_D(QKH) + MLA_D(DN), (size_t)T * MLA_D(N2), MLA_PL(s2), nt * MLA_D(DR),
+                     MLA_D(DR), MLA_D(N2), xs, scratch, sy);
       }
       if ((int)threadIdx.x < nt * half) {
         const int tt = threadIdx.x / half, i = threadIdx.x % half, t = t0 + tt;
         // the query tile is stored pre-scaled by softmax_scale * log2(e)
         const float bq = beta[tt] * p.scale_log2;
-        const float x0 = bq * xs[tt * p.DR + 2 * i], x1 = bq * xs[tt * p.DR + 2 * i + 1];
-        bf16_t* q = p.qcat + ((size_t)t * p.NH + h) * p.KVR + p.R;
+        const float x0 = bq * xs[tt * MLA_D(DR) + 2 * i], x1 = bq * xs[tt * MLA_D(DR) + 2 * i + 1];
+        bf16_t* q = p.qcat + ((size_t)t * MLA_D(NH) + h) * MLA_D(KVR) + MLA_D(R);
         sy.st(q + 2 * i, f32_to_bf16(x0 * rc - x1 * rs));
         sy.st(q + 2 * i + 1, f32_to_bf16(x0 * rs + x1 * rc));
       }
@@ -516,7 +517,7 @@ struct CoreWaitFused {
   // every wave of the workgroup), then releases the others at the barrier
   __device__ void before_rows(int) const {
     if (threadIdx.x == 0) {
-      wait_count(p.sync, (unsigned)p.pl.T, p.sync + kSyncStride);
+      wait_count(p.sync, (unsigned)MLA_PL(T), p.sync + kSyncStride);
       __threadfence();
     }
     __syncthreads();
@@ -524,8 +525,8 @@ struct CoreWaitFused {
   __device__ void before_q(int h0) const {
     const int i = threadIdx.x;
     if (i < 64) {
-      if (i < 16 * HG && h0 + i < p.NH)
-        wait_count(p.sync + (2 + h0 + i) * kSyncStride, (unsigned)p.pl.ncc3, p.sync + kSyncStride);
+      if (i < 16 * HG && h0 + i < MLA_D(NH))
+        wait_count(p.sync + (2 + h0 + i) * kSyncStride, (unsigned)MLA_PL(ncc3), p.sync + kSyncStride);
       __threadfence();  // after every polling lane of the wave is done
     }
     __syncthreads();
@@ -537,7 +538,7 @@ struct CoreWaitFused {
 template <int NT, int HG, int CS>
 __device__ void phase_absorb_core(const StepParams& p, int b, char* lds) {
   const Plan& pl = p.pl;
-  const int T = pl.T, n_abs = p.NH * pl.ncc3;
+  const int T = MLA_PL(T), n_abs = MLA_D(NH) * MLA_PL(ncc3);
   if (b < T) {  // kv row of token b
     phase_absorb<kTT>(p, n_abs + b, reinterpret_cast<float*>(lds));
     count_done(p.sync);
@@ -545,7 +546,7 @@ __device__ void phase_absorb_core(const StepParams& p, int b, char* lds) {
   }
   if (b < T + n_abs) {
     phase_absorb<kTT>(p, b - T, reinterpret_cast<float*>(lds));
-    count_done(p.sync + (2 + (b - T) / pl.ncc3) * kSyncStride);
+    count_done(p.sync + (2 + (b - T) / MLA_PL(ncc3)) * kSyncStride);
     return;
   }
   core_phase<NT, HG, CS>(p, b - T - n_abs, lds, CoreWaitFused<NT, HG, CS>{p});
@@ -569,11 +570,11 @@ constexpr int kOabsPre = 8;  // split partials per thread loaded ahead of the sp
 template <class Sy = HandoffNone>
 __device__ __attribute__((always_inline)) void phase_oabsorb(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
-  const int T = pl.T, NSP = pl.nsplit, R = p.R, DV = p.DV;
-  const int per_h = pl.nc5 * pl.nt5c;
+  const int T = MLA_PL(T), NSP = MLA_PL(nsplit), R = MLA_D(R), DV = MLA_D(DV);
+  const int per_h = pl.nc5 * MLA_PL(nt5c);
   const int h = b / per_h, rem = b % per_h;
-  const int j = rem / pl.nt5c, tch = rem % pl.nt5c;
-  const int t0 = tch * pl.tc5, nt = min(pl.tc5, T - t0);
+  const int j = rem / MLA_PL(nt5c), tch = rem % MLA_PL(nt5c);
+  const int t0 = tch * MLA_PL(tc5), nt = min(MLA_PL(tc5), T - t0);
   const int c0 = j * kOabsCols;
   const int tid = threadIdx.x;
   // piece q = i*256 + tid of a 128-row pass: row q / 8, columns c0 + 8*(q % 8) .. +8
@@ -590,7 +591,7 @@ __device__ __attribute__((always_inline)) void phase_oabsorb(const StepParams& p
   load_pass(0, wr);
   sy.wait();
   float* pmL = lds;                  // [tc5][NSP]: split weights
-  float* linv = pmL + pl.tc5 * NSP;  // [tc5]
+  float* linv = pmL + MLA_PL(tc5) * NSP;  // [tc5]
   float* ol = lds + kOabsOl;            // [tc5][64]
   float* scratch = lds + kOabsScratch;  // 256 float4
   // this thread's combine item (token, 4 columns) and part sp of the splits
@@ -602,8 +603,8 @@ __device__ __attribute__((always_inline)) void phase_oabsorb(const StepParams& p
   const bool has_item = tid < n4 * nsp;
   const int item = tid % n4, sp = tid / n4;
   const int tti = item / C4, c4i = item % C4;
-  const float* src = p.po + ((size_t)(t0 + tti) * NSP * p.NH + h) * R + c0 + 4 * c4i;
-  const size_t sstride = (size_t)p.NH * R;
+  const float* src = p.po + ((size_t)(t0 + tti) * NSP * MLA_D(NH) + h) * R + c0 + 4 * c4i;
+  const size_t sstride = (size_t)MLA_D(NH) * R;
   float4 xpre[kOabsPre];
 #pragma unroll
   for (int k = 0; k < kOabsPre; ++k) {
@@ -617,7 +618,7 @@ __device__ __attribute__((always_inline)) void phase_oabsorb(const StepParams& p
   {
     const int lane = tid & 63, wv = tid >> 6;
     for (int tt = wv; tt < nt; tt += kBlock / kWave) {
-      const size_t q = ((size_t)(t0 + tt) * NSP + lane) * p.NH + h;
+      const size_t q = ((size_t)(t0 + tt) * NSP + lane) * MLA_D(NH) + h;
       const float m = lane < NSP ? p.pm[q] : -INFINITY;
       const float l = lane < NSP ? p.pden[q] : 0.f;
       const float M = wave_max_dpp(m);
@@ -672,7 +673,7 @@ __device__ __attribute__((always_inline)) void phase_oabsorb(const StepParams& p
   }
   // the eight lanes of a row hold its eight pieces: dot products, then a
   // fixed-order reduction over the eight lanes
-  float* ovp = p.ov + (size_t)j * T * p.NH * DV;
+  float* ovp = p.ov + (size_t)j * T * MLA_D(NH) * DV;
   for (int d0 = 0; d0 < DV; d0 += kBlock * kOabsPieces / 8) {
     if (d0 > 0) load_pass(d0, wr);
 #pragma unroll
@@ -687,7 +688,7 @@ __device__ __attribute__((always_inline)) void phase_oabsorb(const StepParams& p
         a += __shfl_xor(a, 1, kWave);
         a += __shfl_xor(a, 2, kWave);
         a += __shfl_xor(a, 4, kWave);
-        if (pc == 0 && d < DV) sy.st(ovp + (size_t)(t0 + tt) * p.NH * DV + (size_t)h * DV + d, a);
+        if (pc == 0 && d < DV) sy.st(ovp + (size_t)(t0 + tt) * MLA_D(NH) * DV + (size_t)h * DV + d, a);
       }
     }
   }
@@ -699,17 +700,17 @@ __device__ __attribute__((always_inline)) void phase_oabsorb(const StepParams& p
 template <int NTT, class Sy = HandoffNone>
 __device__ __attribute__((always_inline)) void phase_oproj(const StepParams& p, int b, float* lds, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
-  const int T = pl.T;
-  const int K = p.NH * p.DV;
+  const int T = MLA_PL(T);
+  const int K = MLA_D(NH) * MLA_D(DV);
   const int slab = b / pl.nt6, tile = b % pl.nt6;
-  const int c0 = tile * pl.tw6, nc = min(pl.tw6, p.H - c0);
-  const int k0 = slab * pl.ks6, ks = min(pl.ks6, K - k0);
+  const int c0 = tile * MLA_PL(tw6), nc = min(MLA_PL(tw6), MLA_D(H) - c0);
+  const int k0 = slab * MLA_PL(ks6), ks = min(MLA_PL(ks6), K - k0);
   float* xs = lds + GemvLds<NTT>::xs;
   float* red = lds + GemvLds<NTT>::red;
   for (int t0 = 0; t0 < T; t0 += NTT) {
     const int nt = min(NTT, T - t0);
     u32x4 v[gemv_unroll(NTT)];
-    gemv_first<gemv_unroll(NTT)>(p.w_o, p.H, k0, ks, c0, nc, v);
+    gemv_first<gemv_unroll(NTT)>(p.w_o, MLA_D(H), k0, ks, c0, nc, v);
     sy.wait();
     // o_v = the output absorption's column-chunk shares, added in chunk order
     for (int idx = threadIdx.x; idx < nt * ks; idx += kBlock) {
@@ -725,7 +726,7 @@ __device__ __attribute__((always_inline)) void phase_oproj(const StepParams& p, 
       xs[tt * kTile + r] = a;
     }
     __syncthreads();
-    gemv_tile<NTT, gemv_unroll(NTT)>(p.w_o, p.H, k0, ks, c0, nc, xs, kTile, nt, p.part6 + ((size_t)slab * T + t0) * p.H, p.H, red, v, sy);
+    gemv_tile<NTT, gemv_unroll(NTT)>(p.w_o, MLA_D(H), k0, ks, c0, nc, xs, kTile, nt, p.part6 + ((size_t)slab * T + t0) * MLA_D(H), MLA_D(H), red, v, sy);
   }
 }
 
@@ -741,18 +742,18 @@ template <class Sy = HandoffNone>
 __device__ __attribute__((always_inline)) void phase_out(const StepParams& p, int b, float*, const Sy& sy = Sy()) {
   const Plan& pl = p.pl;
   sy.wait();
-  const int ncg = (p.H + kOutCols - 1) / kOutCols;
+  const int ncg = (MLA_D(H) + kOutCols - 1) / kOutCols;
   const int t = b / ncg;
   const int part = threadIdx.x & 3;
   const int c = (b % ncg) * kOutCols + 4 * (threadIdx.x >> 2);
-  const bool ok = c < p.H;  // H % 8 == 0: a group of four is wholly inside or outside
-  const size_t stride = (size_t)pl.T * p.H;
-  const float* src = p.part6 + (size_t)t * p.H + (ok ? c : 0);
+  const bool ok = c < MLA_D(H);  // H % 8 == 0: a group of four is wholly inside or outside
+  const size_t stride = (size_t)MLA_PL(T) * MLA_D(H);
+  const float* src = p.part6 + (size_t)t * MLA_D(H) + (ok ? c : 0);
   // this lane's slabs s = part, part + 4, ..., eight loads at a time; a lane
   // loads only slabs that exist (with eight or nine slabs a lane needs two or
   // three, and an unconditional reload of the last would triple the loads)
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int S = pl.s6;
+  const int S = MLA_PL(s6);
   for (int s = part; s < S; s += 32) {
     float4 v[8];
 #pragma unroll
@@ -774,7 +775,7 @@ __device__ __attribute__((always_inline)) void phase_out(const StepParams& p, in
     uint2 o;
     o.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
     o.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
-    *reinterpret_cast<uint2*>(p.out + (size_t)t * p.H + c) = o;
+    *reinterpret_cast<uint2*>(p.out + (size_t)t * MLA_D(H) + c) = o;
   }
 }
 
@@ -790,8 +791,8 @@ __device__ __attribute__((always_inline)) void phase_out(const StepParams& p, in
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool oproj_fold_out(const StepParams& p, int tile, float* lds) {
   const Plan& pl = p.pl;
-  const int T = pl.T, S = pl.s6;
-  const int c0 = tile * pl.tw6, nc = min(pl.tw6, p.H - c0);
+  const int T = MLA_PL(T), S = MLA_PL(s6);
+  const int c0 = tile * MLA_PL(tw6), nc = min(MLA_PL(tw6), MLA_D(H) - c0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   wait_vmcnt<0>();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -802,10 +803,10 @@ __device__ __forceinline__ bool oproj_fold_out(const StepParams& p, int tile, fl
   __syncthreads();
   if (arrived[0] != (unsigned)S - 1u) return false;
   const int n4 = nc / 4;  // H % 8 == 0 and tw6 % 8 == 0
-  const size_t sstride = (size_t)T * p.H;
+  const size_t sstride = (size_t)T * MLA_D(H);
   for (int it = threadIdx.x; it < T * n4; it += kBlock) {
     const int tt = it / n4, c = c0 + 4 * (it % n4);
-    const float* src = p.part6 + (size_t)tt * p.H + c;
+    const float* src = p.part6 + (size_t)tt * MLA_D(H) + c;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < S; s += 8) {
       float4 v[8];
@@ -819,9 +820,9 @@ __device__ __forceinline__ bool oproj_fold_out(const StepParams& p, int tile, fl
     uint2 o;
     o.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
     o.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
-    *reinterpret_cast<uint2*>(p.out + (size_t)tt * p.H + c) = o;
+    *reinterpret_cast<uint2*>(p.out + (size_t)tt * MLA_D(H) + c) = o;
   }
   return true;
 }
 
-}  // namespace mla
+}  // namespace MLA_PHASE_NS

@@ -4,6 +4,23 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// The phase code (phases.h, core_mfma.h) reads the step's dimensions and the
+// plan values of the one-token GEMV path through these two macros.  Normally
+// they read the kernel argument `p`; a translation unit that defines
+// MLA_FIXED_SHAPE (and the struct MlaFixedShape with the values, plus its own
+// MLA_PHASE_NS) compiles the same code with them as constants, so the index
+// arithmetic folds (fixed_shape.hip).
+#ifdef MLA_FIXED_SHAPE
+#define MLA_D(x) (MlaFixedShape::x)
+#define MLA_PL(x) (MlaFixedShape::pl_##x)
+#else
+#define MLA_D(x) (p.x)
+#define MLA_PL(x) (p.pl.x)
+#endif
+#ifndef MLA_PHASE_NS
+#define MLA_PHASE_NS mla
+#endif
+
 namespace mla {
 
 // Work decomposition of one step.  Computed on the host from the dimensions

@@ -183,6 +183,14 @@ def _masked_splits(inp):
     gi[2, 10:] = 2**30  # token 2: only its first ten entries valid, the later splits empty
 
 
+# One token at dimensions other than the DeepSeek-V3.2 ones: the generic
+# one-token kernels (the DeepSeek-V3.2 shape runs a copy compiled with its
+# sizes as constants).
+def test_parity_one_token_generic_kernels():
+    wl = replace(RAGGED, name="ragged_T1", shape=replace(RAGGED.shape, n_tokens=1), seed=501)
+    _run_and_check(wl)
+
+
 # On the matrix-core path the core stores each split's output normalised by
 # its own denominator; a split without a valid row must combine as zeros (and
 # an all-masked token give a zero output row).  Both core shapes that do so:
