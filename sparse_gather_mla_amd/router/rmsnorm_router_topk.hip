@@ -526,6 +526,31 @@ __global__ __launch_bounds__(kBlock) void k_rt_one_token(const uint16_t* __restr
   rt_select<F16>(0, x, gamma, bias, 1, H, E, K, s, eps, act, part, normed, idx, aff, DevLoads());
 }
 
+// The same launch with the DeepSeek-V3 router's sizes as compile-time
+// constants (hidden 7168, 256 experts, top 8; the plan rt_plan gives them:
+// 64-expert tiles, 28 slabs of 256 rows), so the index arithmetic folds.
+constexpr int kDsH = 7168, kDsE = 256, kDsK = 8, kDsKs = 256, kDsTiles = 4, kDsSlabs = 28;
+template <bool F16>
+__global__ __launch_bounds__(kBlock) void k_rt_one_token_ds(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ gamma,
+                                                           const uint16_t* __restrict__ W,
+                                                           const float* __restrict__ bias, float eps, int act,
+                                                           float* __restrict__ part, unsigned* __restrict__ cnt,
+                                                           uint16_t* __restrict__ normed, int32_t* __restrict__ idx,
+                                                           uint16_t* __restrict__ aff) {
+  __shared__ unsigned arrived;
+  rt_partial<F16, 1>(x, gamma, W, 1, kDsH, kDsE, kDsKs, kDsTiles, kDsSlabs, part, HandoffDevStores());
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (arrived != (unsigned)(kDsTiles * kDsSlabs) - 1u) return;
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  rt_select<F16>(0, x, gamma, bias, 1, kDsH, kDsE, kDsK, kDsSlabs, eps, act, part, normed, idx, aff, DevLoads());
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace rt
@@ -570,6 +595,13 @@ int rmsnorm_router_topk_typed(int32_t dtype, const void* hidden_states, const vo
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
   if (n_tokens == 1) {
     const RtPlan pl = rt_plan(1, hidden, n_experts);
+    if (hidden == kDsH && n_experts == kDsE && top_k == kDsK && pl.ks == kDsKs && pl.ntile == kDsTiles &&
+        pl.s == kDsSlabs) {
+      hipLaunchKernelGGL(f16 ? k_rt_one_token_ds<true> : k_rt_one_token_ds<false>, dim3(kDsTiles * kDsSlabs),
+                         dim3(kBlock), 0, s, xh, gh, wh, router_bias, eps, act, part, cnt, (uint16_t*)normed_out,
+                         topk_indices, (uint16_t*)affinities);
+      return hipGetLastError() == hipSuccess ? RT_OK : RT_E_HIP;
+    }
     hipLaunchKernelGGL(f16 ? k_rt_one_token<true> : k_rt_one_token<false>, dim3(pl.ntile * pl.s), dim3(kBlock), 0, s,
                        xh, gh, wh, router_bias, hidden, n_experts, top_k, pl.ks, pl.ntile, pl.s, eps, act, part, cnt,
                        (uint16_t*)normed_out, topk_indices, (uint16_t*)affinities);
