@@ -490,6 +490,18 @@ __global__ __launch_bounds__(kBlock) void k_rt_select(const uint16_t* __restrict
   rt_select<F16>(blockIdx.x, x, gamma, bias, T, H, E, K, s, eps, act, part, normed, idx, aff);
 }
 
+// k_rt_select with the DeepSeek-V3 router's sizes as compile-time constants
+// (hidden 7168, 256 experts, top 8, 28 slabs of partial logits); the token
+// count stays an argument.
+template <bool F16>
+__global__ __launch_bounds__(kBlock) void k_rt_select_ds(const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ gamma,
+                                                        const float* __restrict__ bias, int T, float eps, int act,
+                                                        const float* __restrict__ part, uint16_t* __restrict__ normed,
+                                                        int32_t* __restrict__ idx, uint16_t* __restrict__ aff) {
+  rt_select<F16>(blockIdx.x, x, gamma, bias, T, 7168, 256, 8, 28, eps, act, part, normed, idx, aff);
+}
+
 // Partial logits read back by the last workgroup of the same launch:
 // device-scope loads (they bypass this XCD's L2, which may hold stale lines).
 struct DevLoads {
@@ -622,6 +634,12 @@ int rmsnorm_router_topk_typed(int32_t dtype, const void* hidden_states, const vo
     slabs = pl.s;
   }
   if (hipGetLastError() != hipSuccess) return RT_E_HIP;
+  if (hidden == kDsH && n_experts == kDsE && top_k == kDsK && slabs == kDsSlabs) {
+    hipLaunchKernelGGL(f16 ? k_rt_select_ds<true> : k_rt_select_ds<false>, dim3(n_tokens), dim3(kBlock), 0, s, xh, gh,
+                       router_bias, n_tokens, eps, act, part, (uint16_t*)normed_out, topk_indices,
+                       (uint16_t*)affinities);
+    return hipGetLastError() == hipSuccess ? RT_OK : RT_E_HIP;
+  }
   hipLaunchKernelGGL(f16 ? k_rt_select<true> : k_rt_select<false>, dim3(n_tokens), dim3(kBlock), 0, s, xh, gh,
                      router_bias, n_tokens, hidden, n_experts, top_k, slabs, eps, act, part, (uint16_t*)normed_out,
                      topk_indices, (uint16_t*)affinities);
